@@ -1,0 +1,125 @@
+"""fp64 CPU oracle for the attention forward, partial and merge -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, the smoke check and the bench's CPU-baseline leg use this
+package.  The HIP product path never imports, links or calls it, and it shares
+no code with that path.  ``oracle.c`` holds the definition (see its header for
+the passages of the MSLK pages it follows); ``brute.py`` is an independent dense
+numpy version with a materialised mask bias, used to cross-check it.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+MASK_NONE, MASK_CAUSAL, MASK_BLOCKDIAG, MASK_BLOCKDIAG_CAUSAL = 0, 1, 2, 3
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP, no fast-math) into liboracle.so."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", SRC, "-o", tmp, "-lm"],
+                       check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build(force=True)
+        lib = ctypes.CDLL(LIB)
+        i64, dp, ip = ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)
+        lib.oracle_attention.argtypes = [i64, i64, i64, i64, i64, i64, dp, dp, dp, ctypes.c_int, ctypes.c_int,
+                                         ip, ip, ctypes.c_double, dp, dp]
+        lib.oracle_attention.restype = ctypes.c_int
+        lib.oracle_merge.argtypes = [i64, i64, i64, i64, i64, dp, dp, dp, dp]
+        lib.oracle_merge.restype = ctypes.c_int
+        lib.oracle_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _dp(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def threads() -> int:
+    return int(_load().oracle_threads())
+
+
+def attention(q, k, v, mask: int = MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None):
+    """Exact attention (fp64).
+
+    q [B,Mq,H,K], k [B,Mkv,H,K], v [B,Mkv,H,Kv] -> (out [B,Mq,H,Kv], lse [B,H,Mq]).
+    ``scale`` None means 1/sqrt(K).  Packed-sequence masks take int prefix sums
+    (``seqstart_k`` defaults to ``seqstart_q``) and need B == 1.
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, Mq, H, K = q.shape
+    Mkv, Kv = k.shape[1], v.shape[3]
+    assert k.shape == (B, Mkv, H, K) and v.shape == (B, Mkv, H, Kv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    out = np.empty((B, Mq, H, Kv), dtype=np.float64)
+    lse = np.empty((B, H, Mq), dtype=np.float64)
+    nseq = 0
+    sq = sk = None
+    if mask in (MASK_BLOCKDIAG, MASK_BLOCKDIAG_CAUSAL):
+        sq = np.ascontiguousarray(seqstart_q, dtype=np.int32)
+        sk = np.ascontiguousarray(seqstart_k if seqstart_k is not None else seqstart_q, dtype=np.int32)
+        nseq = len(sq) - 1
+        assert len(sk) == len(sq)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    rc = _load().oracle_attention(B, Mq, Mkv, H, K, Kv, _dp(q), _dp(k), _dp(v), int(mask), nseq,
+                                  sq.ctypes.data_as(ip) if sq is not None else None,
+                                  sk.ctypes.data_as(ip) if sk is not None else None,
+                                  float(scale), _dp(out), _dp(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_attention rejected its arguments (code {rc})")
+    return out, lse
+
+
+def merge(out_chunks, lse_chunks):
+    """Exact LSE-weighted merge of S chunks.
+
+    out_chunks [S,B,M,H,Kv] (or a list of [B,M,H,Kv]), lse_chunks [S,B,H,M]
+    -> (out [B,M,H,Kv], lse [B,H,M]).
+    """
+    oc = np.ascontiguousarray(np.stack(out_chunks) if isinstance(out_chunks, (list, tuple)) else out_chunks,
+                              dtype=np.float64)
+    lc = np.ascontiguousarray(np.stack(lse_chunks) if isinstance(lse_chunks, (list, tuple)) else lse_chunks,
+                              dtype=np.float64)
+    S, B, M, H, Kv = oc.shape
+    assert lc.shape == (S, B, H, M)
+    out = np.empty((B, M, H, Kv), dtype=np.float64)
+    lse = np.empty((B, H, M), dtype=np.float64)
+    rc = _load().oracle_merge(S, B, M, H, Kv, _dp(oc), _dp(lc), _dp(out), _dp(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_merge rejected its arguments (code {rc})")
+    return out, lse
+
+
+def partial(q, k, v, j0: int, j1: int, mask: int = MASK_NONE, scale=None):
+    """Attention over the key shard [j0, j1) alone (the shard is its own key sequence)."""
+    return attention(q, k[:, j0:j1], v[:, j0:j1], mask=mask,
+                     scale=(1.0 / math.sqrt(q.shape[3])) if scale is None else scale)
+
+
+def chunk_bounds(Mkv: int, S: int):
+    """Equal contiguous chunks: chunk s covers [s*c, min(Mkv, (s+1)*c)) with c = ceil(Mkv/S)."""
+    c = -(-Mkv // S)
+    return [(min(Mkv, s * c), min(Mkv, (s + 1) * c)) for s in range(S)]

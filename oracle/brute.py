@@ -1,0 +1,60 @@
+"""Dense numpy fp64 attention with a materialised mask bias -- TEST INFRASTRUCTURE.
+
+An independent second reading of the same definition as ``oracle.c``, written
+the way the pages describe a reference check: build the full [Mq, Mkv] bias of
+zeros and -inf ("Attention - Biases & masks", AttentionBias.materialize), add it
+to the scaled scores, take the softmax over keys and multiply by V
+("Attention - Core fMHA", memory_efficient_attention).  The LSE is the log of
+the plain sum of exponentials, with no maximum subtracted, so it is only meant
+for the small, moderate-valued inputs of the tests.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+MASK_NONE, MASK_CAUSAL, MASK_BLOCKDIAG, MASK_BLOCKDIAG_CAUSAL = 0, 1, 2, 3
+
+
+def materialize(mask: int, Mq: int, Mkv: int, seqstart_q=None, seqstart_k=None) -> np.ndarray:
+    """Dense additive bias [Mq, Mkv]: 0 where the key is visible, -inf elsewhere."""
+    bias = np.full((Mq, Mkv), -np.inf)
+    if mask == MASK_NONE:
+        bias[:] = 0.0
+    elif mask == MASK_CAUSAL:
+        for i in range(Mq):
+            bias[i, : min(Mkv, i + 1)] = 0.0
+    else:
+        sq = list(seqstart_q)
+        sk = list(seqstart_k if seqstart_k is not None else seqstart_q)
+        for s in range(len(sq) - 1):
+            for i in range(sq[s], sq[s + 1]):
+                if mask == MASK_BLOCKDIAG:
+                    bias[i, sk[s]: sk[s + 1]] = 0.0
+                else:
+                    hi = min(sk[s + 1], sk[s] + (i - sq[s]) + 1)
+                    bias[i, sk[s]: hi] = 0.0
+    return bias
+
+
+def attention(q, k, v, mask: int = MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Mq, H, K = q.shape
+    Mkv, Kv = k.shape[1], v.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    bias = materialize(mask, Mq, Mkv, seqstart_q, seqstart_k)
+    out = np.zeros((B, Mq, H, Kv))
+    lse = np.full((B, H, Mq), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, :, h, :] @ k[b, :, h, :].T) + bias
+            e = np.exp(s)
+            tot = e.sum(axis=1)
+            nz = tot > 0
+            out[b, nz, h, :] = (e[nz] / tot[nz, None]) @ v[b, :, h, :]
+            lse[b, h, nz] = np.log(tot[nz])
+    return out, lse

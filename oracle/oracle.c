@@ -1,0 +1,192 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.  A plain, slow fp64 CPU attention
+ * used to check the HIP kernels.  Only the tests, the smoke check and the
+ * bench's CPU-baseline leg may load it; the product path never does.  It
+ * shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes (one definition, written out):
+ *
+ *   MSLK - complete kernel reference for LLM agents, "Attention - Core fMHA",
+ *   memory_efficient_attention: scaled Q K^T, the mask as an additive 0/-inf
+ *   bias, softmax over keys, product with V; the output keeps the query layout
+ *   with the last axis taken from V.
+ *   memory_efficient_attention_forward_requires_grad: also returns the
+ *   per-row log-sum-exp (LSE).
+ *   memory_efficient_attention_partial: the same over one disjoint K/V shard.
+ *   merge_attentions: the exact LSE-weighted combination of shard results.
+ *
+ * For batch b, head h, query row i and allowed key set A(i):
+ *   s_ij   = scale * sum_d q[b,i,h,d] k[b,j,h,d]          (j in A(i))
+ *   m_i    = max_j s_ij
+ *   l_i    = sum_j exp(s_ij - m_i)
+ *   out_i  = sum_j exp(s_ij - m_i) / l_i * v[b,j,h,:]
+ *   lse_i  = m_i + ln l_i                                   (natural log)
+ * An empty A(i) gives out_i = 0 and lse_i = -inf.
+ *
+ * Mask kinds (A(i)):
+ *   0 none:            all keys                      (no attn_bias)
+ *   1 causal top-left: j <= i                        ("Attention - Biases &
+ *                      masks", LowerTriangularMask: zeros on and below the
+ *                      diagonal, -inf above)
+ *   2 block-diagonal:  the keys of the query's own packed sequence
+ *                      (BlockDiagonalMask)
+ *   3 block-diagonal causal: same sequence and j - ks <= i - qs, the
+ *                      top-left causal mask inside every block
+ *                      (BlockDiagonalCausalMask)
+ *
+ * Merge of S chunks (merge_attentions; "MSLK Kernel Library -- Complete
+ * Reference", Quick start, "Exact softmax merge"):
+ *   M* = max_c lse_c,  L = M* + ln sum_c exp(lse_c - M*),
+ *   out = sum_c exp(lse_c - L) out_c.   All chunks at -inf give 0 and -inf.
+ *
+ * Layouts (all contiguous, fp64):
+ *   q [B,Mq,H,K], k [B,Mkv,H,K], v [B,Mkv,H,Kv], out [B,Mq,H,Kv], lse [B,H,Mq].
+ *   Packed sequences: B = 1, seqstart_q/seqstart_k are prefix sums [nseq+1].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_MASK_NONE = 0, OR_MASK_CAUSAL = 1, OR_MASK_BLOCKDIAG = 2, OR_MASK_BLOCKDIAG_CAUSAL = 3 };
+
+/* Sequence index of packed row `r` given prefix sums `ss` of `nseq` sequences, or -1. */
+static int seq_of_row(int64_t r, const int32_t *ss, int nseq) {
+    for (int s = 0; s < nseq; ++s)
+        if (r >= ss[s] && r < ss[s + 1]) return s;
+    return -1;
+}
+
+/* 1 when key j is in A(i). */
+static int key_allowed(int mask, int64_t i, int64_t j, const int32_t *sq, const int32_t *sk,
+                       int nseq) {
+    switch (mask) {
+    case OR_MASK_NONE:
+        return 1;
+    case OR_MASK_CAUSAL:
+        return j <= i;
+    case OR_MASK_BLOCKDIAG:
+    case OR_MASK_BLOCKDIAG_CAUSAL: {
+        int s = seq_of_row(i, sq, nseq);
+        if (s < 0) return 0;
+        if (j < sk[s] || j >= sk[s + 1]) return 0;
+        if (mask == OR_MASK_BLOCKDIAG) return 1;
+        return (j - sk[s]) <= (i - sq[s]);
+    }
+    default:
+        return 0;
+    }
+}
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Returns 0 on success, nonzero on a bad argument. */
+int oracle_attention(int64_t B, int64_t Mq, int64_t Mkv, int64_t H, int64_t K, int64_t Kv,
+                     const double *q, const double *k, const double *v, int mask, int nseq,
+                     const int32_t *seqstart_q, const int32_t *seqstart_k, double scale,
+                     double *out, double *lse) {
+    if (B < 0 || Mq < 0 || Mkv < 0 || H < 0 || K < 1 || Kv < 1) return 1;
+    if (mask < 0 || mask > 3) return 1;
+    if (mask >= OR_MASK_BLOCKDIAG && (B != 1 || nseq < 1 || !seqstart_q || !seqstart_k)) return 1;
+
+    const int64_t rows = B * H * Mq;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Mkv > 0 ? Mkv : 1));
+        char *ok = (char *)malloc((size_t)(Mkv > 0 ? Mkv : 1));
+        if (!s || !ok) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < rows; ++r) {
+                const int64_t b = r / (H * Mq);
+                const int64_t h = (r / Mq) % H;
+                const int64_t i = r % Mq;
+                const double *qi = q + ((b * Mq + i) * H + h) * K;
+                double *oi = out + ((b * Mq + i) * H + h) * Kv;
+
+                /* scores over the allowed keys, and their maximum */
+                double m = -INFINITY;
+                int64_t n_allowed = 0;
+                for (int64_t j = 0; j < Mkv; ++j) {
+                    ok[j] = (char)key_allowed(mask, i, j, seqstart_q, seqstart_k, nseq);
+                    if (!ok[j]) continue;
+                    const double *kj = k + ((b * Mkv + j) * H + h) * K;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < K; ++d) dot += qi[d] * kj[d];
+                    s[j] = scale * dot;
+                    if (s[j] > m) m = s[j];
+                    ++n_allowed;
+                }
+                for (int64_t d = 0; d < Kv; ++d) oi[d] = 0.0;
+                if (n_allowed == 0) {
+                    lse[(b * H + h) * Mq + i] = -INFINITY;
+                    continue;
+                }
+                /* normaliser */
+                double l = 0.0;
+                for (int64_t j = 0; j < Mkv; ++j)
+                    if (ok[j]) l += exp(s[j] - m);
+                /* weighted sum of value rows */
+                for (int64_t j = 0; j < Mkv; ++j) {
+                    if (!ok[j]) continue;
+                    const double p = exp(s[j] - m) / l;
+                    const double *vj = v + ((b * Mkv + j) * H + h) * Kv;
+                    for (int64_t d = 0; d < Kv; ++d) oi[d] += p * vj[d];
+                }
+                lse[(b * H + h) * Mq + i] = m + log(l);
+            }
+        }
+        free(s);
+        free(ok);
+    }
+    return err;
+}
+
+/* out_chunks [S,B,M,H,Kv], lse_chunks [S,B,H,M] -> out [B,M,H,Kv], lse [B,H,M]. */
+int oracle_merge(int64_t S, int64_t B, int64_t M, int64_t H, int64_t Kv, const double *out_chunks,
+                 const double *lse_chunks, double *out, double *lse) {
+    if (S < 1 || B < 0 || M < 0 || H < 0 || Kv < 1) return 1;
+    const int64_t rows = B * M * H;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t b = r / (M * H);
+        const int64_t i = (r / H) % M;
+        const int64_t h = r % H;
+        const int64_t lse_off = (b * H + h) * M + i;
+        double *o = out + r * Kv;
+        for (int64_t d = 0; d < Kv; ++d) o[d] = 0.0;
+
+        double mstar = -INFINITY;
+        for (int64_t c = 0; c < S; ++c) {
+            const double x = lse_chunks[c * B * H * M + lse_off];
+            if (x > mstar) mstar = x;
+        }
+        if (mstar == -INFINITY) {
+            lse[lse_off] = -INFINITY;
+            continue;
+        }
+        double sum = 0.0;
+        for (int64_t c = 0; c < S; ++c) sum += exp(lse_chunks[c * B * H * M + lse_off] - mstar);
+        const double L = mstar + log(sum);
+        for (int64_t c = 0; c < S; ++c) {
+            const double w = exp(lse_chunks[c * B * H * M + lse_off] - L);
+            const double *oc = out_chunks + c * B * M * H * Kv + r * Kv;
+            for (int64_t d = 0; d < Kv; ++d) o[d] += w * oc[d];
+        }
+        lse[lse_off] = L;
+    }
+    return 0;
+}
