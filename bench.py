@@ -1,0 +1,213 @@
+"""Benchmark of the fused attention forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows prefill,decode,varlen,merge,fp32] [--no-cpu]
+
+A step is one attn_fwd call on the causal bf16 prefill workload B=2, M=2048,
+H=32, K=Kv=128 (the pages' Quick-start shape), inputs resident in HBM.  The
+headline value is its throughput in TFLOP/s, counting 4*B*H*M*M*K flops halved
+for the causal mask.  The other rows of the path are timed after it and
+reported under "rows": split-KV decode (B=16, Mkv=32768, H=32, 64 chunks;
+GB/s of K+V), the packed GQA causal prefill (8 sequences, lengths U[256, 4096]),
+the 2- and 8-way partial+merge of Mq=128/Mkv=1024/H=16, and the fp32 tiny case.
+Every figure is timed with HIP events on the stream the kernels run on.  The
+CPU baseline is the fp64 oracle on the host cores over the whole prefill
+workload.  One JSON line is printed at the end.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--rows", default="prefill,decode,varlen,merge,fp32")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return p.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def timed(fn, steps, warmup, torch):
+    """Average ms per call over `steps` calls after `warmup`, HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; bench.py --gpus N with N > 1 is not supported"}))
+        sys.exit(2)
+
+    import torch
+
+    from transformer_attention_02_amd import attn as A
+    from transformer_attention_02_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    rows = set(args.rows.split(","))
+
+    def up(x, dtype="bf16"):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+
+    result = {
+        "metric": "fMHA fwd TFLOP/s (% bf16 MFMA peak); split-KV decode HBM GB/s (% peak)",
+        "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16 by round-to-nearest-even)",
+        "config": {"workload": "causal bf16 attention forward B=2 M=2048 H=32 K=Kv=128 (attn_fwd, top-left causal)",
+                   "batch": 2, "seq_len": 2048, "heads": 32, "head_dim": 128, "mask": "causal"},
+        "rows": {},
+    }
+
+    # ------------------------------------------------------------ headline: causal prefill
+    shp = (2, 2048, 32, 128)
+    qh, kh, vh = synth.qkv(2, shp, shp, shp, "bf16")
+    q, k, v = up(qh), up(kh), up(vh)
+    out = torch.empty_like(q)
+    lse = torch.empty((2, 32, 2048), dtype=torch.float32, device="cuda")
+    flops = 4.0 * 2 * 32 * 2048 * 2048 * 128 / 2
+    ms = timed(lambda: A.attn_fwd(q, k, v, mask=A.MASK_CAUSAL, out=out, lse=lse), args.steps, args.warmup, torch)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"prefill causal bf16 [2,2048,32,128]: {ms * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
+    result["value"] = round(tflops, 2)
+    result["ms_per_step"] = round(ms, 5)
+    result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                          "kernel": "fwd_bf16_kernel<128,4,false>", "flops_per_launch": flops}
+
+    # ------------------------------------------------------------ CPU baseline: the oracle on the same workload
+    if not args.no_cpu:
+        import oracle
+
+        q64, k64, v64 = (synth.to_f64(x, "bf16") for x in (qh, kh, vh))
+        t0 = time.perf_counter()
+        oracle.attention(q64, k64, v64, mask=oracle.MASK_CAUSAL)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.threads(),
+                                  "kind": "oracle", "seconds": round(dt, 3),
+                                  "sample": "the whole causal [2,2048,32,128] workload (all 64 heads), fp64"}
+        log(f"cpu oracle: {dt:.2f} s on {oracle.threads()} threads")
+        del q64, k64, v64
+    del q, k, v, out, lse
+
+    # ------------------------------------------------------------ split-KV decode
+    if "decode" in rows:
+        B, Mkv, H, D, S = 16, 32768, 32, 128, 64
+        log("generating decode inputs ...")
+        qd = up(synth.normal(4, synth.TAG_Q, (B, 1, H, D), "bf16"))
+        kd = up(synth.normal(4, synth.TAG_K, (B, Mkv, H, D), "bf16"))
+        vd = up(synth.normal(4, synth.TAG_V, (B, Mkv, H, D), "bf16"))
+        ws = torch.empty(A.attn_decode_workspace_bytes(B, H, D, S), dtype=torch.uint8, device="cuda")
+        od = torch.empty_like(qd)
+        ld = torch.empty((B, H, 1), dtype=torch.float32, device="cuda")
+        ms_d = timed(lambda: A.attn_decode_splitkv(qd, kd, vd, S, workspace=ws, out=od, lse=ld), 20, 3, torch)
+        kv_bytes = 2.0 * B * Mkv * H * D * 2
+        gbs = kv_bytes / (ms_d * 1e-3) / 1e9
+        log(f"decode split-KV S=64: {ms_d * 1e3:.1f} us/call, {gbs:.0f} GB/s")
+        result["rows"]["decode_splitkv"] = {
+            "workload": "B=16 Mq=1 Mkv=32768 H=32 K=Kv=128 bf16, 64 chunks of 512 (decode kernel + merge kernel)",
+            "ms_per_call": round(ms_d, 5), "value": round(gbs, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_call": kv_bytes,
+                         "note": "algorithmic bytes = K+V once; time covers both launches"}}
+        del qd, kd, vd, ws, od, ld
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ packed GQA causal prefill
+    if "varlen" in rows:
+        lens = synth.varlen_lengths(5, 8, 256, 4096)
+        ss = synth.seqstarts(lens)
+        M = int(ss[-1])
+        qv = up(synth.normal(5, synth.TAG_Q, (1, M, 8, 4, 128), "bf16"))
+        kv = up(synth.normal(5, synth.TAG_K, (1, M, 8, 1, 128), "bf16")).expand(1, M, 8, 4, 128)
+        vv = up(synth.normal(5, synth.TAG_V, (1, M, 8, 1, 128), "bf16")).expand(1, M, 8, 4, 128)
+        sst = torch.from_numpy(ss).to("cuda")
+        ov = torch.empty_like(qv)
+        lv = torch.empty((1, 32, M), dtype=torch.float32, device="cuda")
+        mx = int(lens.max())
+        ms_v = timed(lambda: A.attn_fwd(qv, kv, vv, mask=A.MASK_BLOCKDIAG_CAUSAL, seqstart_q=sst, max_seqlen_q=mx,
+                                        out=ov, lse=lv), 20, 3, torch)
+        fl = 4.0 * 32 * 128 * float(np.sum(lens.astype(np.float64) ** 2)) / 2
+        tf = fl / (ms_v * 1e-3) / 1e12
+        log(f"varlen GQA causal M={M}: {ms_v * 1e3:.1f} us/call, {tf:.1f} TFLOP/s")
+        result["rows"]["varlen_gqa_causal"] = {
+            "workload": f"8 packed sequences {list(map(int, lens))} (M_total={M}), block-diagonal causal, "
+                        "H=32 as 8 KV groups x 4, K=Kv=128 bf16",
+            "ms_per_call": round(ms_v, 5), "value": round(tf, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl}}
+        del qv, kv, vv, ov, lv
+
+    # ------------------------------------------------------------ partial + merge
+    if "merge" in rows:
+        qh3, kh3, vh3 = synth.qkv(3, (1, 128, 16, 128), (1, 1024, 16, 128), (1, 1024, 16, 128), "bf16")
+        q3, k3, v3 = up(qh3), up(kh3), up(vh3)
+        entry = {"workload": "Mq=128 Mkv=1024 H=16 K=Kv=128 bf16; S partials (fp32) + merge vs one attn_fwd"}
+        ms_f = timed(lambda: A.attn_fwd(q3, k3, v3), 100, 5, torch)
+        entry["unsplit_ms"] = round(ms_f, 5)
+        for S in (2, 8):
+            c = 1024 // S
+            po = torch.empty((S, 1, 128, 16, 128), dtype=torch.float32, device="cuda")
+            pl = torch.empty((S, 1, 16, 128), dtype=torch.float32, device="cuda")
+            mo = torch.empty((1, 128, 16, 128), dtype=torch.bfloat16, device="cuda")
+
+            def split_merge():
+                for s in range(S):
+                    A.attn_partial(q3, k3[:, s * c:(s + 1) * c], v3[:, s * c:(s + 1) * c], out=po[s], lse=pl[s])
+                A.attn_merge(po, pl, out=mo)
+
+            ms_s = timed(split_merge, 100, 5, torch)
+            ms_m = timed(lambda: A.attn_merge(po, pl, out=mo), 100, 5, torch)
+            mbytes = S * (128 * 16 * 128 * 4 + 16 * 128 * 4) + 128 * 16 * 128 * 2 + 16 * 128 * 4
+            entry[f"S{S}"] = {"partials_plus_merge_ms": round(ms_s, 5), "merge_ms": round(ms_m, 5),
+                              "merge_GBps": round(mbytes / (ms_m * 1e-3) / 1e9, 1)}
+            log(f"partial+merge S={S}: {ms_s * 1e3:.1f} us (merge {ms_m * 1e3:.1f} us)")
+        result["rows"]["partial_merge"] = entry
+
+    # ------------------------------------------------------------ fp32 tiny
+    if "fp32" in rows:
+        qh1, kh1, vh1 = synth.qkv(1, (1, 128, 2, 64), (1, 128, 2, 64), (1, 128, 2, 64), "f32")
+        q1, k1, v1 = up(qh1, "f32"), up(kh1, "f32"), up(vh1, "f32")
+        ms_1 = timed(lambda: A.attn_fwd(q1, k1, v1, scale=0.125), 100, 5, torch)
+        fl1 = 4.0 * 2 * 128 * 128 * 64
+        result["rows"]["fp32_tiny"] = {"workload": "fp32 B=1 M=128 H=2 K=Kv=64, no mask", "ms_per_call": round(ms_1, 5),
+                                       "value": round(fl1 / (ms_1 * 1e-3) / 1e12, 4), "unit": "TFLOP/s",
+                                       "note": "latency-bound"}
+        log(f"fp32 tiny: {ms_1 * 1e3:.1f} us/call")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

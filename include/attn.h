@@ -1,0 +1,157 @@
+/*
+ * attn.h -- C ABI of a fused attention forward library for AMD MI355X (gfx950).
+ *
+ * Operations follow the MSLK pages ("MSLK - complete kernel reference for LLM
+ * agents", section "Attention - Core fMHA", and "MSLK Kernel Library --
+ * Complete Reference", sections Quick start, Conventions and Glossary):
+ *
+ *   attn_fwd            memory_efficient_attention_forward_requires_grad:
+ *                       scaled Q K^T, an optional mask, softmax, product with
+ *                       V, without materialising the attention matrix; returns
+ *                       the output and the per-row log-sum-exp (LSE).
+ *                       With lse == NULL it is memory_efficient_attention_forward.
+ *   attn_partial        memory_efficient_attention_partial: the same over one
+ *                       disjoint K/V shard, output kept in fp32 for merging.
+ *   attn_merge          merge_attentions: exact LSE-weighted combination of
+ *                       shard results (not an average).
+ *   attn_decode_splitkv split-KV decode (Glossary, "split-K / split-KV"): one
+ *                       query row per (batch, head); the keys are cut into
+ *                       equal contiguous chunks, each chunk's partial result
+ *                       goes to a caller-owned fp32 workspace, and a second
+ *                       pass merges them.
+ *
+ * Conventions shared by every call
+ *   - Tensors are described by attn_tensor: a device pointer, a dtype, 4 dims
+ *     [B, M, H, D] or 5 dims [B, M, G, H, D] (grouped heads, flattened to
+ *     H_total = G*H with flat head g*H + h), and strides in ELEMENTS.  The last
+ *     dim must have stride 1 and the row start of every (b, m, head) must be
+ *     16-byte aligned; other strides are free, including 0 (an explicitly
+ *     expanded K/V head axis for GQA/MQA, "Conventions" and "Sharp edges:
+ *     GQA broadcasting is explicit").
+ *   - out has q's layout with the last dim replaced by V's head dim.
+ *   - lse is fp32, contiguous [B, H_total, Mq]; packed sequences use
+ *     [1, H_total, M_total] indexed by packed row.  LSE is the natural log
+ *     of sum_j exp(s_ij) over the visible keys of the SCALED scores s.
+ *   - A row with no visible key gets out = 0 and lse = -inf.
+ *   - scale: a NaN means 1/sqrt(K).
+ *   - Ownership: the caller allocates and owns every buffer (inputs, outputs,
+ *     lse, workspace, sequence offsets).  The library allocates nothing and
+ *     never synchronises; calls enqueue on `stream` and return.  Results are
+ *     ready once the stream has drained.
+ *   - Errors: a non-zero status means nothing was launched and nothing was
+ *     written; attn_last_error() gives the reason (thread-local).
+ *     ATTN_ERR_INVALID_ARGUMENT: inconsistent shapes, dtypes, strides,
+ *       alignment, null pointers, bad counts.
+ *     ATTN_ERR_UNSUPPORTED: a valid request this build has no kernel for.
+ *     ATTN_ERR_WORKSPACE_TOO_SMALL: workspace_bytes below the requirement.
+ *     ATTN_ERR_LAUNCH: the HIP runtime refused the launch.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *attn_stream_t; /* a hipStream_t; NULL = the null stream */
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARGUMENT = 1,
+    ATTN_ERR_UNSUPPORTED = 2,
+    ATTN_ERR_WORKSPACE_TOO_SMALL = 3,
+    ATTN_ERR_LAUNCH = 4
+} attn_status;
+
+typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
+
+/* Masks ("Attention - Biases & masks" on the kernel reference page). */
+typedef enum {
+    ATTN_MASK_NONE = 0,
+    ATTN_MASK_CAUSAL = 1,            /* LowerTriangularMask: top-left aligned, key j visible iff j <= i */
+    ATTN_MASK_BLOCKDIAG = 2,         /* BlockDiagonalMask: a query row sees its own packed sequence */
+    ATTN_MASK_BLOCKDIAG_CAUSAL = 3   /* BlockDiagonalCausalMask: top-left causal inside every block */
+} attn_mask_kind;
+
+typedef struct {
+    void *data;        /* device pointer */
+    int32_t dtype;     /* attn_dtype */
+    int32_t ndim;      /* 4: [B, M, H, D]; 5: [B, M, G, H, D] */
+    int64_t shape[5];
+    int64_t stride[5]; /* in elements */
+} attn_tensor;
+
+/* Packed variable-length sequences ("Glossary: varlen"; BlockDiagonalMask.from_seqlens).
+ * Required for the two block-diagonal masks, ignored otherwise.  B must be 1.
+ * seqstart_q/seqstart_k are DEVICE int32 prefix sums [nseq + 1]: 0, L0, L0+L1,
+ * ..., M_total.  seqstart_k NULL means seqstart_k = seqstart_q.
+ * max_seqlen_q must be >= every query length.  The offsets live on the device
+ * and are not read by the host: offsets that are not monotone, do not start at
+ * 0, or exceed max_seqlen_q give unspecified output values but never an
+ * out-of-bounds access (the kernels clamp them to [0, M]). */
+typedef struct {
+    const int32_t *seqstart_q;
+    const int32_t *seqstart_k;
+    int32_t nseq;
+    int32_t max_seqlen_q;
+} attn_varlen;
+
+/* memory_efficient_attention_forward_requires_grad ("Attention - Core fMHA").
+ *   q [B, Mq, (G,) H, K], k [B, Mkv, (G,) H, K], v [B, Mkv, (G,) H, Kv]; one dtype.
+ *   out [B, Mq, (G,) H, Kv] with q's dtype.
+ *   lse fp32 [B, H_total, Mq] device buffer, or NULL to skip it.
+ *   varlen: NULL unless mask is one of the block-diagonal kinds.
+ * Built kernels: bf16 with K == Kv in {64, 128} (MFMA); fp32 with K, Kv <= 128. */
+attn_status attn_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                     int32_t mask, const attn_varlen *varlen, float scale,
+                     const attn_tensor *out, float *lse, attn_stream_t stream);
+
+/* memory_efficient_attention_partial ("Attention - Core fMHA").
+ * Same inputs as attn_fwd; k/v are the shard (the mask treats the shard as the
+ * whole key sequence).  out may be fp32 (the default for merging) or q's dtype.
+ * lse is required.  An empty shard (Mkv = 0) gives out = 0, lse = -inf. */
+attn_status attn_partial(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                         int32_t mask, const attn_varlen *varlen, float scale,
+                         const attn_tensor *out, float *lse, attn_stream_t stream);
+
+/* merge_attentions ("Attention - Core fMHA"; "Exact softmax merge" in Quick start).
+ *   n_chunks in [1, ATTN_MAX_CHUNKS]; out_chunks: n_chunks host descriptors
+ *   [B, M, (G,) H, Kv] (fp32 or bf16, all with the same dtype and strides, e.g.
+ *   views of one stacked tensor); lse_chunks: n_chunks device pointers, each
+ *   fp32 contiguous [B, H_total, M].
+ *   out [B, M, (G,) H, Kv] fp32 or bf16; lse_out fp32 [B, H_total, M] or NULL
+ *   (merge_attentions' write_lse=False).
+ *   L = M* + ln sum_c exp(lse_c - M*),  out = sum_c exp(lse_c - L) out_c;
+ *   chunks at -inf weigh 0; if every chunk is -inf, out = 0 and lse = -inf. */
+#define ATTN_MAX_CHUNKS 128
+attn_status attn_merge(int32_t n_chunks, const attn_tensor *out_chunks,
+                       const float *const *lse_chunks, const attn_tensor *out, float *lse_out,
+                       attn_stream_t stream);
+
+/* Bytes of device workspace attn_decode_splitkv needs (fp32 partial outputs
+ * [num_splits, B, H_total, Kv] and LSEs [num_splits, B, H_total], 256-byte aligned). */
+size_t attn_decode_workspace_bytes(int64_t B, int64_t H_total, int64_t Kv, int32_t num_splits);
+
+/* Split-KV decode (Glossary "split-K / split-KV"; ck_splitk.FwOp_S* fixes the split count).
+ *   q [B, 1, (G,) H, K], k/v [B, Mkv, (G,) H, K]; bf16 or fp32, K == Kv in {64, 128}.
+ *   num_splits in [1, ATTN_MAX_CHUNKS]: chunk s covers keys
+ *   [s*c, min(Mkv, (s+1)*c)) with c = ceil(Mkv / num_splits); a chunk may be empty.
+ *   workspace: device, 256-byte aligned, >= attn_decode_workspace_bytes(...).
+ *   out [B, 1, (G,) H, Kv] with q's dtype; lse fp32 [B, H_total, 1] or NULL.
+ *   Two launches on `stream`: per-chunk partials, then the merge. */
+attn_status attn_decode_splitkv(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                int32_t num_splits, float scale, void *workspace,
+                                size_t workspace_bytes, const attn_tensor *out, float *lse,
+                                attn_stream_t stream);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

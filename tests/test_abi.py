@@ -1,0 +1,184 @@
+"""Host-only tests of the C ABI: the library loads, exports what include/attn.h
+declares, and rejects invalid requests before any launch (no GPU needed: the
+descriptors point at fake addresses that the validation never dereferences)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from transformer_attention_02_amd import attn as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(attn_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["attn_fwd", "attn_partial", "attn_merge", "attn_decode_workspace_bytes",
+                                           "attn_decode_splitkv", "attn_last_error"])
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(A._lib, name)
+
+
+def tensor(shape, dtype=A.ATTN_DTYPE_BF16, stride=None, data=FAKE):
+    d = A.AttnTensor()
+    d.data = data
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if stride is None:
+        stride, acc = [], 1
+        for s in reversed(shape):
+            stride.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, stride)):
+        d.shape[i] = s
+        d.stride[i] = st
+    return d
+
+
+def fwd(q, k, v, o, mask=0, varlen=None, scale=float("nan"), lse=FAKE, fn=None):
+    fn = fn or A._lib.attn_fwd
+    return fn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), mask, varlen, scale, ctypes.byref(o),
+              ctypes.c_void_p(lse) if lse else None, None)
+
+
+def std4(M=128, D=128, dt=A.ATTN_DTYPE_BF16):
+    return tensor([2, M, 4, D], dt)
+
+
+@pytest.mark.parametrize("case,status,needle", [
+    ("stride", A.ATTN_ERR_INVALID_ARGUMENT, "stride 1"),
+    ("dtype_mix", A.ATTN_ERR_INVALID_ARGUMENT, "one dtype"),
+    ("k_dim", A.ATTN_ERR_INVALID_ARGUMENT, "head dims differ"),
+    ("kv_rows", A.ATTN_ERR_INVALID_ARGUMENT, "key counts"),
+    ("out_dim", A.ATTN_ERR_INVALID_ARGUMENT, "out head dim"),
+    ("batch", A.ATTN_ERR_INVALID_ARGUMENT, "batch"),
+    ("mask", A.ATTN_ERR_INVALID_ARGUMENT, "mask kind"),
+    ("align", A.ATTN_ERR_INVALID_ARGUMENT, "16-byte"),
+    ("ndim", A.ATTN_ERR_INVALID_ARGUMENT, "ndim"),
+    ("hd96", A.ATTN_ERR_UNSUPPORTED, "K == Kv"),
+    ("f32_big", A.ATTN_ERR_UNSUPPORTED, "<= 128"),
+    ("varlen_missing", A.ATTN_ERR_INVALID_ARGUMENT, "varlen"),
+    ("out_dtype", A.ATTN_ERR_INVALID_ARGUMENT, "q's dtype"),
+    ("scale_inf", A.ATTN_ERR_INVALID_ARGUMENT, "scale"),
+    ("null", A.ATTN_ERR_INVALID_ARGUMENT, "NULL"),
+])
+def test_fwd_rejects(case, status, needle):
+    q, k, v, o = std4(), std4(256), std4(256), std4()
+    kw = {}
+    if case == "stride":
+        q = tensor([2, 128, 4, 128], stride=[65536, 512, 128, 2])
+    elif case == "dtype_mix":
+        k = std4(256, dt=A.ATTN_DTYPE_F32)
+    elif case == "k_dim":
+        k = std4(256, 64)
+    elif case == "kv_rows":
+        v = std4(255)
+    elif case == "out_dim":
+        o = std4(128, 64)
+    elif case == "batch":
+        k = tensor([3, 256, 4, 128])
+    elif case == "mask":
+        kw["mask"] = 7
+    elif case == "align":
+        q = tensor([2, 128, 4, 128], data=FAKE + 8)
+    elif case == "ndim":
+        q = tensor([2, 128, 128])
+    elif case == "hd96":
+        q, k, v, o = std4(128, 96), std4(256, 96), std4(256, 96), std4(128, 96)
+    elif case == "f32_big":
+        f = A.ATTN_DTYPE_F32
+        q, k, v, o = std4(128, 256, f), std4(256, 256, f), std4(256, 256, f), std4(128, 256, f)
+    elif case == "varlen_missing":
+        kw["mask"] = A.MASK_BLOCKDIAG_CAUSAL
+    elif case == "out_dtype":
+        o = std4(dt=A.ATTN_DTYPE_F32)
+    elif case == "scale_inf":
+        kw["scale"] = float("inf")
+    elif case == "null":
+        q = tensor([2, 128, 4, 128], data=0)
+    rc = fwd(q, k, v, o, **kw)
+    assert rc == status
+    assert needle in A.attn_last_error()
+
+
+def test_partial_allows_fp32_out_but_needs_lse():
+    q, k, v = std4(), std4(256), std4(256)
+    o32 = std4(dt=A.ATTN_DTYPE_F32)
+    rc = fwd(q, k, v, o32, lse=0, fn=A._lib.attn_partial)
+    assert rc == A.ATTN_ERR_INVALID_ARGUMENT and "lse is required" in A.attn_last_error()
+
+
+def test_varlen_checks():
+    q, k, v, o = (tensor([1, 300, 4, 128]) for _ in range(4))
+    vl = A.AttnVarlen()
+    vl.seqstart_q = FAKE
+    vl.nseq = 0
+    vl.max_seqlen_q = 100
+    assert fwd(q, k, v, o, mask=A.MASK_BLOCKDIAG, varlen=ctypes.byref(vl)) == A.ATTN_ERR_INVALID_ARGUMENT
+    vl.nseq = 3
+    vl.max_seqlen_q = 301
+    assert fwd(q, k, v, o, mask=A.MASK_BLOCKDIAG, varlen=ctypes.byref(vl)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert "max_seqlen_q" in A.attn_last_error()
+    q2, k2, v2, o2 = (tensor([2, 300, 4, 128]) for _ in range(4))
+    vl.max_seqlen_q = 100
+    assert fwd(q2, k2, v2, o2, mask=A.MASK_BLOCKDIAG, varlen=ctypes.byref(vl)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert "B == 1" in A.attn_last_error()
+
+
+def test_empty_problem_is_a_no_op():
+    q, k, v, o = tensor([0, 128, 4, 128]), tensor([0, 256, 4, 128]), tensor([0, 256, 4, 128]), tensor([0, 128, 4, 128])
+    assert fwd(q, k, v, o) == A.ATTN_OK
+
+
+def merge_call(n, chunks, lses, out, lse_out=FAKE):
+    arr = (A.AttnTensor * max(1, n))(*chunks)
+    lp = (ctypes.c_void_p * max(1, n))(*lses)
+    return A._lib.attn_merge(n, arr, lp, ctypes.byref(out), ctypes.c_void_p(lse_out), None)
+
+
+def test_merge_rejects():
+    c = tensor([1, 128, 16, 128], A.ATTN_DTYPE_F32)
+    o = tensor([1, 128, 16, 128])
+    assert merge_call(0, [], [], o) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert "at least one chunk" in A.attn_last_error()
+    assert merge_call(129, [c] * 129, [FAKE] * 129, o) == A.ATTN_ERR_UNSUPPORTED
+    c2 = tensor([1, 64, 16, 128], A.ATTN_DTYPE_F32)
+    assert merge_call(2, [c, c2], [FAKE, FAKE], o) == A.ATTN_ERR_INVALID_ARGUMENT
+    c3 = tensor([1, 128, 16, 128], A.ATTN_DTYPE_F32, stride=[16 * 128 * 256, 16 * 256, 256, 1])
+    assert merge_call(2, [c, c3], [FAKE, FAKE], o) == A.ATTN_ERR_UNSUPPORTED
+    assert merge_call(2, [c, c], [FAKE, 0], o) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert "lse_chunks[1]" in A.attn_last_error()
+    assert merge_call(1, [c], [FAKE], tensor([1, 128, 8, 128])) == A.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_decode_workspace_and_rejects():
+    B, H, D, S = 16, 32, 128, 64
+    need = A.attn_decode_workspace_bytes(B, H, D, S)
+    assert need == (S * B * H * D * 4 + 255) // 256 * 256 + (S * B * H * 4 + 255) // 256 * 256
+    assert A.attn_decode_workspace_bytes(B, H, D, 0) == 0
+    q, o = tensor([B, 1, H, D]), tensor([B, 1, H, D])
+    k, v = tensor([B, 1024, H, D]), tensor([B, 1024, H, D])
+
+    def call(num_splits=S, ws=FAKE * 256, wsb=need, qq=q):
+        return A._lib.attn_decode_splitkv(ctypes.byref(qq), ctypes.byref(k), ctypes.byref(v), num_splits,
+                                          float("nan"), ctypes.c_void_p(ws), wsb, ctypes.byref(o), None, None)
+    assert call(wsb=need - 1) == A.ATTN_ERR_WORKSPACE_TOO_SMALL
+    assert call(num_splits=0) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(num_splits=129) == A.ATTN_ERR_UNSUPPORTED
+    assert call(ws=FAKE * 256 + 16) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(qq=tensor([B, 2, H, D])) == A.ATTN_ERR_INVALID_ARGUMENT

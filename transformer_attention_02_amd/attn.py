@@ -1,0 +1,194 @@
+"""ctypes binding of libattn.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls (include/attn.h) and
+turns torch tensors into the C descriptors (pointer, dtype, shape, strides in
+elements) plus the current HIP stream.  Torch is used for device memory and
+streams only; every step of the computation runs in the library's HIP kernels.
+Outputs that the caller does not pass are allocated with ``torch.empty``.
+
+Importing this module loads the library and raises ImportError if it is
+missing: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE_TOO_SMALL, ATTN_ERR_LAUNCH = range(5)
+ATTN_DTYPE_F32, ATTN_DTYPE_BF16 = 0, 1
+MASK_NONE, MASK_CAUSAL, MASK_BLOCKDIAG, MASK_BLOCKDIAG_CAUSAL = 0, 1, 2, 3
+MAX_CHUNKS = 128
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m transformer_attention_02_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class AttnTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 5), ("stride", ctypes.c_int64 * 5)]
+
+
+class AttnVarlen(ctypes.Structure):
+    _fields_ = [("seqstart_q", ctypes.c_void_p), ("seqstart_k", ctypes.c_void_p), ("nseq", ctypes.c_int32),
+                ("max_seqlen_q", ctypes.c_int32)]
+
+
+_P = ctypes.POINTER
+_T = _P(AttnTensor)
+_lib.attn_fwd.argtypes = [_T, _T, _T, ctypes.c_int32, _P(AttnVarlen), ctypes.c_float, _T, ctypes.c_void_p,
+                          ctypes.c_void_p]
+_lib.attn_fwd.restype = ctypes.c_int
+_lib.attn_partial.argtypes = _lib.attn_fwd.argtypes
+_lib.attn_partial.restype = ctypes.c_int
+_lib.attn_merge.argtypes = [ctypes.c_int32, _T, _P(ctypes.c_void_p), _T, ctypes.c_void_p, ctypes.c_void_p]
+_lib.attn_merge.restype = ctypes.c_int
+_lib.attn_decode_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+_lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.attn_decode_splitkv.argtypes = [_T, _T, _T, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+                                     _T, ctypes.c_void_p, ctypes.c_void_p]
+_lib.attn_decode_splitkv.restype = ctypes.c_int
+_lib.attn_last_error.argtypes = []
+_lib.attn_last_error.restype = ctypes.c_char_p
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return ATTN_DTYPE_F32
+    if dt == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def desc(t: torch.Tensor) -> AttnTensor:
+    """C descriptor of a 4-D [B,M,H,D] or 5-D [B,M,G,H,D] tensor (strides in elements)."""
+    d = AttnTensor()
+    d.data = t.data_ptr() if t.numel() else None
+    d.dtype = _dtype_code(t.dtype)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int) -> None:
+    if rc != ATTN_OK:
+        raise AttnError(rc, attn_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _scale(scale) -> float:
+    return float("nan") if scale is None else float(scale)
+
+
+def _htot(t: torch.Tensor) -> int:
+    return t.shape[2] * t.shape[3] if t.dim() == 5 else t.shape[2]
+
+
+def _varlen(seqstart_q, seqstart_k, max_seqlen_q):
+    if seqstart_q is None:
+        return None, None
+    vl = AttnVarlen()
+    vl.seqstart_q = seqstart_q.data_ptr()
+    vl.seqstart_k = seqstart_k.data_ptr() if seqstart_k is not None else None
+    vl.nseq = seqstart_q.numel() - 1
+    vl.max_seqlen_q = int(max_seqlen_q)
+    return ctypes.byref(vl), vl
+
+
+def attn_last_error() -> str:
+    return _lib.attn_last_error().decode()
+
+
+def _forward(fn, q, k, v, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, out, lse, stream, out_dtype):
+    if out is None:
+        out = torch.empty((*q.shape[:-1], v.shape[-1]), dtype=out_dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty((q.shape[0], _htot(q), q.shape[1]), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    vref, _keep = _varlen(seqstart_q, seqstart_k, max_seqlen_q)
+    dq, dk, dv, do = desc(q), desc(k), desc(v), desc(out)
+    _check(fn(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(mask), vref, _scale(scale),
+              ctypes.byref(do), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def attn_fwd(q, k, v, mask=MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None, max_seqlen_q=None,
+             out=None, lse=True, stream=None):
+    """memory_efficient_attention_forward_requires_grad: returns (out, lse); lse=False skips the LSE."""
+    return _forward(_lib.attn_fwd, q, k, v, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, out, lse, stream,
+                    q.dtype)
+
+
+def attn_partial(q, k, v, mask=MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None, max_seqlen_q=None,
+                 out=None, lse=True, stream=None, out_dtype=torch.float32):
+    """memory_efficient_attention_partial over the shard (k, v): returns (out fp32 by default, lse)."""
+    return _forward(_lib.attn_partial, q, k, v, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, out, lse,
+                    stream, out_dtype)
+
+
+def attn_merge(out_chunks, lse_chunks, out=None, write_lse=True, out_dtype=None, stream=None):
+    """merge_attentions over a list of chunks (or a stacked [S, ...] tensor): returns (out, lse or None)."""
+    chunks = list(out_chunks.unbind(0)) if isinstance(out_chunks, torch.Tensor) else list(out_chunks)
+    lses = list(lse_chunks.unbind(0)) if isinstance(lse_chunks, torch.Tensor) else list(lse_chunks)
+    if len(chunks) != len(lses):
+        raise ValueError("out_chunks and lse_chunks differ in length")
+    n = len(chunks)
+    c0 = chunks[0] if n else None
+    if out is None and c0 is not None:
+        out = torch.empty(c0.shape, dtype=out_dtype or c0.dtype, device=c0.device)
+    lse = None
+    if write_lse and c0 is not None:
+        lse = torch.empty((c0.shape[0], _htot(c0), c0.shape[1]), dtype=torch.float32, device=c0.device)
+    descs = (AttnTensor * max(1, n))(*[desc(c) for c in chunks])
+    lptrs = (ctypes.c_void_p * max(1, n))(*[x.data_ptr() for x in lses])
+    _check(_lib.attn_merge(n, descs, lptrs, ctypes.byref(desc(out)) if out is not None else None, _ptr(lse),
+                           _stream(stream)))
+    return out, lse
+
+
+def attn_decode_workspace_bytes(B: int, H_total: int, Kv: int, num_splits: int) -> int:
+    return int(_lib.attn_decode_workspace_bytes(B, H_total, Kv, num_splits))
+
+
+def attn_decode_splitkv(q, k, v, num_splits, scale=None, workspace=None, out=None, lse=True, stream=None):
+    """Split-KV decode for q [B,1,(G,)H,K]: returns (out, lse or None)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty((q.shape[0], _htot(q), 1), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    need = attn_decode_workspace_bytes(q.shape[0], _htot(q), q.shape[-1], num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(_lib.attn_decode_splitkv(ctypes.byref(desc(q)), ctypes.byref(desc(k)), ctypes.byref(desc(v)),
+                                    int(num_splits), _scale(scale), _ptr(workspace), workspace.numel(),
+                                    ctypes.byref(desc(out)), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def default_scale(K: int) -> float:
+    return 1.0 / math.sqrt(K)

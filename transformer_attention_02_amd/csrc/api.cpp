@@ -1,0 +1,350 @@
+// C-ABI front end: validates descriptors on the host (integer checks only, no
+// device access, no allocation, no synchronisation), picks a kernel and launches
+// it on the caller's stream.  Any failure returns before a launch, with the
+// reason in a thread-local string (the pages' not_supported_reasons idea,
+// "Attention - Backend operator classes" in the MSLK kernel reference).
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+attn_status fail(attn_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+attn_status ok() {
+    g_err[0] = '\0';
+    return ATTN_OK;
+}
+
+size_t dtype_size(int dt) { return dt == ATTN_DTYPE_F32 ? 4 : 2; }
+
+// A tensor normalised to [B, M, Htot, D] with head addressing (sg, sh, Hin).
+struct View {
+    void *p;
+    int dtype;
+    int ndim;
+    int64_t B, M, G, H, D;
+    attn::Strides s;
+};
+
+attn_status make_view(const attn_tensor *t, const char *name, View *v) {
+    if (!t) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: descriptor is NULL", name);
+    if (t->dtype != ATTN_DTYPE_F32 && t->dtype != ATTN_DTYPE_BF16)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, t->dtype);
+    if (t->ndim != 4 && t->ndim != 5)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: ndim must be 4 [B,M,H,D] or 5 [B,M,G,H,D], got %d", name, t->ndim);
+    for (int i = 0; i < t->ndim; ++i) {
+        if (t->shape[i] < 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: negative shape[%d]", name, i);
+        if (t->shape[i] > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "%s: shape[%d] exceeds 2^31-1", name, i);
+        if (t->stride[i] < 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: negative stride[%d]", name, i);
+    }
+    const int last = t->ndim - 1;
+    if (t->stride[last] != 1)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: the last dimension must have stride 1 (got %lld)", name,
+                    (long long)t->stride[last]);
+    v->p = t->data;
+    v->dtype = t->dtype;
+    v->ndim = t->ndim;
+    v->B = t->shape[0];
+    v->M = t->shape[1];
+    if (t->ndim == 4) {
+        v->G = 1;
+        v->H = t->shape[2];
+        v->s = attn::Strides{t->stride[0], t->stride[1], 0, t->stride[2]};
+    } else {
+        v->G = t->shape[2];
+        v->H = t->shape[3];
+        v->s = attn::Strides{t->stride[0], t->stride[1], t->stride[2], t->stride[3]};
+    }
+    v->D = t->shape[last];
+    if (v->G * v->H > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "%s: too many heads", name);
+    const int64_t n = v->B * v->M * v->G * v->H * v->D;
+    if (n > 0) {
+        if (!v->p) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: data pointer is NULL", name);
+        // 16-byte aligned row starts: base pointer and every outer stride in bytes
+        const size_t es = dtype_size(v->dtype);
+        if (((uintptr_t)v->p) % 16 != 0)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: data pointer is not 16-byte aligned", name);
+        for (int i = 0; i < last; ++i)
+            if ((t->stride[i] * (int64_t)es) % 16 != 0)
+                return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: stride[%d]=%lld elements is not a multiple of 16 bytes",
+                            name, i, (long long)t->stride[i]);
+    }
+    return ATTN_OK;
+}
+
+int64_t htot(const View &v) { return v.G * v.H; }
+
+bool same_heads(const View &a, const View &b) { return a.ndim == b.ndim && a.G == b.G && a.H == b.H; }
+
+attn_status launch_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Shared validation and launch for attn_fwd / attn_partial.
+attn_status forward(const char *fn, bool partial, const attn_tensor *qt, const attn_tensor *kt,
+                    const attn_tensor *vt, int32_t mask, const attn_varlen *varlen, float scale,
+                    const attn_tensor *ot, float *lse, attn_stream_t stream) {
+    View q, k, v, o;
+    attn_status st;
+    if ((st = make_view(qt, "q", &q)) != ATTN_OK) return st;
+    if ((st = make_view(kt, "k", &k)) != ATTN_OK) return st;
+    if ((st = make_view(vt, "v", &v)) != ATTN_OK) return st;
+    if ((st = make_view(ot, "out", &o)) != ATTN_OK) return st;
+    if (k.dtype != q.dtype || v.dtype != q.dtype)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k and v must share one dtype", fn);
+    if (partial) {
+        if (o.dtype != ATTN_DTYPE_F32 && o.dtype != q.dtype)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out must be fp32 or q's dtype", fn);
+        if (!lse) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: lse is required", fn);
+    } else if (o.dtype != q.dtype) {
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out must have q's dtype", fn);
+    }
+    if (!same_heads(q, k) || !same_heads(q, v) || !same_heads(q, o))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out must have the same rank and head axes", fn);
+    if (k.B != q.B || v.B != q.B || o.B != q.B) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: batch sizes differ", fn);
+    if (v.M != k.M) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: k and v have different key counts", fn);
+    if (o.M != q.M) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out must have q's row count", fn);
+    if (k.D != q.D) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q and k head dims differ", fn);
+    if (o.D != v.D) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out head dim must equal v's", fn);
+    if (mask < ATTN_MASK_NONE || mask > ATTN_MASK_BLOCKDIAG_CAUSAL)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: unknown mask kind %d", fn, mask);
+    const bool packed = mask == ATTN_MASK_BLOCKDIAG || mask == ATTN_MASK_BLOCKDIAG_CAUSAL;
+    if (packed) {
+        if (!varlen) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block-diagonal masks need varlen", fn);
+        if (q.B != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: packed sequences need B == 1", fn);
+        if (varlen->nseq < 1 || !varlen->seqstart_q)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: varlen needs nseq >= 1 and seqstart_q", fn);
+        if (varlen->max_seqlen_q < 0 || varlen->max_seqlen_q > q.M)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: max_seqlen_q must be in [0, Mq]", fn);
+        if ((((uintptr_t)varlen->seqstart_q) % 4) || (((uintptr_t)varlen->seqstart_k) % 4))
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: seqstart arrays must be 4-byte aligned", fn);
+    }
+    if (!(std::isnan(scale) || std::isfinite(scale)))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: scale must be finite (or NaN for 1/sqrt(K))", fn);
+    if (lse && ((uintptr_t)lse) % 4) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
+    if (q.D < 1 || v.D < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: head dims must be >= 1", fn);
+
+    if (q.dtype == ATTN_DTYPE_BF16) {
+        if (!((q.D == 64 || q.D == 128) && v.D == q.D))
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: bf16 kernels need K == Kv in {64, 128} (got K=%lld, Kv=%lld)", fn,
+                        (long long)q.D, (long long)v.D);
+    } else {
+        if (q.D > 128 || v.D > 128)
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: fp32 kernel needs K, Kv <= 128 (got K=%lld, Kv=%lld)", fn,
+                        (long long)q.D, (long long)v.D);
+    }
+    if (q.B == 0 || q.M == 0 || htot(q) == 0) return ok();  // nothing to compute
+
+    attn::FwdArgs a;
+    a.q = q.p;
+    a.k = k.p;
+    a.v = v.p;
+    a.o = o.p;
+    a.lse = lse;
+    a.sq = q.s;
+    a.sk = k.s;
+    a.sv = v.s;
+    a.so = o.s;
+    a.B = (int)q.B;
+    a.Mq = (int)q.M;
+    a.Mkv = (int)k.M;
+    a.Htot = (int)htot(q);
+    a.Hin = (int)q.H;
+    a.K = (int)q.D;
+    a.Kv = (int)v.D;
+    const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)q.D) : (double)scale;
+    a.scale_log2 = (float)(sc * 1.4426950408889634);
+    a.mask = mask;
+    if (packed) {
+        a.seqstart_q = varlen->seqstart_q;
+        a.seqstart_k = varlen->seqstart_k;
+        a.nseq = varlen->nseq;
+        a.max_seqlen_q = varlen->max_seqlen_q;
+    } else {
+        a.seqstart_q = a.seqstart_k = nullptr;
+        a.nseq = 1;
+        a.max_seqlen_q = a.Mq;
+    }
+    hipError_t e;
+    if (q.dtype == ATTN_DTYPE_BF16)
+        e = attn::launch_fwd_bf16(a, o.dtype == ATTN_DTYPE_F32, (hipStream_t)stream);
+    else
+        e = attn::launch_fwd_f32(a, (hipStream_t)stream);
+    return launch_status(e, fn);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_last_error(void) { return g_err; }
+
+attn_status attn_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, int32_t mask,
+                     const attn_varlen *varlen, float scale, const attn_tensor *out, float *lse,
+                     attn_stream_t stream) {
+    return forward("attn_fwd", false, q, k, v, mask, varlen, scale, out, lse, stream);
+}
+
+attn_status attn_partial(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, int32_t mask,
+                         const attn_varlen *varlen, float scale, const attn_tensor *out, float *lse,
+                         attn_stream_t stream) {
+    return forward("attn_partial", true, q, k, v, mask, varlen, scale, out, lse, stream);
+}
+
+attn_status attn_merge(int32_t n_chunks, const attn_tensor *out_chunks, const float *const *lse_chunks,
+                       const attn_tensor *out, float *lse_out, attn_stream_t stream) {
+    const char *fn = "attn_merge";
+    if (n_chunks < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: need at least one chunk", fn);
+    if (n_chunks > ATTN_MAX_CHUNKS)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: at most %d chunks per call", fn, ATTN_MAX_CHUNKS);
+    if (!out_chunks || !lse_chunks) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: chunk arrays are NULL", fn);
+    View c0, o;
+    attn_status st;
+    if ((st = make_view(&out_chunks[0], "out_chunks[0]", &c0)) != ATTN_OK) return st;
+    if ((st = make_view(out, "out", &o)) != ATTN_OK) return st;
+    for (int i = 1; i < n_chunks; ++i) {
+        View ci;
+        char nm[32];
+        snprintf(nm, sizeof nm, "out_chunks[%d]", i);
+        if ((st = make_view(&out_chunks[i], nm, &ci)) != ATTN_OK) return st;
+        if (ci.dtype != c0.dtype || ci.ndim != c0.ndim || ci.B != c0.B || ci.M != c0.M || ci.G != c0.G ||
+            ci.H != c0.H || ci.D != c0.D)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: chunk %d differs from chunk 0 in dtype or shape", fn, i);
+        if (ci.s.b != c0.s.b || ci.s.m != c0.s.m || ci.s.g != c0.s.g || ci.s.h != c0.s.h)
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: chunk %d has different strides from chunk 0", fn, i);
+    }
+    if (!same_heads(o, c0) || o.B != c0.B || o.M != c0.M || o.D != c0.D)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out shape differs from the chunks'", fn);
+    const int64_t rows = c0.B * c0.M * htot(c0);
+    for (int i = 0; i < n_chunks; ++i)
+        if (rows > 0 && (!lse_chunks[i] || ((uintptr_t)lse_chunks[i]) % 4))
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: lse_chunks[%d] is NULL or misaligned", fn, i);
+    if (lse_out && ((uintptr_t)lse_out) % 4) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: lse_out misaligned", fn);
+    if (rows == 0 || c0.D == 0) return ok();
+
+    attn::MergeArgs a;
+    memset(&a, 0, sizeof a);
+    for (int i = 0; i < n_chunks; ++i) {
+        a.chunk[i] = out_chunks[i].data;
+        a.lse[i] = lse_chunks[i];
+    }
+    a.sc = c0.s;
+    a.o = o.p;
+    a.so = o.s;
+    a.lse_out = lse_out;
+    a.S = n_chunks;
+    a.B = (int)c0.B;
+    a.M = (int)c0.M;
+    a.Htot = (int)htot(c0);
+    a.Hin = (int)c0.H;
+    a.Kv = (int)c0.D;
+    a.chunk_f32 = c0.dtype == ATTN_DTYPE_F32;
+    a.out_f32 = o.dtype == ATTN_DTYPE_F32;
+    return launch_status(attn::launch_merge(a, (hipStream_t)stream), fn);
+}
+
+size_t attn_decode_workspace_bytes(int64_t B, int64_t H_total, int64_t Kv, int32_t num_splits) {
+    if (B < 0 || H_total < 0 || Kv < 0 || num_splits < 1) return 0;
+    const size_t rows = (size_t)num_splits * (size_t)B * (size_t)H_total;
+    return align256(rows * (size_t)Kv * 4) + align256(rows * 4);
+}
+
+attn_status attn_decode_splitkv(const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
+                                int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                                const attn_tensor *ot, float *lse, attn_stream_t stream) {
+    const char *fn = "attn_decode_splitkv";
+    View q, k, v, o;
+    attn_status st;
+    if ((st = make_view(qt, "q", &q)) != ATTN_OK) return st;
+    if ((st = make_view(kt, "k", &k)) != ATTN_OK) return st;
+    if ((st = make_view(vt, "v", &v)) != ATTN_OK) return st;
+    if ((st = make_view(ot, "out", &o)) != ATTN_OK) return st;
+    if (k.dtype != q.dtype || v.dtype != q.dtype || o.dtype != q.dtype)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out must share one dtype", fn);
+    if (!same_heads(q, k) || !same_heads(q, v) || !same_heads(q, o))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out must have the same rank and head axes", fn);
+    if (k.B != q.B || v.B != q.B || o.B != q.B) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: batch sizes differ", fn);
+    if (q.M != 1 || o.M != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: decode takes one query row (M == 1)", fn);
+    if (v.M != k.M) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: k and v have different key counts", fn);
+    if (k.D != q.D || v.D != q.D || o.D != q.D)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out head dims must match", fn);
+    if (!(q.D == 64 || q.D == 128)) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim must be 64 or 128", fn);
+    if (num_splits < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: num_splits must be >= 1", fn);
+    if (num_splits > ATTN_MAX_CHUNKS)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: num_splits must be <= %d", fn, ATTN_MAX_CHUNKS);
+    if (!(std::isnan(scale) || std::isfinite(scale)))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: scale must be finite (or NaN for 1/sqrt(K))", fn);
+    if (lse && ((uintptr_t)lse) % 4) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
+    const size_t need = attn_decode_workspace_bytes(q.B, htot(q), q.D, num_splits);
+    if (q.B == 0 || htot(q) == 0) return ok();
+    if (!workspace || ((uintptr_t)workspace) % 256)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: workspace is NULL or not 256-byte aligned", fn);
+    if (workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu", fn, need, workspace_bytes);
+    const int64_t rows = (int64_t)num_splits * q.B * htot(q);
+    if (rows > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "%s: too many (split, batch, head) rows", fn);
+
+    attn::DecodeArgs d;
+    d.q = q.p;
+    d.k = k.p;
+    d.v = v.p;
+    d.sq = q.s;
+    d.sk = k.s;
+    d.sv = v.s;
+    d.B = (int)q.B;
+    d.Mkv = (int)k.M;
+    d.Htot = (int)htot(q);
+    d.Hin = (int)q.H;
+    d.D = (int)q.D;
+    d.S = num_splits;
+    d.chunk = (int)((k.M + num_splits - 1) / num_splits);
+    const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)q.D) : (double)scale;
+    d.scale_log2 = (float)(sc * 1.4426950408889634);
+    d.ws_o = (float *)workspace;
+    d.ws_lse = (float *)((char *)workspace + align256((size_t)rows * q.D * 4));
+    hipError_t e = attn::launch_decode_partials(d, q.dtype == ATTN_DTYPE_F32, (hipStream_t)stream);
+    if (e != hipSuccess) return launch_status(e, fn);
+
+    attn::MergeArgs m;
+    memset(&m, 0, sizeof m);
+    const int64_t per = q.B * htot(q);
+    for (int s = 0; s < num_splits; ++s) {
+        m.chunk[s] = d.ws_o + (size_t)s * per * q.D;
+        m.lse[s] = d.ws_lse + (size_t)s * per;
+    }
+    // workspace chunk layout [B, 1, Htot, D] contiguous, addressed like [B, M, G, H, D]
+    m.sc = attn::Strides{htot(q) * q.D, htot(q) * q.D, q.H * q.D, q.D};
+    m.o = o.p;
+    m.so = o.s;
+    m.lse_out = lse;
+    m.S = num_splits;
+    m.B = (int)q.B;
+    m.M = 1;
+    m.Htot = (int)htot(q);
+    m.Hin = (int)q.H;
+    m.Kv = (int)q.D;
+    m.chunk_f32 = 1;
+    m.out_f32 = o.dtype == ATTN_DTYPE_F32;
+    return launch_status(attn::launch_merge(m, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

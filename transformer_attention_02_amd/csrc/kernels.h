@@ -1,0 +1,68 @@
+// Internal interface between the C-ABI front end (api.cpp) and the HIP kernels.
+// Every struct is passed to a kernel by value.  Strides are in elements; a head
+// index hf in [0, Htot) is split as (hf / Hin, hf % Hin) and addressed through
+// (sg, sh), which covers [B,M,H,D] (sg unused) and [B,M,G,H,D] with any strides,
+// including 0 for an explicitly expanded K/V head axis.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct Strides {
+    int64_t b, m, g, h;
+};
+
+__host__ __device__ inline int64_t head_offset(const Strides &s, int hf, int Hin) {
+    return (int64_t)(hf / Hin) * s.g + (int64_t)(hf % Hin) * s.h;
+}
+
+enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskBlockDiag = 2, kMaskBlockDiagCausal = 3 };
+
+// Forward / partial attention over one key range per (batch, head).
+struct FwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;          // [B, Htot, Mlse] or null
+    Strides sq, sk, sv, so;
+    int B, Mq, Mkv, Htot, Hin, K, Kv;
+    float scale_log2;    // scale * log2(e): scores are kept in base-2 units
+    int mask;
+    const int32_t *seqstart_q, *seqstart_k;  // device prefix sums, packed sequences only
+    int nseq;            // 1 when not packed
+    int max_seqlen_q;    // rows covered per sequence (Mq when not packed)
+};
+
+// Split-KV decode partials: one query row per (batch, head), keys cut in S chunks.
+struct DecodeArgs {
+    const void *q, *k, *v;
+    Strides sq, sk, sv;
+    int B, Mkv, Htot, Hin, D;
+    int S, chunk;        // chunk = ceil(Mkv / S)
+    float scale_log2;
+    float *ws_o;         // [S, B, Htot, D] fp32, normalised per chunk
+    float *ws_lse;       // [S, B, Htot] fp32, natural log
+};
+
+constexpr int kMaxChunks = 128;
+
+// Exact merge of S chunk results that share one layout.
+struct MergeArgs {
+    const void *chunk[kMaxChunks];
+    const float *lse[kMaxChunks];  // each [B, Htot, M]
+    Strides sc;                    // chunk strides
+    void *o;
+    Strides so;
+    float *lse_out;                // [B, Htot, M] or null
+    int S, B, M, Htot, Hin, Kv;
+    int chunk_f32, out_f32;
+};
+
+// Launchers return a hipError_t from the launch.
+hipError_t launch_fwd_bf16(const FwdArgs &a, bool out_f32, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_decode_partials(const DecodeArgs &a, bool f32, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
+
+}  // namespace attn
