@@ -36,7 +36,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--rows", default="prefill,decode,varlen,merge,fp32")
+    p.add_argument("--rows", default="decode,varlen,merge,fp32",
+                   help="rows timed after the headline prefill: decode,varlen,merge,fp32,copy or none; "
+                        "copy is a plain 1 GiB device copy used to calibrate the HBM byte counters")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return p.parse_args()
 
@@ -194,6 +196,18 @@ def main():
                               "merge_GBps": round(mbytes / (ms_m * 1e-3) / 1e9, 1)}
             log(f"partial+merge S={S}: {ms_s * 1e3:.1f} us (merge {ms_m * 1e3:.1f} us)")
         result["rows"]["partial_merge"] = entry
+
+    # ------------------------------------------------------------ calibration copy for the HBM counters
+    if "copy" in rows:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        ms_c = timed(lambda: dst.copy_(src), 10, 2, torch)
+        result["rows"]["copy_calibration"] = {"workload": "torch copy_ of 1 GiB (reads 1 GiB, writes 1 GiB)",
+                                              "ms_per_call": round(ms_c, 5),
+                                              "value": round(2 * n / (ms_c * 1e-3) / 1e9, 1), "unit": "GB/s"}
+        log(f"copy 1 GiB: {ms_c * 1e3:.1f} us ({2 * n / (ms_c * 1e-3) / 1e9:.0f} GB/s)")
+        del src, dst
 
     # ------------------------------------------------------------ fp32 tiny
     if "fp32" in rows:
