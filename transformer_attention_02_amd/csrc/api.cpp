@@ -145,6 +145,11 @@ attn_status forward(const char *fn, bool partial, const attn_tensor *qt, const a
         if (!((q.D == 64 || q.D == 128) && v.D == q.D))
             return fail(ATTN_ERR_UNSUPPORTED, "%s: bf16 kernels need K == Kv in {64, 128} (got K=%lld, Kv=%lld)", fn,
                         (long long)q.D, (long long)v.D);
+        // key tiles are fetched through buffer descriptors whose range ends at the last valid key row
+        if (k.M > 1 && (k.s.m < k.D || v.s.m < v.D))
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: bf16 kernels need key/value row strides >= the head dim", fn);
+        if ((k.s.m * 2 * 64 + k.D * 2) >= (int64_t)1 << 31 || (v.s.m * 2 * 64 + v.D * 2) >= (int64_t)1 << 31)
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: key/value row stride too large for 32-bit tile offsets", fn);
     } else {
         if (q.D > 128 || v.D > 128)
             return fail(ATTN_ERR_UNSUPPORTED, "%s: fp32 kernel needs K, Kv <= 128 (got K=%lld, Kv=%lld)", fn,
@@ -171,6 +176,7 @@ attn_status forward(const char *fn, bool partial, const attn_tensor *qt, const a
     a.Kv = (int)v.D;
     const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)q.D) : (double)scale;
     a.scale_log2 = (float)(sc * 1.4426950408889634);
+    if (std::fabs(a.scale_log2) < 1e-30f) a.scale_log2 = std::copysign(1e-30f, a.scale_log2);  // keeps -inf masking exact
     a.mask = mask;
     if (packed) {
         a.seqstart_q = varlen->seqstart_q;

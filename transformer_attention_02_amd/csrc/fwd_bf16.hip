@@ -8,68 +8,122 @@
 // LowerTriangularMask, BlockDiagonalMask, BlockDiagonalCausalMask).
 //
 // Work decomposition
-//   One workgroup = NW waves = 32*NW query rows of one (batch, head[, sequence]).
-//   Each wave owns 32 query rows.  Key/value tiles of 64 rows stream through
-//   LDS, double-buffered: while the waves run the matrix products on tile t,
-//   the global loads of tile t+1 are in flight in registers.
+//   One workgroup = 8 waves = 256 query rows of one (batch, head[, sequence]);
+//   each wave owns 32 rows, and two waves share each SIMD so that one wave's
+//   softmax arithmetic runs while the other's matrix products execute.
+//   Key/value tiles of 64 rows stream through a 3-stage LDS ring filled by
+//   buffer loads that write straight into LDS (no staging registers): while
+//   tile t is computed, tiles t+1 and t+2 are in flight.  Rows past the end of
+//   the keys fall outside the buffer descriptor's range and arrive as zeros.
 //
 // Matrix-core layout (v_mfma_f32_32x32x16_bf16, A 32x16, B 16x32, C 32x32)
-//   S^T = K Q^T: A = K rows from LDS (m = key, k = head dim), B = Q^T held in
-//   registers for the whole kernel (n = query row).  In the C layout lane l
-//   owns query row l%32 and 16 keys, so the softmax row statistics need only
-//   in-lane reductions plus one exchange with lane l^32.
-//   O^T += V^T P^T: B = P^T straight from the S^T registers.  For that to work
-//   without a register shuffle, K rows are stored in LDS under the permutation
-//   key_perm (swap of the middle two groups of 4 in every 16 rows): then lane
-//   half h holds 8 consecutive keys 16t+8h..16t+8h+7 of each 16-key step, which
-//   is exactly the B-operand k layout.  V is transposed while being written to
-//   LDS ([head dim][key]), so the A operand V^T is one 16-byte LDS read.
-//   Both LDS tiles use an XOR swizzle of the 16-byte chunk index by the row to
-//   spread the column reads over the banks.
+//   S^T = K Q^T: A = K rows from LDS (m = key, k = head dim, one 16-byte read),
+//   B = Q^T kept in registers (n = query row).  In the C layout lane l owns
+//   query row l%32 and 16 keys of each 32-key block, so the softmax row
+//   statistics are in-lane reductions plus one v_permlane32_swap.
+//   O^T += V^T P^T: B = P^T straight from the S^T registers; the C layout gives
+//   lane half h the keys {8a + 4h + 0..3}, which defines the k order of the
+//   product.  The A operand V^T is read from row-major V with two
+//   ds_read_b64_tr_b16 per 16-key step: inside each group of 16 lanes the
+//   instruction returns to lane i element i%4 of the 8-byte pieces addressed by
+//   lanes 4j + i/4, so lanes pointing at 4 consecutive key rows and 4-dim column
+//   pieces deliver each lane 4 keys of its own head-dim column.
+//   Both tiles are row-major with the 16-byte chunk index XOR-swizzled by the
+//   row, so that 16 lanes reading one chunk of 16 rows (K) or 32-byte pieces of
+//   4 rows (V) hit distinct LDS banks.
 //
-// Online softmax in base 2: x = s * scale * log2(e); running max m and sum l
-// per row; O is rescaled by 2^(m_old - m_new).  P is rounded to bf16 for the PV
-// product; l accumulates the fp32 values.  lse = (m + log2 l) * ln 2.
-// Causal tiles entirely above the diagonal are never visited; the element mask
-// is evaluated only on tiles that cross the diagonal or the end of the keys.
+// Online softmax in base 2: x = s * scale * log2(e).  Each row keeps a
+// reference maximum m and the sum l of 2^(x - m); the reference is raised
+// (and O, l rescaled) only when a new score exceeds it by more than 2^8, so
+// most tiles skip the rescale.  P is rounded to bf16 for the product with V;
+// l accumulates the fp32 values.  lse = (m + log2 l) * ln 2.
+// Causal tiles entirely above a wave's rows are skipped by that wave; the
+// element mask is applied only on tiles that cross the diagonal or the end of
+// the keys.
 #include "kernels.h"
 
 namespace attn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BN = 64;  // keys per tile
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int NW = 8;          // waves per workgroup
+constexpr int NT = NW * 64;    // threads per workgroup
+constexpr int BM = NW * 32;    // query rows per workgroup
+constexpr int BN = 64;         // keys per tile
+constexpr int STAGES = 3;      // LDS ring depth
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
-// Involution on [0, 16): swaps rows 4..7 with 8..11 (and leaves the other two groups).
-__device__ __forceinline__ int key_perm(int r) { return r ^ ((((r >> 2) ^ (r >> 3)) & 1) * 12); }
+// XOR applied to the 16-byte chunk index of LDS row `row`.
+template <int HD>
+__device__ __forceinline__ int swz(int row) {
+    if (HD == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+}
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <int HD, int NW, bool OUT_F32>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
-    constexpr int NT = NW * 64;
-    constexpr int BM = NW * 32;
-    constexpr int KCH = HD / 8;          // 16-byte chunks per K row
-    constexpr int KS = HD / 16;          // k-steps of S^T over the head dim
-    constexpr int MB = HD / 32;          // 32-row blocks of O^T over the head dim
-    constexpr int KI = BN * KCH / NT;    // K chunks loaded per thread per tile
-    constexpr int VI = (BN / 4) * KCH;   // V items (4 keys x 8 dims) per tile
-    constexpr int K_BYTES = BN * HD * 2;
-    constexpr int V_BYTES = HD * BN * 2;
-    constexpr int BUF_BYTES = K_BYTES + V_BYTES;
-    static_assert(KI >= 1 && KI * NT == BN * KCH, "K tile split");
-    static_assert(VI <= NT, "V tile split");
+// Raw buffer descriptor: byte range [base, base + num_records) is readable, the rest reads as 0.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, unsigned num_records) {
+    const unsigned long long p = (unsigned long long)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)p);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffff));
+    r[2] = __builtin_amdgcn_readfirstlane((int)num_records);
+    r[3] = 0x00020000;
+    return r;
+}
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF_BYTES];
+// 16 bytes per lane from (descriptor, voffset) straight into LDS at lds + 16 * lane.
+// Written as inline asm so that the compiler does not serialise later LDS reads
+// behind these loads: the kernel orders them itself with wait_barrier().
+__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds)
+                 : "memory");
+}
+
+// Wait until at most N of this thread's tile loads are outstanding, then a workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <int HD, bool OUT_F32>
+__global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
+    constexpr int ROWB = HD * 2;                 // bytes per tile row
+    constexpr int CPR = HD / 8;                  // 16-byte chunks per row
+    constexpr int TILE_BYTES = BN * ROWB;        // one K or V tile
+    constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V
+    constexpr int ROUNDS = TILE_BYTES / 16 / NT; // 16-byte loads per thread per tile per tensor
+    constexpr int KS = HD / 16;                  // k-steps of S^T
+    constexpr int MB = HD / 32;                  // 32-row blocks of O^T
+    static_assert(ROUNDS >= 1 && ROUNDS * NT * 16 == TILE_BYTES, "tile split");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * STAGE_BYTES];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+    const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     // ---- which (tile, sequence, batch*head) this workgroup owns; heaviest tiles first
     const int BH = a.B * a.Htot;
@@ -99,150 +153,149 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const __bf16 *qp = (const __bf16 *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin) + (int64_t)qs * a.sq.m;
     const __bf16 *kp = (const __bf16 *)a.k + (int64_t)b * a.sk.b + head_offset(a.sk, hf, a.Hin) + (int64_t)ks * a.sk.m;
     const __bf16 *vp = (const __bf16 *)a.v + (int64_t)b * a.sv.b + head_offset(a.sv, hf, a.Hin) + (int64_t)ks * a.sv.m;
+    const unsigned kstride = (unsigned)a.sk.m * 2u, vstride = (unsigned)a.sv.m * 2u;  // bytes per key row
+
+    // ---- async tile loads: global -> LDS, 16 bytes per lane, OOB rows read as zeros
+    // Slot p of a tile (16 bytes) holds row p / CPR, physical chunk p % CPR.
+    unsigned koff[ROUNDS], voff[ROUNDS];
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+        const int p = (r * NW + wave) * 64 + lane;
+        const int row = p / CPR, c = (p % CPR) ^ swz<HD>(row);
+        koff[r] = row * kstride + c * 16;
+        voff[r] = row * vstride + c * 16;
+    }
+    const unsigned smem_base = (unsigned)(unsigned long long)(unsigned char LDS_AS *)smem;
+    auto issue = [&](int t) {
+        const int kt0 = t * BN;
+        const int nvalid = min(BN, Lk - kt0);
+        const unsigned st = smem_base + (t % STAGES) * STAGE_BYTES;
+        const i32x4 kr = make_rsrc(kp + (int64_t)kt0 * a.sk.m, (nvalid - 1) * kstride + ROWB);
+        const i32x4 vr = make_rsrc(vp + (int64_t)kt0 * a.sv.m, (nvalid - 1) * vstride + ROWB);
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) dma16(kr, koff[r], st + (r * NW + wave) * 1024);
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) dma16(vr, voff[r], st + TILE_BYTES + (r * NW + wave) * 1024);
+    };
 
     // ---- Q^T fragments (B operand), resident for the whole kernel
     const int wrow0 = row0 + wave * 32;  // first local row of this wave
     const int qrow = wrow0 + l32;        // this lane's query row (local to the sequence)
+    float c = a.scale_log2;
+    const unsigned qflip = c < 0.f ? 0x80008000u : 0u;  // negative scale: negate q, keep c > 0
+    c = fabsf(c);
     bf16x8 qf[KS];
     if (qrow < Lq) {
-        const bf16x8 *src = (const bf16x8 *)(qp + (int64_t)qrow * a.sq.m + 8 * hh);
+        const u32x4 *src = (const u32x4 *)(qp + (int64_t)qrow * a.sq.m + 8 * hh);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qf[s] = src[2 * s];
+        for (int s = 0; s < KS; ++s) {
+            u32x4 w = src[2 * s];
+            w ^= u32x4{qflip, qflip, qflip, qflip};
+            qf[s] = __builtin_bit_cast(bf16x8, w);
+        }
     } else {
 #pragma unroll
         for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
     }
 
-    // ---- global -> register staging of one K/V tile
-    u32x4 kr[KI], vr[4];
-    auto gload = [&](int kt0) {
+    // ---- LDS read addresses (byte offsets inside a stage)
+    int kaddr[KS];  // K: row kb*32 + l32 (kb adds 32 rows), chunk 2s + hh
 #pragma unroll
-        for (int i = 0; i < KI; ++i) {
-            const int it = tid + i * NT, r = it / KCH, cc = it % KCH, j = kt0 + r;
-            kr[i] = (j < Lk) ? *(const u32x4 *)(kp + (int64_t)j * a.sk.m + cc * 8) : u32x4{0, 0, 0, 0};
-        }
-        if (tid < VI) {
-            const int a4 = tid / KCH, cc = tid % KCH;
+    for (int s = 0; s < KS; ++s) kaddr[s] = l32 * ROWB + (((2 * s + hh) ^ swz<HD>(l32)) << 4);
+    // V: lane i of 16-lane group G addresses key row 4*hh + i/4 (+ 8e + 16kt + 32kb) and
+    // head-dim columns mb*32 + 16*(G&1) + 4*(i%4) .. +3.
+    const int vrow = 4 * hh + ((lane & 15) >> 2);
+    const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    int vaddr[MB][2];  // [mb][e]; + (kb*32 + kt*16) rows keep the swizzle (rows shift by multiples of 16)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int j = kt0 + 4 * a4 + u;
-                vr[u] = (j < Lk) ? *(const u32x4 *)(vp + (int64_t)j * a.sv.m + cc * 8) : u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    // ---- register -> LDS: K permuted + swizzled, V transposed + swizzled
-    auto lstore = [&](int buf) {
-        unsigned char *kb = smem + buf * BUF_BYTES;
-        unsigned char *vb = kb + K_BYTES;
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < KI; ++i) {
-            const int it = tid + i * NT, r = it / KCH, cc = it % KCH;
-            const int rho = (r & ~15) | key_perm(r & 15);
-            *(u32x4 *)(kb + rho * (HD * 2) + ((cc ^ (rho & (KCH - 1))) << 4)) = kr[i];
+        for (int e = 0; e < 2; ++e) {
+            const int row = vrow + 8 * e, col = mb * 32 + vcol;
+            vaddr[mb][e] = TILE_BYTES + row * ROWB + ((((col >> 3) ^ swz<HD>(row))) << 4) + ((col & 4) << 1);
         }
-        if (tid < VI) {
-            const int a4 = tid / KCH, cc = tid % KCH;
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                const int w = d >> 1;
-                unsigned lo, hi;
-                if (d & 1) {
-                    lo = (vr[0][w] >> 16) | (vr[1][w] & 0xffff0000u);
-                    hi = (vr[2][w] >> 16) | (vr[3][w] & 0xffff0000u);
-                } else {
-                    lo = (vr[0][w] & 0xffffu) | (vr[1][w] << 16);
-                    hi = (vr[2][w] & 0xffffu) | (vr[3][w] << 16);
-                }
-                const int row = cc * 8 + d;
-                *(u32x2 *)(vb + row * (BN * 2) + ((((a4 >> 1) ^ (row & 7))) << 4) + ((a4 & 1) << 3)) = u32x2{lo, hi};
-            }
-        }
-    };
 
     f32x16 o[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) o[i] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
-    const float c = a.scale_log2;
+    float m_ref = -INFINITY, l_run = 0.f;
 
-    if (ntiles > 0) gload(0);
+    if (ntiles > 0) issue(0);
+    if (ntiles > 1) issue(1);
     for (int t = 0; t < ntiles; ++t) {
         const int kt0 = t * BN;
-        lstore(t & 1);
-        __syncthreads();
-        if (t + 1 < ntiles) gload(kt0 + BN);
+        // this thread's loads of tile t have landed once at most the next tile's are outstanding
+        if (t + 1 < ntiles) wait_barrier<2 * ROUNDS>();
+        else wait_barrier<0>();
+        if (t + 2 < ntiles) issue(t + 2);
 
-        const unsigned char *kb = smem + (t & 1) * BUF_BYTES;
-        const unsigned char *vb = kb + K_BYTES;
+        if (causal && kt0 > wrow0 + 31) continue;  // every key of the tile is above this wave's rows
+        const unsigned char LDS_AS *st = (const unsigned char LDS_AS *)smem + (t % STAGES) * STAGE_BYTES;
 
         // S^T = K Q^T for two 32-key blocks
-        f32x16 st[2] = {f32x16{}, f32x16{}};
+        f32x16 sa = f32x16{}, sb = f32x16{};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-                const int rho = kb2 * 32 + l32;
-                const int ch = (2 * s + hh) ^ (rho & (KCH - 1));
-                const bf16x8 af = *(const bf16x8 *)(kb + rho * (HD * 2) + (ch << 4));
-                st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], st[kb2], 0, 0, 0);
-            }
+            const bf16x8 k0 = *(const bf16x8 LDS_AS *)(st + kaddr[s]);
+            const bf16x8 k1 = *(const bf16x8 LDS_AS *)(st + kaddr[s] + 32 * ROWB);
+            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], sb, 0, 0, 0);
         }
 
-        // scale, mask, row max
-        const bool need_mask = (kt0 + BN > Lk) || (causal && kt0 + BN - 1 > wrow0);
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
+        // mask (only tiles crossing the diagonal or the end of the keys)
+        if ((kt0 + BN > Lk) || (causal && kt0 + BN - 1 > wrow0)) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float x = st[kb2][r] * c;
-                if (need_mask) {
-                    const int key = kt0 + kb2 * 32 + key_perm(8 * (r >> 2) + 4 * hh + (r & 3));
-                    if (key >= Lk || (causal && key > qrow)) x = -INFINITY;
-                }
-                st[kb2][r] = x;
-                mt = fmaxf(mt, x);
+                const int key = kt0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (key >= Lk || (causal && key > qrow)) sa[r] = -INFINITY;
+                if (key + 32 >= Lk || (causal && key + 32 > qrow)) sb[r] = -INFINITY;
             }
         }
-        mt = fmaxf(mt, xor32(mt));
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        // row maximum (raw scores; c > 0)
+        float mx = fmaxf(sa[0], sb[0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sa[r], sb[r]));
+        mx = pair_max(mx) * c;
+        // raise the reference only when the row max grows by more than the threshold
+        const bool up = mx > m_ref + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(up)) {
+            const float m_new = up ? mx : m_ref;
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            m_ref = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < MB; ++i) o[i] *= alpha;
+        }
+        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 
         float ls = 0.f;
-        bf16x8 pb[2][2];
+        bf16x8 pb[4];  // [kb*2 + kt]
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(st[kb2][r] - m_use);
-                ls += p;
-                pb[kb2][r >> 3][r & 7] = (__bf16)p;
-            }
+        for (int r = 0; r < 16; ++r) {
+            const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -m_use));
+            const float pbv = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r], c, -m_use));
+            ls += pa + pbv;
+            pb[r >> 3][r & 7] = (__bf16)pa;
+            pb[2 + (r >> 3)][r & 7] = (__bf16)pbv;
         }
-        l_run = l_run * alpha + ls;
-#pragma unroll
-        for (int i = 0; i < MB; ++i) o[i] *= alpha;
+        l_run += ls;
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T over 4 steps of 16 keys
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
+        for (int ksi = 0; ksi < 4; ++ksi) {
+            const int roff = ksi * 16 * ROWB;  // kb*32 + kt*16 rows
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    const int row = mb * 32 + l32;
-                    const int ch = (4 * kb2 + 2 * kt + hh) ^ (row & 7);
-                    const bf16x8 af = *(const bf16x8 *)(vb + row * (BN * 2) + (ch << 4));
-                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[kb2][kt], o[mb], 0, 0, 0);
-                }
+            for (int mb = 0; mb < MB; ++mb) {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS *)(st + vaddr[mb][0] + roff));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS *)(st + vaddr[mb][1] + roff));
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ksi], o[mb], 0, 0, 0);
             }
         }
     }
 
     // ---- normalise and store
-    const float l_tot = l_run + xor32(l_run);
+    const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < Lq) {
         unsigned char *op = (unsigned char *)a.o;
@@ -257,34 +310,32 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                 if (OUT_F32) {
                     *(f32x4 *)(op + (obase + d0) * 4) = f32x4{x0, x1, x2, x3};
                 } else {
-                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
                     *(bf16x4 *)(op + (obase + d0) * 2) = bf16x4{(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
                 }
             }
         }
         if (a.lse && hh == 0) {
             a.lse[((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow] =
-                l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+                l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
         }
     }
 }
 
-template <int HD, int NW, bool OUT_F32>
+template <int HD, bool OUT_F32>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
-    constexpr int BM = NW * 32;
     const int64_t tiles = (a.max_seqlen_q + BM - 1) / BM;
     const int64_t grid = tiles * a.nseq * (int64_t)a.B * a.Htot;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_bf16_kernel<HD, NW, OUT_F32>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<HD, OUT_F32>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool out_f32, hipStream_t stream) {
-    if (a.K == 128) return out_f32 ? launch<128, 4, true>(a, stream) : launch<128, 4, false>(a, stream);
-    if (a.K == 64) return out_f32 ? launch<64, 4, true>(a, stream) : launch<64, 4, false>(a, stream);
+    if (a.K == 128) return out_f32 ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+    if (a.K == 64) return out_f32 ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
     return hipErrorInvalidValue;
 }
 
