@@ -40,6 +40,8 @@
 // Causal tiles entirely above a wave's rows are skipped by that wave; the
 // element mask is applied only on tiles that cross the diagonal or the end of
 // the keys.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace attn {
@@ -113,13 +115,13 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     constexpr int ROWB = HD * 2;                 // bytes per tile row
     constexpr int CPR = HD / 8;                  // 16-byte chunks per row
     constexpr int TILE_BYTES = BN * ROWB;        // one K or V tile
-    constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V
+    constexpr int V_BASE = STAGES * TILE_BYTES;  // K tiles of all stages first, then the V tiles
     constexpr int ROUNDS = TILE_BYTES / 16 / NT; // 16-byte loads per thread per tile per tensor
     constexpr int KS = HD / 16;                  // k-steps of S^T
     constexpr int MB = HD / 32;                  // 32-row blocks of O^T
     static_assert(ROUNDS >= 1 && ROUNDS * NT * 16 == TILE_BYTES, "tile split");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGES * TILE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
@@ -169,13 +171,13 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     auto issue = [&](int t) {
         const int kt0 = t * BN;
         const int nvalid = min(BN, Lk - kt0);
-        const unsigned st = smem_base + (t % STAGES) * STAGE_BYTES;
+        const unsigned st = smem_base + (t % STAGES) * TILE_BYTES;
         const i32x4 kr = make_rsrc(kp + (int64_t)kt0 * a.sk.m, (nvalid - 1) * kstride + ROWB);
         const i32x4 vr = make_rsrc(vp + (int64_t)kt0 * a.sv.m, (nvalid - 1) * vstride + ROWB);
 #pragma unroll
         for (int r = 0; r < ROUNDS; ++r) dma16(kr, koff[r], st + (r * NW + wave) * 1024);
 #pragma unroll
-        for (int r = 0; r < ROUNDS; ++r) dma16(vr, voff[r], st + TILE_BYTES + (r * NW + wave) * 1024);
+        for (int r = 0; r < ROUNDS; ++r) dma16(vr, voff[r], st + V_BASE + (r * NW + wave) * 1024);
     };
 
     // ---- Q^T fragments (B operand), resident for the whole kernel
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int row = vrow + 8 * e, col = mb * 32 + vcol;
-            vaddr[mb][e] = TILE_BYTES + row * ROWB + ((((col >> 3) ^ swz<HD>(row))) << 4) + ((col & 4) << 1);
+            vaddr[mb][e] = V_BASE + row * ROWB + ((((col >> 3) ^ swz<HD>(row))) << 4) + ((col & 4) << 1);
         }
 
     f32x16 o[MB];
@@ -220,17 +222,19 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
     for (int i = 0; i < MB; ++i) o[i] = f32x16{};
     float m_ref = -INFINITY, l_run = 0.f;
 
-    if (ntiles > 0) issue(0);
-    if (ntiles > 1) issue(1);
-    for (int t = 0; t < ntiles; ++t) {
+    // One 64-key tile: S^T, mask (MASKED only), online softmax, O^T update.
+    // STAGE_C >= 0 names the LDS stage at compile time (t % STAGES == STAGE_C), so every LDS
+    // offset becomes an instruction immediate; -1 computes it at run time.
+    auto step = [&](int t, auto masked_tag, auto stage_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        constexpr int STAGE_C = decltype(stage_tag)::value;
+        const int soff = (STAGE_C >= 0 ? STAGE_C : t % STAGES) * TILE_BYTES;
         const int kt0 = t * BN;
-        // this thread's loads of tile t have landed once at most the next tile's are outstanding
         if (t + 1 < ntiles) wait_barrier<2 * ROUNDS>();
         else wait_barrier<0>();
         if (t + 2 < ntiles) issue(t + 2);
-
-        if (causal && kt0 > wrow0 + 31) continue;  // every key of the tile is above this wave's rows
-        const unsigned char LDS_AS *st = (const unsigned char LDS_AS *)smem + (t % STAGES) * STAGE_BYTES;
+        if (MASKED && causal && kt0 > wrow0 + 31) return;  // every key of the tile is above this wave's rows
+        const unsigned char LDS_AS *st = (const unsigned char LDS_AS *)smem + soff;
 
         // S^T = K Q^T for two 32-key blocks
         f32x16 sa = f32x16{}, sb = f32x16{};
@@ -241,9 +245,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
             sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], sa, 0, 0, 0);
             sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], sb, 0, 0, 0);
         }
-
-        // mask (only tiles crossing the diagonal or the end of the keys)
-        if ((kt0 + BN > Lk) || (causal && kt0 + BN - 1 > wrow0)) {
+        if (MASKED) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kt0 + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -251,11 +253,16 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
                 if (key + 32 >= Lk || (causal && key + 32 > qrow)) sb[r] = -INFINITY;
             }
         }
-        // row maximum (raw scores; c > 0)
-        float mx = fmaxf(sa[0], sb[0]);
+        // row maximum of the raw scores (c > 0), pairwise to keep dependency chains short
+        float m8[8];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sa[r], sb[r]));
-        mx = pair_max(mx) * c;
+        for (int i = 0; i < 8; ++i)
+            m8[i] = fmaxf(fmaxf(sa[2 * i], sa[2 * i + 1]), fmaxf(sb[2 * i], sb[2 * i + 1]));
+#pragma unroll
+        for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w; ++i) m8[i] = fmaxf(m8[i], m8[i + w]);
+        const float mx = pair_max(m8[0]) * c;
         // raise the reference only when the row max grows by more than the threshold
         const bool up = mx > m_ref + kRescaleThreshold;
         if (__builtin_amdgcn_ballot_w64(up)) {
@@ -264,21 +271,28 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
             m_ref = m_new;
             l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < MB; ++i) o[i] *= alpha;
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
         }
         const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 
-        float ls = 0.f;
-        bf16x8 pb[4];  // [kb*2 + kt]
+        float p[32];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -m_use));
-            const float pbv = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r], c, -m_use));
-            ls += pa + pbv;
-            pb[r >> 3][r & 7] = (__bf16)pa;
-            pb[2 + (r >> 3)][r & 7] = (__bf16)pbv;
+            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -m_use));
+            p[16 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r], c, -m_use));
         }
-        l_run += ls;
+        bf16x8 pb[4];  // [kb*2 + kt]: keys 32kb + 16kt + {8*(i/4) + 4*hh + i%4}
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pb[j][i] = (__bf16)p[8 * j + i];
+#pragma unroll
+        for (int w = 16; w >= 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w; ++i) p[i] += p[i + w];
+        l_run += p[0];
 
         // O^T += V^T P^T over 4 steps of 16 keys
 #pragma unroll
@@ -292,7 +306,25 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdArgs a) {
                 o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ksi], o[mb], 0, 0, 0);
             }
         }
+    };
+
+    // Tiles before `nfull` need no mask for any wave of the workgroup: keys all below the
+    // workgroup's first row (causal) and all inside the key range.
+    const int nfull = min(causal ? row0 / BN : ntiles, Lk / BN);
+    if (ntiles > 0) issue(0);
+    if (ntiles > 1) issue(1);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using SR = std::integral_constant<int, -1>;
+    int t = 0;
+    for (; t + STAGES <= nfull; t += STAGES) {
+        step(t, std::false_type{}, S0{});
+        step(t + 1, std::false_type{}, S1{});
+        step(t + 2, std::false_type{}, S2{});
     }
+    for (; t < nfull; ++t) step(t, std::false_type{}, SR{});
+    for (; t < ntiles; ++t) step(t, std::true_type{}, SR{});
 
     // ---- normalise and store
     const float l_tot = pair_sum(l_run);
