@@ -9,7 +9,8 @@ for the causal mask.  The other rows of the path are timed after it and
 reported under "rows": split-KV decode (B=16, Mkv=32768, H=32, 64 chunks;
 GB/s of K+V), the packed GQA causal prefill (8 sequences, lengths U[256, 4096]),
 the 2- and 8-way partial+merge of Mq=128/Mkv=1024/H=16, and the fp32 tiny case.
-Every figure is timed with HIP events on the stream the kernels run on.  The
+Every figure is timed with HIP events on the stream the kernels run on; each call is
+marshalled once (attn.prepare_*), so a timed call is one C-ABI call.  The
 CPU baseline is the fp64 oracle on the host cores over the whole prefill
 workload.  One JSON line is printed at the end.
 """
@@ -34,13 +35,69 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=300,
+                   help="untimed steps first; ~25 ms of back-to-back launches brings the clock to steady state")
     p.add_argument("--rows", default="decode,varlen,merge,fp32",
                    help="rows timed after the headline prefill: decode,varlen,merge,fp32,copy or none; "
                         "copy is a plain 1 GiB device copy used to calibrate the HBM byte counters")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--rocpd", metavar="DB", help="summarise a rocprofv3 results database (kernel durations and "
+                   "counters per kernel and grid) instead of running; no GPU needed")
     return p.parse_args()
+
+
+# ----------------------------------------------------------------------------------------- rocprofv3 summaries
+
+def rocpd_summary(db_path):
+    """Per-(kernel, grid) average durations and per-dispatch counter averages from a rocprofv3 database."""
+    import collections
+    import sqlite3
+
+    cur = sqlite3.connect(db_path).cursor()
+    tables = {r[0] for r in cur.execute("select name from sqlite_master")}
+    if "kernels" in tables:
+        g = collections.defaultdict(list)
+        for name, grid, wg, dur in cur.execute("select name, grid_x, workgroup_x, duration from kernels"):
+            g[(name, grid, wg)].append(dur)
+        print("| calls | avg us | median us | grid | workgroup | kernel |")
+        print("|---:|---:|---:|---:|---:|---|")
+        for (name, grid, wg), d in sorted(g.items(), key=lambda kv: -sum(kv[1])):
+            d = sorted(d)
+            print(f"| {len(d)} | {sum(d) / len(d) / 1e3:.2f} | {d[len(d) // 2] / 1e3:.2f} | {grid} | {wg} | {name} |")
+    if "counters_collection" in tables:
+        g = collections.defaultdict(list)
+        for name, grid, cn, val in cur.execute(
+                "select kernel_name, grid_size, counter_name, value from counters_collection"):
+            g[(name, grid, cn)].append(val)
+        if g:
+            print("\n| counter | dispatches | average per dispatch | grid | kernel |")
+            print("|---|---:|---:|---:|---|")
+            for (name, grid, cn), v in sorted(g.items()):
+                print(f"| {cn} | {len(v)} | {sum(v) / len(v):.1f} | {grid} | {name} |")
+
+
+def kernel_source_digest():
+    """sha256 of the prefill kernel sources; HBM byte counters recorded for another digest are stale."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("fwd_bf16.hip", "kernels.h"):
+        with open(os.path.join(ROOT, "transformer_attention_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(key):
+    """HBM bytes per launch from profiles/traffic.json when its kernel digest matches, else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get(key)
+    if not rec or rec.get("source_sha256") != kernel_source_digest():
+        return None
+    return rec["fetch_kib"] * rec["fetch_scale"] * 1024 + rec["write_kib"] * rec["write_scale"] * 1024
 
 
 def log(msg):
@@ -63,6 +120,9 @@ def timed(fn, steps, warmup, torch):
 
 def main():
     args = parse()
+    if args.rocpd:
+        rocpd_summary(args.rocpd)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; bench.py --gpus N with N > 1 is not supported"}))
@@ -99,14 +159,16 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty((2, 32, 2048), dtype=torch.float32, device="cuda")
     flops = 4.0 * 2 * 32 * 2048 * 2048 * 128 / 2
-    ms = timed(lambda: A.attn_fwd(q, k, v, mask=A.MASK_CAUSAL, out=out, lse=lse), args.steps, args.warmup, torch)
+    step = A.prepare_fwd(q, k, v, out, lse, mask=A.MASK_CAUSAL)
+    ms = timed(step, args.steps, args.warmup, torch)
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"prefill causal bf16 [2,2048,32,128]: {ms * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
     result["value"] = round(tflops, 2)
     result["ms_per_step"] = round(ms, 5)
     result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                          "kernel": "fwd_bf16_kernel<128,4,false>", "flops_per_launch": flops}
+                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                          "traffic": recorded_traffic("fwd_bf16 causal 2x2048x32x128"),
+                          "kernel": "fwd_bf16_kernel<128,8,3,false>", "flops_per_launch": flops}
 
     # ------------------------------------------------------------ CPU baseline: the oracle on the same workload
     if not args.no_cpu:
@@ -133,7 +195,7 @@ def main():
         ws = torch.empty(A.attn_decode_workspace_bytes(B, H, D, S), dtype=torch.uint8, device="cuda")
         od = torch.empty_like(qd)
         ld = torch.empty((B, H, 1), dtype=torch.float32, device="cuda")
-        ms_d = timed(lambda: A.attn_decode_splitkv(qd, kd, vd, S, workspace=ws, out=od, lse=ld), 20, 3, torch)
+        ms_d = timed(A.prepare_decode(qd, kd, vd, S, ws, od, ld), 20, 3, torch)
         kv_bytes = 2.0 * B * Mkv * H * D * 2
         gbs = kv_bytes / (ms_d * 1e-3) / 1e9
         log(f"decode split-KV S=64: {ms_d * 1e3:.1f} us/call, {gbs:.0f} GB/s")
@@ -158,8 +220,8 @@ def main():
         ov = torch.empty_like(qv)
         lv = torch.empty((1, 32, M), dtype=torch.float32, device="cuda")
         mx = int(lens.max())
-        ms_v = timed(lambda: A.attn_fwd(qv, kv, vv, mask=A.MASK_BLOCKDIAG_CAUSAL, seqstart_q=sst, max_seqlen_q=mx,
-                                        out=ov, lse=lv), 20, 3, torch)
+        ms_v = timed(A.prepare_fwd(qv, kv, vv, ov, lv, mask=A.MASK_BLOCKDIAG_CAUSAL, seqstart_q=sst, max_seqlen_q=mx),
+                     20, 3, torch)
         fl = 4.0 * 32 * 128 * float(np.sum(lens.astype(np.float64) ** 2)) / 2
         tf = fl / (ms_v * 1e-3) / 1e12
         log(f"varlen GQA causal M={M}: {ms_v * 1e3:.1f} us/call, {tf:.1f} TFLOP/s")
@@ -176,21 +238,28 @@ def main():
         qh3, kh3, vh3 = synth.qkv(3, (1, 128, 16, 128), (1, 1024, 16, 128), (1, 1024, 16, 128), "bf16")
         q3, k3, v3 = up(qh3), up(kh3), up(vh3)
         entry = {"workload": "Mq=128 Mkv=1024 H=16 K=Kv=128 bf16; S partials (fp32) + merge vs one attn_fwd"}
-        ms_f = timed(lambda: A.attn_fwd(q3, k3, v3), 100, 5, torch)
+        o3 = torch.empty_like(q3)
+        l3 = torch.empty((1, 16, 128), dtype=torch.float32, device="cuda")
+        ms_f = timed(A.prepare_fwd(q3, k3, v3, o3, l3), 100, 5, torch)
         entry["unsplit_ms"] = round(ms_f, 5)
         for S in (2, 8):
             c = 1024 // S
             po = torch.empty((S, 1, 128, 16, 128), dtype=torch.float32, device="cuda")
             pl = torch.empty((S, 1, 16, 128), dtype=torch.float32, device="cuda")
             mo = torch.empty((1, 128, 16, 128), dtype=torch.bfloat16, device="cuda")
+            ml = torch.empty((1, 16, 128), dtype=torch.float32, device="cuda")
+
+            calls = [A.prepare_fwd(q3, k3[:, s * c:(s + 1) * c], v3[:, s * c:(s + 1) * c], po[s], pl[s], partial=True)
+                     for s in range(S)]
+            merge = A.prepare_merge(po, pl, mo, ml)
+            calls.append(merge)
 
             def split_merge():
-                for s in range(S):
-                    A.attn_partial(q3, k3[:, s * c:(s + 1) * c], v3[:, s * c:(s + 1) * c], out=po[s], lse=pl[s])
-                A.attn_merge(po, pl, out=mo)
+                for fn in calls:
+                    fn()
 
             ms_s = timed(split_merge, 100, 5, torch)
-            ms_m = timed(lambda: A.attn_merge(po, pl, out=mo), 100, 5, torch)
+            ms_m = timed(merge, 100, 5, torch)
             mbytes = S * (128 * 16 * 128 * 4 + 16 * 128 * 4) + 128 * 16 * 128 * 2 + 16 * 128 * 4
             entry[f"S{S}"] = {"partials_plus_merge_ms": round(ms_s, 5), "merge_ms": round(ms_m, 5),
                               "merge_GBps": round(mbytes / (ms_m * 1e-3) / 1e9, 1)}
@@ -213,7 +282,9 @@ def main():
     if "fp32" in rows:
         qh1, kh1, vh1 = synth.qkv(1, (1, 128, 2, 64), (1, 128, 2, 64), (1, 128, 2, 64), "f32")
         q1, k1, v1 = up(qh1, "f32"), up(kh1, "f32"), up(vh1, "f32")
-        ms_1 = timed(lambda: A.attn_fwd(q1, k1, v1, scale=0.125), 100, 5, torch)
+        o1 = torch.empty_like(q1)
+        l1 = torch.empty((1, 2, 128), dtype=torch.float32, device="cuda")
+        ms_1 = timed(A.prepare_fwd(q1, k1, v1, o1, l1, scale=0.125), 100, 5, torch)
         fl1 = 4.0 * 2 * 128 * 128 * 64
         result["rows"]["fp32_tiny"] = {"workload": "fp32 B=1 M=128 H=2 K=Kv=64, no mask", "ms_per_call": round(ms_1, 5),
                                        "value": round(fl1 / (ms_1 * 1e-3) / 1e12, 4), "unit": "TFLOP/s",

@@ -135,6 +135,51 @@ def _forward(fn, q, k, v, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, out
     return out, lse
 
 
+class Prepared:
+    """A call of one C entry point with its arguments marshalled once.
+
+    Calling the object re-issues the same C call (same tensors, same stream) with
+    no per-call Python work beyond the ctypes call itself; the tensors it was
+    built from are kept alive by the object.
+    """
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+
+
+def prepare_fwd(q, k, v, out, lse, mask=MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None,
+                max_seqlen_q=None, partial=False, stream=None) -> Prepared:
+    """attn_fwd (or attn_partial) with every argument marshalled up front."""
+    vref, vl = _varlen(seqstart_q, seqstart_k, max_seqlen_q)
+    ds = [desc(q), desc(k), desc(v), desc(out)]
+    args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), int(mask), vref, _scale(scale),
+            ctypes.byref(ds[3]), _ptr(lse), _stream(stream))
+    return Prepared(_lib.attn_partial if partial else _lib.attn_fwd, args, (ds, vl, q, k, v, out, lse))
+
+
+def prepare_decode(q, k, v, num_splits, workspace, out, lse, scale=None, stream=None) -> Prepared:
+    """attn_decode_splitkv with every argument marshalled up front."""
+    ds = [desc(q), desc(k), desc(v), desc(out)]
+    args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), int(num_splits), _scale(scale),
+            _ptr(workspace), workspace.numel(), ctypes.byref(ds[3]), _ptr(lse), _stream(stream))
+    return Prepared(_lib.attn_decode_splitkv, args, (ds, q, k, v, workspace, out, lse))
+
+
+def prepare_merge(out_chunks, lse_chunks, out, lse=None, stream=None) -> Prepared:
+    """attn_merge with every argument marshalled up front."""
+    chunks = list(out_chunks.unbind(0)) if isinstance(out_chunks, torch.Tensor) else list(out_chunks)
+    lses = list(lse_chunks.unbind(0)) if isinstance(lse_chunks, torch.Tensor) else list(lse_chunks)
+    n = len(chunks)
+    descs = (AttnTensor * max(1, n))(*[desc(c) for c in chunks])
+    lptrs = (ctypes.c_void_p * max(1, n))(*[x.data_ptr() for x in lses])
+    do = desc(out)
+    args = (n, descs, lptrs, ctypes.byref(do), _ptr(lse), _stream(stream))
+    return Prepared(_lib.attn_merge, args, (descs, lptrs, do, chunks, lses, out, lse))
+
+
 def attn_fwd(q, k, v, mask=MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None, max_seqlen_q=None,
              out=None, lse=True, stream=None):
     """memory_efficient_attention_forward_requires_grad: returns (out, lse); lse=False skips the LSE."""

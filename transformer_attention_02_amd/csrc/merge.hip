@@ -6,21 +6,61 @@
 // exp(lse_c - M*), out = sum_c exp(lse_c - L) out_c.  A chunk at -inf weighs 0;
 // all chunks at -inf give out = 0 and lse = -inf.
 //
-// One wave per row.  The per-row LSE values are wave-uniform (scalar loads); the
-// lanes split the value dimension, so each chunk row is one coalesced read.
-// Memory-bound: every chunk element is read once, every output written once.
+// One workgroup per row.  Threads c < S read the S LSEs and the workgroup
+// reduces them to L; the weights go to LDS.  The value dimension is then read
+// by 8 chunk groups of 32 lanes, each lane taking 4 consecutive elements of
+// every 8th chunk, with all of a lane's loads issued before any arithmetic, and
+// the 8 partial sums are added through LDS.  Memory-bound: every chunk element
+// is read once and every output element written once.
 #include "kernels.h"
 
 namespace attn {
 namespace {
 
-constexpr int WAVES = 4;
+constexpr int NT = 256;
+constexpr int GROUPS = 8;           // chunk groups per row
+constexpr int SPAN = 128;           // elements of the value dim per pass (32 lanes x 4)
+constexpr int MAXPER = kMaxChunks / GROUPS;
 
-__global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
-    const int64_t rows = (int64_t)a.B * a.M * a.Htot;
-    if (row >= rows) return;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float block_reduce(float x, float *red, bool is_max) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float y = __shfl_xor(x, o, 64);
+        x = is_max ? fmaxf(x, y) : x + y;
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    return is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// 4 consecutive elements starting at element d of a chunk row; elements >= n read as 0.
+__device__ __forceinline__ f32x4 load4(const void *base, int64_t off, int d, int n, bool f32) {
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (d + 3 < n && ((off + d) & 3) == 0) {
+        if (f32) return *(const f32x4 *)((const float *)base + off + d);
+        const uint2 w = *(const uint2 *)((const __bf16 *)base + off + d);
+        x[0] = __uint_as_float(w.x << 16);
+        x[1] = __uint_as_float(w.x & 0xffff0000u);
+        x[2] = __uint_as_float(w.y << 16);
+        x[3] = __uint_as_float(w.y & 0xffff0000u);
+        return x;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (d + i < n) x[i] = f32 ? ((const float *)base)[off + d + i] : (float)((const __bf16 *)base)[off + d + i];
+    return x;
+}
+
+__global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
+    __shared__ float red[4];
+    __shared__ float w_s[kMaxChunks];
+    __shared__ f32x4 part[GROUPS][SPAN / 4];
+
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
     const int hf = (int)(row % a.Htot);
     const int m = (int)((row / a.Htot) % a.M);
     const int b = (int)(row / ((int64_t)a.Htot * a.M));
@@ -28,36 +68,52 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeArgs a) {
     const int64_t coff = (int64_t)b * a.sc.b + (int64_t)m * a.sc.m + head_offset(a.sc, hf, a.Hin);
     const int64_t ooff = (int64_t)b * a.so.b + (int64_t)m * a.so.m + head_offset(a.so, hf, a.Hin);
 
-    float mx = -INFINITY;
-    for (int c = 0; c < a.S; ++c) mx = fmaxf(mx, a.lse[c][loff]);
-
-    if (mx == -INFINITY) {
-        for (int d = lane; d < a.Kv; d += 64) {
+    const float lv = tid < a.S ? a.lse[tid][loff] : -INFINITY;
+    const float mx = block_reduce(lv, red, true);
+    if (mx == -INFINITY) {  // every chunk empty (uniform branch)
+        for (int d = tid; d < a.Kv; d += NT) {
             if (a.out_f32) ((float *)a.o)[ooff + d] = 0.f;
             else ((__bf16 *)a.o)[ooff + d] = (__bf16)0.f;
         }
-        if (a.lse_out && lane == 0) a.lse_out[loff] = -INFINITY;
+        if (a.lse_out && tid == 0) a.lse_out[loff] = -INFINITY;
         return;
     }
-    float sum = 0.f;
-    for (int c = 0; c < a.S; ++c) sum += expf(a.lse[c][loff] - mx);
+    const float sum = block_reduce(tid < a.S ? expf(lv - mx) : 0.f, red, false);
     const float L = mx + logf(sum);
+    if (tid < a.S) w_s[tid] = expf(lv - L);
+    if (a.lse_out && tid == 0) a.lse_out[loff] = L;
+    __syncthreads();
 
-    for (int d0 = 0; d0 < a.Kv; d0 += 64) {
-        const int d = d0 + lane;
-        float acc = 0.f;
-        if (d < a.Kv) {
-            for (int c = 0; c < a.S; ++c) {
-                const float w = expf(a.lse[c][loff] - L);
-                const float x = a.chunk_f32 ? ((const float *)a.chunk[c])[coff + d]
-                                            : (float)((const __bf16 *)a.chunk[c])[coff + d];
-                acc = fmaf(w, x, acc);
-            }
-            if (a.out_f32) ((float *)a.o)[ooff + d] = acc;
-            else ((__bf16 *)a.o)[ooff + d] = (__bf16)acc;
+    const int g = tid / (SPAN / 4), j = tid % (SPAN / 4);
+    const bool f32 = a.chunk_f32;
+    for (int d0 = 0; d0 < a.Kv; d0 += SPAN) {
+        const int d = d0 + 4 * j;
+        f32x4 x[MAXPER];
+#pragma unroll
+        for (int i = 0; i < MAXPER; ++i) {
+            const int c = g + GROUPS * i;
+            x[i] = c < a.S ? load4(a.chunk[c], coff, d, a.Kv, f32) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < MAXPER; ++i) {
+            const int c = g + GROUPS * i;
+            if (c < a.S) acc += w_s[c] * x[i];
+        }
+        part[g][j] = acc;
+        __syncthreads();
+        if (tid < SPAN) {
+            float s = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < GROUPS; ++gg) s += part[gg][tid >> 2][tid & 3];
+            const int dd = d0 + tid;
+            if (dd < a.Kv) {
+                if (a.out_f32) ((float *)a.o)[ooff + dd] = s;
+                else ((__bf16 *)a.o)[ooff + dd] = (__bf16)s;
+            }
+        }
+        __syncthreads();
     }
-    if (a.lse_out && lane == 0) a.lse_out[loff] = L;
 }
 
 }  // namespace
@@ -65,9 +121,8 @@ __global__ __launch_bounds__(WAVES * 64) void merge_kernel(MergeArgs a) {
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream) {
     const int64_t rows = (int64_t)a.B * a.M * a.Htot;
     if (rows <= 0) return hipSuccess;
-    const int64_t grid = (rows + WAVES - 1) / WAVES;
-    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
+    if (rows > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
