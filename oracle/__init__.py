@@ -20,6 +20,10 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 MASK_NONE, MASK_CAUSAL, MASK_BLOCKDIAG, MASK_BLOCKDIAG_CAUSAL = 0, 1, 2, 3
+MASK_CAUSAL_BR, MASK_BLOCKDIAG_CAUSAL_BR, MASK_LOCAL_BR, MASK_CAUSAL_LOCAL_BR = 4, 5, 6, 7
+MASK_BLOCKDIAG_CAUSAL_LOCAL, MASK_BLOCKDIAG_CAUSAL_LOCAL_BR = 8, 9
+PACKED = (MASK_BLOCKDIAG, MASK_BLOCKDIAG_CAUSAL, MASK_BLOCKDIAG_CAUSAL_BR, MASK_BLOCKDIAG_CAUSAL_LOCAL,
+          MASK_BLOCKDIAG_CAUSAL_LOCAL_BR)
 
 _lib = None
 
@@ -42,7 +46,7 @@ def _load():
         lib = ctypes.CDLL(LIB)
         i64, dp, ip = ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)
         lib.oracle_attention.argtypes = [i64, i64, i64, i64, i64, i64, dp, dp, dp, ctypes.c_int, ctypes.c_int,
-                                         ip, ip, ctypes.c_double, dp, dp]
+                                         ip, ip, ctypes.c_double, i64, i64, dp, dp]
         lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_merge.argtypes = [i64, i64, i64, i64, i64, dp, dp, dp, dp]
         lib.oracle_merge.restype = ctypes.c_int
@@ -59,12 +63,15 @@ def threads() -> int:
     return int(_load().oracle_threads())
 
 
-def attention(q, k, v, mask: int = MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None):
+def attention(q, k, v, mask: int = MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None, window=None,
+              window_right=None):
     """Exact attention (fp64).
 
     q [B,Mq,H,K], k [B,Mkv,H,K], v [B,Mkv,H,Kv] -> (out [B,Mq,H,Kv], lse [B,H,Mq]).
     ``scale`` None means 1/sqrt(K).  Packed-sequence masks take int prefix sums
-    (``seqstart_k`` defaults to ``seqstart_q``) and need B == 1.
+    (``seqstart_k`` defaults to ``seqstart_q``) and need B == 1.  ``window`` is the
+    window size of the causal-local kinds, or the left window of MASK_LOCAL_BR
+    (with ``window_right``).
     """
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
@@ -78,7 +85,7 @@ def attention(q, k, v, mask: int = MASK_NONE, scale=None, seqstart_q=None, seqst
     lse = np.empty((B, H, Mq), dtype=np.float64)
     nseq = 0
     sq = sk = None
-    if mask in (MASK_BLOCKDIAG, MASK_BLOCKDIAG_CAUSAL):
+    if mask in PACKED:
         sq = np.ascontiguousarray(seqstart_q, dtype=np.int32)
         sk = np.ascontiguousarray(seqstart_k if seqstart_k is not None else seqstart_q, dtype=np.int32)
         nseq = len(sq) - 1
@@ -87,7 +94,7 @@ def attention(q, k, v, mask: int = MASK_NONE, scale=None, seqstart_q=None, seqst
     rc = _load().oracle_attention(B, Mq, Mkv, H, K, Kv, _dp(q), _dp(k), _dp(v), int(mask), nseq,
                                   sq.ctypes.data_as(ip) if sq is not None else None,
                                   sk.ctypes.data_as(ip) if sk is not None else None,
-                                  float(scale), _dp(out), _dp(lse))
+                                  float(scale), int(window or 0), int(window_right or 0), _dp(out), _dp(lse))
     if rc != 0:
         raise ValueError(f"oracle_attention rejected its arguments (code {rc})")
     return out, lse

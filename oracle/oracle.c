@@ -33,6 +33,17 @@
  *   3 block-diagonal causal: same sequence and j - ks <= i - qs, the
  *                      top-left causal mask inside every block
  *                      (BlockDiagonalCausalMask)
+ *   The windowed / bottom-right kinds use, per sequence with Lq query rows and
+ *   Lk keys (the whole tensor when not packed), local row i and local key j:
+ *   d = j - i - shift, visible iff -wl <= d <= wr, where shift = Lk - Lq for
+ *   bottom-right alignment (the diagonal ends in the last key) and 0 otherwise.
+ *   4 causal bottom-right        shift=Lk-Lq, wr=0          (LowerTriangularFromBottomRightMask)
+ *   5 block-diag causal b-right  per block, as 4            (BlockDiagonalCausalFromBottomRightMask)
+ *   6 local bottom-right(L, R)   shift=Lk-Lq, wl=L, wr=R    (LocalAttentionFromBottomRightMask)
+ *   7 causal local b-right(W)    shift=Lk-Lq, wl=W-1, wr=0  (LowerTriangularFromBottomRightLocalAttentionMask)
+ *   8 block-diag causal local(W) per block, shift=0, wl=W-1, wr=0 (BlockDiagonalCausalLocalAttentionMask)
+ *   9 block-diag causal local b-right(W) per block, as 7    (BlockDiagonalCausalLocalAttentionFromBottomRightMask)
+ *   A window of size W lets a row see the W keys ending at its diagonal.
  *
  * Merge of S chunks (merge_attentions; "MSLK Kernel Library -- Complete
  * Reference", Quick start, "Exact softmax merge"):
@@ -61,21 +72,43 @@ static int seq_of_row(int64_t r, const int32_t *ss, int nseq) {
     return -1;
 }
 
-/* 1 when key j is in A(i). */
-static int key_allowed(int mask, int64_t i, int64_t j, const int32_t *sq, const int32_t *sk,
-                       int nseq) {
-    switch (mask) {
-    case OR_MASK_NONE:
-        return 1;
-    case OR_MASK_CAUSAL:
-        return j <= i;
-    case OR_MASK_BLOCKDIAG:
-    case OR_MASK_BLOCKDIAG_CAUSAL: {
+static int is_packed(int mask) { return mask == 2 || mask == 3 || mask == 5 || mask == 8 || mask == 9; }
+
+/* 1 when key j is in A(i).  Mq/Mkv are the whole extents (used when not packed). */
+static int key_allowed(int mask, int64_t i, int64_t j, const int32_t *sq, const int32_t *sk, int nseq,
+                       int64_t Mq, int64_t Mkv, int64_t win_l, int64_t win_r) {
+    int64_t li = i, lj = j, Lq = Mq, Lk = Mkv;
+    if (is_packed(mask)) {
         int s = seq_of_row(i, sq, nseq);
         if (s < 0) return 0;
         if (j < sk[s] || j >= sk[s + 1]) return 0;
-        if (mask == OR_MASK_BLOCKDIAG) return 1;
-        return (j - sk[s]) <= (i - sq[s]);
+        li = i - sq[s];
+        lj = j - sk[s];
+        Lq = sq[s + 1] - sq[s];
+        Lk = sk[s + 1] - sk[s];
+    }
+    switch (mask) {
+    case OR_MASK_NONE:
+    case OR_MASK_BLOCKDIAG:
+        return 1;
+    case OR_MASK_CAUSAL:
+    case OR_MASK_BLOCKDIAG_CAUSAL:
+        return lj <= li;
+    case 4:
+    case 5:
+        return lj - li - (Lk - Lq) <= 0;
+    case 6: {
+        const int64_t d = lj - li - (Lk - Lq);
+        return d >= -win_l && d <= win_r;
+    }
+    case 7:
+    case 9: {
+        const int64_t d = lj - li - (Lk - Lq);
+        return d <= 0 && d > -win_l;  /* win_l is the window size W */
+    }
+    case 8: {
+        const int64_t d = lj - li;
+        return d <= 0 && d > -win_l;
     }
     default:
         return 0;
@@ -91,13 +124,15 @@ int oracle_threads(void) {
 }
 
 /* Returns 0 on success, nonzero on a bad argument. */
+/* win_l / win_r: window parameters of kinds 6 (left, right) and 7-9 (win_l = window size). */
 int oracle_attention(int64_t B, int64_t Mq, int64_t Mkv, int64_t H, int64_t K, int64_t Kv,
                      const double *q, const double *k, const double *v, int mask, int nseq,
                      const int32_t *seqstart_q, const int32_t *seqstart_k, double scale,
-                     double *out, double *lse) {
+                     int64_t win_l, int64_t win_r, double *out, double *lse) {
     if (B < 0 || Mq < 0 || Mkv < 0 || H < 0 || K < 1 || Kv < 1) return 1;
-    if (mask < 0 || mask > 3) return 1;
-    if (mask >= OR_MASK_BLOCKDIAG && (B != 1 || nseq < 1 || !seqstart_q || !seqstart_k)) return 1;
+    if (mask < 0 || mask > 9) return 1;
+    if (is_packed(mask) && (B != 1 || nseq < 1 || !seqstart_q || !seqstart_k)) return 1;
+    if ((mask >= 7 && win_l < 1) || (mask == 6 && (win_l < 0 || win_r < 0))) return 1;
 
     const int64_t rows = B * H * Mq;
     int err = 0;
@@ -121,7 +156,7 @@ int oracle_attention(int64_t B, int64_t Mq, int64_t Mkv, int64_t H, int64_t K, i
                 double m = -INFINITY;
                 int64_t n_allowed = 0;
                 for (int64_t j = 0; j < Mkv; ++j) {
-                    ok[j] = (char)key_allowed(mask, i, j, seqstart_q, seqstart_k, nseq);
+                    ok[j] = (char)key_allowed(mask, i, j, seqstart_q, seqstart_k, nseq, Mq, Mkv, win_l, win_r);
                     if (!ok[j]) continue;
                     const double *kj = k + ((b * Mkv + j) * H + h) * K;
                     double dot = 0.0;

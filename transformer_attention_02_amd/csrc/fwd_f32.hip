@@ -5,25 +5,32 @@
 // masks of "Attention - Biases & masks"), for head dims up to 128.  Nothing is
 // rounded below fp32, so the result tracks the exact softmax to ~1e-6.
 //
-// One wave per workgroup, one query row per lane (64 rows per workgroup).
-// Keys stream through LDS in tiles of 32; every lane reads the same key row at
-// the same time (an LDS broadcast).  Per tile: 32 scores, one max, one rescale
-// of the running output, 32 exponentials.
+// One workgroup = 4 waves over the same 64 query rows (one row per lane); the
+// keys are dealt out in 16-key tiles round-robin over the waves, so the four
+// waves run independent online softmaxes over disjoint key subsets.  Each wave
+// stages its own tiles in LDS (every lane then reads the same key row: an LDS
+// broadcast).  At the end the four (m, l, o) states are combined exactly, as in
+// the merge of key chunks ("Exact softmax merge" in the site's Quick start):
+// two pairwise rounds through LDS.
 #include "kernels.h"
 
 namespace attn {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int TB = 32;  // keys per tile
-constexpr int BM = 64;  // query rows per workgroup
+constexpr int NWV = 4;   // waves, each with its own key subset
+constexpr int TB = 16;   // keys per tile
+constexpr int BM = 64;   // query rows per workgroup (one per lane)
 
 template <int KD, int KVD>
-__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
-    __shared__ __attribute__((aligned(16))) float ks_[TB][KD];
-    __shared__ __attribute__((aligned(16))) float vs_[TB][KVD];
+__global__ __launch_bounds__(NWV * 64) void fwd_f32_kernel(FwdArgs a) {
+    constexpr int TILE_FLOATS = TB * (KD + KVD);
+    // per-wave K and V tiles; reused at the end for the cross-wave combine
+    __shared__ __attribute__((aligned(16))) float smem[NWV * TILE_FLOATS > 2 * 64 * (KVD + 2)
+                                                         ? NWV * TILE_FLOATS
+                                                         : 2 * 64 * (KVD + 2)];
 
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int BH = a.B * a.Htot;
     const int tiles = (a.max_seqlen_q + BM - 1) / BM;
     int id = blockIdx.x;
@@ -51,7 +58,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
     const float *kp = (const float *)a.k + (int64_t)b * a.sk.b + head_offset(a.sk, hf, a.Hin) + (int64_t)kst * a.sk.m;
     const float *vp = (const float *)a.v + (int64_t)b * a.sv.b + head_offset(a.sv, hf, a.Hin) + (int64_t)kst * a.sv.m;
 
-    const int qrow = row0 + tid;
+    const int qrow = row0 + lane;
     float q[KD];
 #pragma unroll
     for (int d = 0; d < KD; ++d) q[d] = (qrow < Lq && d < a.K) ? qp[(int64_t)qrow * a.sq.m + d] : 0.f;
@@ -61,34 +68,39 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
     for (int d = 0; d < KVD; ++d) o[d] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
     const float c = a.scale_log2;
+    float *ks_ = smem + wave * TILE_FLOATS;  // [TB][KD]
+    float *vs_ = ks_ + TB * KD;              // [TB][KVD]
 
-    for (int kt0 = 0; kt0 < nkeys; kt0 += TB) {
-        __syncthreads();
-        for (int idx = tid; idx < TB * KD; idx += 64) {
+    const int rounds = (nkeys + NWV * TB - 1) / (NWV * TB);
+    for (int it = 0; it < rounds; ++it) {
+        const int kt0 = (it * NWV + wave) * TB;  // this wave's tile
+        __syncthreads();                          // previous tile fully read
+        for (int idx = lane; idx < TB * KD; idx += 64) {
             const int r = idx / KD, d = idx % KD, j = kt0 + r;
-            ks_[r][d] = (j < Lk && d < a.K) ? kp[(int64_t)j * a.sk.m + d] : 0.f;
+            ks_[idx] = (j < nkeys && d < a.K) ? kp[(int64_t)j * a.sk.m + d] : 0.f;
         }
-        for (int idx = tid; idx < TB * KVD; idx += 64) {
+        for (int idx = lane; idx < TB * KVD; idx += 64) {
             const int r = idx / KVD, d = idx % KVD, j = kt0 + r;
-            vs_[r][d] = (j < Lk && d < a.Kv) ? vp[(int64_t)j * a.sv.m + d] : 0.f;
+            vs_[idx] = (j < nkeys && d < a.Kv) ? vp[(int64_t)j * a.sv.m + d] : 0.f;
         }
         __syncthreads();
+        if (kt0 >= nkeys) continue;
 
         float s[TB];
         float mt = -INFINITY;
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
-            float dot = 0.f;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int d = 0; d < KD; d += 4) {
-                const float4 kk = *(const float4 *)&ks_[j][d];
-                dot = fmaf(q[d], kk.x, dot);
-                dot = fmaf(q[d + 1], kk.y, dot);
-                dot = fmaf(q[d + 2], kk.z, dot);
-                dot = fmaf(q[d + 3], kk.w, dot);
+                const float4 kk = *(const float4 *)&ks_[j * KD + d];
+                acc[0] = fmaf(q[d], kk.x, acc[0]);
+                acc[1] = fmaf(q[d + 1], kk.y, acc[1]);
+                acc[2] = fmaf(q[d + 2], kk.z, acc[2]);
+                acc[3] = fmaf(q[d + 3], kk.w, acc[3]);
             }
             const int key = kt0 + j;
-            float x = dot * c;
+            float x = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * c;
             if (key >= nkeys || (causal && key > qrow)) x = -INFINITY;
             s[j] = x;
             mt = fmaxf(mt, x);
@@ -106,7 +118,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
             l_run += p;
 #pragma unroll
             for (int d = 0; d < KVD; d += 4) {
-                const float4 vv = *(const float4 *)&vs_[j][d];
+                const float4 vv = *(const float4 *)&vs_[j * KVD + d];
                 o[d] = fmaf(p, vv.x, o[d]);
                 o[d + 1] = fmaf(p, vv.y, o[d + 1]);
                 o[d + 2] = fmaf(p, vv.z, o[d + 2]);
@@ -115,7 +127,33 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
         }
     }
 
-    if (qrow < Lq) {
+    // exact combine of the four waves' states: waves 2,3 -> 0,1, then wave 1 -> 0
+    constexpr int REC = KVD + 2;  // o[KVD], m, l per row
+#pragma unroll
+    for (int step = 2; step >= 1; step >>= 1) {
+        __syncthreads();
+        if (wave >= step && wave < 2 * step) {
+            float *rec = smem + ((wave - step) * 64 + lane) * REC;
+#pragma unroll
+            for (int d = 0; d < KVD; ++d) rec[d] = o[d];
+            rec[KVD] = m_run;
+            rec[KVD + 1] = l_run;
+        }
+        __syncthreads();
+        if (wave < step) {
+            const float *rec = smem + (wave * 64 + lane) * REC;
+            const float m2 = rec[KVD], l2 = rec[KVD + 1];
+            const float mm = fmaxf(m_run, m2);
+            const float mu = (mm == -INFINITY) ? 0.f : mm;
+            const float a1 = exp2f(m_run - mu), a2 = exp2f(m2 - mu);
+#pragma unroll
+            for (int d = 0; d < KVD; ++d) o[d] = o[d] * a1 + rec[d] * a2;
+            l_run = l_run * a1 + l2 * a2;
+            m_run = mm;
+        }
+    }
+
+    if (wave == 0 && qrow < Lq) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
         float *op = (float *)a.o + (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) + (int64_t)(qs + qrow) * a.so.m;
 #pragma unroll
@@ -133,7 +171,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
     const int64_t grid = tiles * a.nseq * (int64_t)a.B * a.Htot;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_f32_kernel<KD, KVD>), dim3((unsigned)grid), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((fwd_f32_kernel<KD, KVD>), dim3((unsigned)grid), dim3(NWV * 64), 0, stream, a);
     return hipGetLastError();
 }
 
