@@ -8,7 +8,8 @@ headline value is its throughput in TFLOP/s, counting 4*B*H*M*M*K flops halved
 for the causal mask.  The other rows of the path are timed after it and
 reported under "rows": split-KV decode (B=16, Mkv=32768, H=32, 64 chunks;
 GB/s of K+V), the packed GQA causal prefill (8 sequences, lengths U[256, 4096]),
-the 2- and 8-way partial+merge of Mq=128/Mkv=1024/H=16, and the fp32 tiny case.
+a causal sliding window of 1024 keys over [2, 8192, 32, 128], the 2- and 8-way
+partial+merge of Mq=128/Mkv=1024/H=16, and the fp32 tiny case.
 Every figure is timed with HIP events on the stream the kernels run on; each call is
 marshalled once (attn.prepare_*), so a timed call is one C-ABI call.  The
 CPU baseline is the fp64 oracle on the host cores over the whole prefill
@@ -38,8 +39,8 @@ def parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=300,
                    help="untimed steps first; ~25 ms of back-to-back launches brings the clock to steady state")
-    p.add_argument("--rows", default="decode,varlen,merge,fp32",
-                   help="rows timed after the headline prefill: decode,varlen,merge,fp32,copy or none; "
+    p.add_argument("--rows", default="decode,varlen,window,merge,fp32",
+                   help="rows timed after the headline prefill: decode,varlen,window,merge,fp32,copy or none; "
                         "copy is a plain 1 GiB device copy used to calibrate the HBM byte counters")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--rocpd", metavar="DB", help="summarise a rocprofv3 results database (kernel durations and "
@@ -232,6 +233,26 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl}}
         del qv, kv, vv, ov, lv
+
+    # ------------------------------------------------------------ sliding-window causal prefill
+    if "window" in rows:
+        Bw, Mw, Hw, Dw, W = 2, 8192, 32, 128, 1024
+        shp = (Bw, Mw, Hw, Dw)
+        qh4, kh4, vh4 = synth.qkv(6, shp, shp, shp, "bf16")
+        qw, kw, vw = up(qh4), up(kh4), up(vh4)
+        ow = torch.empty_like(qw)
+        lw = torch.empty((Bw, Hw, Mw), dtype=torch.float32, device="cuda")
+        ms_w = timed(A.prepare_fwd(qw, kw, vw, ow, lw, mask=A.MASK_CAUSAL_LOCAL_BR, window_size=W), 50, 20, torch)
+        visible = W * (W + 1) / 2 + (Mw - W) * W  # scores per head: row i sees min(i + 1, W) keys
+        fl = 4.0 * Bw * Hw * Dw * visible
+        tf = fl / (ms_w * 1e-3) / 1e12
+        log(f"sliding window W={W} [2,8192,32,128]: {ms_w * 1e3:.1f} us/call, {tf:.1f} TFLOP/s")
+        result["rows"]["sliding_window_causal"] = {
+            "workload": "bf16 B=2 M=8192 H=32 K=Kv=128, causal window of 1024 keys (bottom-right local mask)",
+            "ms_per_call": round(ms_w, 5), "value": round(tf, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl}}
+        del qw, kw, vw, ow, lw
 
     # ------------------------------------------------------------ partial + merge
     if "merge" in rows:

@@ -68,13 +68,38 @@ typedef enum {
 
 typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
 
-/* Masks ("Attention - Biases & masks" on the kernel reference page). */
+/* Masks ("Attention - Biases & masks" on the kernel reference page).  For a
+ * (sequence of) Lq query rows and Lk keys, with local row i and local key j, the
+ * visible keys are those with  -wl <= j - i - shift <= wr,  where shift = Lk - Lq
+ * for the bottom-right kinds (the diagonal ends in the last key) and 0 otherwise.
+ * The BLOCKDIAG kinds apply this inside every packed sequence (attn_varlen). */
 typedef enum {
     ATTN_MASK_NONE = 0,
     ATTN_MASK_CAUSAL = 1,            /* LowerTriangularMask: top-left aligned, key j visible iff j <= i */
     ATTN_MASK_BLOCKDIAG = 2,         /* BlockDiagonalMask: a query row sees its own packed sequence */
-    ATTN_MASK_BLOCKDIAG_CAUSAL = 3   /* BlockDiagonalCausalMask: top-left causal inside every block */
+    ATTN_MASK_BLOCKDIAG_CAUSAL = 3,  /* BlockDiagonalCausalMask: top-left causal inside every block */
+    ATTN_MASK_CAUSAL_BOTTOMRIGHT = 4,            /* LowerTriangularFromBottomRightMask: j <= i + Lk - Lq */
+    ATTN_MASK_BLOCKDIAG_CAUSAL_BOTTOMRIGHT = 5,  /* BlockDiagonalCausalFromBottomRightMask (per block);
+                                                    a block with fewer keys than queries leaves its
+                                                    first Lq - Lk rows empty */
+    ATTN_MASK_LOCAL_BOTTOMRIGHT = 6,             /* LocalAttentionFromBottomRightMask(window_left,
+                                                    window_right): wl = window_left, wr = window_right */
+    ATTN_MASK_CAUSAL_LOCAL_BOTTOMRIGHT = 7,      /* LowerTriangularFromBottomRightLocalAttentionMask(
+                                                    window_size): the window_size keys ending at the
+                                                    diagonal (wl = window_size - 1, wr = 0) */
+    ATTN_MASK_BLOCKDIAG_CAUSAL_LOCAL = 8,        /* BlockDiagonalCausalLocalAttentionMask(window_size):
+                                                    top-left, per block */
+    ATTN_MASK_BLOCKDIAG_CAUSAL_LOCAL_BOTTOMRIGHT = 9  /* BlockDiagonalCausalLocalAttentionFromBottomRightMask */
 } attn_mask_kind;
+
+/* A mask with its window parameters (kinds 6-9 need them; 0-5 ignore them).
+ * window_size >= 1 for kinds 7-9; window_left, window_right >= 0 for kind 6. */
+typedef struct {
+    int32_t kind;
+    int32_t window_size;
+    int32_t window_left;
+    int32_t window_right;
+} attn_mask;
 
 typedef struct {
     void *data;        /* device pointer */
@@ -85,7 +110,7 @@ typedef struct {
 } attn_tensor;
 
 /* Packed variable-length sequences ("Glossary: varlen"; BlockDiagonalMask.from_seqlens).
- * Required for the two block-diagonal masks, ignored otherwise.  B must be 1.
+ * Required for the BLOCKDIAG masks, ignored otherwise.  B must be 1.
  * seqstart_q/seqstart_k are DEVICE int32 prefix sums [nseq + 1]: 0, L0, L0+L1,
  * ..., M_total.  seqstart_k NULL means seqstart_k = seqstart_q.
  * max_seqlen_q must be >= every query length.  The offsets live on the device
@@ -100,6 +125,7 @@ typedef struct {
 } attn_varlen;
 
 /* memory_efficient_attention_forward_requires_grad ("Attention - Core fMHA").
+ *   mask: an attn_mask_kind without window parameters (0-5); attn_fwd_ex takes any kind.
  *   q [B, Mq, (G,) H, K], k [B, Mkv, (G,) H, K], v [B, Mkv, (G,) H, Kv]; one dtype.
  *   out [B, Mq, (G,) H, Kv] with q's dtype.
  *   lse fp32 [B, H_total, Mq] device buffer, or NULL to skip it.
@@ -116,6 +142,15 @@ attn_status attn_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tens
 attn_status attn_partial(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                          int32_t mask, const attn_varlen *varlen, float scale,
                          const attn_tensor *out, float *lse, attn_stream_t stream);
+
+/* attn_fwd / attn_partial with a full mask descriptor (any kind, including the
+ * windowed ones).  Everything else as above. */
+attn_status attn_fwd_ex(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                        const attn_mask *mask, const attn_varlen *varlen, float scale,
+                        const attn_tensor *out, float *lse, attn_stream_t stream);
+attn_status attn_partial_ex(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                            const attn_mask *mask, const attn_varlen *varlen, float scale,
+                            const attn_tensor *out, float *lse, attn_stream_t stream);
 
 /* merge_attentions ("Attention - Core fMHA"; "Exact softmax merge" in Quick start).
  *   n_chunks in [1, ATTN_MAX_CHUNKS]; out_chunks: n_chunks host descriptors

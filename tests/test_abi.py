@@ -22,8 +22,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["attn_fwd", "attn_partial", "attn_merge", "attn_decode_workspace_bytes",
-                                           "attn_decode_splitkv", "attn_last_error"])
+    assert declared_functions() == sorted(["attn_fwd", "attn_partial", "attn_fwd_ex", "attn_partial_ex", "attn_merge",
+                                           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -182,3 +182,25 @@ def test_decode_workspace_and_rejects():
     assert call(num_splits=129) == A.ATTN_ERR_UNSUPPORTED
     assert call(ws=FAKE * 256 + 16) == A.ATTN_ERR_INVALID_ARGUMENT
     assert call(qq=tensor([B, 2, H, D])) == A.ATTN_ERR_INVALID_ARGUMENT
+
+
+def fwd_ex(q, k, v, o, mask, varlen=None, fn=None):
+    fn = fn or A._lib.attn_fwd_ex
+    return fn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(mask) if mask is not None else None,
+              varlen, float("nan"), ctypes.byref(o), ctypes.c_void_p(FAKE), None)
+
+
+def test_windowed_masks_need_the_ex_entry_point_and_valid_windows():
+    q, k, v, o = std4(), std4(256), std4(256), std4()
+    for kind in (6, 7, 8, 9):
+        assert fwd(q, k, v, o, mask=kind) == A.ATTN_ERR_INVALID_ARGUMENT
+        assert "_ex" in A.attn_last_error()
+    assert fwd_ex(q, k, v, o, None) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert fwd_ex(q, k, v, o, A.AttnMask(7, 0, 0, 0)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert "window_size" in A.attn_last_error()
+    assert fwd_ex(q, k, v, o, A.AttnMask(6, 0, -1, 3)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert "window_left" in A.attn_last_error()
+    assert fwd_ex(q, k, v, o, A.AttnMask(10, 1, 0, 0)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert fwd_ex(q, k, v, o, A.AttnMask(8, 4, 0, 0)) == A.ATTN_ERR_INVALID_ARGUMENT  # packed kind, no varlen
+    assert "varlen" in A.attn_last_error()
+    assert fwd_ex(q, k, v, o, A.AttnMask(5, 0, 0, 0), fn=A._lib.attn_partial_ex) == A.ATTN_ERR_INVALID_ARGUMENT

@@ -24,9 +24,9 @@ def A():
     return attn
 
 
-def run_oracle(qh, kh, vh, mask, dtype, scale=None, ss=None, ssk=None):
+def run_oracle(qh, kh, vh, mask, dtype, scale=None, ss=None, ssk=None, window=None, window_right=None):
     return oracle.attention(synth.to_f64(qh, dtype), synth.to_f64(kh, dtype), synth.to_f64(vh, dtype), mask=mask,
-                            scale=scale, seqstart_q=ss, seqstart_k=ssk)
+                            scale=scale, seqstart_q=ss, seqstart_k=ssk, window=window, window_right=window_right)
 
 
 def check(out, lse, oo, ol, tol_out, tol_lse, what):
@@ -275,3 +275,54 @@ def test_merge_fp32_exactness(A):
     torch.cuda.synchronize()
     check(out, lse, mo, ml, 1e-5, 1e-5, "merge fp32")
     assert math.isinf(lse[0, 0, 3].item()) and torch.all(out[0, 3, 0] == 0)
+
+
+# ------------------------------------------------------------------ bottom-right and windowed masks
+
+WINDOW_CASES = [  # (mask, window_size, window_left, window_right, Mq, Mkv)
+    (4, None, None, None, 100, 300),    # bottom-right causal, fewer queries than keys
+    (4, None, None, None, 300, 100),    # more queries than keys: the first 200 rows see nothing
+    (6, None, 37, 5, 200, 333),         # two-sided window around the bottom-right diagonal
+    (6, None, 0, 0, 65, 65),            # a single key per row
+    (7, 64, None, None, 257, 700),      # causal sliding window of one tile
+    (7, 1, None, None, 70, 70),
+    (7, 300, None, None, 1000, 1000),   # window wider than several tiles
+]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_bottomright_and_window_masks(A, dtype, D):
+    tol_o, tol_l = (TOL_BF16_OUT, TOL_LSE) if dtype == "bf16" else (TOL_F32, TOL_F32)
+    seed = 800
+    for mask, win, wl, wr, Mq, Mkv in WINDOW_CASES:
+        seed += 1
+        say(f"case: {dtype} D={D} mask={mask} window={win} left={wl} right={wr} Mq={Mq} Mkv={Mkv}")
+        qh, kh, vh = synth.qkv(seed, (2, Mq, 2, D), (2, Mkv, 2, D), (2, Mkv, 2, D), dtype)
+        out, lse = A.attn_fwd(dev(qh, dtype), dev(kh, dtype), dev(vh, dtype), mask=mask, window_size=win,
+                              window_left=wl, window_right=wr)
+        torch.cuda.synchronize()
+        oo, ol = run_oracle(qh, kh, vh, mask, dtype, window=win if win is not None else wl, window_right=wr)
+        check(out, lse, oo, ol, tol_o, tol_l, f"mask={mask}")
+    # packed kinds, with different query and key packings
+    sq, sk = synth.seqstarts([70, 1, 300, 129]), synth.seqstarts([90, 5, 300, 100])
+    for mask, win in [(5, None), (8, 33), (9, 100), (9, 1)]:
+        seed += 1
+        say(f"case: {dtype} D={D} packed mask={mask} window={win}")
+        qh, kh, vh = synth.qkv(seed, (1, int(sq[-1]), 2, D), (1, int(sk[-1]), 2, D), (1, int(sk[-1]), 2, D), dtype)
+        out, lse = A.attn_fwd(dev(qh, dtype), dev(kh, dtype), dev(vh, dtype), mask=mask, window_size=win,
+                              seqstart_q=torch.from_numpy(sq).to("cuda"), seqstart_k=torch.from_numpy(sk).to("cuda"),
+                              max_seqlen_q=300)
+        torch.cuda.synchronize()
+        oo, ol = run_oracle(qh, kh, vh, mask, dtype, ss=sq, ssk=sk, window=win)
+        check(out, lse, oo, ol, tol_o, tol_l, f"packed mask={mask}")
+
+
+def test_windowed_partial_and_merge(A):
+    """attn_partial with a window mask: the mask treats the shard as the whole key sequence."""
+    say("case: windowed partial")
+    qh, kh, vh = synth.qkv(900, (1, 128, 4, 128), (1, 512, 4, 128), (1, 512, 4, 128), "bf16")
+    q, k, v = dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16")
+    po, pl = A.attn_partial(q, k[:, 256:], v[:, 256:], mask=A.MASK_CAUSAL_LOCAL_BR, window_size=100)
+    torch.cuda.synchronize()
+    oo, ol = run_oracle(qh, kh[:, 256:], vh[:, 256:], 7, "bf16", window=100)
+    check(po, pl, oo, ol, TOL_BF16_OUT, TOL_LSE, "partial window")

@@ -23,6 +23,9 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE_TOO_SMALL, ATTN_ERR_LAUNCH = range(5)
 ATTN_DTYPE_F32, ATTN_DTYPE_BF16 = 0, 1
 MASK_NONE, MASK_CAUSAL, MASK_BLOCKDIAG, MASK_BLOCKDIAG_CAUSAL = 0, 1, 2, 3
+MASK_CAUSAL_BR, MASK_BLOCKDIAG_CAUSAL_BR, MASK_LOCAL_BR, MASK_CAUSAL_LOCAL_BR = 4, 5, 6, 7
+MASK_BLOCKDIAG_CAUSAL_LOCAL, MASK_BLOCKDIAG_CAUSAL_LOCAL_BR = 8, 9
+WINDOWED = (MASK_LOCAL_BR, MASK_CAUSAL_LOCAL_BR, MASK_BLOCKDIAG_CAUSAL_LOCAL, MASK_BLOCKDIAG_CAUSAL_LOCAL_BR)
 MAX_CHUNKS = 128
 
 if not os.path.exists(LIB_PATH):
@@ -33,6 +36,11 @@ _lib = ctypes.CDLL(LIB_PATH)
 class AttnTensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
                 ("shape", ctypes.c_int64 * 5), ("stride", ctypes.c_int64 * 5)]
+
+
+class AttnMask(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("window_size", ctypes.c_int32), ("window_left", ctypes.c_int32),
+                ("window_right", ctypes.c_int32)]
 
 
 class AttnVarlen(ctypes.Structure):
@@ -47,6 +55,11 @@ _lib.attn_fwd.argtypes = [_T, _T, _T, ctypes.c_int32, _P(AttnVarlen), ctypes.c_f
 _lib.attn_fwd.restype = ctypes.c_int
 _lib.attn_partial.argtypes = _lib.attn_fwd.argtypes
 _lib.attn_partial.restype = ctypes.c_int
+_lib.attn_fwd_ex.argtypes = [_T, _T, _T, _P(AttnMask), _P(AttnVarlen), ctypes.c_float, _T, ctypes.c_void_p,
+                             ctypes.c_void_p]
+_lib.attn_fwd_ex.restype = ctypes.c_int
+_lib.attn_partial_ex.argtypes = _lib.attn_fwd_ex.argtypes
+_lib.attn_partial_ex.restype = ctypes.c_int
 _lib.attn_merge.argtypes = [ctypes.c_int32, _T, _P(ctypes.c_void_p), _T, ctypes.c_void_p, ctypes.c_void_p]
 _lib.attn_merge.restype = ctypes.c_int
 _lib.attn_decode_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
@@ -121,6 +134,14 @@ def attn_last_error() -> str:
     return _lib.attn_last_error().decode()
 
 
+def _mask_arg(mask, window_size, window_left, window_right, partial):
+    """(C function, mask argument): the plain entry point for kinds without windows, _ex otherwise."""
+    if mask in WINDOWED or window_size is not None or window_left is not None or window_right is not None:
+        m = AttnMask(int(mask), int(window_size or 0), int(window_left or 0), int(window_right or 0))
+        return (_lib.attn_partial_ex if partial else _lib.attn_fwd_ex), m, ctypes.byref(m)
+    return (_lib.attn_partial if partial else _lib.attn_fwd), None, int(mask)
+
+
 def _forward(fn, q, k, v, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, out, lse, stream, out_dtype):
     if out is None:
         out = torch.empty((*q.shape[:-1], v.shape[-1]), dtype=out_dtype, device=q.device)
@@ -130,8 +151,9 @@ def _forward(fn, q, k, v, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, out
         lse = None
     vref, _keep = _varlen(seqstart_q, seqstart_k, max_seqlen_q)
     dq, dk, dv, do = desc(q), desc(k), desc(v), desc(out)
-    _check(fn(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(mask), vref, _scale(scale),
-              ctypes.byref(do), _ptr(lse), _stream(stream)))
+    cfn, _m, marg = _mask_arg(mask[0], *mask[1:], partial=fn == "partial")
+    _check(cfn(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), marg, vref, _scale(scale),
+               ctypes.byref(do), _ptr(lse), _stream(stream)))
     return out, lse
 
 
@@ -151,13 +173,15 @@ class Prepared:
 
 
 def prepare_fwd(q, k, v, out, lse, mask=MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None,
-                max_seqlen_q=None, partial=False, stream=None) -> Prepared:
-    """attn_fwd (or attn_partial) with every argument marshalled up front."""
+                max_seqlen_q=None, partial=False, stream=None, window_size=None, window_left=None,
+                window_right=None) -> Prepared:
+    """attn_fwd (or attn_partial, or their _ex forms for windowed masks) marshalled up front."""
     vref, vl = _varlen(seqstart_q, seqstart_k, max_seqlen_q)
     ds = [desc(q), desc(k), desc(v), desc(out)]
-    args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), int(mask), vref, _scale(scale),
+    cfn, m, marg = _mask_arg(mask, window_size, window_left, window_right, partial)
+    args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), marg, vref, _scale(scale),
             ctypes.byref(ds[3]), _ptr(lse), _stream(stream))
-    return Prepared(_lib.attn_partial if partial else _lib.attn_fwd, args, (ds, vl, q, k, v, out, lse))
+    return Prepared(cfn, args, (ds, vl, m, q, k, v, out, lse))
 
 
 def prepare_decode(q, k, v, num_splits, workspace, out, lse, scale=None, stream=None) -> Prepared:
@@ -181,17 +205,21 @@ def prepare_merge(out_chunks, lse_chunks, out, lse=None, stream=None) -> Prepare
 
 
 def attn_fwd(q, k, v, mask=MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None, max_seqlen_q=None,
-             out=None, lse=True, stream=None):
-    """memory_efficient_attention_forward_requires_grad: returns (out, lse); lse=False skips the LSE."""
-    return _forward(_lib.attn_fwd, q, k, v, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, out, lse, stream,
-                    q.dtype)
+             out=None, lse=True, stream=None, window_size=None, window_left=None, window_right=None):
+    """memory_efficient_attention_forward_requires_grad: returns (out, lse); lse=False skips the LSE.
+
+    Windowed masks take window_size (kinds 7-9) or window_left/window_right (kind 6) and go
+    through attn_fwd_ex."""
+    return _forward("fwd", q, k, v, (mask, window_size, window_left, window_right), scale, seqstart_q, seqstart_k,
+                    max_seqlen_q, out, lse, stream, q.dtype)
 
 
 def attn_partial(q, k, v, mask=MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None, max_seqlen_q=None,
-                 out=None, lse=True, stream=None, out_dtype=torch.float32):
+                 out=None, lse=True, stream=None, out_dtype=torch.float32, window_size=None, window_left=None,
+                 window_right=None):
     """memory_efficient_attention_partial over the shard (k, v): returns (out fp32 by default, lse)."""
-    return _forward(_lib.attn_partial, q, k, v, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, out, lse,
-                    stream, out_dtype)
+    return _forward("partial", q, k, v, (mask, window_size, window_left, window_right), scale, seqstart_q,
+                    seqstart_k, max_seqlen_q, out, lse, stream, out_dtype)
 
 
 def attn_merge(out_chunks, lse_chunks, out=None, write_lse=True, out_dtype=None, stream=None):

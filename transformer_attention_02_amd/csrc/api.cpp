@@ -97,9 +97,42 @@ attn_status launch_status(hipError_t e, const char *what) {
     return ok();
 }
 
-// Shared validation and launch for attn_fwd / attn_partial.
+// Mask kind -> (packed, bottom_right, wl, wr) of the kernels' visible-key interval.
+struct MaskSpec {
+    int packed, bottom_right, wl, wr;
+};
+
+attn_status mask_spec(const char *fn, const attn_mask &m, MaskSpec *out) {
+    const int inf = attn::kWinInf;
+    auto clampw = [&](int64_t w) { return (int)(w >= inf ? inf : w); };
+    switch (m.kind) {
+    case ATTN_MASK_NONE: *out = {0, 0, inf, inf}; break;
+    case ATTN_MASK_CAUSAL: *out = {0, 0, inf, 0}; break;
+    case ATTN_MASK_BLOCKDIAG: *out = {1, 0, inf, inf}; break;
+    case ATTN_MASK_BLOCKDIAG_CAUSAL: *out = {1, 0, inf, 0}; break;
+    case ATTN_MASK_CAUSAL_BOTTOMRIGHT: *out = {0, 1, inf, 0}; break;
+    case ATTN_MASK_BLOCKDIAG_CAUSAL_BOTTOMRIGHT: *out = {1, 1, inf, 0}; break;
+    case ATTN_MASK_LOCAL_BOTTOMRIGHT:
+        if (m.window_left < 0 || m.window_right < 0)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: window_left and window_right must be >= 0", fn);
+        *out = {0, 1, clampw(m.window_left), clampw(m.window_right)};
+        break;
+    case ATTN_MASK_CAUSAL_LOCAL_BOTTOMRIGHT:
+    case ATTN_MASK_BLOCKDIAG_CAUSAL_LOCAL:
+    case ATTN_MASK_BLOCKDIAG_CAUSAL_LOCAL_BOTTOMRIGHT:
+        if (m.window_size < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: window_size must be >= 1", fn);
+        *out = {m.kind != ATTN_MASK_CAUSAL_LOCAL_BOTTOMRIGHT, m.kind != ATTN_MASK_BLOCKDIAG_CAUSAL_LOCAL,
+                clampw((int64_t)m.window_size - 1), 0};
+        break;
+    default:
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: unknown mask kind %d", fn, m.kind);
+    }
+    return ATTN_OK;
+}
+
+// Shared validation and launch for attn_fwd / attn_partial (and the _ex forms).
 attn_status forward(const char *fn, bool partial, const attn_tensor *qt, const attn_tensor *kt,
-                    const attn_tensor *vt, int32_t mask, const attn_varlen *varlen, float scale,
+                    const attn_tensor *vt, const attn_mask &mask, const attn_varlen *varlen, float scale,
                     const attn_tensor *ot, float *lse, attn_stream_t stream) {
     View q, k, v, o;
     attn_status st;
@@ -123,9 +156,9 @@ attn_status forward(const char *fn, bool partial, const attn_tensor *qt, const a
     if (o.M != q.M) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out must have q's row count", fn);
     if (k.D != q.D) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q and k head dims differ", fn);
     if (o.D != v.D) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out head dim must equal v's", fn);
-    if (mask < ATTN_MASK_NONE || mask > ATTN_MASK_BLOCKDIAG_CAUSAL)
-        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: unknown mask kind %d", fn, mask);
-    const bool packed = mask == ATTN_MASK_BLOCKDIAG || mask == ATTN_MASK_BLOCKDIAG_CAUSAL;
+    MaskSpec ms;
+    if ((st = mask_spec(fn, mask, &ms)) != ATTN_OK) return st;
+    const bool packed = ms.packed;
     if (packed) {
         if (!varlen) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block-diagonal masks need varlen", fn);
         if (q.B != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: packed sequences need B == 1", fn);
@@ -177,7 +210,10 @@ attn_status forward(const char *fn, bool partial, const attn_tensor *qt, const a
     const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)q.D) : (double)scale;
     a.scale_log2 = (float)(sc * 1.4426950408889634);
     if (std::fabs(a.scale_log2) < 1e-30f) a.scale_log2 = std::copysign(1e-30f, a.scale_log2);  // keeps -inf masking exact
-    a.mask = mask;
+    a.packed = ms.packed;
+    a.bottom_right = ms.bottom_right;
+    a.wl = ms.wl;
+    a.wr = ms.wr;
     if (packed) {
         a.seqstart_q = varlen->seqstart_q;
         a.seqstart_k = varlen->seqstart_k;
@@ -204,16 +240,42 @@ extern "C" {
 
 const char *attn_last_error(void) { return g_err; }
 
+static attn_status plain_mask(const char *fn, int32_t kind, attn_mask *m) {
+    if (kind >= ATTN_MASK_LOCAL_BOTTOMRIGHT && kind <= ATTN_MASK_BLOCKDIAG_CAUSAL_LOCAL_BOTTOMRIGHT)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: mask kind %d needs window sizes: use the _ex entry point", fn,
+                    kind);
+    *m = attn_mask{kind, 0, 0, 0};
+    return ATTN_OK;
+}
+
 attn_status attn_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, int32_t mask,
                      const attn_varlen *varlen, float scale, const attn_tensor *out, float *lse,
                      attn_stream_t stream) {
-    return forward("attn_fwd", false, q, k, v, mask, varlen, scale, out, lse, stream);
+    attn_mask m;
+    attn_status st = plain_mask("attn_fwd", mask, &m);
+    return st != ATTN_OK ? st : forward("attn_fwd", false, q, k, v, m, varlen, scale, out, lse, stream);
 }
 
 attn_status attn_partial(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, int32_t mask,
                          const attn_varlen *varlen, float scale, const attn_tensor *out, float *lse,
                          attn_stream_t stream) {
-    return forward("attn_partial", true, q, k, v, mask, varlen, scale, out, lse, stream);
+    attn_mask m;
+    attn_status st = plain_mask("attn_partial", mask, &m);
+    return st != ATTN_OK ? st : forward("attn_partial", true, q, k, v, m, varlen, scale, out, lse, stream);
+}
+
+attn_status attn_fwd_ex(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, const attn_mask *mask,
+                        const attn_varlen *varlen, float scale, const attn_tensor *out, float *lse,
+                        attn_stream_t stream) {
+    if (!mask) return fail(ATTN_ERR_INVALID_ARGUMENT, "attn_fwd_ex: mask is NULL");
+    return forward("attn_fwd_ex", false, q, k, v, *mask, varlen, scale, out, lse, stream);
+}
+
+attn_status attn_partial_ex(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, const attn_mask *mask,
+                            const attn_varlen *varlen, float scale, const attn_tensor *out, float *lse,
+                            attn_stream_t stream) {
+    if (!mask) return fail(ATTN_ERR_INVALID_ARGUMENT, "attn_partial_ex: mask is NULL");
+    return forward("attn_partial_ex", true, q, k, v, *mask, varlen, scale, out, lse, stream);
 }
 
 attn_status attn_merge(int32_t n_chunks, const attn_tensor *out_chunks, const float *const *lse_chunks,

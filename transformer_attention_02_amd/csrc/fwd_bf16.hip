@@ -37,9 +37,10 @@
 // (and O, l rescaled) only when a new score exceeds it by more than 2^8, so
 // most tiles skip the rescale.  P is rounded to bf16 for the product with V;
 // l accumulates the fp32 values.  lse = (m + log2 l) * ln 2.
-// Causal tiles entirely above a wave's rows are skipped by that wave; the
-// element mask is applied only on tiles that cross the diagonal or the end of
-// the keys.
+// Masks are one visible-key interval per row (causal, bottom-right, sliding
+// windows).  Tiles outside every window of a wave's rows are skipped by that
+// wave; the element mask is applied only on tiles that cut a window edge or
+// the end of the keys.
 #include <type_traits>
 
 #include "kernels.h"
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const int b = bh / a.Htot, hf = bh % a.Htot;
 
     int qs = 0, qe = a.Mq, ks = 0, ke = a.Mkv;
-    if (a.mask >= kMaskBlockDiag) {
+    if (a.packed) {
         const int32_t *skp = a.seqstart_k ? a.seqstart_k : a.seqstart_q;
         qs = min(max(a.seqstart_q[seq], 0), a.Mq);
         qe = min(max(a.seqstart_q[seq + 1], qs), a.Mq);
@@ -148,9 +149,20 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const int Lq = qe - qs, Lk = ke - ks;
     const int row0 = tile * BM;
     if (tile < 0 || row0 >= Lq) return;
-    const bool causal = (a.mask == kMaskCausal || a.mask == kMaskBlockDiagCausal);
-    const int nkeys = causal ? min(Lk, row0 + BM) : Lk;
-    const int ntiles = (nkeys + BN - 1) / BN;
+    // Visible keys of local row i: [lo(i), hi(i)] = [i + shift - wl, i + shift + wr] within [0, Lk),
+    // both non-decreasing in i (64-bit: shift and the unbounded extents reach 2^31).
+    const int64_t shift = a.bottom_right ? (int64_t)Lk - Lq : 0;
+    auto clampk = [&](int64_t x, int64_t lo_, int64_t hi_) { return (int)(x < lo_ ? lo_ : (x > hi_ ? hi_ : x)); };
+    const int row_last = min(row0 + BM, Lq) - 1;
+    const int kbeg = clampk((int64_t)row0 + shift - a.wl, 0, Lk);
+    const int kend = clampk((int64_t)row_last + shift + a.wr + 1, 0, Lk);
+    // tiles [tb, te) hold every visible key; [ua, ub) need no mask for any row of the workgroup
+    const int tb = kbeg / BN;
+    const int te = kend > kbeg ? (kend + BN - 1) / BN : tb;
+    int ua = (clampk((int64_t)row_last + shift - a.wl, 0, Lk) + BN - 1) / BN;
+    int ub = clampk((int64_t)row0 + shift + a.wr + 1, 0, Lk) / BN;
+    ua = min(max(ua, tb), te);
+    ub = min(max(ub, ua), te);
 
     const __bf16 *qp = (const __bf16 *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin) + (int64_t)qs * a.sq.m;
     const __bf16 *kp = (const __bf16 *)a.k + (int64_t)b * a.sk.b + head_offset(a.sk, hf, a.Hin) + (int64_t)ks * a.sk.m;
@@ -171,7 +183,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     auto issue = [&](int t) __attribute__((always_inline)) {
         const int kt0 = t * BN;
         const int nvalid = min(BN, Lk - kt0);
-        const unsigned st = smem_base + (t % STAGES) * TILE_BYTES;
+        const unsigned st = smem_base + ((t - tb) % STAGES) * TILE_BYTES;
         const i32x4 kr = make_rsrc(kp + (int64_t)kt0 * a.sk.m, (nvalid - 1) * kstride + ROWB);
         const i32x4 vr = make_rsrc(vp + (int64_t)kt0 * a.sv.m, (nvalid - 1) * vstride + ROWB);
 #pragma unroll
@@ -183,6 +195,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     // ---- Q^T fragments (B operand), resident for the whole kernel
     const int wrow0 = row0 + wave * 32;  // first local row of this wave
     const int qrow = wrow0 + l32;        // this lane's query row (local to the sequence)
+    const int klo = clampk((int64_t)qrow + shift - a.wl, 0, Lk);       // this row's visible keys
+    const int khi = clampk((int64_t)qrow + shift + a.wr, -1, Lk - 1);  // (empty when khi < klo)
     float c = a.scale_log2;
     const unsigned qflip = c < 0.f ? 0x80008000u : 0u;  // negative scale: negate q, keep c > 0
     c = fabsf(c);
@@ -223,17 +237,20 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     float m_ref = -INFINITY, l_run = 0.f;
 
     // One 64-key tile: S^T, mask (MASKED only), online softmax, O^T update.
-    // STAGE_C >= 0 names the LDS stage at compile time (t % STAGES == STAGE_C), so every LDS
-    // offset becomes an instruction immediate; -1 computes it at run time.
+    // STAGE_C >= 0 names the LDS stage at compile time ((t - tb) % STAGES == STAGE_C), so every
+    // LDS offset becomes an instruction immediate; -1 computes it at run time.
     auto step = [&](int t, auto masked_tag, auto stage_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         constexpr int STAGE_C = decltype(stage_tag)::value;
-        const int soff = (STAGE_C >= 0 ? STAGE_C : t % STAGES) * TILE_BYTES;
+        const int soff = (STAGE_C >= 0 ? STAGE_C : (t - tb) % STAGES) * TILE_BYTES;
         const int kt0 = t * BN;
-        if (t + 1 < ntiles) wait_barrier<2 * ROUNDS>();
+        if (t + 1 < te) wait_barrier<2 * ROUNDS>();
         else wait_barrier<0>();
-        if (t + 2 < ntiles) issue(t + 2);
-        if (MASKED && causal && kt0 > wrow0 + 31) return;  // every key of the tile is above this wave's rows
+        if (t + 2 < te) issue(t + 2);
+        // the whole tile lies before or after every window of this wave's 32 rows
+        if (MASKED && ((int64_t)kt0 + BN - 1 < (int64_t)wrow0 + shift - a.wl ||
+                       (int64_t)kt0 > (int64_t)wrow0 + 31 + shift + a.wr))
+            return;
         const unsigned char LDS_AS *st = (const unsigned char LDS_AS *)smem + soff;
 
         // S^T = K Q^T for two 32-key blocks
@@ -249,8 +266,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kt0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                if (key >= Lk || (causal && key > qrow)) sa[r] = -INFINITY;
-                if (key + 32 >= Lk || (causal && key + 32 > qrow)) sb[r] = -INFINITY;
+                if (key < klo || key > khi) sa[r] = -INFINITY;
+                if (key + 32 < klo || key + 32 > khi) sb[r] = -INFINITY;
             }
         }
         // row maximum of the raw scores (c > 0), pairwise to keep dependency chains short
@@ -266,9 +283,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         // raise the reference only when the row max grows by more than the threshold
         const bool up = mx > m_ref + kRescaleThreshold;
         if (__builtin_amdgcn_ballot_w64(up)) {
-            const float m_new = up ? mx : m_ref;
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-            m_ref = m_new;
+            // lanes that keep their reference scale by exactly 1 (m_ref may still be -inf there)
+            const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
+            m_ref = up ? mx : m_ref;
             l_run *= alpha;
 #pragma unroll
             for (int i = 0; i < MB; ++i)
@@ -308,23 +325,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         }
     };
 
-    // Tiles before `nfull` need no mask for any wave of the workgroup: keys all below the
-    // workgroup's first row (causal) and all inside the key range.
-    const int nfull = min(causal ? row0 / BN : ntiles, Lk / BN);
-    if (ntiles > 0) issue(0);
-    if (ntiles > 1) issue(1);
+    if (tb < te) issue(tb);
+    if (tb + 1 < te) issue(tb + 1);
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using SR = std::integral_constant<int, -1>;
-    int t = 0;
-    for (; t + STAGES <= nfull; t += STAGES) {
+    int t = tb;
+    for (; t < ua; ++t) step(t, std::true_type{}, SR{});  // left edge of the windows
+    for (; t < ub && (t - tb) % STAGES != 0; ++t) step(t, std::false_type{}, SR{});
+    for (; t + STAGES <= ub; t += STAGES) {
         step(t, std::false_type{}, S0{});
         step(t + 1, std::false_type{}, S1{});
         step(t + 2, std::false_type{}, S2{});
     }
-    for (; t < nfull; ++t) step(t, std::false_type{}, SR{});
-    for (; t < ntiles; ++t) step(t, std::true_type{}, SR{});
+    for (; t < ub; ++t) step(t, std::false_type{}, SR{});
+    for (; t < te; ++t) step(t, std::true_type{}, SR{});  // diagonal / right edge / key tail
 
     // ---- normalise and store
     const float l_tot = pair_sum(l_run);

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(NWV * 64) void fwd_f32_kernel(FwdArgs a) {
     const int b = bh / a.Htot, hf = bh % a.Htot;
 
     int qs = 0, qe = a.Mq, kst = 0, ke = a.Mkv;
-    if (a.mask >= kMaskBlockDiag) {
+    if (a.packed) {
         const int32_t *skp = a.seqstart_k ? a.seqstart_k : a.seqstart_q;
         qs = min(max(a.seqstart_q[seq], 0), a.Mq);
         qe = min(max(a.seqstart_q[seq + 1], qs), a.Mq);
@@ -51,14 +51,20 @@ __global__ __launch_bounds__(NWV * 64) void fwd_f32_kernel(FwdArgs a) {
     const int Lq = qe - qs, Lk = ke - kst;
     const int row0 = tile * BM;
     if (tile < 0 || row0 >= Lq) return;
-    const bool causal = (a.mask == kMaskCausal || a.mask == kMaskBlockDiagCausal);
-    const int nkeys = causal ? min(Lk, row0 + BM) : Lk;
+    // visible keys of local row i: [i + shift - wl, i + shift + wr] within [0, Lk)
+    const int64_t shift = a.bottom_right ? (int64_t)Lk - Lq : 0;
+    auto clampk = [&](int64_t x, int64_t lo_, int64_t hi_) { return (int)(x < lo_ ? lo_ : (x > hi_ ? hi_ : x)); };
+    const int row_last = min(row0 + BM, Lq) - 1;
+    const int kbeg = clampk((int64_t)row0 + shift - a.wl, 0, Lk);
+    const int kend = max(kbeg, clampk((int64_t)row_last + shift + a.wr + 1, 0, Lk));
 
     const float *qp = (const float *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin) + (int64_t)qs * a.sq.m;
     const float *kp = (const float *)a.k + (int64_t)b * a.sk.b + head_offset(a.sk, hf, a.Hin) + (int64_t)kst * a.sk.m;
     const float *vp = (const float *)a.v + (int64_t)b * a.sv.b + head_offset(a.sv, hf, a.Hin) + (int64_t)kst * a.sv.m;
 
     const int qrow = row0 + lane;
+    const int klo = clampk((int64_t)qrow + shift - a.wl, 0, Lk);
+    const int khi = clampk((int64_t)qrow + shift + a.wr, -1, Lk - 1);
     float q[KD];
 #pragma unroll
     for (int d = 0; d < KD; ++d) q[d] = (qrow < Lq && d < a.K) ? qp[(int64_t)qrow * a.sq.m + d] : 0.f;
@@ -71,20 +77,20 @@ __global__ __launch_bounds__(NWV * 64) void fwd_f32_kernel(FwdArgs a) {
     float *ks_ = smem + wave * TILE_FLOATS;  // [TB][KD]
     float *vs_ = ks_ + TB * KD;              // [TB][KVD]
 
-    const int rounds = (nkeys + NWV * TB - 1) / (NWV * TB);
+    const int rounds = (kend - kbeg + NWV * TB - 1) / (NWV * TB);
     for (int it = 0; it < rounds; ++it) {
-        const int kt0 = (it * NWV + wave) * TB;  // this wave's tile
+        const int kt0 = kbeg + (it * NWV + wave) * TB;  // this wave's tile
         __syncthreads();                          // previous tile fully read
         for (int idx = lane; idx < TB * KD; idx += 64) {
             const int r = idx / KD, d = idx % KD, j = kt0 + r;
-            ks_[idx] = (j < nkeys && d < a.K) ? kp[(int64_t)j * a.sk.m + d] : 0.f;
+            ks_[idx] = (j < kend && d < a.K) ? kp[(int64_t)j * a.sk.m + d] : 0.f;
         }
         for (int idx = lane; idx < TB * KVD; idx += 64) {
             const int r = idx / KVD, d = idx % KVD, j = kt0 + r;
-            vs_[idx] = (j < nkeys && d < a.Kv) ? vp[(int64_t)j * a.sv.m + d] : 0.f;
+            vs_[idx] = (j < kend && d < a.Kv) ? vp[(int64_t)j * a.sv.m + d] : 0.f;
         }
         __syncthreads();
-        if (kt0 >= nkeys) continue;
+        if (kt0 >= kend) continue;
 
         float s[TB];
         float mt = -INFINITY;
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(NWV * 64) void fwd_f32_kernel(FwdArgs a) {
             }
             const int key = kt0 + j;
             float x = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * c;
-            if (key >= nkeys || (causal && key > qrow)) x = -INFINITY;
+            if (key < klo || key > khi) x = -INFINITY;
             s[j] = x;
             mt = fmaxf(mt, x);
         }

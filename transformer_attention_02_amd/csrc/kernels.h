@@ -18,7 +18,9 @@ __host__ __device__ inline int64_t head_offset(const Strides &s, int hf, int Hin
     return (int64_t)(hf / Hin) * s.g + (int64_t)(hf % Hin) * s.h;
 }
 
-enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskBlockDiag = 2, kMaskBlockDiagCausal = 3 };
+// "Unbounded" window extent; row/key indices stay below 2^31, so i + shift +- kWinInf
+// is evaluated in 64-bit arithmetic.
+constexpr int kWinInf = 1 << 30;
 
 // Forward / partial attention over one key range per (batch, head).
 struct FwdArgs {
@@ -28,7 +30,12 @@ struct FwdArgs {
     Strides sq, sk, sv, so;
     int B, Mq, Mkv, Htot, Hin, K, Kv;
     float scale_log2;    // scale * log2(e): scores are kept in base-2 units
-    int mask;
+    // Visible keys of local row i in a sequence of Lq rows and Lk keys:
+    //   [i + shift - wl, i + shift + wr] intersected with [0, Lk),
+    //   shift = bottom_right ? Lk - Lq : 0; kWinInf = unbounded.
+    int packed;          // per-sequence blocks from seqstart_q / seqstart_k
+    int bottom_right;
+    int wl, wr;
     const int32_t *seqstart_q, *seqstart_k;  // device prefix sums, packed sequences only
     int nseq;            // 1 when not packed
     int max_seqlen_q;    // rows covered per sequence (Mq when not packed)
