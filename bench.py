@@ -7,7 +7,7 @@ H=32, K=Kv=128 (the pages' Quick-start shape), inputs resident in HBM.  The
 headline value is its throughput in TFLOP/s, counting 4*B*H*M*M*K flops halved
 for the causal mask.  The other rows of the path are timed after it and
 reported under "rows": split-KV decode (B=16, Mkv=32768, H=32, 64 chunks;
-GB/s of K+V), the packed GQA causal prefill (8 sequences, lengths U[256, 4096]),
+GB/s of K+V) on contiguous and on paged caches, the packed GQA causal prefill (8 sequences, lengths U[256, 4096]),
 a causal sliding window of 1024 keys over [2, 8192, 32, 128], the 2- and 8-way
 partial+merge of Mq=128/Mkv=1024/H=16, and the fp32 tiny case.
 Every figure is timed with HIP events on the stream the kernels run on; each call is
@@ -206,6 +206,20 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_call": kv_bytes,
                          "note": "algorithmic bytes = K+V once; time covers both launches"}}
+        # the same cache as 8192 pages of 64 rows in a random order (PagedBlockDiagonalPaddedKeysMask form)
+        page = 64
+        perm = np.random.Generator(np.random.PCG64(7)).permutation(B * Mkv // page).astype(np.int32)
+        tables = torch.from_numpy(perm.reshape(B, Mkv // page)).to("cuda")
+        lens = torch.full((B,), Mkv, dtype=torch.int32, device="cuda")
+        ms_p = timed(A.prepare_decode_paged(qd, kd.view(1, B * Mkv, H, D), vd.view(1, B * Mkv, H, D), lens, S, Mkv, ws,
+                                            od, ld, block_tables=tables, page_size=page), 20, 3, torch)
+        gbs_p = kv_bytes / (ms_p * 1e-3) / 1e9
+        log(f"paged decode page=64: {ms_p * 1e3:.1f} us/call, {gbs_p:.0f} GB/s")
+        result["rows"]["decode_paged"] = {
+            "workload": "the decode cache as 8192 pages of 64 rows, random page order (block table), 64 chunks",
+            "ms_per_call": round(ms_p, 5), "value": round(gbs_p, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbs_p, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs_p / PEAK_HBM_GBS, 4), "bytes_per_call": kv_bytes}}
         del qd, kd, vd, ws, od, ld
         torch.cuda.empty_cache()
 

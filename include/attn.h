@@ -182,6 +182,29 @@ attn_status attn_decode_splitkv(const attn_tensor *q, const attn_tensor *k, cons
                                 size_t workspace_bytes, const attn_tensor *out, float *lse,
                                 attn_stream_t stream);
 
+/* Split-KV decode against a KV cache ("Attention - Biases & masks": BlockDiagonalPaddedKeysMask
+ * and PagedBlockDiagonalPaddedKeysMask, one query per sequence; "MSLK Kernel Library --
+ * Complete Reference", Glossary "paged KV": cache rows addressed through a block table
+ * and a fixed page size).
+ *   q [B, 1, (G,) H, D]; seqlens: DEVICE int32 [B], keys held by each sequence.
+ *   block_tables NULL: k/v are padded lanes [B, cap, (G,) H, D], sequence b owns keys
+ *     0 .. seqlens[b]-1 of its lane (cap = k's row count).
+ *   block_tables non-NULL: DEVICE int32 [B, max_blocks_per_seq] (row-major) of page
+ *     numbers; k/v are the cache [1, num_pages * page_size, (G,) H, D]; key j of sequence
+ *     b is cache row block_tables[b][j / page_size] * page_size + j % page_size
+ *     (cap = max_blocks_per_seq * page_size).
+ *   max_seqlen_k in [0, cap] bounds every seqlens[b]; the keys are cut into num_splits
+ *     chunks of ceil(max_seqlen_k / num_splits), so shorter sequences have empty chunks.
+ *   Device metadata is not read by the host: seqlens are clamped to [0, cap] and page
+ *   numbers to the cache, so bad metadata gives unspecified values, never an
+ *   out-of-bounds access; keys past num_splits chunks are not seen.
+ *   Workspace, out, lse, scale and errors as in attn_decode_splitkv. */
+attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                      const int32_t *seqlens, const int32_t *block_tables,
+                                      int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                      int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                                      const attn_tensor *out, float *lse, attn_stream_t stream);
+
 /* Reason for the last non-OK status returned on this thread ("" if none). */
 const char *attn_last_error(void);
 

@@ -39,7 +39,8 @@ def maxerr(a, b) -> float:
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    d = np.where(both_inf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):
+        d = np.where(both_inf, 0.0, np.abs(a - b))
     return float(np.nanmax(np.where(np.isnan(d), np.inf, d))) if d.size else 0.0
 
 

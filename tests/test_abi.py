@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd", "attn_partial", "attn_fwd_ex", "attn_partial_ex", "attn_merge",
-                                           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_last_error"])
+                                           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_paged",
+                                           "attn_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -204,3 +205,23 @@ def test_windowed_masks_need_the_ex_entry_point_and_valid_windows():
     assert fwd_ex(q, k, v, o, A.AttnMask(8, 4, 0, 0)) == A.ATTN_ERR_INVALID_ARGUMENT  # packed kind, no varlen
     assert "varlen" in A.attn_last_error()
     assert fwd_ex(q, k, v, o, A.AttnMask(5, 0, 0, 0), fn=A._lib.attn_partial_ex) == A.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_paged_decode_rejects():
+    B, H, D, S = 4, 8, 128, 4
+    need = A.attn_decode_workspace_bytes(B, H, D, S)
+    q, o = tensor([B, 1, H, D]), tensor([B, 1, H, D])
+    cache = tensor([1, 64 * 16, H, D])
+
+    def call(k=cache, seqlens=FAKE, bt=FAKE, mb=8, page=16, mx=128, wsb=need):
+        return A._lib.attn_decode_splitkv_paged(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.c_void_p(seqlens),
+                                                ctypes.c_void_p(bt) if bt else None, mb, page, mx, S, float("nan"),
+                                                ctypes.c_void_p(FAKE * 256), wsb, ctypes.byref(o), None, None)
+    assert call(seqlens=0) == A.ATTN_ERR_INVALID_ARGUMENT and "seqlens" in A.attn_last_error()
+    assert call(page=0) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(page=48) == A.ATTN_ERR_INVALID_ARGUMENT and "whole number of pages" in A.attn_last_error()
+    assert call(mx=8 * 16 + 1) == A.ATTN_ERR_INVALID_ARGUMENT and "max_seqlen_k" in A.attn_last_error()
+    assert call(k=tensor([2, 64 * 16, H, D])) == A.ATTN_ERR_INVALID_ARGUMENT and "batch 1" in A.attn_last_error()
+    assert call(wsb=need - 1) == A.ATTN_ERR_WORKSPACE_TOO_SMALL
+    lanes = tensor([B, 300, H, D])
+    assert call(k=lanes, bt=0, mx=301) == A.ATTN_ERR_INVALID_ARGUMENT   # padded lanes: max_seqlen_k <= lane capacity

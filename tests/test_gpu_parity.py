@@ -326,3 +326,70 @@ def test_windowed_partial_and_merge(A):
     torch.cuda.synchronize()
     oo, ol = run_oracle(qh, kh[:, 256:], vh[:, 256:], 7, "bf16", window=100)
     check(po, pl, oo, ol, TOL_BF16_OUT, TOL_LSE, "partial window")
+
+
+# ------------------------------------------------------------------ KV-cache decode: padded lanes and pages
+
+def _gather(cache_h, table, page, n):
+    """Host copy of the first n logical keys of one sequence of a paged cache [1, P*page, ...]."""
+    rows = [table[j // page] * page + j % page for j in range(n)]
+    return cache_h[:, rows]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_padded_lanes(A, dtype):
+    tol_o, tol_l = (TOL_BF16_OUT, TOL_LSE) if dtype == "bf16" else (TOL_F32, TOL_F32)
+    B, cap, H, D, S = 5, 700, 4, 128, 7
+    lens = np.array([0, 1, 333, 700, 64], dtype=np.int32)
+    say(f"case: decode padded lanes {dtype} lens={list(lens)}")
+    qh, kh, vh = synth.qkv(1000, (B, 1, H, D), (B, cap, H, D), (B, cap, H, D), dtype)
+    out, lse = A.attn_decode_splitkv_paged(dev(qh, dtype), dev(kh, dtype), dev(vh, dtype),
+                                           torch.from_numpy(lens).cuda(), S, int(lens.max()), scale=0.07)
+    torch.cuda.synchronize()
+    for b in range(B):
+        oo, ol = run_oracle(qh[b:b + 1], kh[b:b + 1, :lens[b]], vh[b:b + 1, :lens[b]], 0, dtype, scale=0.07)
+        check(out[b:b + 1], lse[b:b + 1], oo, ol, tol_o, tol_l, f"lane {b} len={lens[b]}")
+
+
+@pytest.mark.parametrize("dtype,page", [("bf16", 16), ("bf16", 64), ("f32", 16)])
+def test_decode_paged_cache(A, dtype, page):
+    tol_o, tol_l = (TOL_BF16_OUT, TOL_LSE) if dtype == "bf16" else (TOL_F32, TOL_F32)
+    B, H, D, S, P, maxb = 3, 4, 64 if dtype == "f32" else 128, 5, 100, 20
+    rng = np.random.Generator(np.random.PCG64(1001 + page))
+    tables = rng.permutation(P)[:B * maxb].reshape(B, maxb).astype(np.int32)
+    lens = np.array([maxb * page, 37, 0], dtype=np.int32)
+    say(f"case: decode paged {dtype} page={page} lens={list(lens)}")
+    qh, kh, vh = synth.qkv(1002, (B, 1, H, D), (1, P * page, H, D), (1, P * page, H, D), dtype)
+    out, lse = A.attn_decode_splitkv_paged(dev(qh, dtype), dev(kh, dtype), dev(vh, dtype),
+                                           torch.from_numpy(lens).cuda(), S, int(lens.max()),
+                                           block_tables=torch.from_numpy(tables).cuda(), page_size=page)
+    torch.cuda.synchronize()
+    for b in range(B):
+        kb, vb = _gather(kh, tables[b], page, lens[b]), _gather(vh, tables[b], page, lens[b])
+        oo, ol = run_oracle(qh[b:b + 1], kb, vb, 0, dtype)
+        check(out[b:b + 1], lse[b:b + 1], oo, ol, tol_o, tol_l, f"seq {b} len={lens[b]}")
+
+
+def test_decode_paged_full_size(A, decode_inputs):
+    """The decode workload's cache as 8192 pages of 64 rows in a random order: sampled (b, h) vs the oracle."""
+    say("case: paged decode full size, page 64, 64 splits")
+    qh, kh, vh = decode_inputs
+    B, Mkv, H, D, page = 16, 32768, 32, 128, 64
+    P = B * Mkv // page
+    perm = np.random.Generator(np.random.PCG64(1003)).permutation(P).astype(np.int32)
+    tables = perm.reshape(B, Mkv // page)
+    q = dev(qh, "bf16")
+    kc = dev(kh, "bf16").view(1, B * Mkv, H, D)
+    vc = dev(vh, "bf16").view(1, B * Mkv, H, D)
+    lens = torch.full((B,), Mkv, dtype=torch.int32, device="cuda")
+    out, lse = A.attn_decode_splitkv_paged(q, kc, vc, lens, 64, Mkv, block_tables=torch.from_numpy(tables).cuda(),
+                                           page_size=page)
+    torch.cuda.synchronize()
+    kflat, vflat = kh.reshape(1, B * Mkv, H, D), vh.reshape(1, B * Mkv, H, D)
+    for b, h in [(0, 3), (9, 30)]:
+        kb = _gather(kflat[:, :, h:h + 1], tables[b], page, Mkv)
+        vb = _gather(vflat[:, :, h:h + 1], tables[b], page, Mkv)
+        oo, ol = run_oracle(qh[b:b + 1, :, h:h + 1], kb, vb, 0, "bf16")
+        check(out[b:b + 1, :, h:h + 1], lse[b:b + 1, h:h + 1], oo, ol, TOL_BF16_OUT, TOL_LSE, f"b={b} h={h}")
+    del q, kc, vc
+    torch.cuda.empty_cache()

@@ -67,6 +67,10 @@ _lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.attn_decode_splitkv.argtypes = [_T, _T, _T, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
                                      _T, ctypes.c_void_p, ctypes.c_void_p]
 _lib.attn_decode_splitkv.restype = ctypes.c_int
+_lib.attn_decode_splitkv_paged.argtypes = [_T, _T, _T, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                           ctypes.c_void_p, ctypes.c_size_t, _T, ctypes.c_void_p, ctypes.c_void_p]
+_lib.attn_decode_splitkv_paged.restype = ctypes.c_int
 _lib.attn_last_error.argtypes = []
 _lib.attn_last_error.restype = ctypes.c_char_p
 
@@ -261,6 +265,42 @@ def attn_decode_splitkv(q, k, v, num_splits, scale=None, workspace=None, out=Non
                                     int(num_splits), _scale(scale), _ptr(workspace), workspace.numel(),
                                     ctypes.byref(desc(out)), _ptr(lse), _stream(stream)))
     return out, lse
+
+
+def _paged_args(q, k, v, seqlens, block_tables, page_size, max_seqlen_k, num_splits, scale, workspace, out, lse,
+                stream):
+    ds = [desc(q), desc(k), desc(v), desc(out)]
+    mb = block_tables.shape[1] if block_tables is not None else 0
+    args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), _ptr(seqlens), _ptr(block_tables),
+            int(mb), int(page_size or 0), int(max_seqlen_k), int(num_splits), _scale(scale), _ptr(workspace),
+            workspace.numel(), ctypes.byref(ds[3]), _ptr(lse), _stream(stream))
+    return args, ds
+
+
+def attn_decode_splitkv_paged(q, k, v, seqlens, num_splits, max_seqlen_k, block_tables=None, page_size=None,
+                              scale=None, workspace=None, out=None, lse=True, stream=None):
+    """Split-KV decode against padded lanes (block_tables None) or a paged cache: returns (out, lse or None)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty((q.shape[0], _htot(q), 1), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    need = attn_decode_workspace_bytes(q.shape[0], _htot(q), q.shape[-1], num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    args, _keep = _paged_args(q, k, v, seqlens, block_tables, page_size, max_seqlen_k, num_splits, scale, workspace,
+                              out, lse, stream)
+    _check(_lib.attn_decode_splitkv_paged(*args))
+    return out, lse
+
+
+def prepare_decode_paged(q, k, v, seqlens, num_splits, max_seqlen_k, workspace, out, lse, block_tables=None,
+                         page_size=None, scale=None, stream=None) -> Prepared:
+    """attn_decode_splitkv_paged with every argument marshalled up front."""
+    args, ds = _paged_args(q, k, v, seqlens, block_tables, page_size, max_seqlen_k, num_splits, scale, workspace,
+                           out, lse, stream)
+    return Prepared(_lib.attn_decode_splitkv_paged, args, (ds, q, k, v, seqlens, block_tables, workspace, out, lse))
 
 
 def default_scale(K: int) -> float:

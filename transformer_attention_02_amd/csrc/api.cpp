@@ -336,10 +336,16 @@ size_t attn_decode_workspace_bytes(int64_t B, int64_t H_total, int64_t Kv, int32
     return align256(rows * (size_t)Kv * 4) + align256(rows * 4);
 }
 
-attn_status attn_decode_splitkv(const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
-                                int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
-                                const attn_tensor *ot, float *lse, attn_stream_t stream) {
-    const char *fn = "attn_decode_splitkv";
+}  // extern "C"
+
+namespace {
+
+// Shared validation and launches of the split-KV decode entry points.  Without block tables
+// k/v are [B, cap, (G,) H, D] lanes; with them k/v are the paged cache [1, pages * page_size, ...].
+attn_status decode(const char *fn, const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
+                   const int32_t *seqlens, const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t page_size,
+                   int32_t max_seqlen_k, int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                   const attn_tensor *ot, float *lse, attn_stream_t stream) {
     View q, k, v, o;
     attn_status st;
     if ((st = make_view(qt, "q", &q)) != ATTN_OK) return st;
@@ -350,7 +356,13 @@ attn_status attn_decode_splitkv(const attn_tensor *qt, const attn_tensor *kt, co
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out must share one dtype", fn);
     if (!same_heads(q, k) || !same_heads(q, v) || !same_heads(q, o))
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out must have the same rank and head axes", fn);
-    if (k.B != q.B || v.B != q.B || o.B != q.B) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: batch sizes differ", fn);
+    const bool paged = block_tables != nullptr;
+    if (o.B != q.B) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: batch sizes differ", fn);
+    if (paged) {
+        if (k.B != 1 || v.B != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: a paged cache has batch 1", fn);
+    } else if (k.B != q.B || v.B != q.B) {
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: batch sizes differ", fn);
+    }
     if (q.M != 1 || o.M != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: decode takes one query row (M == 1)", fn);
     if (v.M != k.M) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: k and v have different key counts", fn);
     if (k.D != q.D || v.D != q.D || o.D != q.D)
@@ -362,6 +374,25 @@ attn_status attn_decode_splitkv(const attn_tensor *qt, const attn_tensor *kt, co
     if (!(std::isnan(scale) || std::isfinite(scale)))
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: scale must be finite (or NaN for 1/sqrt(K))", fn);
     if (lse && ((uintptr_t)lse) % 4) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
+    int64_t cap = k.M;  // keys a sequence may hold
+    if (seqlens || paged) {
+        if (!seqlens || ((uintptr_t)seqlens) % 4)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: seqlens must be a 4-byte aligned device array", fn);
+        if (paged) {
+            if (((uintptr_t)block_tables) % 4)
+                return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block_tables must be 4-byte aligned", fn);
+            if (page_size < 1 || max_blocks_per_seq < 1)
+                return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: page_size and max_blocks_per_seq must be >= 1", fn);
+            if (k.M % page_size != 0 || k.M == 0)
+                return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: the cache must hold a whole number of pages", fn);
+            cap = (int64_t)max_blocks_per_seq * page_size;
+            if (cap > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "%s: sequences too long", fn);
+        }
+        if (max_seqlen_k < 0 || max_seqlen_k > cap)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: max_seqlen_k must be in [0, %lld]", fn, (long long)cap);
+    } else {
+        max_seqlen_k = (int32_t)k.M;
+    }
     const size_t need = attn_decode_workspace_bytes(q.B, htot(q), q.D, num_splits);
     if (q.B == 0 || htot(q) == 0) return ok();
     if (!workspace || ((uintptr_t)workspace) % 256)
@@ -384,11 +415,17 @@ attn_status attn_decode_splitkv(const attn_tensor *qt, const attn_tensor *kt, co
     d.Hin = (int)q.H;
     d.D = (int)q.D;
     d.S = num_splits;
-    d.chunk = (int)((k.M + num_splits - 1) / num_splits);
+    d.chunk = (int)(((int64_t)max_seqlen_k + num_splits - 1) / num_splits);
     const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)q.D) : (double)scale;
     d.scale_log2 = (float)(sc * 1.4426950408889634);
     d.ws_o = (float *)workspace;
     d.ws_lse = (float *)((char *)workspace + align256((size_t)rows * q.D * 4));
+    d.seqlens = seqlens;
+    d.block_tables = block_tables;
+    d.bt_stride = max_blocks_per_seq;
+    d.page_size = page_size;
+    d.num_pages = paged ? (int)(k.M / page_size) : 0;
+    d.cap = (int)cap;
     hipError_t e = attn::launch_decode_partials(d, q.dtype == ATTN_DTYPE_F32, (hipStream_t)stream);
     if (e != hipSuccess) return launch_status(e, fn);
 
@@ -413,6 +450,26 @@ attn_status attn_decode_splitkv(const attn_tensor *qt, const attn_tensor *kt, co
     m.chunk_f32 = 1;
     m.out_f32 = o.dtype == ATTN_DTYPE_F32;
     return launch_status(attn::launch_merge(m, (hipStream_t)stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode_splitkv(const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
+                                int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                                const attn_tensor *ot, float *lse, attn_stream_t stream) {
+    return decode("attn_decode_splitkv", qt, kt, vt, nullptr, nullptr, 0, 0, 0, num_splits, scale, workspace,
+                  workspace_bytes, ot, lse, stream);
+}
+
+attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                      const int32_t *seqlens, const int32_t *block_tables,
+                                      int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                      int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                                      const attn_tensor *out, float *lse, attn_stream_t stream) {
+    return decode("attn_decode_splitkv_paged", q, k, v, seqlens, block_tables, max_blocks_per_seq, page_size,
+                  max_seqlen_k, num_splits, scale, workspace, workspace_bytes, out, lse, stream);
 }
 
 }  // extern "C"

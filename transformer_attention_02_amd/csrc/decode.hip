@@ -15,7 +15,11 @@
 //     kept in LDS; phase 2 takes the exact max and the exponentials over the
 //     chunk (no per-key rescaling); phase 3 streams V and accumulates p v.
 //   * chunks longer than the LDS score buffer are cut into sub-chunks combined
-//     with the running-max rescale.
+//     with the running-max rescale;
+//   * KV-cache layouts ("Attention - Biases & masks": BlockDiagonalPaddedKeysMask,
+//     PagedBlockDiagonalPaddedKeysMask): per-sequence key counts on the device,
+//     and for a paged cache the physical row of every key of a sub-chunk is
+//     resolved once into LDS from the block table.
 // Output: the chunk's normalised fp32 output and its natural-log LSE; an empty
 // chunk gives 0 and -inf.
 #include <type_traits>
@@ -64,7 +68,10 @@ __device__ __forceinline__ float block_sum(float x, float *red) {
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-template <int HD, bool F32>
+// MODE 0: k/v [B, Mkv, ...], every sequence has Mkv keys.  MODE 1: padded lanes [B, cap, ...] with
+// seqlens[b] valid keys.  MODE 2: paged cache [1, num_pages * page_size, ...]; key j of sequence b is
+// row block_tables[b][j / page_size] * page_size + j % page_size (page numbers clamped to the cache).
+template <int HD, bool F32, int MODE>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     constexpr int EPL = F32 ? 4 : 8;   // elements per 16-byte load
     constexpr int LPK = HD / EPL;      // lanes per key row
@@ -74,19 +81,22 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     __shared__ float sc[SUB];
     __shared__ float acc_s[KPP][HD];
     __shared__ float red[4];
+    __shared__ int rows_s[MODE == 2 ? SUB : 1];  // physical cache row of each key of the sub-chunk
 
     int id = blockIdx.x;
     const int hf = id % a.Htot;
     id /= a.Htot;
     const int b = id % a.B;
     const int s = id / a.B;
-    const int j0 = min(a.Mkv, s * a.chunk);
-    const int j1 = min(a.Mkv, j0 + a.chunk);
+    const int Lb = MODE == 0 ? a.Mkv : min(max(a.seqlens[b], 0), a.cap);
+    const int j0 = min(Lb, s * a.chunk);
+    const int j1 = min(Lb, j0 + a.chunk);
+    const int64_t kb = MODE == 2 ? 0 : (int64_t)b * a.sk.b, vb = MODE == 2 ? 0 : (int64_t)b * a.sv.b;
 
     const int tid = threadIdx.x, g = tid / LPK, cl = tid % LPK;
     const T *qp = (const T *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin);
-    const T *kp = (const T *)a.k + (int64_t)b * a.sk.b + head_offset(a.sk, hf, a.Hin) + cl * EPL;
-    const T *vp = (const T *)a.v + (int64_t)b * a.sv.b + head_offset(a.sv, hf, a.Hin) + cl * EPL;
+    const T *kp = (const T *)a.k + kb + head_offset(a.sk, hf, a.Hin) + cl * EPL;
+    const T *vp = (const T *)a.v + vb + head_offset(a.sv, hf, a.Hin) + cl * EPL;
 
     float qv[EPL];
     unpack<F32>(*(const u32x4 *)(qp + cl * EPL), qv);
@@ -100,13 +110,23 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 
     for (int sub0 = j0; sub0 < j1; sub0 += SUB) {
         const int n = min(SUB, j1 - sub0);
+        if (MODE == 2) {
+            const int32_t *bt = a.block_tables + (int64_t)b * a.bt_stride;
+            for (int i = tid; i < n; i += NT) {
+                const int j = sub0 + i;
+                const int pg = min(max(bt[j / a.page_size], 0), a.num_pages - 1);
+                rows_s[i] = pg * a.page_size + j % a.page_size;
+            }
+            __syncthreads();
+        }
         // phase 1: scores
         for (int p = 0; p < n; p += KPP * UNROLL) {
             u32x4 w[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int r = p + u * KPP + g;
-                w[u] = r < n ? *(const u32x4 *)(kp + (int64_t)(sub0 + r) * a.sk.m) : u32x4{0, 0, 0, 0};
+                const int64_t row = MODE == 2 ? (r < n ? rows_s[r] : 0) : sub0 + r;
+                w[u] = r < n ? *(const u32x4 *)(kp + row * a.sk.m) : u32x4{0, 0, 0, 0};
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
@@ -145,7 +165,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int r = p + u * KPP + g;
-                w[u] = r < n ? *(const u32x4 *)(vp + (int64_t)(sub0 + r) * a.sv.m) : u32x4{0, 0, 0, 0};
+                const int64_t row = MODE == 2 ? (r < n ? rows_s[r] : 0) : sub0 + r;
+                w[u] = r < n ? *(const u32x4 *)(vp + row * a.sv.m) : u32x4{0, 0, 0, 0};
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
@@ -174,20 +195,27 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     if (tid == 0) a.ws_lse[obase] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
-template <int HD, bool F32>
+template <int HD, bool F32, int MODE>
 hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
     const int64_t grid = (int64_t)a.S * a.B * a.Htot;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_kernel<HD, F32>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<HD, F32, MODE>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int HD, bool F32>
+hipError_t launch_mode(const DecodeArgs &a, hipStream_t stream) {
+    if (a.block_tables) return launch<HD, F32, 2>(a, stream);
+    if (a.seqlens) return launch<HD, F32, 1>(a, stream);
+    return launch<HD, F32, 0>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode_partials(const DecodeArgs &a, bool f32, hipStream_t stream) {
-    if (a.D == 128) return f32 ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
-    if (a.D == 64) return f32 ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+    if (a.D == 128) return f32 ? launch_mode<128, true>(a, stream) : launch_mode<128, false>(a, stream);
+    if (a.D == 64) return f32 ? launch_mode<64, true>(a, stream) : launch_mode<64, false>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -50,6 +50,10 @@ struct DecodeArgs {
     float scale_log2;
     float *ws_o;         // [S, B, Htot, D] fp32, normalised per chunk
     float *ws_lse;       // [S, B, Htot] fp32, natural log
+    // Per-sequence key counts (padded lanes or pages), both device arrays; null = Mkv keys each.
+    const int32_t *seqlens;       // [B], clamped to [0, cap]
+    const int32_t *block_tables;  // [B, bt_stride] page numbers, or null (lanes [B, cap, ...])
+    int bt_stride, page_size, num_pages, cap;
 };
 
 constexpr int kMaxChunks = 128;
