@@ -51,6 +51,10 @@ def _load():
         lib.oracle_merge.argtypes = [i64, i64, i64, i64, i64, dp, dp, dp, dp]
         lib.oracle_merge.restype = ctypes.c_int
         lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp8_e4m3.restype = ctypes.c_double
+        lib.oracle_dequant_fp8_rowwise.argtypes = [i64, i64, ctypes.c_void_p, dp, dp]
+        lib.oracle_dequant_fp8_rowwise.restype = None
         _lib = lib
     return _lib
 
@@ -124,6 +128,23 @@ def partial(q, k, v, j0: int, j1: int, mask: int = MASK_NONE, scale=None):
     """Attention over the key shard [j0, j1) alone (the shard is its own key sequence)."""
     return attention(q, k[:, j0:j1], v[:, j0:j1], mask=mask,
                      scale=(1.0 / math.sqrt(q.shape[3])) if scale is None else scale)
+
+
+def fp8_e4m3(code: int) -> float:
+    """Value of one FP8 E4M3 code (OCP FN variant)."""
+    return float(_load().oracle_fp8_e4m3(int(code) & 0xFF))
+
+
+def dequant_fp8_rowwise(codes, scale_shift):
+    """codes uint8 [..., D], scale_shift [..., 2] -> fp64 [..., D] = fp8(code) * scale + shift."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    ss = np.ascontiguousarray(scale_shift, dtype=np.float64)
+    assert ss.shape == codes.shape[:-1] + (2,)
+    D = codes.shape[-1]
+    rows = codes.size // D if D else 0
+    x = np.empty(codes.shape, dtype=np.float64)
+    _load().oracle_dequant_fp8_rowwise(rows, D, codes.ctypes.data, _dp(ss), _dp(x))
+    return x
 
 
 def chunk_bounds(Mkv: int, S: int):

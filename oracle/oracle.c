@@ -50,6 +50,12 @@
  *   M* = max_c lse_c,  L = M* + ln sum_c exp(lse_c - M*),
  *   out = sum_c exp(lse_c - L) out_c.   All chunks at -inf give 0 and -inf.
  *
+ * Quantised K/V caches ("Attention - operator protocol", InputsFp8: row or group
+ * quantised FP8 K/V with scale/shift metadata, read directly by the split-K decode
+ * backends): every stored key or value row r of one head holds D FP8 E4M3 codes and
+ * one (scale, shift) pair; its value is fp8(code) * scale + shift.  The attention is
+ * then the definition above applied to those values.
+ *
  * Layouts (all contiguous, fp64):
  *   q [B,Mq,H,K], k [B,Mkv,H,K], v [B,Mkv,H,Kv], out [B,Mq,H,Kv], lse [B,H,Mq].
  *   Packed sequences: B = 1, seqstart_q/seqstart_k are prefix sums [nseq+1].
@@ -188,6 +194,25 @@ int oracle_attention(int64_t B, int64_t Mq, int64_t Mkv, int64_t H, int64_t K, i
         free(ok);
     }
     return err;
+}
+
+/* FP8 E4M3 (OCP "FN" variant, the 8-bit float of MI355X): 1 sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits; exponent 0 holds subnormals m/8 * 2^-6; no infinities;
+ * S.1111.111 is NaN.  Largest finite magnitude 1.75 * 2^8 = 448. */
+double oracle_fp8_e4m3(uint8_t code) {
+    const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* Row-wise dequantisation of an FP8 K/V cache ("Attention - operator protocol" in the kernel
+ * reference, InputsFp8: row/group quantised FP8 caches with scale/shift metadata):
+ * x[r, d] = fp8(codes[r, d]) * ss[r, 0] + ss[r, 1] for `rows` rows of `D` values. */
+void oracle_dequant_fp8_rowwise(int64_t rows, int64_t D, const uint8_t *codes, const double *ss, double *x) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t d = 0; d < D; ++d) x[r * D + d] = oracle_fp8_e4m3(codes[r * D + d]) * ss[2 * r] + ss[2 * r + 1];
 }
 
 /* out_chunks [S,B,M,H,Kv], lse_chunks [S,B,H,M] -> out [B,M,H,Kv], lse [B,H,M]. */

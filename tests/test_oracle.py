@@ -391,3 +391,43 @@ def test_windowed_blockdiag_equals_per_sequence(oracle_mod, mask, single, win):
             os_, ls_ = oracle_mod.attention(q[:, a:b], k[:, c:d], v[:, c:d], mask=single, window=win)
         np.testing.assert_allclose(o[:, a:b], os_, atol=1e-13)
         np.testing.assert_allclose(l[:, :, a:b], ls_, atol=1e-13)
+
+
+# ---------------------------------------------------------------- FP8 E4M3 row-wise caches
+
+def test_fp8_e4m3_decoding_matches_torch_for_every_code(oracle_mod):
+    """All 256 codes against torch.float8_e4m3fn (an independent implementation of the format)."""
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle_mod.fp8_e4m3(c) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2  # S.1111.111
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+
+
+def test_fp8_e4m3_closed_forms(oracle_mod):
+    assert oracle_mod.fp8_e4m3(0x38) == 1.0          # exponent 7 = bias, mantissa 0
+    assert oracle_mod.fp8_e4m3(0x7E) == 448.0        # largest finite
+    assert oracle_mod.fp8_e4m3(0x01) == 2.0 ** -9    # smallest subnormal: 1/8 * 2^-6
+    assert oracle_mod.fp8_e4m3(0x08) == 2.0 ** -6    # smallest normal
+    assert oracle_mod.fp8_e4m3(0xC4) == -3.0         # -1.5 * 2^1
+    assert oracle_mod.fp8_e4m3(0x80) == 0.0 and math.copysign(1, oracle_mod.fp8_e4m3(0x80)) == -1
+
+
+def test_rowwise_dequant_is_affine_per_row(oracle_mod):
+    codes = synth.fp8_codes(3, 1, (2, 5, 3, 16))
+    ss = synth.scale_shift(3, 1, (2, 5, 3))
+    x = oracle_mod.dequant_fp8_rowwise(codes, ss)
+    base = np.vectorize(oracle_mod.fp8_e4m3)(codes)
+    np.testing.assert_array_equal(x, base * ss[..., :1].astype(np.float64) + ss[..., 1:].astype(np.float64))
+    # shift only: a row of zero codes dequantises to its shift
+    z = oracle_mod.dequant_fp8_rowwise(np.zeros((1, 4), np.uint8), np.array([[2.0, -0.5]]))
+    np.testing.assert_array_equal(z, np.full((1, 4), -0.5))
+
+
+def test_fp8_codes_avoid_nan_and_stay_in_range(oracle_mod):
+    codes = synth.fp8_codes(4, 0, (4096,))
+    vals = np.vectorize(oracle_mod.fp8_e4m3)(codes)
+    assert np.all(np.isfinite(vals)) and np.abs(vals).max() <= 15.0 and np.abs(vals).min() >= 2 ** -4
