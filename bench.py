@@ -7,7 +7,7 @@ H=32, K=Kv=128 (the pages' Quick-start shape), inputs resident in HBM.  The
 headline value is its throughput in TFLOP/s, counting 4*B*H*M*M*K flops halved
 for the causal mask.  The other rows of the path are timed after it and
 reported under "rows": split-KV decode (B=16, Mkv=32768, H=32, 64 chunks;
-GB/s of K+V) on contiguous and on paged caches, the packed GQA causal prefill (8 sequences, lengths U[256, 4096]),
+GB/s of K+V) on contiguous and on paged caches and on a row-wise FP8 cache, the packed GQA causal prefill (8 sequences, lengths U[256, 4096]),
 a causal sliding window of 1024 keys over [2, 8192, 32, 128], the 2- and 8-way
 partial+merge of Mq=128/Mkv=1024/H=16, and the fp32 tiny case.
 Every figure is timed with HIP events on the stream the kernels run on; each call is
@@ -78,12 +78,15 @@ def rocpd_summary(db_path):
                 print(f"| {cn} | {len(v)} | {sum(v) / len(v):.1f} | {grid} | {name} |")
 
 
-def kernel_source_digest():
-    """sha256 of the prefill kernel sources; HBM byte counters recorded for another digest are stale."""
+TRAFFIC_SOURCES = {"fwd": ("fwd_bf16.hip", "kernels.h"), "decode": ("decode.hip", "kernels.h")}
+
+
+def kernel_source_digest(kind="fwd"):
+    """sha256 of a kernel's sources; HBM byte counters recorded for another digest are stale."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in ("fwd_bf16.hip", "kernels.h"):
+    for f in TRAFFIC_SOURCES[kind]:
         with open(os.path.join(ROOT, "transformer_attention_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -96,7 +99,7 @@ def recorded_traffic(key):
         return None
     with open(path) as fh:
         rec = json.load(fh).get(key)
-    if not rec or rec.get("source_sha256") != kernel_source_digest():
+    if not rec or rec.get("source_sha256") != kernel_source_digest(rec.get("sources", "fwd")):
         return None
     return rec["fetch_kib"] * rec["fetch_scale"] * 1024 + rec["write_kib"] * rec["write_scale"] * 1024
 
@@ -105,11 +108,18 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def timed(fn, steps, warmup, torch):
-    """Average ms per call over `steps` calls after `warmup`, HIP events on the current stream."""
+def timed(fn, steps, warmup, torch, min_warmup_s=0.25):
+    """Average ms per call over `steps` calls after `warmup` calls and at least `min_warmup_s`
+    seconds of warm-up (the clocks settle after idle host-side set-up), HIP events on the
+    current stream."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_warmup_s:
+        for _ in range(max(1, warmup)):
+            fn()
+        torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(steps):
@@ -205,6 +215,7 @@ def main():
             "ms_per_call": round(ms_d, 5), "value": round(gbs, 1), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_call": kv_bytes,
+                         "traffic": recorded_traffic("decode bf16 16x32768x32x128 s64"),
                          "note": "algorithmic bytes = K+V once; time covers both launches"}}
         # the same cache as 8192 pages of 64 rows in a random order (PagedBlockDiagonalPaddedKeysMask form)
         page = 64
@@ -219,8 +230,31 @@ def main():
             "workload": "the decode cache as 8192 pages of 64 rows, random page order (block table), 64 chunks",
             "ms_per_call": round(ms_p, 5), "value": round(gbs_p, 1), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs_p, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs_p / PEAK_HBM_GBS, 4), "bytes_per_call": kv_bytes}}
-        del qd, kd, vd, ws, od, ld
+                         "frac": round(gbs_p / PEAK_HBM_GBS, 4), "bytes_per_call": kv_bytes,
+                         "traffic": recorded_traffic("decode bf16 paged 16x32768x32x128 page64 s64")}}
+        del kd, vd
+        torch.cuda.empty_cache()
+
+        # the same shape with a row-wise FP8 E4M3 cache: codes + one (scale, shift) fp16 pair per row and head
+        log("generating fp8 decode inputs ...")
+        k8 = torch.from_numpy(synth.fp8_codes(4, synth.TAG_K, (B, Mkv, H, D))).to("cuda").view(torch.float8_e4m3fn)
+        v8 = torch.from_numpy(synth.fp8_codes(4, synth.TAG_V, (B, Mkv, H, D))).to("cuda").view(torch.float8_e4m3fn)
+        kss = torch.from_numpy(synth.scale_shift(4, synth.TAG_K, (B, Mkv, H))).to("cuda")
+        vss = torch.from_numpy(synth.scale_shift(4, synth.TAG_V, (B, Mkv, H))).to("cuda")
+        ms_8 = timed(A.prepare_decode_fp8(qd, k8, v8, kss, vss, S, ws, od, ld), 20, 3, torch)
+        fp8_bytes = 2.0 * B * Mkv * H * (D + 4)
+        gbs_8 = fp8_bytes / (ms_8 * 1e-3) / 1e9
+        log(f"fp8 decode S=64: {ms_8 * 1e3:.1f} us/call, {gbs_8:.0f} GB/s")
+        result["rows"]["decode_fp8"] = {
+            "workload": "B=16 Mq=1 Mkv=32768 H=32 D=128, bf16 q, FP8 E4M3 K/V with per-row fp16 scale/shift, "
+                        "64 chunks of 512",
+            "ms_per_call": round(ms_8, 5), "value": round(gbs_8, 1), "unit": "GB/s",
+            "keys_per_s": round(B * Mkv * H / (ms_8 * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs_8, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs_8 / PEAK_HBM_GBS, 4), "bytes_per_call": fp8_bytes,
+                         "traffic": recorded_traffic("decode fp8 16x32768x32x128 s64"),
+                         "note": "algorithmic bytes = K+V codes and their metadata once"}}
+        del qd, k8, v8, kss, vss, ws, od, ld
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ packed GQA causal prefill

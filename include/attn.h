@@ -66,7 +66,13 @@ typedef enum {
     ATTN_ERR_LAUNCH = 4
 } attn_status;
 
-typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
+typedef enum {
+    ATTN_DTYPE_F32 = 0,
+    ATTN_DTYPE_BF16 = 1,
+    ATTN_DTYPE_FP8_E4M3 = 2, /* OCP E4M3 ("FN": bias 7, no infinities, S.1111.111 = NaN); K/V caches of
+                                attn_decode_splitkv_fp8 only */
+    ATTN_DTYPE_F16 = 3       /* IEEE half; the scale/shift metadata of attn_decode_splitkv_fp8 only */
+} attn_dtype;
 
 /* Masks ("Attention - Biases & masks" on the kernel reference page).  For a
  * (sequence of) Lq query rows and Lk keys, with local row i and local key j, the
@@ -204,6 +210,28 @@ attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k
                                       int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
                                       int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                       const attn_tensor *out, float *lse, attn_stream_t stream);
+
+/* Split-KV decode against a row-wise quantised FP8 K/V cache ("Attention - operator protocol",
+ * InputsFp8: row/group quantised FP8 K/V caches whose scale/shift metadata the split-K decode
+ * backends read directly; triton_splitk.FwOp: row-wise FP8 caches).  Stored row r of head h
+ * holds D codes and one (scale, shift) pair; its values are  fp8(code) * scale + shift,  and
+ * the result is that of attn_decode_splitkv / _paged on those values.
+ *   q [B, 1, (G,) H, D] bf16, D in {64, 128}.
+ *   k, v: ATTN_DTYPE_FP8_E4M3 caches laid out as in attn_decode_splitkv (seqlens and
+ *     block_tables both NULL: every sequence holds all of its lane), or as in
+ *     attn_decode_splitkv_paged (seqlens given: padded lanes; block_tables too: paged).
+ *   k_scale_shift, v_scale_shift: ATTN_DTYPE_F16, the shape of k with D replaced by 2,
+ *     stride-1 last axis and 4-byte aligned rows: (scale, shift) of every cache row and
+ *     head, i.e. one 32-bit word with the scale in its low half.
+ *   out [B, 1, (G,) H, D] bf16 or fp32; lse fp32 [B, H_total, 1] or NULL.
+ *   The codes and metadata are read as they are; NaN codes or metadata propagate.
+ *   Workspace, splits, scale, device-metadata handling and errors as in attn_decode_splitkv_paged. */
+attn_status attn_decode_splitkv_fp8(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                    const attn_tensor *k_scale_shift, const attn_tensor *v_scale_shift,
+                                    const int32_t *seqlens, const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                    int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                                    const attn_tensor *out, float *lse, attn_stream_t stream);
 
 /* Reason for the last non-OK status returned on this thread ("" if none). */
 const char *attn_last_error(void);

@@ -18,13 +18,13 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(attn_[a-z_]+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(attn_[a-z0-9_]+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd", "attn_partial", "attn_fwd_ex", "attn_partial_ex", "attn_merge",
                                            "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_paged",
-                                           "attn_last_error"])
+                                           "attn_decode_splitkv_fp8", "attn_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -225,3 +225,35 @@ def test_paged_decode_rejects():
     assert call(wsb=need - 1) == A.ATTN_ERR_WORKSPACE_TOO_SMALL
     lanes = tensor([B, 300, H, D])
     assert call(k=lanes, bt=0, mx=301) == A.ATTN_ERR_INVALID_ARGUMENT   # padded lanes: max_seqlen_k <= lane capacity
+
+
+def test_fp8_decode_rejects():
+    B, H, D, S, M = 4, 8, 128, 4, 256
+    need = A.attn_decode_workspace_bytes(B, H, D, S)
+    q, o = tensor([B, 1, H, D]), tensor([B, 1, H, D])
+    k8 = tensor([B, M, H, D], A.ATTN_DTYPE_FP8_E4M3)
+    ss = tensor([B, M, H, 2], A.ATTN_DTYPE_F16, data=FAKE + 4)  # 4-byte alignment suffices for metadata
+
+    def call(qq=q, k=k8, kss=ss, vss=ss, oo=o, seqlens=0, bt=0, mx=0):
+        return A._lib.attn_decode_splitkv_fp8(ctypes.byref(qq), ctypes.byref(k), ctypes.byref(k), ctypes.byref(kss),
+                                              ctypes.byref(vss), ctypes.c_void_p(seqlens) if seqlens else None,
+                                              ctypes.c_void_p(bt) if bt else None, 8, 32, mx, S, float("nan"),
+                                              ctypes.c_void_p(FAKE * 256), need, ctypes.byref(oo), None, None)
+    assert call(k=tensor([B, M, H, D])) == A.ATTN_ERR_INVALID_ARGUMENT and "dtype" in A.attn_last_error()
+    assert call(kss=tensor([B, M, H, 2], A.ATTN_DTYPE_F32)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(vss=tensor([B, M, H, 4], A.ATTN_DTYPE_F16)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert "scale/shift" in A.attn_last_error()
+    assert call(kss=tensor([B, M - 1, H, 2], A.ATTN_DTYPE_F16)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(kss=tensor([B, M, H, 2], A.ATTN_DTYPE_F16, data=FAKE + 2)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(qq=tensor([B, 1, H, D], A.ATTN_DTYPE_F32)) == A.ATTN_ERR_INVALID_ARGUMENT and "bf16" in A.attn_last_error()
+    assert call(bt=FAKE) == A.ATTN_ERR_INVALID_ARGUMENT and "seqlens" in A.attn_last_error()
+    assert call(k=tensor([B, M, H, 96], A.ATTN_DTYPE_FP8_E4M3)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(k=tensor([B, M, H, D], A.ATTN_DTYPE_FP8_E4M3, data=FAKE + 8)) == A.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_fp8_and_f16_tensors_are_rejected_outside_the_fp8_decode():
+    q8 = tensor([2, 128, 4, 128], A.ATTN_DTYPE_FP8_E4M3)
+    h = tensor([2, 128, 4, 128], A.ATTN_DTYPE_F16)
+    assert fwd(q8, q8, q8, q8) == A.ATTN_ERR_INVALID_ARGUMENT and "dtype" in A.attn_last_error()
+    assert fwd(h, h, h, h) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert fwd(std4(), q8, q8, std4()) == A.ATTN_ERR_INVALID_ARGUMENT

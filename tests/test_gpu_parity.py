@@ -393,3 +393,118 @@ def test_decode_paged_full_size(A, decode_inputs):
         check(out[b:b + 1, :, h:h + 1], lse[b:b + 1, h:h + 1], oo, ol, TOL_BF16_OUT, TOL_LSE, f"b={b} h={h}")
     del q, kc, vc
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ row-wise FP8 K/V caches
+
+def _fp8(codes: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(codes)).cuda().view(torch.float8_e4m3fn)
+
+
+def _f16(ss: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(ss, dtype=np.float16)).cuda()
+
+
+def _fp8_cache(seed, shape):
+    """(k codes, v codes, k scale/shift, v scale/shift) of a cache of `shape` [..., D]."""
+    return (synth.fp8_codes(seed, synth.TAG_K, shape), synth.fp8_codes(seed, synth.TAG_V, shape),
+            synth.scale_shift(seed, synth.TAG_K, shape[:-1]), synth.scale_shift(seed, synth.TAG_V, shape[:-1]))
+
+
+def _fp8_oracle(qh, kc, vc, kss, vss, scale=None):
+    return oracle.attention(synth.to_f64(qh, "bf16"), oracle.dequant_fp8_rowwise(kc, kss),
+                            oracle.dequant_fp8_rowwise(vc, vss), mask=0, scale=scale)
+
+
+def test_fp8_decode_every_code(A):
+    """Every finite E4M3 code (subnormals, +-0, 448) in K and in V, both halves of each 32-bit word,
+    scale 2^-8 and a random shift: fp32 output against the oracle's exact dequantisation."""
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)  # 254 codes
+    B, H, D, M = 2, 2, 128, 254
+    idx = (np.arange(M)[:, None] * 5 + np.arange(D)[None, :] * 3) % finite.size
+    kc = np.broadcast_to(finite[idx][None, :, None, :], (B, M, H, D)).copy()
+    vc = np.broadcast_to(finite[(idx + 101) % finite.size][None, :, None, :], (B, M, H, D)).copy()
+    kss, vss = synth.scale_shift(7, 1, (B, M, H)), synth.scale_shift(7, 2, (B, M, H))
+    kss[..., 0] = 2.0 ** -8
+    vss[..., 0] = 2.0 ** -8
+    qh = synth.normal(7, synth.TAG_Q, (B, 1, H, D), "bf16")
+    say("case: fp8 decode, every finite code")
+    out, lse = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), _fp8(kc), _fp8(vc), _f16(kss), _f16(vss), 3,
+                                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oo, ol = _fp8_oracle(qh, kc, vc, kss, vss)
+    check(out, lse, oo, ol, TOL_F32, TOL_F32, "every code")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_fp8_decode_contiguous(A, D, out_dtype):
+    tol_o, tol_l = (TOL_BF16_OUT, TOL_F32) if out_dtype == "bf16" else (TOL_F32, TOL_F32)
+    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    for B, M, H, S in [(3, 1000, 4, 7), (2, 5, 3, 8), (1, 5000, 2, 1), (2, 4097, 5, 128)]:
+        say(f"case: fp8 decode D={D} out={out_dtype} B={B} M={M} H={H} S={S}")
+        kc, vc, kss, vss = _fp8_cache(700 + M, (B, M, H, D))
+        qh = synth.normal(700 + M, synth.TAG_Q, (B, 1, H, D), "bf16")
+        out, lse = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), _fp8(kc), _fp8(vc), _f16(kss), _f16(vss), S,
+                                             scale=0.09, out_dtype=tdt)
+        torch.cuda.synchronize()
+        oo, ol = _fp8_oracle(qh, kc, vc, kss, vss, scale=0.09)
+        check(out, lse, oo, ol, tol_o, tol_l, f"fp8 S={S}")
+
+
+def test_fp8_decode_padded_lanes_5d_gqa(A):
+    """Padded lanes, 5-D [B, M, G, H, D] with the K/V and metadata heads broadcast (stride 0) per group."""
+    B, cap, G, Hg, D, S = 4, 600, 2, 3, 128, 5
+    lens = np.array([600, 0, 1, 257], dtype=np.int32)
+    kc, vc, kss, vss = _fp8_cache(1100, (B, cap, G, 1, D))
+    qh = synth.normal(1100, synth.TAG_Q, (B, 1, G, Hg, D), "bf16")
+    say(f"case: fp8 decode padded lanes 5-D GQA lens={list(lens)}")
+    k, v = _fp8(kc).expand(B, cap, G, Hg, D), _fp8(vc).expand(B, cap, G, Hg, D)
+    ks, vs = _f16(kss).expand(B, cap, G, Hg, 2), _f16(vss).expand(B, cap, G, Hg, 2)
+    out, lse = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), k, v, ks, vs, S, seqlens=torch.from_numpy(lens).cuda(),
+                                         max_seqlen_k=int(lens.max()))
+    torch.cuda.synchronize()
+    for b in range(B):
+        rep = lambda x: np.repeat(x[b:b + 1, :lens[b]], Hg, axis=3).reshape(1, lens[b], G * Hg, x.shape[-1])
+        oo, ol = _fp8_oracle(qh[b:b + 1].reshape(1, 1, G * Hg, D), rep(kc), rep(vc), rep(kss), rep(vss))
+        check(out[b:b + 1].reshape(1, 1, G * Hg, D), lse[b:b + 1], oo, ol, TOL_BF16_OUT, TOL_F32,
+              f"lane {b} len={lens[b]}")
+
+
+@pytest.mark.parametrize("page", [16, 64])
+def test_fp8_decode_paged(A, page):
+    B, H, D, S, P, maxb = 3, 4, 128, 5, 100, 20
+    rng = np.random.Generator(np.random.PCG64(1201 + page))
+    tables = rng.permutation(P)[:B * maxb].reshape(B, maxb).astype(np.int32)
+    lens = np.array([maxb * page, 37, 0], dtype=np.int32)
+    kc, vc, kss, vss = _fp8_cache(1202, (1, P * page, H, D))
+    qh = synth.normal(1202, synth.TAG_Q, (B, 1, H, D), "bf16")
+    say(f"case: fp8 decode paged page={page} lens={list(lens)}")
+    out, lse = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), _fp8(kc), _fp8(vc), _f16(kss), _f16(vss), S,
+                                         seqlens=torch.from_numpy(lens).cuda(), max_seqlen_k=int(lens.max()),
+                                         block_tables=torch.from_numpy(tables).cuda(), page_size=page,
+                                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        g = lambda x: _gather(x, tables[b], page, lens[b])
+        oo, ol = _fp8_oracle(qh[b:b + 1], g(kc), g(vc), g(kss), g(vss))
+        check(out[b:b + 1], lse[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"seq {b} len={lens[b]}")
+
+
+def test_fp8_decode_full_size(A):
+    """B=16, Mkv=32768, H=32, D=128 FP8 cache, 64 splits (the decode bench launch): sampled (b, h)."""
+    B, M, H, D = 16, 32768, 32, 128
+    say("generating fp8 decode inputs [16,32768,32,128] x2")
+    kc, vc, kss, vss = _fp8_cache(4, (B, M, H, D))
+    qh = synth.normal(4, synth.TAG_Q, (B, 1, H, D), "bf16")
+    say("case: fp8 decode full size S=64")
+    k, v = _fp8(kc), _fp8(vc)
+    out, lse = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), k, v, _f16(kss), _f16(vss), 64)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (7, 19), (15, 31)]:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        oo, ol = _fp8_oracle(qh[sl], kc[sl], vc[sl], kss[sl], vss[sl])
+        check(out[sl], lse[b:b + 1, h:h + 1], oo, ol, TOL_BF16_OUT, TOL_F32, f"b={b} h={h}")
+    assert not torch.isnan(out).any()
+    del k, v
+    torch.cuda.empty_cache()

@@ -21,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE_TOO_SMALL, ATTN_ERR_LAUNCH = range(5)
-ATTN_DTYPE_F32, ATTN_DTYPE_BF16 = 0, 1
+ATTN_DTYPE_F32, ATTN_DTYPE_BF16, ATTN_DTYPE_FP8_E4M3, ATTN_DTYPE_F16 = 0, 1, 2, 3
 MASK_NONE, MASK_CAUSAL, MASK_BLOCKDIAG, MASK_BLOCKDIAG_CAUSAL = 0, 1, 2, 3
 MASK_CAUSAL_BR, MASK_BLOCKDIAG_CAUSAL_BR, MASK_LOCAL_BR, MASK_CAUSAL_LOCAL_BR = 4, 5, 6, 7
 MASK_BLOCKDIAG_CAUSAL_LOCAL, MASK_BLOCKDIAG_CAUSAL_LOCAL_BR = 8, 9
@@ -71,6 +71,10 @@ _lib.attn_decode_splitkv_paged.argtypes = [_T, _T, _T, ctypes.c_void_p, ctypes.c
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                            ctypes.c_void_p, ctypes.c_size_t, _T, ctypes.c_void_p, ctypes.c_void_p]
 _lib.attn_decode_splitkv_paged.restype = ctypes.c_int
+_lib.attn_decode_splitkv_fp8.argtypes = [_T, _T, _T, _T, _T, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                         ctypes.c_void_p, ctypes.c_size_t, _T, ctypes.c_void_p, ctypes.c_void_p]
+_lib.attn_decode_splitkv_fp8.restype = ctypes.c_int
 _lib.attn_last_error.argtypes = []
 _lib.attn_last_error.restype = ctypes.c_char_p
 
@@ -86,6 +90,10 @@ def _dtype_code(dt: torch.dtype) -> int:
         return ATTN_DTYPE_F32
     if dt == torch.bfloat16:
         return ATTN_DTYPE_BF16
+    if dt == torch.float8_e4m3fn:
+        return ATTN_DTYPE_FP8_E4M3
+    if dt == torch.float16:
+        return ATTN_DTYPE_F16
     raise TypeError(f"unsupported dtype {dt}")
 
 
@@ -301,6 +309,47 @@ def prepare_decode_paged(q, k, v, seqlens, num_splits, max_seqlen_k, workspace, 
     args, ds = _paged_args(q, k, v, seqlens, block_tables, page_size, max_seqlen_k, num_splits, scale, workspace,
                            out, lse, stream)
     return Prepared(_lib.attn_decode_splitkv_paged, args, (ds, q, k, v, seqlens, block_tables, workspace, out, lse))
+
+
+def _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k, num_splits,
+              scale, workspace, out, lse, stream):
+    ds = [desc(q), desc(k), desc(v), desc(k_scale_shift), desc(v_scale_shift), desc(out)]
+    mb = block_tables.shape[1] if block_tables is not None else 0
+    args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), ctypes.byref(ds[3]), ctypes.byref(ds[4]),
+            _ptr(seqlens), _ptr(block_tables), int(mb), int(page_size or 0), int(max_seqlen_k or 0),
+            int(num_splits), _scale(scale), _ptr(workspace), workspace.numel(), ctypes.byref(ds[5]), _ptr(lse),
+            _stream(stream))
+    return args, ds
+
+
+def attn_decode_splitkv_fp8(q, k, v, k_scale_shift, v_scale_shift, num_splits, seqlens=None, max_seqlen_k=None,
+                            block_tables=None, page_size=None, scale=None, workspace=None, out=None, lse=True,
+                            out_dtype=None, stream=None):
+    """Split-KV decode over FP8 E4M3 K/V caches (torch.float8_e4m3fn) with float16 (scale, shift)
+    pairs [..., 2] per cache row and head; lanes, padded lanes (seqlens) or pages (block_tables).
+    Returns (out, lse or None)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty((q.shape[0], _htot(q), 1), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    need = attn_decode_workspace_bytes(q.shape[0], _htot(q), q.shape[-1], num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    args, _keep = _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k,
+                            num_splits, scale, workspace, out, lse, stream)
+    _check(_lib.attn_decode_splitkv_fp8(*args))
+    return out, lse
+
+
+def prepare_decode_fp8(q, k, v, k_scale_shift, v_scale_shift, num_splits, workspace, out, lse, seqlens=None,
+                       max_seqlen_k=None, block_tables=None, page_size=None, scale=None, stream=None) -> Prepared:
+    """attn_decode_splitkv_fp8 with every argument marshalled up front."""
+    args, ds = _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k,
+                         num_splits, scale, workspace, out, lse, stream)
+    return Prepared(_lib.attn_decode_splitkv_fp8, args,
+                    (ds, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, workspace, out, lse))
 
 
 def default_scale(K: int) -> float:

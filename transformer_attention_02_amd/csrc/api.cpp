@@ -31,7 +31,9 @@ attn_status ok() {
     return ATTN_OK;
 }
 
-size_t dtype_size(int dt) { return dt == ATTN_DTYPE_F32 ? 4 : 2; }
+size_t dtype_size(int dt) { return dt == ATTN_DTYPE_F32 ? 4 : (dt == ATTN_DTYPE_FP8_E4M3 ? 1 : 2); }
+
+constexpr unsigned DT_FLOAT = (1u << ATTN_DTYPE_F32) | (1u << ATTN_DTYPE_BF16);  // q/k/v/out of every path
 
 // A tensor normalised to [B, M, Htot, D] with head addressing (sg, sh, Hin).
 struct View {
@@ -42,10 +44,11 @@ struct View {
     attn::Strides s;
 };
 
-attn_status make_view(const attn_tensor *t, const char *name, View *v) {
+// `dtypes`: bit set of the attn_dtype values accepted; `align`: byte alignment of row starts.
+attn_status make_view(const attn_tensor *t, const char *name, View *v, unsigned dtypes = DT_FLOAT, int align = 16) {
     if (!t) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: descriptor is NULL", name);
-    if (t->dtype != ATTN_DTYPE_F32 && t->dtype != ATTN_DTYPE_BF16)
-        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, t->dtype);
+    if (t->dtype < 0 || t->dtype > ATTN_DTYPE_F16 || !((dtypes >> t->dtype) & 1u))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: dtype %d is not accepted here", name, t->dtype);
     if (t->ndim != 4 && t->ndim != 5)
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: ndim must be 4 [B,M,H,D] or 5 [B,M,G,H,D], got %d", name, t->ndim);
     for (int i = 0; i < t->ndim; ++i) {
@@ -76,14 +79,14 @@ attn_status make_view(const attn_tensor *t, const char *name, View *v) {
     const int64_t n = v->B * v->M * v->G * v->H * v->D;
     if (n > 0) {
         if (!v->p) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: data pointer is NULL", name);
-        // 16-byte aligned row starts: base pointer and every outer stride in bytes
+        // aligned row starts: base pointer and every outer stride in bytes
         const size_t es = dtype_size(v->dtype);
-        if (((uintptr_t)v->p) % 16 != 0)
-            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: data pointer is not 16-byte aligned", name);
+        if (((uintptr_t)v->p) % align != 0)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: data pointer is not %d-byte aligned", name, align);
         for (int i = 0; i < last; ++i)
-            if ((t->stride[i] * (int64_t)es) % 16 != 0)
-                return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: stride[%d]=%lld elements is not a multiple of 16 bytes",
-                            name, i, (long long)t->stride[i]);
+            if ((t->stride[i] * (int64_t)es) % align != 0)
+                return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: stride[%d]=%lld elements is not a multiple of %d bytes",
+                            name, i, (long long)t->stride[i], align);
     }
     return ATTN_OK;
 }
@@ -342,18 +345,30 @@ namespace {
 
 // Shared validation and launches of the split-KV decode entry points.  Without block tables
 // k/v are [B, cap, (G,) H, D] lanes; with them k/v are the paged cache [1, pages * page_size, ...].
-attn_status decode(const char *fn, const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
-                   const int32_t *seqlens, const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t page_size,
-                   int32_t max_seqlen_k, int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
-                   const attn_tensor *ot, float *lse, attn_stream_t stream) {
-    View q, k, v, o;
+// `fp8`: k/v are FP8 E4M3 codes with (scale, shift) metadata ksst / vsst.
+attn_status decode(const char *fn, bool fp8, const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
+                   const attn_tensor *ksst, const attn_tensor *vsst, const int32_t *seqlens,
+                   const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                   int32_t num_splits, float scale, void *workspace, size_t workspace_bytes, const attn_tensor *ot,
+                   float *lse, attn_stream_t stream) {
+    View q, k, v, o, kss{}, vss{};
     attn_status st;
+    const unsigned kv_dt = fp8 ? 1u << ATTN_DTYPE_FP8_E4M3 : DT_FLOAT;
     if ((st = make_view(qt, "q", &q)) != ATTN_OK) return st;
-    if ((st = make_view(kt, "k", &k)) != ATTN_OK) return st;
-    if ((st = make_view(vt, "v", &v)) != ATTN_OK) return st;
+    if ((st = make_view(kt, "k", &k, kv_dt)) != ATTN_OK) return st;
+    if ((st = make_view(vt, "v", &v, kv_dt)) != ATTN_OK) return st;
     if ((st = make_view(ot, "out", &o)) != ATTN_OK) return st;
-    if (k.dtype != q.dtype || v.dtype != q.dtype || o.dtype != q.dtype)
+    if (fp8) {
+        if ((st = make_view(ksst, "k_scale_shift", &kss, 1u << ATTN_DTYPE_F16, 4)) != ATTN_OK) return st;
+        if ((st = make_view(vsst, "v_scale_shift", &vss, 1u << ATTN_DTYPE_F16, 4)) != ATTN_OK) return st;
+        if (q.dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q must be bf16", fn);
+        for (const View *m : {&kss, &vss})
+            if (!same_heads(*m, k) || m->B != k.B || m->M != k.M || m->D != 2)
+                return fail(ATTN_ERR_INVALID_ARGUMENT,
+                            "%s: scale/shift tensors must have k's shape with the last axis 2", fn);
+    } else if (k.dtype != q.dtype || v.dtype != q.dtype || o.dtype != q.dtype) {
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out must share one dtype", fn);
+    }
     if (!same_heads(q, k) || !same_heads(q, v) || !same_heads(q, o))
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out must have the same rank and head axes", fn);
     const bool paged = block_tables != nullptr;
@@ -426,7 +441,12 @@ attn_status decode(const char *fn, const attn_tensor *qt, const attn_tensor *kt,
     d.page_size = page_size;
     d.num_pages = paged ? (int)(k.M / page_size) : 0;
     d.cap = (int)cap;
-    hipError_t e = attn::launch_decode_partials(d, q.dtype == ATTN_DTYPE_F32, (hipStream_t)stream);
+    d.kss = kss.p;
+    d.vss = vss.p;
+    d.skss = kss.s;
+    d.svss = vss.s;
+    const int elem = fp8 ? attn::DECODE_FP8 : (q.dtype == ATTN_DTYPE_F32 ? attn::DECODE_F32 : attn::DECODE_BF16);
+    hipError_t e = attn::launch_decode_partials(d, elem, (hipStream_t)stream);
     if (e != hipSuccess) return launch_status(e, fn);
 
     attn::MergeArgs m;
@@ -459,8 +479,8 @@ extern "C" {
 attn_status attn_decode_splitkv(const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
                                 int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                 const attn_tensor *ot, float *lse, attn_stream_t stream) {
-    return decode("attn_decode_splitkv", qt, kt, vt, nullptr, nullptr, 0, 0, 0, num_splits, scale, workspace,
-                  workspace_bytes, ot, lse, stream);
+    return decode("attn_decode_splitkv", false, qt, kt, vt, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, num_splits,
+                  scale, workspace, workspace_bytes, ot, lse, stream);
 }
 
 attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
@@ -468,8 +488,21 @@ attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k
                                       int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
                                       int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                       const attn_tensor *out, float *lse, attn_stream_t stream) {
-    return decode("attn_decode_splitkv_paged", q, k, v, seqlens, block_tables, max_blocks_per_seq, page_size,
-                  max_seqlen_k, num_splits, scale, workspace, workspace_bytes, out, lse, stream);
+    return decode("attn_decode_splitkv_paged", false, q, k, v, nullptr, nullptr, seqlens, block_tables,
+                  max_blocks_per_seq, page_size, max_seqlen_k, num_splits, scale, workspace, workspace_bytes, out, lse,
+                  stream);
+}
+
+attn_status attn_decode_splitkv_fp8(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                    const attn_tensor *k_scale_shift, const attn_tensor *v_scale_shift,
+                                    const int32_t *seqlens, const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                    int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                                    const attn_tensor *out, float *lse, attn_stream_t stream) {
+    const char *fn = "attn_decode_splitkv_fp8";
+    if (block_tables && !seqlens) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block_tables need seqlens", fn);
+    return decode(fn, true, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, max_blocks_per_seq,
+                  page_size, max_seqlen_k, num_splits, scale, workspace, workspace_bytes, out, lse, stream);
 }
 
 }  // extern "C"

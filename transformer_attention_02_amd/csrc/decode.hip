@@ -6,20 +6,26 @@
 //
 // The work is a stream over the K/V cache, about one flop per byte, so the
 // kernel is built for HBM bandwidth, not for the matrix cores:
-//   * one workgroup (4 waves) per (chunk, batch, head); consecutive workgroups
-//     are consecutive heads of the same chunk, so neighbouring workgroups read
-//     neighbouring bytes of the [B, Mkv, H, D] cache;
-//   * a key row (D elements) is read by D/8 lanes (bf16) with 16-byte loads,
-//     eight rows per lane in flight before any arithmetic;
-//   * phase 1 streams K: q.k per row, reduced across the row's lanes, scores
-//     kept in LDS; phase 2 takes the exact max and the exponentials over the
-//     chunk (no per-key rescaling); phase 3 streams V and accumulates p v.
-//   * chunks longer than the LDS score buffer are cut into sub-chunks combined
-//     with the running-max rescale;
+//   * one workgroup (4 waves) per (chunk, batch, group of hpw neighbouring heads); hpw
+//     is picked so that a cache row's segments of those heads are 512 contiguous bytes
+//     (a lone 128- or 256-byte head segment per row streams markedly slower);
+//   * a lane group of D/8 (bf16) or D/16 (FP8) lanes reads one key row of one head with
+//     16-byte loads; K and V rows of the same keys are loaded together, eight rows per
+//     lane in flight before any arithmetic;
+//   * every lane group keeps its own online softmax (base-2 running max, sum of
+//     exponentials, p-weighted V columns) over the rows it reads, so there is no score
+//     buffer and no barrier in the stream; at the end the states of a head's lane
+//     groups are combined exactly through LDS (the same LSE-weighted merge as between
+//     chunks);
 //   * KV-cache layouts ("Attention - Biases & masks": BlockDiagonalPaddedKeysMask,
 //     PagedBlockDiagonalPaddedKeysMask): per-sequence key counts on the device,
 //     and for a paged cache the physical row of every key of a sub-chunk is
-//     resolved once into LDS from the block table.
+//     resolved once into LDS from the block table;
+//   * row-wise FP8 caches ("Attention - operator protocol", InputsFp8): a lane takes
+//     16 E4M3 codes per 16-byte load and widens them with the hardware conversion;
+//     the row's (scale, shift) is applied to the reduced dot product, since
+//     q.(c*scale + shift) = scale*(q.c) + shift*sum(q), and on the V side the
+//     weight p*scale multiplies the codes while p*shift is summed once per row.
 // Output: the chunk's normalised fp32 output and its natural-log LSE; an empty
 // chunk gives 0 and -inf.
 #include <type_traits>
@@ -31,10 +37,20 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int NT = 256;
-constexpr int SUB = 2048;  // scores per sub-chunk held in LDS
-constexpr int UNROLL = 8;  // key rows per lane in flight
+constexpr int SUB = 2048;  // keys per sub-chunk of a paged cache (their rows are resolved into LDS)
+// Tuning (measured on the [16, 32768, 32, 128] decode): 8 key rows per lane in flight, no
+// software pipelining of rounds, 512 contiguous bytes per cache row and workgroup.
+#ifndef DECODE_UNROLL
+#define DECODE_UNROLL 8
+#endif
+#ifndef DECODE_PIPE
+#define DECODE_PIPE 0
+#endif
+constexpr int U = DECODE_UNROLL;        // key rows per lane and round
+constexpr bool PIPE = DECODE_PIPE != 0;  // issue round i+1 before using round i
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <bool F32>
 __device__ __forceinline__ void unpack(const u32x4 &w, float *x) {
@@ -50,42 +66,62 @@ __device__ __forceinline__ void unpack(const u32x4 &w, float *x) {
     }
 }
 
-__device__ __forceinline__ float block_max(float x, float *red) {
+// 16 OCP E4M3 codes (byte i of word j is element 4j+i) to fp32; exact.
+__device__ __forceinline__ void unpack_fp8(const u32x4 &w, float *x) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-    __syncthreads();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    for (int i = 0; i < 4; ++i) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+        x[4 * i] = lo[0];
+        x[4 * i + 1] = lo[1];
+        x[4 * i + 2] = hi[0];
+        x[4 * i + 3] = hi[1];
+    }
 }
 
-__device__ __forceinline__ float block_sum(float x, float *red) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-    __syncthreads();
-    return (red[0] + red[1]) + (red[2] + red[3]);
+template <int ELEM>
+__device__ __forceinline__ void unpack_elem(const u32x4 &w, float *x) {
+    if constexpr (ELEM == DECODE_FP8)
+        unpack_fp8(w, x);
+    else
+        unpack<ELEM == DECODE_F32>(w, x);
+}
+
+// (scale, shift) halves of a metadata word
+__device__ __forceinline__ float ss_scale(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float ss_shift(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// Workgroups are dealt to the 8 XCDs round-robin (workgroup i to XCD i % 8).  Renumbered so
+// that every XCD takes one contiguous range of the logical order: the workgroups of one cache
+// row range (neighbouring heads, which share DRAM pages and the lines of FP8 metadata) then run
+// on one XCD at about the same time.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+    const int x = i & 7, k = i >> 3, q = n >> 3, r = n & 7;
+    return x * q + min(x, r) + k;
 }
 
 // MODE 0: k/v [B, Mkv, ...], every sequence has Mkv keys.  MODE 1: padded lanes [B, cap, ...] with
 // seqlens[b] valid keys.  MODE 2: paged cache [1, num_pages * page_size, ...]; key j of sequence b is
 // row block_tables[b][j / page_size] * page_size + j % page_size (page numbers clamped to the cache).
-template <int HD, bool F32, int MODE>
+template <int HD, int ELEM, int MODE>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
-    constexpr int EPL = F32 ? 4 : 8;   // elements per 16-byte load
-    constexpr int LPK = HD / EPL;      // lanes per key row
-    constexpr int KPP = NT / LPK;      // key rows per pass of the workgroup
-    using T = typename std::conditional<F32, float, __bf16>::type;
+    constexpr bool F32 = ELEM == DECODE_F32, FP8 = ELEM == DECODE_FP8;
+    constexpr int EPL = F32 ? 4 : (FP8 ? 16 : 8);  // elements per 16-byte load
+    constexpr int LPK = HD / EPL;                  // lanes per key row (a lane group)
+    constexpr int KPP = NT / LPK;                  // lane groups of the workgroup
+    using T = typename std::conditional<F32, float, typename std::conditional<FP8, uint8_t, __bf16>::type>::type;
+    using QT = typename std::conditional<F32, float, __bf16>::type;  // FP8 caches take bf16 queries
 
-    __shared__ float sc[SUB];
     __shared__ float acc_s[KPP][HD];
-    __shared__ float red[4];
+    __shared__ float m_s[KPP], l_s[KPP], w_s[KPP];
     __shared__ int rows_s[MODE == 2 ? SUB : 1];  // physical cache row of each key of the sub-chunk
 
-    int id = blockIdx.x;
-    const int hf = id % a.Htot;
-    id /= a.Htot;
+    // Workgroup = (chunk s, batch b, hpw consecutive heads).  Lane group g works on head slot
+    // g % hpw and row slot g / hpw, so one pass reads hpw neighbouring head segments of each row.
+    const int lh = a.log2_hpw, hpw = 1 << lh, RPP = KPP >> lh, R = RPP * U;
+    int id = xcd_remap(blockIdx.x, gridDim.x);
+    const int hg = id % (a.Htot >> lh);
+    id /= a.Htot >> lh;
     const int b = id % a.B;
     const int s = id / a.B;
     const int Lb = MODE == 0 ? a.Mkv : min(max(a.seqlens[b], 0), a.cap);
@@ -94,23 +130,46 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const int64_t kb = MODE == 2 ? 0 : (int64_t)b * a.sk.b, vb = MODE == 2 ? 0 : (int64_t)b * a.sv.b;
 
     const int tid = threadIdx.x, g = tid / LPK, cl = tid % LPK;
-    const T *qp = (const T *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin);
+    const int hs = g & (hpw - 1), rs = g >> lh;
+    const int hf = (hg << lh) + hs;
+    const QT *qp = (const QT *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin) + cl * EPL;
     const T *kp = (const T *)a.k + kb + head_offset(a.sk, hf, a.Hin) + cl * EPL;
     const T *vp = (const T *)a.v + vb + head_offset(a.sv, hf, a.Hin) + cl * EPL;
+    // FP8: per-row metadata words, addressed in fp16 units like a [.., 2] tensor
+    const uint16_t *kss = nullptr, *vss = nullptr;
+    if constexpr (FP8) {
+        kss = (const uint16_t *)a.kss + (MODE == 2 ? 0 : (int64_t)b * a.skss.b) + head_offset(a.skss, hf, a.Hin);
+        vss = (const uint16_t *)a.vss + (MODE == 2 ? 0 : (int64_t)b * a.svss.b) + head_offset(a.svss, hf, a.Hin);
+    }
 
     float qv[EPL];
-    unpack<F32>(*(const u32x4 *)(qp + cl * EPL), qv);
+    if constexpr (FP8) {
+        unpack<false>(*(const u32x4 *)qp, qv);
+        unpack<false>(*(const u32x4 *)(qp + 8), qv + 8);
+    } else {
+        unpack<F32>(*(const u32x4 *)qp, qv);
+    }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[e] *= a.scale_log2;
+    float qsum = 0.f;  // scale_log2 * sum(q), the weight of a row's shift in its score
+    if constexpr (FP8) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qsum += qv[e];
+#pragma unroll
+        for (int o = LPK / 2; o >= 1; o >>= 1) qsum += __shfl_xor(qsum, o, 64);
+    }
 
+    // Online softmax state of this lane group (the same in its LPK lanes): base-2 running max,
+    // sum of exponentials, p-weighted values (this lane's EPL columns) and, for FP8, sum of p*shift.
     float acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY, l_run = 0.f, sh_acc = 0.f;
 
-    for (int sub0 = j0; sub0 < j1; sub0 += SUB) {
-        const int n = min(SUB, j1 - sub0);
+    for (int sub0 = j0; sub0 < j1; sub0 += (MODE == 2 ? SUB : a.chunk)) {
+        const int n = MODE == 2 ? min(SUB, j1 - sub0) : j1 - sub0;
         if (MODE == 2) {
+            __syncthreads();  // the previous sub-chunk's rows are no longer read
             const int32_t *bt = a.block_tables + (int64_t)b * a.bt_stride;
             for (int i = tid; i < n; i += NT) {
                 const int j = sub0 + i;
@@ -119,103 +178,152 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
             }
             __syncthreads();
         }
-        // phase 1: scores
-        for (int p = 0; p < n; p += KPP * UNROLL) {
-            u32x4 w[UNROLL];
+        // K and V rows of the same keys are read together, in rounds of R keys (U per lane);
+        // with PIPE the next round is issued before the current one is used.
+        auto load = [&](int p, u32x4 *wk, u32x4 *wv, uint32_t *sk, uint32_t *sv) __attribute__((always_inline)) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int r = p + u * KPP + g;
+            for (int u = 0; u < U; ++u) {
+                const int r = p + u * RPP + rs;
                 const int64_t row = MODE == 2 ? (r < n ? rows_s[r] : 0) : sub0 + r;
-                w[u] = r < n ? *(const u32x4 *)(kp + row * a.sk.m) : u32x4{0, 0, 0, 0};
+                wk[u] = r < n ? *(const u32x4 *)(kp + row * a.sk.m) : u32x4{0, 0, 0, 0};
+                wv[u] = r < n ? *(const u32x4 *)(vp + row * a.sv.m) : u32x4{0, 0, 0, 0};
+                if constexpr (FP8) {
+                    sk[u] = r < n ? *(const uint32_t *)(kss + row * a.skss.m) : 0u;
+                    sv[u] = r < n ? *(const uint32_t *)(vss + row * a.svss.m) : 0u;
+                }
+            }
+        };
+        constexpr int NS = FP8 ? U : 1;
+        u32x4 wk[U], wv[U], wkn[U], wvn[U];
+        uint32_t sk[NS], sv[NS], skn[NS], svn[NS];
+        load(0, wkn, wvn, skn, svn);
+        for (int p = 0; p < n; p += R) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                wk[u] = wkn[u];
+                wv[u] = wvn[u];
             }
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
+            for (int u = 0; u < NS; ++u) {
+                sk[u] = skn[u];
+                sv[u] = svn[u];
+            }
+            if (PIPE && p + R < n) load(p + R, wkn, wvn, skn, svn);
+            float sc[U];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
                 float x[EPL];
-                unpack<F32>(w[u], x);
+                unpack_elem<ELEM>(wk[u], x);
                 float dot = 0.f;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) dot = fmaf(qv[e], x[e], dot);
 #pragma unroll
                 for (int o = LPK / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
-                const int r = p + u * KPP + g;
-                if (cl == 0 && r < n) sc[r] = dot;
+                if constexpr (FP8) dot = fmaf(ss_scale(sk[u]), dot, ss_shift(sk[u]) * qsum);
+                sc[u] = p + u * RPP + rs < n ? dot : -INFINITY;
+                mx = fmaxf(mx, sc[u]);
             }
-        }
-        __syncthreads();
-        // phase 2: exact max and exponentials over the sub-chunk
-        float mt = -INFINITY;
-        for (int i = tid; i < n; i += NT) mt = fmaxf(mt, sc[i]);
-        mt = block_max(mt, red);
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        float ls = 0.f;
-        for (int i = tid; i < n; i += NT) {
-            const float e = __builtin_amdgcn_exp2f(sc[i] - m_new);
-            sc[i] = e;
-            ls += e;
-        }
-        ls = block_sum(ls, red);  // its barriers also publish the exponentials
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
+            const float m_new = fmaxf(m_run, mx);
+            const float mu = m_new == -INFINITY ? 0.f : m_new;  // no row seen yet: keep exponents finite
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+            m_run = m_new;
+            l_run *= alpha;
+            sh_acc *= alpha;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
-        // phase 3: p-weighted sum of value rows
-        for (int p = 0; p < n; p += KPP * UNROLL) {
-            u32x4 w[UNROLL];
+            for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int r = p + u * KPP + g;
-                const int64_t row = MODE == 2 ? (r < n ? rows_s[r] : 0) : sub0 + r;
-                w[u] = r < n ? *(const u32x4 *)(vp + row * a.sv.m) : u32x4{0, 0, 0, 0};
-            }
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int r = p + u * KPP + g;
-                const float pr = r < n ? sc[r] : 0.f;
+            for (int u = 0; u < U; ++u) {
+                float pr = __builtin_amdgcn_exp2f(sc[u] - mu);
+                l_run += pr;
+                if constexpr (FP8) {
+                    sh_acc = fmaf(pr, ss_shift(sv[u]), sh_acc);
+                    pr *= ss_scale(sv[u]);
+                }
                 float x[EPL];
-                unpack<F32>(w[u], x);
+                unpack_elem<ELEM>(wv[u], x);
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pr, x[e], acc[e]);
             }
+            if (!PIPE && p + R < n) load(p + R, wkn, wvn, skn, svn);
         }
-        __syncthreads();  // sc is rewritten by the next sub-chunk
     }
 
-    // combine the KPP row groups
+    // exact combine of the lane groups' states, per head: groups hs, hs + hpw, ... hold head slot hs
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc_s[g][cl * EPL + e] = acc[e];
-    __syncthreads();
-    const int64_t obase = ((int64_t)s * a.B + b) * a.Htot + hf;
-    for (int d = tid; d < HD; d += NT) {
-        float tot = 0.f;
-#pragma unroll
-        for (int r = 0; r < KPP; ++r) tot += acc_s[r][d];
-        a.ws_o[obase * HD + d] = l_run > 0.f ? tot / l_run : 0.f;
+    for (int e = 0; e < EPL; ++e) acc_s[g][cl * EPL + e] = acc[e] + sh_acc;
+    if (cl == 0) {
+        m_s[g] = m_run;
+        l_s[g] = l_run;
     }
-    if (tid == 0) a.ws_lse[obase] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    __syncthreads();
+    if (tid < KPP) {
+        float M = -INFINITY;
+        for (int r = tid & (hpw - 1); r < KPP; r += hpw) M = fmaxf(M, m_s[r]);
+        w_s[tid] = __builtin_amdgcn_exp2f(m_s[tid] - (M == -INFINITY ? 0.f : M));
+    }
+    __syncthreads();
+    const int64_t obase = ((int64_t)s * a.B + b) * a.Htot + (hg << lh);  // first head of the workgroup
+    for (int t = tid; t < HD << lh; t += NT) {
+        const int h = t / HD, d = t % HD;
+        float tot = 0.f, L = 0.f;
+        for (int r = h; r < KPP; r += hpw) {
+            tot = fmaf(acc_s[r][d], w_s[r], tot);
+            L = fmaf(l_s[r], w_s[r], L);
+        }
+        a.ws_o[(obase + h) * HD + d] = L > 0.f ? tot / L : 0.f;
+    }
+    if (tid < hpw) {
+        float M = -INFINITY, L = 0.f;
+        for (int r = tid; r < KPP; r += hpw) M = fmaxf(M, m_s[r]);
+        for (int r = tid; r < KPP; r += hpw) L = fmaf(l_s[r], w_s[r], L);
+        a.ws_lse[obase + tid] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    }
 }
 
-template <int HD, bool F32, int MODE>
-hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
-    const int64_t grid = (int64_t)a.S * a.B * a.Htot;
+#ifndef DECODE_ROW_BYTES
+#define DECODE_ROW_BYTES 512
+#endif
+template <int HD, int ELEM, int MODE>
+hipError_t launch(const DecodeArgs &args, hipStream_t stream) {
+    // heads per workgroup: enough neighbouring head segments for DECODE_ROW_BYTES contiguous bytes
+    // per cache row, a power of two that divides Htot and leaves every head at least one lane group
+    constexpr int ES = ELEM == DECODE_F32 ? 4 : (ELEM == DECODE_FP8 ? 1 : 2);
+    constexpr int EPL = 16 / ES, KPP = NT / (HD / EPL);
+    DecodeArgs a = args;
+    a.log2_hpw = 0;
+    while ((HD * ES << (a.log2_hpw + 1)) <= DECODE_ROW_BYTES && (2 << a.log2_hpw) <= KPP &&
+           a.Htot % (2 << a.log2_hpw) == 0)
+        ++a.log2_hpw;
+    const int64_t grid = (int64_t)a.S * a.B * (a.Htot >> a.log2_hpw);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_kernel<HD, F32, MODE>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<HD, ELEM, MODE>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int HD, bool F32>
+template <int HD, int ELEM>
 hipError_t launch_mode(const DecodeArgs &a, hipStream_t stream) {
-    if (a.block_tables) return launch<HD, F32, 2>(a, stream);
-    if (a.seqlens) return launch<HD, F32, 1>(a, stream);
-    return launch<HD, F32, 0>(a, stream);
+    if (a.block_tables) return launch<HD, ELEM, 2>(a, stream);
+    if (a.seqlens) return launch<HD, ELEM, 1>(a, stream);
+    return launch<HD, ELEM, 0>(a, stream);
+}
+
+template <int HD>
+hipError_t launch_elem(const DecodeArgs &a, int elem, hipStream_t stream) {
+    switch (elem) {
+    case DECODE_BF16: return launch_mode<HD, DECODE_BF16>(a, stream);
+    case DECODE_F32: return launch_mode<HD, DECODE_F32>(a, stream);
+    case DECODE_FP8: return launch_mode<HD, DECODE_FP8>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_decode_partials(const DecodeArgs &a, bool f32, hipStream_t stream) {
-    if (a.D == 128) return f32 ? launch_mode<128, true>(a, stream) : launch_mode<128, false>(a, stream);
-    if (a.D == 64) return f32 ? launch_mode<64, true>(a, stream) : launch_mode<64, false>(a, stream);
+hipError_t launch_decode_partials(const DecodeArgs &a, int elem, hipStream_t stream) {
+    if (a.D == 128) return launch_elem<128>(a, elem, stream);
+    if (a.D == 64) return launch_elem<64>(a, elem, stream);
     return hipErrorInvalidValue;
 }
 

@@ -54,7 +54,14 @@ struct DecodeArgs {
     const int32_t *seqlens;       // [B], clamped to [0, cap]
     const int32_t *block_tables;  // [B, bt_stride] page numbers, or null (lanes [B, cap, ...])
     int bt_stride, page_size, num_pages, cap;
+    // FP8 caches only: (scale, shift) fp16 pairs per cache row and head; strides in fp16 units
+    const void *kss, *vss;
+    Strides skss, svss;
+    int log2_hpw;  // heads per workgroup = 1 << log2_hpw (set by the launcher)
 };
+
+// Element type of a decode K/V cache (q is bf16 for FP8 caches, else the cache's type).
+enum DecodeElem : int { DECODE_BF16 = 0, DECODE_F32 = 1, DECODE_FP8 = 2 };
 
 constexpr int kMaxChunks = 128;
 
@@ -73,7 +80,7 @@ struct MergeArgs {
 // Launchers return a hipError_t from the launch.
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool out_f32, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
-hipError_t launch_decode_partials(const DecodeArgs &a, bool f32, hipStream_t stream);
+hipError_t launch_decode_partials(const DecodeArgs &a, int elem, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 
 }  // namespace attn
