@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the attention forward, partial and merge -- TEST INFRASTRUCTURE.
+"""fp64 CPU oracle for the attention forward, backward, partial and merge -- TEST INFRASTRUCTURE.
 
 Only ``tests/``, the smoke check and the bench's CPU-baseline leg use this
 package.  The HIP product path never imports, links or calls it, and it shares
@@ -48,6 +48,9 @@ def _load():
         lib.oracle_attention.argtypes = [i64, i64, i64, i64, i64, i64, dp, dp, dp, ctypes.c_int, ctypes.c_int,
                                          ip, ip, ctypes.c_double, i64, i64, dp, dp]
         lib.oracle_attention.restype = ctypes.c_int
+        lib.oracle_attention_backward.argtypes = [i64, i64, i64, i64, i64, i64, dp, dp, dp, dp, dp, dp, ctypes.c_int,
+                                                  ctypes.c_int, ip, ip, ctypes.c_double, i64, i64, dp, dp, dp]
+        lib.oracle_attention_backward.restype = ctypes.c_int
         lib.oracle_merge.argtypes = [i64, i64, i64, i64, i64, dp, dp, dp, dp]
         lib.oracle_merge.restype = ctypes.c_int
         lib.oracle_threads.restype = ctypes.c_int
@@ -102,6 +105,43 @@ def attention(q, k, v, mask: int = MASK_NONE, scale=None, seqstart_q=None, seqst
     if rc != 0:
         raise ValueError(f"oracle_attention rejected its arguments (code {rc})")
     return out, lse
+
+
+def attention_backward(dout, out, lse, q, k, v, mask: int = MASK_NONE, scale=None, seqstart_q=None,
+                       seqstart_k=None, window=None, window_right=None):
+    """Exact gradients (dq, dk, dv) of the attention for upstream gradient ``dout`` (fp64).
+
+    ``out`` and ``lse`` are the forward's results for the same arguments; the mask
+    arguments are those of ``attention``.
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.ascontiguousarray(out, dtype=np.float64)
+    lse = np.ascontiguousarray(lse, dtype=np.float64)
+    dout = np.ascontiguousarray(dout, dtype=np.float64)
+    B, Mq, H, K = q.shape
+    Mkv, Kv = k.shape[1], v.shape[3]
+    assert k.shape == (B, Mkv, H, K) and v.shape == (B, Mkv, H, Kv)
+    assert out.shape == dout.shape == (B, Mq, H, Kv) and lse.shape == (B, H, Mq)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    nseq = 0
+    sq = sk = None
+    if mask in PACKED:
+        sq = np.ascontiguousarray(seqstart_q, dtype=np.int32)
+        sk = np.ascontiguousarray(seqstart_k if seqstart_k is not None else seqstart_q, dtype=np.int32)
+        nseq = len(sq) - 1
+    ip = ctypes.POINTER(ctypes.c_int32)
+    rc = _load().oracle_attention_backward(B, Mq, Mkv, H, K, Kv, _dp(q), _dp(k), _dp(v), _dp(out), _dp(lse),
+                                           _dp(dout), int(mask), nseq,
+                                           sq.ctypes.data_as(ip) if sq is not None else None,
+                                           sk.ctypes.data_as(ip) if sk is not None else None, float(scale),
+                                           int(window or 0), int(window_right or 0), _dp(dq), _dp(dk), _dp(dv))
+    if rc != 0:
+        raise ValueError(f"oracle_attention_backward rejected its arguments (code {rc})")
+    return dq, dk, dv
 
 
 def merge(out_chunks, lse_chunks):

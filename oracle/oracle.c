@@ -13,6 +13,8 @@
  *   memory_efficient_attention_forward_requires_grad: also returns the
  *   per-row log-sum-exp (LSE).
  *   memory_efficient_attention_partial: the same over one disjoint K/V shard.
+ *   memory_efficient_attention_backward: the exact gradients dq, dk, dv for an
+ *   upstream gradient, given the forward's out and lse (oracle_attention_backward).
  *   merge_attentions: the exact LSE-weighted combination of shard results.
  *
  * For batch b, head h, query row i and allowed key set A(i):
@@ -194,6 +196,85 @@ int oracle_attention(int64_t B, int64_t Mq, int64_t Mkv, int64_t H, int64_t K, i
         free(ok);
     }
     return err;
+}
+
+/* Backward of the attention above ("Attention - Core fMHA", memory_efficient_attention_backward:
+ * from the upstream gradient dout, the forward's out and lse and the original q, k, v, return
+ * dq, dk, dv).  With P_ij = exp(s_ij - lse_i) on the visible keys (0 elsewhere), the gradient
+ * of out_i = sum_j P_ij v_j is, written out:
+ *   dv_j  = sum_i P_ij dout_i
+ *   dP_ij = dout_i . v_j,   D_i = dout_i . out_i  (= sum_j P_ij dP_ij)
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dq_i  = scale * sum_j dS_ij k_j,   dk_j = scale * sum_i dS_ij q_i.
+ * Rows with lse = -inf (no visible key) contribute nothing.  Two passes, both parallel and
+ * free of races: one over query rows for dq, one over key rows for dk and dv. */
+static double dotn(const double *a, const double *b, int64_t n) {
+    double acc = 0.0;
+    for (int64_t d = 0; d < n; ++d) acc += a[d] * b[d];
+    return acc;
+}
+
+int oracle_attention_backward(int64_t B, int64_t Mq, int64_t Mkv, int64_t H, int64_t K, int64_t Kv,
+                              const double *q, const double *k, const double *v, const double *out,
+                              const double *lse, const double *dout, int mask, int nseq,
+                              const int32_t *seqstart_q, const int32_t *seqstart_k, double scale, int64_t win_l,
+                              int64_t win_r, double *dq, double *dk, double *dv) {
+    if (B < 0 || Mq < 0 || Mkv < 0 || H < 0 || K < 1 || Kv < 1) return 1;
+    if (mask < 0 || mask > 9) return 1;
+    if (is_packed(mask) && (B != 1 || nseq < 1 || !seqstart_q || !seqstart_k)) return 1;
+    if ((mask >= 7 && win_l < 1) || (mask == 6 && (win_l < 0 || win_r < 0))) return 1;
+
+    double *D = (double *)malloc(sizeof(double) * (size_t)(B * H * Mq > 0 ? B * H * Mq : 1));
+    if (!D) return 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < B * H * Mq; ++r) {
+        const int64_t b = r / (H * Mq), h = (r / Mq) % H, i = r % Mq;
+        const int64_t o = ((b * Mq + i) * H + h) * Kv;
+        D[r] = dotn(dout + o, out + o, Kv);
+    }
+    /* dq: one query row at a time */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < B * H * Mq; ++r) {
+        const int64_t b = r / (H * Mq), h = (r / Mq) % H, i = r % Mq;
+        const double *qi = q + ((b * Mq + i) * H + h) * K;
+        const double *gi = dout + ((b * Mq + i) * H + h) * Kv;
+        double *dqi = dq + ((b * Mq + i) * H + h) * K;
+        const double li = lse[(b * H + h) * Mq + i];
+        for (int64_t d = 0; d < K; ++d) dqi[d] = 0.0;
+        if (li == -INFINITY) continue;
+        for (int64_t j = 0; j < Mkv; ++j) {
+            if (!key_allowed(mask, i, j, seqstart_q, seqstart_k, nseq, Mq, Mkv, win_l, win_r)) continue;
+            const double *kj = k + ((b * Mkv + j) * H + h) * K;
+            const double *vj = v + ((b * Mkv + j) * H + h) * Kv;
+            const double p = exp(scale * dotn(qi, kj, K) - li);
+            const double ds = p * (dotn(gi, vj, Kv) - D[r]);
+            for (int64_t d = 0; d < K; ++d) dqi[d] += scale * ds * kj[d];
+        }
+    }
+    /* dk, dv: one key row at a time */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t c = 0; c < B * H * Mkv; ++c) {
+        const int64_t b = c / (H * Mkv), h = (c / Mkv) % H, j = c % Mkv;
+        const double *kj = k + ((b * Mkv + j) * H + h) * K;
+        const double *vj = v + ((b * Mkv + j) * H + h) * Kv;
+        double *dkj = dk + ((b * Mkv + j) * H + h) * K;
+        double *dvj = dv + ((b * Mkv + j) * H + h) * Kv;
+        for (int64_t d = 0; d < K; ++d) dkj[d] = 0.0;
+        for (int64_t d = 0; d < Kv; ++d) dvj[d] = 0.0;
+        for (int64_t i = 0; i < Mq; ++i) {
+            const int64_t r = (b * H + h) * Mq + i;
+            if (lse[r] == -INFINITY) continue;
+            if (!key_allowed(mask, i, j, seqstart_q, seqstart_k, nseq, Mq, Mkv, win_l, win_r)) continue;
+            const double *qi = q + ((b * Mq + i) * H + h) * K;
+            const double *gi = dout + ((b * Mq + i) * H + h) * Kv;
+            const double p = exp(scale * dotn(qi, kj, K) - lse[r]);
+            const double ds = p * (dotn(gi, vj, Kv) - D[r]);
+            for (int64_t d = 0; d < Kv; ++d) dvj[d] += p * gi[d];
+            for (int64_t d = 0; d < K; ++d) dkj[d] += scale * ds * qi[d];
+        }
+    }
+    free(D);
+    return 0;
 }
 
 /* FP8 E4M3 (OCP "FN" variant, the 8-bit float of MI355X): 1 sign bit, 4 exponent bits

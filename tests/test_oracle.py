@@ -431,3 +431,114 @@ def test_fp8_codes_avoid_nan_and_stay_in_range(oracle_mod):
     codes = synth.fp8_codes(4, 0, (4096,))
     vals = np.vectorize(oracle_mod.fp8_e4m3)(codes)
     assert np.all(np.isfinite(vals)) and np.abs(vals).max() <= 15.0 and np.abs(vals).min() >= 2 ** -4
+
+
+# ---------------------------------------------------------------- backward (dq, dk, dv)
+
+BWD_CASES = [  # mask, window, window_right, seqstart_q, seqstart_k, Mq, Mkv
+    (0, None, None, None, None, 6, 8),
+    (1, None, None, None, None, 7, 7),
+    (2, None, None, [0, 2, 6], [0, 3, 8], 6, 8),
+    (3, None, None, [0, 2, 6], [0, 3, 8], 6, 8),
+    (4, None, None, None, None, 5, 8),
+    (5, None, None, [0, 4, 6], [0, 2, 8], 6, 8),   # first block: 4 queries, 2 keys -> 2 empty rows
+    (6, 2, 1, None, None, 6, 8),
+    (7, 3, None, None, None, 6, 8),
+    (8, 2, None, [0, 3, 6], [0, 3, 8], 6, 8),
+    (9, 2, None, [0, 2, 6], [0, 3, 8], 6, 8),
+]
+
+
+def _loss_grads_fd(oracle_mod, q, k, v, G, case, h=1e-5):
+    """Central differences of L = sum(out * G) through the forward oracle alone."""
+    mask, w, wr, sq, sk = case[:5]
+
+    def loss(qq, kk, vv):
+        o, _ = oracle_mod.attention(qq, kk, vv, mask=mask, seqstart_q=sq, seqstart_k=sk, window=w,
+                                    window_right=wr)
+        return float(np.sum(o * G))
+
+    grads = []
+    for which in range(3):
+        args = [q.copy(), k.copy(), v.copy()]
+        g = np.zeros_like(args[which])
+        flat = args[which].reshape(-1)
+        for idx in range(flat.size):
+            x0 = flat[idx]
+            flat[idx] = x0 + h
+            lp = loss(*args)
+            flat[idx] = x0 - h
+            lm = loss(*args)
+            flat[idx] = x0
+            g.reshape(-1)[idx] = (lp - lm) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[f"mask{c[0]}" for c in BWD_CASES])
+def test_backward_matches_finite_differences(oracle_mod, case):
+    """The backward, fed the forward's out and lse, equals numerical derivatives of the forward."""
+    mask, w, wr, sq, sk, Mq, Mkv = case
+    q, k, v = rnd(200 + mask, 1, Mq, 2, 4), rnd(210 + mask, 1, Mkv, 2, 4), rnd(220 + mask, 1, Mkv, 2, 3)
+    G = rnd(230 + mask, 1, Mq, 2, 3)
+    o, l = oracle_mod.attention(q, k, v, mask=mask, seqstart_q=sq, seqstart_k=sk, window=w, window_right=wr)
+    dq, dk, dv = oracle_mod.attention_backward(G, o, l, q, k, v, mask=mask, seqstart_q=sq, seqstart_k=sk,
+                                               window=w, window_right=wr)
+    fq, fk, fv = _loss_grads_fd(oracle_mod, q, k, v, G, case)
+    np.testing.assert_allclose(dq, fq, rtol=0, atol=2e-8)
+    np.testing.assert_allclose(dk, fk, rtol=0, atol=2e-8)
+    np.testing.assert_allclose(dv, fv, rtol=0, atol=2e-8)
+    if mask == 5:  # empty rows: no gradient flows through them
+        assert np.all(dq[0, :2] == 0)
+
+
+@pytest.mark.parametrize("mask,win,winr", [(0, None, None), (1, None, None), (6, 4, 3), (7, 5, None)])
+def test_backward_matches_torch_autograd(oracle_mod, mask, win, winr):
+    """fp64 autograd of a dense softmax(scale*QK^T + bias) V, the bias materialised as the pages describe."""
+    import torch
+
+    Mq, Mkv, H, K, Kv = 21, 29, 2, 16, 12
+    q, k, v = rnd(240 + mask, 1, Mq, H, K), rnd(250 + mask, 1, Mkv, H, K), rnd(260 + mask, 1, Mkv, H, Kv)
+    G = rnd(270 + mask, 1, Mq, H, Kv)
+    scale = 0.3
+    bias = torch.from_numpy(brute.materialize(mask, Mq, Mkv, window=win, window_right=winr))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = scale * torch.einsum("bihd,bjhd->bhij", tq, tk) + bias
+    out = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, dim=-1), tv)
+    (out * torch.from_numpy(G)).sum().backward()
+    o, l = oracle_mod.attention(q, k, v, mask=mask, scale=scale, window=win, window_right=winr)
+    dq, dk, dv = oracle_mod.attention_backward(G, o, l, q, k, v, mask=mask, scale=scale, window=win,
+                                               window_right=winr)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_backward_closed_forms(oracle_mod):
+    Mq, Mkv, H = 9, 9, 2
+    k, v = rnd(280, 1, Mkv, H, 5), rnd(281, 1, Mkv, H, 4)
+    G = rnd(282, 1, Mq, H, 4)
+    # q = 0, causal: uniform weights over keys 0..i, so dv_j = sum_{i >= j} G_i / (i + 1)
+    q0 = np.zeros((1, Mq, H, 5))
+    o, l = oracle_mod.attention(q0, k, v, mask=1)
+    _, _, dv = oracle_mod.attention_backward(G, o, l, q0, k, v, mask=1)
+    want = np.zeros_like(dv)
+    for j in range(Mkv):
+        for i in range(j, Mq):
+            want[0, j] += G[0, i] / (i + 1)
+    np.testing.assert_allclose(dv, want, atol=1e-14)
+    # all value rows equal: out does not depend on the scores, so dq = dk = 0 and dv_j = sum_i P_ij G_i
+    q = rnd(283, 1, Mq, H, 5)
+    vc = np.broadcast_to(rnd(284, 1, 1, H, 4), (1, Mkv, H, 4)).copy()
+    o, l = oracle_mod.attention(q, k, vc)
+    dq, dk, dv = oracle_mod.attention_backward(G, o, l, q, k, vc)
+    assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14
+    np.testing.assert_allclose(dv.sum(axis=1), G.sum(axis=1), atol=1e-13)  # each row's weights sum to 1
+    # one key: dq = dk = 0, dv = sum of all upstream rows
+    o, l = oracle_mod.attention(q, k[:, :1], v[:, :1])
+    dq, dk, dv = oracle_mod.attention_backward(G, o, l, q, k[:, :1], v[:, :1])
+    assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14
+    np.testing.assert_allclose(dv[0, 0], G[0].sum(axis=0), atol=1e-13)
+    # zero upstream gradient
+    dq, dk, dv = oracle_mod.attention_backward(np.zeros_like(G), *oracle_mod.attention(q, k, v), q, k, v)
+    assert not dq.any() and not dk.any() and not dv.any()
