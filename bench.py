@@ -39,8 +39,8 @@ def parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=300,
                    help="untimed steps first; ~25 ms of back-to-back launches brings the clock to steady state")
-    p.add_argument("--rows", default="decode,varlen,window,merge,fp32",
-                   help="rows timed after the headline prefill: decode,varlen,window,merge,fp32,copy or none; "
+    p.add_argument("--rows", default="bwd,decode,varlen,window,merge,fp32",
+                   help="rows timed after the headline prefill: bwd,decode,varlen,window,merge,fp32,copy or none; "
                         "copy is a plain 1 GiB device copy used to calibrate the HBM byte counters")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--rocpd", metavar="DB", help="summarise a rocprofv3 results database (kernel durations and "
@@ -281,6 +281,29 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl}}
         del qv, kv, vv, ov, lv
+
+    # ------------------------------------------------------------ backward of the causal prefill
+    if "bwd" in rows:
+        Bb, Mb, Hb, Db = 2, 2048, 32, 128
+        shp = (Bb, Mb, Hb, Db)
+        qb_, kb_, vb_ = (up(x) for x in synth.qkv(2, shp, shp, shp, "bf16"))
+        gb_ = up(synth.normal(2, 3, shp, "bf16"))
+        ob_ = torch.empty_like(qb_)
+        lb_ = torch.empty((Bb, Hb, Mb), dtype=torch.float32, device="cuda")
+        A.attn_fwd(qb_, kb_, vb_, mask=A.MASK_CAUSAL, out=ob_, lse=lb_)
+        dqb, dkb, dvb = torch.empty_like(qb_), torch.empty_like(kb_), torch.empty_like(vb_)
+        wsb = torch.empty(A.attn_bwd_workspace_bytes(Bb, Hb, Mb), dtype=torch.uint8, device="cuda")
+        ms_b = timed(A.prepare_bwd(gb_, qb_, kb_, vb_, ob_, lb_, dqb, dkb, dvb, wsb, mask=A.MASK_CAUSAL), 100, 20, torch)
+        fl_b = 2.5 * 4.0 * Bb * Hb * Mb * Mb * Db / 2  # five products of the forward's size, causal half
+        tf_b = fl_b / (ms_b * 1e-3) / 1e12
+        log(f"backward causal bf16 [2,2048,32,128]: {ms_b * 1e3:.1f} us/call, {tf_b:.1f} TFLOP/s")
+        result["rows"]["bwd_causal"] = {
+            "workload": "attn_bwd of the causal bf16 prefill B=2 M=2048 H=32 K=Kv=128 (prep + dK/dV + dQ kernels)",
+            "ms_per_call": round(ms_b, 5), "value": round(tf_b, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_b,
+                         "note": "algorithmic flops = 2.5x the forward's (dS recomputation not counted)"}}
+        del qb_, kb_, vb_, gb_, ob_, lb_, dqb, dkb, dvb, wsb
 
     # ------------------------------------------------------------ sliding-window causal prefill
     if "window" in rows:

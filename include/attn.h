@@ -119,15 +119,18 @@ typedef struct {
  * Required for the BLOCKDIAG masks, ignored otherwise.  B must be 1.
  * seqstart_q/seqstart_k are DEVICE int32 prefix sums [nseq + 1]: 0, L0, L0+L1,
  * ..., M_total.  seqstart_k NULL means seqstart_k = seqstart_q.
- * max_seqlen_q must be >= every query length.  The offsets live on the device
- * and are not read by the host: offsets that are not monotone, do not start at
- * 0, or exceed max_seqlen_q give unspecified output values but never an
- * out-of-bounds access (the kernels clamp them to [0, M]). */
+ * max_seqlen_q must be >= every query length; max_seqlen_k, read by attn_bwd only,
+ * >= every key length, or <= 0 when not known (Mkv is then assumed).  The offsets
+ * live on the device and are not read by the host: offsets that are not monotone,
+ * do not start at 0, or exceed max_seqlen_q / max_seqlen_k give unspecified output
+ * values but never an out-of-bounds access (the kernels clamp them to [0, M]).
+ * Rows outside every sequence are not written. */
 typedef struct {
     const int32_t *seqstart_q;
     const int32_t *seqstart_k;
     int32_t nseq;
     int32_t max_seqlen_q;
+    int32_t max_seqlen_k;
 } attn_varlen;
 
 /* memory_efficient_attention_forward_requires_grad ("Attention - Core fMHA").
@@ -171,6 +174,29 @@ attn_status attn_partial_ex(const attn_tensor *q, const attn_tensor *k, const at
 attn_status attn_merge(int32_t n_chunks, const attn_tensor *out_chunks,
                        const float *const *lse_chunks, const attn_tensor *out, float *lse_out,
                        attn_stream_t stream);
+
+/* Bytes of device workspace attn_bwd needs: two fp32 rows per query row and head
+ * ([B, H_total, Mq] each, 256-byte aligned). */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H_total, int64_t Mq);
+
+/* memory_efficient_attention_backward ("Attention - Core fMHA"): the gradients of the
+ * forward for an upstream gradient, from the forward's output and LSE and the original
+ * q, k, v (no dropout, no bias gradient).  With P_ij = exp(scale q_i.k_j - lse_i) on the
+ * visible keys: dv_j = sum_i P_ij dout_i; dS_ij = P_ij (dout_i.v_j - dout_i.out_i);
+ * dq_i = scale sum_j dS_ij k_j; dk_j = scale sum_i dS_ij q_i.
+ *   dout, out [B, Mq, (G,) H, D]; q [B, Mq, (G,) H, D]; k, v [B, Mkv, (G,) H, D]; bf16,
+ *     D in {64, 128}; lse fp32 [B, H_total, Mq] as attn_fwd wrote it.
+ *   mask, varlen, scale: exactly those of the forward call.
+ *   dq, dk, dv: shapes of q, k, v, bf16, any strides that do not make two elements
+ *     share memory (a stride-0 expanded head axis is rejected: for expanded GQA keys
+ *     pass dk/dv of the expanded shape and sum over each group's heads).
+ *   workspace: device, 256-byte aligned, >= attn_bwd_workspace_bytes(B, H_total, Mq).
+ *   Three launches on `stream`.  Errors as attn_fwd; nothing is written on error. */
+attn_status attn_bwd(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k,
+                     const attn_tensor *v, const attn_tensor *out, const float *lse,
+                     const attn_mask *mask, const attn_varlen *varlen, float scale, void *workspace,
+                     size_t workspace_bytes, const attn_tensor *dq, const attn_tensor *dk,
+                     const attn_tensor *dv, attn_stream_t stream);
 
 /* Bytes of device workspace attn_decode_splitkv needs (fp32 partial outputs
  * [num_splits, B, H_total, Kv] and LSEs [num_splits, B, H_total], 256-byte aligned). */

@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd", "attn_partial", "attn_fwd_ex", "attn_partial_ex", "attn_merge",
                                            "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_paged",
-                                           "attn_decode_splitkv_fp8", "attn_last_error"])
+                                           "attn_decode_splitkv_fp8", "attn_bwd_workspace_bytes", "attn_bwd",
+                                           "attn_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -257,3 +258,33 @@ def test_fp8_and_f16_tensors_are_rejected_outside_the_fp8_decode():
     assert fwd(q8, q8, q8, q8) == A.ATTN_ERR_INVALID_ARGUMENT and "dtype" in A.attn_last_error()
     assert fwd(h, h, h, h) == A.ATTN_ERR_INVALID_ARGUMENT
     assert fwd(std4(), q8, q8, std4()) == A.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_workspace_and_rejects():
+    B, M, H, D = 2, 256, 4, 128
+    need = A.attn_bwd_workspace_bytes(B, H, M)
+    assert need == 2 * ((B * H * M * 4 + 255) // 256 * 256)
+    t = lambda shape=(B, M, H, D), dt=A.ATTN_DTYPE_BF16, stride=None: tensor(list(shape), dt, stride)
+    m = A.AttnMask(1, 0, 0, 0)
+
+    def call(g=None, q=None, k=None, v=None, o=None, dq=None, dk=None, dv=None, mask=m, ws=FAKE * 256, wsb=need,
+             lse=FAKE, varlen=None):
+        ds = [x if x is not None else t() for x in (g, q, k, v, o, dq, dk, dv)]
+        return A._lib.attn_bwd(*[ctypes.byref(x) for x in ds[:5]], ctypes.c_void_p(lse) if lse else None,
+                               ctypes.byref(mask) if mask is not None else None, varlen, float("nan"),
+                               ctypes.c_void_p(ws), wsb, *[ctypes.byref(x) for x in ds[5:]], None)
+    assert call(wsb=need - 1) == A.ATTN_ERR_WORKSPACE_TOO_SMALL
+    assert call(ws=FAKE * 256 + 16) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(lse=0) == A.ATTN_ERR_INVALID_ARGUMENT and "lse" in A.attn_last_error()
+    assert call(mask=None) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(q=t(dt=A.ATTN_DTYPE_F32)) == A.ATTN_ERR_INVALID_ARGUMENT and "dtype" in A.attn_last_error()
+    f32 = t(dt=A.ATTN_DTYPE_F32)
+    assert call(f32, f32, f32, f32, f32, f32, f32, f32) == A.ATTN_ERR_UNSUPPORTED
+    assert call(dq=t((B, M + 1, H, D))) == A.ATTN_ERR_INVALID_ARGUMENT and "q's shape" in A.attn_last_error()
+    assert call(dv=t((B, M, H, 64))) == A.ATTN_ERR_INVALID_ARGUMENT
+    expanded = t(stride=[M * H * D, H * D, 0, 1])
+    assert call(dk=expanded) == A.ATTN_ERR_INVALID_ARGUMENT and "stride-0" in A.attn_last_error()
+    assert call(mask=A.AttnMask(3, 0, 0, 0)) == A.ATTN_ERR_INVALID_ARGUMENT and "varlen" in A.attn_last_error()
+    assert call(mask=A.AttnMask(7, 0, 0, 0)) == A.ATTN_ERR_INVALID_ARGUMENT and "window_size" in A.attn_last_error()
+    d96 = t((B, M, H, 96))
+    assert call(d96, d96, d96, d96, d96, d96, d96, d96) == A.ATTN_ERR_UNSUPPORTED

@@ -508,3 +508,134 @@ def test_fp8_decode_full_size(A):
     assert not torch.isnan(out).any()
     del k, v
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ backward (dq, dk, dv)
+
+from tests.helpers import TOL_BWD_ABS, TOL_BWD_REL  # noqa: E402
+
+
+def check_grads(got, ref, what):
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        err, mag = maxerr(host64(g), r), float(np.abs(r).max()) if r.size else 0.0
+        say(f"  {what} {name}: max|d|={err:.3e} max|ref|={mag:.3e} rel={err / max(mag, 1e-30):.2e}")
+        assert err <= TOL_BWD_REL * mag + TOL_BWD_ABS, f"{what} {name}: error {err} (max|ref| {mag})"
+
+
+def run_bwd(A, qh, kh, vh, gh, mask=0, scale=None, window=None, window_right=None, seqstarts=None, sk=None):
+    """GPU forward then backward on bf16 inputs; oracle backward on the exact values."""
+    q, k, v, g = dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), dev(gh, "bf16")
+    kw = {}
+    if mask in oracle.PACKED:
+        ssq = torch.from_numpy(seqstarts).cuda()
+        ssk = torch.from_numpy(sk if sk is not None else seqstarts).cuda()
+        lq = np.diff(seqstarts)
+        lk = np.diff(sk if sk is not None else seqstarts)
+        kw = dict(seqstart_q=ssq, seqstart_k=ssk, max_seqlen_q=int(lq.max()))
+    wkw = {}
+    if mask == oracle.MASK_LOCAL_BR:
+        wkw = dict(window_left=window, window_right=window_right)
+    elif mask in (oracle.MASK_CAUSAL_LOCAL_BR, oracle.MASK_BLOCKDIAG_CAUSAL_LOCAL, oracle.MASK_BLOCKDIAG_CAUSAL_LOCAL_BR):
+        wkw = dict(window_size=window)
+    out, lse = A.attn_fwd(q, k, v, mask=mask, scale=scale, **kw, **wkw)
+    if mask in oracle.PACKED:
+        kw["max_seqlen_k"] = int(lk.max())
+    dq, dk, dv = A.attn_bwd(g, q, k, v, out, lse, mask=mask, scale=scale, **kw, **wkw)
+    torch.cuda.synchronize()
+    okw = dict(mask=mask, scale=scale, window=window, window_right=window_right, seqstart_q=seqstarts, seqstart_k=sk)
+    q64, k64, v64, g64 = (synth.to_f64(x, "bf16") for x in (qh, kh, vh, gh))
+    oo, ol = oracle.attention(q64, k64, v64, **okw)
+    ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, **okw)
+    return (dq, dk, dv), ref
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask,win,winr,Mq,Mkv", [
+    (0, None, None, 200, 300), (1, None, None, 333, 333), (4, None, None, 150, 290), (4, None, None, 290, 150),
+    (6, 50, 20, 200, 260), (7, 100, None, 257, 257)])
+def test_bwd_ragged_shapes_masks(A, D, mask, win, winr, Mq, Mkv):
+    say(f"case: bwd D={D} mask={mask} win={win},{winr} Mq={Mq} Mkv={Mkv}")
+    B, H = 2, 3
+    qh, kh, vh = synth.qkv(900 + mask + D, (B, Mq, H, D), (B, Mkv, H, D), (B, Mkv, H, D))
+    gh = synth.normal(901 + mask + D, 3, (B, Mq, H, D), "bf16")
+    got, ref = run_bwd(A, qh, kh, vh, gh, mask=mask, window=win, window_right=winr)
+    check_grads(got, ref, f"mask {mask}")
+    if mask == 4 and Mq > Mkv:  # bottom-right with more queries than keys: the first rows see nothing
+        assert torch.all(got[0][:, :Mq - Mkv] == 0)
+
+
+@pytest.mark.parametrize("mask,win", [(2, None), (3, None), (5, None), (8, 70), (9, 70)])
+def test_bwd_packed_masks(A, mask, win):
+    sq = np.array([0, 130, 131, 400, 517], dtype=np.int32)
+    sk = np.array([0, 100, 180, 400, 650], dtype=np.int32) if mask in (2, 5, 9) else sq
+    H, D = 2, 128
+    say(f"case: bwd packed mask={mask} win={win}")
+    qh, kh, vh = synth.qkv(950 + mask, (1, int(sq[-1]), H, D), (1, int(sk[-1]), H, D), (1, int(sk[-1]), H, D))
+    gh = synth.normal(951 + mask, 3, (1, int(sq[-1]), H, D), "bf16")
+    got, ref = run_bwd(A, qh, kh, vh, gh, mask=mask, window=win, seqstarts=sq, sk=sk)
+    check_grads(got, ref, f"packed mask {mask}")
+
+
+def test_bwd_negative_scale_strided_5d(A):
+    """5-D [B, M, G, H, D] inputs viewed out of a wider buffer, negative scale, gradients written
+    into strided views."""
+    B, M, G, Hg, D = 1, 192, 2, 2, 64
+    say("case: bwd 5-D strided, scale=-0.2")
+    qh, kh, vh = synth.qkv(970, (B, M, G, Hg, D), (B, M, G, Hg, D), (B, M, G, Hg, D))
+    gh = synth.normal(971, 3, (B, M, G, Hg, D), "bf16")
+    wide = lambda x: dev(np.concatenate([x, x], axis=-1), "bf16")[..., :D]
+    q, k, v, g = wide(qh), wide(kh), wide(vh), wide(gh)
+    out, lse = A.attn_fwd(q, k, v, mask=1, scale=-0.2)
+    dq = torch.zeros((B, M, G, Hg, 2 * D), dtype=torch.bfloat16, device="cuda")[..., D:]
+    dk = torch.zeros_like(dq.contiguous())
+    dv = torch.zeros_like(dq.contiguous())
+    A.attn_bwd(g, q, k, v, out, lse, mask=1, scale=-0.2, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    flat = lambda x: synth.to_f64(x, "bf16").reshape(B, M, G * Hg, D)
+    q64, k64, v64, g64 = flat(qh), flat(kh), flat(vh), flat(gh)
+    oo, ol = oracle.attention(q64, k64, v64, mask=1, scale=-0.2)
+    ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, mask=1, scale=-0.2)
+    check_grads([x.reshape(B, M, G * Hg, D) for x in (dq, dk, dv)], ref, "5-D strided")
+
+
+def test_bwd_expanded_gqa(A):
+    """K/V heads broadcast with stride 0 (GQA); dk/dv come back per expanded head."""
+    B, M, G, Hg, D = 1, 300, 2, 3, 128
+    say("case: bwd expanded GQA")
+    qh = synth.normal(980, 0, (B, M, G, Hg, D), "bf16")
+    kb, vb = synth.normal(980, 1, (B, M, G, 1, D), "bf16"), synth.normal(980, 2, (B, M, G, 1, D), "bf16")
+    gh = synth.normal(980, 3, (B, M, G, Hg, D), "bf16")
+    q, g = dev(qh, "bf16"), dev(gh, "bf16")
+    k, v = dev(kb, "bf16").expand(B, M, G, Hg, D), dev(vb, "bf16").expand(B, M, G, Hg, D)
+    out, lse = A.attn_fwd(q, k, v, mask=1)
+    dq = torch.empty_like(q)
+    dk = torch.empty((B, M, G, Hg, D), dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty_like(dk)
+    A.attn_bwd(g, q, k, v, out, lse, mask=1, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    rep = lambda x: synth.to_f64(np.repeat(x, Hg, axis=3), "bf16").reshape(B, M, G * Hg, D)
+    q64, g64 = synth.to_f64(qh, "bf16").reshape(B, M, G * Hg, D), synth.to_f64(gh, "bf16").reshape(B, M, G * Hg, D)
+    k64, v64 = rep(kb), rep(vb)
+    oo, ol = oracle.attention(q64, k64, v64, mask=1)
+    ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, mask=1)
+    check_grads([x.reshape(B, M, G * Hg, D) for x in (dq, dk, dv)], ref, "expanded GQA")
+
+
+def test_bwd_causal_full_size(A):
+    """The causal [2, 2048, 32, 128] workload: full launch, oracle on sampled (b, h)."""
+    B, M, H, D = 2, 2048, 32, 128
+    say("case: bwd causal full size")
+    qh, kh, vh = synth.qkv(2, (B, M, H, D), (B, M, H, D), (B, M, H, D))
+    gh = synth.normal(2, 3, (B, M, H, D), "bf16")
+    q, k, v, g = dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), dev(gh, "bf16")
+    out, lse = A.attn_fwd(q, k, v, mask=1)
+    dq, dk, dv = A.attn_bwd(g, q, k, v, out, lse, mask=1)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (1, 17), (1, 31)]:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        q64, k64, v64, g64 = (synth.to_f64(x[sl], "bf16") for x in (qh, kh, vh, gh))
+        oo, ol = oracle.attention(q64, k64, v64, mask=1)
+        ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, mask=1)
+        check_grads([x[sl] for x in (dq, dk, dv)], ref, f"b={b} h={h}")
+    for x in (dq, dk, dv):
+        assert not torch.isnan(x).any()

@@ -45,7 +45,7 @@ class AttnMask(ctypes.Structure):
 
 class AttnVarlen(ctypes.Structure):
     _fields_ = [("seqstart_q", ctypes.c_void_p), ("seqstart_k", ctypes.c_void_p), ("nseq", ctypes.c_int32),
-                ("max_seqlen_q", ctypes.c_int32)]
+                ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32)]
 
 
 _P = ctypes.POINTER
@@ -75,6 +75,11 @@ _lib.attn_decode_splitkv_fp8.argtypes = [_T, _T, _T, _T, _T, ctypes.c_void_p, ct
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                          ctypes.c_void_p, ctypes.c_size_t, _T, ctypes.c_void_p, ctypes.c_void_p]
 _lib.attn_decode_splitkv_fp8.restype = ctypes.c_int
+_lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+_lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+_lib.attn_bwd.argtypes = [_T, _T, _T, _T, _T, ctypes.c_void_p, _P(AttnMask), _P(AttnVarlen), ctypes.c_float,
+                          ctypes.c_void_p, ctypes.c_size_t, _T, _T, _T, ctypes.c_void_p]
+_lib.attn_bwd.restype = ctypes.c_int
 _lib.attn_last_error.argtypes = []
 _lib.attn_last_error.restype = ctypes.c_char_p
 
@@ -131,7 +136,7 @@ def _htot(t: torch.Tensor) -> int:
     return t.shape[2] * t.shape[3] if t.dim() == 5 else t.shape[2]
 
 
-def _varlen(seqstart_q, seqstart_k, max_seqlen_q):
+def _varlen(seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k=None):
     if seqstart_q is None:
         return None, None
     vl = AttnVarlen()
@@ -139,6 +144,7 @@ def _varlen(seqstart_q, seqstart_k, max_seqlen_q):
     vl.seqstart_k = seqstart_k.data_ptr() if seqstart_k is not None else None
     vl.nseq = seqstart_q.numel() - 1
     vl.max_seqlen_q = int(max_seqlen_q)
+    vl.max_seqlen_k = int(max_seqlen_k or 0)
     return ctypes.byref(vl), vl
 
 
@@ -350,6 +356,46 @@ def prepare_decode_fp8(q, k, v, k_scale_shift, v_scale_shift, num_splits, worksp
                          num_splits, scale, workspace, out, lse, stream)
     return Prepared(_lib.attn_decode_splitkv_fp8, args,
                     (ds, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, workspace, out, lse))
+
+
+def attn_bwd_workspace_bytes(B: int, H_total: int, Mq: int) -> int:
+    return int(_lib.attn_bwd_workspace_bytes(B, H_total, Mq))
+
+
+def _bwd_args(dout, q, k, v, out, lse, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k,
+              window_size, window_left, window_right, workspace, dq, dk, dv, stream):
+    vref, vl = _varlen(seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k)
+    m = AttnMask(int(mask), int(window_size or 0), int(window_left or 0), int(window_right or 0))
+    ds = [desc(x) for x in (dout, q, k, v, out, dq, dk, dv)]
+    args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), ctypes.byref(ds[3]), ctypes.byref(ds[4]),
+            _ptr(lse), ctypes.byref(m), vref, _scale(scale), _ptr(workspace), workspace.numel(),
+            ctypes.byref(ds[5]), ctypes.byref(ds[6]), ctypes.byref(ds[7]), _stream(stream))
+    return args, (ds, vl, m)
+
+
+def attn_bwd(dout, q, k, v, out, lse, mask=MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None,
+             max_seqlen_q=None, max_seqlen_k=None, window_size=None, window_left=None, window_right=None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """memory_efficient_attention_backward: returns (dq, dk, dv) for the forward of the same arguments."""
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        need = attn_bwd_workspace_bytes(q.shape[0], _htot(q), q.shape[1])
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    args, _keep = _bwd_args(dout, q, k, v, out, lse, mask, scale, seqstart_q, seqstart_k, max_seqlen_q,
+                            max_seqlen_k, window_size, window_left, window_right, workspace, dq, dk, dv, stream)
+    _check(_lib.attn_bwd(*args))
+    return dq, dk, dv
+
+
+def prepare_bwd(dout, q, k, v, out, lse, dq, dk, dv, workspace, mask=MASK_NONE, scale=None, seqstart_q=None,
+                seqstart_k=None, max_seqlen_q=None, max_seqlen_k=None, window_size=None, window_left=None,
+                window_right=None, stream=None) -> Prepared:
+    """attn_bwd with every argument marshalled up front."""
+    args, keep = _bwd_args(dout, q, k, v, out, lse, mask, scale, seqstart_q, seqstart_k, max_seqlen_q,
+                           max_seqlen_k, window_size, window_left, window_right, workspace, dq, dk, dv, stream)
+    return Prepared(_lib.attn_bwd, args, (keep, dout, q, k, v, out, lse, dq, dk, dv, workspace))
 
 
 def default_scale(K: int) -> float:

@@ -333,6 +333,129 @@ attn_status attn_merge(int32_t n_chunks, const attn_tensor *out_chunks, const fl
     return launch_status(attn::launch_merge(a, (hipStream_t)stream), fn);
 }
 
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H_total, int64_t Mq) {
+    if (B < 0 || H_total < 0 || Mq < 0) return 0;
+    return 2 * align256((size_t)B * (size_t)H_total * (size_t)Mq * 4);
+}
+
+attn_status attn_bwd(const attn_tensor *dot, const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
+                     const attn_tensor *ot, const float *lse, const attn_mask *mask, const attn_varlen *varlen,
+                     float scale, void *workspace, size_t workspace_bytes, const attn_tensor *dqt,
+                     const attn_tensor *dkt, const attn_tensor *dvt, attn_stream_t stream) {
+    const char *fn = "attn_bwd";
+    View g, q, k, v, o, dq, dk, dv;
+    attn_status st;
+    if ((st = make_view(dot, "dout", &g)) != ATTN_OK) return st;
+    if ((st = make_view(qt, "q", &q)) != ATTN_OK) return st;
+    if ((st = make_view(kt, "k", &k)) != ATTN_OK) return st;
+    if ((st = make_view(vt, "v", &v)) != ATTN_OK) return st;
+    if ((st = make_view(ot, "out", &o)) != ATTN_OK) return st;
+    if ((st = make_view(dqt, "dq", &dq)) != ATTN_OK) return st;
+    if ((st = make_view(dkt, "dk", &dk)) != ATTN_OK) return st;
+    if ((st = make_view(dvt, "dv", &dv)) != ATTN_OK) return st;
+    if (!mask) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: mask is NULL", fn);
+    for (const View *x : {&g, &k, &v, &o, &dq, &dk, &dv})
+        if (x->dtype != q.dtype) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: all tensors must share q's dtype", fn);
+    for (const View *x : {&g, &k, &v, &o, &dq, &dk, &dv})
+        if (!same_heads(*x, q)) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: rank and head axes must match q's", fn);
+    auto same_shape = [](const View &a_, const View &b_) { return a_.B == b_.B && a_.M == b_.M && a_.D == b_.D; };
+    if (!same_shape(g, q) || !same_shape(o, q) || !same_shape(dq, q))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: dout, out and dq must have q's shape", fn);
+    if (!same_shape(dk, k) || !same_shape(v, k) || !same_shape(dv, k))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: v, dk and dv must have k's shape", fn);
+    if (k.B != q.B) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: batch sizes differ", fn);
+    if (k.D != q.D) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q and k head dims differ", fn);
+    // gradients are written once per element: no axis of extent > 1 may have stride 0
+    for (const View *x : {&dq, &dk, &dv}) {
+        const int64_t ext[4] = {x->B, x->M, x->G, x->H};
+        const int64_t str[4] = {x->s.b, x->s.m, x->s.g, x->s.h};
+        for (int i = 0; i < 4; ++i)
+            if (ext[i] > 1 && str[i] == 0)
+                return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: gradient tensors must not have stride-0 axes", fn);
+    }
+    if (q.dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED, "%s: the backward is built for bf16", fn);
+    if (!(q.D == 64 || q.D == 128)) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim must be 64 or 128", fn);
+    // tiles of q/dout (key-side kernel) and k/v (query-side kernel) go through buffer descriptors
+    for (const View *x : {&q, &g, &k, &v}) {
+        if (x->M > 1 && x->s.m < x->D)
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: row strides must be >= the head dim", fn);
+        if (x->s.m * 2 * 64 + x->D * 2 >= (int64_t)1 << 31)
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: row stride too large for 32-bit tile offsets", fn);
+    }
+    MaskSpec ms;
+    if ((st = mask_spec(fn, *mask, &ms)) != ATTN_OK) return st;
+    if (ms.packed) {
+        if (!varlen) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block-diagonal masks need varlen", fn);
+        if (q.B != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: packed sequences need B == 1", fn);
+        if (varlen->nseq < 1 || !varlen->seqstart_q)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: varlen needs nseq >= 1 and seqstart_q", fn);
+        if (varlen->max_seqlen_q < 0 || varlen->max_seqlen_q > q.M)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: max_seqlen_q must be in [0, Mq]", fn);
+        if (varlen->max_seqlen_k > k.M)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: max_seqlen_k must be <= Mkv", fn);
+        if ((((uintptr_t)varlen->seqstart_q) % 4) || (((uintptr_t)varlen->seqstart_k) % 4))
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: seqstart arrays must be 4-byte aligned", fn);
+    }
+    if (!(std::isnan(scale) || std::isfinite(scale)))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: scale must be finite (or NaN for 1/sqrt(K))", fn);
+    const int64_t rows = q.B * htot(q) * q.M;
+    if (rows > 0 && (!lse || ((uintptr_t)lse) % 4))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: lse is NULL or not 4-byte aligned", fn);
+    const size_t need = attn_bwd_workspace_bytes(q.B, htot(q), q.M);
+    if (rows > 0 && (!workspace || ((uintptr_t)workspace) % 256))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: workspace is NULL or not 256-byte aligned", fn);
+    if (rows > 0 && workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu", fn, need, workspace_bytes);
+    if (q.B == 0 || htot(q) == 0 || (q.M == 0 && k.M == 0)) return ok();
+
+    attn::BwdArgs a;
+    a.q = q.p;
+    a.k = k.p;
+    a.v = v.p;
+    a.o = o.p;
+    a.dout = g.p;
+    a.dq = dq.p;
+    a.dk = dk.p;
+    a.dv = dv.p;
+    a.sq = q.s;
+    a.sk = k.s;
+    a.sv = v.s;
+    a.so = o.s;
+    a.sdo = g.s;
+    a.sdq = dq.s;
+    a.sdk = dk.s;
+    a.sdv = dv.s;
+    a.lse = lse;
+    a.ws_d = (float *)workspace;
+    a.ws_l2 = (float *)((char *)workspace + need / 2);
+    a.B = (int)q.B;
+    a.Mq = (int)q.M;
+    a.Mkv = (int)k.M;
+    a.Htot = (int)htot(q);
+    a.Hin = (int)q.H;
+    a.D = (int)q.D;
+    const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)q.D) : (double)scale;
+    a.scale = (float)sc;
+    a.scale_log2 = (float)(sc * 1.4426950408889634);
+    a.packed = ms.packed;
+    a.bottom_right = ms.bottom_right;
+    a.wl = ms.wl;
+    a.wr = ms.wr;
+    if (ms.packed) {
+        a.seqstart_q = varlen->seqstart_q;
+        a.seqstart_k = varlen->seqstart_k;
+        a.nseq = varlen->nseq;
+        a.max_seqlen_q = varlen->max_seqlen_q;
+        a.max_seqlen_k = varlen->max_seqlen_k > 0 ? varlen->max_seqlen_k : (int)k.M;
+    } else {
+        a.seqstart_q = a.seqstart_k = nullptr;
+        a.nseq = 1;
+        a.max_seqlen_q = a.Mq;
+        a.max_seqlen_k = a.Mkv;
+    }
+    return launch_status(attn::launch_bwd_bf16(a, (hipStream_t)stream), fn);
+}
+
 size_t attn_decode_workspace_bytes(int64_t B, int64_t H_total, int64_t Kv, int32_t num_splits) {
     if (B < 0 || H_total < 0 || Kv < 0 || num_splits < 1) return 0;
     const size_t rows = (size_t)num_splits * (size_t)B * (size_t)H_total;

@@ -1,0 +1,520 @@
+// Fused attention backward for bf16 inputs on gfx950 matrix cores.
+//
+// Computes dq, dk, dv of the forward (MSLK kernel reference, "Attention - Core fMHA":
+// memory_efficient_attention_backward consumes the upstream gradient, the forward's
+// output and LSE and the original q, k, v; masks from "Attention - Biases & masks").
+// With P_ij = exp(scale q_i.k_j - lse_i) on the visible keys:
+//   dv_j = sum_i P_ij dout_i,  dS_ij = P_ij (dout_i.v_j - D_i),  D_i = dout_i.out_i,
+//   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i.
+// The score matrix is never stored: P is rebuilt from the saved LSE tile by tile.
+//
+// Three launches:
+//   1. bwd_prep_kernel: D_i and the base-2 LSE L_i = lse_i log2(e) (+inf for a row with
+//      no visible key, so every rebuilt P of that row is exactly 0), one pass over out
+//      and dout into a caller workspace.
+//   2. bwd_dkdv_kernel: a workgroup owns 32 keys per wave of one (batch, head, sequence);
+//      those keys' K and V rows stay in registers as matrix-core operands while 64-row
+//      tiles of Q and dout (and their L, D) stream through a 2-stage LDS ring.  Per tile:
+//      S = Q K^T and dP = dout V^T (lane l owns key l%32 and 16 query rows of each
+//      32-row block), P and dS in fp32, then dV^T += dout^T P and dK^T += Q^T dS with the
+//      A operands read transposed from the row-major LDS tiles.
+//   3. bwd_dq_kernel: the forward's arrangement (8 waves, 32 query rows each; q and
+//      dout in registers, 64-key tiles of K and V through LDS): S^T = K Q^T and
+//      dP^T = V dout^T (lane l owns query row l%32), dS^T, then dQ^T += K^T dS^T.
+// P is rounded to bf16 for dV and dS for dK and dQ; every product accumulates in fp32.
+// Same matrix-core layout as the forward (v_mfma_f32_32x32x16_bf16): a B operand taken
+// from C-layout registers gives lane half h the rows {8a + 4h + 0..3} of each 16-row
+// step, which fixes the k order, and the transposed A operand is read with
+// ds_read_b64_tr_b16 from the same swizzled row-major tiles.
+#include <type_traits>
+
+#include "kernels.h"
+#include "tile_common.h"
+
+namespace attn {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int BQ = 64;  // query rows per streamed tile (dK/dV kernel)
+constexpr int BN = 64;  // keys per streamed tile (dQ kernel)
+
+__device__ __forceinline__ int clampk(int64_t x, int64_t lo, int64_t hi) {
+    return (int)(x < lo ? lo : (x > hi ? hi : x));
+}
+
+// Sequence bounds of workgroup sequence `seq`: query rows [qs, qe), key rows [ks, ke).
+__device__ __forceinline__ void seq_bounds(const BwdArgs &a, int seq, int &qs, int &qe, int &ks, int &ke) {
+    qs = 0, qe = a.Mq, ks = 0, ke = a.Mkv;
+    if (a.packed) {
+        const int32_t *skp = a.seqstart_k ? a.seqstart_k : a.seqstart_q;
+        qs = min(max(a.seqstart_q[seq], 0), a.Mq);
+        qe = min(max(a.seqstart_q[seq + 1], qs), a.Mq);
+        ks = min(max(skp[seq], 0), a.Mkv);
+        ke = min(max(skp[seq + 1], ks), a.Mkv);
+    }
+}
+
+// ------------------------------------------------------------------ 1. D and base-2 LSE per row
+
+template <int HD>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+    constexpr int LPR = HD / 8;     // lanes per row, 8 bf16 each
+    constexpr int RPB = 256 / LPR;  // rows per workgroup
+    const int64_t rows = (int64_t)a.B * a.Htot * a.Mq;
+    const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int cl = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (r < rows) {
+        const int i = (int)(r % a.Mq);
+        const int64_t bh = r / a.Mq;
+        const int hf = (int)(bh % a.Htot), b = (int)(bh / a.Htot);
+        const u32x4 ow = *(const u32x4 *)((const __bf16 *)a.o + (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) +
+                                          (int64_t)i * a.so.m + cl * 8);
+        const u32x4 gw = *(const u32x4 *)((const __bf16 *)a.dout + (int64_t)b * a.sdo.b +
+                                          head_offset(a.sdo, hf, a.Hin) + (int64_t)i * a.sdo.m + cl * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(gw[e] << 16), acc);
+            acc = fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), acc);
+        }
+    }
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (r < rows && cl == 0) {
+        a.ws_d[r] = acc;
+        const float l = a.lse[r];
+        a.ws_l2[r] = l == -INFINITY ? INFINITY : l * kLog2e;
+    }
+}
+
+// ------------------------------------------------------------------ 2. dK and dV
+
+// Transposed-read LDS offsets inside a row-major [rows, HD] tile: lane i of 16-lane group G
+// addresses row 4*hh + i/4 (+ 8e, + multiples of 16) and columns mb*32 + 16*(G&1) + 4*(i%4).
+template <int HD, int MB>
+__device__ __forceinline__ void tr_offsets(int lane, int (&taddr)[MB][2]) {
+    constexpr int ROWB = HD * 2;
+    const int hh = lane >> 5;
+    const int trow = 4 * hh + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int row = trow + 8 * e, col = mb * 32 + tcol;
+            taddr[mb][e] = row * ROWB + (((col >> 3) ^ swz<HD>(row)) << 4) + ((col & 4) << 1);
+        }
+}
+
+// A operand (32 columns x 16 rows, transposed) at byte offset `off` of an LDS tile.
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char LDS_AS *base, int off0, int off1) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS *)(base + off0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS *)(base + off1));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int HD, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
+    constexpr int NT = NW * 64;
+    constexpr int BK = NW * 32;               // keys per workgroup
+    constexpr int ROWB = HD * 2;              // bytes per tile row
+    constexpr int CPR = HD / 8;               // 16-byte chunks per row
+    constexpr int TILE_BYTES = BQ * ROWB;     // one Q or dout tile
+    constexpr int STAGES = 2;
+    constexpr int LSD_BASE = STAGES * 2 * TILE_BYTES;  // then per stage 64 L values and 64 D values
+    constexpr int ROUNDS = TILE_BYTES / 16 / NT;
+    constexpr int KS = HD / 16, MB = HD / 32;
+    static_assert(ROUNDS >= 1 && ROUNDS * NT * 16 == TILE_BYTES, "tile split");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[LSD_BASE + STAGES * 2 * BQ * 4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // ---- which (key tile, sequence, batch*head); key tiles in ascending order
+    const int BH = a.B * a.Htot;
+    int id = blockIdx.x;
+    const int bh = id % BH;
+    id /= BH;
+    const int seq = id % a.nseq;
+    const int ktile = id / a.nseq;
+    const int b = bh / a.Htot, hf = bh % a.Htot;
+    int qs, qe, ks, ke;
+    seq_bounds(a, seq, qs, qe, ks, ke);
+    const int Lq = qe - qs, Lk = ke - ks;
+    const int k0 = ktile * BK;
+    if (k0 >= Lk) return;
+    const int k1 = min(k0 + BK, Lk);
+    const int64_t shift = a.bottom_right ? (int64_t)Lk - Lq : 0;
+    // key j is visible from row i iff i + shift - wl <= j <= i + shift + wr
+    const int qbeg = clampk((int64_t)k0 - shift - a.wr, 0, Lq);
+    const int qend = clampk((int64_t)k1 - 1 - shift + a.wl + 1, 0, Lq);
+    const int tb = qbeg / BQ;
+    const int te = qend > qbeg ? (qend + BQ - 1) / BQ : tb;
+    // tiles [ua, ub): every row < Lq and every key of [k0, k1) inside every row's window
+    int ua = (clampk((int64_t)k1 - 1 - shift - a.wr, 0, Lq) + BQ - 1) / BQ;
+    int ub = clampk(min((int64_t)k0 - shift + a.wl, (int64_t)Lq - 1) + 1, 0, Lq) / BQ;
+    ua = min(max(ua, tb), te);
+    ub = min(max(ub, ua), te);
+
+    const __bf16 *qp = (const __bf16 *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin) + (int64_t)qs * a.sq.m;
+    const __bf16 *gp =
+        (const __bf16 *)a.dout + (int64_t)b * a.sdo.b + head_offset(a.sdo, hf, a.Hin) + (int64_t)qs * a.sdo.m;
+    const __bf16 *kp = (const __bf16 *)a.k + (int64_t)b * a.sk.b + head_offset(a.sk, hf, a.Hin) + (int64_t)ks * a.sk.m;
+    const __bf16 *vp = (const __bf16 *)a.v + (int64_t)b * a.sv.b + head_offset(a.sv, hf, a.Hin) + (int64_t)ks * a.sv.m;
+    const int64_t wrow = ((int64_t)b * a.Htot + hf) * a.Mq + qs;  // workspace row of local query 0
+    const unsigned qstride = (unsigned)a.sq.m * 2u, gstride = (unsigned)a.sdo.m * 2u;
+
+    // ---- async tile loads: Q and dout rows of one 64-row tile, and their L and D values
+    unsigned qoff[ROUNDS], goff[ROUNDS];
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+        const int p = (r * NW + wave) * 64 + lane;
+        const int row = p / CPR, c = (p % CPR) ^ swz<HD>(row);
+        qoff[r] = row * qstride + c * 16;
+        goff[r] = row * gstride + c * 16;
+    }
+    const unsigned smem_base = (unsigned)(unsigned long long)(unsigned char LDS_AS *)smem;
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const int q0 = t * BQ;
+        const int nvalid = min(BQ, Lq - q0);
+        const int stage = (t - tb) % STAGES;
+        const unsigned st = smem_base + stage * 2 * TILE_BYTES;
+        const i32x4 qr = make_rsrc(qp + (int64_t)q0 * a.sq.m, (nvalid - 1) * qstride + ROWB);
+        const i32x4 gr = make_rsrc(gp + (int64_t)q0 * a.sdo.m, (nvalid - 1) * gstride + ROWB);
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) dma16(qr, qoff[r], st + (r * NW + wave) * 1024);
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) dma16(gr, goff[r], st + TILE_BYTES + (r * NW + wave) * 1024);
+        if (wave == 0) {  // rows past the sequence read as 0 and are always masked
+            const unsigned ls = smem_base + LSD_BASE + stage * 2 * BQ * 4;
+            dma4(make_rsrc(a.ws_l2 + wrow + q0, nvalid * 4), lane * 4, ls);
+            dma4(make_rsrc(a.ws_d + wrow + q0, nvalid * 4), lane * 4, ls + BQ * 4);
+        }
+    };
+
+    // ---- this wave's 32 keys: K and V rows as B operands, resident for the whole kernel
+    const int kw0 = k0 + wave * 32;  // first local key of this wave
+    const int key = kw0 + l32;       // this lane's key
+    bf16x8 kf[KS], vf[KS];
+    if (key < Lk) {
+        const u32x4 *ksrc = (const u32x4 *)(kp + (int64_t)key * a.sk.m + 8 * hh);
+        const u32x4 *vsrc = (const u32x4 *)(vp + (int64_t)key * a.sv.m + 8 * hh);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            kf[s] = __builtin_bit_cast(bf16x8, ksrc[2 * s]);
+            vf[s] = __builtin_bit_cast(bf16x8, vsrc[2 * s]);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kf[s] = vf[s] = bf16x8{};
+    }
+    // rows that see this key: [qlo, qhi]
+    const int qlo = clampk((int64_t)key - shift - a.wr, 0, Lq);
+    const int qhi = clampk((int64_t)key - shift + a.wl, -1, Lq - 1);
+    const float c = a.scale_log2;
+
+    int raddr[KS];  // row reads: row l32 (+ 32 per block), chunk 2s + hh
+#pragma unroll
+    for (int s = 0; s < KS; ++s) raddr[s] = l32 * ROWB + (((2 * s + hh) ^ swz<HD>(l32)) << 4);
+    int taddr[MB][2];
+    tr_offsets<HD, MB>(lane, taddr);
+
+    f32x16 dv[MB], dk[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) dv[i] = dk[i] = f32x16{};
+
+    auto step = [&](int t, auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const int q0 = t * BQ;
+        const int stage = (t - tb) % STAGES;
+        wait_barrier<0>();
+        if (t + 1 < te) issue(t + 1);
+        if (kw0 >= Lk) return;
+        if (MASKED && ((int64_t)kw0 > (int64_t)q0 + BQ - 1 + shift + a.wr ||
+                       (int64_t)kw0 + 31 < (int64_t)q0 + shift - a.wl))
+            return;
+        const unsigned char LDS_AS *st = (const unsigned char LDS_AS *)smem + stage * 2 * TILE_BYTES;
+        const float LDS_AS *ls = (const float LDS_AS *)(smem + LSD_BASE + stage * 2 * BQ * 4);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            // S = Q K^T and dP = dout V^T for 32 query rows: lane owns key l32, rows 8g + 4hh + j
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const bf16x8 qa = *(const bf16x8 LDS_AS *)(st + raddr[k] + qb * 32 * ROWB);
+                const bf16x8 ga = *(const bf16x8 LDS_AS *)(st + TILE_BYTES + raddr[k] + qb * 32 * ROWB);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[k], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[k], dp, 0, 0, 0);
+            }
+            float p[16], ds[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int row = qb * 32 + 8 * g + 4 * hh;
+                const f32x4 l2 = *(const f32x4 LDS_AS *)(ls + row);
+                const f32x4 dd = *(const f32x4 LDS_AS *)(ls + BQ + row);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * g + j;
+                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[j]));
+                    if (MASKED) {
+                        const int q = q0 + row + j;
+                        if (q < qlo || q > qhi) pr = 0.f;
+                    }
+                    p[r] = pr;
+                    ds[r] = pr * (dp[r] - dd[j]);
+                }
+            }
+            // bf16 operands in the product's k order: step kt, element i <-> register 8kt + i
+            bf16x8 pb[2], dsb[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    pb[kt][i] = (__bf16)p[8 * kt + i];
+                    dsb[kt][i] = (__bf16)ds[8 * kt + i];
+                }
+            // dV^T += dout^T P and dK^T += Q^T dS over the two 16-row steps of this block
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int roff = (qb * 32 + kt * 16) * ROWB;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const bf16x8 gt = tr_frag(st + TILE_BYTES, taddr[mb][0] + roff, taddr[mb][1] + roff);
+                    dv[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt, pb[kt], dv[mb], 0, 0, 0);
+                    const bf16x8 qt = tr_frag(st, taddr[mb][0] + roff, taddr[mb][1] + roff);
+                    dk[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsb[kt], dk[mb], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    if (tb < te) issue(tb);
+    int t = tb;
+    for (; t < ua; ++t) step(t, std::true_type{});
+    for (; t < ub; ++t) step(t, std::false_type{});
+    for (; t < te; ++t) step(t, std::true_type{});
+
+    // ---- store: lane owns key `key`; register r of block mb is column 32mb + 8(r/4) + 4hh + r%4
+    if (key < Lk) {
+        unsigned char *dkp = (unsigned char *)a.dk;
+        unsigned char *dvp = (unsigned char *)a.dv;
+        const int64_t kb_ = (int64_t)b * a.sdk.b + head_offset(a.sdk, hf, a.Hin) + (int64_t)(ks + key) * a.sdk.m;
+        const int64_t vb_ = (int64_t)b * a.sdv.b + head_offset(a.sdv, hf, a.Hin) + (int64_t)(ks + key) * a.sdv.m;
+        const float sc = a.scale;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = mb * 32 + 8 * g + 4 * hh;
+                *(bf16x4 *)(dkp + (kb_ + d0) * 2) =
+                    bf16x4{(__bf16)(dk[mb][4 * g] * sc), (__bf16)(dk[mb][4 * g + 1] * sc),
+                           (__bf16)(dk[mb][4 * g + 2] * sc), (__bf16)(dk[mb][4 * g + 3] * sc)};
+                *(bf16x4 *)(dvp + (vb_ + d0) * 2) =
+                    bf16x4{(__bf16)dv[mb][4 * g], (__bf16)dv[mb][4 * g + 1], (__bf16)dv[mb][4 * g + 2],
+                           (__bf16)dv[mb][4 * g + 3]};
+            }
+    }
+}
+
+// ------------------------------------------------------------------ 3. dQ
+
+template <int HD, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
+    constexpr int NT = NW * 64;
+    constexpr int BM = NW * 32;               // query rows per workgroup
+    constexpr int ROWB = HD * 2;
+    constexpr int CPR = HD / 8;
+    constexpr int TILE_BYTES = BN * ROWB;     // one K or V tile
+    constexpr int STAGES = 2;
+    constexpr int ROUNDS = TILE_BYTES / 16 / NT;
+    constexpr int KS = HD / 16, MB = HD / 32;
+    static_assert(ROUNDS >= 1 && ROUNDS * NT * 16 == TILE_BYTES, "tile split");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * 2 * TILE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // ---- which (query tile, sequence, batch*head); heaviest tiles first
+    const int BH = a.B * a.Htot;
+    const int tiles = (a.max_seqlen_q + BM - 1) / BM;
+    int id = blockIdx.x;
+    const int bh = id % BH;
+    id /= BH;
+    const int seq = id % a.nseq;
+    const int tile = tiles - 1 - id / a.nseq;
+    const int b = bh / a.Htot, hf = bh % a.Htot;
+    int qs, qe, ks, ke;
+    seq_bounds(a, seq, qs, qe, ks, ke);
+    const int Lq = qe - qs, Lk = ke - ks;
+    const int row0 = tile * BM;
+    if (tile < 0 || row0 >= Lq) return;
+    const int64_t shift = a.bottom_right ? (int64_t)Lk - Lq : 0;
+    const int row_last = min(row0 + BM, Lq) - 1;
+    const int kbeg = clampk((int64_t)row0 + shift - a.wl, 0, Lk);
+    const int kend = clampk((int64_t)row_last + shift + a.wr + 1, 0, Lk);
+    const int tb = kbeg / BN;
+    const int te = kend > kbeg ? (kend + BN - 1) / BN : tb;
+    int ua = (clampk((int64_t)row_last + shift - a.wl, 0, Lk) + BN - 1) / BN;
+    int ub = clampk((int64_t)row0 + shift + a.wr + 1, 0, Lk) / BN;
+    ua = min(max(ua, tb), te);
+    ub = min(max(ub, ua), te);
+
+    const __bf16 *qp = (const __bf16 *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin) + (int64_t)qs * a.sq.m;
+    const __bf16 *gp =
+        (const __bf16 *)a.dout + (int64_t)b * a.sdo.b + head_offset(a.sdo, hf, a.Hin) + (int64_t)qs * a.sdo.m;
+    const __bf16 *kp = (const __bf16 *)a.k + (int64_t)b * a.sk.b + head_offset(a.sk, hf, a.Hin) + (int64_t)ks * a.sk.m;
+    const __bf16 *vp = (const __bf16 *)a.v + (int64_t)b * a.sv.b + head_offset(a.sv, hf, a.Hin) + (int64_t)ks * a.sv.m;
+    const unsigned kstride = (unsigned)a.sk.m * 2u, vstride = (unsigned)a.sv.m * 2u;
+
+    unsigned koff[ROUNDS], voff[ROUNDS];
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+        const int p = (r * NW + wave) * 64 + lane;
+        const int row = p / CPR, c = (p % CPR) ^ swz<HD>(row);
+        koff[r] = row * kstride + c * 16;
+        voff[r] = row * vstride + c * 16;
+    }
+    const unsigned smem_base = (unsigned)(unsigned long long)(unsigned char LDS_AS *)smem;
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const int kt0 = t * BN;
+        const int nvalid = min(BN, Lk - kt0);
+        const unsigned st = smem_base + ((t - tb) % STAGES) * 2 * TILE_BYTES;
+        const i32x4 kr = make_rsrc(kp + (int64_t)kt0 * a.sk.m, (nvalid - 1) * kstride + ROWB);
+        const i32x4 vr = make_rsrc(vp + (int64_t)kt0 * a.sv.m, (nvalid - 1) * vstride + ROWB);
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) dma16(kr, koff[r], st + (r * NW + wave) * 1024);
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) dma16(vr, voff[r], st + TILE_BYTES + (r * NW + wave) * 1024);
+    };
+
+    // ---- this lane's query row: q and dout as B operands, its L and D
+    const int wrow0 = row0 + wave * 32;
+    const int qrow = wrow0 + l32;
+    const int klo = clampk((int64_t)qrow + shift - a.wl, 0, Lk);
+    const int khi = clampk((int64_t)qrow + shift + a.wr, -1, Lk - 1);
+    bf16x8 qf[KS], gf[KS];
+    float l2 = INFINITY, dd = 0.f;
+    if (qrow < Lq) {
+        const u32x4 *qsrc = (const u32x4 *)(qp + (int64_t)qrow * a.sq.m + 8 * hh);
+        const u32x4 *gsrc = (const u32x4 *)(gp + (int64_t)qrow * a.sdo.m + 8 * hh);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            qf[s] = __builtin_bit_cast(bf16x8, qsrc[2 * s]);
+            gf[s] = __builtin_bit_cast(bf16x8, gsrc[2 * s]);
+        }
+        const int64_t w = ((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow;
+        l2 = a.ws_l2[w];
+        dd = a.ws_d[w];
+    } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qf[s] = gf[s] = bf16x8{};
+    }
+    const float c = a.scale_log2;
+
+    int raddr[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) raddr[s] = l32 * ROWB + (((2 * s + hh) ^ swz<HD>(l32)) << 4);
+    int taddr[MB][2];
+    tr_offsets<HD, MB>(lane, taddr);
+
+    f32x16 dq[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) dq[i] = f32x16{};
+
+    auto step = [&](int t, auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const int kt0 = t * BN;
+        wait_barrier<0>();
+        if (t + 1 < te) issue(t + 1);
+        if (MASKED && ((int64_t)kt0 + BN - 1 < (int64_t)wrow0 + shift - a.wl ||
+                       (int64_t)kt0 > (int64_t)wrow0 + 31 + shift + a.wr))
+            return;
+        const unsigned char LDS_AS *st = (const unsigned char LDS_AS *)smem + ((t - tb) % STAGES) * 2 * TILE_BYTES;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            // S^T = K Q^T and dP^T = V dout^T for 32 keys: lane owns query l32, keys 8g + 4hh + j
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const bf16x8 ka = *(const bf16x8 LDS_AS *)(st + raddr[k] + kb * 32 * ROWB);
+                const bf16x8 va = *(const bf16x8 LDS_AS *)(st + TILE_BYTES + raddr[k] + kb * 32 * ROWB);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[k], dp, 0, 0, 0);
+            }
+            float ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
+                if (MASKED) {
+                    const int kk = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (kk < klo || kk > khi) pr = 0.f;
+                }
+                ds[r] = pr * (dp[r] - dd);
+            }
+            bf16x8 dsb[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dsb[kt][i] = (__bf16)ds[8 * kt + i];
+            // dQ^T += K^T dS^T over the two 16-key steps of this block
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int roff = (kb * 32 + kt * 16) * ROWB;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const bf16x8 kt_ = tr_frag(st, taddr[mb][0] + roff, taddr[mb][1] + roff);
+                    dq[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_, dsb[kt], dq[mb], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    if (tb < te) issue(tb);
+    int t = tb;
+    for (; t < ua; ++t) step(t, std::true_type{});
+    for (; t < ub; ++t) step(t, std::false_type{});
+    for (; t < te; ++t) step(t, std::true_type{});
+
+    if (qrow < Lq) {
+        unsigned char *dqp = (unsigned char *)a.dq;
+        const int64_t base = (int64_t)b * a.sdq.b + head_offset(a.sdq, hf, a.Hin) + (int64_t)(qs + qrow) * a.sdq.m;
+        const float sc = a.scale;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = mb * 32 + 8 * g + 4 * hh;
+                *(bf16x4 *)(dqp + (base + d0) * 2) =
+                    bf16x4{(__bf16)(dq[mb][4 * g] * sc), (__bf16)(dq[mb][4 * g + 1] * sc),
+                           (__bf16)(dq[mb][4 * g + 2] * sc), (__bf16)(dq[mb][4 * g + 3] * sc)};
+            }
+    }
+}
+
+template <int HD>
+hipError_t launch_hd(const BwdArgs &a, hipStream_t stream) {
+    constexpr int NW_KV = 4, NW_Q = 8;
+    const int64_t rows = (int64_t)a.B * a.Htot * a.Mq;
+    const int64_t g1 = (rows + 256 / (HD / 8) - 1) / (256 / (HD / 8));
+    const int64_t g2 = (int64_t)((a.max_seqlen_k + NW_KV * 32 - 1) / (NW_KV * 32)) * a.nseq * a.B * a.Htot;
+    const int64_t g3 = (int64_t)((a.max_seqlen_q + NW_Q * 32 - 1) / (NW_Q * 32)) * a.nseq * a.B * a.Htot;
+    if (g1 > 0x7fffffff || g2 > 0x7fffffff || g3 > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (g1 > 0) hipLaunchKernelGGL((bwd_prep_kernel<HD>), dim3((unsigned)g1), dim3(256), 0, stream, a);
+    if (g2 > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<HD, NW_KV>), dim3((unsigned)g2), dim3(NW_KV * 64), 0, stream, a);
+    if (g3 > 0) hipLaunchKernelGGL((bwd_dq_kernel<HD, NW_Q>), dim3((unsigned)g3), dim3(NW_Q * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream) {
+    if (a.D == 128) return launch_hd<128>(a, stream);
+    if (a.D == 64) return launch_hd<64>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attn

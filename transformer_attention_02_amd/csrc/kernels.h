@@ -80,6 +80,22 @@ struct MergeArgs {
 // Launchers return a hipError_t from the launch.
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool out_f32, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
+// Backward of the forward above: dq, dk, dv from dout, out and lse (same masks and layouts).
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    void *dq, *dk, *dv;
+    Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
+    const float *lse;     // [B, Htot, Mq], natural log
+    float *ws_d, *ws_l2;  // [B, Htot, Mq] each: dout.out per row, and lse * log2(e) (+inf for empty rows)
+    int B, Mq, Mkv, Htot, Hin, D;
+    float scale, scale_log2;
+    int packed, bottom_right, wl, wr;
+    const int32_t *seqstart_q, *seqstart_k;
+    int nseq, max_seqlen_q, max_seqlen_k;
+};
+
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
+
 hipError_t launch_decode_partials(const DecodeArgs &a, int elem, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 
