@@ -191,7 +191,7 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H_total, int64_t Mq);
  *     share memory (a stride-0 expanded head axis is rejected: for expanded GQA keys
  *     pass dk/dv of the expanded shape and sum over each group's heads).
  *   workspace: device, 256-byte aligned, >= attn_bwd_workspace_bytes(B, H_total, Mq).
- *   Three launches on `stream`.  Errors as attn_fwd; nothing is written on error. */
+ *   Two launches on `stream`.  Errors as attn_fwd; nothing is written on error. */
 attn_status attn_bwd(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k,
                      const attn_tensor *v, const attn_tensor *out, const float *lse,
                      const attn_mask *mask, const attn_varlen *varlen, float scale, void *workspace,

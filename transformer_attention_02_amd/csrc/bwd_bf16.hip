@@ -8,19 +8,19 @@
 //   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i.
 // The score matrix is never stored: P is rebuilt from the saved LSE tile by tile.
 //
-// Three launches:
-//   1. bwd_prep_kernel: D_i and the base-2 LSE L_i = lse_i log2(e) (+inf for a row with
-//      no visible key, so every rebuilt P of that row is exactly 0), one pass over out
-//      and dout into a caller workspace.
+// Two launches:
+//   1. bwd_dq_kernel: the forward's arrangement (8 waves, 32 query rows each; q and
+//      dout in registers, 64-key tiles of K and V through LDS): S^T = K Q^T and
+//      dP^T = V dout^T (lane l owns query row l%32), dS^T, then dQ^T += K^T dS^T.
+//      Each lane first forms its row's D_i and base-2 LSE L_i = lse_i log2(e) (+inf for
+//      a row with no visible key, so every rebuilt P of that row is exactly 0) and
+//      stores both in a caller workspace for the second launch.
 //   2. bwd_dkdv_kernel: a workgroup owns 32 keys per wave of one (batch, head, sequence);
 //      those keys' K and V rows stay in registers as matrix-core operands while 64-row
 //      tiles of Q and dout (and their L, D) stream through a 2-stage LDS ring.  Per tile:
 //      S = Q K^T and dP = dout V^T (lane l owns key l%32 and 16 query rows of each
 //      32-row block), P and dS in fp32, then dV^T += dout^T P and dK^T += Q^T dS with the
 //      A operands read transposed from the row-major LDS tiles.
-//   3. bwd_dq_kernel: the forward's arrangement (8 waves, 32 query rows each; q and
-//      dout in registers, 64-key tiles of K and V through LDS): S^T = K Q^T and
-//      dP^T = V dout^T (lane l owns query row l%32), dS^T, then dQ^T += K^T dS^T.
 // P is rounded to bf16 for dV and dS for dK and dQ; every product accumulates in fp32.
 // Same matrix-core layout as the forward (v_mfma_f32_32x32x16_bf16): a B operand taken
 // from C-layout registers gives lane half h the rows {8a + 4h + 0..3} of each 16-row
@@ -54,40 +54,7 @@ __device__ __forceinline__ void seq_bounds(const BwdArgs &a, int seq, int &qs, i
     }
 }
 
-// ------------------------------------------------------------------ 1. D and base-2 LSE per row
-
-template <int HD>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-    constexpr int LPR = HD / 8;     // lanes per row, 8 bf16 each
-    constexpr int RPB = 256 / LPR;  // rows per workgroup
-    const int64_t rows = (int64_t)a.B * a.Htot * a.Mq;
-    const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-    const int cl = threadIdx.x % LPR;
-    float acc = 0.f;
-    if (r < rows) {
-        const int i = (int)(r % a.Mq);
-        const int64_t bh = r / a.Mq;
-        const int hf = (int)(bh % a.Htot), b = (int)(bh / a.Htot);
-        const u32x4 ow = *(const u32x4 *)((const __bf16 *)a.o + (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) +
-                                          (int64_t)i * a.so.m + cl * 8);
-        const u32x4 gw = *(const u32x4 *)((const __bf16 *)a.dout + (int64_t)b * a.sdo.b +
-                                          head_offset(a.sdo, hf, a.Hin) + (int64_t)i * a.sdo.m + cl * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc = fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(gw[e] << 16), acc);
-            acc = fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), acc);
-        }
-    }
-#pragma unroll
-    for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (r < rows && cl == 0) {
-        a.ws_d[r] = acc;
-        const float l = a.lse[r];
-        a.ws_l2[r] = l == -INFINITY ? INFINITY : l * kLog2e;
-    }
-}
-
-// ------------------------------------------------------------------ 2. dK and dV
+// ------------------------------------------------------------------ dK and dV
 
 // Transposed-read LDS offsets inside a row-major [rows, HD] tile: lane i of 16-lane group G
 // addresses row 4*hh + i/4 (+ 8e, + multiples of 16) and columns mb*32 + 16*(G&1) + 4*(i%4).
@@ -318,7 +285,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
-// ------------------------------------------------------------------ 3. dQ
+// ------------------------------------------------------------------ dQ (runs first)
 
 template <int HD, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
@@ -406,12 +373,33 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
             qf[s] = __builtin_bit_cast(bf16x8, qsrc[2 * s]);
             gf[s] = __builtin_bit_cast(bf16x8, gsrc[2 * s]);
         }
+        // D = dout.out over the row: this lane holds half of its columns, the lane 32 away the rest
+        const u32x4 *osrc = (const u32x4 *)((const __bf16 *)a.o + (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) +
+                                            (int64_t)(qs + qrow) * a.so.m + 8 * hh);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const u32x4 ow = osrc[2 * s], gw = __builtin_bit_cast(u32x4, gf[s]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dd = fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(gw[e] << 16), dd);
+                dd = fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), dd);
+            }
+        }
         const int64_t w = ((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow;
-        l2 = a.ws_l2[w];
-        dd = a.ws_d[w];
+        const float lse = a.lse[w];
+        l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
     } else {
 #pragma unroll
         for (int s = 0; s < KS; ++s) qf[s] = gf[s] = bf16x8{};
+    }
+    {
+        auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(dd), __float_as_uint(dd), false, false);
+        dd = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    if (qrow < Lq && hh == 0) {
+        const int64_t w = ((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow;
+        a.ws_d[w] = dd;
+        a.ws_l2[w] = l2;
     }
     const float c = a.scale_log2;
 
@@ -498,14 +486,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
 template <int HD>
 hipError_t launch_hd(const BwdArgs &a, hipStream_t stream) {
     constexpr int NW_KV = 4, NW_Q = 8;
-    const int64_t rows = (int64_t)a.B * a.Htot * a.Mq;
-    const int64_t g1 = (rows + 256 / (HD / 8) - 1) / (256 / (HD / 8));
-    const int64_t g2 = (int64_t)((a.max_seqlen_k + NW_KV * 32 - 1) / (NW_KV * 32)) * a.nseq * a.B * a.Htot;
-    const int64_t g3 = (int64_t)((a.max_seqlen_q + NW_Q * 32 - 1) / (NW_Q * 32)) * a.nseq * a.B * a.Htot;
-    if (g1 > 0x7fffffff || g2 > 0x7fffffff || g3 > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (g1 > 0) hipLaunchKernelGGL((bwd_prep_kernel<HD>), dim3((unsigned)g1), dim3(256), 0, stream, a);
-    if (g2 > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<HD, NW_KV>), dim3((unsigned)g2), dim3(NW_KV * 64), 0, stream, a);
-    if (g3 > 0) hipLaunchKernelGGL((bwd_dq_kernel<HD, NW_Q>), dim3((unsigned)g3), dim3(NW_Q * 64), 0, stream, a);
+    const int64_t gq = (int64_t)((a.max_seqlen_q + NW_Q * 32 - 1) / (NW_Q * 32)) * a.nseq * a.B * a.Htot;
+    const int64_t gkv = (int64_t)((a.max_seqlen_k + NW_KV * 32 - 1) / (NW_KV * 32)) * a.nseq * a.B * a.Htot;
+    if (gq > 0x7fffffff || gkv > 0x7fffffff) return hipErrorInvalidConfiguration;
+    // the dQ launch writes the per-row D and L that the dK/dV launch reads
+    if (gq > 0) hipLaunchKernelGGL((bwd_dq_kernel<HD, NW_Q>), dim3((unsigned)gq), dim3(NW_Q * 64), 0, stream, a);
+    if (gkv > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<HD, NW_KV>), dim3((unsigned)gkv), dim3(NW_KV * 64), 0, stream, a);
     return hipGetLastError();
 }
 
