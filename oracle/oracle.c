@@ -58,6 +58,10 @@
  * one (scale, shift) pair; its value is fp8(code) * scale + shift.  The attention is
  * then the definition above applied to those values.
  *
+ * INT4 caches (triton_splitk.FwOp, "row/group INT4 ... stored through int32"): unsigned
+ * 4-bit codes, two per byte, with one (scale, shift) pair per group of D/G consecutive
+ * elements of a row: x = code * scale + shift (oracle_dequant_int4_groupwise).
+ *
  * Layouts (all contiguous, fp64):
  *   q [B,Mq,H,K], k [B,Mkv,H,K], v [B,Mkv,H,Kv], out [B,Mq,H,Kv], lse [B,H,Mq].
  *   Packed sequences: B = 1, seqstart_q/seqstart_k are prefix sums [nseq+1].
@@ -294,6 +298,24 @@ void oracle_dequant_fp8_rowwise(int64_t rows, int64_t D, const uint8_t *codes, c
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t d = 0; d < D; ++d) x[r * D + d] = oracle_fp8_e4m3(codes[r * D + d]) * ss[2 * r] + ss[2 * r + 1];
+}
+
+/* Group-wise INT4 dequantisation (triton_splitk.FwOp: row/group INT4 caches stored through
+ * int32 words): each of `rows` rows holds D unsigned 4-bit codes, two per byte, element 2i in
+ * the low nibble of byte i (so eight per 32-bit word), and G (scale, shift) pairs, one per
+ * group of D/G consecutive elements:  x[r, d] = code[r, d] * ss[r, g, 0] + ss[r, g, 1],
+ * g = d / (D/G).  G = 1 is the row-wise form. */
+void oracle_dequant_int4_groupwise(int64_t rows, int64_t D, int64_t G, const uint8_t *codes, const double *ss,
+                                   double *x) {
+    const int64_t gs = D / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t d = 0; d < D; ++d) {
+            const uint8_t byte = codes[r * (D / 2) + d / 2];
+            const int code = (d % 2 == 0) ? (byte & 15) : (byte >> 4);
+            const int64_t g = d / gs;
+            x[r * D + d] = code * ss[(r * G + g) * 2] + ss[(r * G + g) * 2 + 1];
+        }
 }
 
 /* out_chunks [S,B,M,H,Kv], lse_chunks [S,B,H,M] -> out [B,M,H,Kv], lse [B,H,M]. */

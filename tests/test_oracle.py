@@ -542,3 +542,46 @@ def test_backward_closed_forms(oracle_mod):
     # zero upstream gradient
     dq, dk, dv = oracle_mod.attention_backward(np.zeros_like(G), *oracle_mod.attention(q, k, v), q, k, v)
     assert not dq.any() and not dk.any() and not dv.any()
+
+
+# ---------------------------------------------------------------- INT4 group-wise caches
+
+def _pack_int4(codes):
+    """Independent packer: byte i = codes[2i] + 16 * codes[2i+1], with Python integers."""
+    flat = [int(c) for c in np.asarray(codes).reshape(-1)]
+    return np.array([flat[2 * i] + 16 * flat[2 * i + 1] for i in range(len(flat) // 2)],
+                    dtype=np.uint8).reshape(np.asarray(codes).shape[:-1] + (-1,))
+
+
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_int4_dequant_round_trip(oracle_mod, G):
+    """Codes packed by an independent encoder come back as code * scale + shift of their own group."""
+    rows, D = 5, 16
+    codes = np.random.Generator(np.random.PCG64(7 + G)).integers(0, 16, (rows, D))
+    ss = np.zeros((rows, G, 2))
+    ss[..., 0] = 1.0 + np.arange(G)          # group g scales by g + 1
+    ss[..., 1] = 100.0 * np.arange(rows)[:, None] + 10.0 * np.arange(G)[None, :]
+    x = oracle_mod.dequant_int4_groupwise(_pack_int4(codes), ss)
+    gs = D // G
+    for r in range(rows):
+        for d in range(D):
+            g = d // gs
+            assert x[r, d] == codes[r, d] * (g + 1) + 100.0 * r + 10.0 * g
+
+
+def test_int4_closed_forms(oracle_mod):
+    # byte 0xA5: element 0 = 5 (low nibble), element 1 = 10
+    x = oracle_mod.dequant_int4_groupwise(np.array([[0xA5, 0x0F]], np.uint8), np.array([[[2.0, -1.0]]]))
+    np.testing.assert_array_equal(x, [[9.0, 19.0, 29.0, -1.0]])
+    # all-zero codes give the shift of each group
+    z = oracle_mod.dequant_int4_groupwise(np.zeros((1, 4), np.uint8), np.array([[[3.0, 0.5], [3.0, -0.5]]]))
+    np.testing.assert_array_equal(z, [[0.5] * 4 + [-0.5] * 4])
+
+
+def test_int4_generators(oracle_mod):
+    codes = synth.int4_codes(3, 1, (64, 64))
+    lo, hi = codes & 15, codes >> 4
+    assert lo.min() == 0 and lo.max() == 15 and hi.min() == 0 and hi.max() == 15
+    ss = synth.int4_scale_shift(3, 1, (64, 4))
+    x = oracle_mod.dequant_int4_groupwise(codes.reshape(64, 64), ss)
+    assert abs(float(x.mean())) < 0.1 and 0.5 < float(x.std()) < 2.0
