@@ -7,7 +7,8 @@ H=32, K=Kv=128 (the pages' Quick-start shape), inputs resident in HBM.  The
 headline value is its throughput in TFLOP/s, counting 4*B*H*M*M*K flops halved
 for the causal mask.  The other rows of the path are timed after it and
 reported under "rows": split-KV decode (B=16, Mkv=32768, H=32, 64 chunks;
-GB/s of K+V) on contiguous and on paged caches and on a row-wise FP8 cache, the packed GQA causal prefill (8 sequences, lengths U[256, 4096]),
+GB/s of K+V) on contiguous and on paged caches and on row-wise FP8 and row/group-wise INT4 caches,
+the backward of the causal prefill, the packed GQA causal prefill (8 sequences, lengths U[256, 4096]),
 a causal sliding window of 1024 keys over [2, 8192, 32, 128], the 2- and 8-way
 partial+merge of Mq=128/Mkv=1024/H=16, and the fp32 tiny case.
 Every figure is timed with HIP events on the stream the kernels run on; each call is
@@ -254,8 +255,34 @@ def main():
                          "frac": round(gbs_8 / PEAK_HBM_GBS, 4), "bytes_per_call": fp8_bytes,
                          "traffic": recorded_traffic("decode fp8 16x32768x32x128 s64"),
                          "note": "algorithmic bytes = K+V codes and their metadata once"}}
-        del qd, k8, v8, kss, vss, ws, od, ld
+        del k8, v8, kss, vss
         torch.cuda.empty_cache()
+
+        # the same shape with INT4 caches: two codes per byte, (scale, shift) fp16 pairs per row / group
+        for G in (1, 4):
+            log(f"generating int4 decode inputs (G={G}) ...")
+            cshape = (B, Mkv, H, D // 2)
+            k4 = torch.from_numpy(synth.int4_codes(4, synth.TAG_K, cshape)).to("cuda")
+            v4 = torch.from_numpy(synth.int4_codes(4, synth.TAG_V, cshape)).to("cuda")
+            ks4 = torch.from_numpy(synth.int4_scale_shift(4, synth.TAG_K, (B, Mkv, H, G)).reshape(B, Mkv, H, 2 * G))
+            vs4 = torch.from_numpy(synth.int4_scale_shift(4, synth.TAG_V, (B, Mkv, H, G)).reshape(B, Mkv, H, 2 * G))
+            ks4, vs4 = ks4.to("cuda"), vs4.to("cuda")
+            ms_4 = timed(A.prepare_decode_int4(qd, k4, v4, ks4, vs4, S, ws, od, ld), 20, 3, torch)
+            i4_bytes = 2.0 * B * Mkv * H * (D // 2 + 4 * G)
+            gbs_4 = i4_bytes / (ms_4 * 1e-3) / 1e9
+            log(f"int4 decode G={G} S=64: {ms_4 * 1e3:.1f} us/call, {gbs_4:.0f} GB/s")
+            result["rows"][f"decode_int4_g{G}"] = {
+                "workload": f"B=16 Mq=1 Mkv=32768 H=32 D=128, bf16 q, INT4 K/V (two codes per byte) with "
+                            f"{'one fp16 (scale, shift) pair per row' if G == 1 else f'{G} groups of {D // G} per row'}"
+                            ", 64 chunks of 512",
+                "ms_per_call": round(ms_4, 5), "value": round(gbs_4, 1), "unit": "GB/s",
+                "keys_per_s": round(B * Mkv * H / (ms_4 * 1e-3), 1),
+                "roofline": {"bound": "hbm", "achieved": round(gbs_4, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs_4 / PEAK_HBM_GBS, 4), "bytes_per_call": i4_bytes,
+                             "note": "algorithmic bytes = K+V codes and their metadata once"}}
+            del k4, v4, ks4, vs4
+            torch.cuda.empty_cache()
+        del qd, ws, od, ld
 
     # ------------------------------------------------------------ packed GQA causal prefill
     if "varlen" in rows:

@@ -71,7 +71,10 @@ typedef enum {
     ATTN_DTYPE_BF16 = 1,
     ATTN_DTYPE_FP8_E4M3 = 2, /* OCP E4M3 ("FN": bias 7, no infinities, S.1111.111 = NaN); K/V caches of
                                 attn_decode_splitkv_fp8 only */
-    ATTN_DTYPE_F16 = 3       /* IEEE half; the scale/shift metadata of attn_decode_splitkv_fp8 only */
+    ATTN_DTYPE_F16 = 3,      /* IEEE half; the scale/shift metadata of the quantised decodes only */
+    ATTN_DTYPE_INT4X2 = 4    /* two unsigned 4-bit codes per byte, element 2i in the low nibble of byte i;
+                                shape and strides of such a tensor count bytes (last dim = D / 2);
+                                K/V caches of attn_decode_splitkv_int4 only */
 } attn_dtype;
 
 /* Masks ("Attention - Biases & masks" on the kernel reference page).  For a
@@ -258,6 +261,24 @@ attn_status attn_decode_splitkv_fp8(const attn_tensor *q, const attn_tensor *k, 
                                     int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
                                     int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                     const attn_tensor *out, float *lse, attn_stream_t stream);
+
+/* Split-KV decode against a row/group-wise INT4 K/V cache (triton_splitk.FwOp: fused
+ * row/group INT4 caches stored through int32 words).  Row r of head h holds D codes
+ * 0..15, eight per 32-bit word, and G (scale, shift) pairs, one per group of D/G
+ * consecutive elements; element d is  code_d * scale_g + shift_g  with g = d / (D/G).
+ *   q [B, 1, (G,) H, D] bf16, D in {64, 128}.
+ *   k, v: ATTN_DTYPE_INT4X2 caches, last dim D/2 bytes, laid out as in
+ *     attn_decode_splitkv_fp8 (lanes, padded lanes or pages).
+ *   k_scale_shift, v_scale_shift: ATTN_DTYPE_F16, the shape of k with the last axis 2G
+ *     (G pairs, scale first), stride-1 last axis, 4-byte aligned rows; D/G must be a
+ *     multiple of 32 (G in {1, 2, 4} for D = 128; {1, 2} for D = 64).
+ *   Everything else as in attn_decode_splitkv_fp8. */
+attn_status attn_decode_splitkv_int4(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                     const attn_tensor *k_scale_shift, const attn_tensor *v_scale_shift,
+                                     const int32_t *seqlens, const int32_t *block_tables,
+                                     int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                     int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                                     const attn_tensor *out, float *lse, attn_stream_t stream);
 
 /* Reason for the last non-OK status returned on this thread ("" if none). */
 const char *attn_last_error(void);

@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd", "attn_partial", "attn_fwd_ex", "attn_partial_ex", "attn_merge",
                                            "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_paged",
-                                           "attn_decode_splitkv_fp8", "attn_bwd_workspace_bytes", "attn_bwd",
+                                           "attn_decode_splitkv_fp8", "attn_decode_splitkv_int4", "attn_bwd_workspace_bytes",
+                                           "attn_bwd",
                                            "attn_last_error"])
 
 
@@ -288,3 +289,26 @@ def test_bwd_workspace_and_rejects():
     assert call(mask=A.AttnMask(7, 0, 0, 0)) == A.ATTN_ERR_INVALID_ARGUMENT and "window_size" in A.attn_last_error()
     d96 = t((B, M, H, 96))
     assert call(d96, d96, d96, d96, d96, d96, d96, d96) == A.ATTN_ERR_UNSUPPORTED
+
+
+def test_int4_decode_rejects():
+    B, H, D, S, M = 4, 8, 128, 4, 256
+    need = A.attn_decode_workspace_bytes(B, H, D, S)
+    q, o = tensor([B, 1, H, D]), tensor([B, 1, H, D])
+    k4 = tensor([B, M, H, D // 2], A.ATTN_DTYPE_INT4X2)
+    ss = lambda G: tensor([B, M, H, 2 * G], A.ATTN_DTYPE_F16, data=FAKE + 4)
+
+    def call(k=k4, kss=None, vss=None, fn=A._lib.attn_decode_splitkv_int4):
+        kss = kss or ss(1)
+        vss = vss or kss
+        return fn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(kss), ctypes.byref(vss), None, None,
+                  0, 0, 0, S, float("nan"), ctypes.c_void_p(FAKE * 256), need, ctypes.byref(o), None, None)
+    assert call(kss=ss(8)) == A.ATTN_ERR_UNSUPPORTED and "multiple of 32" in A.attn_last_error()   # groups of 16
+    assert call(kss=ss(3)) == A.ATTN_ERR_UNSUPPORTED
+    assert call(kss=ss(2), vss=ss(4)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(k=tensor([B, M, H, D], A.ATTN_DTYPE_INT4X2)) == A.ATTN_ERR_INVALID_ARGUMENT  # D codes = D/2 bytes
+    assert call(k=tensor([B, M, H, D // 2], A.ATTN_DTYPE_FP8_E4M3)) == A.ATTN_ERR_INVALID_ARGUMENT
+    k8 = tensor([B, M, H, D], A.ATTN_DTYPE_FP8_E4M3)
+    assert call(k=k8, kss=ss(2), fn=A._lib.attn_decode_splitkv_fp8) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert "row-wise" in A.attn_last_error()
+    assert call(k=tensor([B, M, H, D // 2], A.ATTN_DTYPE_INT4X2, data=FAKE + 8)) == A.ATTN_ERR_INVALID_ARGUMENT

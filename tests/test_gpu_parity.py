@@ -639,3 +639,121 @@ def test_bwd_causal_full_size(A):
         check_grads([x[sl] for x in (dq, dk, dv)], ref, f"b={b} h={h}")
     for x in (dq, dk, dv):
         assert not torch.isnan(x).any()
+
+
+# ------------------------------------------------------------------ row/group-wise INT4 K/V caches
+
+def _u8(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).cuda()
+
+
+def _int4_cache(seed, shape, G):
+    """(k codes, v codes, k scale/shift, v scale/shift) of an INT4 cache of `shape` [..., D]."""
+    cshape = shape[:-1] + (shape[-1] // 2,)
+    return (synth.int4_codes(seed, synth.TAG_K, cshape), synth.int4_codes(seed, synth.TAG_V, cshape),
+            synth.int4_scale_shift(seed, synth.TAG_K, shape[:-1] + (G,)),
+            synth.int4_scale_shift(seed, synth.TAG_V, shape[:-1] + (G,)))
+
+
+def _int4_oracle(qh, kc, vc, kss, vss, scale=None):
+    return oracle.attention(synth.to_f64(qh, "bf16"), oracle.dequant_int4_groupwise(kc, kss),
+                            oracle.dequant_int4_groupwise(vc, vss), mask=0, scale=scale)
+
+
+def _flat_ss(ss):  # [..., G, 2] -> [..., 2G], the layout the entry point takes
+    return _f16(ss.reshape(ss.shape[:-2] + (-1,)))
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_int4_decode_every_code_in_every_position(A, G):
+    """All 16 codes in both nibbles of every byte position, scale 1/16 and zero shift: fp32 output."""
+    B, M, H, D = 1, 256, 2, 128
+    idx = (np.arange(M)[:, None] + np.arange(D // 2)[None, :])
+    codes = ((idx % 16) | (((idx // 16 + 3 * np.arange(M)[:, None]) % 16) << 4)).astype(np.uint8)
+    kc = np.broadcast_to(codes[None, :, None, :], (B, M, H, D // 2)).copy()
+    vc = np.broadcast_to(codes[None, ::-1, None, :], (B, M, H, D // 2)).copy()
+    kss = np.zeros((B, M, H, G, 2), np.float16)
+    kss[..., 0] = 1.0 / 16
+    vss = kss.copy()
+    qh = synth.normal(8, synth.TAG_Q, (B, 1, H, D), "bf16")
+    say(f"case: int4 decode, every code, G={G}")
+    out, lse = A.attn_decode_splitkv_int4(dev(qh, "bf16"), _u8(kc), _u8(vc), _flat_ss(kss), _flat_ss(vss), 3,
+                                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oo, ol = _int4_oracle(qh, kc, vc, kss, vss)
+    check(out, lse, oo, ol, TOL_F32, TOL_F32, "every code")
+
+
+@pytest.mark.parametrize("D,G", [(64, 1), (64, 2), (128, 1), (128, 2), (128, 4)])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_int4_decode_contiguous(A, D, G, out_dtype):
+    tol_o = TOL_BF16_OUT if out_dtype == "bf16" else TOL_F32
+    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    for B, M, H, S in [(3, 1000, 4, 7), (2, 5, 3, 8), (2, 4097, 5, 128)]:
+        say(f"case: int4 decode D={D} G={G} out={out_dtype} B={B} M={M} H={H} S={S}")
+        kc, vc, kss, vss = _int4_cache(720 + M + G, (B, M, H, D), G)
+        qh = synth.normal(720 + M, synth.TAG_Q, (B, 1, H, D), "bf16")
+        out, lse = A.attn_decode_splitkv_int4(dev(qh, "bf16"), _u8(kc), _u8(vc), _flat_ss(kss), _flat_ss(vss), S,
+                                              scale=0.09, out_dtype=tdt)
+        torch.cuda.synchronize()
+        oo, ol = _int4_oracle(qh, kc, vc, kss, vss, scale=0.09)
+        check(out, lse, oo, ol, tol_o, TOL_F32, f"int4 S={S}")
+
+
+def test_int4_decode_padded_lanes_5d_gqa(A):
+    B, cap, G5, Hg, D, S, G = 4, 600, 2, 3, 128, 5, 2
+    lens = np.array([600, 0, 1, 257], dtype=np.int32)
+    kc, vc, kss, vss = _int4_cache(1110, (B, cap, G5, 1, D), G)
+    qh = synth.normal(1110, synth.TAG_Q, (B, 1, G5, Hg, D), "bf16")
+    say(f"case: int4 decode padded lanes 5-D GQA lens={list(lens)}")
+    k = _u8(kc).expand(B, cap, G5, Hg, D // 2)
+    v = _u8(vc).expand(B, cap, G5, Hg, D // 2)
+    ks = _flat_ss(kss).expand(B, cap, G5, Hg, 2 * G)
+    vs = _flat_ss(vss).expand(B, cap, G5, Hg, 2 * G)
+    out, lse = A.attn_decode_splitkv_int4(dev(qh, "bf16"), k, v, ks, vs, S, seqlens=torch.from_numpy(lens).cuda(),
+                                          max_seqlen_k=int(lens.max()), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        rep = lambda x: np.repeat(x[b:b + 1, :lens[b]], Hg, axis=3).reshape((1, lens[b], G5 * Hg) + x.shape[4:])
+        oo, ol = _int4_oracle(qh[b:b + 1].reshape(1, 1, G5 * Hg, D), rep(kc), rep(vc), rep(kss), rep(vss))
+        check(out[b:b + 1].reshape(1, 1, G5 * Hg, D), lse[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"lane {b} len={lens[b]}")
+
+
+@pytest.mark.parametrize("page", [16, 64])
+def test_int4_decode_paged(A, page):
+    B, H, D, S, P, maxb, G = 3, 4, 128, 5, 100, 20, 4
+    rng = np.random.Generator(np.random.PCG64(1301 + page))
+    tables = rng.permutation(P)[:B * maxb].reshape(B, maxb).astype(np.int32)
+    lens = np.array([maxb * page, 37, 0], dtype=np.int32)
+    kc, vc, kss, vss = _int4_cache(1302, (1, P * page, H, D), G)
+    qh = synth.normal(1302, synth.TAG_Q, (B, 1, H, D), "bf16")
+    say(f"case: int4 decode paged page={page} lens={list(lens)}")
+    out, lse = A.attn_decode_splitkv_int4(dev(qh, "bf16"), _u8(kc), _u8(vc), _flat_ss(kss), _flat_ss(vss), S,
+                                          seqlens=torch.from_numpy(lens).cuda(), max_seqlen_k=int(lens.max()),
+                                          block_tables=torch.from_numpy(tables).cuda(), page_size=page,
+                                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        g = lambda x: _gather(x, tables[b], page, lens[b])
+        oo, ol = _int4_oracle(qh[b:b + 1], g(kc), g(vc), g(kss), g(vss))
+        check(out[b:b + 1], lse[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"seq {b} len={lens[b]}")
+
+
+def test_int4_decode_full_size(A):
+    """B=16, Mkv=32768, H=32, D=128 INT4 cache, 64 splits: sampled (b, h), row-wise and 4 groups."""
+    B, M, H, D = 16, 32768, 32, 128
+    qh = synth.normal(4, synth.TAG_Q, (B, 1, H, D), "bf16")
+    for G in (1, 4):
+        say(f"generating int4 decode inputs [16,32768,32,128] G={G}")
+        kc, vc, kss, vss = _int4_cache(4, (B, M, H, D), G)
+        say(f"case: int4 decode full size S=64 G={G}")
+        k, v = _u8(kc), _u8(vc)
+        out, lse = A.attn_decode_splitkv_int4(dev(qh, "bf16"), k, v, _flat_ss(kss), _flat_ss(vss), 64)
+        torch.cuda.synchronize()
+        for b, h in [(0, 0), (7, 19), (15, 31)]:
+            sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+            oo, ol = _int4_oracle(qh[sl], kc[sl], vc[sl], kss[sl], vss[sl])
+            check(out[sl], lse[b:b + 1, h:h + 1], oo, ol, TOL_BF16_OUT, TOL_F32, f"b={b} h={h}")
+        assert not torch.isnan(out).any()
+        del k, v
+        torch.cuda.empty_cache()

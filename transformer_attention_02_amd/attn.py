@@ -21,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE_TOO_SMALL, ATTN_ERR_LAUNCH = range(5)
-ATTN_DTYPE_F32, ATTN_DTYPE_BF16, ATTN_DTYPE_FP8_E4M3, ATTN_DTYPE_F16 = 0, 1, 2, 3
+ATTN_DTYPE_F32, ATTN_DTYPE_BF16, ATTN_DTYPE_FP8_E4M3, ATTN_DTYPE_F16, ATTN_DTYPE_INT4X2 = 0, 1, 2, 3, 4
 MASK_NONE, MASK_CAUSAL, MASK_BLOCKDIAG, MASK_BLOCKDIAG_CAUSAL = 0, 1, 2, 3
 MASK_CAUSAL_BR, MASK_BLOCKDIAG_CAUSAL_BR, MASK_LOCAL_BR, MASK_CAUSAL_LOCAL_BR = 4, 5, 6, 7
 MASK_BLOCKDIAG_CAUSAL_LOCAL, MASK_BLOCKDIAG_CAUSAL_LOCAL_BR = 8, 9
@@ -75,6 +75,8 @@ _lib.attn_decode_splitkv_fp8.argtypes = [_T, _T, _T, _T, _T, ctypes.c_void_p, ct
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                          ctypes.c_void_p, ctypes.c_size_t, _T, ctypes.c_void_p, ctypes.c_void_p]
 _lib.attn_decode_splitkv_fp8.restype = ctypes.c_int
+_lib.attn_decode_splitkv_int4.argtypes = _lib.attn_decode_splitkv_fp8.argtypes
+_lib.attn_decode_splitkv_int4.restype = ctypes.c_int
 _lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
 _lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.attn_bwd.argtypes = [_T, _T, _T, _T, _T, ctypes.c_void_p, _P(AttnMask), _P(AttnVarlen), ctypes.c_float,
@@ -102,11 +104,12 @@ def _dtype_code(dt: torch.dtype) -> int:
     raise TypeError(f"unsupported dtype {dt}")
 
 
-def desc(t: torch.Tensor) -> AttnTensor:
-    """C descriptor of a 4-D [B,M,H,D] or 5-D [B,M,G,H,D] tensor (strides in elements)."""
+def desc(t: torch.Tensor, dtype_code=None) -> AttnTensor:
+    """C descriptor of a 4-D [B,M,H,D] or 5-D [B,M,G,H,D] tensor (strides in elements); `dtype_code`
+    overrides the code derived from the torch dtype (uint8 INT4 caches are ATTN_DTYPE_INT4X2)."""
     d = AttnTensor()
     d.data = t.data_ptr() if t.numel() else None
-    d.dtype = _dtype_code(t.dtype)
+    d.dtype = _dtype_code(t.dtype) if dtype_code is None else dtype_code
     d.ndim = t.dim()
     for i in range(t.dim()):
         d.shape[i] = t.shape[i]
@@ -318,8 +321,8 @@ def prepare_decode_paged(q, k, v, seqlens, num_splits, max_seqlen_k, workspace, 
 
 
 def _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k, num_splits,
-              scale, workspace, out, lse, stream):
-    ds = [desc(q), desc(k), desc(v), desc(k_scale_shift), desc(v_scale_shift), desc(out)]
+              scale, workspace, out, lse, stream, kv_code=None):
+    ds = [desc(q), desc(k, kv_code), desc(v, kv_code), desc(k_scale_shift), desc(v_scale_shift), desc(out)]
     mb = block_tables.shape[1] if block_tables is not None else 0
     args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), ctypes.byref(ds[3]), ctypes.byref(ds[4]),
             _ptr(seqlens), _ptr(block_tables), int(mb), int(page_size or 0), int(max_seqlen_k or 0),
@@ -396,6 +399,36 @@ def prepare_bwd(dout, q, k, v, out, lse, dq, dk, dv, workspace, mask=MASK_NONE, 
     args, keep = _bwd_args(dout, q, k, v, out, lse, mask, scale, seqstart_q, seqstart_k, max_seqlen_q,
                            max_seqlen_k, window_size, window_left, window_right, workspace, dq, dk, dv, stream)
     return Prepared(_lib.attn_bwd, args, (keep, dout, q, k, v, out, lse, dq, dk, dv, workspace))
+
+
+def attn_decode_splitkv_int4(q, k, v, k_scale_shift, v_scale_shift, num_splits, seqlens=None, max_seqlen_k=None,
+                             block_tables=None, page_size=None, scale=None, workspace=None, out=None, lse=True,
+                             out_dtype=None, stream=None):
+    """Split-KV decode over INT4 K/V caches: uint8 tensors [..., D/2] (two 4-bit codes per byte,
+    even element low) with float16 (scale, shift) pairs [..., 2G] per cache row, head and group.
+    Lanes, padded lanes (seqlens) or pages (block_tables).  Returns (out, lse or None)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty((q.shape[0], _htot(q), 1), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    need = attn_decode_workspace_bytes(q.shape[0], _htot(q), q.shape[-1], num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    args, _keep = _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k,
+                            num_splits, scale, workspace, out, lse, stream, kv_code=ATTN_DTYPE_INT4X2)
+    _check(_lib.attn_decode_splitkv_int4(*args))
+    return out, lse
+
+
+def prepare_decode_int4(q, k, v, k_scale_shift, v_scale_shift, num_splits, workspace, out, lse, seqlens=None,
+                        max_seqlen_k=None, block_tables=None, page_size=None, scale=None, stream=None) -> Prepared:
+    """attn_decode_splitkv_int4 with every argument marshalled up front."""
+    args, ds = _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k,
+                         num_splits, scale, workspace, out, lse, stream, kv_code=ATTN_DTYPE_INT4X2)
+    return Prepared(_lib.attn_decode_splitkv_int4, args,
+                    (ds, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, workspace, out, lse))
 
 
 def default_scale(K: int) -> float:

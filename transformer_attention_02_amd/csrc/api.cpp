@@ -31,7 +31,9 @@ attn_status ok() {
     return ATTN_OK;
 }
 
-size_t dtype_size(int dt) { return dt == ATTN_DTYPE_F32 ? 4 : (dt == ATTN_DTYPE_FP8_E4M3 ? 1 : 2); }
+size_t dtype_size(int dt) {
+    return dt == ATTN_DTYPE_F32 ? 4 : ((dt == ATTN_DTYPE_FP8_E4M3 || dt == ATTN_DTYPE_INT4X2) ? 1 : 2);
+}
 
 constexpr unsigned DT_FLOAT = (1u << ATTN_DTYPE_F32) | (1u << ATTN_DTYPE_BF16);  // q/k/v/out of every path
 
@@ -47,7 +49,7 @@ struct View {
 // `dtypes`: bit set of the attn_dtype values accepted; `align`: byte alignment of row starts.
 attn_status make_view(const attn_tensor *t, const char *name, View *v, unsigned dtypes = DT_FLOAT, int align = 16) {
     if (!t) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: descriptor is NULL", name);
-    if (t->dtype < 0 || t->dtype > ATTN_DTYPE_F16 || !((dtypes >> t->dtype) & 1u))
+    if (t->dtype < 0 || t->dtype > ATTN_DTYPE_INT4X2 || !((dtypes >> t->dtype) & 1u))
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: dtype %d is not accepted here", name, t->dtype);
     if (t->ndim != 4 && t->ndim != 5)
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: ndim must be 4 [B,M,H,D] or 5 [B,M,G,H,D], got %d", name, t->ndim);
@@ -468,27 +470,42 @@ namespace {
 
 // Shared validation and launches of the split-KV decode entry points.  Without block tables
 // k/v are [B, cap, (G,) H, D] lanes; with them k/v are the paged cache [1, pages * page_size, ...].
-// `fp8`: k/v are FP8 E4M3 codes with (scale, shift) metadata ksst / vsst.
-attn_status decode(const char *fn, bool fp8, const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
+// `quant`: 0 = k/v share q's dtype; ATTN_DTYPE_FP8_E4M3 / ATTN_DTYPE_INT4X2 = k/v are codes of that
+// type with (scale, shift) metadata ksst / vsst.
+attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
                    const attn_tensor *ksst, const attn_tensor *vsst, const int32_t *seqlens,
                    const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
                    int32_t num_splits, float scale, void *workspace, size_t workspace_bytes, const attn_tensor *ot,
                    float *lse, attn_stream_t stream) {
     View q, k, v, o, kss{}, vss{};
     attn_status st;
-    const unsigned kv_dt = fp8 ? 1u << ATTN_DTYPE_FP8_E4M3 : DT_FLOAT;
+    const unsigned kv_dt = quant ? 1u << quant : DT_FLOAT;
     if ((st = make_view(qt, "q", &q)) != ATTN_OK) return st;
     if ((st = make_view(kt, "k", &k, kv_dt)) != ATTN_OK) return st;
     if ((st = make_view(vt, "v", &v, kv_dt)) != ATTN_OK) return st;
     if ((st = make_view(ot, "out", &o)) != ATTN_OK) return st;
-    if (fp8) {
+    int group = 0;  // elements per (scale, shift) group
+    if (quant) {
         if ((st = make_view(ksst, "k_scale_shift", &kss, 1u << ATTN_DTYPE_F16, 4)) != ATTN_OK) return st;
         if ((st = make_view(vsst, "v_scale_shift", &vss, 1u << ATTN_DTYPE_F16, 4)) != ATTN_OK) return st;
         if (q.dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q must be bf16", fn);
+        // INT4 rows are D/2 bytes: compare head dims in elements
+        if (quant == ATTN_DTYPE_INT4X2) {
+            k.D *= 2;
+            v.D *= 2;
+        }
+        const int64_t G = kss.D / 2;
+        if (kss.D % 2 || kss.D != vss.D)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: scale/shift last axes must be 2G (equal for k and v)", fn);
         for (const View *m : {&kss, &vss})
-            if (!same_heads(*m, k) || m->B != k.B || m->M != k.M || m->D != 2)
+            if (!same_heads(*m, k) || m->B != k.B || m->M != k.M)
                 return fail(ATTN_ERR_INVALID_ARGUMENT,
-                            "%s: scale/shift tensors must have k's shape with the last axis 2", fn);
+                            "%s: scale/shift tensors must have k's shape with the last axis 2G", fn);
+        if (quant == ATTN_DTYPE_FP8_E4M3 && G != 1)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: FP8 caches are row-wise (scale/shift last axis 2)", fn);
+        if (G < 1 || k.D % G || (k.D / G) % 32)
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: groups of D/G elements must be a multiple of 32", fn);
+        group = (int)(k.D / G);
     } else if (k.dtype != q.dtype || v.dtype != q.dtype || o.dtype != q.dtype) {
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out must share one dtype", fn);
     }
@@ -568,7 +585,10 @@ attn_status decode(const char *fn, bool fp8, const attn_tensor *qt, const attn_t
     d.vss = vss.p;
     d.skss = kss.s;
     d.svss = vss.s;
-    const int elem = fp8 ? attn::DECODE_FP8 : (q.dtype == ATTN_DTYPE_F32 ? attn::DECODE_F32 : attn::DECODE_BF16);
+    d.group = group;
+    const int elem = quant == ATTN_DTYPE_FP8_E4M3 ? attn::DECODE_FP8
+                     : quant == ATTN_DTYPE_INT4X2 ? attn::DECODE_INT4
+                     : (q.dtype == ATTN_DTYPE_F32 ? attn::DECODE_F32 : attn::DECODE_BF16);
     hipError_t e = attn::launch_decode_partials(d, elem, (hipStream_t)stream);
     if (e != hipSuccess) return launch_status(e, fn);
 
@@ -602,7 +622,7 @@ extern "C" {
 attn_status attn_decode_splitkv(const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
                                 int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                 const attn_tensor *ot, float *lse, attn_stream_t stream) {
-    return decode("attn_decode_splitkv", false, qt, kt, vt, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, num_splits,
+    return decode("attn_decode_splitkv", 0, qt, kt, vt, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, num_splits,
                   scale, workspace, workspace_bytes, ot, lse, stream);
 }
 
@@ -611,7 +631,7 @@ attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k
                                       int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
                                       int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                       const attn_tensor *out, float *lse, attn_stream_t stream) {
-    return decode("attn_decode_splitkv_paged", false, q, k, v, nullptr, nullptr, seqlens, block_tables,
+    return decode("attn_decode_splitkv_paged", 0, q, k, v, nullptr, nullptr, seqlens, block_tables,
                   max_blocks_per_seq, page_size, max_seqlen_k, num_splits, scale, workspace, workspace_bytes, out, lse,
                   stream);
 }
@@ -624,8 +644,22 @@ attn_status attn_decode_splitkv_fp8(const attn_tensor *q, const attn_tensor *k, 
                                     const attn_tensor *out, float *lse, attn_stream_t stream) {
     const char *fn = "attn_decode_splitkv_fp8";
     if (block_tables && !seqlens) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block_tables need seqlens", fn);
-    return decode(fn, true, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, max_blocks_per_seq,
-                  page_size, max_seqlen_k, num_splits, scale, workspace, workspace_bytes, out, lse, stream);
+    return decode(fn, ATTN_DTYPE_FP8_E4M3, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables,
+                  max_blocks_per_seq, page_size, max_seqlen_k, num_splits, scale, workspace, workspace_bytes, out,
+                  lse, stream);
+}
+
+attn_status attn_decode_splitkv_int4(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                     const attn_tensor *k_scale_shift, const attn_tensor *v_scale_shift,
+                                     const int32_t *seqlens, const int32_t *block_tables,
+                                     int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                     int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                                     const attn_tensor *out, float *lse, attn_stream_t stream) {
+    const char *fn = "attn_decode_splitkv_int4";
+    if (block_tables && !seqlens) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block_tables need seqlens", fn);
+    return decode(fn, ATTN_DTYPE_INT4X2, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables,
+                  max_blocks_per_seq, page_size, max_seqlen_k, num_splits, scale, workspace, workspace_bytes, out,
+                  lse, stream);
 }
 
 }  // extern "C"

@@ -9,9 +9,9 @@
 //   * one workgroup (4 waves) per (chunk, batch, group of hpw neighbouring heads); hpw
 //     is picked so that a cache row's segments of those heads are 512 contiguous bytes
 //     (a lone 128- or 256-byte head segment per row streams markedly slower);
-//   * a lane group of D/8 (bf16) or D/16 (FP8) lanes reads one key row of one head with
-//     16-byte loads; K and V rows of the same keys are loaded together, eight rows per
-//     lane in flight before any arithmetic;
+//   * a lane group of D/8 (bf16), D/16 (FP8) or D/32 (INT4) lanes reads one key row of one
+//     head with 16-byte loads; K and V rows of the same keys are loaded together, eight
+//     rows per lane (four for INT4) in flight before any arithmetic;
 //   * every lane group keeps its own online softmax (base-2 running max, sum of
 //     exponentials, p-weighted V columns) over the rows it reads, so there is no score
 //     buffer and no barrier in the stream; at the end the states of a head's lane
@@ -21,11 +21,13 @@
 //     PagedBlockDiagonalPaddedKeysMask): per-sequence key counts on the device,
 //     and for a paged cache the physical row of every key of a sub-chunk is
 //     resolved once into LDS from the block table;
-//   * row-wise FP8 caches ("Attention - operator protocol", InputsFp8): a lane takes
-//     16 E4M3 codes per 16-byte load and widens them with the hardware conversion;
-//     the row's (scale, shift) is applied to the reduced dot product, since
-//     q.(c*scale + shift) = scale*(q.c) + shift*sum(q), and on the V side the
-//     weight p*scale multiplies the codes while p*shift is summed once per row.
+//   * quantised caches: row-wise FP8 ("Attention - operator protocol", InputsFp8) and
+//     row/group-wise INT4 (triton_splitk.FwOp).  A lane takes 16 E4M3 codes (hardware
+//     conversion) or 32 4-bit codes (byte conversions) per 16-byte load, all inside one
+//     (scale, shift) group; the group's pair is applied to the lane's partial dot product
+//     before the reduction over the row's lanes, since q.(c*scale + shift) =
+//     scale*(q.c) + shift*sum(q), and on the V side the weight p*scale multiplies the
+//     codes while p*shift is summed once per row and lane.
 // Output: the chunk's normalised fp32 output and its natural-log LSE; an empty
 // chunk gives 0 and -inf.
 #include <type_traits>
@@ -43,11 +45,15 @@ constexpr int SUB = 2048;  // keys per sub-chunk of a paged cache (their rows ar
 #ifndef DECODE_UNROLL
 #define DECODE_UNROLL 8
 #endif
+#ifndef DECODE_UNROLL_INT4
+#define DECODE_UNROLL_INT4 4
+#endif
 #ifndef DECODE_PIPE
 #define DECODE_PIPE 0
 #endif
-constexpr int U = DECODE_UNROLL;        // key rows per lane and round
-constexpr bool PIPE = DECODE_PIPE != 0;  // issue round i+1 before using round i
+constexpr int U_DEF = DECODE_UNROLL;       // key rows per lane and round
+constexpr int U_INT4 = DECODE_UNROLL_INT4;  // the same for INT4 caches (32 codes per lane and row)
+constexpr bool PIPE = DECODE_PIPE != 0;     // issue round i+1 before using round i
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -79,10 +85,25 @@ __device__ __forceinline__ void unpack_fp8(const u32x4 &w, float *x) {
     }
 }
 
+// 32 unsigned 4-bit codes (element 2i in the low nibble of byte i) to fp32; exact.
+__device__ __forceinline__ void unpack_int4(const u32x4 &w, float *x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned lo = w[i] & 0x0f0f0f0fu, hi = (w[i] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[8 * i + 2 * j] = (float)((lo >> (8 * j)) & 0xffu);
+            x[8 * i + 2 * j + 1] = (float)((hi >> (8 * j)) & 0xffu);
+        }
+    }
+}
+
 template <int ELEM>
 __device__ __forceinline__ void unpack_elem(const u32x4 &w, float *x) {
     if constexpr (ELEM == DECODE_FP8)
         unpack_fp8(w, x);
+    else if constexpr (ELEM == DECODE_INT4)
+        unpack_int4(w, x);
     else
         unpack<ELEM == DECODE_F32>(w, x);
 }
@@ -93,7 +114,7 @@ __device__ __forceinline__ float ss_shift(uint32_t w) { return (float)__builtin_
 
 // Workgroups are dealt to the 8 XCDs round-robin (workgroup i to XCD i % 8).  Renumbered so
 // that every XCD takes one contiguous range of the logical order: the workgroups of one cache
-// row range (neighbouring heads, which share DRAM pages and the lines of FP8 metadata) then run
+// row range (neighbouring heads, which share DRAM pages and the lines of quantisation metadata) then run
 // on one XCD at about the same time.  A bijection on [0, n).
 __device__ __forceinline__ int xcd_remap(int i, int n) {
     const int x = i & 7, k = i >> 3, q = n >> 3, r = n & 7;
@@ -105,12 +126,16 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
 // row block_tables[b][j / page_size] * page_size + j % page_size (page numbers clamped to the cache).
 template <int HD, int ELEM, int MODE>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
-    constexpr bool F32 = ELEM == DECODE_F32, FP8 = ELEM == DECODE_FP8;
-    constexpr int EPL = F32 ? 4 : (FP8 ? 16 : 8);  // elements per 16-byte load
-    constexpr int LPK = HD / EPL;                  // lanes per key row (a lane group)
-    constexpr int KPP = NT / LPK;                  // lane groups of the workgroup
-    using T = typename std::conditional<F32, float, typename std::conditional<FP8, uint8_t, __bf16>::type>::type;
-    using QT = typename std::conditional<F32, float, __bf16>::type;  // FP8 caches take bf16 queries
+    constexpr bool F32 = ELEM == DECODE_F32, INT4 = ELEM == DECODE_INT4;
+    constexpr bool QUANT = ELEM == DECODE_FP8 || INT4;             // codes + (scale, shift) metadata
+    constexpr int EPL = F32 ? 4 : (INT4 ? 32 : (QUANT ? 16 : 8));  // elements per 16-byte load
+    constexpr int LPK = HD / EPL;                                  // lanes per key row (a lane group)
+    constexpr int KPP = NT / LPK;                                  // lane groups of the workgroup
+    constexpr int U = INT4 ? U_INT4 : U_DEF;                       // key rows per lane and round
+    // cache element type (bytes for the quantised caches; their strides count bytes) and q's
+    using T = typename std::conditional<F32, float, typename std::conditional<QUANT, uint8_t, __bf16>::type>::type;
+    using QT = typename std::conditional<F32, float, __bf16>::type;
+    constexpr int TPL = 16 / (int)sizeof(T);  // cache elements of type T per 16-byte load
 
     __shared__ float acc_s[KPP][HD];
     __shared__ float m_s[KPP], l_s[KPP], w_s[KPP];
@@ -133,34 +158,37 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const int hs = g & (hpw - 1), rs = g >> lh;
     const int hf = (hg << lh) + hs;
     const QT *qp = (const QT *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin) + cl * EPL;
-    const T *kp = (const T *)a.k + kb + head_offset(a.sk, hf, a.Hin) + cl * EPL;
-    const T *vp = (const T *)a.v + vb + head_offset(a.sv, hf, a.Hin) + cl * EPL;
-    // FP8: per-row metadata words, addressed in fp16 units like a [.., 2] tensor
+    const T *kp = (const T *)a.k + kb + head_offset(a.sk, hf, a.Hin) + cl * TPL;
+    const T *vp = (const T *)a.v + vb + head_offset(a.sv, hf, a.Hin) + cl * TPL;
+    // quantised caches: the metadata word of this lane's group in every row, addressed in fp16
+    // units like a [.., G, 2] tensor (a lane's EPL elements never straddle two groups)
     const uint16_t *kss = nullptr, *vss = nullptr;
-    if constexpr (FP8) {
-        kss = (const uint16_t *)a.kss + (MODE == 2 ? 0 : (int64_t)b * a.skss.b) + head_offset(a.skss, hf, a.Hin);
-        vss = (const uint16_t *)a.vss + (MODE == 2 ? 0 : (int64_t)b * a.svss.b) + head_offset(a.svss, hf, a.Hin);
+    if constexpr (QUANT) {
+        const int gw = 2 * ((cl * EPL) / a.group);
+        kss = (const uint16_t *)a.kss + (MODE == 2 ? 0 : (int64_t)b * a.skss.b) + head_offset(a.skss, hf, a.Hin) + gw;
+        vss = (const uint16_t *)a.vss + (MODE == 2 ? 0 : (int64_t)b * a.svss.b) + head_offset(a.svss, hf, a.Hin) + gw;
     }
 
     float qv[EPL];
-    if constexpr (FP8) {
-        unpack<false>(*(const u32x4 *)qp, qv);
-        unpack<false>(*(const u32x4 *)(qp + 8), qv + 8);
+    if constexpr (F32) {
+        unpack<true>(*(const u32x4 *)qp, qv);
     } else {
-        unpack<F32>(*(const u32x4 *)qp, qv);
+#pragma unroll
+        for (int i = 0; i < EPL / 8; ++i) unpack<false>(*(const u32x4 *)(qp + 8 * i), qv + 8 * i);
     }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[e] *= a.scale_log2;
-    float qsum = 0.f;  // scale_log2 * sum(q), the weight of a row's shift in its score
-    if constexpr (FP8) {
+    // quantised caches: scale_log2 * (sum of this lane's q elements), the weight of its group's
+    // shift; q.(c*scale + shift) summed over the lanes = sum of scale*(q.c) + shift*sum(q)
+    float qsum = 0.f;
+    if constexpr (QUANT) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qsum += qv[e];
-#pragma unroll
-        for (int o = LPK / 2; o >= 1; o >>= 1) qsum += __shfl_xor(qsum, o, 64);
     }
 
     // Online softmax state of this lane group (the same in its LPK lanes): base-2 running max,
-    // sum of exponentials, p-weighted values (this lane's EPL columns) and, for FP8, sum of p*shift.
+    // sum of exponentials, p-weighted values (this lane's EPL columns) and, for the quantised
+    // caches, the sum of p * shift of this lane's group.
     float acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
@@ -187,13 +215,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
                 const int64_t row = MODE == 2 ? (r < n ? rows_s[r] : 0) : sub0 + r;
                 wk[u] = r < n ? *(const u32x4 *)(kp + row * a.sk.m) : u32x4{0, 0, 0, 0};
                 wv[u] = r < n ? *(const u32x4 *)(vp + row * a.sv.m) : u32x4{0, 0, 0, 0};
-                if constexpr (FP8) {
+                if constexpr (QUANT) {
                     sk[u] = r < n ? *(const uint32_t *)(kss + row * a.skss.m) : 0u;
                     sv[u] = r < n ? *(const uint32_t *)(vss + row * a.svss.m) : 0u;
                 }
             }
         };
-        constexpr int NS = FP8 ? U : 1;
+        constexpr int NS = QUANT ? U : 1;
         u32x4 wk[U], wv[U], wkn[U], wvn[U];
         uint32_t sk[NS], sv[NS], skn[NS], svn[NS];
         load(0, wkn, wvn, skn, svn);
@@ -218,9 +246,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
                 float dot = 0.f;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) dot = fmaf(qv[e], x[e], dot);
+                if constexpr (QUANT) dot = fmaf(ss_scale(sk[u]), dot, ss_shift(sk[u]) * qsum);
 #pragma unroll
                 for (int o = LPK / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
-                if constexpr (FP8) dot = fmaf(ss_scale(sk[u]), dot, ss_shift(sk[u]) * qsum);
                 sc[u] = p + u * RPP + rs < n ? dot : -INFINITY;
                 mx = fmaxf(mx, sc[u]);
             }
@@ -236,7 +264,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
             for (int u = 0; u < U; ++u) {
                 float pr = __builtin_amdgcn_exp2f(sc[u] - mu);
                 l_run += pr;
-                if constexpr (FP8) {
+                if constexpr (QUANT) {
                     sh_acc = fmaf(pr, ss_shift(sv[u]), sh_acc);
                     pr *= ss_scale(sv[u]);
                 }
@@ -288,11 +316,11 @@ template <int HD, int ELEM, int MODE>
 hipError_t launch(const DecodeArgs &args, hipStream_t stream) {
     // heads per workgroup: enough neighbouring head segments for DECODE_ROW_BYTES contiguous bytes
     // per cache row, a power of two that divides Htot and leaves every head at least one lane group
-    constexpr int ES = ELEM == DECODE_F32 ? 4 : (ELEM == DECODE_FP8 ? 1 : 2);
-    constexpr int EPL = 16 / ES, KPP = NT / (HD / EPL);
+    constexpr int RB = ELEM == DECODE_F32 ? 4 * HD : (ELEM == DECODE_FP8 ? HD : (ELEM == DECODE_INT4 ? HD / 2 : 2 * HD));
+    constexpr int KPP = NT / (RB / 16);  // lane groups: one 16-byte load per lane per row
     DecodeArgs a = args;
     a.log2_hpw = 0;
-    while ((HD * ES << (a.log2_hpw + 1)) <= DECODE_ROW_BYTES && (2 << a.log2_hpw) <= KPP &&
+    while ((RB << (a.log2_hpw + 1)) <= DECODE_ROW_BYTES && (2 << a.log2_hpw) <= KPP &&
            a.Htot % (2 << a.log2_hpw) == 0)
         ++a.log2_hpw;
     const int64_t grid = (int64_t)a.S * a.B * (a.Htot >> a.log2_hpw);
@@ -315,6 +343,7 @@ hipError_t launch_elem(const DecodeArgs &a, int elem, hipStream_t stream) {
     case DECODE_BF16: return launch_mode<HD, DECODE_BF16>(a, stream);
     case DECODE_F32: return launch_mode<HD, DECODE_F32>(a, stream);
     case DECODE_FP8: return launch_mode<HD, DECODE_FP8>(a, stream);
+    case DECODE_INT4: return launch_mode<HD, DECODE_INT4>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

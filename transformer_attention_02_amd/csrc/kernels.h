@@ -54,14 +54,17 @@ struct DecodeArgs {
     const int32_t *seqlens;       // [B], clamped to [0, cap]
     const int32_t *block_tables;  // [B, bt_stride] page numbers, or null (lanes [B, cap, ...])
     int bt_stride, page_size, num_pages, cap;
-    // FP8 caches only: (scale, shift) fp16 pairs per cache row and head; strides in fp16 units
+    // FP8 / INT4 caches only: (scale, shift) fp16 pairs per cache row, head and group of
+    // `group` consecutive elements (a multiple of 32 dividing D); strides in fp16 units
     const void *kss, *vss;
     Strides skss, svss;
+    int group;
     int log2_hpw;  // heads per workgroup = 1 << log2_hpw (set by the launcher)
 };
 
-// Element type of a decode K/V cache (q is bf16 for FP8 caches, else the cache's type).
-enum DecodeElem : int { DECODE_BF16 = 0, DECODE_F32 = 1, DECODE_FP8 = 2 };
+// Element type of a decode K/V cache (q is bf16 for the quantised caches, else the cache's type).
+// INT4: two unsigned 4-bit codes per byte, element 2i in the low nibble of byte i.
+enum DecodeElem : int { DECODE_BF16 = 0, DECODE_F32 = 1, DECODE_FP8 = 2, DECODE_INT4 = 3 };
 
 constexpr int kMaxChunks = 128;
 
