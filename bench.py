@@ -279,6 +279,7 @@ def main():
                 "keys_per_s": round(B * Mkv * H / (ms_4 * 1e-3), 1),
                 "roofline": {"bound": "hbm", "achieved": round(gbs_4, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(gbs_4 / PEAK_HBM_GBS, 4), "bytes_per_call": i4_bytes,
+                             "traffic": recorded_traffic(f"decode int4 g{G} 16x32768x32x128 s64"),
                              "note": "algorithmic bytes = K+V codes and their metadata once"}}
             del k4, v4, ks4, vs4
             torch.cuda.empty_cache()
