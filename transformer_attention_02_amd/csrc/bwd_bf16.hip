@@ -15,12 +15,13 @@
 //      Each lane first forms its row's D_i and base-2 LSE L_i = lse_i log2(e) (+inf for
 //      a row with no visible key, so every rebuilt P of that row is exactly 0) and
 //      stores both in a caller workspace for the second launch.
-//   2. bwd_dkdv_kernel: a workgroup owns 32 keys per wave of one (batch, head, sequence);
-//      those keys' K and V rows stay in registers as matrix-core operands while 64-row
-//      tiles of Q and dout (and their L, D) stream through a 2-stage LDS ring.  Per tile:
-//      S = Q K^T and dP = dout V^T (lane l owns key l%32 and 16 query rows of each
-//      32-row block), P and dS in fp32, then dV^T += dout^T P and dK^T += Q^T dS with the
-//      A operands read transposed from the row-major LDS tiles.
+//   2. bwd_dkdv_pair_kernel: a workgroup owns 128 keys of one (batch, head, sequence), 32
+//      per pair of waves; the pair keeps those keys' K and V rows in registers as
+//      matrix-core operands while 64-row tiles of Q and dout (and their L, D) stream
+//      through a 2-stage LDS ring.  Per tile and 32-row block: S = Q K^T and
+//      dP = dout V^T (lane l owns key l%32 and 16 query rows), P and dS in fp32, then
+//      dV^T += dout^T P and dK^T += Q^T dS with the A operands read transposed from the
+//      row-major LDS tiles.
 // P is rounded to bf16 for dV and dS for dK and dQ; every product accumulates in fp32.
 // Same matrix-core layout as the forward (v_mfma_f32_32x32x16_bf16): a B operand taken
 // from C-layout registers gives lane half h the rows {8a + 4h + 0..3} of each 16-row
@@ -80,26 +81,34 @@ __device__ __forceinline__ bf16x8 tr_frag(const unsigned char LDS_AS *base, int 
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int HD, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
-    constexpr int NT = NW * 64;
-    constexpr int BK = NW * 32;               // keys per workgroup
-    constexpr int ROWB = HD * 2;              // bytes per tile row
-    constexpr int CPR = HD / 8;               // 16-byte chunks per row
-    constexpr int TILE_BYTES = BQ * ROWB;     // one Q or dout tile
+// dK/dV kernel: 8 waves, 128 keys.  Waves w and w + 4 (which share a SIMD) own the same 32
+// keys; wave w computes S = Q K^T, P and dV^T += dout^T P and passes P through LDS, wave
+// w + 4 computes dP = dout V^T, dS = P (dP - D) and dK^T += Q^T dS.  Each wave holds one
+// accumulator set and one resident operand (K or V), so two waves fit per SIMD and one's
+// matrix-core ops overlap the other's LDS reads and fp32 work (a single wave doing all
+// four products needs ~320 registers per lane and runs alone on its SIMD).
+template <int HD>
+__global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
+    constexpr int NW = 8, NT = NW * 64, BK = 128;  // keys per workgroup (32 per wave pair)
+    constexpr int ROWB = HD * 2;
+    constexpr int CPR = HD / 8;
+    constexpr int TILE_BYTES = BQ * ROWB;
     constexpr int STAGES = 2;
-    constexpr int LSD_BASE = STAGES * 2 * TILE_BYTES;  // then per stage 64 L values and 64 D values
+    constexpr int LSD_BASE = STAGES * 2 * TILE_BYTES;       // per stage: 64 L values, 64 D values
+    constexpr int PX_BASE = LSD_BASE + STAGES * 2 * BQ * 4;  // P exchange: [pair][2 buffers][4 KB]
+    constexpr int PX_BYTES = 32 * 32 * 4;                    // one 32x32 fp32 block
     constexpr int ROUNDS = TILE_BYTES / 16 / NT;
     constexpr int KS = HD / 16, MB = HD / 32;
     static_assert(ROUNDS >= 1 && ROUNDS * NT * 16 == TILE_BYTES, "tile split");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[LSD_BASE + STAGES * 2 * BQ * 4];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[PX_BASE + 4 * 2 * PX_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave & 3;
+    const bool pside = wave < 4;  // S, P, dV side; the other wave of the pair does dP, dS, dK
 
-    // ---- which (key tile, sequence, batch*head); key tiles in ascending order
     const int BH = a.B * a.Htot;
     int id = blockIdx.x;
     const int bh = id % BH;
@@ -114,12 +123,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
     if (k0 >= Lk) return;
     const int k1 = min(k0 + BK, Lk);
     const int64_t shift = a.bottom_right ? (int64_t)Lk - Lq : 0;
-    // key j is visible from row i iff i + shift - wl <= j <= i + shift + wr
     const int qbeg = clampk((int64_t)k0 - shift - a.wr, 0, Lq);
     const int qend = clampk((int64_t)k1 - 1 - shift + a.wl + 1, 0, Lq);
     const int tb = qbeg / BQ;
     const int te = qend > qbeg ? (qend + BQ - 1) / BQ : tb;
-    // tiles [ua, ub): every row < Lq and every key of [k0, k1) inside every row's window
     int ua = (clampk((int64_t)k1 - 1 - shift - a.wr, 0, Lq) + BQ - 1) / BQ;
     int ub = clampk(min((int64_t)k0 - shift + a.wl, (int64_t)Lq - 1) + 1, 0, Lq) / BQ;
     ua = min(max(ua, tb), te);
@@ -130,10 +137,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
         (const __bf16 *)a.dout + (int64_t)b * a.sdo.b + head_offset(a.sdo, hf, a.Hin) + (int64_t)qs * a.sdo.m;
     const __bf16 *kp = (const __bf16 *)a.k + (int64_t)b * a.sk.b + head_offset(a.sk, hf, a.Hin) + (int64_t)ks * a.sk.m;
     const __bf16 *vp = (const __bf16 *)a.v + (int64_t)b * a.sv.b + head_offset(a.sv, hf, a.Hin) + (int64_t)ks * a.sv.m;
-    const int64_t wrow = ((int64_t)b * a.Htot + hf) * a.Mq + qs;  // workspace row of local query 0
+    const int64_t wrow = ((int64_t)b * a.Htot + hf) * a.Mq + qs;
     const unsigned qstride = (unsigned)a.sq.m * 2u, gstride = (unsigned)a.sdo.m * 2u;
 
-    // ---- async tile loads: Q and dout rows of one 64-row tile, and their L and D values
     unsigned qoff[ROUNDS], goff[ROUNDS];
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
@@ -161,36 +167,33 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
         }
     };
 
-    // ---- this wave's 32 keys: K and V rows as B operands, resident for the whole kernel
-    const int kw0 = k0 + wave * 32;  // first local key of this wave
-    const int key = kw0 + l32;       // this lane's key
-    bf16x8 kf[KS], vf[KS];
+    // ---- this pair's 32 keys; the P side keeps K, the other side V, as B operands
+    const int kw0 = k0 + pair * 32;
+    const int key = kw0 + l32;
+    bf16x8 rf[KS];
     if (key < Lk) {
-        const u32x4 *ksrc = (const u32x4 *)(kp + (int64_t)key * a.sk.m + 8 * hh);
-        const u32x4 *vsrc = (const u32x4 *)(vp + (int64_t)key * a.sv.m + 8 * hh);
+        const u32x4 *src = (const u32x4 *)((pside ? kp + (int64_t)key * a.sk.m : vp + (int64_t)key * a.sv.m) + 8 * hh);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            kf[s] = __builtin_bit_cast(bf16x8, ksrc[2 * s]);
-            vf[s] = __builtin_bit_cast(bf16x8, vsrc[2 * s]);
-        }
+        for (int s = 0; s < KS; ++s) rf[s] = __builtin_bit_cast(bf16x8, src[2 * s]);
     } else {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kf[s] = vf[s] = bf16x8{};
+        for (int s = 0; s < KS; ++s) rf[s] = bf16x8{};
     }
-    // rows that see this key: [qlo, qhi]
     const int qlo = clampk((int64_t)key - shift - a.wr, 0, Lq);
     const int qhi = clampk((int64_t)key - shift + a.wl, -1, Lq - 1);
     const float c = a.scale_log2;
 
-    int raddr[KS];  // row reads: row l32 (+ 32 per block), chunk 2s + hh
+    int raddr[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) raddr[s] = l32 * ROWB + (((2 * s + hh) ^ swz<HD>(l32)) << 4);
     int taddr[MB][2];
     tr_offsets<HD, MB>(lane, taddr);
+    // P exchange slot of this lane: float4 r4 of 16 values at [pair][buf][r4][lane]
+    float LDS_AS *px = (float LDS_AS *)(smem + PX_BASE) + pair * 2 * (PX_BYTES / 4) + lane * 4;
 
-    f32x16 dv[MB], dk[MB];
+    f32x16 acc[MB];  // dV^T on the P side, dK^T on the other
 #pragma unroll
-    for (int i = 0; i < MB; ++i) dv[i] = dk[i] = f32x16{};
+    for (int i = 0; i < MB; ++i) acc[i] = f32x16{};
 
     auto step = [&](int t, auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
@@ -198,60 +201,74 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
         const int stage = (t - tb) % STAGES;
         wait_barrier<0>();
         if (t + 1 < te) issue(t + 1);
-        if (kw0 >= Lk) return;
-        if (MASKED && ((int64_t)kw0 > (int64_t)q0 + BQ - 1 + shift + a.wr ||
-                       (int64_t)kw0 + 31 < (int64_t)q0 + shift - a.wl))
-            return;
+        // this pair's keys see no row of the tile: compute nothing, still meet every barrier
+        const bool active = kw0 < Lk && !(MASKED && ((int64_t)kw0 > (int64_t)q0 + BQ - 1 + shift + a.wr ||
+                                                      (int64_t)kw0 + 31 < (int64_t)q0 + shift - a.wl));
         const unsigned char LDS_AS *st = (const unsigned char LDS_AS *)smem + stage * 2 * TILE_BYTES;
         const float LDS_AS *ls = (const float LDS_AS *)(smem + LSD_BASE + stage * 2 * BQ * 4);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            // S = Q K^T and dP = dout V^T for 32 query rows: lane owns key l32, rows 8g + 4hh + j
-            f32x16 s = f32x16{}, dp = f32x16{};
+            float LDS_AS *pxb = px + ((2 * (t - tb) + qb) & 1) * (PX_BYTES / 4);
+            f32x16 x = f32x16{};  // S on the P side, dP on the other
+            bf16x8 ob[2];         // P (P side) or dS (other side) as bf16 B operands
+            if (active) {
+                const int aoff = pside ? 0 : TILE_BYTES;  // Q rows or dout rows
 #pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                const bf16x8 qa = *(const bf16x8 LDS_AS *)(st + raddr[k] + qb * 32 * ROWB);
-                const bf16x8 ga = *(const bf16x8 LDS_AS *)(st + TILE_BYTES + raddr[k] + qb * 32 * ROWB);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[k], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[k], dp, 0, 0, 0);
-            }
-            float p[16], ds[16];
+                for (int k = 0; k < KS; ++k) {
+                    const bf16x8 fa = *(const bf16x8 LDS_AS *)(st + aoff + raddr[k] + qb * 32 * ROWB);
+                    x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, rf[k], x, 0, 0, 0);
+                }
+                if (pside) {
+                    float p[16];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int row = qb * 32 + 8 * g + 4 * hh;
-                const f32x4 l2 = *(const f32x4 LDS_AS *)(ls + row);
-                const f32x4 dd = *(const f32x4 LDS_AS *)(ls + BQ + row);
+                    for (int g = 0; g < 4; ++g) {
+                        const int row = qb * 32 + 8 * g + 4 * hh;
+                        const f32x4 l2 = *(const f32x4 LDS_AS *)(ls + row);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * g + j;
-                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[j]));
-                    if (MASKED) {
-                        const int q = q0 + row + j;
-                        if (q < qlo || q > qhi) pr = 0.f;
+                        for (int j = 0; j < 4; ++j) {
+                            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x[4 * g + j], c, -l2[j]));
+                            if (MASKED) {
+                                const int q = q0 + row + j;
+                                if (q < qlo || q > qhi) pr = 0.f;
+                            }
+                            p[4 * g + j] = pr;
+                        }
+                        *(f32x4 LDS_AS *)(pxb + g * 256) = f32x4{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
                     }
-                    p[r] = pr;
-                    ds[r] = pr * (dp[r] - dd[j]);
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) ob[kt][i] = (__bf16)p[8 * kt + i];
                 }
             }
-            // bf16 operands in the product's k order: step kt, element i <-> register 8kt + i
-            bf16x8 pb[2], dsb[2];
+            // P of this block is in LDS; the other side's dP is in its registers
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (active) {
+                if (!pside) {
+                    float ds[16];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+                    for (int g = 0; g < 4; ++g) {
+                        const int row = qb * 32 + 8 * g + 4 * hh;
+                        const f32x4 dd = *(const f32x4 LDS_AS *)(ls + BQ + row);
+                        const f32x4 pv = *(const f32x4 LDS_AS *)(pxb + g * 256);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    pb[kt][i] = (__bf16)p[8 * kt + i];
-                    dsb[kt][i] = (__bf16)ds[8 * kt + i];
+                        for (int j = 0; j < 4; ++j) ds[4 * g + j] = pv[j] * (x[4 * g + j] - dd[j]);
+                    }
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) ob[kt][i] = (__bf16)ds[8 * kt + i];
                 }
-            // dV^T += dout^T P and dK^T += Q^T dS over the two 16-row steps of this block
+                // dV^T += dout^T P (P side) or dK^T += Q^T dS (other side)
+                const int toff = pside ? TILE_BYTES : 0;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const int roff = (qb * 32 + kt * 16) * ROWB;
+                for (int kt = 0; kt < 2; ++kt) {
+                    const int roff = (qb * 32 + kt * 16) * ROWB;
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    const bf16x8 gt = tr_frag(st + TILE_BYTES, taddr[mb][0] + roff, taddr[mb][1] + roff);
-                    dv[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt, pb[kt], dv[mb], 0, 0, 0);
-                    const bf16x8 qt = tr_frag(st, taddr[mb][0] + roff, taddr[mb][1] + roff);
-                    dk[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsb[kt], dk[mb], 0, 0, 0);
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const bf16x8 ft = tr_frag(st + toff, taddr[mb][0] + roff, taddr[mb][1] + roff);
+                        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ft, ob[kt], acc[mb], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -263,24 +280,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
     for (; t < ub; ++t) step(t, std::false_type{});
     for (; t < te; ++t) step(t, std::true_type{});
 
-    // ---- store: lane owns key `key`; register r of block mb is column 32mb + 8(r/4) + 4hh + r%4
     if (key < Lk) {
-        unsigned char *dkp = (unsigned char *)a.dk;
-        unsigned char *dvp = (unsigned char *)a.dv;
-        const int64_t kb_ = (int64_t)b * a.sdk.b + head_offset(a.sdk, hf, a.Hin) + (int64_t)(ks + key) * a.sdk.m;
-        const int64_t vb_ = (int64_t)b * a.sdv.b + head_offset(a.sdv, hf, a.Hin) + (int64_t)(ks + key) * a.sdv.m;
-        const float sc = a.scale;
+        unsigned char *dp_ = (unsigned char *)(pside ? a.dv : a.dk);
+        const Strides &so = pside ? a.sdv : a.sdk;
+        const int64_t base = (int64_t)b * so.b + head_offset(so, hf, a.Hin) + (int64_t)(ks + key) * so.m;
+        const float sc = pside ? 1.f : a.scale;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d0 = mb * 32 + 8 * g + 4 * hh;
-                *(bf16x4 *)(dkp + (kb_ + d0) * 2) =
-                    bf16x4{(__bf16)(dk[mb][4 * g] * sc), (__bf16)(dk[mb][4 * g + 1] * sc),
-                           (__bf16)(dk[mb][4 * g + 2] * sc), (__bf16)(dk[mb][4 * g + 3] * sc)};
-                *(bf16x4 *)(dvp + (vb_ + d0) * 2) =
-                    bf16x4{(__bf16)dv[mb][4 * g], (__bf16)dv[mb][4 * g + 1], (__bf16)dv[mb][4 * g + 2],
-                           (__bf16)dv[mb][4 * g + 3]};
+                *(bf16x4 *)(dp_ + (base + d0) * 2) =
+                    bf16x4{(__bf16)(acc[mb][4 * g] * sc), (__bf16)(acc[mb][4 * g + 1] * sc),
+                           (__bf16)(acc[mb][4 * g + 2] * sc), (__bf16)(acc[mb][4 * g + 3] * sc)};
             }
     }
 }
@@ -485,13 +497,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
 
 template <int HD>
 hipError_t launch_hd(const BwdArgs &a, hipStream_t stream) {
-    constexpr int NW_KV = 4, NW_Q = 8;
+    constexpr int NW_Q = 8;
     const int64_t gq = (int64_t)((a.max_seqlen_q + NW_Q * 32 - 1) / (NW_Q * 32)) * a.nseq * a.B * a.Htot;
-    const int64_t gkv = (int64_t)((a.max_seqlen_k + NW_KV * 32 - 1) / (NW_KV * 32)) * a.nseq * a.B * a.Htot;
+    const int64_t gkv = (int64_t)((a.max_seqlen_k + 127) / 128) * a.nseq * a.B * a.Htot;
     if (gq > 0x7fffffff || gkv > 0x7fffffff) return hipErrorInvalidConfiguration;
     // the dQ launch writes the per-row D and L that the dK/dV launch reads
     if (gq > 0) hipLaunchKernelGGL((bwd_dq_kernel<HD, NW_Q>), dim3((unsigned)gq), dim3(NW_Q * 64), 0, stream, a);
-    if (gkv > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<HD, NW_KV>), dim3((unsigned)gkv), dim3(NW_KV * 64), 0, stream, a);
+    if (gkv > 0) hipLaunchKernelGGL((bwd_dkdv_pair_kernel<HD>), dim3((unsigned)gkv), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
