@@ -87,13 +87,12 @@ __device__ __forceinline__ bf16x8 tr_frag(const unsigned char LDS_AS *base, int 
 // accumulator set and one resident operand (K or V), so two waves fit per SIMD and one's
 // matrix-core ops overlap the other's LDS reads and fp32 work (a single wave doing all
 // four products needs ~320 registers per lane and runs alone on its SIMD).
-template <int HD>
+template <int HD, int STAGES>
 __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
     constexpr int NW = 8, NT = NW * 64, BK = 128;  // keys per workgroup (32 per wave pair)
     constexpr int ROWB = HD * 2;
     constexpr int CPR = HD / 8;
     constexpr int TILE_BYTES = BQ * ROWB;
-    constexpr int STAGES = 2;
     constexpr int LSD_BASE = STAGES * 2 * TILE_BYTES;       // per stage: 64 L values, 64 D values
     constexpr int PX_BASE = LSD_BASE + STAGES * 2 * BQ * 4;  // P exchange: [pair][2 buffers][4 KB]
     constexpr int PX_BYTES = 32 * 32 * 4;                    // one 32x32 fp32 block
@@ -199,8 +198,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int q0 = t * BQ;
         const int stage = (t - tb) % STAGES;
-        wait_barrier<0>();
-        if (t + 1 < te) issue(t + 1);
+        // tile t has landed (with STAGES - 1 tiles in flight, tile t + 1's loads may be pending)
+        if (STAGES == 3 && t + 1 < te) wait_barrier<2 * ROUNDS>();
+        else wait_barrier<0>();
+        if (t + STAGES - 1 < te) issue(t + STAGES - 1);
         // this pair's keys see no row of the tile: compute nothing, still meet every barrier
         const bool active = kw0 < Lk && !(MASKED && ((int64_t)kw0 > (int64_t)q0 + BQ - 1 + shift + a.wr ||
                                                       (int64_t)kw0 + 31 < (int64_t)q0 + shift - a.wl));
@@ -275,6 +276,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
     };
 
     if (tb < te) issue(tb);
+    if (STAGES == 3 && tb + 1 < te) issue(tb + 1);
     int t = tb;
     for (; t < ua; ++t) step(t, std::true_type{});
     for (; t < ub; ++t) step(t, std::false_type{});
@@ -299,14 +301,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ dQ (runs first)
 
-template <int HD, int NW>
+template <int HD, int NW, int STAGES>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
     constexpr int NT = NW * 64;
     constexpr int BM = NW * 32;               // query rows per workgroup
     constexpr int ROWB = HD * 2;
     constexpr int CPR = HD / 8;
     constexpr int TILE_BYTES = BN * ROWB;     // one K or V tile
-    constexpr int STAGES = 2;
     constexpr int ROUNDS = TILE_BYTES / 16 / NT;
     constexpr int KS = HD / 16, MB = HD / 32;
     static_assert(ROUNDS >= 1 && ROUNDS * NT * 16 == TILE_BYTES, "tile split");
@@ -428,8 +429,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
     auto step = [&](int t, auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int kt0 = t * BN;
-        wait_barrier<0>();
-        if (t + 1 < te) issue(t + 1);
+        if (STAGES == 3 && t + 1 < te) wait_barrier<2 * ROUNDS>();
+        else wait_barrier<0>();
+        if (t + STAGES - 1 < te) issue(t + STAGES - 1);
         if (MASKED && ((int64_t)kt0 + BN - 1 < (int64_t)wrow0 + shift - a.wl ||
                        (int64_t)kt0 > (int64_t)wrow0 + 31 + shift + a.wr))
             return;
@@ -474,6 +476,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
     };
 
     if (tb < te) issue(tb);
+    if (STAGES == 3 && tb + 1 < te) issue(tb + 1);
     int t = tb;
     for (; t < ua; ++t) step(t, std::true_type{});
     for (; t < ub; ++t) step(t, std::false_type{});
@@ -498,12 +501,20 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
 template <int HD>
 hipError_t launch_hd(const BwdArgs &a, hipStream_t stream) {
     constexpr int NW_Q = 8;
+    // LDS ring depth of the two kernels: 2 (one tile in flight while one is used); a third
+    // stage was measured no faster for either and costs registers
+#ifndef BWD_STAGES_Q
+#define BWD_STAGES_Q 2
+#endif
+#ifndef BWD_STAGES_KV
+#define BWD_STAGES_KV 2
+#endif
     const int64_t gq = (int64_t)((a.max_seqlen_q + NW_Q * 32 - 1) / (NW_Q * 32)) * a.nseq * a.B * a.Htot;
     const int64_t gkv = (int64_t)((a.max_seqlen_k + 127) / 128) * a.nseq * a.B * a.Htot;
     if (gq > 0x7fffffff || gkv > 0x7fffffff) return hipErrorInvalidConfiguration;
     // the dQ launch writes the per-row D and L that the dK/dV launch reads
-    if (gq > 0) hipLaunchKernelGGL((bwd_dq_kernel<HD, NW_Q>), dim3((unsigned)gq), dim3(NW_Q * 64), 0, stream, a);
-    if (gkv > 0) hipLaunchKernelGGL((bwd_dkdv_pair_kernel<HD>), dim3((unsigned)gkv), dim3(512), 0, stream, a);
+    if (gq > 0) hipLaunchKernelGGL((bwd_dq_kernel<HD, NW_Q, BWD_STAGES_Q>), dim3((unsigned)gq), dim3(NW_Q * 64), 0, stream, a);
+    if (gkv > 0) hipLaunchKernelGGL((bwd_dkdv_pair_kernel<HD, BWD_STAGES_KV>), dim3((unsigned)gkv), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
