@@ -187,10 +187,11 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H_total, int64_t Mq);
  * q, k, v (no dropout, no bias gradient).  With P_ij = exp(scale q_i.k_j - lse_i) on the
  * visible keys: dv_j = sum_i P_ij dout_i; dS_ij = P_ij (dout_i.v_j - dout_i.out_i);
  * dq_i = scale sum_j dS_ij k_j; dk_j = scale sum_i dS_ij q_i.
- *   dout, out [B, Mq, (G,) H, D]; q [B, Mq, (G,) H, D]; k, v [B, Mkv, (G,) H, D]; bf16,
- *     D in {64, 128}; lse fp32 [B, H_total, Mq] as attn_fwd wrote it.
+ *   q [B, Mq, (G,) H, K]; k [B, Mkv, (G,) H, K]; v [B, Mkv, (G,) H, Kv];
+ *     dout, out [B, Mq, (G,) H, Kv]; one dtype: bf16 with K == Kv in {64, 128} (matrix
+ *     cores) or fp32 with K, Kv <= 128; lse fp32 [B, H_total, Mq] as attn_fwd wrote it.
  *   mask, varlen, scale: exactly those of the forward call.
- *   dq, dk, dv: shapes of q, k, v, bf16, any strides that do not make two elements
+ *   dq, dk, dv: shapes of q, k, v, q's dtype, any strides that do not make two elements
  *     share memory (a stride-0 expanded head axis is rejected: for expanded GQA keys
  *     pass dk/dv of the expanded shape and sum over each group's heads).
  *   workspace: device, 256-byte aligned, >= attn_bwd_workspace_bytes(B, H_total, Mq).

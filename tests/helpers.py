@@ -21,6 +21,8 @@ TOL_F32 = 1e-5        # max error of every output of the fp32 path
 # (which enters D = dout.out) each add relative errors of ~2^-9 of the largest terms
 TOL_BWD_REL = 1e-2    # max |grad - oracle| <= TOL_BWD_REL * max|oracle| + TOL_BWD_ABS
 TOL_BWD_ABS = 2e-3
+# fp32 gradients: fp32 throughout, so the sums' rounding only (bounded by the largest terms)
+TOL_BWD_F32 = 1e-5    # max |grad - oracle| <= TOL_BWD_F32 * (1 + max|oracle|)
 
 
 def say(msg: str) -> None:

@@ -279,9 +279,10 @@ def test_bwd_workspace_and_rejects():
     assert call(lse=0) == A.ATTN_ERR_INVALID_ARGUMENT and "lse" in A.attn_last_error()
     assert call(mask=None) == A.ATTN_ERR_INVALID_ARGUMENT
     assert call(q=t(dt=A.ATTN_DTYPE_F32)) == A.ATTN_ERR_INVALID_ARGUMENT and "dtype" in A.attn_last_error()
-    f32 = t(dt=A.ATTN_DTYPE_F32)
+    f32 = t((B, M, H, 160), dt=A.ATTN_DTYPE_F32)  # fp32 head dims above 128 are not built
     assert call(f32, f32, f32, f32, f32, f32, f32, f32) == A.ATTN_ERR_UNSUPPORTED
     assert call(dq=t((B, M + 1, H, D))) == A.ATTN_ERR_INVALID_ARGUMENT and "q's shape" in A.attn_last_error()
+    assert call(g=t((B, M, H, 64))) == A.ATTN_ERR_INVALID_ARGUMENT and "dout" in A.attn_last_error()
     assert call(dv=t((B, M, H, 64))) == A.ATTN_ERR_INVALID_ARGUMENT
     expanded = t(stride=[M * H * D, H * D, 0, 1])
     assert call(dk=expanded) == A.ATTN_ERR_INVALID_ARGUMENT and "stride-0" in A.attn_last_error()

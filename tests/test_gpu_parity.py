@@ -757,3 +757,52 @@ def test_int4_decode_full_size(A):
         assert not torch.isnan(out).any()
         del k, v
         torch.cuda.empty_cache()
+
+
+from tests.helpers import TOL_BWD_F32  # noqa: E402
+
+
+@pytest.mark.parametrize("mask,win,winr,Mq,Mkv,K,Kv", [
+    (0, None, None, 70, 90, 64, 64), (1, None, None, 130, 130, 128, 128), (4, None, None, 100, 45, 64, 96),
+    (6, 20, 9, 80, 110, 32, 128), (7, 33, None, 150, 150, 100, 64)])
+def test_bwd_fp32(A, mask, win, winr, Mq, Mkv, K, Kv):
+    say(f"case: bwd fp32 mask={mask} Mq={Mq} Mkv={Mkv} K={K} Kv={Kv}")
+    B, H = 2, 3
+    qh, kh, vh = synth.qkv(990 + mask, (B, Mq, H, K), (B, Mkv, H, K), (B, Mkv, H, Kv), "f32")
+    gh = synth.normal(991 + mask, 3, (B, Mq, H, Kv), "f32")
+    q, k, v, g = dev(qh, "f32"), dev(kh, "f32"), dev(vh, "f32"), dev(gh, "f32")
+    wkw = {}
+    if mask == 6:
+        wkw = dict(window_left=win, window_right=winr)
+    elif mask == 7:
+        wkw = dict(window_size=win)
+    out, lse = A.attn_fwd(q, k, v, mask=mask, scale=0.11, **wkw)
+    dq, dk, dv = A.attn_bwd(g, q, k, v, out, lse, mask=mask, scale=0.11, **wkw)
+    torch.cuda.synchronize()
+    okw = dict(mask=mask, scale=0.11, window=win, window_right=winr)
+    oo, ol = oracle.attention(qh, kh, vh, **okw)
+    ref = oracle.attention_backward(gh, oo, ol, qh, kh, vh, **okw)
+    for name, gg, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        err, mag = maxerr(host64(gg), r), float(np.abs(r).max())
+        say(f"  {name}: max|d|={err:.3e} max|ref|={mag:.3e}")
+        assert err <= TOL_BWD_F32 * (1 + mag), f"{name}: error {err}"
+
+
+def test_bwd_fp32_packed(A):
+    sq = np.array([0, 40, 41, 100], dtype=np.int32)
+    sk = np.array([0, 30, 70, 120], dtype=np.int32)
+    H, K = 2, 64
+    say("case: bwd fp32 packed block-diagonal causal bottom-right")
+    qh, kh, vh = synth.qkv(995, (1, 100, H, K), (1, 120, H, K), (1, 120, H, K), "f32")
+    gh = synth.normal(996, 3, (1, 100, H, K), "f32")
+    q, k, v, g = dev(qh, "f32"), dev(kh, "f32"), dev(vh, "f32"), dev(gh, "f32")
+    kw = dict(seqstart_q=torch.from_numpy(sq).cuda(), seqstart_k=torch.from_numpy(sk).cuda(), max_seqlen_q=59)
+    out, lse = A.attn_fwd(q, k, v, mask=5, **kw)
+    dq, dk, dv = A.attn_bwd(g, q, k, v, out, lse, mask=5, max_seqlen_k=50, **kw)
+    torch.cuda.synchronize()
+    oo, ol = oracle.attention(qh, kh, vh, mask=5, seqstart_q=sq, seqstart_k=sk)
+    ref = oracle.attention_backward(gh, oo, ol, qh, kh, vh, mask=5, seqstart_q=sq, seqstart_k=sk)
+    for name, gg, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        err, mag = maxerr(host64(gg), r), float(np.abs(r).max())
+        say(f"  {name}: max|d|={err:.3e} max|ref|={mag:.3e}")
+        assert err <= TOL_BWD_F32 * (1 + mag), f"{name}: error {err}"

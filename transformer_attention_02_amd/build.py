@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libattn.so")
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "merge.hip", "bwd_bf16.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "merge.hip", "bwd_bf16.hip", "bwd_f32.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 

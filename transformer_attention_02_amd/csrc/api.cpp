@@ -361,10 +361,12 @@ attn_status attn_bwd(const attn_tensor *dot, const attn_tensor *qt, const attn_t
     for (const View *x : {&g, &k, &v, &o, &dq, &dk, &dv})
         if (!same_heads(*x, q)) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: rank and head axes must match q's", fn);
     auto same_shape = [](const View &a_, const View &b_) { return a_.B == b_.B && a_.M == b_.M && a_.D == b_.D; };
-    if (!same_shape(g, q) || !same_shape(o, q) || !same_shape(dq, q))
-        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: dout, out and dq must have q's shape", fn);
-    if (!same_shape(dk, k) || !same_shape(v, k) || !same_shape(dv, k))
-        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: v, dk and dv must have k's shape", fn);
+    if (!same_shape(dq, q)) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: dq must have q's shape", fn);
+    if (!same_shape(dk, k)) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: dk must have k's shape", fn);
+    if (!same_shape(dv, v)) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: dv must have v's shape", fn);
+    if (g.B != q.B || g.M != q.M || o.B != q.B || o.M != q.M || g.D != v.D || o.D != v.D)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: dout and out must be [B, Mq, ..., Kv]", fn);
+    if (v.B != k.B || v.M != k.M) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: k and v have different key counts", fn);
     if (k.B != q.B) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: batch sizes differ", fn);
     if (k.D != q.D) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q and k head dims differ", fn);
     // gradients are written once per element: no axis of extent > 1 may have stride 0
@@ -375,14 +377,19 @@ attn_status attn_bwd(const attn_tensor *dot, const attn_tensor *qt, const attn_t
             if (ext[i] > 1 && str[i] == 0)
                 return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: gradient tensors must not have stride-0 axes", fn);
     }
-    if (q.dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED, "%s: the backward is built for bf16", fn);
-    if (!(q.D == 64 || q.D == 128)) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim must be 64 or 128", fn);
-    // tiles of q/dout (key-side kernel) and k/v (query-side kernel) go through buffer descriptors
-    for (const View *x : {&q, &g, &k, &v}) {
-        if (x->M > 1 && x->s.m < x->D)
-            return fail(ATTN_ERR_UNSUPPORTED, "%s: row strides must be >= the head dim", fn);
-        if (x->s.m * 2 * 64 + x->D * 2 >= (int64_t)1 << 31)
-            return fail(ATTN_ERR_UNSUPPORTED, "%s: row stride too large for 32-bit tile offsets", fn);
+    if (q.D < 1 || v.D < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: head dims must be >= 1", fn);
+    if (q.dtype == ATTN_DTYPE_BF16) {
+        if (!((q.D == 64 || q.D == 128) && v.D == q.D))
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: the bf16 backward needs K == Kv in {64, 128}", fn);
+        // tiles of q/dout (key-side kernel) and k/v (query-side kernel) go through buffer descriptors
+        for (const View *x : {&q, &g, &k, &v}) {
+            if (x->M > 1 && x->s.m < x->D)
+                return fail(ATTN_ERR_UNSUPPORTED, "%s: row strides must be >= the head dim", fn);
+            if (x->s.m * 2 * 64 + x->D * 2 >= (int64_t)1 << 31)
+                return fail(ATTN_ERR_UNSUPPORTED, "%s: row stride too large for 32-bit tile offsets", fn);
+        }
+    } else if (q.D > 128 || v.D > 128) {
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: the fp32 backward needs K, Kv <= 128", fn);
     }
     MaskSpec ms;
     if ((st = mask_spec(fn, *mask, &ms)) != ATTN_OK) return st;
@@ -436,6 +443,7 @@ attn_status attn_bwd(const attn_tensor *dot, const attn_tensor *qt, const attn_t
     a.Htot = (int)htot(q);
     a.Hin = (int)q.H;
     a.D = (int)q.D;
+    a.Dv = (int)v.D;
     const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)q.D) : (double)scale;
     a.scale = (float)sc;
     a.scale_log2 = (float)(sc * 1.4426950408889634);
@@ -455,7 +463,9 @@ attn_status attn_bwd(const attn_tensor *dot, const attn_tensor *qt, const attn_t
         a.max_seqlen_q = a.Mq;
         a.max_seqlen_k = a.Mkv;
     }
-    return launch_status(attn::launch_bwd_bf16(a, (hipStream_t)stream), fn);
+    return launch_status(q.dtype == ATTN_DTYPE_BF16 ? attn::launch_bwd_bf16(a, (hipStream_t)stream)
+                                                    : attn::launch_bwd_f32(a, (hipStream_t)stream),
+                         fn);
 }
 
 size_t attn_decode_workspace_bytes(int64_t B, int64_t H_total, int64_t Kv, int32_t num_splits) {

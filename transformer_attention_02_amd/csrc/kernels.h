@@ -90,7 +90,7 @@ struct BwdArgs {
     Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
     const float *lse;     // [B, Htot, Mq], natural log
     float *ws_d, *ws_l2;  // [B, Htot, Mq] each: dout.out per row, and lse * log2(e) (+inf for empty rows)
-    int B, Mq, Mkv, Htot, Hin, D;
+    int B, Mq, Mkv, Htot, Hin, D, Dv;  // D: q/k head dim, Dv: v/out head dim
     float scale, scale_log2;
     int packed, bottom_right, wl, wr;
     const int32_t *seqstart_q, *seqstart_k;
@@ -98,6 +98,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdArgs &a, hipStream_t stream);
 
 hipError_t launch_decode_partials(const DecodeArgs &a, int elem, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
