@@ -806,3 +806,48 @@ def test_bwd_fp32_packed(A):
         err, mag = maxerr(host64(gg), r), float(np.abs(r).max())
         say(f"  {name}: max|d|={err:.3e} max|ref|={mag:.3e}")
         assert err <= TOL_BWD_F32 * (1 + mag), f"{name}: error {err}"
+
+
+# ------------------------------------------------------------------ the largest supported sizes
+
+def test_long_sequence_causal_sampled_rows(A):
+    """One 32768-token causal sequence (B=1, H=2, K=128): windows of 64 rows at the start, the
+    middle and the end, each checked as a bottom-right causal problem over keys 0..i1-1."""
+    M, H, D = 32768, 2, 128
+    say(f"case: causal prefill M={M}")
+    qh, kh, vh = synth.qkv(1400, (1, M, H, D), (1, M, H, D), (1, M, H, D))
+    out, lse = A.attn_fwd(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), mask=1)
+    torch.cuda.synchronize()
+    for i0 in (0, 12345, M - 64):
+        i1 = i0 + 64
+        oo, ol = run_oracle(qh[:, i0:i1], kh[:, :i1], vh[:, :i1], oracle.MASK_CAUSAL_BR, "bf16")
+        check(out[:, i0:i1], lse[:, :, i0:i1], oo, ol, TOL_BF16_OUT, TOL_LSE, f"rows {i0}..{i1 - 1}")
+
+
+def test_decode_long_cache_max_splits(A):
+    """262144 keys per sequence and the largest split count (128 chunks of 2048 keys)."""
+    B, M, H, D, S = 2, 262144, 4, 128, 128
+    say(f"case: decode Mkv={M} S={S}")
+    qh, kh, vh = synth.qkv(1401, (B, 1, H, D), (B, M, H, D), (B, M, H, D))
+    out, lse = A.attn_decode_splitkv(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), S)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (1, 3)]:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        oo, ol = run_oracle(qh[sl], kh[sl], vh[sl], 0, "bf16")
+        check(out[sl], lse[b:b + 1, h:h + 1], oo, ol, TOL_BF16_OUT, TOL_LSE, f"b={b} h={h}")
+
+
+def test_merge_max_chunks(A):
+    """The largest merge (128 chunks), some chunks and rows empty, fp32 in and out."""
+    say("case: merge of 128 chunks")
+    rng = np.random.Generator(np.random.PCG64(1402))
+    S, B, M, H, D = 128, 1, 40, 4, 64
+    oc = rng.standard_normal((S, B, M, H, D)).astype(np.float32)
+    lc = (rng.standard_normal((S, B, H, M)) * 6).astype(np.float32)
+    lc[::7] = -np.inf
+    lc[:, 0, 1, 5] = -np.inf
+    mo, ml = oracle.merge(oc.astype(np.float64), lc.astype(np.float64))
+    out, lse = A.attn_merge(torch.from_numpy(oc).cuda(), torch.from_numpy(lc).cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check(out, lse, mo, ml, 1e-5, 1e-5, "merge S=128")
+    assert math.isinf(lse[0, 1, 5].item()) and torch.all(out[0, 5, 1] == 0)
