@@ -109,6 +109,27 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def provenance(torch):
+    """Seeds of every workload, library versions and the host and device the run used."""
+    import platform
+
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    return {"seeds": {"causal prefill and backward": 2, "backward dout": "2 (tag 3)", "partial+merge": 3,
+                      "decode caches (bf16, FP8, INT4)": 4, "paged decode block table": 7, "packed GQA": 5,
+                      "sliding window": 6, "fp32 tiny": 1},
+            "numpy": np.__version__, "torch": torch.__version__, "python": platform.python_version(),
+            "host_cores": cores, "host_cpu": cpu, "gpu": torch.cuda.get_device_name(0)}
+
+
 def timed(fn, steps, warmup, torch, min_warmup_s=0.25):
     """Average ms per call over `steps` calls after `warmup` calls and at least `min_warmup_s`
     seconds of warm-up (the clocks settle after idle host-side set-up), HIP events on the
@@ -162,6 +183,7 @@ def main():
         "config": {"workload": "causal bf16 attention forward B=2 M=2048 H=32 K=Kv=128 (attn_fwd, top-left causal)",
                    "batch": 2, "seq_len": 2048, "heads": 32, "head_dim": 128, "mask": "causal"},
         "rows": {},
+        "provenance": provenance(torch),
     }
 
     # ------------------------------------------------------------ headline: causal prefill
@@ -406,9 +428,13 @@ def main():
         l1 = torch.empty((1, 2, 128), dtype=torch.float32, device="cuda")
         ms_1 = timed(A.prepare_fwd(q1, k1, v1, o1, l1, scale=0.125), 100, 5, torch)
         fl1 = 4.0 * 2 * 128 * 128 * 64
+        tf1 = fl1 / (ms_1 * 1e-3) / 1e12
         result["rows"]["fp32_tiny"] = {"workload": "fp32 B=1 M=128 H=2 K=Kv=64, no mask", "ms_per_call": round(ms_1, 5),
-                                       "value": round(fl1 / (ms_1 * 1e-3) / 1e12, 4), "unit": "TFLOP/s",
-                                       "note": "latency-bound"}
+                                       "value": round(tf1, 4), "unit": "TFLOP/s",
+                                       "roofline": {"bound": "latency", "achieved": round(tf1, 4),
+                                                    "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                                                    "frac": round(tf1 / PEAK_FP32_TFLOPS, 6),
+                                                    "note": "fp32 vector peak, for information: 4 workgroups"}}
         log(f"fp32 tiny: {ms_1 * 1e3:.1f} us/call")
 
     print(json.dumps(result), flush=True)
