@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--rocpd", metavar="DB", help="summarise a rocprofv3 results database (kernel durations and "
                    "counters per kernel and grid) instead of running; no GPU needed")
+    p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                   help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE rocprofv3 run of "
+                        "'bench.py --rows decode,copy --no-cpu --steps 3 --warmup 1'; no GPU needed")
     return p.parse_args()
 
 
@@ -105,6 +108,78 @@ def recorded_traffic(key):
     return rec["fetch_kib"] * rec["fetch_scale"] * 1024 + rec["write_kib"] * rec["write_scale"] * 1024
 
 
+# (record key, sources digested, kernel name, which value cluster of the dispatches when two workloads
+# launch the same kernel on the same grid: 0 the lower, 1 the higher, None all)
+TRAFFIC_KERNELS = (
+    ("fwd_bf16 causal 2x2048x32x128", "fwd", "fwd_bf16_kernel<128, 8, 3, false>", None),
+    ("decode bf16 16x32768x32x128 s64", "decode", "decode_kernel<128, 0, 0>", None),
+    ("decode bf16 paged 16x32768x32x128 page64 s64", "decode", "decode_kernel<128, 0, 2>", None),
+    ("decode fp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 2, 0>", None),
+    ("decode int4 g1 16x32768x32x128 s64", "decode", "decode_kernel<128, 3, 0>", 0),
+    ("decode int4 g4 16x32768x32x128 s64", "decode", "decode_kernel<128, 3, 0>", 1),
+)
+COPY_KERNEL, COPY_KIB = "__amd_rocclr_copyBuffer", 1 << 20  # the 1 GiB copy row reads and writes 1 GiB
+
+
+def _counter_values(db_path, counter):
+    import collections
+    import sqlite3
+
+    g = collections.defaultdict(list)
+    cur = sqlite3.connect(db_path).cursor()
+    for name, cn, val in cur.execute("select kernel_name, counter_name, value from counters_collection"):
+        if cn == counter:
+            g[name].append(val)
+    return g
+
+
+def _cluster_mean(vals, which):
+    """Mean of all values, or of the lower/higher side of the widest gap between sorted values."""
+    v = sorted(vals)
+    if which is None or len(v) < 2:
+        return sum(v) / len(v)
+    cut = max(range(1, len(v)), key=lambda i: v[i] - v[i - 1])
+    if v[cut] - v[cut - 1] < 0.01 * v[-1]:  # one cluster: both workloads read the same bytes
+        return sum(v) / len(v)
+    side = v[:cut] if which == 0 else v[cut:]
+    return sum(side) / len(side)
+
+
+def write_traffic(fetch_db, write_db):
+    fetch, write = _counter_values(fetch_db, "FETCH_SIZE"), _counter_values(write_db, "WRITE_SIZE")
+
+    def find(g, needle):
+        hits = [k for k in g if needle in k]
+        if len(hits) != 1:
+            raise SystemExit(f"{needle}: {len(hits)} kernels match in the counter database")
+        return g[hits[0]]
+
+    def copy_mean(vals):  # the 1 GiB copies are the largest copyBuffer dispatches
+        big = [v for v in vals if v >= 0.99 * max(vals)]
+        return sum(big) / len(big)
+
+    copy_f, copy_w = copy_mean(find(fetch, COPY_KERNEL)), copy_mean(find(write, COPY_KERNEL))
+    cal = (f"{COPY_KERNEL} of 1 GiB (bench.py --rows copy): FETCH_SIZE {copy_f:.1f} KiB, "
+           f"WRITE_SIZE {copy_w:.1f} KiB per dispatch")
+    cmd = "python bench.py --rows decode,copy --no-cpu --steps 3 --warmup 1"
+    out = {}
+    for key, src, kname, which in TRAFFIC_KERNELS:
+        out[key] = {"kernel": kname, "sources": src, "source_sha256": kernel_source_digest(src),
+                    "fetch_kib": round(_cluster_mean(find(fetch, kname), which), 1),
+                    "fetch_scale": round(COPY_KIB / copy_f, 5),
+                    "write_kib": round(_cluster_mean(find(write, kname), which), 1),
+                    "write_scale": round(COPY_KIB / copy_w, 5), "calibration": cal,
+                    "commands": [f"rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -- {cmd}",
+                                 f"rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -- {cmd}",
+                                 f"python bench.py --traffic {fetch_db} {write_db}"]}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    for key, rec in out.items():
+        print(f"{key}: fetch {rec['fetch_kib'] * rec['fetch_scale'] / 1024:.1f} MiB, "
+              f"write {rec['write_kib'] * rec['write_scale'] / 1024:.1f} MiB per launch")
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -127,7 +202,9 @@ def provenance(torch):
                       "decode caches (bf16, FP8, INT4)": 4, "paged decode block table": 7, "packed GQA": 5,
                       "sliding window": 6, "fp32 tiny": 1},
             "numpy": np.__version__, "torch": torch.__version__, "python": platform.python_version(),
-            "host_cores": cores, "host_cpu": cpu, "gpu": torch.cuda.get_device_name(0)}
+            "host_cores": cores, "host_cpu": cpu, "gpu": f"{torch.cuda.get_device_name(0) or 'unnamed'} "
+                   f"({torch.cuda.get_device_properties(0).gcnArchName}, "
+                   f"{torch.cuda.get_device_properties(0).multi_processor_count} CUs)"}
 
 
 def timed(fn, steps, warmup, torch, min_warmup_s=0.25):
@@ -156,9 +233,12 @@ def main():
     if args.rocpd:
         rocpd_summary(args.rocpd)
         return
+    if args.traffic:
+        write_traffic(*args.traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; bench.py --gpus N with N > 1 is not supported"}))
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus N with N > 1 is not supported"}))
         sys.exit(2)
 
     import torch
@@ -209,13 +289,17 @@ def main():
         import oracle
 
         q64, k64, v64 = (synth.to_f64(x, "bf16") for x in (qh, kh, vh))
-        t0 = time.perf_counter()
-        oracle.attention(q64, k64, v64, mask=oracle.MASK_CAUSAL)
-        dt = time.perf_counter() - t0
+        # whole passes over the workload until about 10 s of CPU work have run
+        passes, t0 = 0, time.perf_counter()
+        while passes == 0 or time.perf_counter() - t0 < 10.0:
+            oracle.attention(q64, k64, v64, mask=oracle.MASK_CAUSAL)
+            passes += 1
+        dt = (time.perf_counter() - t0) / passes
         result["cpu_baseline"] = {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.threads(),
-                                  "kind": "oracle", "seconds": round(dt, 3),
-                                  "sample": "the whole causal [2,2048,32,128] workload (all 64 heads), fp64"}
-        log(f"cpu oracle: {dt:.2f} s on {oracle.threads()} threads")
+                                  "kind": "oracle", "seconds_per_pass": round(dt, 3), "passes": passes,
+                                  "sample": f"{passes} passes over the whole causal [2,2048,32,128] workload "
+                                            "(all 64 heads), fp64"}
+        log(f"cpu oracle: {dt:.2f} s per pass, {passes} passes on {oracle.threads()} threads")
         del q64, k64, v64
     del q, k, v, out, lse
 
@@ -348,7 +432,7 @@ def main():
         tf_b = fl_b / (ms_b * 1e-3) / 1e12
         log(f"backward causal bf16 [2,2048,32,128]: {ms_b * 1e3:.1f} us/call, {tf_b:.1f} TFLOP/s")
         result["rows"]["bwd_causal"] = {
-            "workload": "attn_bwd of the causal bf16 prefill B=2 M=2048 H=32 K=Kv=128 (prep + dK/dV + dQ kernels)",
+            "workload": "attn_bwd of the causal bf16 prefill B=2 M=2048 H=32 K=Kv=128 (dQ kernel, then the dK/dV kernel)",
             "ms_per_call": round(ms_b, 5), "value": round(tf_b, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_b,
