@@ -207,6 +207,22 @@ def provenance(torch):
                    f"{torch.cuda.get_device_properties(0).multi_processor_count} CUs)"}
 
 
+def oracle_mod():
+    import oracle
+
+    return oracle
+
+
+def oracle_timing(fn, work, unit, sample):
+    """One timed pass of the CPU oracle over a sample; ``work`` is the sample's size in ``unit`` x seconds."""
+    t0 = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t0
+    log(f"cpu oracle ({sample}): {dt:.2f} s")
+    return {"value": round(work / dt, 5), "unit": unit, "seconds": round(dt, 3), "cores": oracle_mod().threads(),
+            "kind": "oracle", "sample": sample}
+
+
 def timed(fn, steps, warmup, torch, min_warmup_s=0.25):
     """Average ms per call over `steps` calls after `warmup` calls and at least `min_warmup_s`
     seconds of warm-up (the clocks settle after idle host-side set-up), HIP events on the
@@ -307,9 +323,10 @@ def main():
     if "decode" in rows:
         B, Mkv, H, D, S = 16, 32768, 32, 128, 64
         log("generating decode inputs ...")
-        qd = up(synth.normal(4, synth.TAG_Q, (B, 1, H, D), "bf16"))
-        kd = up(synth.normal(4, synth.TAG_K, (B, Mkv, H, D), "bf16"))
-        vd = up(synth.normal(4, synth.TAG_V, (B, Mkv, H, D), "bf16"))
+        qdh = synth.normal(4, synth.TAG_Q, (B, 1, H, D), "bf16")
+        kdh = synth.normal(4, synth.TAG_K, (B, Mkv, H, D), "bf16")
+        vdh = synth.normal(4, synth.TAG_V, (B, Mkv, H, D), "bf16")
+        qd, kd, vd = up(qdh), up(kdh), up(vdh)
         ws = torch.empty(A.attn_decode_workspace_bytes(B, H, D, S), dtype=torch.uint8, device="cuda")
         od = torch.empty_like(qd)
         ld = torch.empty((B, H, 1), dtype=torch.float32, device="cuda")
@@ -324,6 +341,13 @@ def main():
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_call": kv_bytes,
                          "traffic": recorded_traffic("decode bf16 16x32768x32x128 s64"),
                          "note": "algorithmic bytes = K+V once; time covers both launches"}}
+        if not args.no_cpu:  # the oracle on batch element 0 of 16 (one sequence's 32768 keys, all 32 heads)
+            sample = [synth.to_f64(x[:1], "bf16") for x in (qdh, kdh, vdh)]
+            result["rows"]["decode_splitkv"]["cpu_oracle"] = oracle_timing(
+                lambda: oracle_mod().attention(*sample), kv_bytes / B / 1e9, "GB/s",
+                "batch element 0 of 16 (32768 keys x 32 heads), fp64 exact attention; GB/s of its bf16 K+V")
+            del sample
+        del qdh, kdh, vdh
         # the same cache as 8192 pages of 64 rows in a random order (PagedBlockDiagonalPaddedKeysMask form)
         page = 64
         perm = np.random.Generator(np.random.PCG64(7)).permutation(B * Mkv // page).astype(np.int32)
@@ -414,6 +438,14 @@ def main():
             "ms_per_call": round(ms_v, 5), "value": round(tf, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl}}
+        if not args.no_cpu:  # the whole packed workload, k and v broadcast over the 4 heads of a group
+            qo = synth.to_f64(synth.normal(5, synth.TAG_Q, (1, M, 8, 4, 128), "bf16"), "bf16").reshape(1, M, 32, 128)
+            ko, vo = (np.broadcast_to(synth.to_f64(synth.normal(5, tag, (1, M, 8, 1, 128), "bf16"), "bf16"),
+                                      (1, M, 8, 4, 128)).reshape(1, M, 32, 128) for tag in (synth.TAG_K, synth.TAG_V))
+            result["rows"]["varlen_gqa_causal"]["cpu_oracle"] = oracle_timing(
+                lambda: oracle_mod().attention(qo, ko, vo, mask=oracle_mod().MASK_BLOCKDIAG_CAUSAL, seqstart_q=ss),
+                fl / 1e12, "TFLOP/s", "the whole packed workload, fp64")
+            del qo, ko, vo
         del qv, kv, vv, ov, lv
 
     # ------------------------------------------------------------ backward of the causal prefill
