@@ -719,6 +719,37 @@ def test_int4_decode_padded_lanes_5d_gqa(A):
         check(out[b:b + 1].reshape(1, 1, G5 * Hg, D), lse[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"lane {b} len={lens[b]}")
 
 
+@pytest.mark.parametrize("kind", ["bf16", "int4"])
+def test_decode_permuted_head_order(A, kind):
+    """5-D [B, M, G, H, D] caches viewed out of [B, M, H, G, D] memory (G inner to H): inside a
+    workgroup's neighbouring heads the offsets fall back, so the kernel takes its general
+    (64-bit per-lane) address path instead of the uniform-row one."""
+    B, M, G5, Hg, D, S, G = 2, 1000, 2, 3, 128, 7, 2
+    say(f"case: decode {kind} permuted head order B={B} M={M} G={G5} H={Hg}")
+    qh = synth.normal(1400, synth.TAG_Q, (B, 1, G5, Hg, D), "bf16")
+    qf = qh.reshape(B, 1, G5 * Hg, D)
+    perm = lambda t: t.permute(0, 1, 3, 2, 4)  # [B, M, H, G, x] memory -> [B, M, G, H, x] view
+    flat = lambda x: np.ascontiguousarray(np.swapaxes(x, 2, 3)).reshape((B, M, G5 * Hg) + x.shape[4:])
+    if kind == "bf16":
+        kh = synth.normal(1400, synth.TAG_K, (B, M, Hg, G5, D), "bf16")
+        vh = synth.normal(1400, synth.TAG_V, (B, M, Hg, G5, D), "bf16")
+        out, lse = A.attn_decode_splitkv(dev(qh, "bf16"), perm(dev(kh, "bf16")), perm(dev(vh, "bf16")), S,
+                                         scale=0.09)
+        torch.cuda.synchronize()
+        oo, ol = run_oracle(qf, flat(kh), flat(vh), 0, "bf16", scale=0.09)
+        check(out.reshape(B, 1, G5 * Hg, D), lse, oo, ol, TOL_BF16_OUT, TOL_LSE, "permuted bf16")
+    else:
+        kc, vc, kss, vss = _int4_cache(1401, (B, M, Hg, G5, D), G)
+        ks = _f16(kss.reshape(B, M, Hg, G5, 2 * G))
+        vs = _f16(vss.reshape(B, M, Hg, G5, 2 * G))
+        out, lse = A.attn_decode_splitkv_int4(dev(qh, "bf16"), perm(_u8(kc)), perm(_u8(vc)), perm(ks), perm(vs), S,
+                                              scale=0.09, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        fss = lambda x: np.ascontiguousarray(np.swapaxes(x, 2, 3)).reshape(B, M, G5 * Hg, G, 2)
+        oo, ol = _int4_oracle(qf, flat(kc), flat(vc), fss(kss), fss(vss), scale=0.09)
+        check(out.reshape(B, 1, G5 * Hg, D), lse, oo, ol, TOL_F32, TOL_F32, "permuted int4")
+
+
 @pytest.mark.parametrize("page", [16, 64])
 def test_int4_decode_paged(A, page):
     B, H, D, S, P, maxb, G = 3, 4, 128, 5, 100, 20, 4

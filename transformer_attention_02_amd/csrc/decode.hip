@@ -23,11 +23,14 @@
 //     resolved once into LDS from the block table;
 //   * quantised caches: row-wise FP8 ("Attention - operator protocol", InputsFp8) and
 //     row/group-wise INT4 (triton_splitk.FwOp).  A lane takes 16 E4M3 codes (hardware
-//     conversion) or 32 4-bit codes (byte conversions) per 16-byte load, all inside one
-//     (scale, shift) group; the group's pair is applied to the lane's partial dot product
-//     before the reduction over the row's lanes, since q.(c*scale + shift) =
-//     scale*(q.c) + shift*sum(q), and on the V side the weight p*scale multiplies the
-//     codes while p*shift is summed once per row and lane.
+//     conversion) or 32 4-bit codes per 16-byte load, all inside one (scale, shift) group;
+//     the group's pair is applied to the lane's partial dot product before the reduction
+//     over the row's lanes, since q.(c*scale + shift) = scale*(q.c) + shift*sum(q), and on
+//     the V side the weight p*scale multiplies the codes while p*shift is summed once per
+//     row and lane.  On the K side INT4 codes become the bf16 values 128 + 8 * code (a shift
+//     and one v_and_or_b32 per pair) and feed v_dot2_f32_bf16 against q's bf16 pairs (exact
+//     products, fp32 sums); 128 * sum(q) is taken off afterwards.  The V side converts the
+//     codes exactly and accumulates in fp32.
 // Output: the chunk's normalised fp32 output and its natural-log LSE; an empty
 // chunk gives 0 and -inf.
 #include <type_traits>
@@ -40,20 +43,16 @@ namespace {
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int NT = 256;
 constexpr int SUB = 2048;  // keys per sub-chunk of a paged cache (their rows are resolved into LDS)
-// Tuning (measured on the [16, 32768, 32, 128] decode): 8 key rows per lane in flight, no
-// software pipelining of rounds, 512 contiguous bytes per cache row and workgroup.
+// Tuning (measured on the [16, 32768, 32, 128] decode): 8 key rows per lane in flight (4 for
+// INT4), no software pipelining of rounds, 512 contiguous bytes per cache row and workgroup.
 #ifndef DECODE_UNROLL
 #define DECODE_UNROLL 8
 #endif
 #ifndef DECODE_UNROLL_INT4
 #define DECODE_UNROLL_INT4 4
 #endif
-#ifndef DECODE_PIPE
-#define DECODE_PIPE 0
-#endif
 constexpr int U_DEF = DECODE_UNROLL;       // key rows per lane and round
 constexpr int U_INT4 = DECODE_UNROLL_INT4;  // the same for INT4 caches (32 codes per lane and row)
-constexpr bool PIPE = DECODE_PIPE != 0;     // issue round i+1 before using round i
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -85,17 +84,41 @@ __device__ __forceinline__ void unpack_fp8(const u32x4 &w, float *x) {
     }
 }
 
-// 32 unsigned 4-bit codes (element 2i in the low nibble of byte i) to fp32; exact.
+// Sum over the LPK consecutive lanes of a lane group.
+template <int LPK>
+__device__ __forceinline__ float lane_group_sum(float x) {
+#pragma unroll
+    for (int o = LPK / 2; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// 32 unsigned 4-bit codes (element 2i in the low nibble of byte i) to fp32; exact.  The masked
+// words are hidden from the compiler so that each byte converts with one v_cvt_f32_ubyte{0..3}
+// instead of a field extract plus a conversion.
 __device__ __forceinline__ void unpack_int4(const u32x4 &w, float *x) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const unsigned lo = w[i] & 0x0f0f0f0fu, hi = (w[i] >> 4) & 0x0f0f0f0fu;
+        unsigned lo = w[i] & 0x0f0f0f0fu, hi = (w[i] >> 4) & 0x0f0f0f0fu;
+        asm("" : "+v"(lo), "+v"(hi));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             x[8 * i + 2 * j] = (float)((lo >> (8 * j)) & 0xffu);
             x[8 * i + 2 * j + 1] = (float)((hi >> (8 * j)) & 0xffu);
         }
     }
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x2 as_bf16x2(unsigned w) { return __builtin_bit_cast(bf16x2, w); }
+
+// Two 4-bit codes as the bf16 values 128 + 8 * code: the code fills mantissa bits 3..6 of 2^7
+// (0x4300), which keeps the offset only 2x the largest code term.  Shifting the word so that
+// nibble s sits at bits 3..6 and masking with 0x00780078 picks elements s and 4 + s of the
+// word's 8 (s = 0..3).  The two constants come in registers (m = 0x00780078, c = 0x43004300)
+// that the compiler cannot see through, so the mask and the or fuse into one v_and_or_b32.
+__device__ __forceinline__ unsigned int4_pair(unsigned w, int s, unsigned m, unsigned c) {
+    const unsigned x = s == 0 ? w << 3 : w >> (4 * s - 3);
+    return (x & m) | c;
 }
 
 template <int ELEM>
@@ -185,6 +208,23 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qsum += qv[e];
     }
+    // INT4 K side on v_dot2: q's bf16 pairs in the order int4_pair() yields the codes (elements
+    // 8i + s and 8i + 4 + s in pair 4i + s) and the sum of q (times 128, the codes' offset)
+    unsigned q2[INT4 ? 16 : 1];
+    float qraw = 0.f;
+    unsigned m4 = 0x00780078u, c43 = 0x43004300u;
+    asm("" : "+v"(m4), "+v"(c43));
+    if constexpr (INT4) {
+        const uint16_t *qh = (const uint16_t *)qp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const unsigned lo = qh[8 * i + s2], hi = qh[8 * i + 4 + s2];
+                q2[4 * i + s2] = lo | (hi << 16);
+                qraw += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
+            }
+    }
 
     // Online softmax state of this lane group (the same in its LPK lanes): base-2 running max,
     // sum of exponentials, p-weighted values (this lane's EPL columns) and, for the quantised
@@ -193,6 +233,33 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f, sh_acc = 0.f;
+
+    constexpr int NS = QUANT ? U : 1;
+    u32x4 wk[U], wv[U];
+    uint32_t sk[NS], sv[NS];
+    // lane32 path: uniform bases at head hf0 = hg * hpw, byte strides, 32-bit lane offsets
+    // (head part + 16-byte column slice + row slot); the launcher checks that they fit
+    const int hf0 = hg << lh;
+    const char *kbase = (const char *)a.k + (kb + head_offset(a.sk, hf0, a.Hin)) * (int64_t)sizeof(T);
+    const char *vbase = (const char *)a.v + (vb + head_offset(a.sv, hf0, a.Hin)) * (int64_t)sizeof(T);
+    const int64_t kstr = a.sk.m * (int64_t)sizeof(T), vstr = a.sv.m * (int64_t)sizeof(T);
+    const uint32_t klane = (uint32_t)((head_offset(a.sk, hf, a.Hin) - head_offset(a.sk, hf0, a.Hin) + cl * TPL) *
+                                      (int64_t)sizeof(T) + rs * kstr);
+    const uint32_t vlane = (uint32_t)((head_offset(a.sv, hf, a.Hin) - head_offset(a.sv, hf0, a.Hin) + cl * TPL) *
+                                      (int64_t)sizeof(T) + rs * vstr);
+    const char *ksbase = nullptr, *vsbase = nullptr;
+    int64_t ksstr = 0, vsstr = 0;
+    uint32_t kslane = 0, vslane = 0;
+    if constexpr (QUANT) {
+        const int gw = 2 * ((cl * EPL) / a.group);
+        const int64_t bk = MODE == 2 ? 0 : (int64_t)b * a.skss.b, bv = MODE == 2 ? 0 : (int64_t)b * a.svss.b;
+        ksbase = (const char *)a.kss + (bk + head_offset(a.skss, hf0, a.Hin)) * 2;
+        vsbase = (const char *)a.vss + (bv + head_offset(a.svss, hf0, a.Hin)) * 2;
+        ksstr = a.skss.m * 2;
+        vsstr = a.svss.m * 2;
+        kslane = (uint32_t)((head_offset(a.skss, hf, a.Hin) - head_offset(a.skss, hf0, a.Hin) + gw) * 2 + rs * ksstr);
+        vslane = (uint32_t)((head_offset(a.svss, hf, a.Hin) - head_offset(a.svss, hf0, a.Hin) + gw) * 2 + rs * vsstr);
+    }
 
     for (int sub0 = j0; sub0 < j1; sub0 += (MODE == 2 ? SUB : a.chunk)) {
         const int n = MODE == 2 ? min(SUB, j1 - sub0) : j1 - sub0;
@@ -206,49 +273,69 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
             }
             __syncthreads();
         }
-        // K and V rows of the same keys are read together, in rounds of R keys (U per lane);
-        // with PIPE the next round is issued before the current one is used.
-        auto load = [&](int p, u32x4 *wk, u32x4 *wv, uint32_t *sk, uint32_t *sv) __attribute__((always_inline)) {
+        // K and V rows of the same keys are read together, in rounds of R keys (U per lane),
+        // straight into the registers the round computes on.  A full round (every row < n) takes
+        // no per-lane checks; with `lane32` the row part of each address is uniform and the
+        // lane's part a 32-bit byte offset, so address arithmetic stays on the scalar unit.
+        auto load = [&](int p, auto full_tag) __attribute__((always_inline)) {
+            constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int r = p + u * RPP + rs;
-                const int64_t row = MODE == 2 ? (r < n ? rows_s[r] : 0) : sub0 + r;
-                wk[u] = r < n ? *(const u32x4 *)(kp + row * a.sk.m) : u32x4{0, 0, 0, 0};
-                wv[u] = r < n ? *(const u32x4 *)(vp + row * a.sv.m) : u32x4{0, 0, 0, 0};
-                if constexpr (QUANT) {
-                    sk[u] = r < n ? *(const uint32_t *)(kss + row * a.skss.m) : 0u;
-                    sv[u] = r < n ? *(const uint32_t *)(vss + row * a.svss.m) : 0u;
+                const bool ok = FULL || r < n;
+                if (MODE != 2 && a.lane32 && FULL) {
+                    const int64_t ru = sub0 + p + u * RPP;  // uniform row of this lane's row slot 0
+                    wk[u] = *(const u32x4 *)(kbase + ru * kstr + klane);
+                    wv[u] = *(const u32x4 *)(vbase + ru * vstr + vlane);
+                    if constexpr (QUANT) {
+                        sk[u] = *(const uint32_t *)(ksbase + ru * ksstr + kslane);
+                        sv[u] = *(const uint32_t *)(vsbase + ru * vsstr + vslane);
+                    }
+                } else {
+                    const int64_t row = MODE == 2 ? (ok ? rows_s[r] : 0) : sub0 + r;
+                    wk[u] = ok ? *(const u32x4 *)(kp + row * a.sk.m) : u32x4{0, 0, 0, 0};
+                    wv[u] = ok ? *(const u32x4 *)(vp + row * a.sv.m) : u32x4{0, 0, 0, 0};
+                    if constexpr (QUANT) {
+                        sk[u] = ok ? *(const uint32_t *)(kss + row * a.skss.m) : 0u;
+                        sv[u] = ok ? *(const uint32_t *)(vss + row * a.svss.m) : 0u;
+                    }
                 }
             }
         };
-        constexpr int NS = QUANT ? U : 1;
-        u32x4 wk[U], wv[U], wkn[U], wvn[U];
-        uint32_t sk[NS], sv[NS], skn[NS], svn[NS];
-        load(0, wkn, wvn, skn, svn);
+        auto load_round = [&](int p) __attribute__((always_inline)) {
+            if (p + R <= n)
+                load(p, std::true_type{});
+            else
+                load(p, std::false_type{});
+        };
+        load_round(0);
         for (int p = 0; p < n; p += R) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                wk[u] = wkn[u];
-                wv[u] = wvn[u];
-            }
-#pragma unroll
-            for (int u = 0; u < NS; ++u) {
-                sk[u] = skn[u];
-                sv[u] = svn[u];
-            }
-            if (PIPE && p + R < n) load(p + R, wkn, wvn, skn, svn);
             float sc[U];
             float mx = -INFINITY;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float x[EPL];
-                unpack_elem<ELEM>(wk[u], x);
                 float dot = 0.f;
+                if constexpr (INT4) {
+                    // sum of q * (128 + 8 code) over the lane's 32 elements, in two chains
+                    float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) dot = fmaf(qv[e], x[e], dot);
-                if constexpr (QUANT) dot = fmaf(ss_scale(sk[u]), dot, ss_shift(sk[u]) * qsum);
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int o = LPK / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
+                        for (int s2 = 0; s2 < 4; ++s2) {
+                            float &d = (i & 1) ? d1 : d0;
+                            d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(int4_pair(wk[u][i], s2, m4, c43)),
+                                                                as_bf16x2(q2[4 * i + s2]), d, false);
+                        }
+                    const float qc = ((d0 + d1) - 128.f * qraw) * 0.125f;  // q.code
+                    dot = a.scale_log2 * fmaf(ss_scale(sk[u]), qc, ss_shift(sk[u]) * qraw);
+                } else {
+                    float x[EPL];
+                    unpack_elem<ELEM>(wk[u], x);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) dot = fmaf(qv[e], x[e], dot);
+                    if constexpr (QUANT) dot = fmaf(ss_scale(sk[u]), dot, ss_shift(sk[u]) * qsum);
+                }
+                dot = lane_group_sum<LPK>(dot);
                 sc[u] = p + u * RPP + rs < n ? dot : -INFINITY;
                 mx = fmaxf(mx, sc[u]);
             }
@@ -273,7 +360,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pr, x[e], acc[e]);
             }
-            if (!PIPE && p + R < n) load(p + R, wkn, wvn, skn, svn);
+            if (p + R < n) load_round(p + R);
         }
     }
 
@@ -323,6 +410,26 @@ hipError_t launch(const DecodeArgs &args, hipStream_t stream) {
     while ((RB << (a.log2_hpw + 1)) <= DECODE_ROW_BYTES && (2 << a.log2_hpw) <= KPP &&
            a.Htot % (2 << a.log2_hpw) == 0)
         ++a.log2_hpw;
+    // lane32: within every workgroup (hpw heads from a multiple of hpw, RPP row slots, LPK
+    // 16-byte column slices) the offsets from the first head's row are >= 0 and < 2^32 bytes
+    constexpr int EPL = ELEM == DECODE_F32 ? 4 : (ELEM == DECODE_INT4 ? 32 : (ELEM == DECODE_FP8 ? 16 : 8));
+    constexpr int LPK = HD / EPL;
+    const int64_t RPP = (NT / LPK) >> a.log2_hpw, hpw = 1 << a.log2_hpw;
+    auto fits = [&](const Strides &st, int64_t es, int64_t col) {
+        int64_t lo = 0, hi = 0;
+        for (int h0 = 0; h0 < a.Htot; h0 += (int)hpw)
+            for (int h = h0; h < h0 + hpw; ++h) {
+                const int64_t d = head_offset(st, h, a.Hin) - head_offset(st, h0, a.Hin);
+                lo = d < lo ? d : lo;
+                hi = d > hi ? d : hi;
+            }
+        return lo >= 0 && (hi + col) * es + (RPP - 1) * st.m * es < (int64_t(1) << 32);
+    };
+    const int64_t es = ELEM == DECODE_F32 ? 4 : (ELEM == DECODE_BF16 ? 2 : 1);
+    a.lane32 = MODE != 2 && fits(a.sk, es, 16 / es * (LPK - 1)) && fits(a.sv, es, 16 / es * (LPK - 1));
+    if (ELEM == DECODE_FP8 || ELEM == DECODE_INT4)
+        a.lane32 = a.lane32 && fits(a.skss, 2, 2 * ((LPK - 1) * EPL / a.group)) &&
+                   fits(a.svss, 2, 2 * ((LPK - 1) * EPL / a.group));
     const int64_t grid = (int64_t)a.S * a.B * (a.Htot >> a.log2_hpw);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;

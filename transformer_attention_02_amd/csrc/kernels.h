@@ -60,6 +60,7 @@ struct DecodeArgs {
     Strides skss, svss;
     int group;
     int log2_hpw;  // heads per workgroup = 1 << log2_hpw (set by the launcher)
+    int lane32;    // every lane's offset from its workgroup's first head and row fits 32 bits (set by the launcher)
 };
 
 // Element type of a decode K/V cache (q is bf16 for the quantised caches, else the cache's type).
