@@ -341,10 +341,24 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
 // 8 waves (256 query rows) per workgroup, one workgroup per CU, 3-stage K/V ring (96 KB of
 // LDS for head dim 128).  Measured on MI355X against two 4-wave workgroups per CU with a
 // 2-stage ring (30% slower) and against a staggered two-group schedule with a 4-stage ring
-// (no faster).
+// (no faster).  Problems too small to give every CU a workgroup (few heads, short query
+// ranges) take workgroups of 4, 2 or 1 waves instead, so that more CUs share the work.
+#ifndef FWD_MIN_GRID
+#define FWD_MIN_GRID 256
+#endif
+template <int HD, bool OUT_F32>
+hipError_t launch_nw(const FwdArgs &a, hipStream_t stream) {
+    const int64_t units = (int64_t)a.nseq * a.B * a.Htot;
+    auto grid = [&](int bm) { return (a.max_seqlen_q + bm - 1) / bm * units; };
+    if (grid(256) >= FWD_MIN_GRID) return launch<HD, 8, 3, OUT_F32>(a, stream);
+    if (grid(128) >= FWD_MIN_GRID) return launch<HD, 4, 3, OUT_F32>(a, stream);
+    if (grid(64) >= FWD_MIN_GRID) return launch<HD, 2, 3, OUT_F32>(a, stream);
+    return launch<HD, 1, 3, OUT_F32>(a, stream);
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool out_f32, hipStream_t stream) {
-    if (a.K == 128) return out_f32 ? launch<128, 8, 3, true>(a, stream) : launch<128, 8, 3, false>(a, stream);
-    if (a.K == 64) return out_f32 ? launch<64, 8, 3, true>(a, stream) : launch<64, 8, 3, false>(a, stream);
+    if (a.K == 128) return out_f32 ? launch_nw<128, true>(a, stream) : launch_nw<128, false>(a, stream);
+    if (a.K == 64) return out_f32 ? launch_nw<64, true>(a, stream) : launch_nw<64, false>(a, stream);
     return hipErrorInvalidValue;
 }
 
