@@ -5,30 +5,63 @@
 // masks of "Attention - Biases & masks"), for head dims up to 128.  Nothing is
 // rounded below fp32, so the result tracks the exact softmax to ~1e-6.
 //
-// One workgroup = 4 waves over the same 64 query rows (one row per lane); the
-// keys are dealt out in 16-key tiles round-robin over the waves, so the four
-// waves run independent online softmaxes over disjoint key subsets.  Each wave
+// One workgroup = 8 waves (4 for head dims above 64) over the same 64 query rows
+// (one row per lane); the keys are dealt out in 16-key tiles round-robin over the
+// waves, so the waves run independent online softmaxes over disjoint key subsets.  Each wave
 // stages its own tiles in LDS (every lane then reads the same key row: an LDS
-// broadcast).  At the end the four (m, l, o) states are combined exactly, as in
+// broadcast).  At the end the waves' (m, l, o) states are combined exactly, as in
 // the merge of key chunks ("Exact softmax merge" in the site's Quick start):
-// two pairwise rounds through LDS.
+// pairwise rounds through LDS.
 #include "kernels.h"
 
 namespace attn {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int NWV = 4;   // waves, each with its own key subset
+// waves, each with its own key subset: 8 while q and o fit 256 registers per lane beside the
+// staging, else 4 (so that the register file holds two waves' q and o)
+template <int KD, int KVD>
+constexpr int nwaves() { return KD + KVD <= 128 ? 8 : 4; }
 constexpr int TB = 16;   // keys per tile
 constexpr int BM = 64;   // query rows per workgroup (one per lane)
 
+// Rows [0, TB) x columns [0, N) of a row-major tile at `src` (row stride `stride` floats) into
+// LDS, rows >= nrows and columns >= ncols as zeros.  Every load of the tile is issued before
+// the first LDS store (16-byte loads where the four columns are valid, single floats at the
+// column tail), so a tile costs one memory round trip.
+template <int N>
+__device__ __forceinline__ void stage_tile(const float *src, int64_t stride, int nrows, int ncols, float *dst, int lane) {
+    constexpr int C4 = N / 4, CNT = TB * C4 / 64;
+    static_assert(CNT * 64 == TB * C4, "tile split");
+    float4 r[CNT];
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+        const int idx = lane + 64 * i, row = idx / C4, c = 4 * (idx % C4);
+        const float *p = src + (int64_t)row * stride + c;
+        if (row < nrows && c + 4 <= ncols) {
+            r[i] = *(const float4 *)p;
+        } else {
+            r[i].x = (row < nrows && c < ncols) ? p[0] : 0.f;
+            r[i].y = (row < nrows && c + 1 < ncols) ? p[1] : 0.f;
+            r[i].z = (row < nrows && c + 2 < ncols) ? p[2] : 0.f;
+            r[i].w = (row < nrows && c + 3 < ncols) ? p[3] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+        const int idx = lane + 64 * i;
+        *(float4 *)&dst[(idx / C4) * N + 4 * (idx % C4)] = r[i];
+    }
+}
+
 template <int KD, int KVD>
-__global__ __launch_bounds__(NWV * 64) void fwd_f32_kernel(FwdArgs a) {
+__global__ __launch_bounds__((nwaves<KD, KVD>() * 64)) void fwd_f32_kernel(FwdArgs a) {
+    constexpr int NWV = nwaves<KD, KVD>();
     constexpr int TILE_FLOATS = TB * (KD + KVD);
     // per-wave K and V tiles; reused at the end for the cross-wave combine
-    __shared__ __attribute__((aligned(16))) float smem[NWV * TILE_FLOATS > 2 * 64 * (KVD + 2)
+    __shared__ __attribute__((aligned(16))) float smem[NWV * TILE_FLOATS > NWV / 2 * 64 * (KVD + 2)
                                                          ? NWV * TILE_FLOATS
-                                                         : 2 * 64 * (KVD + 2)];
+                                                         : NWV / 2 * 64 * (KVD + 2)];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int BH = a.B * a.Htot;
@@ -81,14 +114,9 @@ __global__ __launch_bounds__(NWV * 64) void fwd_f32_kernel(FwdArgs a) {
     for (int it = 0; it < rounds; ++it) {
         const int kt0 = kbeg + (it * NWV + wave) * TB;  // this wave's tile
         __syncthreads();                          // previous tile fully read
-        for (int idx = lane; idx < TB * KD; idx += 64) {
-            const int r = idx / KD, d = idx % KD, j = kt0 + r;
-            ks_[idx] = (j < kend && d < a.K) ? kp[(int64_t)j * a.sk.m + d] : 0.f;
-        }
-        for (int idx = lane; idx < TB * KVD; idx += 64) {
-            const int r = idx / KVD, d = idx % KVD, j = kt0 + r;
-            vs_[idx] = (j < kend && d < a.Kv) ? vp[(int64_t)j * a.sv.m + d] : 0.f;
-        }
+        const int nrows = min(TB, kend - kt0);    // <= 0: this wave has no tile this round
+        stage_tile<KD>(kp + (int64_t)kt0 * a.sk.m, a.sk.m, nrows, a.K, ks_, lane);
+        stage_tile<KVD>(vp + (int64_t)kt0 * a.sv.m, a.sv.m, nrows, a.Kv, vs_, lane);
         __syncthreads();
         if (kt0 >= kend) continue;
 
@@ -133,10 +161,10 @@ __global__ __launch_bounds__(NWV * 64) void fwd_f32_kernel(FwdArgs a) {
         }
     }
 
-    // exact combine of the four waves' states: waves 2,3 -> 0,1, then wave 1 -> 0
+    // exact combine of the waves' states, pairwise: waves [step, 2 step) -> [0, step)
     constexpr int REC = KVD + 2;  // o[KVD], m, l per row
 #pragma unroll
-    for (int step = 2; step >= 1; step >>= 1) {
+    for (int step = NWV / 2; step >= 1; step >>= 1) {
         __syncthreads();
         if (wave >= step && wave < 2 * step) {
             float *rec = smem + ((wave - step) * 64 + lane) * REC;
@@ -177,7 +205,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
     const int64_t grid = tiles * a.nseq * (int64_t)a.B * a.Htot;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_f32_kernel<KD, KVD>), dim3((unsigned)grid), dim3(NWV * 64), 0, stream, a);
+    hipLaunchKernelGGL((fwd_f32_kernel<KD, KVD>), dim3((unsigned)grid), dim3(nwaves<KD, KVD>() * 64), 0, stream, a);
     return hipGetLastError();
 }
 
