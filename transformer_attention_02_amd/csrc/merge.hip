@@ -6,11 +6,11 @@
 // exp(lse_c - M*), out = sum_c exp(lse_c - L) out_c.  A chunk at -inf weighs 0;
 // all chunks at -inf give out = 0 and lse = -inf.
 //
-// One workgroup per row.  Threads c < S read the S LSEs and the workgroup
-// reduces them to L; the weights go to LDS.  The value dimension is then read
-// by 8 chunk groups of 32 lanes, each lane taking 4 consecutive elements of
-// every 8th chunk, with all of a lane's loads issued before any arithmetic, and
-// the 8 partial sums are added through LDS.  Memory-bound: every chunk element
+// One workgroup per row.  The value dimension is read by 8 chunk groups of 32
+// lanes, each lane taking 4 consecutive elements of every 8th chunk, with all of
+// a lane's loads issued first (before the LSEs are even reduced).  Threads c < S
+// read the S LSEs and the workgroup reduces them to L; the weights go to LDS,
+// and the 8 weighted partial sums are added through LDS.  Memory-bound: every chunk element
 // is read once and every output element written once.
 #include "kernels.h"
 
@@ -68,6 +68,21 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
     const int64_t coff = (int64_t)b * a.sc.b + (int64_t)m * a.sc.m + head_offset(a.sc, hf, a.Hin);
     const int64_t ooff = (int64_t)b * a.so.b + (int64_t)m * a.so.m + head_offset(a.so, hf, a.Hin);
 
+    // the first pass's chunk values do not depend on the weights: issue their loads before
+    // the LSE reduction, so that a row costs one memory round trip when Kv <= SPAN
+    const int g = tid / (SPAN / 4), j = tid % (SPAN / 4);
+    const bool f32 = a.chunk_f32;
+    f32x4 x[MAXPER];
+    auto load_pass = [&](int d0) __attribute__((always_inline)) {
+        const int d = d0 + 4 * j;
+#pragma unroll
+        for (int i = 0; i < MAXPER; ++i) {
+            const int c = g + GROUPS * i;
+            x[i] = c < a.S ? load4(a.chunk[c], coff, d, a.Kv, f32) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    load_pass(0);
+
     const float lv = tid < a.S ? a.lse[tid][loff] : -INFINITY;
     const float mx = block_reduce(lv, red, true);
     if (mx == -INFINITY) {  // every chunk empty (uniform branch)
@@ -84,16 +99,8 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
     if (a.lse_out && tid == 0) a.lse_out[loff] = L;
     __syncthreads();
 
-    const int g = tid / (SPAN / 4), j = tid % (SPAN / 4);
-    const bool f32 = a.chunk_f32;
     for (int d0 = 0; d0 < a.Kv; d0 += SPAN) {
-        const int d = d0 + 4 * j;
-        f32x4 x[MAXPER];
-#pragma unroll
-        for (int i = 0; i < MAXPER; ++i) {
-            const int c = g + GROUPS * i;
-            x[i] = c < a.S ? load4(a.chunk[c], coff, d, a.Kv, f32) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        if (d0 > 0) load_pass(d0);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < MAXPER; ++i) {
