@@ -96,9 +96,12 @@ def kernel_source_digest(kind="fwd"):
     return h.hexdigest()
 
 
-def recorded_traffic(key):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def recorded_traffic(key, path=None):
     """HBM bytes per launch from profiles/traffic.json when its kernel digest matches, else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = path or TRAFFIC_JSON
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -145,7 +148,7 @@ def _cluster_mean(vals, which):
     return sum(side) / len(side)
 
 
-def write_traffic(fetch_db, write_db):
+def write_traffic(fetch_db, write_db, out_path=None):
     fetch, write = _counter_values(fetch_db, "FETCH_SIZE"), _counter_values(write_db, "WRITE_SIZE")
 
     def find(g, needle):
@@ -172,7 +175,7 @@ def write_traffic(fetch_db, write_db):
                     "commands": [f"rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -- {cmd}",
                                  f"rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -- {cmd}",
                                  f"python bench.py --traffic {fetch_db} {write_db}"]}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+    with open(out_path or TRAFFIC_JSON, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     for key, rec in out.items():
