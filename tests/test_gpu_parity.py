@@ -750,6 +750,36 @@ def test_decode_permuted_head_order(A, kind):
         check(out.reshape(B, 1, G5 * Hg, D), lse, oo, ol, TOL_F32, TOL_F32, "permuted int4")
 
 
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "int4"])
+def test_decode_negative_scale(A, kind):
+    """A negative softmax scale (the largest score is then the most negative dot product):
+    every decode element type, fp32 output, a ragged key count."""
+    B, M, H, D, S, sc = 2, 777, 4, 128, 5, -0.3
+    say(f"case: decode {kind} scale={sc}")
+    qh = synth.normal(1500, synth.TAG_Q, (B, 1, H, D), "bf16")
+    if kind == "bf16":
+        kh = synth.normal(1500, synth.TAG_K, (B, M, H, D), "bf16")
+        vh = synth.normal(1500, synth.TAG_V, (B, M, H, D), "bf16")
+        out, lse = A.attn_decode_splitkv(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), S, scale=sc)
+        torch.cuda.synchronize()
+        oo, ol = run_oracle(qh, kh, vh, 0, "bf16", scale=sc)
+        check(out, lse, oo, ol, TOL_BF16_OUT, TOL_LSE, "bf16 negative scale")
+    elif kind == "fp8":
+        kc, vc, kss, vss = _fp8_cache(1500, (B, M, H, D))
+        out, lse = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), _fp8(kc), _fp8(vc), _f16(kss), _f16(vss), S,
+                                             scale=sc, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        oo, ol = _fp8_oracle(qh, kc, vc, kss, vss, scale=sc)
+        check(out, lse, oo, ol, TOL_F32, TOL_F32, "fp8 negative scale")
+    else:
+        kc, vc, kss, vss = _int4_cache(1500, (B, M, H, D), 4)
+        out, lse = A.attn_decode_splitkv_int4(dev(qh, "bf16"), _u8(kc), _u8(vc), _flat_ss(kss), _flat_ss(vss), S,
+                                              scale=sc, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        oo, ol = _int4_oracle(qh, kc, vc, kss, vss, scale=sc)
+        check(out, lse, oo, ol, TOL_F32, TOL_F32, "int4 negative scale")
+
+
 @pytest.mark.parametrize("page", [16, 64])
 def test_int4_decode_paged(A, page):
     B, H, D, S, P, maxb, G = 3, 4, 128, 5, 100, 20, 4
