@@ -349,6 +349,7 @@ def main():
             result["rows"]["decode_splitkv"]["cpu_oracle"] = oracle_timing(
                 lambda: oracle_mod().attention(*sample), kv_bytes / B / 1e9, "GB/s",
                 "batch element 0 of 16 (32768 keys x 32 heads), fp64 exact attention; GB/s of its bf16 K+V")
+            result["rows"]["decode_splitkv"]["cpu_oracle"]["host_bytes"] = int(sum(x.nbytes for x in sample))
             del sample
         del qdh, kdh, vdh
         # the same cache as 8192 pages of 64 rows in a random order (PagedBlockDiagonalPaddedKeysMask form)
@@ -525,6 +526,15 @@ def main():
             entry[f"S{S}"] = {"partials_plus_merge_ms": round(ms_s, 5), "merge_ms": round(ms_m, 5),
                               "merge_GBps": round(mbytes / (ms_m * 1e-3) / 1e9, 1)}
             log(f"partial+merge S={S}: {ms_s * 1e3:.1f} us (merge {ms_m * 1e3:.1f} us)")
+        if not args.no_cpu:  # the oracle's 8 partials over the same shards and their merge
+            qo3, ko3, vo3 = (synth.to_f64(x, "bf16") for x in (qh3, kh3, vh3))
+
+            def oracle_split():
+                parts = [oracle_mod().partial(qo3, ko3, vo3, s * 128, (s + 1) * 128) for s in range(8)]
+                oracle_mod().merge([o for o, _ in parts], [l for _, l in parts])
+
+            entry["cpu_oracle"] = oracle_timing(oracle_split, 4.0 * 16 * 128 * 1024 * 128 / 1e12, "TFLOP/s",
+                                                "8 partials of 128 keys and their merge, fp64")
         result["rows"]["partial_merge"] = entry
 
     # ------------------------------------------------------------ calibration copy for the HBM counters
@@ -555,6 +565,11 @@ def main():
                                                     "frac": round(tf1 / PEAK_FP32_TFLOPS, 6),
                                                     "note": "fp32 vector peak, for information: 4 workgroups"}}
         log(f"fp32 tiny: {ms_1 * 1e3:.1f} us/call")
+        if not args.no_cpu:
+            qo1, ko1, vo1 = (synth.to_f64(x, "f32") for x in (qh1, kh1, vh1))
+            result["rows"]["fp32_tiny"]["cpu_oracle"] = oracle_timing(
+                lambda: oracle_mod().attention(qo1, ko1, vo1, scale=0.125), fl1 / 1e12, "TFLOP/s",
+                "the whole fp32 tiny workload, fp64")
 
     print(json.dumps(result), flush=True)
 
