@@ -167,6 +167,27 @@ def test_ragged_shapes_all_masks(A, dtype, D):
         check(out, lse, oo, ol, tol_o, tol_l, f"packed mask={mask}")
 
 
+@pytest.mark.parametrize("H,D", [(64, 128), (32, 128), (16, 128), (8, 128), (32, 64), (16, 64), (8, 64)])
+def test_forward_workgroup_sizes(A, H, D):
+    """1000 query rows with 64, 32, 16 or 8 heads: the launcher takes 8-, 4-, 2- and 1-wave
+    workgroups (256, 128, 64 and 32 rows; the 8-wave one with its paired 4-slot ring, the
+    others with a 3-slot ring).  Causal and causal-window masks, bf16 and fp32 outputs, three
+    sampled heads against the oracle."""
+    B, M = 1, 1000
+    qh, kh, vh = synth.qkv(1600 + H + D, (B, M, H, D), (B, M, H, D), (B, M, H, D), "bf16")
+    heads = [0, H // 2, H - 1]
+    sub = lambda x: np.ascontiguousarray(x[:, :, heads])
+    for mask, win in [(1, None), (7, 300)]:
+        say(f"case: workgroup sizes H={H} D={D} mask={mask} window={win}")
+        kw = {"window_size": win} if win else {}
+        out, lse = A.attn_fwd(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), mask=mask, scale=0.1, **kw)
+        po, pl = A.attn_partial(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), mask=mask, scale=0.1, **kw)
+        torch.cuda.synchronize()
+        oo, ol = run_oracle(sub(qh), sub(kh), sub(vh), mask, "bf16", scale=0.1, window=win)
+        check(out[:, :, heads], lse[:, heads], oo, ol, TOL_BF16_OUT, TOL_LSE, f"H={H} bf16 out")
+        check(po[:, :, heads], pl[:, heads], oo, ol, TOL_BF16_OUT, TOL_LSE, f"H={H} fp32 partial out")
+
+
 def test_packed_with_distinct_key_offsets(A):
     """Block-diagonal with separate key offsets (queries and keys packed differently), incl. an empty key block."""
     sq, sk = synth.seqstarts([5, 70, 130]), synth.seqstarts([90, 0, 200])
