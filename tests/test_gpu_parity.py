@@ -188,6 +188,40 @@ def test_forward_workgroup_sizes(A, H, D):
         check(po[:, :, heads], pl[:, heads], oo, ol, TOL_BF16_OUT, TOL_LSE, f"H={H} fp32 partial out")
 
 
+@pytest.mark.parametrize("K,Kv", [(64, 128), (128, 64)])
+def test_bf16_distinct_head_dims(A, K, Kv):
+    """q/k head dim K and v/out head dim Kv differ (each 64 or 128): ragged shapes with no mask,
+    causal and a causal window on small grids (1-wave workgroups) and on 64 heads (8-wave
+    workgroups, sampled heads), and packed block-diagonal causal sequences; bf16 out and the
+    fp32 partial output."""
+    seed = 1700 + K
+    for B, Mq, Mkv, H, mask, win in [(2, 129, 1000, 3, 0, None), (2, 1000, 1000, 3, 1, None),
+                                     (1, 1000, 1000, 64, 1, None), (1, 777, 777, 64, 7, 200), (2, 65, 7, 2, 1, None)]:
+        seed += 1
+        say(f"case: bf16 K={K} Kv={Kv} B={B} Mq={Mq} Mkv={Mkv} H={H} mask={mask} window={win}")
+        qh, kh, vh = synth.qkv(seed, (B, Mq, H, K), (B, Mkv, H, K), (B, Mkv, H, Kv), "bf16")
+        kw = {"window_size": win} if win else {}
+        out, lse = A.attn_fwd(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), mask=mask, scale=0.1, **kw)
+        po, pl = A.attn_partial(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), mask=mask, scale=0.1, **kw)
+        torch.cuda.synchronize()
+        heads = list(range(H)) if H <= 3 else [0, 17, H - 1]
+        sub = lambda x: np.ascontiguousarray(x[:, :, heads])
+        oo, ol = run_oracle(sub(qh), sub(kh), sub(vh), mask, "bf16", scale=0.1, window=win)
+        assert out.shape == (B, Mq, H, Kv) and po.shape == (B, Mq, H, Kv)
+        check(out[:, :, heads], lse[:, heads], oo, ol, TOL_BF16_OUT, TOL_LSE, f"K={K} Kv={Kv} bf16 out")
+        check(po[:, :, heads], pl[:, heads], oo, ol, TOL_BF16_OUT, TOL_LSE, f"K={K} Kv={Kv} fp32 partial")
+    lens = [1, 129, 64, 7, 300, 65]
+    ss = synth.seqstarts(lens)
+    M = int(ss[-1])
+    say(f"case: bf16 K={K} Kv={Kv} packed causal lens={lens}")
+    qh, kh, vh = synth.qkv(seed + 1, (1, M, 2, K), (1, M, 2, K), (1, M, 2, Kv), "bf16")
+    out, lse = A.attn_fwd(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), mask=3,
+                          seqstart_q=torch.from_numpy(ss).to("cuda"), max_seqlen_q=max(lens))
+    torch.cuda.synchronize()
+    oo, ol = run_oracle(qh, kh, vh, 3, "bf16", ss=ss)
+    check(out, lse, oo, ol, TOL_BF16_OUT, TOL_LSE, f"K={K} Kv={Kv} packed causal")
+
+
 def test_packed_with_distinct_key_offsets(A):
     """Block-diagonal with separate key offsets (queries and keys packed differently), incl. an empty key block."""
     sq, sk = synth.seqstarts([5, 70, 130]), synth.seqstarts([90, 0, 200])

@@ -67,24 +67,27 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// NW waves (32 query rows each) per workgroup; STAGES-deep LDS ring of K/V tiles.
-template <int HD, int NW, int STAGES, bool OUT_F32>
+// NW waves (32 query rows each) per workgroup; STAGES-deep LDS ring of K/V tiles; KD and VD
+// are the head dims of q/k and of v/out.
+template <int KD, int VD, int NW, int STAGES, bool OUT_F32>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     constexpr int NT = NW * 64;                  // threads per workgroup
     constexpr int BM = NW * 32;                  // query rows per workgroup
     static_assert(STAGES == 3 || STAGES == 4, "the unrolled tile loop names three or four LDS stages");
     // STAGES == 4: the ring is filled two tiles at a time, with one wait + barrier per two tiles
     constexpr bool PAIRS = STAGES == 4;
-    constexpr int ROWB = HD * 2;                 // bytes per tile row
-    constexpr int CPR = HD / 8;                  // 16-byte chunks per row
-    constexpr int TILE_BYTES = BN * ROWB;        // one K or V tile
-    constexpr int V_BASE = STAGES * TILE_BYTES;  // K tiles of all stages first, then the V tiles
-    constexpr int ROUNDS = TILE_BYTES / 16 / NT; // 16-byte loads per thread per tile per tensor
-    constexpr int KS = HD / 16;                  // k-steps of S^T
-    constexpr int MB = HD / 32;                  // 32-row blocks of O^T
-    static_assert(ROUNDS >= 1 && ROUNDS * NT * 16 == TILE_BYTES, "tile split");
+    constexpr int KROWB = KD * 2, VROWB = VD * 2;    // bytes per K / V tile row
+    constexpr int KCPR = KD / 8, VCPR = VD / 8;      // 16-byte chunks per row
+    constexpr int KTILE = BN * KROWB, VTILE = BN * VROWB;
+    constexpr int V_BASE = STAGES * KTILE;           // K tiles of all stages first, then the V tiles
+    constexpr int KROUNDS = KTILE / 16 / NT;         // 16-byte loads per thread per K tile
+    constexpr int VROUNDS = VTILE / 16 / NT;         // and per V tile
+    constexpr int KS = KD / 16;                      // k-steps of S^T
+    constexpr int MB = VD / 32;                      // 32-row blocks of O^T
+    static_assert(KROUNDS >= 1 && KROUNDS * NT * 16 == KTILE && VROUNDS >= 1 && VROUNDS * NT * 16 == VTILE,
+                  "tile split");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGES * TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * (KTILE + VTILE)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
@@ -133,25 +136,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 
     // ---- async tile loads: global -> LDS, 16 bytes per lane, OOB rows read as zeros
     // Slot p of a tile (16 bytes) holds row p / CPR, physical chunk p % CPR.
-    unsigned koff[ROUNDS], voff[ROUNDS];
+    unsigned koff[KROUNDS], voff[VROUNDS];
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
+    for (int r = 0; r < KROUNDS; ++r) {
         const int p = (r * NW + wave) * 64 + lane;
-        const int row = p / CPR, c = (p % CPR) ^ swz<HD>(row);
+        const int row = p / KCPR, c = (p % KCPR) ^ swz<KD>(row);
         koff[r] = row * kstride + c * 16;
+    }
+#pragma unroll
+    for (int r = 0; r < VROUNDS; ++r) {
+        const int p = (r * NW + wave) * 64 + lane;
+        const int row = p / VCPR, c = (p % VCPR) ^ swz<VD>(row);
         voff[r] = row * vstride + c * 16;
     }
     const unsigned smem_base = (unsigned)(unsigned long long)(unsigned char LDS_AS *)smem;
     auto issue = [&](int t) __attribute__((always_inline)) {
         const int kt0 = t * BN;
         const int nvalid = min(BN, Lk - kt0);
-        const unsigned st = smem_base + ((t - tb) % STAGES) * TILE_BYTES;
-        const i32x4 kr = make_rsrc(kp + (int64_t)kt0 * a.sk.m, (nvalid - 1) * kstride + ROWB);
-        const i32x4 vr = make_rsrc(vp + (int64_t)kt0 * a.sv.m, (nvalid - 1) * vstride + ROWB);
+        const int slot = (t - tb) % STAGES;
+        const unsigned kst = smem_base + slot * KTILE, vst = smem_base + V_BASE + slot * VTILE;
+        const i32x4 kr = make_rsrc(kp + (int64_t)kt0 * a.sk.m, (nvalid - 1) * kstride + KROWB);
+        const i32x4 vr = make_rsrc(vp + (int64_t)kt0 * a.sv.m, (nvalid - 1) * vstride + VROWB);
 #pragma unroll
-        for (int r = 0; r < ROUNDS; ++r) dma16(kr, koff[r], st + (r * NW + wave) * 1024);
+        for (int r = 0; r < KROUNDS; ++r) dma16(kr, koff[r], kst + (r * NW + wave) * 1024);
 #pragma unroll
-        for (int r = 0; r < ROUNDS; ++r) dma16(vr, voff[r], st + V_BASE + (r * NW + wave) * 1024);
+        for (int r = 0; r < VROUNDS; ++r) dma16(vr, voff[r], vst + (r * NW + wave) * 1024);
     };
 
     // ---- Q^T fragments (B operand), resident for the whole kernel
@@ -179,7 +188,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     // ---- LDS read addresses (byte offsets inside a stage)
     int kaddr[KS];  // K: row kb*32 + l32 (kb adds 32 rows), chunk 2s + hh
 #pragma unroll
-    for (int s = 0; s < KS; ++s) kaddr[s] = l32 * ROWB + (((2 * s + hh) ^ swz<HD>(l32)) << 4);
+    for (int s = 0; s < KS; ++s) kaddr[s] = l32 * KROWB + (((2 * s + hh) ^ swz<KD>(l32)) << 4);
     // V: lane i of 16-lane group G addresses key row 4*hh + i/4 (+ 8e + 16kt + 32kb) and
     // head-dim columns mb*32 + 16*(G&1) + 4*(i%4) .. +3.
     const int vrow = 4 * hh + ((lane & 15) >> 2);
@@ -190,7 +199,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int row = vrow + 8 * e, col = mb * 32 + vcol;
-            vaddr[mb][e] = V_BASE + row * ROWB + ((((col >> 3) ^ swz<HD>(row))) << 4) + ((col & 4) << 1);
+            vaddr[mb][e] = V_BASE + row * VROWB + ((((col >> 3) ^ swz<VD>(row))) << 4) + ((col & 4) << 1);
         }
 
     f32x16 o[MB];
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     auto step = [&](int t, auto masked_tag, auto stage_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         constexpr int STAGE_C = decltype(stage_tag)::value;
-        const int soff = (STAGE_C >= 0 ? STAGE_C : (t - tb) % STAGES) * TILE_BYTES;
+        const int slot = STAGE_C >= 0 ? STAGE_C : (t - tb) % STAGES;
         const int kt0 = t * BN;
         if (PAIRS) {
             // even tile of a pair: both tiles of the pair are in, and the two slots of the
@@ -215,7 +224,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                 if (t + 3 < te) issue(t + 3);
             }
         } else {
-            if (t + 1 < te) wait_barrier<2 * ROUNDS>();
+            if (t + 1 < te) wait_barrier<KROUNDS + VROUNDS>();
             else wait_barrier<0>();
             if (t + 2 < te) issue(t + 2);
         }
@@ -223,14 +232,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         if (MASKED && ((int64_t)kt0 + BN - 1 < (int64_t)wrow0 + shift - a.wl ||
                        (int64_t)kt0 > (int64_t)wrow0 + 31 + shift + a.wr))
             return;
-        const unsigned char LDS_AS *st = (const unsigned char LDS_AS *)smem + soff;
+        const unsigned char LDS_AS *kst = (const unsigned char LDS_AS *)smem + slot * KTILE;  // K tile
+        const unsigned char LDS_AS *vst = (const unsigned char LDS_AS *)smem + slot * VTILE;  // + vaddr (from V_BASE)
 
         // S^T = K Q^T for two 32-key blocks
         f32x16 sa = f32x16{}, sb = f32x16{};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const bf16x8 k0 = *(const bf16x8 LDS_AS *)(st + kaddr[s]);
-            const bf16x8 k1 = *(const bf16x8 LDS_AS *)(st + kaddr[s] + 32 * ROWB);
+            const bf16x8 k0 = *(const bf16x8 LDS_AS *)(kst + kaddr[s]);
+            const bf16x8 k1 = *(const bf16x8 LDS_AS *)(kst + kaddr[s] + 32 * KROWB);
             sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], sa, 0, 0, 0);
             sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], sb, 0, 0, 0);
         }
@@ -286,11 +296,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         // O^T += V^T P^T over 4 steps of 16 keys
 #pragma unroll
         for (int ksi = 0; ksi < 4; ++ksi) {
-            const int roff = ksi * 16 * ROWB;  // kb*32 + kt*16 rows
+            const int roff = ksi * 16 * VROWB;  // kb*32 + kt*16 rows
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS *)(st + vaddr[mb][0] + roff));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS *)(st + vaddr[mb][1] + roff));
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS *)(vst + vaddr[mb][0] + roff));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS *)(vst + vaddr[mb][1] + roff));
                 const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ksi], o[mb], 0, 0, 0);
             }
@@ -343,14 +353,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     }
 }
 
-template <int HD, int NW, int STAGES, bool OUT_F32>
+template <int KD, int VD, int NW, int STAGES, bool OUT_F32>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
     constexpr int BM = NW * 32;
     const int64_t tiles = (a.max_seqlen_q + BM - 1) / BM;
     const int64_t grid = tiles * a.nseq * (int64_t)a.B * a.Htot;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_bf16_kernel<HD, NW, STAGES, OUT_F32>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<KD, VD, NW, STAGES, OUT_F32>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -365,19 +375,26 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
 #ifndef FWD_MIN_GRID
 #define FWD_MIN_GRID 256
 #endif
-template <int HD, bool OUT_F32>
+template <int KD, int VD, bool OUT_F32>
 hipError_t launch_nw(const FwdArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)a.nseq * a.B * a.Htot;
     auto grid = [&](int bm) { return (a.max_seqlen_q + bm - 1) / bm * units; };
-    if (grid(256) >= FWD_MIN_GRID) return launch<HD, 8, 4, OUT_F32>(a, stream);
-    if (grid(128) >= FWD_MIN_GRID) return launch<HD, 4, 3, OUT_F32>(a, stream);
-    if (grid(64) >= FWD_MIN_GRID) return launch<HD, 2, 3, OUT_F32>(a, stream);
-    return launch<HD, 1, 3, OUT_F32>(a, stream);
+    if (grid(256) >= FWD_MIN_GRID) return launch<KD, VD, 8, 4, OUT_F32>(a, stream);
+    if (grid(128) >= FWD_MIN_GRID) return launch<KD, VD, 4, 3, OUT_F32>(a, stream);
+    if (grid(64) >= FWD_MIN_GRID) return launch<KD, VD, 2, 3, OUT_F32>(a, stream);
+    return launch<KD, VD, 1, 3, OUT_F32>(a, stream);
+}
+
+template <int KD, int VD>
+hipError_t launch_out(const FwdArgs &a, bool out_f32, hipStream_t stream) {
+    return out_f32 ? launch_nw<KD, VD, true>(a, stream) : launch_nw<KD, VD, false>(a, stream);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool out_f32, hipStream_t stream) {
-    if (a.K == 128) return out_f32 ? launch_nw<128, true>(a, stream) : launch_nw<128, false>(a, stream);
-    if (a.K == 64) return out_f32 ? launch_nw<64, true>(a, stream) : launch_nw<64, false>(a, stream);
+    if (a.K == 128 && a.Kv == 128) return launch_out<128, 128>(a, out_f32, stream);
+    if (a.K == 64 && a.Kv == 64) return launch_out<64, 64>(a, out_f32, stream);
+    if (a.K == 64 && a.Kv == 128) return launch_out<64, 128>(a, out_f32, stream);
+    if (a.K == 128 && a.Kv == 64) return launch_out<128, 64>(a, out_f32, stream);
     return hipErrorInvalidValue;
 }
 
