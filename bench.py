@@ -114,7 +114,7 @@ def recorded_traffic(key, path=None):
 # (record key, sources digested, kernel name, which value cluster of the dispatches when two workloads
 # launch the same kernel on the same grid: 0 the lower, 1 the higher, None all)
 TRAFFIC_KERNELS = (
-    ("fwd_bf16 causal 2x2048x32x128", "fwd", "fwd_bf16_kernel<128, 8, 4, false>", None),
+    ("fwd_bf16 causal 2x2048x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false>", None),
     ("decode bf16 16x32768x32x128 s64", "decode", "decode_kernel<128, 0, 0>", None),
     ("decode bf16 paged 16x32768x32x128 page64 s64", "decode", "decode_kernel<128, 0, 2>", None),
     ("decode fp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 2, 0>", None),
@@ -301,7 +301,7 @@ def main():
     result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                           "traffic": recorded_traffic("fwd_bf16 causal 2x2048x32x128"),
-                          "kernel": "fwd_bf16_kernel<128,8,4,false>", "flops_per_launch": flops}
+                          "kernel": "fwd_bf16_kernel<128,128,8,4,false>", "flops_per_launch": flops}
 
     # ------------------------------------------------------------ CPU baseline: the oracle on the same workload
     if not args.no_cpu:
