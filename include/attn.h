@@ -27,7 +27,8 @@
  *     dim must have stride 1 and the row start of every (b, m, head) must be
  *     16-byte aligned; other strides are free, including 0 (an explicitly
  *     expanded K/V head axis for GQA/MQA, "Conventions" and "Sharp edges:
- *     GQA broadcasting is explicit").
+ *     GQA broadcasting is explicit").  Tensors a call writes (out, the
+ *     gradients) take no stride 0 on an axis of extent > 1.
  *   - out has q's layout with the last dim replaced by V's head dim.
  *   - lse is fp32, contiguous [B, H_total, Mq]; packed sequences use
  *     [1, H_total, M_total] indexed by packed row.  LSE is the natural log

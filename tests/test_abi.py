@@ -79,6 +79,7 @@ def std4(M=128, D=128, dt=A.ATTN_DTYPE_BF16):
     ("out_dtype", A.ATTN_ERR_INVALID_ARGUMENT, "q's dtype"),
     ("scale_inf", A.ATTN_ERR_INVALID_ARGUMENT, "scale"),
     ("null", A.ATTN_ERR_INVALID_ARGUMENT, "NULL"),
+    ("out_broadcast", A.ATTN_ERR_INVALID_ARGUMENT, "stride-0"),
 ])
 def test_fwd_rejects(case, status, needle):
     q, k, v, o = std4(), std4(256), std4(256), std4()
@@ -114,6 +115,8 @@ def test_fwd_rejects(case, status, needle):
         kw["scale"] = float("inf")
     elif case == "null":
         q = tensor([2, 128, 4, 128], data=0)
+    elif case == "out_broadcast":  # both batch elements would store to the same rows
+        o = tensor([2, 128, 4, 128], stride=[0, 512, 128, 1])
     rc = fwd(q, k, v, o, **kw)
     assert rc == status
     assert needle in A.attn_last_error()
@@ -167,6 +170,9 @@ def test_merge_rejects():
     assert merge_call(2, [c, c], [FAKE, 0], o) == A.ATTN_ERR_INVALID_ARGUMENT
     assert "lse_chunks[1]" in A.attn_last_error()
     assert merge_call(1, [c], [FAKE], tensor([1, 128, 8, 128])) == A.ATTN_ERR_INVALID_ARGUMENT
+    o_heads0 = tensor([1, 128, 16, 128], stride=[128 * 128, 128, 0, 1])
+    assert merge_call(2, [c, c], [FAKE, FAKE], o_heads0) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert "stride-0" in A.attn_last_error()
 
 
 def test_decode_workspace_and_rejects():
@@ -185,6 +191,11 @@ def test_decode_workspace_and_rejects():
     assert call(num_splits=129) == A.ATTN_ERR_UNSUPPORTED
     assert call(ws=FAKE * 256 + 16) == A.ATTN_ERR_INVALID_ARGUMENT
     assert call(qq=tensor([B, 2, H, D])) == A.ATTN_ERR_INVALID_ARGUMENT
+    o_b0 = tensor([B, 1, H, D], stride=[0, H * D, D, 1])
+    assert A._lib.attn_decode_splitkv(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), S, float("nan"),
+                                      ctypes.c_void_p(FAKE * 256), need, ctypes.byref(o_b0), None,
+                                      None) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert "stride-0" in A.attn_last_error()
 
 
 def fwd_ex(q, k, v, o, mask, varlen=None, fn=None):

@@ -97,6 +97,17 @@ int64_t htot(const View &v) { return v.G * v.H; }
 
 bool same_heads(const View &a, const View &b) { return a.ndim == b.ndim && a.G == b.G && a.H == b.H; }
 
+// Tensors the kernels write get each element written once: an axis of extent > 1 with
+// stride 0 would have several workgroups store to the same address.
+attn_status check_written(const char *fn, const char *name, const View &x) {
+    const int64_t ext[4] = {x.B, x.M, x.G, x.H};
+    const int64_t str[4] = {x.s.b, x.s.m, x.s.g, x.s.h};
+    for (int i = 0; i < 4; ++i)
+        if (ext[i] > 1 && str[i] == 0)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: %s must not have stride-0 axes", fn, name);
+    return ATTN_OK;
+}
+
 attn_status launch_status(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
     return ok();
@@ -161,6 +172,7 @@ attn_status forward(const char *fn, bool partial, const attn_tensor *qt, const a
     if (o.M != q.M) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out must have q's row count", fn);
     if (k.D != q.D) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q and k head dims differ", fn);
     if (o.D != v.D) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out head dim must equal v's", fn);
+    if ((st = check_written(fn, "out", o)) != ATTN_OK) return st;
     MaskSpec ms;
     if ((st = mask_spec(fn, mask, &ms)) != ATTN_OK) return st;
     const bool packed = ms.packed;
@@ -307,6 +319,7 @@ attn_status attn_merge(int32_t n_chunks, const attn_tensor *out_chunks, const fl
     }
     if (!same_heads(o, c0) || o.B != c0.B || o.M != c0.M || o.D != c0.D)
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out shape differs from the chunks'", fn);
+    if ((st = check_written(fn, "out", o)) != ATTN_OK) return st;
     const int64_t rows = c0.B * c0.M * htot(c0);
     for (int i = 0; i < n_chunks; ++i)
         if (rows > 0 && (!lse_chunks[i] || ((uintptr_t)lse_chunks[i]) % 4))
@@ -369,14 +382,8 @@ attn_status attn_bwd(const attn_tensor *dot, const attn_tensor *qt, const attn_t
     if (v.B != k.B || v.M != k.M) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: k and v have different key counts", fn);
     if (k.B != q.B) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: batch sizes differ", fn);
     if (k.D != q.D) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q and k head dims differ", fn);
-    // gradients are written once per element: no axis of extent > 1 may have stride 0
-    for (const View *x : {&dq, &dk, &dv}) {
-        const int64_t ext[4] = {x->B, x->M, x->G, x->H};
-        const int64_t str[4] = {x->s.b, x->s.m, x->s.g, x->s.h};
-        for (int i = 0; i < 4; ++i)
-            if (ext[i] > 1 && str[i] == 0)
-                return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: gradient tensors must not have stride-0 axes", fn);
-    }
+    for (const View *x : {&dq, &dk, &dv})
+        if ((st = check_written(fn, "gradient tensors", *x)) != ATTN_OK) return st;
     if (q.D < 1 || v.D < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: head dims must be >= 1", fn);
     if (q.dtype == ATTN_DTYPE_BF16) {
         if (!((q.D == 64 || q.D == 128) && v.D == q.D))
@@ -529,6 +536,7 @@ attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: batch sizes differ", fn);
     }
     if (q.M != 1 || o.M != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: decode takes one query row (M == 1)", fn);
+    if ((st = check_written(fn, "out", o)) != ATTN_OK) return st;
     if (v.M != k.M) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: k and v have different key counts", fn);
     if (k.D != q.D || v.D != q.D || o.D != q.D)
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out head dims must match", fn);
