@@ -1,0 +1,65 @@
+"""Host-side argument checks of the Python binding: every case is refused before any C call, so
+these run without a GPU (the tensors here live in host memory)."""
+import pytest
+import torch
+
+from transformer_attention_02_amd import attn as A
+
+
+def qkv(B=1, M=64, H=2, D=64):
+    return [torch.zeros(B, M, H, D, dtype=torch.bfloat16) for _ in range(3)]
+
+
+def test_host_tensors_are_refused():
+    q, k, v = qkv()
+    with pytest.raises(ValueError, match="device"):
+        A.attn_fwd(q, k, v)
+    with pytest.raises(ValueError, match="device"):
+        A.attn_partial(q, k, v, lse=False)
+
+
+def test_sequence_offsets_must_be_int32_and_contiguous():
+    q, k, v = qkv()
+    with pytest.raises(TypeError, match="int32"):
+        A.attn_fwd(q, k, v, mask=A.MASK_BLOCKDIAG_CAUSAL, seqstart_q=torch.tensor([0, 32, 64]), max_seqlen_q=32)
+    strided = torch.zeros(6, dtype=torch.int32)[::2]
+    with pytest.raises(ValueError, match="contiguous"):
+        A.attn_fwd(q, k, v, mask=A.MASK_BLOCKDIAG_CAUSAL, seqstart_q=strided, max_seqlen_q=32)
+
+
+def test_caller_lse_must_be_fp32_contiguous_and_large_enough():
+    q, k, v = qkv()
+    with pytest.raises(TypeError, match="float32"):
+        A.attn_fwd(q, k, v, lse=torch.empty(1, 2, 64, dtype=torch.float64))
+    with pytest.raises(ValueError, match="contiguous"):
+        A.attn_fwd(q, k, v, lse=torch.empty(1, 64, 2).transpose(1, 2))
+    with pytest.raises(ValueError, match="holds 127 values; the call needs 128"):
+        A.attn_fwd(q, k, v, lse=torch.empty(127))
+    with pytest.raises(ValueError, match="holds"):
+        A.prepare_fwd(q, k, v, torch.empty_like(q), torch.empty(10))
+
+
+def test_decode_index_arrays_and_lse():
+    q = torch.zeros(2, 1, 2, 64, dtype=torch.bfloat16)
+    cache = torch.zeros(1, 256, 2, 64, dtype=torch.bfloat16)
+    lens32 = torch.tensor([100, 50], dtype=torch.int32)
+    with pytest.raises(TypeError, match="block_tables must be int32"):
+        A.attn_decode_splitkv_paged(q, cache, cache, lens32, 4, 128, block_tables=torch.zeros(2, 2, dtype=torch.int64),
+                                    page_size=64)
+    with pytest.raises(TypeError, match="seqlens must be int32"):
+        A.attn_decode_splitkv_paged(q, cache, cache, lens32.long(), 4, 128)
+    with pytest.raises(ValueError, match="holds"):
+        A.attn_decode_splitkv(q, cache.expand(2, 256, 2, 64), cache.expand(2, 256, 2, 64), 4, lse=torch.empty(3))
+
+
+def test_merge_lse_chunks_are_checked():
+    c = torch.zeros(1, 16, 2, 64)
+    good = torch.zeros(1, 2, 16)
+    with pytest.raises(ValueError, match="differ in length"):
+        A.attn_merge([c, c], [good])
+    with pytest.raises(TypeError, match=r"lse_chunks\[1\] must be float32"):
+        A.attn_merge([c, c], [good, good.double()])
+    with pytest.raises(ValueError, match=r"lse_chunks\[0\] holds"):
+        A.attn_merge([c, c], [good[:, :1], good])
+    with pytest.raises(ValueError, match="device"):
+        A.attn_merge([c, c], [good, good])

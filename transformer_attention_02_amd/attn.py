@@ -104,9 +104,53 @@ def _dtype_code(dt: torch.dtype) -> int:
     raise TypeError(f"unsupported dtype {dt}")
 
 
-def desc(t: torch.Tensor, dtype_code=None) -> AttnTensor:
+def _dev(t, name: str):
+    """The kernels dereference every pointer on the GPU: host tensors are refused here."""
+    if t is not None and t.numel() and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor, got one on {t.device}")
+    return t
+
+
+def _index(t, name: str):
+    """Sequence offsets, lengths and block tables: int32 and contiguous (the device check comes
+    with the other tensors')."""
+    if t is None:
+        return None
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _lse_buf(lse, rows: int, name: str = "lse"):
+    """A caller's LSE array ([B, H_total, M] fp32, contiguous) with room for the `rows` values a call
+    reads or writes."""
+    if lse is None:
+        return None
+    if lse.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {lse.dtype}")
+    if not lse.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if lse.numel() < rows:
+        raise ValueError(f"{name} holds {lse.numel()} values; the call needs {rows}")
+    return lse
+
+
+def _on_device(**tensors) -> None:
+    for name, t in tensors.items():
+        _dev(t, name)
+
+
+def _ws_bytes(workspace) -> int:
+    _dev(workspace, "workspace")
+    return workspace.numel() * workspace.element_size()
+
+
+def desc(t: torch.Tensor, dtype_code=None, name: str = "tensor") -> AttnTensor:
     """C descriptor of a 4-D [B,M,H,D] or 5-D [B,M,G,H,D] tensor (strides in elements); `dtype_code`
     overrides the code derived from the torch dtype (uint8 INT4 caches are ATTN_DTYPE_INT4X2)."""
+    _dev(t, name)
     d = AttnTensor()
     d.data = t.data_ptr() if t.numel() else None
     d.dtype = _dtype_code(t.dtype) if dtype_code is None else dtype_code
@@ -117,8 +161,9 @@ def desc(t: torch.Tensor, dtype_code=None) -> AttnTensor:
     return d
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream() if stream is None else stream
+def _stream(stream, device=None) -> ctypes.c_void_p:
+    """The caller's stream, else the current stream of the tensors' device."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -142,6 +187,8 @@ def _htot(t: torch.Tensor) -> int:
 def _varlen(seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k=None):
     if seqstart_q is None:
         return None, None
+    _index(seqstart_q, "seqstart_q")
+    _index(seqstart_k, "seqstart_k")
     vl = AttnVarlen()
     vl.seqstart_q = seqstart_q.data_ptr()
     vl.seqstart_k = seqstart_k.data_ptr() if seqstart_k is not None else None
@@ -171,10 +218,12 @@ def _forward(fn, q, k, v, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, out
     elif lse is False:
         lse = None
     vref, _keep = _varlen(seqstart_q, seqstart_k, max_seqlen_q)
-    dq, dk, dv, do = desc(q), desc(k), desc(v), desc(out)
+    _lse_buf(lse, q.shape[0] * _htot(q) * q.shape[1])
+    _on_device(seqstart_q=seqstart_q, seqstart_k=seqstart_k, lse=lse)
+    dq, dk, dv, do = desc(q, name="q"), desc(k, name="k"), desc(v, name="v"), desc(out, name="out")
     cfn, _m, marg = _mask_arg(mask[0], *mask[1:], partial=fn == "partial")
     _check(cfn(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), marg, vref, _scale(scale),
-               ctypes.byref(do), _ptr(lse), _stream(stream)))
+               ctypes.byref(do), _ptr(lse), _stream(stream, q.device)))
     return out, lse
 
 
@@ -198,19 +247,34 @@ def prepare_fwd(q, k, v, out, lse, mask=MASK_NONE, scale=None, seqstart_q=None, 
                 window_right=None) -> Prepared:
     """attn_fwd (or attn_partial, or their _ex forms for windowed masks) marshalled up front."""
     vref, vl = _varlen(seqstart_q, seqstart_k, max_seqlen_q)
-    ds = [desc(q), desc(k), desc(v), desc(out)]
+    _lse_buf(lse, q.shape[0] * _htot(q) * q.shape[1])
+    _on_device(seqstart_q=seqstart_q, seqstart_k=seqstart_k, lse=lse)
+    ds = [desc(q, name="q"), desc(k, name="k"), desc(v, name="v"), desc(out, name="out")]
     cfn, m, marg = _mask_arg(mask, window_size, window_left, window_right, partial)
     args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), marg, vref, _scale(scale),
-            ctypes.byref(ds[3]), _ptr(lse), _stream(stream))
+            ctypes.byref(ds[3]), _ptr(lse), _stream(stream, q.device))
     return Prepared(cfn, args, (ds, vl, m, q, k, v, out, lse))
 
 
 def prepare_decode(q, k, v, num_splits, workspace, out, lse, scale=None, stream=None) -> Prepared:
     """attn_decode_splitkv with every argument marshalled up front."""
-    ds = [desc(q), desc(k), desc(v), desc(out)]
+    _on_device(lse=_lse_buf(lse, q.shape[0] * _htot(q)))
+    ds = [desc(q, name="q"), desc(k, name="k"), desc(v, name="v"), desc(out, name="out")]
     args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), int(num_splits), _scale(scale),
-            _ptr(workspace), workspace.numel(), ctypes.byref(ds[3]), _ptr(lse), _stream(stream))
+            _ptr(workspace), _ws_bytes(workspace), ctypes.byref(ds[3]), _ptr(lse), _stream(stream, q.device))
     return Prepared(_lib.attn_decode_splitkv, args, (ds, q, k, v, workspace, out, lse))
+
+
+def _merge_lses(chunks, lses, lse_out, out):
+    if len(chunks) != len(lses):
+        raise ValueError("out_chunks and lse_chunks differ in length")
+    if not chunks:
+        return
+    rows = chunks[0].shape[0] * _htot(chunks[0]) * chunks[0].shape[1]
+    for i, x in enumerate(lses):
+        _lse_buf(x, rows, f"lse_chunks[{i}]")
+    _lse_buf(lse_out, rows, "lse")
+    _on_device(lse=lse_out, **{f"lse_chunks[{i}]": x for i, x in enumerate(lses)})
 
 
 def prepare_merge(out_chunks, lse_chunks, out, lse=None, stream=None) -> Prepared:
@@ -218,10 +282,11 @@ def prepare_merge(out_chunks, lse_chunks, out, lse=None, stream=None) -> Prepare
     chunks = list(out_chunks.unbind(0)) if isinstance(out_chunks, torch.Tensor) else list(out_chunks)
     lses = list(lse_chunks.unbind(0)) if isinstance(lse_chunks, torch.Tensor) else list(lse_chunks)
     n = len(chunks)
-    descs = (AttnTensor * max(1, n))(*[desc(c) for c in chunks])
+    _merge_lses(chunks, lses, lse, out)
+    descs = (AttnTensor * max(1, n))(*[desc(c, name=f"out_chunks[{i}]") for i, c in enumerate(chunks)])
     lptrs = (ctypes.c_void_p * max(1, n))(*[x.data_ptr() for x in lses])
-    do = desc(out)
-    args = (n, descs, lptrs, ctypes.byref(do), _ptr(lse), _stream(stream))
+    do = desc(out, name="out")
+    args = (n, descs, lptrs, ctypes.byref(do), _ptr(lse), _stream(stream, out.device))
     return Prepared(_lib.attn_merge, args, (descs, lptrs, do, chunks, lses, out, lse))
 
 
@@ -247,8 +312,6 @@ def attn_merge(out_chunks, lse_chunks, out=None, write_lse=True, out_dtype=None,
     """merge_attentions over a list of chunks (or a stacked [S, ...] tensor): returns (out, lse or None)."""
     chunks = list(out_chunks.unbind(0)) if isinstance(out_chunks, torch.Tensor) else list(out_chunks)
     lses = list(lse_chunks.unbind(0)) if isinstance(lse_chunks, torch.Tensor) else list(lse_chunks)
-    if len(chunks) != len(lses):
-        raise ValueError("out_chunks and lse_chunks differ in length")
     n = len(chunks)
     c0 = chunks[0] if n else None
     if out is None and c0 is not None:
@@ -256,10 +319,11 @@ def attn_merge(out_chunks, lse_chunks, out=None, write_lse=True, out_dtype=None,
     lse = None
     if write_lse and c0 is not None:
         lse = torch.empty((c0.shape[0], _htot(c0), c0.shape[1]), dtype=torch.float32, device=c0.device)
-    descs = (AttnTensor * max(1, n))(*[desc(c) for c in chunks])
+    _merge_lses(chunks, lses, lse, out)
+    descs = (AttnTensor * max(1, n))(*[desc(c, name=f"out_chunks[{i}]") for i, c in enumerate(chunks)])
     lptrs = (ctypes.c_void_p * max(1, n))(*[x.data_ptr() for x in lses])
-    _check(_lib.attn_merge(n, descs, lptrs, ctypes.byref(desc(out)) if out is not None else None, _ptr(lse),
-                           _stream(stream)))
+    _check(_lib.attn_merge(n, descs, lptrs, ctypes.byref(desc(out, name="out")) if out is not None else None,
+                           _ptr(lse), _stream(stream, out.device if out is not None else None)))
     return out, lse
 
 
@@ -278,19 +342,25 @@ def attn_decode_splitkv(q, k, v, num_splits, scale=None, workspace=None, out=Non
     need = attn_decode_workspace_bytes(q.shape[0], _htot(q), q.shape[-1], num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check(_lib.attn_decode_splitkv(ctypes.byref(desc(q)), ctypes.byref(desc(k)), ctypes.byref(desc(v)),
-                                    int(num_splits), _scale(scale), _ptr(workspace), workspace.numel(),
-                                    ctypes.byref(desc(out)), _ptr(lse), _stream(stream)))
+    _on_device(lse=_lse_buf(lse, q.shape[0] * _htot(q)))
+    _check(_lib.attn_decode_splitkv(ctypes.byref(desc(q, name="q")), ctypes.byref(desc(k, name="k")),
+                                    ctypes.byref(desc(v, name="v")), int(num_splits), _scale(scale),
+                                    _ptr(workspace), _ws_bytes(workspace), ctypes.byref(desc(out, name="out")),
+                                    _ptr(lse), _stream(stream, q.device)))
     return out, lse
 
 
 def _paged_args(q, k, v, seqlens, block_tables, page_size, max_seqlen_k, num_splits, scale, workspace, out, lse,
                 stream):
-    ds = [desc(q), desc(k), desc(v), desc(out)]
+    _index(seqlens, "seqlens")
+    _index(block_tables, "block_tables")
+    _lse_buf(lse, q.shape[0] * _htot(q))
+    _on_device(seqlens=seqlens, block_tables=block_tables, lse=lse)
+    ds = [desc(q, name="q"), desc(k, name="k"), desc(v, name="v"), desc(out, name="out")]
     mb = block_tables.shape[1] if block_tables is not None else 0
     args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), _ptr(seqlens), _ptr(block_tables),
             int(mb), int(page_size or 0), int(max_seqlen_k), int(num_splits), _scale(scale), _ptr(workspace),
-            workspace.numel(), ctypes.byref(ds[3]), _ptr(lse), _stream(stream))
+            _ws_bytes(workspace), ctypes.byref(ds[3]), _ptr(lse), _stream(stream, q.device))
     return args, ds
 
 
@@ -322,12 +392,17 @@ def prepare_decode_paged(q, k, v, seqlens, num_splits, max_seqlen_k, workspace, 
 
 def _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k, num_splits,
               scale, workspace, out, lse, stream, kv_code=None):
-    ds = [desc(q), desc(k, kv_code), desc(v, kv_code), desc(k_scale_shift), desc(v_scale_shift), desc(out)]
+    _index(seqlens, "seqlens")
+    _index(block_tables, "block_tables")
+    _lse_buf(lse, q.shape[0] * _htot(q))
+    _on_device(seqlens=seqlens, block_tables=block_tables, lse=lse)
+    ds = [desc(q, name="q"), desc(k, kv_code, "k"), desc(v, kv_code, "v"), desc(k_scale_shift, name="k_scale_shift"),
+          desc(v_scale_shift, name="v_scale_shift"), desc(out, name="out")]
     mb = block_tables.shape[1] if block_tables is not None else 0
     args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), ctypes.byref(ds[3]), ctypes.byref(ds[4]),
             _ptr(seqlens), _ptr(block_tables), int(mb), int(page_size or 0), int(max_seqlen_k or 0),
-            int(num_splits), _scale(scale), _ptr(workspace), workspace.numel(), ctypes.byref(ds[5]), _ptr(lse),
-            _stream(stream))
+            int(num_splits), _scale(scale), _ptr(workspace), _ws_bytes(workspace), ctypes.byref(ds[5]), _ptr(lse),
+            _stream(stream, q.device))
     return args, ds
 
 
@@ -367,12 +442,15 @@ def attn_bwd_workspace_bytes(B: int, H_total: int, Mq: int) -> int:
 
 def _bwd_args(dout, q, k, v, out, lse, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k,
               window_size, window_left, window_right, workspace, dq, dk, dv, stream):
+    _lse_buf(lse, q.shape[0] * _htot(q) * q.shape[1])
     vref, vl = _varlen(seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k)
+    _on_device(lse=lse, seqstart_q=seqstart_q, seqstart_k=seqstart_k)
     m = AttnMask(int(mask), int(window_size or 0), int(window_left or 0), int(window_right or 0))
-    ds = [desc(x) for x in (dout, q, k, v, out, dq, dk, dv)]
+    ds = [desc(x, name=n) for x, n in ((dout, "dout"), (q, "q"), (k, "k"), (v, "v"), (out, "out"), (dq, "dq"),
+                                        (dk, "dk"), (dv, "dv"))]
     args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), ctypes.byref(ds[3]), ctypes.byref(ds[4]),
-            _ptr(lse), ctypes.byref(m), vref, _scale(scale), _ptr(workspace), workspace.numel(),
-            ctypes.byref(ds[5]), ctypes.byref(ds[6]), ctypes.byref(ds[7]), _stream(stream))
+            _ptr(lse), ctypes.byref(m), vref, _scale(scale), _ptr(workspace), _ws_bytes(workspace),
+            ctypes.byref(ds[5]), ctypes.byref(ds[6]), ctypes.byref(ds[7]), _stream(stream, q.device))
     return args, (ds, vl, m)
 
 
