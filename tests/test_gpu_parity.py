@@ -273,6 +273,73 @@ def test_expanded_gqa_equals_repeated_heads(A):
 
 # ------------------------------------------------------------------ degenerate cases
 
+def _climbing_scores(seed, M, D=128, H=3):
+    """bf16 q/k/v [1, M, H, D] whose scaled scores are 0.1 * j (+ small noise) along the keys j in
+    head 0 (every 64-key tile raises each row's maximum by ~6.4, more than 2^8 in base 2),
+    0.1 * (M - 1 - j) in head 1 (the first keys hold every maximum) and plain N(0,1) in head 2."""
+    scale = 1.0 / math.sqrt(D)
+    q = synth.normal(seed, synth.TAG_Q, (1, M, H, D)) * np.float32(0.3)
+    k = synth.normal(seed, synth.TAG_K, (1, M, H, D)) * np.float32(0.3)
+    v = synth.normal(seed, synth.TAG_V, (1, M, H, D))
+    j = np.arange(M, dtype=np.float32)
+    q[:, :, :2, 0] = 8.0
+    k[0, :, 0, 0] = 0.1 * j / (8.0 * scale)
+    k[0, :, 1, 0] = 0.1 * (M - 1 - j) / (8.0 * scale)
+    q[:, :, 2], k[:, :, 2] = q[:, :, 2] / np.float32(0.3), k[:, :, 2] / np.float32(0.3)
+    return tuple(synth.f32_to_bf16_bits(x) for x in (q, k, v))
+
+
+def test_climbing_and_falling_row_maxima(A):
+    """Row maxima that grow on every key tile (the forward's running reference is raised and O, l
+    rescaled tile after tile), that sit in the first tile, and plain ones: forward (causal and
+    unmasked), two partials and their merge, and the split-KV decode of the last row, all against
+    the oracle on the same bf16 values.  Scores reach ~100, so fp32 accumulation error stays far
+    below the LSE bound."""
+    say("case: climbing / falling row maxima, [1,1024,3,128] bf16")
+    M = 1024
+    qh, kh, vh = _climbing_scores(900, M)
+    q, k, v = dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16")
+    for mask in (A.MASK_CAUSAL, A.MASK_NONE):
+        out, lse = A.attn_fwd(q, k, v, mask=mask)
+        torch.cuda.synchronize()
+        oo, ol = run_oracle(qh, kh, vh, mask, "bf16")
+        assert ol[0, 0, -1] > 90 and ol[0, 1, -1] > 90, "scores are not in the intended range"
+        check(out, lse, oo, ol, TOL_BF16_OUT, TOL_LSE, f"forward mask={mask}")
+    h = M // 2
+    p1 = A.attn_partial(q, k[:, :h], v[:, :h])
+    p2 = A.attn_partial(q, k[:, h:], v[:, h:])
+    mo, ml = A.attn_merge([p1[0], p2[0]], [p1[1], p2[1]], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check(mo, ml, oo, ol, TOL_BF16_OUT, TOL_LSE, "two partials + merge")
+    do, dl = A.attn_decode_splitkv(q[:, -1:].contiguous(), k, v, 8)
+    torch.cuda.synchronize()
+    check(do, dl, oo[:, -1:], ol[:, :, -1:], TOL_BF16_OUT, TOL_LSE, "decode of the last row, 8 splits")
+    # The backward recomputes P from the saved LSE at these magnitudes.  Its D = dout.out comes
+    # from the bf16 out it is given, and in heads 0 and 1 the keys share a component of up to
+    # ~145, which multiplies D's rounding into dq (dq_i holds scale * D_i * sum_j P_ij k_j,
+    # which cancels only for exact D).  The oracle measures that sensitivity itself: its
+    # gradients with out rounded to bf16 against those with the exact out.  The bound adds
+    # three times that change (the GPU's out also carries the forward's own error, about one
+    # bf16 half-ulp here) to the usual bf16 gradient tolerance.
+    gh = synth.normal(900, 3, (1, M, 3, 128), "bf16")
+    out, lse = A.attn_fwd(q, k, v, mask=A.MASK_CAUSAL)
+    dq, dk, dv = A.attn_bwd(dev(gh, "bf16"), q, k, v, out, lse, mask=A.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    q64, k64, v64, g64 = (synth.to_f64(x, "bf16") for x in (qh, kh, vh, gh))
+    oo, ol = oracle.attention(q64, k64, v64, mask=1)
+    ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, mask=1)
+    o_bf16 = synth.to_f64(synth.f32_to_bf16_bits(oo.astype(np.float32)), "bf16")
+    ref_b = oracle.attention_backward(g64, o_bf16, ol, q64, k64, v64, mask=1)
+    for name, got, r, rb in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, ref_b):
+        for h in range(3):
+            err, mag = maxerr(host64(got[:, :, h]), r[:, :, h]), float(np.abs(r[:, :, h]).max())
+            sens = float(np.abs(r[:, :, h] - rb[:, :, h]).max())
+            say(f"  climbing maxima bwd {name} head {h}: max|d|={err:.3e} max|ref|={mag:.3e} "
+                f"bf16-out sensitivity={sens:.3e}")
+            assert err <= TOL_BWD_REL * mag + TOL_BWD_ABS + 3 * sens, f"{name} head {h}: error {err}"
+    assert float(np.abs(ref[0][:, :, 2] - ref_b[0][:, :, 2]).max()) < 0.01  # the plain head is well conditioned
+
+
 def test_empty_shard_and_no_lse(A):
     say("case: empty shard, lse=None, Mq=0")
     qh, kh, vh = synth.qkv(500, (1, 37, 2, 128), (1, 50, 2, 128), (1, 50, 2, 128), "bf16")
