@@ -563,7 +563,7 @@ def main():
                                        "roofline": {"bound": "latency", "achieved": round(tf1, 4),
                                                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                                                     "frac": round(tf1 / PEAK_FP32_TFLOPS, 6),
-                                                    "note": "fp32 vector peak, for information: 4 workgroups"}}
+                                                    "note": "fp32 vector peak, for information: 16 workgroups"}}
         log(f"fp32 tiny: {ms_1 * 1e3:.1f} us/call")
         if not args.no_cpu:
             qo1, ko1, vo1 = (synth.to_f64(x, "f32") for x in (qh1, kh1, vh1))
