@@ -1,6 +1,6 @@
 """Benchmark of the fused attention forward path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows prefill,decode,varlen,merge,fp32] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows full,bwd,decode,varlen,window,merge,fp32] [--no-cpu]
 
 A step is one attn_fwd call on the causal bf16 prefill workload B=2, M=2048,
 H=32, K=Kv=128 (the pages' Quick-start shape), inputs resident in HBM.  The
@@ -40,8 +40,8 @@ def parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=300,
                    help="untimed steps first; ~25 ms of back-to-back launches brings the clock to steady state")
-    p.add_argument("--rows", default="bwd,decode,varlen,window,merge,fp32",
-                   help="rows timed after the headline prefill: bwd,decode,varlen,window,merge,fp32,copy or none; "
+    p.add_argument("--rows", default="full,bwd,decode,varlen,window,merge,fp32",
+                   help="rows timed after the headline prefill: full,bwd,decode,varlen,window,merge,fp32,copy or none; "
                         "copy is a plain 1 GiB device copy used to calibrate the HBM byte counters")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--rocpd", metavar="DB", help="summarise a rocprofv3 results database (kernel durations and "
@@ -302,6 +302,20 @@ def main():
                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                           "traffic": recorded_traffic("fwd_bf16 causal 2x2048x32x128"),
                           "kernel": "fwd_bf16_kernel<128,128,8,4,false>", "flops_per_launch": flops}
+
+    # the same shape without a mask: the kernel's steady state, free of the causal diagonal
+    if "full" in rows:
+        of = torch.empty_like(q)
+        ms_f = timed(A.prepare_fwd(q, k, v, of, lse, mask=A.MASK_NONE), 100, 20, torch)
+        fl_f = 2.0 * flops
+        tf_f = fl_f / (ms_f * 1e-3) / 1e12
+        log(f"prefill unmasked bf16 [2,2048,32,128]: {ms_f * 1e3:.1f} us/call, {tf_f:.1f} TFLOP/s")
+        result["rows"]["prefill_unmasked"] = {
+            "workload": "bf16 B=2 M=2048 H=32 K=Kv=128, no mask (the headline shape without the causal diagonal)",
+            "ms_per_call": round(ms_f, 5), "value": round(tf_f, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf_f, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf_f / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_f}}
+        del of
 
     # ------------------------------------------------------------ CPU baseline: the oracle on the same workload
     if not args.no_cpu:
