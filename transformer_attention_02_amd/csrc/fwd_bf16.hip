@@ -168,6 +168,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const int qrow = wrow0 + l32;        // this lane's query row (local to the sequence)
     const int klo = clampk((int64_t)qrow + shift - a.wl, 0, Lk);       // this row's visible keys
     const int khi = clampk((int64_t)qrow + shift + a.wr, -1, Lk - 1);  // (empty when khi < klo)
+    // both bounds are non-decreasing in the row: the wave's last row has the largest lower
+    // bound, its first row the smallest upper bound
+    const int klo_w = clampk((int64_t)wrow0 + 31 + shift - a.wl, 0, Lk);
+    const int khi_w = clampk((int64_t)wrow0 + shift + a.wr, -1, Lk - 1);
     float c = a.scale_log2;
     const unsigned qflip = c < 0.f ? 0x80008000u : 0u;  // negative scale: negate q, keep c > 0
     c = fabsf(c);
@@ -245,11 +249,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
             sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], sb, 0, 0, 0);
         }
         if (MASKED) {
+            // element r of sa holds key kt0 + 4 hh + off(r), of sb 32 keys later; only the bounds
+            // that cut this tile for some row of the wave are tested
+            const int dlo = klo - kt0 - 4 * hh, dhi = khi - kt0 - 4 * hh;
+            const bool cut_lo = kt0 < klo_w, cut_hi = kt0 + BN - 1 > khi_w;
+            if (cut_lo && cut_hi) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kt0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                if (key < klo || key > khi) sa[r] = -INFINITY;
-                if (key + 32 < klo || key + 32 > khi) sb[r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    if (off < dlo || off > dhi) sa[r] = -INFINITY;
+                    if (off + 32 < dlo || off + 32 > dhi) sb[r] = -INFINITY;
+                }
+            } else if (cut_hi) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    if (off > dhi) sa[r] = -INFINITY;
+                    if (off + 32 > dhi) sb[r] = -INFINITY;
+                }
+            } else if (cut_lo) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    if (off < dlo) sa[r] = -INFINITY;
+                    if (off + 32 < dlo) sb[r] = -INFINITY;
+                }
             }
         }
         // row maximum of the raw scores (c > 0), pairwise to keep dependency chains short
