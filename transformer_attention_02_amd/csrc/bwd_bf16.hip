@@ -180,6 +180,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
     }
     const int qlo = clampk((int64_t)key - shift - a.wr, 0, Lq);
     const int qhi = clampk((int64_t)key - shift + a.wl, -1, Lq - 1);
+    // both are non-decreasing in the key: the pair's last key has the largest lower bound, its
+    // first key the smallest upper bound
+    const int qlo_w = clampk((int64_t)kw0 + 31 - shift - a.wr, 0, Lq);
+    const int qhi_w = clampk((int64_t)kw0 - shift + a.wl, -1, Lq - 1);
     const float c = a.scale_log2;
 
     int raddr[KS];
@@ -226,16 +230,34 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
                         const int row = qb * 32 + 8 * g + 4 * hh;
                         const f32x4 l2 = *(const f32x4 LDS_AS *)(ls + row);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x[4 * g + j], c, -l2[j]));
-                            if (MASKED) {
-                                const int q = q0 + row + j;
-                                if (q < qlo || q > qhi) pr = 0.f;
-                            }
-                            p[4 * g + j] = pr;
-                        }
-                        *(f32x4 LDS_AS *)(pxb + g * 256) = f32x4{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+                        for (int j = 0; j < 4; ++j)
+                            p[4 * g + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[4 * g + j], c, -l2[j]));
                     }
+                    if (MASKED) {
+                        // element 4g + j is query q0 + 32 qb + 4 hh + 8g + j; only the bounds that
+                        // cut this block for one of the pair's keys are tested
+                        const int qb0 = q0 + qb * 32;
+                        const int dlo = qlo - qb0 - 4 * hh, dhi = qhi - qb0 - 4 * hh;
+                        const bool cut_lo = qb0 < qlo_w, cut_hi = qb0 + 31 > qhi_w;
+                        if (cut_lo && cut_hi) {
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) {
+                                const int off = 8 * (e >> 2) + (e & 3);
+                                if (off < dlo || off > dhi) p[e] = 0.f;
+                            }
+                        } else if (cut_hi) {
+#pragma unroll
+                            for (int e = 0; e < 16; ++e)
+                                if (8 * (e >> 2) + (e & 3) > dhi) p[e] = 0.f;
+                        } else if (cut_lo) {
+#pragma unroll
+                            for (int e = 0; e < 16; ++e)
+                                if (8 * (e >> 2) + (e & 3) < dlo) p[e] = 0.f;
+                        }
+                    }
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *(f32x4 LDS_AS *)(pxb + g * 256) = f32x4{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -376,6 +398,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
     const int qrow = wrow0 + l32;
     const int klo = clampk((int64_t)qrow + shift - a.wl, 0, Lk);
     const int khi = clampk((int64_t)qrow + shift + a.wr, -1, Lk - 1);
+    // non-decreasing in the row: the wave's last row has the largest lower bound, its first
+    // row the smallest upper bound
+    const int klo_w = clampk((int64_t)wrow0 + 31 + shift - a.wl, 0, Lk);
+    const int khi_w = clampk((int64_t)wrow0 + shift + a.wr, -1, Lk - 1);
     bf16x8 qf[KS], gf[KS];
     float l2 = INFINITY, dd = 0.f;
     if (qrow < Lq) {
@@ -447,16 +473,34 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[k], dp, 0, 0, 0);
             }
+            float pr[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
+            if (MASKED) {
+                // element r is key kt0 + 32 kb + 4 hh + off(r); only the bounds that cut this block
+                // for one of the wave's rows are tested
+                const int kb0 = kt0 + kb * 32;
+                const int dlo = klo - kb0 - 4 * hh, dhi = khi - kb0 - 4 * hh;
+                const bool cut_lo = kb0 < klo_w, cut_hi = kb0 + 31 > khi_w;
+                if (cut_lo && cut_hi) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = 8 * (r >> 2) + (r & 3);
+                        if (off < dlo || off > dhi) pr[r] = 0.f;
+                    }
+                } else if (cut_hi) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (8 * (r >> 2) + (r & 3) > dhi) pr[r] = 0.f;
+                } else if (cut_lo) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (8 * (r >> 2) + (r & 3) < dlo) pr[r] = 0.f;
+                }
+            }
             float ds[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
-                if (MASKED) {
-                    const int kk = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (kk < klo || kk > khi) pr = 0.f;
-                }
-                ds[r] = pr * (dp[r] - dd);
-            }
+            for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (dp[r] - dd);
             bf16x8 dsb[2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
