@@ -289,6 +289,28 @@ def _climbing_scores(seed, M, D=128, H=3):
     return tuple(synth.f32_to_bf16_bits(x) for x in (q, k, v))
 
 
+@pytest.mark.parametrize("K,Kv", [(50, 30), (100, 128), (128, 36), (17, 64)])
+def test_fp32_odd_head_dims(A, K, Kv):
+    """fp32 forward with head dims that are not multiples of 4 or 16 (rows padded to a 16-byte
+    stride, as the ABI requires): every output and LSE within 1e-5, three masks."""
+    say(f"case: fp32 forward K={K} Kv={Kv}")
+    B, Mq, Mkv, H = 2, 77, 93, 3
+    qh, kh, vh = synth.qkv(1200 + K, (B, Mq, H, K), (B, Mkv, H, K), (B, Mkv, H, Kv), "f32")
+    pad = lambda x: (x.shape[-1] + 3) // 4 * 4
+
+    def up(x):
+        t = torch.zeros(*x.shape[:-1], pad(x), dtype=torch.float32, device="cuda")
+        t[..., :x.shape[-1]] = dev(x, "f32")
+        return t[..., :x.shape[-1]]
+    q, k, v = up(qh), up(kh), up(vh)
+    out = torch.zeros(B, Mq, H, pad(vh), dtype=torch.float32, device="cuda")[..., :Kv]
+    for mask, kw, okw in [(0, {}, {}), (4, {}, {}), (7, {"window_size": 20}, {"window": 20})]:
+        o, lse = A.attn_fwd(q, k, v, mask=mask, scale=0.13, out=out, **kw)
+        torch.cuda.synchronize()
+        oo, ol = run_oracle(qh, kh, vh, mask, "f32", scale=0.13, **okw)
+        check(o, lse, oo, ol, TOL_F32, TOL_F32, f"K={K} Kv={Kv} mask={mask}")
+
+
 def test_climbing_and_falling_row_maxima(A):
     """Row maxima that grow on every key tile (the forward's running reference is raised and O, l
     rescaled tile after tile), that sit in the first tile, and plain ones: forward (causal and
