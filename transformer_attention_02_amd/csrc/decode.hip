@@ -84,12 +84,28 @@ __device__ __forceinline__ void unpack_fp8(const u32x4 &w, float *x) {
     }
 }
 
-// Sum over the LPK consecutive lanes of a lane group.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the LPK consecutive lanes of a lane group.  Groups of 4, 8 and 16 lanes use DPP
+// (no LDS round trip): each step adds a lane's value to its partner's under a pairing that is
+// its own inverse (rotate by 8 in a 16-lane row, which is lane xor 8; mirror within 8 lanes;
+// xor 2 and xor 1 inside quads), so every lane of the group ends with the same bits.
 template <int LPK>
 __device__ __forceinline__ float lane_group_sum(float x) {
+    if constexpr (LPK == 4 || LPK == 8 || LPK == 16) {
+        if constexpr (LPK == 16) x = dpp_add<0x128>(x);  // row_ror:8
+        if constexpr (LPK >= 8) x = dpp_add<0x141>(x);   // row_half_mirror
+        x = dpp_add<0x4E>(x);                            // quad_perm [2, 3, 0, 1]
+        x = dpp_add<0xB1>(x);                            // quad_perm [1, 0, 3, 2]
+        return x;
+    } else {
 #pragma unroll
-    for (int o = LPK / 2; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+        for (int o = LPK / 2; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+        return x;
+    }
 }
 
 // 32 unsigned 4-bit codes (element 2i in the low nibble of byte i) to fp32; exact.  The masked
