@@ -277,6 +277,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         vslane = (uint32_t)((head_offset(a.svss, hf, a.Hin) - head_offset(a.svss, hf0, a.Hin) + gw) * 2 + rs * vsstr);
     }
 
+    // byte distance between row slot 0 of consecutive rows of a lane (RPP rows apart)
+    const int64_t kstep = RPP * kstr, vstep = RPP * vstr, ksstep = RPP * ksstr, vsstep = RPP * vsstr;
     for (int sub0 = j0; sub0 < j1; sub0 += (MODE == 2 ? SUB : a.chunk)) {
         const int n = MODE == 2 ? min(SUB, j1 - sub0) : j1 - sub0;
         if (MODE == 2) {
@@ -295,6 +297,24 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         // lane's part a 32-bit byte offset, so address arithmetic stays on the scalar unit.
         auto load = [&](int p, auto full_tag) __attribute__((always_inline)) {
             constexpr bool FULL = decltype(full_tag)::value;
+            if constexpr (QUANT && MODE != 2 && FULL) {
+                // quantised caches: the round's uniform row bases (row slot 0 of its first row) are
+                // formed once, and each row adds a uniform step and the lanes' 32-bit offsets
+                // (FP8 and INT4 4-6% faster than per-row bases; bf16 1% slower, so it keeps those)
+                if (a.lane32) {
+                    const int64_t r0 = sub0 + p;
+                    const char *kr = kbase + r0 * kstr, *vr = vbase + r0 * vstr;
+                    const char *ksr = ksbase + r0 * ksstr, *vsr = vsbase + r0 * vsstr;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        wk[u] = *(const u32x4 *)(kr + u * kstep + klane);
+                        wv[u] = *(const u32x4 *)(vr + u * vstep + vlane);
+                        sk[u] = *(const uint32_t *)(ksr + u * ksstep + kslane);
+                        sv[u] = *(const uint32_t *)(vsr + u * vsstep + vslane);
+                    }
+                    return;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int r = p + u * RPP + rs;
