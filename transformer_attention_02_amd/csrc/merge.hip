@@ -9,9 +9,11 @@
 // One workgroup per row.  The value dimension is read by 8 chunk groups of 32
 // lanes, each lane taking 4 consecutive elements of every 8th chunk, with all of
 // a lane's loads issued first (before the LSEs are even reduced).  Threads c < S
-// read the S LSEs and the workgroup reduces them to L; the weights go to LDS,
-// and the 8 weighted partial sums are added through LDS.  Memory-bound: every chunk element
-// is read once and every output element written once.
+// read the S LSEs and reduce them to L (wave 0 alone when S <= 64, one barrier);
+// the weights go to LDS, and the 8 weighted partial sums are added through LDS.
+// The kernel is instantiated for 1, 2, 4, 8 or 16 chunks per lane, so a merge of few
+// chunks holds few registers and keeps more rows in flight.  Memory-bound: every chunk
+// element is read once and every output element written once.
 #include "kernels.h"
 
 namespace attn {
@@ -54,6 +56,9 @@ __device__ __forceinline__ f32x4 load4(const void *base, int64_t off, int d, int
     return x;
 }
 
+// MAXP: chunks per lane and pass (ceil(S / GROUPS), rounded up to a power of two), so that small
+// merges hold few registers and keep more rows in flight
+template <int MAXP>
 __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
     __shared__ float red[4];
     __shared__ float w_s[kMaxChunks];
@@ -72,20 +77,49 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
     // the LSE reduction, so that a row costs one memory round trip when Kv <= SPAN
     const int g = tid / (SPAN / 4), j = tid % (SPAN / 4);
     const bool f32 = a.chunk_f32;
-    f32x4 x[MAXPER];
+    f32x4 x[MAXP];
     auto load_pass = [&](int d0) __attribute__((always_inline)) {
         const int d = d0 + 4 * j;
 #pragma unroll
-        for (int i = 0; i < MAXPER; ++i) {
+        for (int i = 0; i < MAXP; ++i) {
             const int c = g + GROUPS * i;
             x[i] = c < a.S ? load4(a.chunk[c], coff, d, a.Kv, f32) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
     load_pass(0);
 
-    const float lv = tid < a.S ? a.lse[tid][loff] : -INFINITY;
-    const float mx = block_reduce(lv, red, true);
-    if (mx == -INFINITY) {  // every chunk empty (uniform branch)
+    float L;
+    if (a.S <= 64) {
+        // every LSE sits in wave 0: it forms the weights alone, and one barrier publishes them
+        if (tid < 64) {
+            const float lv = tid < a.S ? a.lse[tid][loff] : -INFINITY;
+            float mx = lv;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+            float Lw = -INFINITY;
+            if (mx != -INFINITY) {
+                float e = tid < a.S ? expf(lv - mx) : 0.f;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) e += __shfl_xor(e, o, 64);
+                Lw = mx + logf(e);
+                if (tid < a.S) w_s[tid] = expf(lv - Lw);
+            }
+            if (tid == 0) red[0] = Lw;
+        }
+        __syncthreads();
+        L = red[0];
+    } else {
+        const float lv = tid < a.S ? a.lse[tid][loff] : -INFINITY;
+        const float mx = block_reduce(lv, red, true);
+        L = -INFINITY;
+        if (mx != -INFINITY) {
+            const float sum = block_reduce(tid < a.S ? expf(lv - mx) : 0.f, red, false);
+            L = mx + logf(sum);
+            if (tid < a.S) w_s[tid] = expf(lv - L);
+            __syncthreads();
+        }
+    }
+    if (L == -INFINITY) {  // every chunk empty (uniform)
         for (int d = tid; d < a.Kv; d += NT) {
             if (a.out_f32) ((float *)a.o)[ooff + d] = 0.f;
             else ((__bf16 *)a.o)[ooff + d] = (__bf16)0.f;
@@ -93,17 +127,13 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
         if (a.lse_out && tid == 0) a.lse_out[loff] = -INFINITY;
         return;
     }
-    const float sum = block_reduce(tid < a.S ? expf(lv - mx) : 0.f, red, false);
-    const float L = mx + logf(sum);
-    if (tid < a.S) w_s[tid] = expf(lv - L);
     if (a.lse_out && tid == 0) a.lse_out[loff] = L;
-    __syncthreads();
 
     for (int d0 = 0; d0 < a.Kv; d0 += SPAN) {
         if (d0 > 0) load_pass(d0);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < MAXPER; ++i) {
+        for (int i = 0; i < MAXP; ++i) {
             const int c = g + GROUPS * i;
             if (c < a.S) acc += w_s[c] * x[i];
         }
@@ -129,7 +159,12 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t stream) {
     const int64_t rows = (int64_t)a.B * a.M * a.Htot;
     if (rows <= 0) return hipSuccess;
     if (rows > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, a);
+    const int per = (a.S + GROUPS - 1) / GROUPS;
+    if (per <= 1) hipLaunchKernelGGL(merge_kernel<1>, dim3((unsigned)rows), dim3(NT), 0, stream, a);
+    else if (per <= 2) hipLaunchKernelGGL(merge_kernel<2>, dim3((unsigned)rows), dim3(NT), 0, stream, a);
+    else if (per <= 4) hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)rows), dim3(NT), 0, stream, a);
+    else if (per <= 8) hipLaunchKernelGGL(merge_kernel<8>, dim3((unsigned)rows), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL(merge_kernel<MAXPER>, dim3((unsigned)rows), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
