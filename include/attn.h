@@ -43,7 +43,7 @@
  *     written; attn_last_error() gives the reason (thread-local).
  *     ATTN_ERR_INVALID_ARGUMENT: inconsistent shapes, dtypes, strides,
  *       alignment, null pointers, bad counts.
- *     ATTN_ERR_UNSUPPORTED: a valid request this build has no kernel for.
+ *     ATTN_ERR_UNSUPPORTED: a valid request the library has no kernel for.
  *     ATTN_ERR_WORKSPACE_TOO_SMALL: workspace_bytes below the requirement.
  *     ATTN_ERR_LAUNCH: the HIP runtime refused the launch.
  */
