@@ -67,15 +67,18 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// NW waves (32 query rows each) per workgroup; STAGES-deep LDS ring of K/V tiles; KD and VD
-// are the head dims of q/k and of v/out.
-template <int KD, int VD, int NW, int STAGES, bool OUT_F32>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
+// NW waves per workgroup; STAGES-deep LDS ring of K/V tiles; KD and VD are the head dims of
+// q/k and of v/out.  KSPLIT waves share each 32-row block: with KSPLIT = 2 (and the paired ring)
+// wave 2i takes the first tile of every resident pair and wave 2i + 1 the second, and their
+// softmax states are merged exactly at the end.
+template <int KD, int VD, int NW, int STAGES, bool OUT_F32, int KSPLIT>
+__device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     constexpr int NT = NW * 64;                  // threads per workgroup
-    constexpr int BM = NW * 32;                  // query rows per workgroup
+    constexpr int BM = NW / KSPLIT * 32;         // query rows per workgroup
     static_assert(STAGES == 3 || STAGES == 4, "the unrolled tile loop names three or four LDS stages");
     // STAGES == 4: the ring is filled two tiles at a time, with one wait + barrier per two tiles
     constexpr bool PAIRS = STAGES == 4;
+    static_assert(KSPLIT == 1 || (KSPLIT == 2 && PAIRS), "split keys need the paired ring");
     constexpr int KROWB = KD * 2, VROWB = VD * 2;    // bytes per K / V tile row
     constexpr int KCPR = KD / 8, VCPR = VD / 8;      // 16-byte chunks per row
     constexpr int KTILE = BN * KROWB, VTILE = BN * VROWB;
@@ -164,7 +167,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     };
 
     // ---- Q^T fragments (B operand), resident for the whole kernel
-    const int wrow0 = row0 + wave * 32;  // first local row of this wave
+    const int wsub = wave % KSPLIT;                // which tile of each pair this wave takes (KSPLIT = 2)
+    const int wrow0 = row0 + wave / KSPLIT * 32;  // first local row of this wave
     const int qrow = wrow0 + l32;        // this lane's query row (local to the sequence)
     const int klo = clampk((int64_t)qrow + shift - a.wl, 0, Lk);       // this row's visible keys
     const int khi = clampk((int64_t)qrow + shift + a.wr, -1, Lk - 1);  // (empty when khi < klo)
@@ -232,6 +236,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
             else wait_barrier<0>();
             if (t + 2 < te) issue(t + 2);
         }
+        // split keys: the other wave of the block takes this tile
+        if (KSPLIT > 1 && ((STAGE_C >= 0 ? STAGE_C : (t - tb)) & 1) != wsub) return;
         // the whole tile lies before or after every window of this wave's 32 rows
         if (MASKED && ((int64_t)kt0 + BN - 1 < (int64_t)wrow0 + shift - a.wl ||
                        (int64_t)kt0 > (int64_t)wrow0 + 31 + shift + a.wr))
@@ -350,6 +356,35 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     for (; t < ub; ++t) step(t, std::false_type{}, SR{});
     for (; t < te; ++t) step(t, std::true_type{}, SR{});  // diagonal / right edge / key tail
 
+    if constexpr (KSPLIT == 2) {
+        // exact merge of the two waves' states of a block: the second wave leaves its (o, m, l)
+        // in LDS (the ring is free once both waves are past the loop), the first rescales both
+        // to the larger reference and adds them
+        constexpr int REC = MB * 16 + 2;
+        float *rec = (float *)smem + ((wave / 2) * 64 + lane) * REC;
+        __syncthreads();
+        if (wsub == 1) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) rec[16 * i + r] = o[i][r];
+            rec[MB * 16] = m_ref;
+            rec[MB * 16 + 1] = l_run;
+        }
+        __syncthreads();
+        if (wsub == 1) return;
+        const float m2 = rec[MB * 16], l2 = rec[MB * 16 + 1];
+        const float mm = fmaxf(m_ref, m2);
+        const float mu = mm == -INFINITY ? 0.f : mm;
+        const float a1 = __builtin_amdgcn_exp2f(m_ref - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[i][r] = o[i][r] * a1 + rec[16 * i + r] * a2;
+        l_run = l_run * a1 + l2 * a2;
+        m_ref = mm;
+    }
+
     // ---- normalise and store
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -378,13 +413,28 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 }
 
 template <int KD, int VD, int NW, int STAGES, bool OUT_F32>
+__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
+    fwd_bf16_body<KD, VD, NW, STAGES, OUT_F32, 1>(a);
+}
+
+// two waves per 32-row block, splitting its keys (paired ring)
+template <int KD, int VD, bool OUT_F32>
+__global__ __launch_bounds__(128) void fwd_bf16_split_kernel(FwdArgs a) {
+    fwd_bf16_body<KD, VD, 2, 4, OUT_F32, 2>(a);
+}
+
+template <int KD, int VD, int NW, int STAGES, bool OUT_F32, int KSPLIT = 1>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
-    constexpr int BM = NW * 32;
+    constexpr int BM = NW / KSPLIT * 32;
     const int64_t tiles = (a.max_seqlen_q + BM - 1) / BM;
     const int64_t grid = tiles * a.nseq * (int64_t)a.B * a.Htot;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_bf16_kernel<KD, VD, NW, STAGES, OUT_F32>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
+    if constexpr (KSPLIT == 2)
+        hipLaunchKernelGGL((fwd_bf16_split_kernel<KD, VD, OUT_F32>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<KD, VD, NW, STAGES, OUT_F32>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
+                           a);
     return hipGetLastError();
 }
 
@@ -406,7 +456,8 @@ hipError_t launch_nw(const FwdArgs &a, hipStream_t stream) {
     if (grid(256) >= FWD_MIN_GRID) return launch<KD, VD, 8, 4, OUT_F32>(a, stream);
     if (grid(128) >= FWD_MIN_GRID) return launch<KD, VD, 4, 3, OUT_F32>(a, stream);
     if (grid(64) >= FWD_MIN_GRID) return launch<KD, VD, 2, 3, OUT_F32>(a, stream);
-    return launch<KD, VD, 1, 3, OUT_F32>(a, stream);
+    // fewer than FWD_MIN_GRID blocks of 32 rows: two waves split each block's keys
+    return launch<KD, VD, 2, 4, OUT_F32, 2>(a, stream);
 }
 
 template <int KD, int VD>
