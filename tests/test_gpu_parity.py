@@ -169,10 +169,11 @@ def test_ragged_shapes_all_masks(A, dtype, D):
 
 @pytest.mark.parametrize("H,D", [(64, 128), (32, 128), (16, 128), (8, 128), (32, 64), (16, 64), (8, 64)])
 def test_forward_workgroup_sizes(A, H, D):
-    """1000 query rows with 64, 32, 16 or 8 heads: the launcher takes 8-, 4-, 2- and 1-wave
-    workgroups (256, 128, 64 and 32 rows; the 8-wave one with its paired 4-slot ring, the
-    others with a 3-slot ring).  Causal and causal-window masks, bf16 and fp32 outputs, three
-    sampled heads against the oracle."""
+    """1000 query rows with 64, 32, 16 or 8 heads: the launcher takes 8-, 4- and 2-wave
+    workgroups (256, 128 and 64 rows; the 8-wave one with its paired 4-slot ring, the others
+    with a 3-slot ring) and, for 8 heads, the split-key kernel (two waves per 32-row block,
+    each taking one tile of every resident pair, states merged at the end).  Causal and
+    causal-window masks, bf16 and fp32 outputs, three sampled heads against the oracle."""
     B, M = 1, 1000
     qh, kh, vh = synth.qkv(1600 + H + D, (B, M, H, D), (B, M, H, D), (B, M, H, D), "bf16")
     heads = [0, H // 2, H - 1]
