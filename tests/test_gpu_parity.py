@@ -312,6 +312,35 @@ def test_fp32_odd_head_dims(A, K, Kv):
         check(o, lse, oo, ol, TOL_F32, TOL_F32, f"K={K} Kv={Kv} mask={mask}")
 
 
+def test_side_stream(A):
+    """Every entry point enqueues on the stream it is given: the forward, two partials and their
+    merge, the split-KV decode and the backward, run on a side stream (default priority), give
+    the same bits as on the current stream."""
+    say("case: side stream")
+    qh, kh, vh = synth.qkv(1300, (1, 300, 4, 128), (1, 300, 4, 128), (1, 300, 4, 128), "bf16")
+    gh = synth.normal(1300, 3, (1, 300, 4, 128), "bf16")
+    q, k, v, g = dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), dev(gh, "bf16")
+    qd = q[:, :1].contiguous()
+
+    def run(stream):
+        o, l = A.attn_fwd(q, k, v, mask=A.MASK_CAUSAL, stream=stream)
+        p1 = A.attn_partial(q, k[:, :150], v[:, :150], stream=stream)
+        p2 = A.attn_partial(q, k[:, 150:], v[:, 150:], stream=stream)
+        mo, ml = A.attn_merge([p1[0], p2[0]], [p1[1], p2[1]], stream=stream)
+        do, dl = A.attn_decode_splitkv(qd, k, v, 4, stream=stream)
+        grads = A.attn_bwd(g, q, k, v, o, l, mask=A.MASK_CAUSAL, stream=stream)
+        return [o, l, mo, ml, do, dl, *grads]
+    ref = run(None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = run(side)
+    side.synchronize()
+    for i, (x, y) in enumerate(zip(got, ref)):
+        assert torch.equal(x, y), f"output {i} differs on the side stream"
+
+
 def test_climbing_and_falling_row_maxima(A):
     """Row maxima that grow on every key tile (the forward's running reference is raised and O, l
     rescaled tile after tile), that sit in the first tile, and plain ones: forward (causal and
