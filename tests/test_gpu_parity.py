@@ -341,6 +341,48 @@ def test_side_stream(A):
         assert torch.equal(x, y), f"output {i} differs on the side stream"
 
 
+def test_hip_graph_replay(A):
+    """The library allocates and synchronises nothing, so its calls can be captured in a HIP graph:
+    the causal forward and the split-KV decode (decode and merge launches) captured once, then
+    replayed three times with new inputs copied into the captured buffers, eager calls and
+    synchronisations in between; every replay equals the eager result bit for bit."""
+    say("case: HIP graph capture and replay")
+    shp, dshp = (1, 256, 4, 128), (2, 1024, 4, 128)
+    q, k, v = (torch.empty(shp, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    qd = torch.empty((2, 1, 4, 128), dtype=torch.bfloat16, device="cuda")
+    kd, vd = (torch.empty(dshp, dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    o, l = torch.empty_like(q), torch.empty((1, 4, 256), device="cuda")
+    do, dl = torch.empty_like(qd), torch.empty((2, 4, 1), device="cuda")
+    ws = torch.empty(A.attn_decode_workspace_bytes(2, 4, 128, 8), dtype=torch.uint8, device="cuda")
+
+    def fill(seed):
+        for t, tag in ((q, 0), (k, 1), (v, 2)):
+            t.copy_(dev(synth.normal(seed, tag, shp, "bf16"), "bf16"))
+        qd.copy_(dev(synth.normal(seed, 3, (2, 1, 4, 128), "bf16"), "bf16"))
+        kd.copy_(dev(synth.normal(seed, 4, dshp, "bf16"), "bf16"))
+        vd.copy_(dev(synth.normal(seed, 5, dshp, "bf16"), "bf16"))
+    fill(1400)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up before capture
+        A.attn_fwd(q, k, v, mask=A.MASK_CAUSAL, out=o, lse=l)
+        A.attn_decode_splitkv(qd, kd, vd, 8, workspace=ws, out=do, lse=dl)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        A.attn_fwd(q, k, v, mask=A.MASK_CAUSAL, out=o, lse=l)
+        A.attn_decode_splitkv(qd, kd, vd, 8, workspace=ws, out=do, lse=dl)
+    for r in range(3):
+        fill(1401 + r)
+        graph.replay()
+        torch.cuda.synchronize()
+        eo, el = A.attn_fwd(q, k, v, mask=A.MASK_CAUSAL)
+        edo, edl = A.attn_decode_splitkv(qd, kd, vd, 8)
+        torch.cuda.synchronize()
+        for name, x, y in (("out", o, eo), ("lse", l, el), ("decode out", do, edo), ("decode lse", dl, edl)):
+            assert torch.equal(x, y), f"replay {r}: {name} differs from the eager call"
+
+
 def test_climbing_and_falling_row_maxima(A):
     """Row maxima that grow on every key tile (the forward's running reference is raised and O, l
     rescaled tile after tile), that sit in the first tile, and plain ones: forward (causal and
