@@ -20,6 +20,12 @@
  *                       goes to a caller-owned fp32 workspace, and a second
  *                       pass merges them.
  *
+ *   Further entry points, each documented at its declaration below:
+ *   attn_fwd_ex / attn_partial_ex (bottom-right and sliding-window masks),
+ *   attn_decode_splitkv_paged (padded lanes or a paged KV cache),
+ *   attn_decode_splitkv_fp8 / attn_decode_splitkv_int4 (quantised KV caches) and
+ *   attn_bwd (gradients from the forward's output and LSE).
+ *
  * Conventions shared by every call
  *   - Tensors are described by attn_tensor: a device pointer, a dtype, 4 dims
  *     [B, M, H, D] or 5 dims [B, M, G, H, D] (grouped heads, flattened to
