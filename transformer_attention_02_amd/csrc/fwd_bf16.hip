@@ -38,9 +38,15 @@
 //
 // Online softmax in base 2: x = s * scale * log2(e).  Each row keeps a
 // reference maximum m and the sum l of 2^(x - m); the reference is raised
-// (and O, l rescaled) only when a new score exceeds it by more than 2^8, so
-// most tiles skip the rescale.  P is rounded to bf16 for the product with V;
-// l accumulates the fp32 values.  lse = (m + log2 l) * ln 2.
+// (and O, l rescaled) only when a new x exceeds it by more than 8, so most
+// tiles skip the rescale.  Once every row of a wave has a finite reference, a
+// tile takes its exponentials against it straight away and checks afterwards:
+// each lane's partial row sum bounds every value it summed, so a sum of at most
+// 2^8 shows that no value needs the rescale and the tile's row maximum is never
+// formed.  A tile that fails the check computes its scores again from the K
+// tile still in LDS and takes the exact path (row maximum, rescale,
+// exponentials).  P is rounded to bf16 for the product with V; l accumulates
+// the fp32 values.  lse = (m + log2 l) * ln 2.
 // Masks are one visible-key interval per row (causal, bottom-right, sliding
 // windows).  Tiles outside every window of a wave's rows are skipped by that
 // wave; the element mask is applied only on tiles that cut a window edge or
@@ -56,6 +62,7 @@ namespace {
 constexpr int BN = 64;         // keys per tile
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kSumThreshold = 256.0f;    // 2^kRescaleThreshold
 
 __device__ __forceinline__ float pair_max(float x) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -245,83 +252,106 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
         const unsigned char LDS_AS *kst = (const unsigned char LDS_AS *)smem + slot * KTILE;  // K tile
         const unsigned char LDS_AS *vst = (const unsigned char LDS_AS *)smem + slot * VTILE;  // + vaddr (from V_BASE)
 
-        // S^T = K Q^T for two 32-key blocks
-        f32x16 sa = f32x16{}, sb = f32x16{};
+        // S^T = K Q^T for two 32-key blocks, masked on edge tiles
+        auto scores = [&](f32x16 &sa, f32x16 &sb) __attribute__((always_inline)) {
+            sa = f32x16{}; sb = f32x16{};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const bf16x8 k0 = *(const bf16x8 LDS_AS *)(kst + kaddr[s]);
-            const bf16x8 k1 = *(const bf16x8 LDS_AS *)(kst + kaddr[s] + 32 * KROWB);
-            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], sa, 0, 0, 0);
-            sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], sb, 0, 0, 0);
-        }
-        if (MASKED) {
-            // element r of sa holds key kt0 + 4 hh + off(r), of sb 32 keys later; only the bounds
-            // that cut this tile for some row of the wave are tested
-            const int dlo = klo - kt0 - 4 * hh, dhi = khi - kt0 - 4 * hh;
-            const bool cut_lo = kt0 < klo_w, cut_hi = kt0 + BN - 1 > khi_w;
-            if (cut_lo && cut_hi) {
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 k0 = *(const bf16x8 LDS_AS *)(kst + kaddr[s]);
+                const bf16x8 k1 = *(const bf16x8 LDS_AS *)(kst + kaddr[s] + 32 * KROWB);
+                sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], sa, 0, 0, 0);
+                sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], sb, 0, 0, 0);
+            }
+            if (MASKED) {
+                // element r of sa holds key kt0 + 4 hh + off(r), of sb 32 keys later; only the bounds
+                // that cut this tile for some row of the wave are tested
+                const int dlo = klo - kt0 - 4 * hh, dhi = khi - kt0 - 4 * hh;
+                const bool cut_lo = kt0 < klo_w, cut_hi = kt0 + BN - 1 > khi_w;
+                if (cut_lo && cut_hi) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int off = 8 * (r >> 2) + (r & 3);
-                    if (off < dlo || off > dhi) sa[r] = -INFINITY;
-                    if (off + 32 < dlo || off + 32 > dhi) sb[r] = -INFINITY;
-                }
-            } else if (cut_hi) {
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = 8 * (r >> 2) + (r & 3);
+                        if (off < dlo || off > dhi) sa[r] = -INFINITY;
+                        if (off + 32 < dlo || off + 32 > dhi) sb[r] = -INFINITY;
+                    }
+                } else if (cut_hi) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int off = 8 * (r >> 2) + (r & 3);
-                    if (off > dhi) sa[r] = -INFINITY;
-                    if (off + 32 > dhi) sb[r] = -INFINITY;
-                }
-            } else if (cut_lo) {
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = 8 * (r >> 2) + (r & 3);
+                        if (off > dhi) sa[r] = -INFINITY;
+                        if (off + 32 > dhi) sb[r] = -INFINITY;
+                    }
+                } else if (cut_lo) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int off = 8 * (r >> 2) + (r & 3);
-                    if (off < dlo) sa[r] = -INFINITY;
-                    if (off + 32 < dlo) sb[r] = -INFINITY;
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = 8 * (r >> 2) + (r & 3);
+                        if (off < dlo) sa[r] = -INFINITY;
+                        if (off + 32 < dlo) sb[r] = -INFINITY;
+                    }
                 }
             }
+        };
+        f32x16 sa, sb;
+        scores(sa, sb);
+        float psum;
+        // Fast path once every row of the wave has a finite reference: exponentials first, then
+        // the partial row sums decide whether any value exceeded 2^8 (the exponentials overwrite
+        // the scores, so a failing tile computes them again and takes the exact path)
+        auto exponentials = [&](float m_use) __attribute__((always_inline)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sa[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -m_use));
+                sb[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r], c, -m_use));
+            }
+            float ps[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ps[i] = sa[i] + sb[i];
+#pragma unroll
+            for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+                for (int i = 0; i < w; ++i) ps[i] += ps[i + w];
+            return ps[0];
+        };
+        bool exact = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0;
+        if (!exact) {
+            psum = exponentials(m_ref);
+            if (__builtin_amdgcn_ballot_w64(!(psum <= kSumThreshold))) {
+                exact = true;
+                __asm__ volatile("" ::: "memory");  // read K again rather than keep its fragments live
+                scores(sa, sb);
+            }
         }
-        // row maximum of the raw scores (c > 0), pairwise to keep dependency chains short
-        float m8[8];
+        if (exact) {
+            // row maximum of the raw scores (c > 0), pairwise to keep dependency chains short
+            float m8[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            m8[i] = fmaxf(fmaxf(sa[2 * i], sa[2 * i + 1]), fmaxf(sb[2 * i], sb[2 * i + 1]));
+            for (int i = 0; i < 8; ++i)
+                m8[i] = fmaxf(fmaxf(sa[2 * i], sa[2 * i + 1]), fmaxf(sb[2 * i], sb[2 * i + 1]));
 #pragma unroll
-        for (int w = 4; w >= 1; w >>= 1)
+            for (int w = 4; w >= 1; w >>= 1)
 #pragma unroll
-            for (int i = 0; i < w; ++i) m8[i] = fmaxf(m8[i], m8[i + w]);
-        const float mx = pair_max(m8[0]) * c;
-        // raise the reference only when the row max grows by more than the threshold
-        const bool up = mx > m_ref + kRescaleThreshold;
-        if (__builtin_amdgcn_ballot_w64(up)) {
-            // lanes that keep their reference scale by exactly 1 (m_ref may still be -inf there)
-            const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
-            m_ref = up ? mx : m_ref;
-            l_run *= alpha;
+                for (int i = 0; i < w; ++i) m8[i] = fmaxf(m8[i], m8[i + w]);
+            const float mx = pair_max(m8[0]) * c;
+            // raise the reference only when the row max grows by more than the threshold
+            const bool up = mx > m_ref + kRescaleThreshold;
+            if (__builtin_amdgcn_ballot_w64(up)) {
+                // lanes that keep their reference scale by exactly 1 (m_ref may still be -inf there)
+                const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
+                m_ref = up ? mx : m_ref;
+                l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
+                for (int i = 0; i < MB; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-        }
-        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-
-        float p[32];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -m_use));
-            p[16 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[r], c, -m_use));
+                    for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+            }
+            psum = exponentials((m_ref == -INFINITY) ? 0.f : m_ref);
         }
         bf16x8 pb[4];  // [kb*2 + kt]: keys 32kb + 16kt + {8*(i/4) + 4*hh + i%4}
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pb[j][i] = (__bf16)p[8 * j + i];
-#pragma unroll
-        for (int w = 16; w >= 1; w >>= 1)
-#pragma unroll
-            for (int i = 0; i < w; ++i) p[i] += p[i + w];
-        l_run += p[0];
+            for (int i = 0; i < 8; ++i) pb[j][i] = (__bf16)(j < 2 ? sa[8 * j + i] : sb[8 * (j - 2) + i]);
+        l_run += psum;
 
         // O^T += V^T P^T over 4 steps of 16 keys
 #pragma unroll
@@ -445,7 +475,8 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
 // per 128 keys (4% faster than a 3-stage ring with a barrier per tile).  Measured on MI355X
 // against two 4-wave workgroups per CU with a 2-stage ring (30% slower) and against
 // staggered two-group schedules (no faster).  Problems too small to give every CU a workgroup (few heads, short query
-// ranges) take workgroups of 4, 2 or 1 waves instead, so that more CUs share the work.
+// ranges) take workgroups of 4 or 2 waves instead, so that more CUs share the work; below that,
+// two waves share each 32-row block and split its keys between them.
 #ifndef FWD_MIN_GRID
 #define FWD_MIN_GRID 256
 #endif
