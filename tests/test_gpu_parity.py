@@ -434,6 +434,58 @@ def test_climbing_and_falling_row_maxima(A):
     assert float(np.abs(ref[0][:, :, 2] - ref_b[0][:, :, 2]).max()) < 0.01  # the plain head is well conditioned
 
 
+def _plateau_scores(seed, H, M=384, D=128):
+    """bf16 q/k/v [1, M, H, D] whose scores, in base-2 units x = s * scale * log2(e), follow fixed
+    per-tile patterns along the keys (every query row alike, up to noise of ~1e-3).  Even heads:
+    tile 0 one key at 0 and the rest at -10 (the first reference); tile 1 every key at 4.5 (row
+    sums of 2^4.5 per key exceed 2^8, yet no value needs the reference raised); tile 2 eight keys
+    at 7.5 and the rest at -20 (the same, closer to the threshold); tile 3 one key at 8.6 (the
+    reference is raised); tiles 4-5 at 3.  The tiles carry comparable shares of the softmax, so
+    mishandling any of them shows in the output.  Odd heads: tiles 0-2 near 0, tile 3 at 150
+    (its exponentials against the old reference overflow to inf), tiles 4-5 at 149."""
+    assert M == 384
+    scale = 1.0 / math.sqrt(D)
+    unit = 8.0 * scale * math.log2(math.e)  # x per unit of k[..., 0] when q[..., 0] = 8
+    q = synth.normal(seed, synth.TAG_Q, (1, M, H, D)) * np.float32(0.01)
+    k = synth.normal(seed, synth.TAG_K, (1, M, H, D)) * np.float32(0.01)
+    v = synth.normal(seed, synth.TAG_V, (1, M, H, D))
+    even = np.full(M, 3.0)
+    even[:64] = -10.0
+    even[0] = 0.0
+    even[64:128] = 4.5
+    even[128:192] = -20.0
+    even[128:192:8] = 7.5
+    even[192:256] = 0.0
+    even[200] = 8.6
+    odd = np.zeros(M)
+    odd[:192] = 0.5 * np.sin(np.arange(192))
+    odd[192:256] = 150.0
+    odd[256:] = 149.0
+    q[:, :, :, 0] = 8.0
+    for h in range(H):
+        k[0, :, h, 0] = (odd if h % 2 else even) / unit
+    return tuple(synth.f32_to_bf16_bits(x) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("H", [2, 128])
+def test_row_sum_check_plateaus(A, H):
+    """The forward skips a tile's row maximum when its partial row sums stay within 2^8 and
+    otherwise computes the scores again and takes the exact path.  Tiles whose sums exceed 2^8
+    while no value needs a rescale, a rescale by a small step and one whose exponentials overflow
+    against the old reference, with H = 2 (two waves per 32-row block) and H = 128 (8-wave
+    workgroups), causal and unmasked, against the oracle."""
+    say(f"case: row-sum check plateaus, [1,384,{H},128] bf16")
+    qh, kh, vh = _plateau_scores(950 + H, H)
+    q, k, v = dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16")
+    for mask in (A.MASK_NONE, A.MASK_CAUSAL):
+        out, lse = A.attn_fwd(q, k, v, mask=mask)
+        torch.cuda.synchronize()
+        oo, ol = run_oracle(qh, kh, vh, mask, "bf16")
+        if mask == A.MASK_NONE:
+            assert 100 < ol[0, 1, 0] < 110 and 7 < ol[0, 0, 0] < 10, "scores are not in the intended range"
+        check(out, lse, oo, ol, TOL_BF16_OUT, TOL_LSE, f"forward mask={mask}")
+
+
 def test_empty_shard_and_no_lse(A):
     say("case: empty shard, lse=None, Mq=0")
     qh, kh, vh = synth.qkv(500, (1, 37, 2, 128), (1, 50, 2, 128), (1, 50, 2, 128), "bf16")
