@@ -304,20 +304,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
     for (; t < ub; ++t) step(t, std::false_type{});
     for (; t < te; ++t) step(t, std::true_type{});
 
-    if (key < Lk) {
-        unsigned char *dp_ = (unsigned char *)(pside ? a.dv : a.dk);
+    {
+        // gradient rows go out whole, staged in the now idle ring
         const Strides &so = pside ? a.sdv : a.sdk;
-        const int64_t base = (int64_t)b * so.b + head_offset(so, hf, a.Hin) + (int64_t)(ks + key) * so.m;
-        const float sc = pside ? 1.f : a.scale;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = mb * 32 + 8 * g + 4 * hh;
-                *(bf16x4 *)(dp_ + (base + d0) * 2) =
-                    bf16x4{(__bf16)(acc[mb][4 * g] * sc), (__bf16)(acc[mb][4 * g + 1] * sc),
-                           (__bf16)(acc[mb][4 * g + 2] * sc), (__bf16)(acc[mb][4 * g + 3] * sc)};
-            }
+        __syncthreads();  // every wave has finished reading the Q/dout ring
+        store_rows_bf16<HD>(acc, pside ? 1.f : a.scale, (unsigned char LDS_AS *)smem + wave * 32 * ROWB,
+                            (unsigned char *)(pside ? a.dv : a.dk),
+                            (int64_t)b * so.b + head_offset(so, hf, a.Hin) + (int64_t)(ks + kw0) * so.m, so.m, Lk - kw0);
     }
 }
 
@@ -526,20 +519,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
     for (; t < ub; ++t) step(t, std::false_type{});
     for (; t < te; ++t) step(t, std::true_type{});
 
-    if (qrow < Lq) {
-        unsigned char *dqp = (unsigned char *)a.dq;
-        const int64_t base = (int64_t)b * a.sdq.b + head_offset(a.sdq, hf, a.Hin) + (int64_t)(qs + qrow) * a.sdq.m;
-        const float sc = a.scale;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = mb * 32 + 8 * g + 4 * hh;
-                *(bf16x4 *)(dqp + (base + d0) * 2) =
-                    bf16x4{(__bf16)(dq[mb][4 * g] * sc), (__bf16)(dq[mb][4 * g + 1] * sc),
-                           (__bf16)(dq[mb][4 * g + 2] * sc), (__bf16)(dq[mb][4 * g + 3] * sc)};
-            }
-    }
+    // dq rows go out whole, staged in the now idle ring
+    __syncthreads();  // every wave has finished reading the K/V ring
+    store_rows_bf16<HD>(dq, a.scale, (unsigned char LDS_AS *)smem + wave * 32 * ROWB, (unsigned char *)a.dq,
+                        (int64_t)b * a.sdq.b + head_offset(a.sdq, hf, a.Hin) + (int64_t)(qs + wrow0) * a.sdq.m,
+                        a.sdq.m, Lq - wrow0);
 }
 
 template <int HD>

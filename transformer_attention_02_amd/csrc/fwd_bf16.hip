@@ -419,29 +419,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if constexpr (!OUT_F32 && KSPLIT == 1) {
-        // bf16 rows go out whole: each wave stages its 32 normalised rows in the (now idle) ring,
-        // row-major with the 16-byte chunk index XORed by the row, and writes them back with
-        // 16-byte stores, 16 lanes per 256-byte row, instead of 8 bytes per lane at 32 rows
-        constexpr int OCPR = VD / 8;  // 16-byte chunks per output row
-        __syncthreads();              // every wave has finished reading the K/V ring
-        unsigned char LDS_AS *ost = (unsigned char LDS_AS *)smem + wave * 32 * VROWB;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int pc = (4 * mb + g) ^ (l32 & (OCPR - 1));
-                *(bf16x4 LDS_AS *)(ost + l32 * VROWB + pc * 16 + hh * 8) =
-                    bf16x4{(__bf16)(o[mb][4 * g] * inv), (__bf16)(o[mb][4 * g + 1] * inv),
-                           (__bf16)(o[mb][4 * g + 2] * inv), (__bf16)(o[mb][4 * g + 3] * inv)};
-            }
-        unsigned char *op = (unsigned char *)a.o;
-        const int64_t obase = (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) + (int64_t)qs * a.so.m;
-#pragma unroll
-        for (int i = 0; i < 32 * OCPR / 64; ++i) {
-            const int idx = i * 64 + lane, r = idx / OCPR, ch = idx % OCPR;
-            const u32x4 val = *(const u32x4 LDS_AS *)(ost + r * VROWB + ((ch ^ (r & (OCPR - 1))) << 4));
-            if (wrow0 + r < Lq) *(u32x4 *)(op + (obase + (int64_t)(wrow0 + r) * a.so.m + ch * 8) * 2) = val;
-        }
+        // bf16 rows go out whole, staged in the now idle ring (16-byte stores, whole rows, instead
+        // of 8 bytes per lane at 32 rows 8 KB apart)
+        __syncthreads();  // every wave has finished reading the K/V ring
+        store_rows_bf16<VD>(o, inv, (unsigned char LDS_AS *)smem + wave * 32 * VROWB, (unsigned char *)a.o,
+                            (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) + (int64_t)(qs + wrow0) * a.so.m,
+                            a.so.m, Lq - wrow0);
         if (qrow < Lq && a.lse && hh == 0)
             a.lse[((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow] =
                 l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;

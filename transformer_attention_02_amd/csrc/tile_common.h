@@ -60,4 +60,33 @@ __device__ __forceinline__ void wait_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
+// Writes one wave's 32 output rows of HD bf16 values held in the 32x32 matrix-core C layout
+// (lane l owns row l % 32; element 4g + j of block mb is column 32 mb + 8 g + 4 (l / 32) + j),
+// each value times the lane's `sc`.  The rows are staged in `stage` (32 * HD * 2 bytes of LDS
+// that no other wave touches; 16-byte chunk index XORed by the row, so that neither the 8-byte
+// writes nor the 16-byte reads conflict) and leave as whole rows: 16-byte stores, HD / 8
+// consecutive lanes per row.  Row r goes to out + 2 * (first + r * stride) bytes and is written
+// only when r < nrows.  Row starts must be 16-byte aligned.
+template <int HD>
+__device__ __forceinline__ void store_rows_bf16(const f32x16 *acc, float sc, unsigned char LDS_AS *stage,
+                                                unsigned char *out, int64_t first, int64_t stride, int nrows) {
+    constexpr int CPR = HD / 8;  // 16-byte chunks per row
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int mb = 0; mb < HD / 32; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int pc = (4 * mb + g) ^ (l32 & (CPR - 1));
+            *(bf16x4 LDS_AS *)(stage + l32 * HD * 2 + pc * 16 + hh * 8) =
+                bf16x4{(__bf16)(acc[mb][4 * g] * sc), (__bf16)(acc[mb][4 * g + 1] * sc),
+                       (__bf16)(acc[mb][4 * g + 2] * sc), (__bf16)(acc[mb][4 * g + 3] * sc)};
+        }
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+        const int idx = i * 64 + lane, r = idx / CPR, ch = idx % CPR;
+        const u32x4 val = *(const u32x4 LDS_AS *)(stage + r * HD * 2 + ((ch ^ (r & (CPR - 1))) << 4));
+        if (r < nrows) *(u32x4 *)(out + (first + (int64_t)r * stride + ch * 8) * 2) = val;
+    }
+}
+
 }  // namespace attn
