@@ -259,6 +259,43 @@ def test_strided_and_5d_inputs(A):
     assert torch.equal(out5.view(2, 200, 4, 128), ref_out) and torch.equal(lse5, ref_lse)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_outputs_into_strided_views(A, D):
+    """Forward out and backward dq/dk/dv written into views of a wider buffer: heads-major
+    storage (row stride 3D, head stride M*3D) with the view in the middle third of each row.
+    The values equal those written into contiguous tensors bit for bit, and every element
+    outside the views keeps its sentinel (the kernels store whole 16-byte row pieces).  B=2,
+    H=64, M=300 runs the 8-wave forward with a ragged second query tile."""
+    B, M, H = 2, 300, 64
+    say(f"case: outputs into strided views, [{B},{M},{H},{D}] bf16")
+    qh, kh, vh = synth.qkv(1300 + D, (B, M, H, D), (B, M, H, D), (B, M, H, D), "bf16")
+    gh = synth.normal(1301 + D, 3, (B, M, H, D), "bf16")
+    q, k, v, g = (dev(x, "bf16") for x in (qh, kh, vh, gh))
+
+    def wide():
+        buf = torch.full((B, H, M, 3 * D), 7.0, dtype=torch.bfloat16, device="cuda")
+        return buf, buf[..., D:2 * D].transpose(1, 2)
+
+    def untouched(buf):
+        return bool((buf[..., :D] == 7.0).all()) and bool((buf[..., 2 * D:] == 7.0).all())
+
+    ref_out, ref_lse = A.attn_fwd(q, k, v, mask=A.MASK_CAUSAL)
+    wo, out = wide()
+    assert not out.is_contiguous()
+    o2, l2 = A.attn_fwd(q, k, v, mask=A.MASK_CAUSAL, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(l2, ref_lse), "forward into a strided view differs"
+    assert untouched(wo), "forward wrote outside its output view"
+
+    rdq, rdk, rdv = A.attn_bwd(g, q, k, v, ref_out, ref_lse, mask=A.MASK_CAUSAL)
+    (wq, dq), (wk, dk), (wv, dv) = wide(), wide(), wide()
+    A.attn_bwd(g, q, k, v, ref_out, ref_lse, mask=A.MASK_CAUSAL, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for name, got, ref, buf in (("dq", dq, rdq, wq), ("dk", dk, rdk, wk), ("dv", dv, rdv, wv)):
+        assert torch.equal(got, ref), f"{name} into a strided view differs"
+        assert untouched(buf), f"{name} written outside its view"
+
+
 def test_expanded_gqa_equals_repeated_heads(A):
     say("case: GQA stride-0 vs materialised repeat")
     qh = synth.normal(400, 0, (1, 300, 2, 3, 128), "bf16")
