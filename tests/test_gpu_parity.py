@@ -192,7 +192,7 @@ def test_forward_workgroup_sizes(A, H, D):
 @pytest.mark.parametrize("K,Kv", [(64, 128), (128, 64)])
 def test_bf16_distinct_head_dims(A, K, Kv):
     """q/k head dim K and v/out head dim Kv differ (each 64 or 128): ragged shapes with no mask,
-    causal and a causal window on small grids (1-wave workgroups) and on 64 heads (8-wave
+    causal and a causal window on small grids (the split-key kernel) and on 64 heads (8-wave
     workgroups, sampled heads), and packed block-diagonal causal sequences; bf16 out and the
     fp32 partial output."""
     seed = 1700 + K
@@ -510,7 +510,8 @@ def test_row_sum_check_plateaus(A, H):
     otherwise computes the scores again and takes the exact path.  Tiles whose sums exceed 2^8
     while no value needs a rescale, a rescale by a small step and one whose exponentials overflow
     against the old reference, with H = 2 (two waves per 32-row block) and H = 128 (8-wave
-    workgroups), causal and unmasked, against the oracle."""
+    workgroups), causal and unmasked, and unmasked fp32 partials over two key shards plus their
+    merge, against the oracle."""
     say(f"case: row-sum check plateaus, [1,384,{H},128] bf16")
     qh, kh, vh = _plateau_scores(950 + H, H)
     q, k, v = dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16")
@@ -521,6 +522,13 @@ def test_row_sum_check_plateaus(A, H):
         if mask == A.MASK_NONE:
             assert 100 < ol[0, 1, 0] < 110 and 7 < ol[0, 0, 0] < 10, "scores are not in the intended range"
         check(out, lse, oo, ol, TOL_BF16_OUT, TOL_LSE, f"forward mask={mask}")
+        if mask == A.MASK_NONE:
+            # fp32 partials over two key shards that split the plateaus, and their merge
+            p1 = A.attn_partial(q, k[:, :160], v[:, :160])
+            p2 = A.attn_partial(q, k[:, 160:], v[:, 160:])
+            mo, ml = A.attn_merge([p1[0], p2[0]], [p1[1], p2[1]], out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            check(mo, ml, oo, ol, TOL_BF16_OUT, TOL_LSE, "two fp32 partials + merge")
 
 
 def test_empty_shard_and_no_lse(A):
