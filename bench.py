@@ -226,10 +226,12 @@ def oracle_timing(fn, work, unit, sample):
             "kind": "oracle", "sample": sample}
 
 
-def timed(fn, steps, warmup, torch, min_warmup_s=0.25):
-    """Average ms per call over `steps` calls after `warmup` calls and at least `min_warmup_s`
-    seconds of warm-up (the clocks settle after idle host-side set-up), HIP events on the
-    current stream."""
+def timed(fn, steps, warmup, torch, min_warmup_s=0.25, repeats=5, detail=None):
+    """Per-call ms: the median over `repeats` consecutive repeats that together make exactly `steps`
+    calls, after `warmup` calls and at least `min_warmup_s` seconds of warm-up (the clocks settle after
+    idle host-side set-up).  HIP events on the current stream (the one the calls enqueue on) bracket
+    each repeat; the device is synchronised before the first and after the last.  `detail`, a dict,
+    receives every repeat's ms per call."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -238,13 +240,22 @@ def timed(fn, steps, warmup, torch, min_warmup_s=0.25):
         for _ in range(max(1, warmup)):
             fn()
         torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
-        fn()
-    e.record()
+    reps = max(1, min(repeats, steps))
+    sizes = [steps // reps + (1 if i < steps % reps else 0) for i in range(reps)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / steps
+    ev[0].record()
+    for i, n in enumerate(sizes):
+        for _ in range(n):
+            fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) / n for i, n in enumerate(sizes)]
+    if detail is not None:
+        detail["repeats_ms_per_call"] = [round(x, 5) for x in per]
+        detail["mean_ms_per_call"] = round(ev[0].elapsed_time(ev[-1]) / steps, 5)
+        detail["timing"] = f"median of {reps} consecutive repeats ({'+'.join(map(str, sizes))} calls)"
+    return float(np.median(per))
 
 
 def main():
@@ -293,11 +304,13 @@ def main():
     lse = torch.empty((2, 32, 2048), dtype=torch.float32, device="cuda")
     flops = 4.0 * 2 * 32 * 2048 * 2048 * 128 / 2
     step = A.prepare_fwd(q, k, v, out, lse, mask=A.MASK_CAUSAL)
-    ms = timed(step, args.steps, args.warmup, torch)
+    head_timing = {}
+    ms = timed(step, args.steps, args.warmup, torch, detail=head_timing)
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"prefill causal bf16 [2,2048,32,128]: {ms * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
     result["value"] = round(tflops, 2)
     result["ms_per_step"] = round(ms, 5)
+    result["timing"] = head_timing
     result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                           "traffic": recorded_traffic("fwd_bf16 causal 2x2048x32x128"),
@@ -306,7 +319,8 @@ def main():
     # the same shape without a mask: the kernel's steady state, free of the causal diagonal
     if "full" in rows:
         of = torch.empty_like(q)
-        ms_f = timed(A.prepare_fwd(q, k, v, of, lse, mask=A.MASK_NONE), 100, 20, torch)
+        tm = {}
+        ms_f = timed(A.prepare_fwd(q, k, v, of, lse, mask=A.MASK_NONE), 100, 20, torch, detail=tm)
         fl_f = 2.0 * flops
         tf_f = fl_f / (ms_f * 1e-3) / 1e12
         log(f"prefill unmasked bf16 [2,2048,32,128]: {ms_f * 1e3:.1f} us/call, {tf_f:.1f} TFLOP/s")
@@ -314,7 +328,13 @@ def main():
             "workload": "bf16 B=2 M=2048 H=32 K=Kv=128, no mask (the headline shape without the causal diagonal)",
             "ms_per_call": round(ms_f, 5), "value": round(tf_f, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf_f, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf_f / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_f}}
+                         "frac": round(tf_f / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_f}, **tm}
+        if not args.no_cpu:  # batch element 0, heads 0..7 of 32, no mask
+            sample = [synth.to_f64(x[:1, :, :8], "bf16") for x in (qh, kh, vh)]
+            result["rows"]["prefill_unmasked"]["cpu_oracle"] = oracle_timing(
+                lambda: oracle_mod().attention(*sample), fl_f / 8 / 1e12, "TFLOP/s",
+                "batch element 0, heads 0-7 (8 of the 64 (b, h) problems), no mask, fp64")
+            del sample
         del of
 
     # ------------------------------------------------------------ CPU baseline: the oracle on the same workload
@@ -347,7 +367,8 @@ def main():
         ws = torch.empty(A.attn_decode_workspace_bytes(B, H, D, S), dtype=torch.uint8, device="cuda")
         od = torch.empty_like(qd)
         ld = torch.empty((B, H, 1), dtype=torch.float32, device="cuda")
-        ms_d = timed(A.prepare_decode(qd, kd, vd, S, ws, od, ld), 20, 3, torch)
+        tm = {}
+        ms_d = timed(A.prepare_decode(qd, kd, vd, S, ws, od, ld), 40, 3, torch, detail=tm)
         kv_bytes = 2.0 * B * Mkv * H * D * 2
         gbs = kv_bytes / (ms_d * 1e-3) / 1e9
         log(f"decode split-KV S=64: {ms_d * 1e3:.1f} us/call, {gbs:.0f} GB/s")
@@ -357,22 +378,23 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_call": kv_bytes,
                          "traffic": recorded_traffic("decode bf16 16x32768x32x128 s64"),
-                         "note": "algorithmic bytes = K+V once; time covers both launches"}}
+                         "note": "algorithmic bytes = K+V once; time covers both launches"}, **tm}
         if not args.no_cpu:  # the oracle on batch element 0 of 16 (one sequence's 32768 keys, all 32 heads)
             sample = [synth.to_f64(x[:1], "bf16") for x in (qdh, kdh, vdh)]
+            q0 = sample[0]
             result["rows"]["decode_splitkv"]["cpu_oracle"] = oracle_timing(
                 lambda: oracle_mod().attention(*sample), kv_bytes / B / 1e9, "GB/s",
                 "batch element 0 of 16 (32768 keys x 32 heads), fp64 exact attention; GB/s of its bf16 K+V")
             result["rows"]["decode_splitkv"]["cpu_oracle"]["host_bytes"] = int(sum(x.nbytes for x in sample))
             del sample
-        del qdh, kdh, vdh
         # the same cache as 8192 pages of 64 rows in a random order (PagedBlockDiagonalPaddedKeysMask form)
         page = 64
         perm = np.random.Generator(np.random.PCG64(7)).permutation(B * Mkv // page).astype(np.int32)
         tables = torch.from_numpy(perm.reshape(B, Mkv // page)).to("cuda")
         lens = torch.full((B,), Mkv, dtype=torch.int32, device="cuda")
+        tm = {}
         ms_p = timed(A.prepare_decode_paged(qd, kd.view(1, B * Mkv, H, D), vd.view(1, B * Mkv, H, D), lens, S, Mkv, ws,
-                                            od, ld, block_tables=tables, page_size=page), 20, 3, torch)
+                                            od, ld, block_tables=tables, page_size=page), 40, 3, torch, detail=tm)
         gbs_p = kv_bytes / (ms_p * 1e-3) / 1e9
         log(f"paged decode page=64: {ms_p * 1e3:.1f} us/call, {gbs_p:.0f} GB/s")
         result["rows"]["decode_paged"] = {
@@ -380,8 +402,21 @@ def main():
             "ms_per_call": round(ms_p, 5), "value": round(gbs_p, 1), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs_p, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs_p / PEAK_HBM_GBS, 4), "bytes_per_call": kv_bytes,
-                         "traffic": recorded_traffic("decode bf16 paged 16x32768x32x128 page64 s64")}}
-        del kd, vd
+                         "traffic": recorded_traffic("decode bf16 paged 16x32768x32x128 page64 s64")}, **tm}
+        if not args.no_cpu:  # sequence 0's keys gathered through its block table, then the oracle
+            k0, v0 = kdh.reshape(1, B * Mkv, H, D), vdh.reshape(1, B * Mkv, H, D)
+            rows_b0 = (perm[:Mkv // page, None] * page + np.arange(page)[None, :]).reshape(-1)
+
+            def paged_oracle():
+                kg, vg = (synth.to_f64(x[:, rows_b0], "bf16") for x in (k0, v0))
+                oracle_mod().attention(q0, kg, vg)
+
+            result["rows"]["decode_paged"]["cpu_oracle"] = oracle_timing(
+                paged_oracle, kv_bytes / B / 1e9, "GB/s",
+                "sequence 0 of 16: its 32768 keys gathered through the block table and widened, then fp64 "
+                "exact attention over all 32 heads; GB/s of its bf16 K+V")
+            del k0, v0
+        del kd, vd, kdh, vdh
         torch.cuda.empty_cache()
 
         # the same shape with a row-wise FP8 E4M3 cache: codes + one (scale, shift) fp16 pair per row and head
@@ -390,7 +425,8 @@ def main():
         v8 = torch.from_numpy(synth.fp8_codes(4, synth.TAG_V, (B, Mkv, H, D))).to("cuda").view(torch.float8_e4m3fn)
         kss = torch.from_numpy(synth.scale_shift(4, synth.TAG_K, (B, Mkv, H))).to("cuda")
         vss = torch.from_numpy(synth.scale_shift(4, synth.TAG_V, (B, Mkv, H))).to("cuda")
-        ms_8 = timed(A.prepare_decode_fp8(qd, k8, v8, kss, vss, S, ws, od, ld), 20, 3, torch)
+        tm = {}
+        ms_8 = timed(A.prepare_decode_fp8(qd, k8, v8, kss, vss, S, ws, od, ld), 40, 3, torch, detail=tm)
         fp8_bytes = 2.0 * B * Mkv * H * (D + 4)
         gbs_8 = fp8_bytes / (ms_8 * 1e-3) / 1e9
         log(f"fp8 decode S=64: {ms_8 * 1e3:.1f} us/call, {gbs_8:.0f} GB/s")
@@ -402,7 +438,17 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs_8, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs_8 / PEAK_HBM_GBS, 4), "bytes_per_call": fp8_bytes,
                          "traffic": recorded_traffic("decode fp8 16x32768x32x128 s64"),
-                         "note": "algorithmic bytes = K+V codes and their metadata once"}}
+                         "note": "algorithmic bytes = K+V codes and their metadata once"}, **tm}
+        if not args.no_cpu:  # batch element 0: dequantise its codes, then the oracle
+            c8 = [synth.fp8_codes(4, t, (1, Mkv, H, D)) for t in (synth.TAG_K, synth.TAG_V)]
+            s8 = [synth.scale_shift(4, t, (1, Mkv, H)) for t in (synth.TAG_K, synth.TAG_V)]
+            result["rows"]["decode_fp8"]["cpu_oracle"] = oracle_timing(
+                lambda: oracle_mod().attention(q0, oracle_mod().dequant_fp8_rowwise(c8[0], s8[0]),
+                                               oracle_mod().dequant_fp8_rowwise(c8[1], s8[1])),
+                fp8_bytes / B / 1e9, "GB/s",
+                "batch element 0 of 16 (32768 keys x 32 heads): FP8 dequantisation and fp64 exact attention; "
+                "GB/s of its codes and metadata")
+            del c8, s8
         del k8, v8, kss, vss
         torch.cuda.empty_cache()
 
@@ -415,7 +461,8 @@ def main():
             ks4 = torch.from_numpy(synth.int4_scale_shift(4, synth.TAG_K, (B, Mkv, H, G)).reshape(B, Mkv, H, 2 * G))
             vs4 = torch.from_numpy(synth.int4_scale_shift(4, synth.TAG_V, (B, Mkv, H, G)).reshape(B, Mkv, H, 2 * G))
             ks4, vs4 = ks4.to("cuda"), vs4.to("cuda")
-            ms_4 = timed(A.prepare_decode_int4(qd, k4, v4, ks4, vs4, S, ws, od, ld), 20, 3, torch)
+            tm = {}
+            ms_4 = timed(A.prepare_decode_int4(qd, k4, v4, ks4, vs4, S, ws, od, ld), 40, 3, torch, detail=tm)
             i4_bytes = 2.0 * B * Mkv * H * (D // 2 + 4 * G)
             gbs_4 = i4_bytes / (ms_4 * 1e-3) / 1e9
             log(f"int4 decode G={G} S=64: {ms_4 * 1e3:.1f} us/call, {gbs_4:.0f} GB/s")
@@ -428,7 +475,17 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": round(gbs_4, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(gbs_4 / PEAK_HBM_GBS, 4), "bytes_per_call": i4_bytes,
                              "traffic": recorded_traffic(f"decode int4 g{G} 16x32768x32x128 s64"),
-                             "note": "algorithmic bytes = K+V codes and their metadata once"}}
+                             "note": "algorithmic bytes = K+V codes and their metadata once"}, **tm}
+            if not args.no_cpu:  # batch element 0: dequantise its codes, then the oracle
+                c4 = [synth.int4_codes(4, t, (1, Mkv, H, D // 2)) for t in (synth.TAG_K, synth.TAG_V)]
+                s4 = [synth.int4_scale_shift(4, t, (1, Mkv, H, G)) for t in (synth.TAG_K, synth.TAG_V)]
+                result["rows"][f"decode_int4_g{G}"]["cpu_oracle"] = oracle_timing(
+                    lambda: oracle_mod().attention(q0, oracle_mod().dequant_int4_groupwise(c4[0], s4[0]),
+                                                   oracle_mod().dequant_int4_groupwise(c4[1], s4[1])),
+                    i4_bytes / B / 1e9, "GB/s",
+                    f"batch element 0 of 16 (32768 keys x 32 heads): INT4 (G={G}) dequantisation and fp64 exact "
+                    "attention; GB/s of its codes and metadata")
+                del c4, s4
             del k4, v4, ks4, vs4
             torch.cuda.empty_cache()
         del qd, ws, od, ld
@@ -445,8 +502,9 @@ def main():
         ov = torch.empty_like(qv)
         lv = torch.empty((1, 32, M), dtype=torch.float32, device="cuda")
         mx = int(lens.max())
+        tm = {}
         ms_v = timed(A.prepare_fwd(qv, kv, vv, ov, lv, mask=A.MASK_BLOCKDIAG_CAUSAL, seqstart_q=sst, max_seqlen_q=mx),
-                     20, 3, torch)
+                     50, 5, torch, detail=tm)
         fl = 4.0 * 32 * 128 * float(np.sum(lens.astype(np.float64) ** 2)) / 2
         tf = fl / (ms_v * 1e-3) / 1e12
         log(f"varlen GQA causal M={M}: {ms_v * 1e3:.1f} us/call, {tf:.1f} TFLOP/s")
@@ -455,7 +513,7 @@ def main():
                         "H=32 as 8 KV groups x 4, K=Kv=128 bf16",
             "ms_per_call": round(ms_v, 5), "value": round(tf, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl}}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl}, **tm}
         if not args.no_cpu:  # the whole packed workload, k and v broadcast over the 4 heads of a group
             qo = synth.to_f64(synth.normal(5, synth.TAG_Q, (1, M, 8, 4, 128), "bf16"), "bf16").reshape(1, M, 32, 128)
             ko, vo = (np.broadcast_to(synth.to_f64(synth.normal(5, tag, (1, M, 8, 1, 128), "bf16"), "bf16"),
@@ -477,7 +535,9 @@ def main():
         A.attn_fwd(qb_, kb_, vb_, mask=A.MASK_CAUSAL, out=ob_, lse=lb_)
         dqb, dkb, dvb = torch.empty_like(qb_), torch.empty_like(kb_), torch.empty_like(vb_)
         wsb = torch.empty(A.attn_bwd_workspace_bytes(Bb, Hb, Mb), dtype=torch.uint8, device="cuda")
-        ms_b = timed(A.prepare_bwd(gb_, qb_, kb_, vb_, ob_, lb_, dqb, dkb, dvb, wsb, mask=A.MASK_CAUSAL), 100, 20, torch)
+        tm = {}
+        ms_b = timed(A.prepare_bwd(gb_, qb_, kb_, vb_, ob_, lb_, dqb, dkb, dvb, wsb, mask=A.MASK_CAUSAL), 100, 20, torch,
+                     detail=tm)
         fl_b = 2.5 * 4.0 * Bb * Hb * Mb * Mb * Db / 2  # five products of the forward's size, causal half
         tf_b = fl_b / (ms_b * 1e-3) / 1e12
         log(f"backward causal bf16 [2,2048,32,128]: {ms_b * 1e3:.1f} us/call, {tf_b:.1f} TFLOP/s")
@@ -486,7 +546,16 @@ def main():
             "ms_per_call": round(ms_b, 5), "value": round(tf_b, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_b,
-                         "note": "algorithmic flops = 2.5x the forward's (dS recomputation not counted)"}}
+                         "note": "algorithmic flops = 2.5x the forward's (dS recomputation not counted)"}, **tm}
+        if not args.no_cpu:  # batch element 0, heads 0..7: the oracle's forward (for out, lse) and backward
+            hq, hk, hv = (synth.to_f64(x[:1, :, :8], "bf16") for x in synth.qkv(2, shp, shp, shp, "bf16"))
+            hg = synth.to_f64(synth.normal(2, 3, shp, "bf16")[:1, :, :8], "bf16")
+            ho, hl = oracle_mod().attention(hq, hk, hv, mask=oracle_mod().MASK_CAUSAL)
+            result["rows"]["bwd_causal"]["cpu_oracle"] = oracle_timing(
+                lambda: oracle_mod().attention_backward(hg, ho, hl, hq, hk, hv, mask=oracle_mod().MASK_CAUSAL),
+                fl_b / 8 / 1e12, "TFLOP/s", "batch element 0, heads 0-7 (8 of 64), fp64 backward from the oracle's "
+                "own out and lse")
+            del hq, hk, hv, hg, ho, hl
         del qb_, kb_, vb_, gb_, ob_, lb_, dqb, dkb, dvb, wsb
 
     # ------------------------------------------------------------ sliding-window causal prefill
@@ -497,7 +566,9 @@ def main():
         qw, kw, vw = up(qh4), up(kh4), up(vh4)
         ow = torch.empty_like(qw)
         lw = torch.empty((Bw, Hw, Mw), dtype=torch.float32, device="cuda")
-        ms_w = timed(A.prepare_fwd(qw, kw, vw, ow, lw, mask=A.MASK_CAUSAL_LOCAL_BR, window_size=W), 50, 20, torch)
+        tm = {}
+        ms_w = timed(A.prepare_fwd(qw, kw, vw, ow, lw, mask=A.MASK_CAUSAL_LOCAL_BR, window_size=W), 50, 20, torch,
+                     detail=tm)
         visible = W * (W + 1) / 2 + (Mw - W) * W  # scores per head: row i sees min(i + 1, W) keys
         fl = 4.0 * Bw * Hw * Dw * visible
         tf = fl / (ms_w * 1e-3) / 1e12
@@ -506,7 +577,13 @@ def main():
             "workload": "bf16 B=2 M=8192 H=32 K=Kv=128, causal window of 1024 keys (bottom-right local mask)",
             "ms_per_call": round(ms_w, 5), "value": round(tf, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl}}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl}, **tm}
+        if not args.no_cpu:  # batch element 0, heads 0..3 of 32
+            sample = [synth.to_f64(x[:1, :, :4], "bf16") for x in (qh4, kh4, vh4)]
+            result["rows"]["sliding_window_causal"]["cpu_oracle"] = oracle_timing(
+                lambda: oracle_mod().attention(*sample, mask=oracle_mod().MASK_CAUSAL_LOCAL_BR, window=W),
+                fl / 16 / 1e12, "TFLOP/s", "batch element 0, heads 0-3 (4 of the 64 (b, h) problems), fp64")
+            del sample
         del qw, kw, vw, ow, lw
 
     # ------------------------------------------------------------ partial + merge

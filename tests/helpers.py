@@ -59,3 +59,24 @@ def varlen_workload(seed=5, n=8, lo=256, hi=4096, G=8, Hg=4, D=128):
     kb = synth.normal(seed, synth.TAG_K, (1, M, G, 1, D), "bf16")
     vb = synth.normal(seed, synth.TAG_V, (1, M, G, 1, D), "bf16")
     return lens, ss, q, kb, vb
+
+
+def f64_threads(x: np.ndarray, dtype: str = "bf16", workers: int = 16) -> np.ndarray:
+    """synth.to_f64 of a large array, split over threads along its first axis of extent > 1
+    (numpy's conversions release the GIL); exact, like synth.to_f64 itself."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    x = np.asarray(x)
+    out = np.empty(x.shape, dtype=np.float64)
+    ax = next((i for i, n in enumerate(x.shape) if n > 1), 0)
+    n = x.shape[ax] if x.ndim else 1
+    parts = max(1, min(workers, n))
+    bounds = [(n * i // parts, n * (i + 1) // parts) for i in range(parts)]
+
+    def one(ab):
+        sl = (slice(None),) * ax + (slice(*ab),)
+        out[sl] = synth.to_f64(x[sl], dtype)
+
+    with ThreadPoolExecutor(parts) as ex:
+        list(ex.map(one, bounds))
+    return out

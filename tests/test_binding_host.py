@@ -63,3 +63,32 @@ def test_merge_lse_chunks_are_checked():
         A.attn_merge([c, c], [good[:, :1], good])
     with pytest.raises(ValueError, match="device"):
         A.attn_merge([c, c], [good, good])
+
+
+def test_short_index_arrays_are_refused():
+    # the kernels read seqstart_k[s + 1] for every sequence of seqstart_q, seqlens[b] and row b of
+    # the block table for every batch element: shorter arrays would be read past their end
+    q, k, v = qkv()
+    ssq = torch.tensor([0, 32, 64], dtype=torch.int32)
+    with pytest.raises(ValueError, match="seqstart_k has 2 entries; seqstart_q has 3"):
+        A.attn_fwd(q, k, v, mask=A.MASK_BLOCKDIAG_CAUSAL, seqstart_q=ssq,
+                   seqstart_k=torch.tensor([0, 64], dtype=torch.int32), max_seqlen_q=32)
+    qd = torch.zeros(3, 1, 2, 64, dtype=torch.bfloat16)
+    cache = torch.zeros(1, 256, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="seqlens holds 2 values; q has 3 batch elements"):
+        A.attn_decode_splitkv_paged(qd, cache, cache, torch.tensor([10, 20], dtype=torch.int32), 4, 128,
+                                    block_tables=torch.zeros(3, 2, dtype=torch.int32), page_size=64)
+    lens = torch.tensor([10, 20, 30], dtype=torch.int32)
+    with pytest.raises(ValueError, match="at least 3 rows"):
+        A.attn_decode_splitkv_paged(qd, cache, cache, lens, 4, 128, block_tables=torch.zeros(2, 2, dtype=torch.int32),
+                                    page_size=64)
+    with pytest.raises(ValueError, match="2-D"):
+        A.attn_decode_splitkv_paged(qd, cache, cache, lens, 4, 128, block_tables=torch.zeros(6, dtype=torch.int32),
+                                    page_size=64)
+    codes = torch.zeros(1, 256, 2, 64, dtype=torch.uint8)
+    meta = torch.zeros(1, 256, 2, 2, dtype=torch.float16)
+    with pytest.raises(ValueError, match="seqlens holds 2 values"):
+        A.attn_decode_splitkv_fp8(qd, codes, codes, meta, meta, 4, seqlens=lens[:2], max_seqlen_k=128)
+    with pytest.raises(ValueError, match="at least 3 rows"):
+        A.attn_decode_splitkv_int4(qd, codes[..., :32], codes[..., :32], meta, meta, 4, seqlens=lens, max_seqlen_k=128,
+                                   block_tables=torch.zeros(1, 4, dtype=torch.int32), page_size=64)

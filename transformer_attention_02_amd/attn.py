@@ -12,7 +12,6 @@ missing: there is no fallback implementation.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -189,6 +188,9 @@ def _varlen(seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k=None):
         return None, None
     _index(seqstart_q, "seqstart_q")
     _index(seqstart_k, "seqstart_k")
+    if seqstart_k is not None and seqstart_k.numel() != seqstart_q.numel():
+        # the kernels read seqstart_k[s + 1] for every sequence s of seqstart_q
+        raise ValueError(f"seqstart_k has {seqstart_k.numel()} entries; seqstart_q has {seqstart_q.numel()}")
     vl = AttnVarlen()
     vl.seqstart_q = seqstart_q.data_ptr()
     vl.seqstart_k = seqstart_k.data_ptr() if seqstart_k is not None else None
@@ -350,10 +352,21 @@ def attn_decode_splitkv(q, k, v, num_splits, scale=None, workspace=None, out=Non
     return out, lse
 
 
-def _paged_args(q, k, v, seqlens, block_tables, page_size, max_seqlen_k, num_splits, scale, workspace, out, lse,
-                stream):
+def _cache_index(q, seqlens, block_tables):
+    """seqlens [>= B] and block_tables [>= B, n] int32: the kernels read seqlens[b] and row b of the
+    table for every batch element b of q."""
     _index(seqlens, "seqlens")
     _index(block_tables, "block_tables")
+    B = q.shape[0]
+    if seqlens is not None and seqlens.numel() < B:
+        raise ValueError(f"seqlens holds {seqlens.numel()} values; q has {B} batch elements")
+    if block_tables is not None and (block_tables.dim() != 2 or block_tables.shape[0] < B):
+        raise ValueError(f"block_tables must be 2-D with at least {B} rows, got shape {tuple(block_tables.shape)}")
+
+
+def _paged_args(q, k, v, seqlens, block_tables, page_size, max_seqlen_k, num_splits, scale, workspace, out, lse,
+                stream):
+    _cache_index(q, seqlens, block_tables)
     _lse_buf(lse, q.shape[0] * _htot(q))
     _on_device(seqlens=seqlens, block_tables=block_tables, lse=lse)
     ds = [desc(q, name="q"), desc(k, name="k"), desc(v, name="v"), desc(out, name="out")]
@@ -392,8 +405,7 @@ def prepare_decode_paged(q, k, v, seqlens, num_splits, max_seqlen_k, workspace, 
 
 def _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k, num_splits,
               scale, workspace, out, lse, stream, kv_code=None):
-    _index(seqlens, "seqlens")
-    _index(block_tables, "block_tables")
+    _cache_index(q, seqlens, block_tables)
     _lse_buf(lse, q.shape[0] * _htot(q))
     _on_device(seqlens=seqlens, block_tables=block_tables, lse=lse)
     ds = [desc(q, name="q"), desc(k, kv_code, "k"), desc(v, kv_code, "v"), desc(k_scale_shift, name="k_scale_shift"),
@@ -508,6 +520,3 @@ def prepare_decode_int4(q, k, v, k_scale_shift, v_scale_shift, num_splits, works
     return Prepared(_lib.attn_decode_splitkv_int4, args,
                     (ds, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, workspace, out, lse))
 
-
-def default_scale(K: int) -> float:
-    return 1.0 / math.sqrt(K)

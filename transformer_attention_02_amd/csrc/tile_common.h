@@ -54,10 +54,13 @@ __device__ __forceinline__ void dma4(i32x4 rsrc, unsigned voff, unsigned lds) {
                  : "memory");
 }
 
-// Wait until at most N of this wave's tile loads are outstanding, then a workgroup barrier.
+// Wait until at most N of this wave's tile loads are outstanding and every LDS read of this
+// wave has returned, then a workgroup barrier.  After the barrier other waves refill ring slots
+// that this wave has just read: a read still in flight (its consuming matrix op moved below the
+// barrier by the compiler) would race with that refill, so lgkmcnt(0) is part of the wait.
 template <int N>
 __device__ __forceinline__ void wait_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
 // Writes one wave's 32 output rows of HD bf16 values held in the 32x32 matrix-core C layout
