@@ -22,6 +22,7 @@
  *
  *   Further entry points, each documented at its declaration below:
  *   attn_fwd_ex / attn_partial_ex (bottom-right and sliding-window masks),
+ *   attn_decode_splitkv_noalloc (the decode with library-held scratch, no workspace),
  *   attn_decode_splitkv_paged (padded lanes or a paged KV cache),
  *   attn_decode_splitkv_fp8 / attn_decode_splitkv_int4 (quantised KV caches) and
  *   attn_bwd (gradients from the forward's output and LSE).
@@ -224,6 +225,23 @@ attn_status attn_decode_splitkv(const attn_tensor *q, const attn_tensor *k, cons
                                 int32_t num_splits, float scale, void *workspace,
                                 size_t workspace_bytes, const attn_tensor *out, float *lse,
                                 attn_stream_t stream);
+
+/* attn_decode_splitkv for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The per-chunk partials go to a
+ * static device array of ATTN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends (its address is looked up once per device, on that device's first
+ * call, with the device current: the stream must belong to the current device).  No allocation
+ * of any kind happens in the call.
+ *   Arguments, layouts, results and errors as attn_decode_splitkv, without the workspace.  A call
+ *   whose attn_decode_workspace_bytes(B, H_total, Kv, num_splits) exceeds the scratch returns
+ *   ATTN_ERR_UNSUPPORTED and launches nothing.
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap on one GPU (other
+ *   streams, other threads) race and must be ordered by the caller.  Each call writes every
+ *   scratch entry it reads, so nothing needs clearing between calls. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+attn_status attn_decode_splitkv_noalloc(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                        int32_t num_splits, float scale, const attn_tensor *out, float *lse,
+                                        attn_stream_t stream);
 
 /* Split-KV decode against a KV cache ("Attention - Biases & masks": BlockDiagonalPaddedKeysMask
  * and PagedBlockDiagonalPaddedKeysMask, one query per sequence; "MSLK Kernel Library --

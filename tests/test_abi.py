@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd", "attn_partial", "attn_fwd_ex", "attn_partial_ex", "attn_merge",
-                                           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_paged",
+                                           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_noalloc",
+                                           "attn_decode_splitkv_paged",
                                            "attn_decode_splitkv_fp8", "attn_decode_splitkv_int4", "attn_bwd_workspace_bytes",
                                            "attn_bwd",
                                            "attn_last_error"])
@@ -324,3 +325,21 @@ def test_int4_decode_rejects():
     assert call(k=k8, kss=ss(2), fn=A._lib.attn_decode_splitkv_fp8) == A.ATTN_ERR_INVALID_ARGUMENT
     assert "row-wise" in A.attn_last_error()
     assert call(k=tensor([B, M, H, D // 2], A.ATTN_DTYPE_INT4X2, data=FAKE + 8)) == A.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_decode_refuses_more_than_its_scratch():
+    # 64 x 64 x 128 rows of 128 floats need 268 MB of partials: refused before any launch
+    q = tensor([64, 1, 64, 128])
+    k = tensor([64, 256, 64, 128])
+    o = tensor([64, 1, 64, 128])
+    assert A.attn_decode_workspace_bytes(64, 64, 128, 128) > A.NOALLOC_SCRATCH_BYTES
+    rc = A._lib.attn_decode_splitkv_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 128, float("nan"),
+                                            ctypes.byref(o), None, None)
+    assert rc == A.ATTN_ERR_UNSUPPORTED
+    assert "bytes of scratch" in A.attn_last_error()
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == A.NOALLOC_SCRATCH_BYTES

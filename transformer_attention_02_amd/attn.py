@@ -66,6 +66,9 @@ _lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.attn_decode_splitkv.argtypes = [_T, _T, _T, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
                                      _T, ctypes.c_void_p, ctypes.c_void_p]
 _lib.attn_decode_splitkv.restype = ctypes.c_int
+_lib.attn_decode_splitkv_noalloc.argtypes = [_T, _T, _T, ctypes.c_int32, ctypes.c_float, _T, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+_lib.attn_decode_splitkv_noalloc.restype = ctypes.c_int
 _lib.attn_decode_splitkv_paged.argtypes = [_T, _T, _T, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                            ctypes.c_void_p, ctypes.c_size_t, _T, ctypes.c_void_p, ctypes.c_void_p]
@@ -349,6 +352,21 @@ def attn_decode_splitkv(q, k, v, num_splits, scale=None, workspace=None, out=Non
                                     ctypes.byref(desc(v, name="v")), int(num_splits), _scale(scale),
                                     _ptr(workspace), _ws_bytes(workspace), ctypes.byref(desc(out, name="out")),
                                     _ptr(lse), _stream(stream, q.device)))
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def attn_decode_splitkv_noalloc(q, k, v, num_splits, out, lse=None, scale=None, stream=None):
+    """attn_decode_splitkv without a workspace: the partials live in the library's static per-GPU
+    scratch.  The caller passes `out` (and `lse` [B, H_total, 1] fp32, or None), so that nothing is
+    allocated here either.  Calls that may overlap on one GPU share that scratch and race."""
+    _on_device(lse=_lse_buf(lse, q.shape[0] * _htot(q)))
+    _check(_lib.attn_decode_splitkv_noalloc(ctypes.byref(desc(q, name="q")), ctypes.byref(desc(k, name="k")),
+                                            ctypes.byref(desc(v, name="v")), int(num_splits), _scale(scale),
+                                            ctypes.byref(desc(out, name="out")), _ptr(lse),
+                                            _stream(stream, q.device)))
     return out, lse
 
 

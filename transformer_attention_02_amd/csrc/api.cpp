@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -635,7 +636,59 @@ attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_
 
 }  // namespace
 
+// Device scratch of attn_decode_splitkv_noalloc: the decode's per-chunk partial outputs and LSEs
+// live here instead of in a caller workspace.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in, not device memory:
+// its device address comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up on the device's first call.
+attn_status scratch_address(const char *fn, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(ATTN_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn, dev,
+                        hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return ATTN_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+attn_status attn_decode_splitkv_noalloc(const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
+                                        int32_t num_splits, float scale, const attn_tensor *ot, float *lse,
+                                        attn_stream_t stream) {
+    const char *fn = "attn_decode_splitkv_noalloc";
+    View q;
+    attn_status st;
+    if ((st = make_view(qt, "q", &q)) != ATTN_OK) return st;
+    const size_t need = attn_decode_workspace_bytes(q.B, htot(q), q.D, num_splits);
+    if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "%s: the call needs %zu bytes of scratch, more than the library's static %zu; "
+                    "use attn_decode_splitkv with a caller workspace",
+                    fn, need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((st = scratch_address(fn, &ws)) != ATTN_OK) return st;
+    return decode(fn, 0, qt, kt, vt, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, num_splits, scale, ws,
+                  (size_t)ATTN_NOALLOC_SCRATCH_BYTES, ot, lse, stream);
+}
 
 attn_status attn_decode_splitkv(const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
                                 int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
