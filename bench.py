@@ -48,7 +48,7 @@ def parse():
                    "counters per kernel and grid) instead of running; no GPU needed")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE rocprofv3 run of "
-                        "'bench.py --rows decode,copy --no-cpu --steps 3 --warmup 1'; no GPU needed")
+                        "'bench.py --rows decode,copy,varlen,window --no-cpu --steps 3 --warmup 1'; no GPU needed")
     return p.parse_args()
 
 
@@ -112,9 +112,14 @@ def recorded_traffic(key, path=None):
 
 
 # (record key, sources digested, kernel name, which value cluster of the dispatches when two workloads
-# launch the same kernel on the same grid: 0 the lower, 1 the higher, None all)
+# launch the same kernel on the same grid: 0 the lower, 1 the higher, None all; grid in threads, or
+# None for every grid)
+TRAFFIC_GRID = {"fwd_bf16 causal 2x2048x32x128": 512 * 512, "fwd_bf16 varlen gqa causal 8 seqs": 3584 * 512,
+                "fwd_bf16 sliding window 1024 2x8192x32x128": 2048 * 512}
 TRAFFIC_KERNELS = (
     ("fwd_bf16 causal 2x2048x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false>", None),
+    ("fwd_bf16 varlen gqa causal 8 seqs", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false>", None),
+    ("fwd_bf16 sliding window 1024 2x8192x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false>", None),
     ("decode bf16 16x32768x32x128 s64", "decode", "decode_kernel<128, 0, 0>", None),
     ("decode bf16 paged 16x32768x32x128 page64 s64", "decode", "decode_kernel<128, 0, 2>", None),
     ("decode fp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 2, 0>", None),
@@ -124,14 +129,14 @@ TRAFFIC_KERNELS = (
 COPY_KERNEL, COPY_KIB = "__amd_rocclr_copyBuffer", 1 << 20  # the 1 GiB copy row reads and writes 1 GiB
 
 
-def _counter_values(db_path, counter):
+def _counter_values(db_path, counter, grid=None):
     import collections
     import sqlite3
 
     g = collections.defaultdict(list)
     cur = sqlite3.connect(db_path).cursor()
-    for name, cn, val in cur.execute("select kernel_name, counter_name, value from counters_collection"):
-        if cn == counter:
+    for name, gs, cn, val in cur.execute("select kernel_name, grid_size, counter_name, value from counters_collection"):
+        if cn == counter and (grid is None or gs == grid):
             g[name].append(val)
     return g
 
@@ -164,13 +169,17 @@ def write_traffic(fetch_db, write_db, out_path=None):
     copy_f, copy_w = copy_mean(find(fetch, COPY_KERNEL)), copy_mean(find(write, COPY_KERNEL))
     cal = (f"{COPY_KERNEL} of 1 GiB (bench.py --rows copy): FETCH_SIZE {copy_f:.1f} KiB, "
            f"WRITE_SIZE {copy_w:.1f} KiB per dispatch")
-    cmd = "python bench.py --rows decode,copy --no-cpu --steps 3 --warmup 1"
+    cmd = "python bench.py --rows decode,copy,varlen,window --no-cpu --steps 3 --warmup 1"
     out = {}
     for key, src, kname, which in TRAFFIC_KERNELS:
+        grid = TRAFFIC_GRID.get(key)
+        fk = _counter_values(fetch_db, "FETCH_SIZE", grid) if grid else fetch
+        wk = _counter_values(write_db, "WRITE_SIZE", grid) if grid else write
         out[key] = {"kernel": kname, "sources": src, "source_sha256": kernel_source_digest(src),
-                    "fetch_kib": round(_cluster_mean(find(fetch, kname), which), 1),
+                    "grid_threads": grid,
+                    "fetch_kib": round(_cluster_mean(find(fk, kname), which), 1),
                     "fetch_scale": round(COPY_KIB / copy_f, 5),
-                    "write_kib": round(_cluster_mean(find(write, kname), which), 1),
+                    "write_kib": round(_cluster_mean(find(wk, kname), which), 1),
                     "write_scale": round(COPY_KIB / copy_w, 5), "calibration": cal,
                     "commands": [f"rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -- {cmd}",
                                  f"rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -- {cmd}",
@@ -513,7 +522,11 @@ def main():
                         "H=32 as 8 KV groups x 4, K=Kv=128 bf16",
             "ms_per_call": round(ms_v, 5), "value": round(tf, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl}, **tm}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl,
+                         "traffic": recorded_traffic("fwd_bf16 varlen gqa causal 8 seqs"),
+                         "algorithmic_bytes": 20608 * M,
+                         "note": "algorithmic bytes: q and out 8192 B per row, the unique K and V of the 8 groups "
+                                 "2048 B each, lse 128 B"}, **tm}
         if not args.no_cpu:  # the whole packed workload, k and v broadcast over the 4 heads of a group
             qo = synth.to_f64(synth.normal(5, synth.TAG_Q, (1, M, 8, 4, 128), "bf16"), "bf16").reshape(1, M, 32, 128)
             ko, vo = (np.broadcast_to(synth.to_f64(synth.normal(5, tag, (1, M, 8, 1, 128), "bf16"), "bf16"),
@@ -577,7 +590,9 @@ def main():
             "workload": "bf16 B=2 M=8192 H=32 K=Kv=128, causal window of 1024 keys (bottom-right local mask)",
             "ms_per_call": round(ms_w, 5), "value": round(tf, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl}, **tm}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl,
+                         "traffic": recorded_traffic("fwd_bf16 sliding window 1024 2x8192x32x128"),
+                         "algorithmic_bytes": 4 * Bw * Mw * Hw * Dw * 2 + Bw * Hw * Mw * 4}, **tm}
         if not args.no_cpu:  # batch element 0, heads 0..3 of 32
             sample = [synth.to_f64(x[:1, :, :4], "bf16") for x in (qh4, kh4, vh4)]
             result["rows"]["sliding_window_causal"]["cpu_oracle"] = oracle_timing(

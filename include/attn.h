@@ -23,6 +23,7 @@
  *   Further entry points, each documented at its declaration below:
  *   attn_fwd_ex / attn_partial_ex (bottom-right and sliding-window masks),
  *   attn_decode_splitkv_noalloc (the decode with library-held scratch, no workspace),
+ *   attn_decode_num_splits (a split count for a decode shape),
  *   attn_decode_splitkv_paged (padded lanes or a paged KV cache),
  *   attn_decode_splitkv_fp8 / attn_decode_splitkv_int4 (quantised KV caches) and
  *   attn_bwd (gradients from the forward's output and LSE).
@@ -210,12 +211,21 @@ attn_status attn_bwd(const attn_tensor *dout, const attn_tensor *q, const attn_t
                      size_t workspace_bytes, const attn_tensor *dq, const attn_tensor *dk,
                      const attn_tensor *dv, attn_stream_t stream);
 
+/* A split count for the split-KV decodes (the pages' get_split_k(B, H, Mk) of ck_splitk.FwOp and
+ * triton_splitk.FwOp): the smallest power of two S <= ATTN_MAX_CHUNKS with B * H_total * S at least
+ * eight per compute unit of the current device, while chunks keep >= 256 keys (S = 1 for empty
+ * shapes).  Measured on MI355X within a few percent of the best split over 1..128 for B*H_total
+ * from 16 to 4096 and Mkv from 1 K to 128 K keys.  Host-only: reads the device's compute-unit
+ * count once per device (256 when no device answers), enqueues nothing. */
+int32_t attn_decode_num_splits(int64_t B, int64_t H_total, int64_t Mkv);
+
 /* Bytes of device workspace attn_decode_splitkv needs (fp32 partial outputs
  * [num_splits, B, H_total, Kv] and LSEs [num_splits, B, H_total], 256-byte aligned). */
 size_t attn_decode_workspace_bytes(int64_t B, int64_t H_total, int64_t Kv, int32_t num_splits);
 
 /* Split-KV decode (Glossary "split-K / split-KV"; ck_splitk.FwOp_S* fixes the split count).
- *   q [B, 1, (G,) H, K], k/v [B, Mkv, (G,) H, K]; bf16 or fp32, K == Kv in {64, 128}.
+ *   q [B, 1, (G,) H, K], k/v [B, Mkv, (G,) H, K]; bf16 or fp32, K == Kv in {64, 128, 256}
+ *   (ck_splitk.FwOp: head dims up to 256).
  *   num_splits in [1, ATTN_MAX_CHUNKS]: chunk s covers keys
  *   [s*c, min(Mkv, (s+1)*c)) with c = ceil(Mkv / num_splits); a chunk may be empty.
  *   workspace: device, 256-byte aligned, >= attn_decode_workspace_bytes(...).
@@ -271,7 +281,7 @@ attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k
  * backends read directly; triton_splitk.FwOp: row-wise FP8 caches).  Stored row r of head h
  * holds D codes and one (scale, shift) pair; its values are  fp8(code) * scale + shift,  and
  * the result is that of attn_decode_splitkv / _paged on those values.
- *   q [B, 1, (G,) H, D] bf16, D in {64, 128}.
+ *   q [B, 1, (G,) H, D] bf16, D in {64, 128, 256}.
  *   k, v: ATTN_DTYPE_FP8_E4M3 caches laid out as in attn_decode_splitkv (seqlens and
  *     block_tables both NULL: every sequence holds all of its lane), or as in
  *     attn_decode_splitkv_paged (seqlens given: padded lanes; block_tables too: paged).
@@ -292,7 +302,7 @@ attn_status attn_decode_splitkv_fp8(const attn_tensor *q, const attn_tensor *k, 
  * row/group INT4 caches stored through int32 words).  Row r of head h holds D codes
  * 0..15, eight per 32-bit word, and G (scale, shift) pairs, one per group of D/G
  * consecutive elements; element d is  code_d * scale_g + shift_g  with g = d / (D/G).
- *   q [B, 1, (G,) H, D] bf16, D in {64, 128}.
+ *   q [B, 1, (G,) H, D] bf16, D in {64, 128, 256}.
  *   k, v: ATTN_DTYPE_INT4X2 caches, last dim D/2 bytes, laid out as in
  *     attn_decode_splitkv_fp8 (lanes, padded lanes or pages).
  *   k_scale_shift, v_scale_shift: ATTN_DTYPE_F16, the shape of k with the last axis 2G

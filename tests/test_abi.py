@@ -18,12 +18,13 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(attn_[a-z0-9_]+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\*?\s*(attn_[a-z0-9_]+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd", "attn_partial", "attn_fwd_ex", "attn_partial_ex", "attn_merge",
-                                           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_noalloc",
+                                           "attn_decode_workspace_bytes", "attn_decode_num_splits", "attn_decode_splitkv",
+                                           "attn_decode_splitkv_noalloc",
                                            "attn_decode_splitkv_paged",
                                            "attn_decode_splitkv_fp8", "attn_decode_splitkv_int4", "attn_bwd_workspace_bytes",
                                            "attn_bwd",
@@ -343,3 +344,20 @@ def test_noalloc_scratch_size_matches_the_header():
     text = open(HEADER).read()
     m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == A.NOALLOC_SCRATCH_BYTES
+
+
+def test_decode_num_splits_fills_the_device_with_chunks_of_256_keys_or_more():
+    # host-only: with no GPU the library assumes MI355X's 256 compute units; B * H * S reaches 8 per
+    # unit unless chunks would fall below 256 keys, and S stays a power of two <= 128
+    cus = 256
+    for B, H, M in [(16, 32, 32768), (1, 32, 32768), (1, 8, 131072), (64, 32, 4096), (128, 8, 1024),
+                    (4, 32, 8192), (16, 16, 16384), (32, 8, 2048), (1, 1, 100), (3, 5, 1 << 20)]:
+        S = A.attn_decode_num_splits(B, H, M)
+        assert 1 <= S <= 128 and S & (S - 1) == 0
+        enough = B * H * S >= 8 * cus or S == 128 or M // (2 * S) < 256
+        assert enough, (B, H, M, S)
+        assert S == 1 or M // S >= 256, (B, H, M, S)
+        assert S == 1 or B * H * (S // 2) < 8 * cus, (B, H, M, S)  # the smallest such power of two
+    assert A.attn_decode_num_splits(16, 32, 32768) == 4
+    assert A.attn_decode_num_splits(1, 32, 32768) == 64
+    assert A.attn_decode_num_splits(0, 32, 32768) == 1

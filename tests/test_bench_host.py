@@ -30,9 +30,11 @@ def test_cluster_mean_splits_two_workloads_at_the_widest_gap():
 
 
 def _counter_db(path, counter, rows):
+    """rows: (kernel name, value) or (kernel name, value, grid in threads)."""
     con = sqlite3.connect(path)
-    con.execute("create table counters_collection (kernel_name text, counter_name text, value real)")
-    con.executemany("insert into counters_collection values (?, ?, ?)", [(k, counter, v) for k, v in rows])
+    con.execute("create table counters_collection (kernel_name text, grid_size integer, counter_name text, value real)")
+    con.executemany("insert into counters_collection values (?, ?, ?, ?)",
+                    [(r[0], r[2] if len(r) > 2 else 64, counter, r[1]) for r in rows])
     con.commit()
     con.close()
 
@@ -42,9 +44,15 @@ def test_write_traffic_from_counter_databases(tmp_path):
     # a 1 GiB copy that reports half its bytes on FETCH_SIZE and all of them on WRITE_SIZE
     fetch = [(copy, 524288.0), (copy, 524288.0), (copy, 8.0)]
     write = [(copy, 1048576.0), (copy, 1048576.0)]
-    for key, src, kname, which in bench.TRAFFIC_KERNELS:
+    fwd_vals = {}
+    for i, (key, src, kname, which) in enumerate(bench.TRAFFIC_KERNELS):
         base = {"fwd": 1000.0, "decode": 5000.0}[src]
-        if which is None:
+        grid = bench.TRAFFIC_GRID.get(key)
+        if grid:  # one forward kernel on three grids: each record takes only its own grid's dispatches
+            fwd_vals[key] = base + 100.0 * i
+            fetch.append((f"void attn::{kname}(args)", fwd_vals[key], grid))
+            write.append((f"void attn::{kname}(args)", 10.0, grid))
+        elif which is None:
             fetch.append((f"void attn::{kname}(args)", base))
             write.append((f"void attn::{kname}(args)", 10.0))
     # the two INT4 workloads share a kernel name: values 3000 (G=1) and 3500 (G=4)
@@ -62,9 +70,11 @@ def test_write_traffic_from_counter_databases(tmp_path):
     assert g1["fetch_scale"] == pytest.approx(2.0) and g1["write_scale"] == pytest.approx(1.0)
     fwd = rec["fwd_bf16 causal 2x2048x32x128"]
     assert fwd["source_sha256"] == bench.kernel_source_digest("fwd")
+    for key, val in fwd_vals.items():
+        assert rec[key]["fetch_kib"] == pytest.approx(val)
     # bytes per launch = FETCH x scale + WRITE x scale, in bytes
     assert bench.recorded_traffic("fwd_bf16 causal 2x2048x32x128", str(out)) == pytest.approx(
-        (1000.0 * 2.0 + 10.0) * 1024)
+        (fwd_vals["fwd_bf16 causal 2x2048x32x128"] * 2.0 + 10.0) * 1024)
 
 
 def test_stale_digest_retires_the_record(tmp_path):

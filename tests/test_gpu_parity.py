@@ -1224,3 +1224,57 @@ def test_merge_max_chunks(A):
     torch.cuda.synchronize()
     check(out, lse, mo, ml, 1e-5, 1e-5, "merge S=128")
     assert math.isinf(lse[0, 1, 5].item()) and torch.all(out[0, 5, 1] == 0)
+
+
+# ------------------------------------------------------------------ head dim 256 decodes, automatic splits
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_head_dim_256(A, dtype):
+    """ck_splitk.FwOp takes head dims up to 256: contiguous lanes and padded lanes, uneven chunks."""
+    tol_o, tol_l = (TOL_BF16_OUT, TOL_LSE) if dtype == "bf16" else (TOL_F32, TOL_F32)
+    B, M, H, D = 3, 1000, 8, 256
+    say(f"case: decode head dim 256 {dtype}")
+    qh, kh, vh = synth.qkv(51, (B, 1, H, D), (B, M, H, D), (B, M, H, D), dtype)
+    q, k, v = dev(qh, dtype), dev(kh, dtype), dev(vh, dtype)
+    out, lse = A.attn_decode_splitkv(q, k, v, 7)
+    lens = np.array([1000, 1, 517], dtype=np.int32)
+    outp, lsep = A.attn_decode_splitkv_paged(q, k, v, torch.from_numpy(lens).cuda(), 5, 1000)
+    torch.cuda.synchronize()
+    oo, ol = run_oracle(qh, kh, vh, 0, dtype)
+    check(out, lse, oo, ol, tol_o, tol_l, "lanes")
+    for b in range(B):
+        oo, ol = run_oracle(qh[b:b + 1], kh[b:b + 1, :lens[b]], vh[b:b + 1, :lens[b]], 0, dtype)
+        check(outp[b:b + 1], lsep[b:b + 1], oo, ol, tol_o, tol_l, f"padded lane {b} len={lens[b]}")
+
+
+def test_quantised_decodes_head_dim_256(A):
+    """FP8 (row-wise) and INT4 (1 and 8 groups of 32) caches with head dim 256: fp32 outputs."""
+    B, M, H, D = 2, 700, 4, 256
+    qh = synth.normal(52, synth.TAG_Q, (B, 1, H, D), "bf16")
+    say("case: fp8 decode head dim 256")
+    kc, vc, kss, vss = _fp8_cache(52, (B, M, H, D))
+    out, lse = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), _fp8(kc), _fp8(vc), _f16(kss), _f16(vss), 6,
+                                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oo, ol = _fp8_oracle(qh, kc, vc, kss, vss)
+    check(out, lse, oo, ol, TOL_F32, TOL_F32, "fp8 D=256")
+    for G in (1, 8):
+        say(f"case: int4 decode head dim 256 G={G}")
+        kc, vc, kss, vss = _int4_cache(53, (B, M, H, D), G)
+        out, lse = A.attn_decode_splitkv_int4(dev(qh, "bf16"), _u8(kc), _u8(vc), _flat_ss(kss), _flat_ss(vss), 6,
+                                              out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        oo, ol = _int4_oracle(qh, kc, vc, kss, vss)
+        check(out, lse, oo, ol, TOL_F32, TOL_F32, f"int4 D=256 G={G}")
+
+
+@pytest.mark.parametrize("B,H,M", [(1, 32, 32768), (16, 32, 4096), (4, 8, 3000)])
+def test_decode_automatic_split_count(A, B, H, M):
+    """num_splits=None takes attn_decode_num_splits(B, H, Mkv); the result is the oracle's."""
+    S = A.attn_decode_num_splits(B, H, M)
+    say(f"case: decode B={B} H={H} M={M}, automatic split count {S}")
+    qh, kh, vh = synth.qkv(54, (B, 1, H, 128), (B, M, H, 128), (B, M, H, 128), "bf16")
+    out, lse = A.attn_decode_splitkv(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), None)
+    torch.cuda.synchronize()
+    oo, ol = oracle.attention(*(f64_threads(x) for x in (qh, kh, vh)))
+    check(out, lse, oo, ol, TOL_BF16_OUT, TOL_LSE, f"S={S}")

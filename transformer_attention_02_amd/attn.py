@@ -61,6 +61,8 @@ _lib.attn_partial_ex.argtypes = _lib.attn_fwd_ex.argtypes
 _lib.attn_partial_ex.restype = ctypes.c_int
 _lib.attn_merge.argtypes = [ctypes.c_int32, _T, _P(ctypes.c_void_p), _T, ctypes.c_void_p, ctypes.c_void_p]
 _lib.attn_merge.restype = ctypes.c_int
+_lib.attn_decode_num_splits.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+_lib.attn_decode_num_splits.restype = ctypes.c_int32
 _lib.attn_decode_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
 _lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.attn_decode_splitkv.argtypes = [_T, _T, _T, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
@@ -336,8 +338,16 @@ def attn_decode_workspace_bytes(B: int, H_total: int, Kv: int, num_splits: int) 
     return int(_lib.attn_decode_workspace_bytes(B, H_total, Kv, num_splits))
 
 
+def attn_decode_num_splits(B: int, H_total: int, Mkv: int) -> int:
+    """The library's split count for a decode of B x H_total rows over Mkv keys."""
+    return int(_lib.attn_decode_num_splits(int(B), int(H_total), int(Mkv)))
+
+
 def attn_decode_splitkv(q, k, v, num_splits, scale=None, workspace=None, out=None, lse=True, stream=None):
-    """Split-KV decode for q [B,1,(G,)H,K]: returns (out, lse or None)."""
+    """Split-KV decode for q [B,1,(G,)H,K]: returns (out, lse or None).  num_splits None: the
+    library's choice (attn_decode_num_splits)."""
+    if num_splits is None:
+        num_splits = attn_decode_num_splits(q.shape[0], _htot(q), k.shape[1])
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is True:
@@ -397,7 +407,10 @@ def _paged_args(q, k, v, seqlens, block_tables, page_size, max_seqlen_k, num_spl
 
 def attn_decode_splitkv_paged(q, k, v, seqlens, num_splits, max_seqlen_k, block_tables=None, page_size=None,
                               scale=None, workspace=None, out=None, lse=True, stream=None):
-    """Split-KV decode against padded lanes (block_tables None) or a paged cache: returns (out, lse or None)."""
+    """Split-KV decode against padded lanes (block_tables None) or a paged cache: returns (out, lse or None).
+    num_splits None: the library's choice for max_seqlen_k keys."""
+    if num_splits is None:
+        num_splits = attn_decode_num_splits(q.shape[0], _htot(q), max_seqlen_k)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is True:
@@ -442,6 +455,8 @@ def attn_decode_splitkv_fp8(q, k, v, k_scale_shift, v_scale_shift, num_splits, s
     """Split-KV decode over FP8 E4M3 K/V caches (torch.float8_e4m3fn) with float16 (scale, shift)
     pairs [..., 2] per cache row and head; lanes, padded lanes (seqlens) or pages (block_tables).
     Returns (out, lse or None)."""
+    if num_splits is None:  # the library's choice for the keys a sequence may hold
+        num_splits = attn_decode_num_splits(q.shape[0], _htot(q), max_seqlen_k or k.shape[1])
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if lse is True:
@@ -515,6 +530,8 @@ def attn_decode_splitkv_int4(q, k, v, k_scale_shift, v_scale_shift, num_splits, 
     """Split-KV decode over INT4 K/V caches: uint8 tensors [..., D/2] (two 4-bit codes per byte,
     even element low) with float16 (scale, shift) pairs [..., 2G] per cache row, head and group.
     Lanes, padded lanes (seqlens) or pages (block_tables).  Returns (out, lse or None)."""
+    if num_splits is None:  # the library's choice for the keys a sequence may hold
+        num_splits = attn_decode_num_splits(q.shape[0], _htot(q), max_seqlen_k or k.shape[1])
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if lse is True:

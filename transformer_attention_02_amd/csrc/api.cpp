@@ -476,6 +476,27 @@ attn_status attn_bwd(const attn_tensor *dot, const attn_tensor *qt, const attn_t
                          fn);
 }
 
+int32_t attn_decode_num_splits(int64_t B, int64_t H_total, int64_t Mkv) {
+    if (B <= 0 || H_total <= 0 || Mkv <= 0) return 1;
+    // compute units of the current device (256 on MI355X; that value when no device answers)
+    static int cus[64] = {};
+    int dev = 0, n = 256;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        if (!cus[dev]) {
+            int c = 0;
+            cus[dev] = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0 ? c : 256;
+        }
+        n = cus[dev];
+    } else {
+        (void)hipGetLastError();  // leave no error behind for the caller's next HIP call
+    }
+    // enough (split, batch, head) rows for 8 per compute unit, chunks of at least 256 keys
+    const int64_t units = B * H_total, target = 8 * (int64_t)n;
+    int32_t S = 1;
+    while (S < ATTN_MAX_CHUNKS && units * S < target && Mkv / (2 * S) >= 256) S *= 2;
+    return S;
+}
+
 size_t attn_decode_workspace_bytes(int64_t B, int64_t H_total, int64_t Kv, int32_t num_splits) {
     if (B < 0 || H_total < 0 || Kv < 0 || num_splits < 1) return 0;
     const size_t rows = (size_t)num_splits * (size_t)B * (size_t)H_total;
@@ -541,7 +562,8 @@ attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_
     if (v.M != k.M) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: k and v have different key counts", fn);
     if (k.D != q.D || v.D != q.D || o.D != q.D)
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out head dims must match", fn);
-    if (!(q.D == 64 || q.D == 128)) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim must be 64 or 128", fn);
+    if (!(q.D == 64 || q.D == 128 || q.D == 256))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim must be 64, 128 or 256", fn);
     if (num_splits < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: num_splits must be >= 1", fn);
     if (num_splits > ATTN_MAX_CHUNKS)
         return fail(ATTN_ERR_UNSUPPORTED, "%s: num_splits must be <= %d", fn, ATTN_MAX_CHUNKS);

@@ -496,6 +496,7 @@ hipError_t launch_elem(const DecodeArgs &a, int elem, hipStream_t stream) {
 hipError_t launch_decode_partials(const DecodeArgs &a, int elem, hipStream_t stream) {
     if (a.D == 128) return launch_elem<128>(a, elem, stream);
     if (a.D == 64) return launch_elem<64>(a, elem, stream);
+    if (a.D == 256) return launch_elem<256>(a, elem, stream);
     return hipErrorInvalidValue;
 }
 
