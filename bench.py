@@ -40,8 +40,9 @@ def parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=300,
                    help="untimed steps first; ~25 ms of back-to-back launches brings the clock to steady state")
-    p.add_argument("--rows", default="full,bwd,decode,varlen,window,merge,fp32",
-                   help="rows timed after the headline prefill: full,bwd,decode,varlen,window,merge,fp32,copy or none; "
+    p.add_argument("--rows", default="full,bwd,decode,kvcache,varlen,window,merge,fp32",
+                   help="rows timed after the headline prefill: full,bwd,decode,kvcache,varlen,window,merge,fp32,copy or "
+                        "none (kvcache needs decode: it reuses the decode cache); "
                         "copy is a plain 1 GiB device copy used to calibrate the HBM byte counters")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--rocpd", metavar="DB", help="summarise a rocprofv3 results database (kernel durations and "
@@ -425,6 +426,48 @@ def main():
                 "sequence 0 of 16: its 32768 keys gathered through the block table and widened, then fp64 "
                 "exact attention over all 32 heads; GB/s of its bf16 K+V")
             del k0, v0
+        if "kvcache" in rows:
+            # chunked prefill against the same cache as 2048 pages of 256 keys in a random order:
+            # 256 new queries per sequence, causal with offset (PagedBlockDiagonalCausalWithOffsetPaddedKeysMask)
+            pg, Lq = 256, 256
+            permk = np.random.Generator(np.random.PCG64(7)).permutation(B * Mkv // pg).astype(np.int32)
+            tab_k = torch.from_numpy(permk.reshape(B, Mkv // pg)).to("cuda")
+            qkh = synth.normal(8, synth.TAG_Q, (1, B * Lq, H, D), "bf16")
+            qk = up(qkh)
+            ssq = torch.from_numpy(np.arange(0, B * Lq + 1, Lq, dtype=np.int32)).to("cuda")
+            ok_ = torch.empty_like(qk)
+            lk_ = torch.empty((1, H, B * Lq), dtype=torch.float32, device="cuda")
+            Sk = 4
+            wsk = torch.empty(A.attn_fwd_kvcache_workspace_bytes(B * Lq, H, D, Sk), dtype=torch.uint8, device="cuda")
+            tm = {}
+            ms_k = timed(A.prepare_fwd_kvcache(qk, kd.view(1, B * Mkv, H, D), vd.view(1, B * Mkv, H, D), ssq, lens, Lq,
+                                               Mkv, ok_, lk_, mask=A.MASK_CAUSAL_BR, block_tables=tab_k, page_size=pg,
+                                               num_splits=Sk, workspace=wsk), 20, 3, torch, detail=tm)
+            vis = Lq * (Mkv - Lq) + Lq * (Lq + 1) / 2  # keys seen per (sequence, head)
+            fl_k = 4.0 * D * H * B * vis
+            tf_k = fl_k / (ms_k * 1e-3) / 1e12
+            log(f"kv-cache chunked prefill: {ms_k * 1e3:.1f} us/call, {tf_k:.1f} TFLOP/s")
+            result["rows"]["kvcache_chunked_prefill"] = {
+                "workload": "16 sequences x 256 new queries against 32768 cached keys each, cache in 2048 pages of 256 "
+                            "keys (random order), causal with offset, H=32 K=Kv=128 bf16, 4 key chunks + merge "
+                            "(attn_fwd_kvcache)",
+                "ms_per_call": round(ms_k, 5), "value": round(tf_k, 2), "unit": "TFLOP/s",
+                "kv_GBps": round(kv_bytes / (ms_k * 1e-3) / 1e9, 1),
+                "roofline": {"bound": "mfma", "achieved": round(tf_k, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tf_k / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_k}, **tm}
+            if not args.no_cpu:  # sequence 0's keys gathered through its table, its 256 queries, all 32 heads
+                rows_k = (permk[:Mkv // pg, None] * pg + np.arange(pg)[None, :]).reshape(-1)
+                kq0 = synth.to_f64(qkh[:, :Lq], "bf16")
+
+                def kv_oracle():
+                    kg, vg = (synth.to_f64(x[:, rows_k], "bf16") for x in (kdh.reshape(1, B * Mkv, H, D),
+                                                                        vdh.reshape(1, B * Mkv, H, D)))
+                    oracle_mod().attention(kq0, kg, vg, mask=oracle_mod().MASK_CAUSAL_BR)
+
+                result["rows"]["kvcache_chunked_prefill"]["cpu_oracle"] = oracle_timing(
+                    kv_oracle, fl_k / B / 1e12, "TFLOP/s",
+                    "sequence 0 of 16 (256 queries x 32768 keys gathered from its pages, all 32 heads), fp64")
+            del qk, ok_, lk_, wsk
         del kd, vd, kdh, vdh
         torch.cuda.empty_cache()
 

@@ -22,6 +22,7 @@
  *
  *   Further entry points, each documented at its declaration below:
  *   attn_fwd_ex / attn_partial_ex (bottom-right and sliding-window masks),
+ *   attn_fwd_kvcache (packed query blocks against padded or paged KV caches),
  *   attn_decode_splitkv_noalloc (the decode with library-held scratch, no workspace),
  *   attn_decode_num_splits (a split count for a decode shape),
  *   attn_decode_splitkv_paged (padded lanes or a paged KV cache),
@@ -186,6 +187,42 @@ attn_status attn_partial_ex(const attn_tensor *q, const attn_tensor *k, const at
 attn_status attn_merge(int32_t n_chunks, const attn_tensor *out_chunks,
                        const float *const *lse_chunks, const attn_tensor *out, float *lse_out,
                        attn_stream_t stream);
+
+/* Bytes of device workspace attn_fwd_kvcache needs with num_splits >= 2 (fp32 partial outputs
+ * [num_splits, Mq, H_total, Kv] and LSEs [num_splits, H_total, Mq], 256-byte aligned); 0 for 1. */
+size_t attn_fwd_kvcache_workspace_bytes(int64_t Mq, int64_t H_total, int64_t Kv, int32_t num_splits);
+
+/* Packed query blocks against a KV cache ("Attention - Biases & masks": BlockDiagonalPaddedKeysMask,
+ * BlockDiagonalCausalWithOffsetPaddedKeysMask, BlockDiagonalLocalAttentionPaddedKeysMask,
+ * BlockDiagonalCausalLocalAttentionPaddedKeysMask and their Paged... forms, "packed Q blocks attending
+ * fixed-capacity padded K/V lanes" mapped to physical cache pages): chunked prefill and several
+ * queries per sequence, e.g. speculative decoding.
+ *   q [1, Mq, (G,) H, K] bf16: sequence s owns query rows seqstart_q[s] .. seqstart_q[s+1]-1
+ *     (DEVICE int32 [nseq + 1] prefix sums; every block at most max_seqlen_q rows).
+ *   seqlens_k: DEVICE int32 [nseq], keys held by each sequence (clamped to [0, cap]).
+ *   block_tables NULL: k/v are padded lanes [B >= nseq, cap, (G,) H, K/Kv]; sequence s owns keys
+ *     0 .. seqlens_k[s]-1 of lane s.
+ *   block_tables non-NULL: DEVICE int32 [nseq, max_blocks_per_seq] page numbers; k/v are the cache
+ *     [1, num_pages * page_size, (G,) H, D] (K == Kv); key j of sequence s is cache row
+ *     block_tables[s][j / page_size] * page_size + j % page_size; page_size a multiple of 64 and
+ *     max_blocks_per_seq <= 8192 (cap = max_blocks_per_seq * page_size).
+ *   mask: ATTN_MASK_NONE (all of the sequence's keys), ATTN_MASK_CAUSAL_BOTTOMRIGHT (the "with
+ *     offset" causal form: the block's Lq queries are the sequence's last ones, query i sees keys
+ *     j <= i + Lk - Lq), ATTN_MASK_LOCAL_BOTTOMRIGHT (window_left, window_right around that
+ *     diagonal) or ATTN_MASK_CAUSAL_LOCAL_BOTTOMRIGHT (window_size); per sequence, with Lk =
+ *     seqlens_k[s] and Lq its query count.  Rows that see no key get out = 0, lse = -inf.
+ *   num_splits in [1, ATTN_MAX_CHUNKS]: the keys are cut into chunks of ceil(max_seqlen_k /
+ *     num_splits) rounded up to 64 keys; with num_splits >= 2 the chunks' fp32 partial results go to
+ *     `workspace` (device, 256-byte aligned, >= attn_fwd_kvcache_workspace_bytes) and a merge
+ *     launch combines them (for few query blocks over long caches).
+ *   out [1, Mq, (G,) H, Kv] bf16; lse fp32 [1, H_total, Mq] or NULL.  K, Kv in {64, 128}.
+ *   Device metadata is not read by the host; bad values give unspecified results, never an
+ *   out-of-bounds access.  Errors as attn_fwd. */
+attn_status attn_fwd_kvcache(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, const attn_mask *mask,
+                             const int32_t *seqstart_q, int32_t nseq, int32_t max_seqlen_q, const int32_t *seqlens_k,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t page_size,
+                             int32_t max_seqlen_k, int32_t num_splits, float scale, void *workspace,
+                             size_t workspace_bytes, const attn_tensor *out, float *lse, attn_stream_t stream);
 
 /* Bytes of device workspace attn_bwd needs: two fp32 rows per query row and head
  * ([B, H_total, Mq] each, 256-byte aligned). */

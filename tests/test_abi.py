@@ -23,6 +23,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["attn_fwd", "attn_partial", "attn_fwd_ex", "attn_partial_ex", "attn_merge",
+                                           "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_bytes",
                                            "attn_decode_workspace_bytes", "attn_decode_num_splits", "attn_decode_splitkv",
                                            "attn_decode_splitkv_noalloc",
                                            "attn_decode_splitkv_paged",
@@ -361,3 +362,37 @@ def test_decode_num_splits_fills_the_device_with_chunks_of_256_keys_or_more():
     assert A.attn_decode_num_splits(16, 32, 32768) == 4
     assert A.attn_decode_num_splits(1, 32, 32768) == 64
     assert A.attn_decode_num_splits(0, 32, 32768) == 1
+
+
+def test_fwd_kvcache_rejects():
+    # packed queries [1, 300, 8, 128] against 4 lanes of 1024 keys or a paged cache of 64 pages of 256
+    q, o = tensor([1, 300, 8, 128]), tensor([1, 300, 8, 128])
+    lanes = tensor([4, 1024, 8, 128])
+    cache = tensor([1, 64 * 256, 8, 128])
+    ss, lens, tab = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 64), ctypes.c_void_p(FAKE + 128)
+
+    def call(k=lanes, kind=A.MASK_CAUSAL_BR, nseq=4, mq=100, tables=None, mb=0, page=0, mk=1024, S=1, ws=None,
+             wsb=0, qq=q, oo=o, W=0):
+        m = A.AttnMask(kind, W, 0, 0)
+        return A._lib.attn_fwd_kvcache(ctypes.byref(qq), ctypes.byref(k), ctypes.byref(k), ctypes.byref(m), ss, nseq,
+                                       mq, lens, tables, mb, page, mk, S, float("nan"), ws, wsb, ctypes.byref(oo),
+                                       None, None)
+
+    assert call(kind=A.MASK_CAUSAL) == A.ATTN_ERR_INVALID_ARGUMENT and "mask kind" in A.attn_last_error()
+    assert call(kind=A.MASK_BLOCKDIAG) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(nseq=5) == A.ATTN_ERR_INVALID_ARGUMENT and "lane per sequence" in A.attn_last_error()
+    assert call(mq=301) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(mk=1025) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(S=0) == A.ATTN_ERR_INVALID_ARGUMENT and call(S=129) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(S=4) == A.ATTN_ERR_INVALID_ARGUMENT  # no workspace
+    need = A.attn_fwd_kvcache_workspace_bytes(300, 8, 128, 4)
+    assert need == (4 * 300 * 8 * 128 * 4 + 255) // 256 * 256 + (4 * 300 * 8 * 4 + 255) // 256 * 256
+    assert call(S=4, ws=ctypes.c_void_p(FAKE * 256), wsb=need - 1) == A.ATTN_ERR_WORKSPACE_TOO_SMALL
+    assert call(k=cache, tables=tab, mb=64, page=96) == A.ATTN_ERR_UNSUPPORTED and "multiple of 64" in A.attn_last_error()
+    assert call(k=cache, tables=tab, mb=8193, page=256, mk=256) == A.ATTN_ERR_UNSUPPORTED
+    assert call(k=tensor([2, 64 * 256, 8, 128]), tables=tab, mb=64, page=256) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(k=tensor([1, 64 * 256 + 64, 8, 128]), tables=tab, mb=64, page=256) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(qq=tensor([2, 150, 8, 128]), oo=tensor([2, 150, 8, 128])) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(qq=tensor([1, 300, 8, 128], A.ATTN_DTYPE_F32)) == A.ATTN_ERR_UNSUPPORTED
+    assert call(kind=A.MASK_CAUSAL_LOCAL_BR, W=0) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert A.attn_fwd_kvcache_workspace_bytes(300, 8, 128, 1) == 0

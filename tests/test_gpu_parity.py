@@ -1278,3 +1278,112 @@ def test_decode_automatic_split_count(A, B, H, M):
     torch.cuda.synchronize()
     oo, ol = oracle.attention(*(f64_threads(x) for x in (qh, kh, vh)))
     check(out, lse, oo, ol, TOL_BF16_OUT, TOL_LSE, f"S={S}")
+
+
+# ------------------------------------------------------------------ packed queries against a KV cache
+
+_KV_ORACLE_MASK = {0: oracle.MASK_NONE, 4: oracle.MASK_CAUSAL_BR, 6: oracle.MASK_LOCAL_BR, 7: oracle.MASK_CAUSAL_LOCAL_BR}
+
+
+def _kvcache_case(A, lq, lk, cap, H, D, mask, seed, page=None, splits=1, window_size=None, wl=None, wr=None,
+                  G=None, check_seqs=None):
+    """q blocks of lq[s] rows against sequence s's lk[s] keys in padded lanes [nseq, cap] or in a paged
+    cache (a PCG64 permutation of pages); the oracle sees each sequence's own keys gathered."""
+    nseq = len(lq)
+    ss = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    M = int(ss[-1])
+    hs = (1, M, G, H, D) if G else (1, M, H, D)
+    qh = synth.normal(seed, synth.TAG_Q, hs, "bf16")
+    if page:
+        nb = cap // page
+        P = nseq * nb
+        ks_ = (1, P * page, G, H, D) if G else (1, P * page, H, D)
+        tables = np.random.Generator(np.random.PCG64(seed)).permutation(P).astype(np.int32).reshape(nseq, nb)
+    else:
+        ks_ = (nseq, cap, G, H, D) if G else (nseq, cap, H, D)
+    kh = synth.normal(seed, synth.TAG_K, ks_, "bf16")
+    vh = synth.normal(seed, synth.TAG_V, ks_, "bf16")
+    q, k, v = dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16")
+    kw = dict(mask=mask, window_size=window_size, window_left=wl, window_right=wr, num_splits=splits)
+    if page:
+        kw.update(block_tables=torch.from_numpy(tables).cuda(), page_size=page)
+    out, lse = A.attn_fwd_kvcache(q, k, v, torch.from_numpy(ss).cuda(), torch.from_numpy(np.asarray(lk, np.int32)).cuda(),
+                                  int(max(lq)), int(max(lk)), **kw)
+    torch.cuda.synchronize()
+    Ht = (G or 1) * H
+    o64 = host64(out).reshape(1, M, Ht, D)
+    l64 = host64(lse)
+    okw = {}
+    if mask == 7:
+        okw["window"] = window_size
+    if mask == 6:
+        okw["window"], okw["window_right"] = wl, wr
+    for s in (range(nseq) if check_seqs is None else check_seqs):
+        qs_ = qh[:, ss[s]:ss[s + 1]]
+        if page:
+            kf, vf = kh.reshape((1, -1) + kh.shape[2:]), vh.reshape((1, -1) + vh.shape[2:])
+            ksq, vsq = _gather(kf, tables[s], page, lk[s]), _gather(vf, tables[s], page, lk[s])
+        else:
+            ksq, vsq = kh[s:s + 1, :lk[s]], vh[s:s + 1, :lk[s]]
+        oo, ol = oracle.attention(f64_threads(qs_).reshape(1, lq[s], Ht, D), f64_threads(ksq).reshape(1, lk[s], Ht, D),
+                                  f64_threads(vsq).reshape(1, lk[s], Ht, D), mask=_KV_ORACLE_MASK[mask], **okw)
+        eo = maxerr(o64[:, ss[s]:ss[s + 1]], oo)
+        el = maxerr(l64[:, :, ss[s]:ss[s + 1]], ol)
+        say(f"  seq {s} lq={lq[s]} lk={lk[s]}: max|dout|={eo:.3e} max|dlse|={el:.3e}")
+        assert eo <= TOL_BF16_OUT and el <= TOL_LSE, (s, eo, el)
+
+
+@pytest.mark.parametrize("mask", [0, 4])
+def test_kvcache_padded_lanes(A, mask):
+    """BlockDiagonalPaddedKeysMask / BlockDiagonalCausalWithOffsetPaddedKeysMask: query blocks of 1 to 300
+    rows, sequences holding 0 to 2100 keys (one with more queries than keys)."""
+    say(f"case: kv cache padded lanes mask={mask}")
+    _kvcache_case(A, [1, 4, 100, 300, 300], [50, 1000, 0, 2100, 100], 2200, 8, 128, mask, 61)
+
+
+@pytest.mark.parametrize("page,splits", [(64, 1), (256, 1), (128, 4)])
+def test_kvcache_paged_causal_with_offset(A, page, splits):
+    """PagedBlockDiagonalCausalWithOffsetPaddedKeysMask with pages of 64, 128 and 256 keys in a random
+    order, whole and split into key chunks (fp32 partials, then the merge)."""
+    say(f"case: kv cache paged causal page={page} splits={splits}")
+    _kvcache_case(A, [7, 130, 257, 64], [3000, 130, 700, 1], 3072, 8, 128, 4, 62, page=page, splits=splits)
+
+
+def test_kvcache_local_windows(A):
+    """The local padded-keys masks: window (70, 20) around the bottom-right diagonal over pages, and a
+    causal window of 100 keys over lanes split in three chunks."""
+    say("case: kv cache local windows")
+    _kvcache_case(A, [100, 300, 5], [1500, 600, 900], 1536, 8, 128, 6, 63, page=128, wl=70, wr=20)
+    _kvcache_case(A, [100, 300, 5], [1500, 600, 900], 1536, 8, 128, 7, 64, window_size=100, splits=3)
+
+
+def test_kvcache_head_dim_64_and_grouped_heads(A):
+    """Head dim 64 over pages, and grouped q-heads [1, M, 2, 4, 128] against lanes of 2 KV heads
+    expanded with stride 0."""
+    say("case: kv cache head dim 64 paged")
+    _kvcache_case(A, [50, 200], [800, 1999], 2048, 4, 64, 4, 65, page=64)
+    say("case: kv cache grouped heads")
+    lq, lk, cap, G, H, D = [40, 300], [512, 1100], 1200, 2, 4, 128
+    ss = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    M = int(ss[-1])
+    qh = synth.normal(66, synth.TAG_Q, (1, M, G, H, D), "bf16")
+    kh = synth.normal(66, synth.TAG_K, (2, cap, G, 1, D), "bf16")
+    vh = synth.normal(66, synth.TAG_V, (2, cap, G, 1, D), "bf16")
+    out, lse = A.attn_fwd_kvcache(dev(qh, "bf16"), dev(kh, "bf16").expand(2, cap, G, H, D),
+                                  dev(vh, "bf16").expand(2, cap, G, H, D), torch.from_numpy(ss).cuda(),
+                                  torch.from_numpy(np.asarray(lk, np.int32)).cuda(), max(lq), max(lk), mask=4)
+    torch.cuda.synchronize()
+    for s in range(2):
+        rep = lambda x: np.ascontiguousarray(np.broadcast_to(f64_threads(x[s:s + 1, :lk[s]]), (1, lk[s], G, H, D))
+                                             ).reshape(1, lk[s], G * H, D)
+        oo, ol = oracle.attention(f64_threads(qh[:, ss[s]:ss[s + 1]]).reshape(1, lq[s], G * H, D), rep(kh), rep(vh),
+                                  mask=oracle.MASK_CAUSAL_BR)
+        check(out[:, ss[s]:ss[s + 1]].reshape(1, lq[s], G * H, D), lse[:, :, ss[s]:ss[s + 1]], oo, ol, TOL_BF16_OUT,
+              TOL_LSE, f"grouped seq {s}")
+
+
+def test_kvcache_chunked_prefill_full_size(A):
+    """The bench's KV-cache launch: 16 sequences x 256 new queries against 32768 cached keys each in pages of 256
+    (random order), causal with offset, H=32, D=128, 4 key chunks; the oracle checks sequences 0 and 15."""
+    say("case: kv cache chunked prefill full size")
+    _kvcache_case(A, [256] * 16, [32768] * 16, 32768, 32, 128, 4, 67, page=256, splits=4, check_seqs=(0, 15))

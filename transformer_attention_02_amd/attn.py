@@ -61,6 +61,13 @@ _lib.attn_partial_ex.argtypes = _lib.attn_fwd_ex.argtypes
 _lib.attn_partial_ex.restype = ctypes.c_int
 _lib.attn_merge.argtypes = [ctypes.c_int32, _T, _P(ctypes.c_void_p), _T, ctypes.c_void_p, ctypes.c_void_p]
 _lib.attn_merge.restype = ctypes.c_int
+_lib.attn_fwd_kvcache.argtypes = [_T, _T, _T, _P(AttnMask), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, _T,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+_lib.attn_fwd_kvcache.restype = ctypes.c_int
+_lib.attn_fwd_kvcache_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+_lib.attn_fwd_kvcache_workspace_bytes.restype = ctypes.c_size_t
 _lib.attn_decode_num_splits.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
 _lib.attn_decode_num_splits.restype = ctypes.c_int32
 _lib.attn_decode_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
@@ -365,6 +372,62 @@ def attn_decode_splitkv(q, k, v, num_splits, scale=None, workspace=None, out=Non
     return out, lse
 
 
+def attn_fwd_kvcache_workspace_bytes(Mq: int, H_total: int, Kv: int, num_splits: int) -> int:
+    return int(_lib.attn_fwd_kvcache_workspace_bytes(int(Mq), int(H_total), int(Kv), int(num_splits)))
+
+
+def _kvcache_args(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k, mask, window_size, window_left,
+                  window_right, block_tables, page_size, num_splits, scale, workspace, out, lse, stream):
+    _index(seqstart_q, "seqstart_q")
+    if seqlens_k is None:
+        raise ValueError("seqlens_k is required")
+    _cache_index(q, seqlens_k, block_tables, "sequences", B=seqstart_q.numel() - 1)
+    _lse_buf(lse, _htot(q) * q.shape[1])
+    _on_device(seqstart_q=seqstart_q, seqlens_k=seqlens_k, block_tables=block_tables, lse=lse, workspace=workspace)
+    m = AttnMask(int(mask), int(window_size or 0), int(window_left or 0), int(window_right or 0))
+    ds = [desc(q, name="q"), desc(k, name="k"), desc(v, name="v"), desc(out, name="out")]
+    mb = block_tables.shape[1] if block_tables is not None else 0
+    args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), ctypes.byref(m), _ptr(seqstart_q),
+            int(seqstart_q.numel() - 1), int(max_seqlen_q), _ptr(seqlens_k), _ptr(block_tables), int(mb),
+            int(page_size or 0), int(max_seqlen_k), int(num_splits), _scale(scale), _ptr(workspace),
+            _ws_bytes(workspace) if workspace is not None else 0, ctypes.byref(ds[3]), _ptr(lse),
+            _stream(stream, q.device))
+    return args, (ds, m)
+
+
+def attn_fwd_kvcache(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k, mask=MASK_NONE, window_size=None,
+                     window_left=None, window_right=None, block_tables=None, page_size=None, num_splits=1,
+                     scale=None, workspace=None, out=None, lse=True, stream=None):
+    """Packed query blocks [1, Mq, (G,) H, K] against padded KV lanes (block_tables None) or a paged
+    cache, with the padded-keys masks aligned from the bottom right of each sequence (MASK_NONE,
+    MASK_CAUSAL_BR, MASK_LOCAL_BR, MASK_CAUSAL_LOCAL_BR).  Returns (out, lse or None)."""
+    if out is None:
+        out = torch.empty((*q.shape[:-1], v.shape[-1]), dtype=q.dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty((1, _htot(q), q.shape[1]), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    if workspace is None and num_splits > 1:
+        need = attn_fwd_kvcache_workspace_bytes(q.shape[1], _htot(q), v.shape[-1], num_splits)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    args, _keep = _kvcache_args(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k, mask, window_size,
+                                window_left, window_right, block_tables, page_size, num_splits, scale, workspace, out,
+                                lse, stream)
+    _check(_lib.attn_fwd_kvcache(*args))
+    return out, lse
+
+
+def prepare_fwd_kvcache(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k, out, lse, mask=MASK_NONE,
+                        window_size=None, window_left=None, window_right=None, block_tables=None, page_size=None,
+                        num_splits=1, scale=None, workspace=None, stream=None) -> Prepared:
+    """attn_fwd_kvcache with every argument marshalled up front."""
+    args, keep = _kvcache_args(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k, mask, window_size,
+                               window_left, window_right, block_tables, page_size, num_splits, scale, workspace, out,
+                               lse, stream)
+    return Prepared(_lib.attn_fwd_kvcache, args, (keep, q, k, v, seqstart_q, seqlens_k, block_tables, workspace, out,
+                                                   lse))
+
+
 NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
 
 
@@ -380,14 +443,14 @@ def attn_decode_splitkv_noalloc(q, k, v, num_splits, out, lse=None, scale=None, 
     return out, lse
 
 
-def _cache_index(q, seqlens, block_tables):
+def _cache_index(q, seqlens, block_tables, what="batch elements", B=None):
     """seqlens [>= B] and block_tables [>= B, n] int32: the kernels read seqlens[b] and row b of the
-    table for every batch element b of q."""
+    table for every batch element b of q (or every sequence b of B)."""
     _index(seqlens, "seqlens")
     _index(block_tables, "block_tables")
-    B = q.shape[0]
+    B = q.shape[0] if B is None else B
     if seqlens is not None and seqlens.numel() < B:
-        raise ValueError(f"seqlens holds {seqlens.numel()} values; q has {B} batch elements")
+        raise ValueError(f"seqlens holds {seqlens.numel()} values; q has {B} {what}")
     if block_tables is not None and (block_tables.dim() != 2 or block_tables.shape[0] < B):
         raise ValueError(f"block_tables must be 2-D with at least {B} rows, got shape {tuple(block_tables.shape)}")
 

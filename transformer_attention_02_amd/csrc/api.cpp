@@ -242,6 +242,13 @@ attn_status forward(const char *fn, bool partial, const attn_tensor *qt, const a
         a.nseq = 1;
         a.max_seqlen_q = a.Mq;
     }
+    a.kv_groups = (k.s.h == 0 && v.s.h == 0 && q.H > 1) ? (int)(htot(q) / q.H) : 0;
+    a.seqlens_k = nullptr;
+    a.block_tables = nullptr;
+    a.bt_stride = a.page_size = a.num_pages = a.cap = 0;
+    a.splits = 1;
+    a.chunk = 0;
+    a.o_split = a.lse_split = 0;
     hipError_t e;
     if (q.dtype == ATTN_DTYPE_BF16)
         e = attn::launch_fwd_bf16(a, o.dtype == ATTN_DTYPE_F32, (hipStream_t)stream);
@@ -347,6 +354,166 @@ attn_status attn_merge(int32_t n_chunks, const attn_tensor *out_chunks, const fl
     a.chunk_f32 = c0.dtype == ATTN_DTYPE_F32;
     a.out_f32 = o.dtype == ATTN_DTYPE_F32;
     return launch_status(attn::launch_merge(a, (hipStream_t)stream), fn);
+}
+
+size_t attn_fwd_kvcache_workspace_bytes(int64_t Mq, int64_t H_total, int64_t Kv, int32_t num_splits) {
+    if (Mq < 0 || H_total < 0 || Kv < 0 || num_splits < 2) return 0;
+    const size_t rows = (size_t)num_splits * (size_t)Mq * (size_t)H_total;
+    return align256(rows * (size_t)Kv * 4) + align256(rows * 4);
+}
+
+attn_status attn_fwd_kvcache(const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt, const attn_mask *mask,
+                             const int32_t *seqstart_q, int32_t nseq, int32_t max_seqlen_q, const int32_t *seqlens_k,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t page_size,
+                             int32_t max_seqlen_k, int32_t num_splits, float scale, void *workspace,
+                             size_t workspace_bytes, const attn_tensor *ot, float *lse, attn_stream_t stream) {
+    const char *fn = "attn_fwd_kvcache";
+    View q, k, v, o;
+    attn_status st;
+    if ((st = make_view(qt, "q", &q)) != ATTN_OK) return st;
+    if ((st = make_view(kt, "k", &k)) != ATTN_OK) return st;
+    if ((st = make_view(vt, "v", &v)) != ATTN_OK) return st;
+    if ((st = make_view(ot, "out", &o)) != ATTN_OK) return st;
+    if (!mask) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: mask is NULL", fn);
+    if (q.dtype != ATTN_DTYPE_BF16 || k.dtype != q.dtype || v.dtype != q.dtype || o.dtype != q.dtype)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: q, k, v and out must be bf16", fn);
+    if (!same_heads(q, k) || !same_heads(q, v) || !same_heads(q, o))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out must have the same rank and head axes", fn);
+    if (q.B != 1 || o.B != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: packed queries need B == 1", fn);
+    if (o.M != q.M) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out must have q's row count", fn);
+    if (k.D != q.D) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q and k head dims differ", fn);
+    if (o.D != v.D) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: out head dim must equal v's", fn);
+    if (v.M != k.M || v.B != k.B) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: k and v caches differ in shape", fn);
+    if ((st = check_written(fn, "out", o)) != ATTN_OK) return st;
+    // the padded-keys masks: every one aligned from the bottom right of its sequence
+    const int kind = mask->kind;
+    if (kind != ATTN_MASK_NONE && kind != ATTN_MASK_CAUSAL_BOTTOMRIGHT && kind != ATTN_MASK_LOCAL_BOTTOMRIGHT &&
+        kind != ATTN_MASK_CAUSAL_LOCAL_BOTTOMRIGHT)
+        return fail(ATTN_ERR_INVALID_ARGUMENT,
+                    "%s: mask kind %d; the KV-cache forward takes NONE, CAUSAL_BOTTOMRIGHT, LOCAL_BOTTOMRIGHT or "
+                    "CAUSAL_LOCAL_BOTTOMRIGHT",
+                    fn, kind);
+    MaskSpec ms;
+    if ((st = mask_spec(fn, *mask, &ms)) != ATTN_OK) return st;
+    if (nseq < 1 || !seqstart_q || !seqlens_k)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: needs nseq >= 1, seqstart_q and seqlens_k", fn);
+    if ((((uintptr_t)seqstart_q) % 4) || (((uintptr_t)seqlens_k) % 4) || (((uintptr_t)block_tables) % 4))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: index arrays must be 4-byte aligned", fn);
+    if (max_seqlen_q < 0 || max_seqlen_q > q.M)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: max_seqlen_q must be in [0, Mq]", fn);
+    const bool paged = block_tables != nullptr;
+    int64_t cap;
+    if (paged) {
+        if (k.B != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: a paged cache has batch 1", fn);
+        if (page_size < 64 || page_size % 64)
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: page_size must be a multiple of 64 (got %d)", fn, page_size);
+        if (max_blocks_per_seq < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: max_blocks_per_seq must be >= 1", fn);
+        if (max_blocks_per_seq > 8192)
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: at most 8192 pages per sequence (got %d)", fn, max_blocks_per_seq);
+        if (k.M % page_size || k.M == 0)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: the cache must hold a whole number of pages", fn);
+        if (k.D != v.D) return fail(ATTN_ERR_UNSUPPORTED, "%s: a paged cache needs equal head dims", fn);
+        cap = (int64_t)max_blocks_per_seq * page_size;
+        if (cap > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "%s: sequences too long", fn);
+    } else {
+        if (k.B < nseq) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: k/v need a lane per sequence (B >= nseq)", fn);
+        cap = k.M;
+    }
+    if (max_seqlen_k < 0 || max_seqlen_k > cap)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: max_seqlen_k must be in [0, %lld]", fn, (long long)cap);
+    if (num_splits < 1 || num_splits > ATTN_MAX_CHUNKS)
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: num_splits must be in [1, %d]", fn, ATTN_MAX_CHUNKS);
+    if (!(std::isnan(scale) || std::isfinite(scale)))
+        return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: scale must be finite (or NaN for 1/sqrt(K))", fn);
+    if (lse && ((uintptr_t)lse) % 4) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
+    if (!((q.D == 64 || q.D == 128) && (v.D == 64 || v.D == 128)))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: head dims K and Kv must be in {64, 128}", fn);
+    if ((k.M > 1 && (k.s.m < k.D || v.s.m < v.D)) || (k.s.m * 2 * 64 + k.D * 2) >= (int64_t)1 << 31 ||
+        (v.s.m * 2 * 64 + v.D * 2) >= (int64_t)1 << 31)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: key/value row strides must be >= the head dim and < 2^24 bytes", fn);
+    const int64_t Htot = htot(q);
+    const size_t need = attn_fwd_kvcache_workspace_bytes(q.M, Htot, v.D, num_splits);
+    if (q.M == 0 || Htot == 0) return ok();
+    if (num_splits > 1) {
+        if (!workspace || ((uintptr_t)workspace) % 256)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: workspace is NULL or not 256-byte aligned", fn);
+        if (workspace_bytes < need)
+            return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                        workspace_bytes);
+    }
+
+    attn::FwdArgs a;
+    a.q = q.p;
+    a.k = k.p;
+    a.v = v.p;
+    a.sq = q.s;
+    a.sk = k.s;
+    a.sv = v.s;
+    a.B = 1;
+    a.Mq = (int)q.M;
+    a.Mkv = (int)k.M;
+    a.Htot = (int)Htot;
+    a.Hin = (int)q.H;
+    a.K = (int)q.D;
+    a.Kv = (int)v.D;
+    const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)q.D) : (double)scale;
+    a.scale_log2 = (float)(sc * 1.4426950408889634);
+    if (std::fabs(a.scale_log2) < 1e-30f) a.scale_log2 = std::copysign(1e-30f, a.scale_log2);
+    a.packed = 1;
+    a.bottom_right = 1;
+    a.wl = ms.wl;
+    a.wr = ms.wr;
+    a.seqstart_q = seqstart_q;
+    a.seqstart_k = nullptr;
+    a.nseq = nseq;
+    a.max_seqlen_q = max_seqlen_q;
+    a.kv_groups = (k.s.h == 0 && v.s.h == 0 && q.H > 1) ? (int)(Htot / q.H) : 0;
+    a.seqlens_k = seqlens_k;
+    a.block_tables = block_tables;
+    a.bt_stride = paged ? max_blocks_per_seq : 0;
+    a.page_size = paged ? page_size : 0;
+    a.num_pages = paged ? (int)(k.M / page_size) : 0;
+    a.cap = (int)cap;
+    a.splits = num_splits;
+    // chunks of whole 64-key tiles
+    a.chunk = (int)(((int64_t)max_seqlen_k + num_splits - 1) / num_splits + 63) / 64 * 64;
+    const int64_t rows = q.M * Htot;
+    const attn::Strides part{rows * v.D, Htot * v.D, q.H * v.D, v.D};  // [1, Mq, (G,) H, Kv] fp32, per chunk
+    if (num_splits == 1) {
+        a.o = o.p;
+        a.so = o.s;
+        a.lse = lse;
+        a.o_split = a.lse_split = 0;
+        return launch_status(attn::launch_fwd_bf16(a, false, (hipStream_t)stream), fn);
+    }
+    float *ws_o = (float *)workspace;
+    float *ws_lse = (float *)((char *)workspace + align256((size_t)num_splits * rows * v.D * 4));
+    a.o = ws_o;
+    a.so = part;
+    a.lse = ws_lse;
+    a.o_split = rows * v.D;
+    a.lse_split = rows;
+    hipError_t e = attn::launch_fwd_bf16(a, true, (hipStream_t)stream);
+    if (e != hipSuccess) return launch_status(e, fn);
+    attn::MergeArgs m;
+    memset(&m, 0, sizeof m);
+    for (int c = 0; c < num_splits; ++c) {
+        m.chunk[c] = ws_o + (size_t)c * rows * v.D;
+        m.lse[c] = ws_lse + (size_t)c * rows;
+    }
+    m.sc = part;
+    m.o = o.p;
+    m.so = o.s;
+    m.lse_out = lse;
+    m.S = num_splits;
+    m.B = 1;
+    m.M = (int)q.M;
+    m.Htot = (int)Htot;
+    m.Hin = (int)q.H;
+    m.Kv = (int)v.D;
+    m.chunk_f32 = 1;
+    m.out_f32 = 0;
+    return launch_status(attn::launch_merge(m, (hipStream_t)stream), fn);
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H_total, int64_t Mq) {

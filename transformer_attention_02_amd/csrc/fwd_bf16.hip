@@ -78,7 +78,11 @@ __device__ __forceinline__ float pair_sum(float x) {
 // q/k and of v/out.  KSPLIT waves share each 32-row block: with KSPLIT = 2 (and the paired ring)
 // wave 2i takes the first tile of every resident pair and wave 2i + 1 the second, and their
 // softmax states are merged exactly at the end.
-template <int KD, int VD, int NW, int STAGES, bool OUT_F32, int KSPLIT>
+// Entries of a sequence's block-table row resolved into LDS (32 KB): paged caches of up to this many
+// pages per sequence.
+constexpr int kMaxPages = 8192;
+
+template <int KD, int VD, int NW, int STAGES, bool OUT_F32, int KSPLIT, bool PAGED>
 __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     constexpr int NT = NW * 64;                  // threads per workgroup
     constexpr int BM = NW / KSPLIT * 32;         // query rows per workgroup
@@ -98,39 +102,57 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
                   "tile split");
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * (KTILE + VTILE)];
+    __shared__ int ptab[PAGED ? kMaxPages : 1];  // page numbers of this workgroup's key tiles
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // ---- which (tile, sequence, batch*head) this workgroup owns; heaviest tiles first
+    // ---- which (key chunk, tile, sequence, batch*head) this workgroup owns; heaviest tiles first
     const int BH = a.B * a.Htot;
     const int tiles = (a.max_seqlen_q + BM - 1) / BM;
     int id = blockIdx.x;
-    const int bh = id % BH;
+    const int split = id % a.splits;
+    id /= a.splits;
+    int bh = id % BH;
     id /= BH;
+    if (a.kv_groups > 0) {
+        // expanded GQA: consecutive workgroup ids (round-robin over the XCDs) walk the groups
+        // first, so that all heads of a group share an XCD and its L2 copy of the group's K/V
+        const int r = bh % a.Htot;
+        bh += (r % a.kv_groups) * a.Hin + r / a.kv_groups - r;
+    }
     const int seq = id % a.nseq;
     const int tile = tiles - 1 - id / a.nseq;
     const int b = bh / a.Htot, hf = bh % a.Htot;
 
     int qs = 0, qe = a.Mq, ks = 0, ke = a.Mkv;
     if (a.packed) {
-        const int32_t *skp = a.seqstart_k ? a.seqstart_k : a.seqstart_q;
         qs = min(max(a.seqstart_q[seq], 0), a.Mq);
         qe = min(max(a.seqstart_q[seq + 1], qs), a.Mq);
-        ks = min(max(skp[seq], 0), a.Mkv);
-        ke = min(max(skp[seq + 1], ks), a.Mkv);
+        if (a.seqlens_k) {
+            // KV cache: the sequence's keys start at row 0 of its lane (or its first page)
+            ks = 0;
+            ke = min(max(a.seqlens_k[seq], 0), a.cap);
+        } else {
+            const int32_t *skp = a.seqstart_k ? a.seqstart_k : a.seqstart_q;
+            ks = min(max(skp[seq], 0), a.Mkv);
+            ke = min(max(skp[seq + 1], ks), a.Mkv);
+        }
     }
     const int Lq = qe - qs, Lk = ke - ks;
     const int row0 = tile * BM;
     if (tile < 0 || row0 >= Lq) return;
+    // this workgroup's key chunk [kc0, kc1) (the whole sequence unless the keys are split)
+    const int kc0 = a.splits > 1 ? min(split * a.chunk, Lk) : 0;
+    const int kc1 = a.splits > 1 ? min(kc0 + a.chunk, Lk) : Lk;
     // Visible keys of local row i: [lo(i), hi(i)] = [i + shift - wl, i + shift + wr] within [0, Lk),
     // both non-decreasing in i (64-bit: shift and the unbounded extents reach 2^31).
     const int64_t shift = a.bottom_right ? (int64_t)Lk - Lq : 0;
     auto clampk = [&](int64_t x, int64_t lo_, int64_t hi_) { return (int)(x < lo_ ? lo_ : (x > hi_ ? hi_ : x)); };
     const int row_last = min(row0 + BM, Lq) - 1;
-    const int kbeg = clampk((int64_t)row0 + shift - a.wl, 0, Lk);
-    const int kend = clampk((int64_t)row_last + shift + a.wr + 1, 0, Lk);
+    const int kbeg = clampk((int64_t)row0 + shift - a.wl, kc0, kc1);
+    const int kend = clampk((int64_t)row_last + shift + a.wr + 1, kc0, kc1);
     // tiles [tb, te) hold every visible key; [ua, ub) need no mask for any row of the workgroup
     const int tb = kbeg / BN;
     const int te = kend > kbeg ? (kend + BN - 1) / BN : tb;
@@ -140,8 +162,18 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     ub = min(max(ub, ua), te);
 
     const __bf16 *qp = (const __bf16 *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin) + (int64_t)qs * a.sq.m;
-    const __bf16 *kp = (const __bf16 *)a.k + (int64_t)b * a.sk.b + head_offset(a.sk, hf, a.Hin) + (int64_t)ks * a.sk.m;
-    const __bf16 *vp = (const __bf16 *)a.v + (int64_t)b * a.sv.b + head_offset(a.sv, hf, a.Hin) + (int64_t)ks * a.sv.m;
+    // K/V rows of key 0 (a KV cache's lane of this sequence; paged caches start at the cache)
+    const int64_t kvb = a.seqlens_k && !PAGED ? seq : b;
+    const __bf16 *kp = (const __bf16 *)a.k + (PAGED ? 0 : kvb * a.sk.b) + head_offset(a.sk, hf, a.Hin) + (int64_t)ks * a.sk.m;
+    const __bf16 *vp = (const __bf16 *)a.v + (PAGED ? 0 : kvb * a.sv.b) + head_offset(a.sv, hf, a.Hin) + (int64_t)ks * a.sv.m;
+    if constexpr (PAGED) {
+        // page numbers of tiles [tb, te) (pages hold a whole number of 64-key tiles), clamped to the
+        // cache; every wave reads them before its first tile load
+        const int p0 = tb * BN / a.page_size, p1 = te > tb ? ((te * BN - 1) / a.page_size + 1) : p0;
+        for (int i = p0 + tid; i < p1 && i - p0 < kMaxPages; i += NT)
+            ptab[i - p0] = min(max(a.block_tables[(int64_t)seq * a.bt_stride + i], 0), a.num_pages - 1);
+        __syncthreads();
+    }
     const unsigned kstride = (unsigned)a.sk.m * 2u, vstride = (unsigned)a.sv.m * 2u;  // bytes per key row
 
     // ---- async tile loads: global -> LDS, 16 bytes per lane, OOB rows read as zeros
@@ -165,8 +197,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
         const int nvalid = min(BN, Lk - kt0);
         const int slot = (t - tb) % STAGES;
         const unsigned kst = smem_base + slot * KTILE, vst = smem_base + V_BASE + slot * VTILE;
-        const i32x4 kr = make_rsrc(kp + (int64_t)kt0 * a.sk.m, (nvalid - 1) * kstride + KROWB);
-        const i32x4 vr = make_rsrc(vp + (int64_t)kt0 * a.sv.m, (nvalid - 1) * vstride + VROWB);
+        int64_t row = kt0;  // cache row of the tile's first key
+        if constexpr (PAGED)
+            row = (int64_t)min(max(ptab[kt0 / a.page_size - tb * BN / a.page_size], 0), a.num_pages - 1) * a.page_size +
+                  kt0 % a.page_size;
+        const i32x4 kr = make_rsrc(kp + row * a.sk.m, (nvalid - 1) * kstride + KROWB);
+        const i32x4 vr = make_rsrc(vp + row * a.sv.m, (nvalid - 1) * vstride + VROWB);
 #pragma unroll
         for (int r = 0; r < KROUNDS; ++r) dma16(kr, koff[r], kst + (r * NW + wave) * 1024);
 #pragma unroll
@@ -418,18 +454,20 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     // ---- normalise and store
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    unsigned char *const obase_p = (unsigned char *)a.o + split * a.o_split * (OUT_F32 ? 4 : 2);
+    float *const lse_p = a.lse ? a.lse + split * a.lse_split : nullptr;
     if constexpr (!OUT_F32 && KSPLIT == 1) {
         // bf16 rows go out whole, staged in the now idle ring (16-byte stores, whole rows, instead
         // of 8 bytes per lane at 32 rows 8 KB apart)
         __syncthreads();  // every wave has finished reading the K/V ring
-        store_rows_bf16<VD>(o, inv, (unsigned char LDS_AS *)smem + wave * 32 * VROWB, (unsigned char *)a.o,
+        store_rows_bf16<VD>(o, inv, (unsigned char LDS_AS *)smem + wave * 32 * VROWB, obase_p,
                             (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) + (int64_t)(qs + wrow0) * a.so.m,
                             a.so.m, Lq - wrow0);
-        if (qrow < Lq && a.lse && hh == 0)
-            a.lse[((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow] =
+        if (qrow < Lq && lse_p && hh == 0)
+            lse_p[((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow] =
                 l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     } else if (qrow < Lq) {
-        unsigned char *op = (unsigned char *)a.o;
+        unsigned char *op = obase_p;
         const int64_t obase = (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) + (int64_t)(qs + qrow) * a.so.m;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -445,36 +483,37 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
                 }
             }
         }
-        if (a.lse && hh == 0) {
-            a.lse[((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow] =
+        if (lse_p && hh == 0) {
+            lse_p[((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow] =
                 l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
         }
     }
 }
 
-template <int KD, int VD, int NW, int STAGES, bool OUT_F32>
+template <int KD, int VD, int NW, int STAGES, bool OUT_F32, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
-    fwd_bf16_body<KD, VD, NW, STAGES, OUT_F32, 1>(a);
+    fwd_bf16_body<KD, VD, NW, STAGES, OUT_F32, 1, PAGED>(a);
 }
 
 // two waves per 32-row block, splitting its keys (paired ring)
-template <int KD, int VD, bool OUT_F32>
+template <int KD, int VD, bool OUT_F32, bool PAGED>
 __global__ __launch_bounds__(128) void fwd_bf16_split_kernel(FwdArgs a) {
-    fwd_bf16_body<KD, VD, 2, 4, OUT_F32, 2>(a);
+    fwd_bf16_body<KD, VD, 2, 4, OUT_F32, 2, PAGED>(a);
 }
 
-template <int KD, int VD, int NW, int STAGES, bool OUT_F32, int KSPLIT = 1>
+template <int KD, int VD, int NW, int STAGES, bool OUT_F32, bool PAGED, int KSPLIT = 1>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
     constexpr int BM = NW / KSPLIT * 32;
     const int64_t tiles = (a.max_seqlen_q + BM - 1) / BM;
-    const int64_t grid = tiles * a.nseq * (int64_t)a.B * a.Htot;
+    const int64_t grid = tiles * a.nseq * (int64_t)a.B * a.Htot * a.splits;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     if constexpr (KSPLIT == 2)
-        hipLaunchKernelGGL((fwd_bf16_split_kernel<KD, VD, OUT_F32>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
-    else
-        hipLaunchKernelGGL((fwd_bf16_kernel<KD, VD, NW, STAGES, OUT_F32>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
+        hipLaunchKernelGGL((fwd_bf16_split_kernel<KD, VD, OUT_F32, PAGED>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
                            a);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<KD, VD, NW, STAGES, OUT_F32, PAGED>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                           stream, a);
     return hipGetLastError();
 }
 
@@ -490,27 +529,32 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
 #ifndef FWD_MIN_GRID
 #define FWD_MIN_GRID 256
 #endif
-template <int KD, int VD, bool OUT_F32>
+template <int KD, int VD, bool OUT_F32, bool PAGED>
 hipError_t launch_nw(const FwdArgs &a, hipStream_t stream) {
-    const int64_t units = (int64_t)a.nseq * a.B * a.Htot;
+    const int64_t units = (int64_t)a.nseq * a.B * a.Htot * a.splits;
     auto grid = [&](int bm) { return (a.max_seqlen_q + bm - 1) / bm * units; };
-    if (grid(256) >= FWD_MIN_GRID) return launch<KD, VD, 8, 4, OUT_F32>(a, stream);
-    if (grid(128) >= FWD_MIN_GRID) return launch<KD, VD, 4, 3, OUT_F32>(a, stream);
-    if (grid(64) >= FWD_MIN_GRID) return launch<KD, VD, 2, 3, OUT_F32>(a, stream);
+    if (grid(256) >= FWD_MIN_GRID) return launch<KD, VD, 8, 4, OUT_F32, PAGED>(a, stream);
+    if (grid(128) >= FWD_MIN_GRID) return launch<KD, VD, 4, 3, OUT_F32, PAGED>(a, stream);
+    if (grid(64) >= FWD_MIN_GRID) return launch<KD, VD, 2, 3, OUT_F32, PAGED>(a, stream);
     // fewer than FWD_MIN_GRID blocks of 32 rows: two waves split each block's keys
-    return launch<KD, VD, 2, 4, OUT_F32, 2>(a, stream);
+    return launch<KD, VD, 2, 4, OUT_F32, PAGED, 2>(a, stream);
 }
 
-template <int KD, int VD>
+template <int KD, int VD, bool PAGED>
 hipError_t launch_out(const FwdArgs &a, bool out_f32, hipStream_t stream) {
-    return out_f32 ? launch_nw<KD, VD, true>(a, stream) : launch_nw<KD, VD, false>(a, stream);
+    return out_f32 ? launch_nw<KD, VD, true, PAGED>(a, stream) : launch_nw<KD, VD, false, PAGED>(a, stream);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool out_f32, hipStream_t stream) {
-    if (a.K == 128 && a.Kv == 128) return launch_out<128, 128>(a, out_f32, stream);
-    if (a.K == 64 && a.Kv == 64) return launch_out<64, 64>(a, out_f32, stream);
-    if (a.K == 64 && a.Kv == 128) return launch_out<64, 128>(a, out_f32, stream);
-    if (a.K == 128 && a.Kv == 64) return launch_out<128, 64>(a, out_f32, stream);
+    if (a.block_tables) {  // paged KV caches: equal head dims only
+        if (a.K == 128 && a.Kv == 128) return launch_out<128, 128, true>(a, out_f32, stream);
+        if (a.K == 64 && a.Kv == 64) return launch_out<64, 64, true>(a, out_f32, stream);
+        return hipErrorInvalidValue;
+    }
+    if (a.K == 128 && a.Kv == 128) return launch_out<128, 128, false>(a, out_f32, stream);
+    if (a.K == 64 && a.Kv == 64) return launch_out<64, 64, false>(a, out_f32, stream);
+    if (a.K == 64 && a.Kv == 128) return launch_out<64, 128, false>(a, out_f32, stream);
+    if (a.K == 128 && a.Kv == 64) return launch_out<128, 64, false>(a, out_f32, stream);
     return hipErrorInvalidValue;
 }
 

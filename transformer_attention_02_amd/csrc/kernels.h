@@ -39,6 +39,21 @@ struct FwdArgs {
     const int32_t *seqstart_q, *seqstart_k;  // device prefix sums, packed sequences only
     int nseq;            // 1 when not packed
     int max_seqlen_q;    // rows covered per sequence (Mq when not packed)
+    // > 0: the K/V rows of a head depend only on its group hf / Hin (an explicitly expanded GQA
+    // head axis); the kernels then order heads so that the kv_groups = Htot / Hin groups each land
+    // on one XCD, whose L2 serves the group's K/V to all of its heads
+    int kv_groups;
+    // KV cache (packed query blocks against per-sequence keys), bf16 only; seqlens_k null otherwise.
+    // Sequence s holds keys 0 .. seqlens_k[s] - 1 (clamped to [0, cap]): rows of its lane
+    // k + s * sk.b (block_tables null), or rows block_tables[s][j / page_size] * page_size +
+    // j % page_size of the cache k (page numbers clamped to [0, num_pages)).
+    const int32_t *seqlens_k;
+    const int32_t *block_tables;  // [nseq, bt_stride]
+    int bt_stride, page_size, num_pages, cap;
+    // keys cut into `splits` chunks of `chunk` keys (a multiple of the 64-key tile): chunk c of a
+    // query block writes its fp32 partial output at o + c * o_split and its LSE at lse + c * lse_split
+    int splits, chunk;
+    int64_t o_split, lse_split;
 };
 
 // Split-KV decode partials: one query row per (batch, head), keys cut in S chunks.
