@@ -49,7 +49,7 @@ def parse():
                    "counters per kernel and grid) instead of running; no GPU needed")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE rocprofv3 run of "
-                        "'bench.py --rows decode,copy,varlen,window --no-cpu --steps 3 --warmup 1'; no GPU needed")
+                        "'bench.py --rows decode,kvcache,copy,varlen,window --no-cpu --steps 3 --warmup 1'; no GPU needed")
     return p.parse_args()
 
 
@@ -116,11 +116,13 @@ def recorded_traffic(key, path=None):
 # launch the same kernel on the same grid: 0 the lower, 1 the higher, None all; grid in threads, or
 # None for every grid)
 TRAFFIC_GRID = {"fwd_bf16 causal 2x2048x32x128": 512 * 512, "fwd_bf16 varlen gqa causal 8 seqs": 3584 * 512,
-                "fwd_bf16 sliding window 1024 2x8192x32x128": 2048 * 512}
+                "fwd_bf16 sliding window 1024 2x8192x32x128": 2048 * 512,
+                "fwd_bf16 kvcache paged 16x256x32768 s4": 2048 * 512}
 TRAFFIC_KERNELS = (
-    ("fwd_bf16 causal 2x2048x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false>", None),
-    ("fwd_bf16 varlen gqa causal 8 seqs", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false>", None),
-    ("fwd_bf16 sliding window 1024 2x8192x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false>", None),
+    ("fwd_bf16 causal 2x2048x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
+    ("fwd_bf16 varlen gqa causal 8 seqs", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
+    ("fwd_bf16 sliding window 1024 2x8192x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
+    ("fwd_bf16 kvcache paged 16x256x32768 s4", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, true, true>", None),
     ("decode bf16 16x32768x32x128 s64", "decode", "decode_kernel<128, 0, 0>", None),
     ("decode bf16 paged 16x32768x32x128 page64 s64", "decode", "decode_kernel<128, 0, 2>", None),
     ("decode fp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 2, 0>", None),
@@ -170,7 +172,7 @@ def write_traffic(fetch_db, write_db, out_path=None):
     copy_f, copy_w = copy_mean(find(fetch, COPY_KERNEL)), copy_mean(find(write, COPY_KERNEL))
     cal = (f"{COPY_KERNEL} of 1 GiB (bench.py --rows copy): FETCH_SIZE {copy_f:.1f} KiB, "
            f"WRITE_SIZE {copy_w:.1f} KiB per dispatch")
-    cmd = "python bench.py --rows decode,copy,varlen,window --no-cpu --steps 3 --warmup 1"
+    cmd = "python bench.py --rows decode,kvcache,copy,varlen,window --no-cpu --steps 3 --warmup 1"
     out = {}
     for key, src, kname, which in TRAFFIC_KERNELS:
         grid = TRAFFIC_GRID.get(key)
@@ -324,7 +326,7 @@ def main():
     result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                           "traffic": recorded_traffic("fwd_bf16 causal 2x2048x32x128"),
-                          "kernel": "fwd_bf16_kernel<128,128,8,4,false>", "flops_per_launch": flops}
+                          "kernel": "fwd_bf16_kernel<128, 128, 8, 4, false, false>", "flops_per_launch": flops}
 
     # the same shape without a mask: the kernel's steady state, free of the causal diagonal
     if "full" in rows:
@@ -454,7 +456,12 @@ def main():
                 "ms_per_call": round(ms_k, 5), "value": round(tf_k, 2), "unit": "TFLOP/s",
                 "kv_GBps": round(kv_bytes / (ms_k * 1e-3) / 1e9, 1),
                 "roofline": {"bound": "mfma", "achieved": round(tf_k, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(tf_k / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_k}, **tm}
+                             "frac": round(tf_k / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_k,
+                             "traffic": recorded_traffic("fwd_bf16 kvcache paged 16x256x32768 s4"),
+                             "algorithmic_bytes": kv_bytes + B * Lq * H * (2 * D + Sk * (4 * D + 4)),
+                             "note": "traffic and algorithmic bytes are the attention launch's: K+V once, q, and the "
+                                     "fp32 partial rows and LSEs of its 4 key chunks; the time covers it and the merge"},
+                **tm}
             if not args.no_cpu:  # sequence 0's keys gathered through its table, its 256 queries, all 32 heads
                 rows_k = (permk[:Mkv // pg, None] * pg + np.arange(pg)[None, :]).reshape(-1)
                 kq0 = synth.to_f64(qkh[:, :Lq], "bf16")
@@ -671,10 +678,18 @@ def main():
 
             ms_s = timed(split_merge, 100, 5, torch)
             ms_m = timed(merge, 100, 5, torch)
+            # the same S shards as key chunks of one launch (the 1024 keys as one padded lane), then the merge
+            ssq3 = torch.tensor([0, 128], dtype=torch.int32, device="cuda")
+            sl3 = torch.tensor([1024], dtype=torch.int32, device="cuda")
+            ws3 = torch.empty(A.attn_fwd_kvcache_workspace_bytes(128, 16, 128, S), dtype=torch.uint8, device="cuda")
+            ms_1l = timed(A.prepare_fwd_kvcache(q3, k3, v3, ssq3, sl3, 128, 1024, mo, ml, num_splits=S, workspace=ws3),
+                          100, 5, torch)
             mbytes = S * (128 * 16 * 128 * 4 + 16 * 128 * 4) + 128 * 16 * 128 * 2 + 16 * 128 * 4
             entry[f"S{S}"] = {"partials_plus_merge_ms": round(ms_s, 5), "merge_ms": round(ms_m, 5),
-                              "merge_GBps": round(mbytes / (ms_m * 1e-3) / 1e9, 1)}
-            log(f"partial+merge S={S}: {ms_s * 1e3:.1f} us (merge {ms_m * 1e3:.1f} us)")
+                              "merge_GBps": round(mbytes / (ms_m * 1e-3) / 1e9, 1),
+                              "one_launch_chunks_plus_merge_ms": round(ms_1l, 5)}
+            log(f"partial+merge S={S}: {ms_s * 1e3:.1f} us (merge {ms_m * 1e3:.1f} us); "
+                f"as chunks of one launch + merge: {ms_1l * 1e3:.1f} us")
         if not args.no_cpu:  # the oracle's 8 partials over the same shards and their merge
             qo3, ko3, vo3 = (synth.to_f64(x, "bf16") for x in (qh3, kh3, vh3))
 

@@ -450,10 +450,8 @@ def test_climbing_and_falling_row_maxima(A):
     # The backward recomputes P from the saved LSE at these magnitudes.  Its D = dout.out comes
     # from the bf16 out it is given, and in heads 0 and 1 the keys share a component of up to
     # ~145, which multiplies D's rounding into dq (dq_i holds scale * D_i * sum_j P_ij k_j,
-    # which cancels only for exact D).  The oracle measures that sensitivity itself: its
-    # gradients with out rounded to bf16 against those with the exact out.  The bound adds
-    # three times that change (the GPU's out also carries the forward's own error, about one
-    # bf16 half-ulp here) to the usual bf16 gradient tolerance.
+    # which cancels only for exact D).  The derived bound carries that through its D term; the
+    # oracle's own change under a bf16-rounded out is printed beside it.
     gh = synth.normal(900, 3, (1, M, 3, 128), "bf16")
     out, lse = A.attn_fwd(q, k, v, mask=A.MASK_CAUSAL)
     dq, dk, dv = A.attn_bwd(dev(gh, "bf16"), q, k, v, out, lse, mask=A.MASK_CAUSAL)
@@ -463,13 +461,16 @@ def test_climbing_and_falling_row_maxima(A):
     ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, mask=1)
     o_bf16 = synth.to_f64(synth.f32_to_bf16_bits(oo.astype(np.float32)), "bf16")
     ref_b = oracle.attention_backward(g64, o_bf16, ol, q64, k64, v64, mask=1)
-    for name, got, r, rb in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, ref_b):
+    bound = bwd_error_bound(q64, k64, v64, g64, oo, ol, ref, mask=1)
+    for name, got, r, rb, bd in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, ref_b, bound):
         for h in range(3):
-            err, mag = maxerr(host64(got[:, :, h]), r[:, :, h]), float(np.abs(r[:, :, h]).max())
+            gh_ = host64(got[:, :, h])
+            err, mag = maxerr(gh_, r[:, :, h]), float(np.abs(r[:, :, h]).max())
             sens = float(np.abs(r[:, :, h] - rb[:, :, h]).max())
+            ratio = bound_ratio(gh_, r[:, :, h], bd[:, :, h])
             say(f"  climbing maxima bwd {name} head {h}: max|d|={err:.3e} max|ref|={mag:.3e} "
-                f"bf16-out sensitivity={sens:.3e}")
-            assert err <= TOL_BWD_REL * mag + TOL_BWD_ABS + 3 * sens, f"{name} head {h}: error {err}"
+                f"bf16-out sensitivity={sens:.3e} max err/bound={ratio:.3f}")
+            assert ratio <= 1.0, f"{name} head {h}: an element exceeds its error bound ({ratio:.3f}; max|d| {err})"
     assert float(np.abs(ref[0][:, :, 2] - ref_b[0][:, :, 2]).max()) < 0.01  # the plain head is well conditioned
 
 
@@ -828,14 +829,18 @@ def test_fp8_decode_full_size(A):
 
 # ------------------------------------------------------------------ backward (dq, dk, dv)
 
-from tests.helpers import TOL_BWD_ABS, TOL_BWD_REL  # noqa: E402
+from tests.bwd_bound import bound_ratio, bwd_error_bound  # noqa: E402
 
 
-def check_grads(got, ref, what):
-    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
-        err, mag = maxerr(host64(g), r), float(np.abs(r).max()) if r.size else 0.0
-        say(f"  {what} {name}: max|d|={err:.3e} max|ref|={mag:.3e} rel={err / max(mag, 1e-30):.2e}")
-        assert err <= TOL_BWD_REL * mag + TOL_BWD_ABS, f"{what} {name}: error {err} (max|ref| {mag})"
+def check_grads(got, ref, what, bound):
+    """Every gradient element within the worst-case bound derived from the kernels' bf16/fp32
+    arithmetic (tests/bwd_bound.py), evaluated from the oracle's exact values."""
+    for name, g, r, b in zip(("dq", "dk", "dv"), got, ref, bound):
+        gh = host64(g)
+        err, mag = maxerr(gh, r), float(np.abs(r).max()) if r.size else 0.0
+        ratio = bound_ratio(gh, r, b)
+        say(f"  {what} {name}: max|d|={err:.3e} max|ref|={mag:.3e} max err/bound={ratio:.3f}")
+        assert ratio <= 1.0, f"{what} {name}: an element exceeds its error bound ({ratio:.3f} of it; max|d| {err})"
 
 
 def run_bwd(A, qh, kh, vh, gh, mask=0, scale=None, window=None, window_right=None, seqstarts=None, sk=None):
@@ -862,7 +867,7 @@ def run_bwd(A, qh, kh, vh, gh, mask=0, scale=None, window=None, window_right=Non
     q64, k64, v64, g64 = (synth.to_f64(x, "bf16") for x in (qh, kh, vh, gh))
     oo, ol = oracle.attention(q64, k64, v64, **okw)
     ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, **okw)
-    return (dq, dk, dv), ref
+    return (dq, dk, dv), ref, bwd_error_bound(q64, k64, v64, g64, oo, ol, ref, **okw)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -874,8 +879,8 @@ def test_bwd_ragged_shapes_masks(A, D, mask, win, winr, Mq, Mkv):
     B, H = 2, 3
     qh, kh, vh = synth.qkv(900 + mask + D, (B, Mq, H, D), (B, Mkv, H, D), (B, Mkv, H, D))
     gh = synth.normal(901 + mask + D, 3, (B, Mq, H, D), "bf16")
-    got, ref = run_bwd(A, qh, kh, vh, gh, mask=mask, window=win, window_right=winr)
-    check_grads(got, ref, f"mask {mask}")
+    got, ref, bound = run_bwd(A, qh, kh, vh, gh, mask=mask, window=win, window_right=winr)
+    check_grads(got, ref, f"mask {mask}", bound)
     if mask == 4 and Mq > Mkv:  # bottom-right with more queries than keys: the first rows see nothing
         assert torch.all(got[0][:, :Mq - Mkv] == 0)
 
@@ -888,8 +893,8 @@ def test_bwd_packed_masks(A, mask, win):
     say(f"case: bwd packed mask={mask} win={win}")
     qh, kh, vh = synth.qkv(950 + mask, (1, int(sq[-1]), H, D), (1, int(sk[-1]), H, D), (1, int(sk[-1]), H, D))
     gh = synth.normal(951 + mask, 3, (1, int(sq[-1]), H, D), "bf16")
-    got, ref = run_bwd(A, qh, kh, vh, gh, mask=mask, window=win, seqstarts=sq, sk=sk)
-    check_grads(got, ref, f"packed mask {mask}")
+    got, ref, bound = run_bwd(A, qh, kh, vh, gh, mask=mask, window=win, seqstarts=sq, sk=sk)
+    check_grads(got, ref, f"packed mask {mask}", bound)
 
 
 def test_bwd_negative_scale_strided_5d(A):
@@ -911,7 +916,8 @@ def test_bwd_negative_scale_strided_5d(A):
     q64, k64, v64, g64 = flat(qh), flat(kh), flat(vh), flat(gh)
     oo, ol = oracle.attention(q64, k64, v64, mask=1, scale=-0.2)
     ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, mask=1, scale=-0.2)
-    check_grads([x.reshape(B, M, G * Hg, D) for x in (dq, dk, dv)], ref, "5-D strided")
+    bound = bwd_error_bound(q64, k64, v64, g64, oo, ol, ref, mask=1, scale=-0.2)
+    check_grads([x.reshape(B, M, G * Hg, D) for x in (dq, dk, dv)], ref, "5-D strided", bound)
 
 
 def test_bwd_expanded_gqa(A):
@@ -934,7 +940,8 @@ def test_bwd_expanded_gqa(A):
     k64, v64 = rep(kb), rep(vb)
     oo, ol = oracle.attention(q64, k64, v64, mask=1)
     ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, mask=1)
-    check_grads([x.reshape(B, M, G * Hg, D) for x in (dq, dk, dv)], ref, "expanded GQA")
+    bound = bwd_error_bound(q64, k64, v64, g64, oo, ol, ref, mask=1)
+    check_grads([x.reshape(B, M, G * Hg, D) for x in (dq, dk, dv)], ref, "expanded GQA", bound)
 
 
 def test_bwd_causal_full_size(A):
@@ -950,7 +957,8 @@ def test_bwd_causal_full_size(A):
     q64, k64, v64, g64 = (f64_threads(x) for x in (qh, kh, vh, gh))
     oo, ol = oracle.attention(q64, k64, v64, mask=1)
     ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, mask=1)
-    check_grads((dq, dk, dv), ref, "all 64 (b, h)")
+    bound = bwd_error_bound(q64, k64, v64, g64, oo, ol, ref, mask=1)
+    check_grads((dq, dk, dv), ref, "all 64 (b, h)", bound)
 
 
 # ------------------------------------------------------------------ row/group-wise INT4 K/V caches

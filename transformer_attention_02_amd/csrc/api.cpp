@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "kernels.h"
@@ -646,14 +647,15 @@ attn_status attn_bwd(const attn_tensor *dot, const attn_tensor *qt, const attn_t
 int32_t attn_decode_num_splits(int64_t B, int64_t H_total, int64_t Mkv) {
     if (B <= 0 || H_total <= 0 || Mkv <= 0) return 1;
     // compute units of the current device (256 on MI355X; that value when no device answers)
-    static int cus[64] = {};
+    static std::atomic<int> cus[64];  // per device, 0 until first asked; racing threads store the same value
     int dev = 0, n = 256;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-        if (!cus[dev]) {
+        n = cus[dev].load(std::memory_order_relaxed);
+        if (!n) {
             int c = 0;
-            cus[dev] = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0 ? c : 256;
+            n = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0 ? c : 256;
+            cus[dev].store(n, std::memory_order_relaxed);
         }
-        n = cus[dev];
     } else {
         (void)hipGetLastError();  // leave no error behind for the caller's next HIP call
     }
