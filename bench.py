@@ -1,13 +1,15 @@
 """Benchmark of the fused attention forward path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows full,bwd,decode,varlen,window,merge,fp32] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows full,hd256,bwd,decode,kvcache,varlen,window,merge,fp32] [--no-cpu]
 
 A step is one attn_fwd call on the causal bf16 prefill workload B=2, M=2048,
 H=32, K=Kv=128 (the pages' Quick-start shape), inputs resident in HBM.  The
 headline value is its throughput in TFLOP/s, counting 4*B*H*M*M*K flops halved
 for the causal mask.  The other rows of the path are timed after it and
-reported under "rows": split-KV decode (B=16, Mkv=32768, H=32, 64 chunks;
+reported under "rows": the same prefill unmasked and at head dim 256 ([2, 2048, 16, 256]),
+split-KV decode (B=16, Mkv=32768, H=32, 64 chunks;
 GB/s of K+V) on contiguous and on paged caches and on row-wise FP8 and row/group-wise INT4 caches,
+a KV-cache chunked prefill (16 x 256 queries against 32768 paged keys each),
 the backward of the causal prefill, the packed GQA causal prefill (8 sequences, lengths U[256, 4096]),
 a causal sliding window of 1024 keys over [2, 8192, 32, 128], the 2- and 8-way
 partial+merge of Mq=128/Mkv=1024/H=16, and the fp32 tiny case.
@@ -40,8 +42,8 @@ def parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=300,
                    help="untimed steps first; ~25 ms of back-to-back launches brings the clock to steady state")
-    p.add_argument("--rows", default="full,bwd,decode,kvcache,varlen,window,merge,fp32",
-                   help="rows timed after the headline prefill: full,bwd,decode,kvcache,varlen,window,merge,fp32,copy or "
+    p.add_argument("--rows", default="full,hd256,bwd,decode,kvcache,varlen,window,merge,fp32",
+                   help="rows timed after the headline prefill: full,hd256,bwd,decode,kvcache,varlen,window,merge,fp32,copy or "
                         "none (kvcache needs decode: it reuses the decode cache); "
                         "copy is a plain 1 GiB device copy used to calibrate the HBM byte counters")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -348,6 +350,32 @@ def main():
                 "batch element 0, heads 0-7 (8 of the 64 (b, h) problems), no mask, fp64")
             del sample
         del of
+
+    # the same flop count with head dim 256: [2, 2048, 16, 256] causal (two launches over the value columns)
+    if "hd256" in rows:
+        s2 = (2, 2048, 16, 256)
+        q2h, k2h, v2h = synth.qkv(21, s2, s2, s2, "bf16")
+        q2, k2, v2 = up(q2h), up(k2h), up(v2h)
+        o2 = torch.empty_like(q2)
+        l2 = torch.empty((2, 16, 2048), dtype=torch.float32, device="cuda")
+        tm = {}
+        ms_2 = timed(A.prepare_fwd(q2, k2, v2, o2, l2, mask=A.MASK_CAUSAL), 200, 50, torch, detail=tm)
+        tf_2 = flops / (ms_2 * 1e-3) / 1e12
+        log(f"prefill causal bf16 [2,2048,16,256]: {ms_2 * 1e3:.1f} us/call, {tf_2:.1f} TFLOP/s")
+        result["rows"]["prefill_causal_hd256"] = {
+            "workload": "bf16 B=2 M=2048 H=16 K=Kv=256, top-left causal (the headline's flop count at head dim 256)",
+            "ms_per_call": round(ms_2, 5), "value": round(tf_2, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf_2, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf_2 / PEAK_BF16_TFLOPS, 4), "flops_per_call": flops,
+                         "note": "two launches over the value columns [0,128) and [128,256), each computing the "
+                                 "scores: 1.5x the counted matrix work"}, **tm}
+        if not args.no_cpu:  # batch element 0, heads 0..3 of 16
+            sample = [synth.to_f64(x[:1, :, :4], "bf16") for x in (q2h, k2h, v2h)]
+            result["rows"]["prefill_causal_hd256"]["cpu_oracle"] = oracle_timing(
+                lambda: oracle_mod().attention(*sample, mask=oracle_mod().MASK_CAUSAL), flops / 8 / 1e12, "TFLOP/s",
+                "batch element 0, heads 0-3 (4 of the 32 (b, h) problems), causal, fp64")
+            del sample
+        del q2, k2, v2, o2, l2
 
     # ------------------------------------------------------------ CPU baseline: the oracle on the same workload
     if not args.no_cpu:

@@ -152,7 +152,9 @@ typedef struct {
  *   out [B, Mq, (G,) H, Kv] with q's dtype.
  *   lse fp32 [B, H_total, Mq] device buffer, or NULL to skip it.
  *   varlen: NULL unless mask is one of the block-diagonal kinds.
- * Built kernels: bf16 with K and Kv each in {64, 128} (MFMA); fp32 with K, Kv <= 128. */
+ * Built kernels: bf16 with K and Kv each in {64, 128, 256} (MFMA; ck_splitk.FwOp in "Attention -
+ * Backend operators" takes head dims up to 256; Kv = 256 runs as two launches over the value
+ * columns, each recomputing the scores); fp32 with K, Kv <= 128. */
 attn_status attn_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                      int32_t mask, const attn_varlen *varlen, float scale,
                      const attn_tensor *out, float *lse, attn_stream_t stream);

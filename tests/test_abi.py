@@ -76,7 +76,7 @@ def std4(M=128, D=128, dt=A.ATTN_DTYPE_BF16):
     ("mask", A.ATTN_ERR_INVALID_ARGUMENT, "mask kind"),
     ("align", A.ATTN_ERR_INVALID_ARGUMENT, "16-byte"),
     ("ndim", A.ATTN_ERR_INVALID_ARGUMENT, "ndim"),
-    ("hd96", A.ATTN_ERR_UNSUPPORTED, "K and Kv in {64, 128}"),
+    ("hd96", A.ATTN_ERR_UNSUPPORTED, "K and Kv in {64, 128, 256}"),
     ("f32_big", A.ATTN_ERR_UNSUPPORTED, "<= 128"),
     ("varlen_missing", A.ATTN_ERR_INVALID_ARGUMENT, "varlen"),
     ("out_dtype", A.ATTN_ERR_INVALID_ARGUMENT, "q's dtype"),

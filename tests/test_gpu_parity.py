@@ -191,9 +191,10 @@ def test_forward_workgroup_sizes(A, H, D):
         check(po[:, :, heads], pl[:, heads], oo, ol, TOL_BF16_OUT, TOL_LSE, f"H={H} fp32 partial out")
 
 
-@pytest.mark.parametrize("K,Kv", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("K,Kv", [(64, 128), (128, 64), (256, 256), (256, 128), (256, 64), (128, 256), (64, 256)])
 def test_bf16_distinct_head_dims(A, K, Kv):
-    """q/k head dim K and v/out head dim Kv differ (each 64 or 128): ragged shapes with no mask,
+    """q/k head dim K and v/out head dim Kv (each 64, 128 or 256; ck_splitk.FwOp takes head dims up
+    to 256, and Kv = 256 runs as two launches over the value columns): ragged shapes with no mask,
     causal and a causal window on small grids (the split-key kernel) and on 64 heads (8-wave
     workgroups, sampled heads), and packed block-diagonal causal sequences; bf16 out and the
     fp32 partial output."""
@@ -223,6 +224,18 @@ def test_bf16_distinct_head_dims(A, K, Kv):
     torch.cuda.synchronize()
     oo, ol = run_oracle(qh, kh, vh, 3, "bf16", ss=ss)
     check(out, lse, oo, ol, TOL_BF16_OUT, TOL_LSE, f"K={K} Kv={Kv} packed causal")
+
+
+def test_causal_head_dim_256_full_size(A):
+    """Causal [2, 2048, 16, 256] bf16 (the flop count of the [2, 2048, 32, 128] prefill): the
+    whole launch, every out and lse element against the oracle."""
+    B, M, H, D = 2, 2048, 16, 256
+    say("case: causal head dim 256 full size")
+    qh, kh, vh = synth.qkv(21, (B, M, H, D), (B, M, H, D), (B, M, H, D), "bf16")
+    out, lse = A.attn_fwd(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), mask=A.MASK_CAUSAL)
+    torch.cuda.synchronize()
+    oo, ol = oracle.attention(*(f64_threads(x) for x in (qh, kh, vh)), mask=oracle.MASK_CAUSAL)
+    check(out, lse, oo, ol, TOL_BF16_OUT, TOL_LSE, "all 32 (b, h)")
 
 
 def test_packed_with_distinct_key_offsets(A):

@@ -194,9 +194,10 @@ attn_status forward(const char *fn, bool partial, const attn_tensor *qt, const a
     if (q.D < 1 || v.D < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: head dims must be >= 1", fn);
 
     if (q.dtype == ATTN_DTYPE_BF16) {
-        if (!((q.D == 64 || q.D == 128) && (v.D == 64 || v.D == 128)))
-            return fail(ATTN_ERR_UNSUPPORTED, "%s: bf16 kernels need K and Kv in {64, 128} (got K=%lld, Kv=%lld)", fn,
-                        (long long)q.D, (long long)v.D);
+        auto dim_ok = [](int64_t d) { return d == 64 || d == 128 || d == 256; };
+        if (!(dim_ok(q.D) && dim_ok(v.D)))
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: bf16 kernels need K and Kv in {64, 128, 256} (got K=%lld, Kv=%lld)",
+                        fn, (long long)q.D, (long long)v.D);
         // key tiles are fetched through buffer descriptors whose range ends at the last valid key row
         if (k.M > 1 && (k.s.m < k.D || v.s.m < v.D))
             return fail(ATTN_ERR_UNSUPPORTED, "%s: bf16 kernels need key/value row strides >= the head dim", fn);

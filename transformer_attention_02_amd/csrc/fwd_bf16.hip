@@ -160,6 +160,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     int ub = clampk((int64_t)row0 + shift + a.wr + 1, 0, Lk) / BN;
     ua = min(max(ua, tb), te);
     ub = min(max(ub, ua), te);
+    // Position p of the key loop takes the tile of [tb, te) congruent to p modulo the tile count: workgroups whose ranges have the same length and overlap (the query tiles of a
+    // sliding window) then read each shared key tile at the same step, so the XCD's L2 serves the
+    // later requests.  Ranges that start at tile 0 (causal, unmasked) keep their order.
+    const int nt = te - tb;
+    const int t_first = nt > 0 ? tb + (nt - tb % nt) % nt : tb;  // the tile at position 0
+    int t_issue = t_first;  // the next tile to load (loads go out in position order)
 
     const __bf16 *qp = (const __bf16 *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin) + (int64_t)qs * a.sq.m;
     // K/V rows of key 0 (a KV cache's lane of this sequence; paged caches start at the cache)
@@ -192,10 +198,11 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
         voff[r] = row * vstride + c * 16;
     }
     const unsigned smem_base = (unsigned)(unsigned long long)(unsigned char LDS_AS *)smem;
-    auto issue = [&](int t) __attribute__((always_inline)) {
-        const int kt0 = t * BN;
+    auto issue = [&](int p) __attribute__((always_inline)) {
+        const int kt0 = t_issue * BN;
+        t_issue = t_issue + 1 == te ? tb : t_issue + 1;
         const int nvalid = min(BN, Lk - kt0);
-        const int slot = (t - tb) % STAGES;
+        const int slot = p % STAGES;
         const unsigned kst = smem_base + slot * KTILE, vst = smem_base + V_BASE + slot * VTILE;
         int64_t row = kt0;  // cache row of the tile's first key
         if constexpr (PAGED)
@@ -258,29 +265,29 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     for (int i = 0; i < MB; ++i) o[i] = f32x16{};
     float m_ref = -INFINITY, l_run = 0.f;
 
-    // One 64-key tile: S^T, mask (MASKED only), online softmax, O^T update.
-    // STAGE_C >= 0 names the LDS stage at compile time ((t - tb) % STAGES == STAGE_C), so every
-    // LDS offset becomes an instruction immediate; -1 computes it at run time.
-    auto step = [&](int t, auto masked_tag, auto stage_tag) __attribute__((always_inline)) {
+    // One 64-key tile at loop position p: S^T, mask (MASKED only), online softmax, O^T update.
+    // STAGE_C >= 0 names the LDS stage at compile time (p % STAGES == STAGE_C), so every LDS
+    // offset becomes an instruction immediate; -1 computes it at run time.
+    auto step = [&](int p, int t, auto masked_tag, auto stage_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         constexpr int STAGE_C = decltype(stage_tag)::value;
-        const int slot = STAGE_C >= 0 ? STAGE_C : (t - tb) % STAGES;
+        const int slot = STAGE_C >= 0 ? STAGE_C : p % STAGES;
         const int kt0 = t * BN;
         if (PAIRS) {
-            // even tile of a pair: both tiles of the pair are in, and the two slots of the
+            // even position of a pair: both tiles of the pair are in, and the two slots of the
             // previous pair, which every wave has finished, take the next pair
-            if (((STAGE_C >= 0 ? STAGE_C : (t - tb)) & 1) == 0) {
+            if (((STAGE_C >= 0 ? STAGE_C : p) & 1) == 0) {
                 wait_barrier<0>();
-                if (t + 2 < te) issue(t + 2);
-                if (t + 3 < te) issue(t + 3);
+                if (p + 2 < nt) issue(p + 2);
+                if (p + 3 < nt) issue(p + 3);
             }
         } else {
-            if (t + 1 < te) wait_barrier<KROUNDS + VROUNDS>();
+            if (p + 1 < nt) wait_barrier<KROUNDS + VROUNDS>();
             else wait_barrier<0>();
-            if (t + 2 < te) issue(t + 2);
+            if (p + 2 < nt) issue(p + 2);
         }
         // split keys: the other wave of the block takes this tile
-        if (KSPLIT > 1 && ((STAGE_C >= 0 ? STAGE_C : (t - tb)) & 1) != wsub) return;
+        if (KSPLIT > 1 && ((STAGE_C >= 0 ? STAGE_C : p) & 1) != wsub) return;
         // the whole tile lies before or after every window of this wave's 32 rows
         if (MASKED && ((int64_t)kt0 + BN - 1 < (int64_t)wrow0 + shift - a.wl ||
                        (int64_t)kt0 > (int64_t)wrow0 + 31 + shift + a.wr))
@@ -403,24 +410,32 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
         }
     };
 
-    if (tb < te) issue(tb);
-    if (tb + 1 < te) issue(tb + 1);
+    if (nt > 0) issue(0);
+    if (nt > 1) issue(1);
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
     using SR = std::integral_constant<int, -1>;
-    int t = tb;
-    for (; t < ua; ++t) step(t, std::true_type{}, SR{});  // left edge of the windows
-    for (; t < ub && (t - tb) % STAGES != 0; ++t) step(t, std::false_type{}, SR{});
-    for (; t + STAGES <= ub; t += STAGES) {
-        step(t, std::false_type{}, S0{});
-        step(t + 1, std::false_type{}, S1{});
-        step(t + 2, std::false_type{}, S2{});
-        if constexpr (STAGES == 4) step(t + 3, std::false_type{}, S3{});
-    }
-    for (; t < ub; ++t) step(t, std::false_type{}, SR{});
-    for (; t < te; ++t) step(t, std::true_type{}, SR{});  // diagonal / right edge / key tail
+    // The tiles [t, tend) of one unwrapped piece of the order, by class: the left edge of the
+    // windows (masked), inner tiles (unmasked, unrolled by the ring's slots), then the diagonal,
+    // right edge and key tail (masked).  The order is [t_first, te) then [tb, t_first).
+    int p = 0;
+    auto run = [&](int t, const int tend) __attribute__((always_inline)) {
+        for (const int le = min(tend, ua); t < le; ++p, ++t) step(p, t, std::true_type{}, SR{});
+        const int ie = min(tend, ub);
+        for (; t < ie && p % STAGES != 0; ++p, ++t) step(p, t, std::false_type{}, SR{});
+        for (; t + STAGES <= ie; p += STAGES, t += STAGES) {
+            step(p, t, std::false_type{}, S0{});
+            step(p + 1, t + 1, std::false_type{}, S1{});
+            step(p + 2, t + 2, std::false_type{}, S2{});
+            if constexpr (STAGES == 4) step(p + 3, t + 3, std::false_type{}, S3{});
+        }
+        for (; t < ie; ++p, ++t) step(p, t, std::false_type{}, SR{});
+        for (; t < tend; ++p, ++t) step(p, t, std::true_type{}, SR{});
+    };
+    run(t_first, te);
+    run(tb, t_first);
 
     if constexpr (KSPLIT == 2) {
         // exact merge of the two waves' states of a block: the second wave leaves its (o, m, l)
@@ -533,11 +548,19 @@ template <int KD, int VD, bool OUT_F32, bool PAGED>
 hipError_t launch_nw(const FwdArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)a.nseq * a.B * a.Htot * a.splits;
     auto grid = [&](int bm) { return (a.max_seqlen_q + bm - 1) / bm * units; };
+    if constexpr (KD == 256) {
+        // 512-byte K rows: a 3-slot ring (144 KB with 256-byte V rows) fits the LDS, a 4-slot one
+        // does not, so every size keeps one barrier per tile (and no split-key form)
+        if (grid(256) >= FWD_MIN_GRID) return launch<KD, VD, 8, 3, OUT_F32, PAGED>(a, stream);
+        if (grid(128) >= FWD_MIN_GRID) return launch<KD, VD, 4, 3, OUT_F32, PAGED>(a, stream);
+        return launch<KD, VD, 2, 3, OUT_F32, PAGED>(a, stream);
+    } else {
     if (grid(256) >= FWD_MIN_GRID) return launch<KD, VD, 8, 4, OUT_F32, PAGED>(a, stream);
     if (grid(128) >= FWD_MIN_GRID) return launch<KD, VD, 4, 3, OUT_F32, PAGED>(a, stream);
     if (grid(64) >= FWD_MIN_GRID) return launch<KD, VD, 2, 3, OUT_F32, PAGED>(a, stream);
     // fewer than FWD_MIN_GRID blocks of 32 rows: two waves split each block's keys
     return launch<KD, VD, 2, 4, OUT_F32, PAGED, 2>(a, stream);
+    }
 }
 
 template <int KD, int VD, bool PAGED>
@@ -551,6 +574,20 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, bool out_f32, hipStream_t stream) {
         if (a.K == 64 && a.Kv == 64) return launch_out<64, 64, true>(a, out_f32, stream);
         return hipErrorInvalidValue;
     }
+    if (a.Kv == 256) {
+        // value head dim 256: two launches over the value columns [0, 128) and [128, 256); both
+        // compute the same scores and softmax (so the same LSE, written by the first)
+        FwdArgs h = a;
+        h.Kv = 128;
+        hipError_t e = launch_fwd_bf16(h, out_f32, stream);
+        if (e != hipSuccess) return e;
+        h.v = (const __bf16 *)a.v + 128;
+        h.o = (unsigned char *)a.o + 128 * (out_f32 ? 4 : 2);
+        h.lse = nullptr;
+        return launch_fwd_bf16(h, out_f32, stream);
+    }
+    if (a.K == 256 && a.Kv == 128) return launch_out<256, 128, false>(a, out_f32, stream);
+    if (a.K == 256 && a.Kv == 64) return launch_out<256, 64, false>(a, out_f32, stream);
     if (a.K == 128 && a.Kv == 128) return launch_out<128, 128, false>(a, out_f32, stream);
     if (a.K == 64 && a.Kv == 64) return launch_out<64, 64, false>(a, out_f32, stream);
     if (a.K == 64 && a.Kv == 128) return launch_out<64, 128, false>(a, out_f32, stream);

@@ -21,7 +21,8 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // at 4 column offsets (the transpose reads), hit distinct banks.
 template <int HD>
 __device__ __forceinline__ int swz(int row) {
-    if (HD == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+    // rows of 256 bytes or more: the low four chunk bits span the 64 banks once
+    if (HD >= 128) return ((row & 7) << 1) | ((row >> 3) & 1);
     return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
 }
 
