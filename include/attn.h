@@ -153,8 +153,7 @@ typedef struct {
  *   lse fp32 [B, H_total, Mq] device buffer, or NULL to skip it.
  *   varlen: NULL unless mask is one of the block-diagonal kinds.
  * Built kernels: bf16 with K and Kv each in {64, 128, 256} (MFMA; ck_splitk.FwOp in "Attention -
- * Backend operators" takes head dims up to 256; Kv = 256 runs as two launches over the value
- * columns, each recomputing the scores); fp32 with K, Kv <= 128. */
+ * Backend operators" takes head dims up to 256); fp32 with K, Kv <= 128. */
 attn_status attn_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                      int32_t mask, const attn_varlen *varlen, float scale,
                      const attn_tensor *out, float *lse, attn_stream_t stream);
@@ -202,8 +201,14 @@ size_t attn_fwd_kvcache_workspace_bytes(int64_t Mq, int64_t H_total, int64_t Kv,
  *   q [1, Mq, (G,) H, K] bf16: sequence s owns query rows seqstart_q[s] .. seqstart_q[s+1]-1
  *     (DEVICE int32 [nseq + 1] prefix sums; every block at most max_seqlen_q rows).
  *   seqlens_k: DEVICE int32 [nseq], keys held by each sequence (clamped to [0, cap]).
- *   block_tables NULL: k/v are padded lanes [B >= nseq, cap, (G,) H, K/Kv]; sequence s owns keys
- *     0 .. seqlens_k[s]-1 of lane s.
+ *   seqstart_k non-NULL (gappy lanes: BlockDiagonalGappyKeysMask,
+ *     BlockDiagonalCausalWithOffsetGappyKeysMask, BlockDiagonalLocalAttentionFromBottomRightGappyKeysMask,
+ *     "K/V lanes with arbitrary starts and independently used lengths"): DEVICE int32 [nseq];
+ *     k/v are one tensor [1, Mk, (G,) H, K/Kv] and sequence s owns its rows seqstart_k[s] ..
+ *     seqstart_k[s] + seqlens_k[s] - 1 (clamped to [0, Mk]; lanes may overlap or leave gaps);
+ *     block_tables must be NULL (the paged gappy form is not built); cap = Mk.
+ *   block_tables NULL (and seqstart_k NULL): k/v are padded lanes [B >= nseq, cap, (G,) H, K/Kv];
+ *     sequence s owns keys 0 .. seqlens_k[s]-1 of lane s.
  *   block_tables non-NULL: DEVICE int32 [nseq, max_blocks_per_seq] page numbers; k/v are the cache
  *     [1, num_pages * page_size, (G,) H, D] (K == Kv); key j of sequence s is cache row
  *     block_tables[s][j / page_size] * page_size + j % page_size; page_size a multiple of 64 and
@@ -221,7 +226,8 @@ size_t attn_fwd_kvcache_workspace_bytes(int64_t Mq, int64_t H_total, int64_t Kv,
  *   Device metadata is not read by the host; bad values give unspecified results, never an
  *   out-of-bounds access.  Errors as attn_fwd. */
 attn_status attn_fwd_kvcache(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, const attn_mask *mask,
-                             const int32_t *seqstart_q, int32_t nseq, int32_t max_seqlen_q, const int32_t *seqlens_k,
+                             const int32_t *seqstart_q, int32_t nseq, int32_t max_seqlen_q, const int32_t *seqstart_k,
+                             const int32_t *seqlens_k,
                              const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t page_size,
                              int32_t max_seqlen_k, int32_t num_splits, float scale, void *workspace,
                              size_t workspace_bytes, const attn_tensor *out, float *lse, attn_stream_t stream);

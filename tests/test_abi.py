@@ -372,11 +372,11 @@ def test_fwd_kvcache_rejects():
     ss, lens, tab = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 64), ctypes.c_void_p(FAKE + 128)
 
     def call(k=lanes, kind=A.MASK_CAUSAL_BR, nseq=4, mq=100, tables=None, mb=0, page=0, mk=1024, S=1, ws=None,
-             wsb=0, qq=q, oo=o, W=0):
+             wsb=0, qq=q, oo=o, W=0, starts=None):
         m = A.AttnMask(kind, W, 0, 0)
         return A._lib.attn_fwd_kvcache(ctypes.byref(qq), ctypes.byref(k), ctypes.byref(k), ctypes.byref(m), ss, nseq,
-                                       mq, lens, tables, mb, page, mk, S, float("nan"), ws, wsb, ctypes.byref(oo),
-                                       None, None)
+                                       mq, starts, lens, tables, mb, page, mk, S, float("nan"), ws, wsb,
+                                       ctypes.byref(oo), None, None)
 
     assert call(kind=A.MASK_CAUSAL) == A.ATTN_ERR_INVALID_ARGUMENT and "mask kind" in A.attn_last_error()
     assert call(kind=A.MASK_BLOCKDIAG) == A.ATTN_ERR_INVALID_ARGUMENT
@@ -396,3 +396,9 @@ def test_fwd_kvcache_rejects():
     assert call(qq=tensor([1, 300, 8, 128], A.ATTN_DTYPE_F32)) == A.ATTN_ERR_UNSUPPORTED
     assert call(kind=A.MASK_CAUSAL_LOCAL_BR, W=0) == A.ATTN_ERR_INVALID_ARGUMENT
     assert A.attn_fwd_kvcache_workspace_bytes(300, 8, 128, 1) == 0
+    # gappy lanes: key starts into one k/v tensor (B == 1), not over a paged cache
+    gappy = ctypes.c_void_p(FAKE + 192)
+    assert call(starts=gappy) == A.ATTN_ERR_INVALID_ARGUMENT and "B == 1" in A.attn_last_error()
+    assert call(k=cache, tables=tab, mb=64, page=256, starts=gappy) == A.ATTN_ERR_UNSUPPORTED
+    assert call(k=tensor([1, 4096, 8, 128]), starts=gappy, mk=4097) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(k=tensor([1, 4096, 8, 128]), starts=ctypes.c_void_p(FAKE + 194)) == A.ATTN_ERR_INVALID_ARGUMENT

@@ -1307,9 +1307,10 @@ _KV_ORACLE_MASK = {0: oracle.MASK_NONE, 4: oracle.MASK_CAUSAL_BR, 6: oracle.MASK
 
 
 def _kvcache_case(A, lq, lk, cap, H, D, mask, seed, page=None, splits=1, window_size=None, wl=None, wr=None,
-                  G=None, check_seqs=None):
-    """q blocks of lq[s] rows against sequence s's lk[s] keys in padded lanes [nseq, cap] or in a paged
-    cache (a PCG64 permutation of pages); the oracle sees each sequence's own keys gathered."""
+                  G=None, check_seqs=None, starts=None):
+    """q blocks of lq[s] rows against sequence s's lk[s] keys in padded lanes [nseq, cap], in a paged
+    cache (a PCG64 permutation of pages) or, with `starts`, in gappy lanes (rows starts[s] ..
+    starts[s] + lk[s] - 1 of one [1, cap] tensor); the oracle sees each sequence's own keys gathered."""
     nseq = len(lq)
     ss = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
     M = int(ss[-1])
@@ -1320,6 +1321,8 @@ def _kvcache_case(A, lq, lk, cap, H, D, mask, seed, page=None, splits=1, window_
         P = nseq * nb
         ks_ = (1, P * page, G, H, D) if G else (1, P * page, H, D)
         tables = np.random.Generator(np.random.PCG64(seed)).permutation(P).astype(np.int32).reshape(nseq, nb)
+    elif starts is not None:
+        ks_ = (1, cap, G, H, D) if G else (1, cap, H, D)
     else:
         ks_ = (nseq, cap, G, H, D) if G else (nseq, cap, H, D)
     kh = synth.normal(seed, synth.TAG_K, ks_, "bf16")
@@ -1328,6 +1331,8 @@ def _kvcache_case(A, lq, lk, cap, H, D, mask, seed, page=None, splits=1, window_
     kw = dict(mask=mask, window_size=window_size, window_left=wl, window_right=wr, num_splits=splits)
     if page:
         kw.update(block_tables=torch.from_numpy(tables).cuda(), page_size=page)
+    if starts is not None:
+        kw.update(seqstart_k=torch.from_numpy(np.asarray(starts, np.int32)).cuda())
     out, lse = A.attn_fwd_kvcache(q, k, v, torch.from_numpy(ss).cuda(), torch.from_numpy(np.asarray(lk, np.int32)).cuda(),
                                   int(max(lq)), int(max(lk)), **kw)
     torch.cuda.synchronize()
@@ -1344,6 +1349,8 @@ def _kvcache_case(A, lq, lk, cap, H, D, mask, seed, page=None, splits=1, window_
         if page:
             kf, vf = kh.reshape((1, -1) + kh.shape[2:]), vh.reshape((1, -1) + vh.shape[2:])
             ksq, vsq = _gather(kf, tables[s], page, lk[s]), _gather(vf, tables[s], page, lk[s])
+        elif starts is not None:
+            ksq, vsq = kh[:, starts[s]:starts[s] + lk[s]], vh[:, starts[s]:starts[s] + lk[s]]
         else:
             ksq, vsq = kh[s:s + 1, :lk[s]], vh[s:s + 1, :lk[s]]
         oo, ol = oracle.attention(f64_threads(qs_).reshape(1, lq[s], Ht, D), f64_threads(ksq).reshape(1, lk[s], Ht, D),
@@ -1376,6 +1383,18 @@ def test_kvcache_local_windows(A):
     say("case: kv cache local windows")
     _kvcache_case(A, [100, 300, 5], [1500, 600, 900], 1536, 8, 128, 6, 63, page=128, wl=70, wr=20)
     _kvcache_case(A, [100, 300, 5], [1500, 600, 900], 1536, 8, 128, 7, 64, window_size=100, splits=3)
+
+
+@pytest.mark.parametrize("mask,splits", [(0, 1), (4, 1), (4, 3), (6, 1), (7, 2)])
+def test_kvcache_gappy_lanes(A, mask, splits):
+    """BlockDiagonalGappyKeysMask and its causal-with-offset and bottom-right local forms: each
+    sequence's keys start anywhere in one k/v tensor; lanes with gaps between them, one overlapping
+    its neighbour, one empty, one starting at row 0 and one ending at the last row."""
+    say(f"case: kv cache gappy lanes mask={mask} splits={splits}")
+    lq, lk, starts = [3, 200, 64, 1, 130], [900, 333, 0, 1000, 64], [100, 950, 1200, 1100, 2036]
+    kw = {"window_size": 100} if mask == 7 else ({"wl": 70, "wr": 20} if mask == 6 else {})
+    _kvcache_case(A, lq, lk, 2100, 8, 128, mask, 65 + mask, splits=splits, starts=starts, **kw)
+    _kvcache_case(A, [17, 1], [500, 2100], 2100, 4, 64, mask, 75 + mask, splits=splits, starts=[0, 0], **kw)
 
 
 def test_kvcache_head_dim_64_and_grouped_heads(A):

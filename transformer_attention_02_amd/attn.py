@@ -62,8 +62,8 @@ _lib.attn_partial_ex.restype = ctypes.c_int
 _lib.attn_merge.argtypes = [ctypes.c_int32, _T, _P(ctypes.c_void_p), _T, ctypes.c_void_p, ctypes.c_void_p]
 _lib.attn_merge.restype = ctypes.c_int
 _lib.attn_fwd_kvcache.argtypes = [_T, _T, _T, _P(AttnMask), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                   ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, _T,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, _T,
                                    ctypes.c_void_p, ctypes.c_void_p]
 _lib.attn_fwd_kvcache.restype = ctypes.c_int
 _lib.attn_fwd_kvcache_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
@@ -377,18 +377,22 @@ def attn_fwd_kvcache_workspace_bytes(Mq: int, H_total: int, Kv: int, num_splits:
 
 
 def _kvcache_args(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k, mask, window_size, window_left,
-                  window_right, block_tables, page_size, num_splits, scale, workspace, out, lse, stream):
+                  window_right, block_tables, page_size, num_splits, scale, workspace, out, lse, stream, seqstart_k=None):
     _index(seqstart_q, "seqstart_q")
     if seqlens_k is None:
         raise ValueError("seqlens_k is required")
     _cache_index(q, seqlens_k, block_tables, "sequences", B=seqstart_q.numel() - 1)
+    _index(seqstart_k, "seqstart_k")
+    if seqstart_k is not None and seqstart_k.numel() < seqstart_q.numel() - 1:
+        raise ValueError(f"seqstart_k holds {seqstart_k.numel()} values; there are {seqstart_q.numel() - 1} sequences")
     _lse_buf(lse, _htot(q) * q.shape[1])
-    _on_device(seqstart_q=seqstart_q, seqlens_k=seqlens_k, block_tables=block_tables, lse=lse, workspace=workspace)
+    _on_device(seqstart_q=seqstart_q, seqlens_k=seqlens_k, block_tables=block_tables, lse=lse, workspace=workspace,
+               seqstart_k=seqstart_k)
     m = AttnMask(int(mask), int(window_size or 0), int(window_left or 0), int(window_right or 0))
     ds = [desc(q, name="q"), desc(k, name="k"), desc(v, name="v"), desc(out, name="out")]
     mb = block_tables.shape[1] if block_tables is not None else 0
     args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), ctypes.byref(m), _ptr(seqstart_q),
-            int(seqstart_q.numel() - 1), int(max_seqlen_q), _ptr(seqlens_k), _ptr(block_tables), int(mb),
+            int(seqstart_q.numel() - 1), int(max_seqlen_q), _ptr(seqstart_k), _ptr(seqlens_k), _ptr(block_tables), int(mb),
             int(page_size or 0), int(max_seqlen_k), int(num_splits), _scale(scale), _ptr(workspace),
             _ws_bytes(workspace) if workspace is not None else 0, ctypes.byref(ds[3]), _ptr(lse),
             _stream(stream, q.device))
@@ -397,10 +401,11 @@ def _kvcache_args(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k, ma
 
 def attn_fwd_kvcache(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k, mask=MASK_NONE, window_size=None,
                      window_left=None, window_right=None, block_tables=None, page_size=None, num_splits=1,
-                     scale=None, workspace=None, out=None, lse=True, stream=None):
-    """Packed query blocks [1, Mq, (G,) H, K] against padded KV lanes (block_tables None) or a paged
-    cache, with the padded-keys masks aligned from the bottom right of each sequence (MASK_NONE,
-    MASK_CAUSAL_BR, MASK_LOCAL_BR, MASK_CAUSAL_LOCAL_BR).  Returns (out, lse or None)."""
+                     scale=None, workspace=None, out=None, lse=True, stream=None, seqstart_k=None):
+    """Packed query blocks [1, Mq, (G,) H, K] against padded KV lanes (block_tables None), a paged
+    cache, or gappy lanes (seqstart_k: each sequence's first row of one k/v tensor), with the
+    padded-keys masks aligned from the bottom right of each sequence (MASK_NONE, MASK_CAUSAL_BR,
+    MASK_LOCAL_BR, MASK_CAUSAL_LOCAL_BR).  Returns (out, lse or None)."""
     if out is None:
         out = torch.empty((*q.shape[:-1], v.shape[-1]), dtype=q.dtype, device=q.device)
     if lse is True:
@@ -412,20 +417,20 @@ def attn_fwd_kvcache(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k,
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     args, _keep = _kvcache_args(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k, mask, window_size,
                                 window_left, window_right, block_tables, page_size, num_splits, scale, workspace, out,
-                                lse, stream)
+                                lse, stream, seqstart_k)
     _check(_lib.attn_fwd_kvcache(*args))
     return out, lse
 
 
 def prepare_fwd_kvcache(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k, out, lse, mask=MASK_NONE,
                         window_size=None, window_left=None, window_right=None, block_tables=None, page_size=None,
-                        num_splits=1, scale=None, workspace=None, stream=None) -> Prepared:
+                        num_splits=1, scale=None, workspace=None, stream=None, seqstart_k=None) -> Prepared:
     """attn_fwd_kvcache with every argument marshalled up front."""
     args, keep = _kvcache_args(q, k, v, seqstart_q, seqlens_k, max_seqlen_q, max_seqlen_k, mask, window_size,
                                window_left, window_right, block_tables, page_size, num_splits, scale, workspace, out,
-                               lse, stream)
+                               lse, stream, seqstart_k)
     return Prepared(_lib.attn_fwd_kvcache, args, (keep, q, k, v, seqstart_q, seqlens_k, block_tables, workspace, out,
-                                                   lse))
+                                                   lse, seqstart_k))
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_NOALLOC_SCRATCH_BYTES

@@ -365,7 +365,8 @@ size_t attn_fwd_kvcache_workspace_bytes(int64_t Mq, int64_t H_total, int64_t Kv,
 }
 
 attn_status attn_fwd_kvcache(const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt, const attn_mask *mask,
-                             const int32_t *seqstart_q, int32_t nseq, int32_t max_seqlen_q, const int32_t *seqlens_k,
+                             const int32_t *seqstart_q, int32_t nseq, int32_t max_seqlen_q, const int32_t *seqstart_k,
+                             const int32_t *seqlens_k,
                              const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t page_size,
                              int32_t max_seqlen_k, int32_t num_splits, float scale, void *workspace,
                              size_t workspace_bytes, const attn_tensor *ot, float *lse, attn_stream_t stream) {
@@ -399,8 +400,11 @@ attn_status attn_fwd_kvcache(const attn_tensor *qt, const attn_tensor *kt, const
     if ((st = mask_spec(fn, *mask, &ms)) != ATTN_OK) return st;
     if (nseq < 1 || !seqstart_q || !seqlens_k)
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: needs nseq >= 1, seqstart_q and seqlens_k", fn);
-    if ((((uintptr_t)seqstart_q) % 4) || (((uintptr_t)seqlens_k) % 4) || (((uintptr_t)block_tables) % 4))
+    if ((((uintptr_t)seqstart_q) % 4) || (((uintptr_t)seqlens_k) % 4) || (((uintptr_t)block_tables) % 4) ||
+        (((uintptr_t)seqstart_k) % 4))
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: index arrays must be 4-byte aligned", fn);
+    if (seqstart_k && block_tables)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: gappy lanes (seqstart_k) over a paged cache are not built", fn);
     if (max_seqlen_q < 0 || max_seqlen_q > q.M)
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: max_seqlen_q must be in [0, Mq]", fn);
     const bool paged = block_tables != nullptr;
@@ -417,6 +421,9 @@ attn_status attn_fwd_kvcache(const attn_tensor *qt, const attn_tensor *kt, const
         if (k.D != v.D) return fail(ATTN_ERR_UNSUPPORTED, "%s: a paged cache needs equal head dims", fn);
         cap = (int64_t)max_blocks_per_seq * page_size;
         if (cap > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "%s: sequences too long", fn);
+    } else if (seqstart_k) {
+        if (k.B != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: gappy lanes index one k/v tensor (B == 1)", fn);
+        cap = k.M;
     } else {
         if (k.B < nseq) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: k/v need a lane per sequence (B >= nseq)", fn);
         cap = k.M;
@@ -466,7 +473,7 @@ attn_status attn_fwd_kvcache(const attn_tensor *qt, const attn_tensor *kt, const
     a.wl = ms.wl;
     a.wr = ms.wr;
     a.seqstart_q = seqstart_q;
-    a.seqstart_k = nullptr;
+    a.seqstart_k = seqstart_k;  // gappy lanes (with seqlens_k): the sequences' first key rows
     a.nseq = nseq;
     a.max_seqlen_q = max_seqlen_q;
     a.kv_groups = (k.s.h == 0 && v.s.h == 0 && q.H > 1) ? (int)(Htot / q.H) : 0;

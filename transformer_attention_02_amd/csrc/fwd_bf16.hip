@@ -86,7 +86,7 @@ template <int KD, int VD, int NW, int STAGES, bool OUT_F32, int KSPLIT, bool PAG
 __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     constexpr int NT = NW * 64;                  // threads per workgroup
     constexpr int BM = NW / KSPLIT * 32;         // query rows per workgroup
-    static_assert(STAGES == 3 || STAGES == 4, "the unrolled tile loop names three or four LDS stages");
+    static_assert(STAGES >= 2 && STAGES <= 4, "the unrolled tile loop names two to four LDS stages");
     // STAGES == 4: the ring is filled two tiles at a time, with one wait + barrier per two tiles
     constexpr bool PAIRS = STAGES == 4;
     static_assert(KSPLIT == 1 || (KSPLIT == 2 && PAIRS), "split keys need the paired ring");
@@ -122,8 +122,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
         const int r = bh % a.Htot;
         bh += (r % a.kv_groups) * a.Hin + r / a.kv_groups - r;
     }
-    const int seq = id % a.nseq;
-    const int tile = tiles - 1 - id / a.nseq;
+    // expanded GQA over packed sequences: the query tiles of one sequence (longest first) run
+    // together on the group's XCD, so they stream the sequence's keys in step and share them in
+    // L2 (otherwise every tile level of every sequence in turn, heaviest first)
+    const bool seq_major = a.kv_groups > 0 && a.nseq > 1;
+    const int seq = seq_major ? id / tiles : id % a.nseq;
+    const int tile = tiles - 1 - (seq_major ? id % tiles : id / a.nseq);
     const int b = bh / a.Htot, hf = bh % a.Htot;
 
     int qs = 0, qe = a.Mq, ks = 0, ke = a.Mkv;
@@ -131,9 +135,10 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
         qs = min(max(a.seqstart_q[seq], 0), a.Mq);
         qe = min(max(a.seqstart_q[seq + 1], qs), a.Mq);
         if (a.seqlens_k) {
-            // KV cache: the sequence's keys start at row 0 of its lane (or its first page)
-            ks = 0;
-            ke = min(max(a.seqlens_k[seq], 0), a.cap);
+            // KV cache: the sequence's keys start at row 0 of its lane (or its first page), or at
+            // row seqstart_k[seq] of the one k/v tensor (gappy lanes)
+            ks = a.seqstart_k ? min(max(a.seqstart_k[seq], 0), a.Mkv) : 0;
+            ke = ks + min(max(a.seqlens_k[seq], 0), a.cap - ks);
         } else {
             const int32_t *skp = a.seqstart_k ? a.seqstart_k : a.seqstart_q;
             ks = min(max(skp[seq], 0), a.Mkv);
@@ -169,7 +174,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
 
     const __bf16 *qp = (const __bf16 *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin) + (int64_t)qs * a.sq.m;
     // K/V rows of key 0 (a KV cache's lane of this sequence; paged caches start at the cache)
-    const int64_t kvb = a.seqlens_k && !PAGED ? seq : b;
+    const int64_t kvb = a.seqlens_k && !PAGED && !a.seqstart_k ? seq : b;
     const __bf16 *kp = (const __bf16 *)a.k + (PAGED ? 0 : kvb * a.sk.b) + head_offset(a.sk, hf, a.Hin) + (int64_t)ks * a.sk.m;
     const __bf16 *vp = (const __bf16 *)a.v + (PAGED ? 0 : kvb * a.sv.b) + head_offset(a.sv, hf, a.Hin) + (int64_t)ks * a.sv.m;
     if constexpr (PAGED) {
@@ -281,6 +286,10 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
                 if (p + 2 < nt) issue(p + 2);
                 if (p + 3 < nt) issue(p + 3);
             }
+        } else if (STAGES == 2) {
+            // double buffer: tile p is in and every wave is past tile p - 1, whose slot takes p + 1
+            wait_barrier<0>();
+            if (p + 1 < nt) issue(p + 1);
         } else {
             if (p + 1 < nt) wait_barrier<KROUNDS + VROUNDS>();
             else wait_barrier<0>();
@@ -411,7 +420,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     };
 
     if (nt > 0) issue(0);
-    if (nt > 1) issue(1);
+    if (STAGES > 2 && nt > 1) issue(1);
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
@@ -428,7 +437,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
         for (; t + STAGES <= ie; p += STAGES, t += STAGES) {
             step(p, t, std::false_type{}, S0{});
             step(p + 1, t + 1, std::false_type{}, S1{});
-            step(p + 2, t + 2, std::false_type{}, S2{});
+            if constexpr (STAGES >= 3) step(p + 2, t + 2, std::false_type{}, S2{});
             if constexpr (STAGES == 4) step(p + 3, t + 3, std::false_type{}, S3{});
         }
         for (; t < ie; ++p, ++t) step(p, t, std::false_type{}, SR{});
@@ -548,7 +557,12 @@ template <int KD, int VD, bool OUT_F32, bool PAGED>
 hipError_t launch_nw(const FwdArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)a.nseq * a.B * a.Htot * a.splits;
     auto grid = [&](int bm) { return (a.max_seqlen_q + bm - 1) / bm * units; };
-    if constexpr (KD == 256) {
+    if constexpr (VD == 256) {
+        // 512-byte K and V rows, a 256-column O^T (128 accumulator registers besides Q^T's 64):
+        // one wave per SIMD and a double-buffered ring (128 KB)
+        if (grid(128) >= FWD_MIN_GRID) return launch<KD, VD, 4, 2, OUT_F32, PAGED>(a, stream);
+        return launch<KD, VD, 2, 2, OUT_F32, PAGED>(a, stream);
+    } else if constexpr (KD == 256) {
         // 512-byte K rows: a 3-slot ring (144 KB with 256-byte V rows) fits the LDS, a 4-slot one
         // does not, so every size keeps one barrier per tile (and no split-key form)
         if (grid(256) >= FWD_MIN_GRID) return launch<KD, VD, 8, 3, OUT_F32, PAGED>(a, stream);
@@ -575,16 +589,10 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, bool out_f32, hipStream_t stream) {
         return hipErrorInvalidValue;
     }
     if (a.Kv == 256) {
-        // value head dim 256: two launches over the value columns [0, 128) and [128, 256); both
-        // compute the same scores and softmax (so the same LSE, written by the first)
-        FwdArgs h = a;
-        h.Kv = 128;
-        hipError_t e = launch_fwd_bf16(h, out_f32, stream);
-        if (e != hipSuccess) return e;
-        h.v = (const __bf16 *)a.v + 128;
-        h.o = (unsigned char *)a.o + 128 * (out_f32 ? 4 : 2);
-        h.lse = nullptr;
-        return launch_fwd_bf16(h, out_f32, stream);
+        if (a.K == 256) return launch_out<256, 256, false>(a, out_f32, stream);
+        if (a.K == 128) return launch_out<128, 256, false>(a, out_f32, stream);
+        if (a.K == 64) return launch_out<64, 256, false>(a, out_f32, stream);
+        return hipErrorInvalidValue;
     }
     if (a.K == 256 && a.Kv == 128) return launch_out<256, 128, false>(a, out_f32, stream);
     if (a.K == 256 && a.Kv == 64) return launch_out<256, 64, false>(a, out_f32, stream);
