@@ -311,6 +311,10 @@ attn_status attn_decode_splitkv_noalloc(const attn_tensor *q, const attn_tensor 
  *     (cap = max_blocks_per_seq * page_size).
  *   max_seqlen_k in [0, cap] bounds every seqlens[b]; the keys are cut into num_splits
  *     chunks of ceil(max_seqlen_k / num_splits), so shorter sequences have empty chunks.
+ *   window_size 0: every key of the sequence.  window_size W >= 1: the query (its sequence's
+ *     last position) sees only the sequence's last W keys (BlockDiagonalCausalLocalAttention-
+ *     PaddedKeysMask and PagedBlockDiagonalCausalLocalPaddedKeysMask with one query per
+ *     sequence); the chunks then cut those keys, ceil(min(max_seqlen_k, W) / num_splits) each.
  *   Device metadata is not read by the host: seqlens are clamped to [0, cap] and page
  *   numbers to the cache, so bad metadata gives unspecified values, never an
  *   out-of-bounds access; keys past num_splits chunks are not seen.
@@ -318,6 +322,7 @@ attn_status attn_decode_splitkv_noalloc(const attn_tensor *q, const attn_tensor 
 attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                                       const int32_t *seqlens, const int32_t *block_tables,
                                       int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                      int32_t window_size,
                                       int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                       const attn_tensor *out, float *lse, attn_stream_t stream);
 
@@ -335,11 +340,13 @@ attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k
  *     head, i.e. one 32-bit word with the scale in its low half.
  *   out [B, 1, (G,) H, D] bf16 or fp32; lse fp32 [B, H_total, 1] or NULL.
  *   The codes and metadata are read as they are; NaN codes or metadata propagate.
- *   Workspace, splits, scale, device-metadata handling and errors as in attn_decode_splitkv_paged. */
+ *   Workspace, splits, window_size, scale, device-metadata handling and errors as in
+ *   attn_decode_splitkv_paged (with seqlens NULL every sequence holds its whole lane). */
 attn_status attn_decode_splitkv_fp8(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                                     const attn_tensor *k_scale_shift, const attn_tensor *v_scale_shift,
                                     const int32_t *seqlens, const int32_t *block_tables,
                                     int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                    int32_t window_size,
                                     int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                     const attn_tensor *out, float *lse, attn_stream_t stream);
 
@@ -358,6 +365,7 @@ attn_status attn_decode_splitkv_int4(const attn_tensor *q, const attn_tensor *k,
                                      const attn_tensor *k_scale_shift, const attn_tensor *v_scale_shift,
                                      const int32_t *seqlens, const int32_t *block_tables,
                                      int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                     int32_t window_size,
                                      int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                      const attn_tensor *out, float *lse, attn_stream_t stream);
 

@@ -229,9 +229,9 @@ def test_paged_decode_rejects():
     q, o = tensor([B, 1, H, D]), tensor([B, 1, H, D])
     cache = tensor([1, 64 * 16, H, D])
 
-    def call(k=cache, seqlens=FAKE, bt=FAKE, mb=8, page=16, mx=128, wsb=need):
+    def call(k=cache, seqlens=FAKE, bt=FAKE, mb=8, page=16, mx=128, wsb=need, W=0):
         return A._lib.attn_decode_splitkv_paged(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.c_void_p(seqlens),
-                                                ctypes.c_void_p(bt) if bt else None, mb, page, mx, S, float("nan"),
+                                                ctypes.c_void_p(bt) if bt else None, mb, page, mx, W, S, float("nan"),
                                                 ctypes.c_void_p(FAKE * 256), wsb, ctypes.byref(o), None, None)
     assert call(seqlens=0) == A.ATTN_ERR_INVALID_ARGUMENT and "seqlens" in A.attn_last_error()
     assert call(page=0) == A.ATTN_ERR_INVALID_ARGUMENT
@@ -241,6 +241,7 @@ def test_paged_decode_rejects():
     assert call(wsb=need - 1) == A.ATTN_ERR_WORKSPACE_TOO_SMALL
     lanes = tensor([B, 300, H, D])
     assert call(k=lanes, bt=0, mx=301) == A.ATTN_ERR_INVALID_ARGUMENT   # padded lanes: max_seqlen_k <= lane capacity
+    assert call(W=-1) == A.ATTN_ERR_INVALID_ARGUMENT and "window_size" in A.attn_last_error()
 
 
 def test_fp8_decode_rejects():
@@ -253,7 +254,7 @@ def test_fp8_decode_rejects():
     def call(qq=q, k=k8, kss=ss, vss=ss, oo=o, seqlens=0, bt=0, mx=0):
         return A._lib.attn_decode_splitkv_fp8(ctypes.byref(qq), ctypes.byref(k), ctypes.byref(k), ctypes.byref(kss),
                                               ctypes.byref(vss), ctypes.c_void_p(seqlens) if seqlens else None,
-                                              ctypes.c_void_p(bt) if bt else None, 8, 32, mx, S, float("nan"),
+                                              ctypes.c_void_p(bt) if bt else None, 8, 32, mx, 0, S, float("nan"),
                                               ctypes.c_void_p(FAKE * 256), need, ctypes.byref(oo), None, None)
     assert call(k=tensor([B, M, H, D])) == A.ATTN_ERR_INVALID_ARGUMENT and "dtype" in A.attn_last_error()
     assert call(kss=tensor([B, M, H, 2], A.ATTN_DTYPE_F32)) == A.ATTN_ERR_INVALID_ARGUMENT
@@ -317,7 +318,7 @@ def test_int4_decode_rejects():
         kss = kss or ss(1)
         vss = vss or kss
         return fn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(kss), ctypes.byref(vss), None, None,
-                  0, 0, 0, S, float("nan"), ctypes.c_void_p(FAKE * 256), need, ctypes.byref(o), None, None)
+                  0, 0, 0, 0, S, float("nan"), ctypes.c_void_p(FAKE * 256), need, ctypes.byref(o), None, None)
     assert call(kss=ss(8)) == A.ATTN_ERR_UNSUPPORTED and "multiple of 32" in A.attn_last_error()   # groups of 16
     assert call(kss=ss(3)) == A.ATTN_ERR_UNSUPPORTED
     assert call(kss=ss(2), vss=ss(4)) == A.ATTN_ERR_INVALID_ARGUMENT

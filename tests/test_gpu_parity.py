@@ -1052,6 +1052,73 @@ def test_int4_decode_padded_lanes_5d_gqa(A):
         check(out[b:b + 1].reshape(1, 1, G5 * Hg, D), lse[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"lane {b} len={lens[b]}")
 
 
+@pytest.mark.parametrize("S", [1, 4, None])
+def test_decode_sliding_window(A, S):
+    """BlockDiagonalCausalLocalAttentionPaddedKeysMask and its paged form with one query per sequence:
+    the query sees its sequence's last W keys.  Sequences shorter than, as long as and longer than
+    the window, one empty; lanes and 64-row pages; 1 and 4 splits and the library's split count
+    (the chunks cut the window's keys).  bf16 against the oracle's causal local mask (bottom right)."""
+    B, cap, H, D, W, page = 5, 700, 4, 128, 100, 64
+    lens = np.array([0, 37, 100, 700, 333], dtype=np.int32)
+    say(f"case: decode sliding window W={W} S={S} lens={list(lens)}")
+    qh, kh, vh = synth.qkv(1150, (B, 1, H, D), (B, cap, H, D), (B, cap, H, D), "bf16")
+    out, lse = A.attn_decode_splitkv_paged(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"),
+                                           torch.from_numpy(lens).cuda(), S, int(lens.max()), window_size=W)
+    nb = (cap + page - 1) // page
+    P = B * nb
+    tables = np.random.Generator(np.random.PCG64(1151)).permutation(P).astype(np.int32).reshape(B, nb)
+    kpg = np.zeros((1, P * page, H, D), dtype=kh.dtype)
+    vpg = np.zeros_like(kpg)
+    for b in range(B):
+        for i in range(nb):
+            rows = slice(i * page, min(cap, (i + 1) * page))
+            n = rows.stop - rows.start
+            kpg[0, tables[b, i] * page:tables[b, i] * page + n] = kh[b, rows]
+            vpg[0, tables[b, i] * page:tables[b, i] * page + n] = vh[b, rows]
+    po, pl = A.attn_decode_splitkv_paged(dev(qh, "bf16"), dev(kpg, "bf16"), dev(vpg, "bf16"),
+                                         torch.from_numpy(lens).cuda(), S, int(lens.max()),
+                                         block_tables=torch.from_numpy(tables).cuda(), page_size=page, window_size=W)
+    torch.cuda.synchronize()
+    for b in range(B):
+        oo, ol = run_oracle(qh[b:b + 1], kh[b:b + 1, :lens[b]], vh[b:b + 1, :lens[b]], oracle.MASK_CAUSAL_LOCAL_BR,
+                            "bf16", window=W)
+        check(out[b:b + 1], lse[b:b + 1], oo, ol, TOL_BF16_OUT, TOL_LSE, f"lane {b} len={lens[b]}")
+        check(po[b:b + 1], pl[b:b + 1], oo, ol, TOL_BF16_OUT, TOL_LSE, f"paged seq {b} len={lens[b]}")
+
+
+def test_quantised_decodes_sliding_window(A):
+    """FP8 and INT4 caches with a window of 300 keys: contiguous lanes (seqlens NULL, every lane
+    holds 1000 keys) and padded lanes; fp32 outputs against the oracle's dequantised values."""
+    B, M, H, D, W, S = 3, 1000, 2, 128, 300, 3
+    lens = np.array([1000, 299, 301], dtype=np.int32)
+    qh = synth.normal(1160, synth.TAG_Q, (B, 1, H, D), "bf16")
+    kc8, vc8 = (synth.fp8_codes(1160, t, (B, M, H, D)) for t in (synth.TAG_K, synth.TAG_V))
+    ks8, vs8 = (synth.scale_shift(1160, t, (B, M, H)) for t in (synth.TAG_K, synth.TAG_V))
+    kc4, vc4, ks4, vs4 = _int4_cache(1161, (B, M, H, D), 4)
+    for kind in ("fp8", "int4"):
+        for seqlens in (None, lens):
+            say(f"case: {kind} decode window W={W} seqlens={None if seqlens is None else list(seqlens)}")
+            kw = dict(seqlens=torch.from_numpy(seqlens).cuda(), max_seqlen_k=M) if seqlens is not None else {}
+            if kind == "fp8":
+                k, v = (torch.from_numpy(x).cuda().view(torch.float8_e4m3fn) for x in (kc8, vc8))
+                out, lse = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), k, v, _f16(ks8), _f16(vs8), S, window_size=W,
+                                                     out_dtype=torch.float32, **kw)
+            else:
+                out, lse = A.attn_decode_splitkv_int4(dev(qh, "bf16"), _u8(kc4), _u8(vc4), _flat_ss(ks4),
+                                                      _flat_ss(vs4), S, window_size=W, out_dtype=torch.float32, **kw)
+            torch.cuda.synchronize()
+            for b in range(B):
+                n = M if seqlens is None else int(seqlens[b])
+                lo = max(0, n - W)
+                if kind == "fp8":
+                    oo, ol = _fp8_oracle(qh[b:b + 1], kc8[b:b + 1, lo:n], vc8[b:b + 1, lo:n], ks8[b:b + 1, lo:n],
+                                         vs8[b:b + 1, lo:n])
+                else:
+                    oo, ol = _int4_oracle(qh[b:b + 1], kc4[b:b + 1, lo:n], vc4[b:b + 1, lo:n], ks4[b:b + 1, lo:n],
+                                          vs4[b:b + 1, lo:n])
+                check(out[b:b + 1], lse[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"{kind} b={b} keys [{lo}, {n})")
+
+
 @pytest.mark.parametrize("kind", ["bf16", "int4"])
 def test_decode_permuted_head_order(A, kind):
     """5-D [B, M, G, H, D] caches viewed out of [B, M, H, G, D] memory (G inner to H): inside a

@@ -79,12 +79,14 @@ _lib.attn_decode_splitkv_noalloc.argtypes = [_T, _T, _T, ctypes.c_int32, ctypes.
                                               ctypes.c_void_p]
 _lib.attn_decode_splitkv_noalloc.restype = ctypes.c_int
 _lib.attn_decode_splitkv_paged.argtypes = [_T, _T, _T, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
-                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
-                                           ctypes.c_void_p, ctypes.c_size_t, _T, ctypes.c_void_p, ctypes.c_void_p]
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, _T, ctypes.c_void_p,
+                                           ctypes.c_void_p]
 _lib.attn_decode_splitkv_paged.restype = ctypes.c_int
 _lib.attn_decode_splitkv_fp8.argtypes = [_T, _T, _T, _T, _T, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
-                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
-                                         ctypes.c_void_p, ctypes.c_size_t, _T, ctypes.c_void_p, ctypes.c_void_p]
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, _T, ctypes.c_void_p,
+                                         ctypes.c_void_p]
 _lib.attn_decode_splitkv_fp8.restype = ctypes.c_int
 _lib.attn_decode_splitkv_int4.argtypes = _lib.attn_decode_splitkv_fp8.argtypes
 _lib.attn_decode_splitkv_int4.restype = ctypes.c_int
@@ -461,24 +463,25 @@ def _cache_index(q, seqlens, block_tables, what="batch elements", B=None):
 
 
 def _paged_args(q, k, v, seqlens, block_tables, page_size, max_seqlen_k, num_splits, scale, workspace, out, lse,
-                stream):
+                stream, window_size=None):
     _cache_index(q, seqlens, block_tables)
     _lse_buf(lse, q.shape[0] * _htot(q))
     _on_device(seqlens=seqlens, block_tables=block_tables, lse=lse)
     ds = [desc(q, name="q"), desc(k, name="k"), desc(v, name="v"), desc(out, name="out")]
     mb = block_tables.shape[1] if block_tables is not None else 0
     args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), _ptr(seqlens), _ptr(block_tables),
-            int(mb), int(page_size or 0), int(max_seqlen_k), int(num_splits), _scale(scale), _ptr(workspace),
-            _ws_bytes(workspace), ctypes.byref(ds[3]), _ptr(lse), _stream(stream, q.device))
+            int(mb), int(page_size or 0), int(max_seqlen_k), int(window_size or 0), int(num_splits), _scale(scale),
+            _ptr(workspace), _ws_bytes(workspace), ctypes.byref(ds[3]), _ptr(lse), _stream(stream, q.device))
     return args, ds
 
 
 def attn_decode_splitkv_paged(q, k, v, seqlens, num_splits, max_seqlen_k, block_tables=None, page_size=None,
-                              scale=None, workspace=None, out=None, lse=True, stream=None):
+                              scale=None, workspace=None, out=None, lse=True, stream=None, window_size=None):
     """Split-KV decode against padded lanes (block_tables None) or a paged cache: returns (out, lse or None).
-    num_splits None: the library's choice for max_seqlen_k keys."""
+    num_splits None: the library's choice for max_seqlen_k keys (or the window's).  window_size W: the
+    query sees only its sequence's last W keys."""
     if num_splits is None:
-        num_splits = attn_decode_num_splits(q.shape[0], _htot(q), max_seqlen_k)
+        num_splits = attn_decode_num_splits(q.shape[0], _htot(q), min(max_seqlen_k, window_size or max_seqlen_k))
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is True:
@@ -489,21 +492,21 @@ def attn_decode_splitkv_paged(q, k, v, seqlens, num_splits, max_seqlen_k, block_
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     args, _keep = _paged_args(q, k, v, seqlens, block_tables, page_size, max_seqlen_k, num_splits, scale, workspace,
-                              out, lse, stream)
+                              out, lse, stream, window_size)
     _check(_lib.attn_decode_splitkv_paged(*args))
     return out, lse
 
 
 def prepare_decode_paged(q, k, v, seqlens, num_splits, max_seqlen_k, workspace, out, lse, block_tables=None,
-                         page_size=None, scale=None, stream=None) -> Prepared:
+                         page_size=None, scale=None, stream=None, window_size=None) -> Prepared:
     """attn_decode_splitkv_paged with every argument marshalled up front."""
     args, ds = _paged_args(q, k, v, seqlens, block_tables, page_size, max_seqlen_k, num_splits, scale, workspace,
-                           out, lse, stream)
+                           out, lse, stream, window_size)
     return Prepared(_lib.attn_decode_splitkv_paged, args, (ds, q, k, v, seqlens, block_tables, workspace, out, lse))
 
 
 def _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k, num_splits,
-              scale, workspace, out, lse, stream, kv_code=None):
+              scale, workspace, out, lse, stream, kv_code=None, window_size=None):
     _cache_index(q, seqlens, block_tables)
     _lse_buf(lse, q.shape[0] * _htot(q))
     _on_device(seqlens=seqlens, block_tables=block_tables, lse=lse)
@@ -512,14 +515,14 @@ def _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page
     mb = block_tables.shape[1] if block_tables is not None else 0
     args = (ctypes.byref(ds[0]), ctypes.byref(ds[1]), ctypes.byref(ds[2]), ctypes.byref(ds[3]), ctypes.byref(ds[4]),
             _ptr(seqlens), _ptr(block_tables), int(mb), int(page_size or 0), int(max_seqlen_k or 0),
-            int(num_splits), _scale(scale), _ptr(workspace), _ws_bytes(workspace), ctypes.byref(ds[5]), _ptr(lse),
-            _stream(stream, q.device))
+            int(window_size or 0), int(num_splits), _scale(scale), _ptr(workspace), _ws_bytes(workspace),
+            ctypes.byref(ds[5]), _ptr(lse), _stream(stream, q.device))
     return args, ds
 
 
 def attn_decode_splitkv_fp8(q, k, v, k_scale_shift, v_scale_shift, num_splits, seqlens=None, max_seqlen_k=None,
                             block_tables=None, page_size=None, scale=None, workspace=None, out=None, lse=True,
-                            out_dtype=None, stream=None):
+                            out_dtype=None, stream=None, window_size=None):
     """Split-KV decode over FP8 E4M3 K/V caches (torch.float8_e4m3fn) with float16 (scale, shift)
     pairs [..., 2] per cache row and head; lanes, padded lanes (seqlens) or pages (block_tables).
     Returns (out, lse or None)."""
@@ -535,16 +538,17 @@ def attn_decode_splitkv_fp8(q, k, v, k_scale_shift, v_scale_shift, num_splits, s
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     args, _keep = _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k,
-                            num_splits, scale, workspace, out, lse, stream)
+                            num_splits, scale, workspace, out, lse, stream, window_size=window_size)
     _check(_lib.attn_decode_splitkv_fp8(*args))
     return out, lse
 
 
 def prepare_decode_fp8(q, k, v, k_scale_shift, v_scale_shift, num_splits, workspace, out, lse, seqlens=None,
-                       max_seqlen_k=None, block_tables=None, page_size=None, scale=None, stream=None) -> Prepared:
+                       max_seqlen_k=None, block_tables=None, page_size=None, scale=None, stream=None,
+                       window_size=None) -> Prepared:
     """attn_decode_splitkv_fp8 with every argument marshalled up front."""
     args, ds = _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k,
-                         num_splits, scale, workspace, out, lse, stream)
+                         num_splits, scale, workspace, out, lse, stream, window_size=window_size)
     return Prepared(_lib.attn_decode_splitkv_fp8, args,
                     (ds, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, workspace, out, lse))
 
@@ -594,7 +598,7 @@ def prepare_bwd(dout, q, k, v, out, lse, dq, dk, dv, workspace, mask=MASK_NONE, 
 
 def attn_decode_splitkv_int4(q, k, v, k_scale_shift, v_scale_shift, num_splits, seqlens=None, max_seqlen_k=None,
                              block_tables=None, page_size=None, scale=None, workspace=None, out=None, lse=True,
-                             out_dtype=None, stream=None):
+                             out_dtype=None, stream=None, window_size=None):
     """Split-KV decode over INT4 K/V caches: uint8 tensors [..., D/2] (two 4-bit codes per byte,
     even element low) with float16 (scale, shift) pairs [..., 2G] per cache row, head and group.
     Lanes, padded lanes (seqlens) or pages (block_tables).  Returns (out, lse or None)."""
@@ -610,16 +614,19 @@ def attn_decode_splitkv_int4(q, k, v, k_scale_shift, v_scale_shift, num_splits, 
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     args, _keep = _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k,
-                            num_splits, scale, workspace, out, lse, stream, kv_code=ATTN_DTYPE_INT4X2)
+                            num_splits, scale, workspace, out, lse, stream, kv_code=ATTN_DTYPE_INT4X2,
+                            window_size=window_size)
     _check(_lib.attn_decode_splitkv_int4(*args))
     return out, lse
 
 
 def prepare_decode_int4(q, k, v, k_scale_shift, v_scale_shift, num_splits, workspace, out, lse, seqlens=None,
-                        max_seqlen_k=None, block_tables=None, page_size=None, scale=None, stream=None) -> Prepared:
+                        max_seqlen_k=None, block_tables=None, page_size=None, scale=None, stream=None,
+                        window_size=None) -> Prepared:
     """attn_decode_splitkv_int4 with every argument marshalled up front."""
     args, ds = _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page_size, max_seqlen_k,
-                         num_splits, scale, workspace, out, lse, stream, kv_code=ATTN_DTYPE_INT4X2)
+                         num_splits, scale, workspace, out, lse, stream, kv_code=ATTN_DTYPE_INT4X2,
+                         window_size=window_size)
     return Prepared(_lib.attn_decode_splitkv_int4, args,
                     (ds, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, workspace, out, lse))
 

@@ -691,8 +691,8 @@ namespace {
 attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
                    const attn_tensor *ksst, const attn_tensor *vsst, const int32_t *seqlens,
                    const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
-                   int32_t num_splits, float scale, void *workspace, size_t workspace_bytes, const attn_tensor *ot,
-                   float *lse, attn_stream_t stream) {
+                   int32_t window_size, int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                   const attn_tensor *ot, float *lse, attn_stream_t stream) {
     View q, k, v, o, kss{}, vss{};
     attn_status st;
     const unsigned kv_dt = quant ? 1u << quant : DT_FLOAT;
@@ -744,6 +744,7 @@ attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_
     if (num_splits < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: num_splits must be >= 1", fn);
     if (num_splits > ATTN_MAX_CHUNKS)
         return fail(ATTN_ERR_UNSUPPORTED, "%s: num_splits must be <= %d", fn, ATTN_MAX_CHUNKS);
+    if (window_size < 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: window_size must be >= 0 (0: none)", fn);
     if (!(std::isnan(scale) || std::isfinite(scale)))
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: scale must be finite (or NaN for 1/sqrt(K))", fn);
     if (lse && ((uintptr_t)lse) % 4) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
@@ -788,7 +789,10 @@ attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_
     d.Hin = (int)q.H;
     d.D = (int)q.D;
     d.S = num_splits;
-    d.chunk = (int)(((int64_t)max_seqlen_k + num_splits - 1) / num_splits);
+    // with a window the chunks cover the last window_size keys of each sequence
+    const int64_t span = window_size > 0 ? std::min<int64_t>(max_seqlen_k, window_size) : max_seqlen_k;
+    d.chunk = (int)((span + num_splits - 1) / num_splits);
+    d.window = window_size;
     const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)q.D) : (double)scale;
     d.scale_log2 = (float)(sc * 1.4426950408889634);
     d.ws_o = (float *)workspace;
@@ -885,51 +889,54 @@ attn_status attn_decode_splitkv_noalloc(const attn_tensor *qt, const attn_tensor
                     fn, need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
     void *ws = nullptr;
     if ((st = scratch_address(fn, &ws)) != ATTN_OK) return st;
-    return decode(fn, 0, qt, kt, vt, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, num_splits, scale, ws,
+    return decode(fn, 0, qt, kt, vt, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, num_splits, scale, ws,
                   (size_t)ATTN_NOALLOC_SCRATCH_BYTES, ot, lse, stream);
 }
 
 attn_status attn_decode_splitkv(const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
                                 int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                 const attn_tensor *ot, float *lse, attn_stream_t stream) {
-    return decode("attn_decode_splitkv", 0, qt, kt, vt, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, num_splits,
+    return decode("attn_decode_splitkv", 0, qt, kt, vt, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, num_splits,
                   scale, workspace, workspace_bytes, ot, lse, stream);
 }
 
 attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                                       const int32_t *seqlens, const int32_t *block_tables,
                                       int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                      int32_t window_size,
                                       int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                       const attn_tensor *out, float *lse, attn_stream_t stream) {
     return decode("attn_decode_splitkv_paged", 0, q, k, v, nullptr, nullptr, seqlens, block_tables,
-                  max_blocks_per_seq, page_size, max_seqlen_k, num_splits, scale, workspace, workspace_bytes, out, lse,
-                  stream);
+                  max_blocks_per_seq, page_size, max_seqlen_k, window_size, num_splits, scale, workspace,
+                  workspace_bytes, out, lse, stream);
 }
 
 attn_status attn_decode_splitkv_fp8(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                                     const attn_tensor *k_scale_shift, const attn_tensor *v_scale_shift,
                                     const int32_t *seqlens, const int32_t *block_tables,
                                     int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                    int32_t window_size,
                                     int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                     const attn_tensor *out, float *lse, attn_stream_t stream) {
     const char *fn = "attn_decode_splitkv_fp8";
     if (block_tables && !seqlens) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block_tables need seqlens", fn);
     return decode(fn, ATTN_DTYPE_FP8_E4M3, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables,
-                  max_blocks_per_seq, page_size, max_seqlen_k, num_splits, scale, workspace, workspace_bytes, out,
-                  lse, stream);
+                  max_blocks_per_seq, page_size, max_seqlen_k, window_size, num_splits, scale, workspace,
+                  workspace_bytes, out, lse, stream);
 }
 
 attn_status attn_decode_splitkv_int4(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                                      const attn_tensor *k_scale_shift, const attn_tensor *v_scale_shift,
                                      const int32_t *seqlens, const int32_t *block_tables,
                                      int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                     int32_t window_size,
                                      int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                      const attn_tensor *out, float *lse, attn_stream_t stream) {
     const char *fn = "attn_decode_splitkv_int4";
     if (block_tables && !seqlens) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block_tables need seqlens", fn);
     return decode(fn, ATTN_DTYPE_INT4X2, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables,
-                  max_blocks_per_seq, page_size, max_seqlen_k, num_splits, scale, workspace, workspace_bytes, out,
-                  lse, stream);
+                  max_blocks_per_seq, page_size, max_seqlen_k, window_size, num_splits, scale, workspace,
+                  workspace_bytes, out, lse, stream);
 }
 
 }  // extern "C"

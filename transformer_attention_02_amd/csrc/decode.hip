@@ -189,7 +189,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const int b = id % a.B;
     const int s = id / a.B;
     const int Lb = MODE == 0 ? a.Mkv : min(max(a.seqlens[b], 0), a.cap);
-    const int j0 = min(Lb, s * a.chunk);
+    const int jb = a.window > 0 ? max(0, Lb - a.window) : 0;  // first key the query sees
+    const int j0 = min(Lb, jb + s * a.chunk);
     const int j1 = min(Lb, j0 + a.chunk);
     const int64_t kb = MODE == 2 ? 0 : (int64_t)b * a.sk.b, vb = MODE == 2 ? 0 : (int64_t)b * a.sv.b;
 

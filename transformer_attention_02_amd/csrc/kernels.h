@@ -69,6 +69,7 @@ struct DecodeArgs {
     const int32_t *seqlens;       // [B], clamped to [0, cap]
     const int32_t *block_tables;  // [B, bt_stride] page numbers, or null (lanes [B, cap, ...])
     int bt_stride, page_size, num_pages, cap;
+    int window;  // > 0: the query sees only its sequence's last `window` keys; chunks cover those
     // FP8 / INT4 caches only: (scale, shift) fp16 pairs per cache row, head and group of
     // `group` consecutive elements (a multiple of 32 dividing D); strides in fp16 units
     const void *kss, *vss;
