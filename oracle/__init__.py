@@ -58,6 +58,8 @@ def _load():
         lib.oracle_fp8_e4m3.restype = ctypes.c_double
         lib.oracle_dequant_fp8_rowwise.argtypes = [i64, i64, ctypes.c_void_p, dp, dp]
         lib.oracle_dequant_fp8_rowwise.restype = None
+        lib.oracle_dequant_fp8_groupwise.argtypes = [i64, i64, i64, ctypes.c_void_p, dp, dp]
+        lib.oracle_dequant_fp8_groupwise.restype = None
         lib.oracle_dequant_int4_groupwise.argtypes = [i64, i64, i64, ctypes.c_void_p, dp, dp]
         lib.oracle_dequant_int4_groupwise.restype = None
         _lib = lib
@@ -186,6 +188,20 @@ def dequant_fp8_rowwise(codes, scale_shift):
     rows = codes.size // D if D else 0
     x = np.empty(codes.shape, dtype=np.float64)
     _load().oracle_dequant_fp8_rowwise(rows, D, codes.ctypes.data, _dp(ss), _dp(x))
+    return x
+
+
+def dequant_fp8_groupwise(codes, scale_shift):
+    """codes uint8 [..., D] (E4M3), scale_shift [..., G, 2] -> fp64 [..., D] = fp8(code) * scale +
+    shift of the element's group (D/G consecutive elements per group)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    ss = np.ascontiguousarray(scale_shift, dtype=np.float64)
+    G = ss.shape[-2]
+    D = codes.shape[-1]
+    assert ss.shape == codes.shape[:-1] + (G, 2) and D % G == 0
+    rows = codes.size // D if D else 0
+    x = np.empty(codes.shape, dtype=np.float64)
+    _load().oracle_dequant_fp8_groupwise(rows, D, G, codes.ctypes.data, _dp(ss), _dp(x))
     return x
 
 

@@ -300,6 +300,21 @@ void oracle_dequant_fp8_rowwise(int64_t rows, int64_t D, const uint8_t *codes, c
         for (int64_t d = 0; d < D; ++d) x[r * D + d] = oracle_fp8_e4m3(codes[r * D + d]) * ss[2 * r] + ss[2 * r + 1];
 }
 
+/* Group-wise FP8 dequantisation (InputsFp8: "row/group quantised" FP8 caches): each of `rows`
+ * rows holds D E4M3 codes and G (scale, shift) pairs, one per group of D/G consecutive elements:
+ * x[r, d] = fp8(codes[r, d]) * ss[r, g, 0] + ss[r, g, 1],  g = d / (D/G).  G = 1 is the
+ * row-wise form above. */
+void oracle_dequant_fp8_groupwise(int64_t rows, int64_t D, int64_t G, const uint8_t *codes, const double *ss,
+                                  double *x) {
+    const int64_t gs = D / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t d = 0; d < D; ++d) {
+            const int64_t g = d / gs;
+            x[r * D + d] = oracle_fp8_e4m3(codes[r * D + d]) * ss[(r * G + g) * 2] + ss[(r * G + g) * 2 + 1];
+        }
+}
+
 /* Group-wise INT4 dequantisation (triton_splitk.FwOp: row/group INT4 caches stored through
  * int32 words): each of `rows` rows holds D unsigned 4-bit codes, two per byte, element 2i in
  * the low nibble of byte i (so eight per 32-bit word), and G (scale, shift) pairs, one per

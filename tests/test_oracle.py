@@ -429,6 +429,32 @@ def test_rowwise_dequant_is_affine_per_row(oracle_mod):
     np.testing.assert_array_equal(z, np.full((1, 4), -0.5))
 
 
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_fp8_groupwise_dequant(oracle_mod, G):
+    """Group-wise FP8 ("row/group quantised" caches): each element is its code's E4M3 value (taken
+    from torch.float8_e4m3fn, an independent decoder) times its own group's scale plus that group's
+    shift; distinct scales and shifts per group and row catch a wrong group index."""
+    import torch
+
+    rows, D = 5, 32
+    codes = synth.fp8_codes(11 + G, 1, (rows, D))
+    ss = np.zeros((rows, G, 2))
+    ss[..., 0] = 1.0 + np.arange(G)
+    ss[..., 1] = 100.0 * np.arange(rows)[:, None] + 10.0 * np.arange(G)[None, :]
+    x = oracle_mod.dequant_fp8_groupwise(codes, ss)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    gs = D // G
+    for r in range(rows):
+        for d in range(D):
+            g = d // gs
+            assert x[r, d] == vals[r, d] * (g + 1) + 100.0 * r + 10.0 * g
+    if G == 1:  # the row-wise form
+        np.testing.assert_array_equal(x, oracle_mod.dequant_fp8_rowwise(codes, ss[:, 0]))
+    # zero codes give each group's shift
+    z = oracle_mod.dequant_fp8_groupwise(np.zeros((1, 4), np.uint8), np.array([[[3.0, 0.5], [3.0, -0.5]]]))
+    np.testing.assert_array_equal(z, [[0.5, 0.5, -0.5, -0.5]])
+
+
 def test_fp8_codes_avoid_nan_and_stay_in_range(oracle_mod):
     codes = synth.fp8_codes(4, 0, (4096,))
     vals = np.vectorize(oracle_mod.fp8_e4m3)(codes)
