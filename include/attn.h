@@ -329,15 +329,18 @@ attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k
 /* Split-KV decode against a row-wise quantised FP8 K/V cache ("Attention - operator protocol",
  * InputsFp8: row/group quantised FP8 K/V caches whose scale/shift metadata the split-K decode
  * backends read directly; triton_splitk.FwOp: row-wise FP8 caches).  Stored row r of head h
- * holds D codes and one (scale, shift) pair; its values are  fp8(code) * scale + shift,  and
- * the result is that of attn_decode_splitkv / _paged on those values.
+ * holds D codes and G (scale, shift) pairs; its values are  fp8(code) * scale + shift  of
+ * each element's group, and the result is that of attn_decode_splitkv / _paged on those
+ * values.
  *   q [B, 1, (G,) H, D] bf16, D in {64, 128, 256}.
  *   k, v: ATTN_DTYPE_FP8_E4M3 caches laid out as in attn_decode_splitkv (seqlens and
  *     block_tables both NULL: every sequence holds all of its lane), or as in
  *     attn_decode_splitkv_paged (seqlens given: padded lanes; block_tables too: paged).
- *   k_scale_shift, v_scale_shift: ATTN_DTYPE_F16, the shape of k with D replaced by 2,
- *     stride-1 last axis and 4-byte aligned rows: (scale, shift) of every cache row and
- *     head, i.e. one 32-bit word with the scale in its low half.
+ *   k_scale_shift, v_scale_shift: ATTN_DTYPE_F16, the shape of k with D replaced by 2G,
+ *     stride-1 last axis and 4-byte aligned rows: G (scale, shift) pairs of every cache row
+ *     and head, one per group of D/G consecutive elements (G = 1: row-wise; D/G a multiple
+ *     of 16), each one 32-bit word with the scale in its low half; element d's value is
+ *     fp8(code) * scale_g + shift_g with g = d / (D/G).
  *   out [B, 1, (G,) H, D] bf16 or fp32; lse fp32 [B, H_total, 1] or NULL.
  *   The codes and metadata are read as they are; NaN codes or metadata propagate.
  *   Workspace, splits, window_size, scale, device-metadata handling and errors as in

@@ -325,8 +325,9 @@ def test_int4_decode_rejects():
     assert call(k=tensor([B, M, H, D], A.ATTN_DTYPE_INT4X2)) == A.ATTN_ERR_INVALID_ARGUMENT  # D codes = D/2 bytes
     assert call(k=tensor([B, M, H, D // 2], A.ATTN_DTYPE_FP8_E4M3)) == A.ATTN_ERR_INVALID_ARGUMENT
     k8 = tensor([B, M, H, D], A.ATTN_DTYPE_FP8_E4M3)
-    assert call(k=k8, kss=ss(2), fn=A._lib.attn_decode_splitkv_fp8) == A.ATTN_ERR_INVALID_ARGUMENT
-    assert "row-wise" in A.attn_last_error()
+    # FP8 groups: a lane's 16 codes share one group, so D/G must be a multiple of 16
+    assert call(k=k8, kss=ss(16), fn=A._lib.attn_decode_splitkv_fp8) == A.ATTN_ERR_UNSUPPORTED
+    assert "multiple of 16" in A.attn_last_error()
     assert call(k=tensor([B, M, H, D // 2], A.ATTN_DTYPE_INT4X2, data=FAKE + 8)) == A.ATTN_ERR_INVALID_ARGUMENT
 
 

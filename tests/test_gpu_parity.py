@@ -782,6 +782,52 @@ def test_fp8_decode_contiguous(A, D, out_dtype):
         check(out, lse, oo, ol, tol_o, tol_l, f"fp8 S={S}")
 
 
+@pytest.mark.parametrize("D,G", [(128, 2), (128, 8), (64, 4), (256, 4)])
+def test_fp8_decode_groupwise(A, D, G):
+    """Group-wise FP8 caches (InputsFp8 "row/group quantised"): G (scale, shift) pairs per row and
+    head, groups of D/G elements down to 16; contiguous lanes with 3 splits, padded lanes and
+    64-row pages in a random order; fp32 outputs against the oracle's group-wise dequantisation."""
+    B, M, H, S, page = 3, 640, 4, 3, 64
+    lens = np.array([640, 1, 333], dtype=np.int32)
+    say(f"case: fp8 decode group-wise D={D} G={G}")
+    qh = synth.normal(1170 + G, synth.TAG_Q, (B, 1, H, D), "bf16")
+    kc, vc = (synth.fp8_codes(1170 + G, t, (B, M, H, D)) for t in (synth.TAG_K, synth.TAG_V))
+    kss, vss = (synth.scale_shift(1170 + G, t, (B, M, H, G)) for t in (synth.TAG_K, synth.TAG_V))
+    flat = lambda x: _f16(x.reshape(B, M, H, 2 * G))
+    k8, v8 = (torch.from_numpy(x).cuda().view(torch.float8_e4m3fn) for x in (kc, vc))
+    ref = [oracle.attention(synth.to_f64(qh[b:b + 1], "bf16"), oracle.dequant_fp8_groupwise(kc[b:b + 1], kss[b:b + 1]),
+                            oracle.dequant_fp8_groupwise(vc[b:b + 1], vss[b:b + 1])) for b in range(B)]
+    out, lse = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), k8, v8, flat(kss), flat(vss), S, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        check(out[b:b + 1], lse[b:b + 1], *ref[b], TOL_F32, TOL_F32, f"contiguous b={b}")
+    out, lse = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), k8, v8, flat(kss), flat(vss), S,
+                                         seqlens=torch.from_numpy(lens).cuda(), max_seqlen_k=M,
+                                         out_dtype=torch.float32)
+    # the same rows as 64-row pages of one cache, in a random order
+    nb = M // page
+    tables = np.random.Generator(np.random.PCG64(1171)).permutation(B * nb).astype(np.int32).reshape(B, nb)
+    pc = lambda x: np.concatenate([x[b, i * page:(i + 1) * page] for b in range(B) for i in range(nb)])
+    order = np.argsort(tables.reshape(-1))
+    def pg(x):
+        pages = pc(x).reshape((B * nb, page) + x.shape[2:])[order]
+        return np.ascontiguousarray(pages.reshape((1, B * M) + x.shape[2:]))
+    kp, vp = (torch.from_numpy(pg(x)).cuda().view(torch.float8_e4m3fn) for x in (kc, vc))
+    po, pl = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), kp, vp, _f16(pg(kss).reshape(1, B * M, H, 2 * G)),
+                                       _f16(pg(vss).reshape(1, B * M, H, 2 * G)), S,
+                                       seqlens=torch.from_numpy(lens).cuda(), max_seqlen_k=M,
+                                       block_tables=torch.from_numpy(tables).cuda(), page_size=page,
+                                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        n = int(lens[b])
+        oo, ol = oracle.attention(synth.to_f64(qh[b:b + 1], "bf16"),
+                                  oracle.dequant_fp8_groupwise(kc[b:b + 1, :n], kss[b:b + 1, :n]),
+                                  oracle.dequant_fp8_groupwise(vc[b:b + 1, :n], vss[b:b + 1, :n]))
+        check(out[b:b + 1], lse[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"padded lane b={b} len={n}")
+        check(po[b:b + 1], pl[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"paged b={b} len={n}")
+
+
 def test_fp8_decode_padded_lanes_5d_gqa(A):
     """Padded lanes, 5-D [B, M, G, H, D] with the K/V and metadata heads broadcast (stride 0) per group."""
     B, cap, G, Hg, D, S = 4, 600, 2, 3, 128, 5

@@ -717,10 +717,11 @@ attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_
             if (!same_heads(*m, k) || m->B != k.B || m->M != k.M)
                 return fail(ATTN_ERR_INVALID_ARGUMENT,
                             "%s: scale/shift tensors must have k's shape with the last axis 2G", fn);
-        if (quant == ATTN_DTYPE_FP8_E4M3 && G != 1)
-            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: FP8 caches are row-wise (scale/shift last axis 2)", fn);
-        if (G < 1 || k.D % G || (k.D / G) % 32)
-            return fail(ATTN_ERR_UNSUPPORTED, "%s: groups of D/G elements must be a multiple of 32", fn);
+        // a lane reads 16 FP8 codes or 32 INT4 codes of one row: each lane's codes share a group
+        const int64_t lane_elems = quant == ATTN_DTYPE_FP8_E4M3 ? 16 : 32;
+        if (G < 1 || k.D % G || (k.D / G) % lane_elems)
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: groups of D/G elements must be a multiple of %lld", fn,
+                        (long long)lane_elems);
         group = (int)(k.D / G);
     } else if (k.dtype != q.dtype || v.dtype != q.dtype || o.dtype != q.dtype) {
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q, k, v and out must share one dtype", fn);
