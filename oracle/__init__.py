@@ -60,6 +60,10 @@ def _load():
         lib.oracle_dequant_fp8_rowwise.restype = None
         lib.oracle_dequant_fp8_groupwise.argtypes = [i64, i64, i64, ctypes.c_void_p, dp, dp]
         lib.oracle_dequant_fp8_groupwise.restype = None
+        lib.oracle_e8m0.argtypes = [ctypes.c_uint8]
+        lib.oracle_e8m0.restype = ctypes.c_double
+        lib.oracle_dequant_mxfp8.argtypes = [i64, i64, ctypes.c_void_p, ctypes.c_void_p, dp]
+        lib.oracle_dequant_mxfp8.restype = None
         lib.oracle_dequant_int4_groupwise.argtypes = [i64, i64, i64, ctypes.c_void_p, dp, dp]
         lib.oracle_dequant_int4_groupwise.restype = None
         _lib = lib
@@ -202,6 +206,24 @@ def dequant_fp8_groupwise(codes, scale_shift):
     rows = codes.size // D if D else 0
     x = np.empty(codes.shape, dtype=np.float64)
     _load().oracle_dequant_fp8_groupwise(rows, D, G, codes.ctypes.data, _dp(ss), _dp(x))
+    return x
+
+
+def e8m0(e: int) -> float:
+    """Value of one E8M0 block scale: 2^(e - 127), NaN for 255."""
+    return float(_load().oracle_e8m0(int(e) & 0xFF))
+
+
+def dequant_mxfp8(codes, scales):
+    """codes uint8 [..., D] (E4M3), scales uint8 [..., D/32] (E8M0, one per block of 32 elements)
+    -> fp64 [..., D] = fp8(code) * 2^(e - 127)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    sc = np.ascontiguousarray(scales, dtype=np.uint8)
+    D = codes.shape[-1]
+    assert D % 32 == 0 and sc.shape == codes.shape[:-1] + (D // 32,)
+    rows = codes.size // D if D else 0
+    x = np.empty(codes.shape, dtype=np.float64)
+    _load().oracle_dequant_mxfp8(rows, D, codes.ctypes.data, sc.ctypes.data, _dp(x))
     return x
 
 

@@ -315,6 +315,20 @@ void oracle_dequant_fp8_groupwise(int64_t rows, int64_t D, int64_t G, const uint
         }
 }
 
+/* E8M0 block scale (the MX formats' shared scale): 2^(e - 127) for e = 0 .. 254; e = 255 is NaN. */
+double oracle_e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* MXFP8 dequantisation ("Attention - operator protocol": InputsMXFp8, FP8 K/V with E8M0 block
+ * scales): each of `rows` rows holds D E4M3 codes and D/32 E8M0 scales, one per block of 32
+ * consecutive elements (the MX standard's block size):  x[r, d] = fp8(codes[r, d]) * 2^(e[r, d/32] - 127). */
+void oracle_dequant_mxfp8(int64_t rows, int64_t D, const uint8_t *codes, const uint8_t *e8m0, double *x) {
+    const int64_t nb = D / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t d = 0; d < D; ++d)
+            x[r * D + d] = oracle_fp8_e4m3(codes[r * D + d]) * oracle_e8m0(e8m0[r * nb + d / 32]);
+}
+
 /* Group-wise INT4 dequantisation (triton_splitk.FwOp: row/group INT4 caches stored through
  * int32 words): each of `rows` rows holds D unsigned 4-bit codes, two per byte, element 2i in
  * the low nibble of byte i (so eight per 32-bit word), and G (scale, shift) pairs, one per

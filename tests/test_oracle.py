@@ -455,6 +455,34 @@ def test_fp8_groupwise_dequant(oracle_mod, G):
     np.testing.assert_array_equal(z, [[0.5, 0.5, -0.5, -0.5]])
 
 
+def test_e8m0_scales_match_torch(oracle_mod):
+    """All 256 E8M0 codes against torch.float8_e8m0fnu (an independent decoder); closed forms."""
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = np.array([oracle_mod.e8m0(c) for c in codes])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    np.testing.assert_array_equal(got[:255], ref[:255])
+    assert oracle_mod.e8m0(127) == 1.0 and oracle_mod.e8m0(128) == 2.0 and oracle_mod.e8m0(0) == 2.0 ** -127
+
+
+def test_mxfp8_dequant(oracle_mod):
+    """MXFP8: each element is its E4M3 value (torch's decoder) times 2^(e - 127) of its own block of
+    32; distinct scales per block and row catch a wrong block index, scale 127 leaves the codes."""
+    import torch
+
+    rows, D = 3, 128
+    codes = synth.fp8_codes(21, 1, (rows, D))
+    e = (120 + np.arange(rows)[:, None] * 4 + np.arange(D // 32)[None, :]).astype(np.uint8)
+    x = oracle_mod.dequant_mxfp8(codes, e)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for r in range(rows):
+        for d in range(D):
+            assert x[r, d] == vals[r, d] * 2.0 ** (int(e[r, d // 32]) - 127)
+    np.testing.assert_array_equal(oracle_mod.dequant_mxfp8(codes, np.full((rows, D // 32), 127, np.uint8)), vals)
+
+
 def test_fp8_codes_avoid_nan_and_stay_in_range(oracle_mod):
     codes = synth.fp8_codes(4, 0, (4096,))
     vals = np.vectorize(oracle_mod.fp8_e4m3)(codes)
