@@ -128,6 +128,7 @@ TRAFFIC_KERNELS = (
     ("decode bf16 16x32768x32x128 s64", "decode", "decode_kernel<128, 0, 0>", None),
     ("decode bf16 paged 16x32768x32x128 page64 s64", "decode", "decode_kernel<128, 0, 2>", None),
     ("decode fp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 2, 0>", None),
+    ("decode mxfp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 4, 0>", None),
     ("decode int4 g1 16x32768x32x128 s64", "decode", "decode_kernel<128, 3, 0>", 0),
     ("decode int4 g4 16x32768x32x128 s64", "decode", "decode_kernel<128, 3, 0>", 1),
 )
@@ -535,7 +536,35 @@ def main():
                 "batch element 0 of 16 (32768 keys x 32 heads): FP8 dequantisation and fp64 exact attention; "
                 "GB/s of its codes and metadata")
             del c8, s8
-        del k8, v8, kss, vss
+        # the same codes as an MXFP8 cache: one E8M0 scale per block of 32 elements (2^-6 .. 2^-1)
+        kex = torch.from_numpy(synth.e8m0_scales(4, synth.TAG_K, (B, Mkv, H, D // 32), 121, 126)).to("cuda")
+        vex = torch.from_numpy(synth.e8m0_scales(4, synth.TAG_V, (B, Mkv, H, D // 32), 121, 126)).to("cuda")
+        kex, vex = kex.view(torch.float8_e8m0fnu), vex.view(torch.float8_e8m0fnu)
+        tm = {}
+        ms_x = timed(A.prepare_decode_mxfp8(qd, k8, v8, kex, vex, S, ws, od, ld), 40, 3, torch, detail=tm)
+        mx_bytes = 2.0 * B * Mkv * H * (D + D // 32)
+        gbs_x = mx_bytes / (ms_x * 1e-3) / 1e9
+        log(f"mxfp8 decode S=64: {ms_x * 1e3:.1f} us/call, {gbs_x:.0f} GB/s")
+        result["rows"]["decode_mxfp8"] = {
+            "workload": "B=16 Mq=1 Mkv=32768 H=32 D=128, bf16 q, MXFP8 K/V (E4M3 codes, one E8M0 scale per 32 "
+                        "elements), 64 chunks of 512",
+            "ms_per_call": round(ms_x, 5), "value": round(gbs_x, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbs_x, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs_x / PEAK_HBM_GBS, 4), "bytes_per_call": mx_bytes,
+                         "traffic": recorded_traffic("decode mxfp8 16x32768x32x128 s64"),
+                         "note": "algorithmic bytes = K+V codes and their block scales once"}, **tm}
+        if not args.no_cpu:  # batch element 0: dequantise its codes, then the oracle
+            c8 = [synth.fp8_codes(4, t, (1, Mkv, H, D)) for t in (synth.TAG_K, synth.TAG_V)]
+            e8 = [synth.e8m0_scales(4, synth.TAG_K, (B, Mkv, H, D // 32), 121, 126)[:1],
+                  synth.e8m0_scales(4, synth.TAG_V, (B, Mkv, H, D // 32), 121, 126)[:1]]
+            result["rows"]["decode_mxfp8"]["cpu_oracle"] = oracle_timing(
+                lambda: oracle_mod().attention(q0, oracle_mod().dequant_mxfp8(c8[0], e8[0]),
+                                               oracle_mod().dequant_mxfp8(c8[1], e8[1])),
+                mx_bytes / B / 1e9, "GB/s",
+                "batch element 0 of 16 (32768 keys x 32 heads): MXFP8 dequantisation and fp64 exact attention; "
+                "GB/s of its codes and scales")
+            del c8, e8
+        del k8, v8, kss, vss, kex, vex
         torch.cuda.empty_cache()
 
         # the same shape with INT4 caches: two codes per byte, (scale, shift) fp16 pairs per row / group

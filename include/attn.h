@@ -82,9 +82,11 @@ typedef enum {
     ATTN_DTYPE_FP8_E4M3 = 2, /* OCP E4M3 ("FN": bias 7, no infinities, S.1111.111 = NaN); K/V caches of
                                 attn_decode_splitkv_fp8 only */
     ATTN_DTYPE_F16 = 3,      /* IEEE half; the scale/shift metadata of the quantised decodes only */
-    ATTN_DTYPE_INT4X2 = 4    /* two unsigned 4-bit codes per byte, element 2i in the low nibble of byte i;
+    ATTN_DTYPE_INT4X2 = 4,   /* two unsigned 4-bit codes per byte, element 2i in the low nibble of byte i;
                                 shape and strides of such a tensor count bytes (last dim = D / 2);
                                 K/V caches of attn_decode_splitkv_int4 only */
+    ATTN_DTYPE_E8M0 = 5      /* one byte e per block: the scale 2^(e - 127), e = 255 NaN (the MX formats'
+                                shared exponent); block scales of attn_decode_splitkv_mxfp8 only */
 } attn_dtype;
 
 /* Masks ("Attention - Biases & masks" on the kernel reference page).  For a
@@ -371,6 +373,23 @@ attn_status attn_decode_splitkv_int4(const attn_tensor *q, const attn_tensor *k,
                                      int32_t window_size,
                                      int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
                                      const attn_tensor *out, float *lse, attn_stream_t stream);
+
+/* Split-KV decode against an MXFP8 K/V cache ("Attention - operator protocol": InputsMXFp8, FP8 K/V
+ * with E8M0 block scales k_fp8_scale / v_fp8_scale).  Row r of head h holds D E4M3 codes and D/32
+ * E8M0 scales, one per block of 32 consecutive elements (the MX standard block); element d's value
+ * is  fp8(code_d) * 2^(e_{d/32} - 127).
+ *   q [B, 1, (G,) H, D] bf16, D in {64, 128, 256}.
+ *   k, v: ATTN_DTYPE_FP8_E4M3 caches laid out as in attn_decode_splitkv_fp8 (lanes, padded
+ *     lanes or pages).
+ *   k_scale, v_scale: ATTN_DTYPE_E8M0, the shape of k with the last axis D/32, stride-1 last axis.
+ *   Everything else as in attn_decode_splitkv_fp8. */
+attn_status attn_decode_splitkv_mxfp8(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                      const attn_tensor *k_scale, const attn_tensor *v_scale,
+                                      const int32_t *seqlens, const int32_t *block_tables,
+                                      int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                      int32_t window_size,
+                                      int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                                      const attn_tensor *out, float *lse, attn_stream_t stream);
 
 /* Reason for the last non-OK status returned on this thread ("" if none). */
 const char *attn_last_error(void);

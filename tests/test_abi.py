@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
                                            "attn_decode_workspace_bytes", "attn_decode_num_splits", "attn_decode_splitkv",
                                            "attn_decode_splitkv_noalloc",
                                            "attn_decode_splitkv_paged",
-                                           "attn_decode_splitkv_fp8", "attn_decode_splitkv_int4", "attn_bwd_workspace_bytes",
+                                           "attn_decode_splitkv_fp8", "attn_decode_splitkv_int4",
+                                           "attn_decode_splitkv_mxfp8", "attn_bwd_workspace_bytes",
                                            "attn_bwd",
                                            "attn_last_error"])
 
@@ -266,6 +267,26 @@ def test_fp8_decode_rejects():
     assert call(bt=FAKE) == A.ATTN_ERR_INVALID_ARGUMENT and "seqlens" in A.attn_last_error()
     assert call(k=tensor([B, M, H, 96], A.ATTN_DTYPE_FP8_E4M3)) == A.ATTN_ERR_INVALID_ARGUMENT
     assert call(k=tensor([B, M, H, D], A.ATTN_DTYPE_FP8_E4M3, data=FAKE + 8)) == A.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_mxfp8_decode_rejects():
+    B, H, D, S, M = 4, 8, 128, 4, 256
+    need = A.attn_decode_workspace_bytes(B, H, D, S)
+    q, o = tensor([B, 1, H, D]), tensor([B, 1, H, D])
+    k8 = tensor([B, M, H, D], A.ATTN_DTYPE_FP8_E4M3)
+    sc = lambda n, dt=A.ATTN_DTYPE_E8M0: tensor([B, M, H, n], dt, data=FAKE + 1)  # byte scales: any alignment
+
+    def call(k=k8, ks=None, vs=None):
+        ks = ks or sc(D // 32)
+        vs = vs or ks
+        return A._lib.attn_decode_splitkv_mxfp8(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(ks),
+                                                ctypes.byref(vs), None, None, 0, 0, 0, 0, S, float("nan"),
+                                                ctypes.c_void_p(FAKE * 256), need, ctypes.byref(o), None, None)
+    assert call(ks=sc(D // 32, A.ATTN_DTYPE_F16)) == A.ATTN_ERR_INVALID_ARGUMENT and "dtype" in A.attn_last_error()
+    assert call(ks=sc(D // 16)) == A.ATTN_ERR_INVALID_ARGUMENT and "D/32" in A.attn_last_error()
+    assert call(vs=tensor([B, M - 1, H, D // 32], A.ATTN_DTYPE_E8M0)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(k=tensor([B, M, H, D // 2], A.ATTN_DTYPE_INT4X2)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert call(k=tensor([B, M, H, 48], A.ATTN_DTYPE_FP8_E4M3), ks=sc(1)) == A.ATTN_ERR_INVALID_ARGUMENT
 
 
 def test_fp8_and_f16_tensors_are_rejected_outside_the_fp8_decode():

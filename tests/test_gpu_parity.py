@@ -828,6 +828,65 @@ def test_fp8_decode_groupwise(A, D, G):
         check(po[b:b + 1], pl[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"paged b={b} len={n}")
 
 
+def _e8m0(seed, tag, shape, hi):
+    """E8M0 block-scale bytes 121 .. hi (scales 2^-6 .. 2^(hi - 127)) and every 97th one 0 (2^-127,
+    a subnormal fp32 scale)."""
+    r = np.random.Generator(np.random.PCG64([seed, tag]))
+    e = r.integers(121, hi + 1, shape).astype(np.uint8)
+    e.reshape(-1)[::97] = 0
+    return e
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_mxfp8_decode(A, D):
+    """InputsMXFp8: E4M3 K/V with one E8M0 scale per block of 32 elements: contiguous lanes with 3
+    splits, padded lanes with a window of 200 keys and 64-row pages in a random order; fp32 outputs
+    against the oracle's MXFP8 dequantisation, blocks scaled by 2^-127 included."""
+    B, M, H, S, W, page = 3, 640, 4, 3, 200, 64
+    lens = np.array([640, 1, 333], dtype=np.int32)
+    say(f"case: mxfp8 decode D={D}")
+    qh = synth.normal(1180 + D, synth.TAG_Q, (B, 1, H, D), "bf16")
+    kc, vc = (synth.fp8_codes(1180 + D, t, (B, M, H, D)) for t in (synth.TAG_K, synth.TAG_V))
+    # scales up to 2^-1 keep scores, LSE and outputs near unit size (codes reach 15), where the
+    # absolute 1e-5 bound on fp32 results is meaningful
+    ke, ve = _e8m0(1180 + D, 1, (B, M, H, D // 32), 126), _e8m0(1180 + D, 2, (B, M, H, D // 32), 126)
+    up8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda().view(torch.float8_e4m3fn)
+    upe = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda().view(torch.float8_e8m0fnu)
+    deq = oracle.dequant_mxfp8
+    q64 = synth.to_f64(qh, "bf16")
+    out, lse = A.attn_decode_splitkv_mxfp8(dev(qh, "bf16"), up8(kc), up8(vc), upe(ke), upe(ve), S,
+                                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        oo, ol = oracle.attention(q64[b:b + 1], deq(kc[b:b + 1], ke[b:b + 1]), deq(vc[b:b + 1], ve[b:b + 1]))
+        check(out[b:b + 1], lse[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"contiguous b={b}")
+    out, lse = A.attn_decode_splitkv_mxfp8(dev(qh, "bf16"), up8(kc), up8(vc), upe(ke), upe(ve), S,
+                                           seqlens=torch.from_numpy(lens).cuda(), max_seqlen_k=M, window_size=W,
+                                           out_dtype=torch.float32)
+    nb = M // page
+    tables = np.random.Generator(np.random.PCG64(1181)).permutation(B * nb).astype(np.int32).reshape(B, nb)
+    order = np.argsort(tables.reshape(-1))
+
+    def pg(x):
+        pages = np.concatenate([x[b, i * page:(i + 1) * page] for b in range(B) for i in range(nb)])
+        pages = pages.reshape((B * nb, page) + x.shape[2:])[order]
+        return np.ascontiguousarray(pages.reshape((1, B * M) + x.shape[2:]))
+    po, pl = A.attn_decode_splitkv_mxfp8(dev(qh, "bf16"), up8(pg(kc)), up8(pg(vc)), upe(pg(ke)), upe(pg(ve)), S,
+                                         seqlens=torch.from_numpy(lens).cuda(), max_seqlen_k=M,
+                                         block_tables=torch.from_numpy(tables).cuda(), page_size=page,
+                                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        n = int(lens[b])
+        oo, ol = oracle.attention(q64[b:b + 1], deq(kc[b:b + 1, :n], ke[b:b + 1, :n]),
+                                  deq(vc[b:b + 1, :n], ve[b:b + 1, :n]))
+        check(po[b:b + 1], pl[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"paged b={b} len={n}")
+        lo = max(0, n - W)
+        oo, ol = oracle.attention(q64[b:b + 1], deq(kc[b:b + 1, lo:n], ke[b:b + 1, lo:n]),
+                                  deq(vc[b:b + 1, lo:n], ve[b:b + 1, lo:n]))
+        check(out[b:b + 1], lse[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"padded lane b={b} keys [{lo}, {n})")
+
+
 def test_fp8_decode_padded_lanes_5d_gqa(A):
     """Padded lanes, 5-D [B, M, G, H, D] with the K/V and metadata heads broadcast (stride 0) per group."""
     B, cap, G, Hg, D, S = 4, 600, 2, 3, 128, 5

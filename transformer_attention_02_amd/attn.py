@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARGUMENT, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE_TOO_SMALL, ATTN_ERR_LAUNCH = range(5)
-ATTN_DTYPE_F32, ATTN_DTYPE_BF16, ATTN_DTYPE_FP8_E4M3, ATTN_DTYPE_F16, ATTN_DTYPE_INT4X2 = 0, 1, 2, 3, 4
+ATTN_DTYPE_F32, ATTN_DTYPE_BF16, ATTN_DTYPE_FP8_E4M3, ATTN_DTYPE_F16, ATTN_DTYPE_INT4X2, ATTN_DTYPE_E8M0 = range(6)
 MASK_NONE, MASK_CAUSAL, MASK_BLOCKDIAG, MASK_BLOCKDIAG_CAUSAL = 0, 1, 2, 3
 MASK_CAUSAL_BR, MASK_BLOCKDIAG_CAUSAL_BR, MASK_LOCAL_BR, MASK_CAUSAL_LOCAL_BR = 4, 5, 6, 7
 MASK_BLOCKDIAG_CAUSAL_LOCAL, MASK_BLOCKDIAG_CAUSAL_LOCAL_BR = 8, 9
@@ -90,6 +90,8 @@ _lib.attn_decode_splitkv_fp8.argtypes = [_T, _T, _T, _T, _T, ctypes.c_void_p, ct
 _lib.attn_decode_splitkv_fp8.restype = ctypes.c_int
 _lib.attn_decode_splitkv_int4.argtypes = _lib.attn_decode_splitkv_fp8.argtypes
 _lib.attn_decode_splitkv_int4.restype = ctypes.c_int
+_lib.attn_decode_splitkv_mxfp8.argtypes = _lib.attn_decode_splitkv_fp8.argtypes
+_lib.attn_decode_splitkv_mxfp8.restype = ctypes.c_int
 _lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
 _lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.attn_bwd.argtypes = [_T, _T, _T, _T, _T, ctypes.c_void_p, _P(AttnMask), _P(AttnVarlen), ctypes.c_float,
@@ -114,6 +116,8 @@ def _dtype_code(dt: torch.dtype) -> int:
         return ATTN_DTYPE_FP8_E4M3
     if dt == torch.float16:
         return ATTN_DTYPE_F16
+    if dt == torch.float8_e8m0fnu:
+        return ATTN_DTYPE_E8M0
     raise TypeError(f"unsupported dtype {dt}")
 
 
@@ -630,3 +634,36 @@ def prepare_decode_int4(q, k, v, k_scale_shift, v_scale_shift, num_splits, works
     return Prepared(_lib.attn_decode_splitkv_int4, args,
                     (ds, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, workspace, out, lse))
 
+
+def attn_decode_splitkv_mxfp8(q, k, v, k_scale, v_scale, num_splits, seqlens=None, max_seqlen_k=None,
+                              block_tables=None, page_size=None, scale=None, workspace=None, out=None, lse=True,
+                              out_dtype=None, stream=None, window_size=None):
+    """Split-KV decode over MXFP8 K/V caches: E4M3 codes (torch.float8_e4m3fn) with one E8M0 block
+    scale per 32 elements (torch.float8_e8m0fnu [..., D/32]).  Lanes, padded lanes (seqlens) or
+    pages (block_tables).  Returns (out, lse or None)."""
+    if num_splits is None:  # the library's choice for the keys a sequence may hold
+        n = max_seqlen_k or k.shape[1]
+        num_splits = attn_decode_num_splits(q.shape[0], _htot(q), min(n, window_size or n))
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty((q.shape[0], _htot(q), 1), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    need = attn_decode_workspace_bytes(q.shape[0], _htot(q), q.shape[-1], num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    args, _keep = _fp8_args(q, k, v, k_scale, v_scale, seqlens, block_tables, page_size, max_seqlen_k, num_splits,
+                            scale, workspace, out, lse, stream, window_size=window_size)
+    _check(_lib.attn_decode_splitkv_mxfp8(*args))
+    return out, lse
+
+
+def prepare_decode_mxfp8(q, k, v, k_scale, v_scale, num_splits, workspace, out, lse, seqlens=None,
+                         max_seqlen_k=None, block_tables=None, page_size=None, scale=None, stream=None,
+                         window_size=None) -> Prepared:
+    """attn_decode_splitkv_mxfp8 with every argument marshalled up front."""
+    args, ds = _fp8_args(q, k, v, k_scale, v_scale, seqlens, block_tables, page_size, max_seqlen_k, num_splits,
+                         scale, workspace, out, lse, stream, window_size=window_size)
+    return Prepared(_lib.attn_decode_splitkv_mxfp8, args,
+                    (ds, q, k, v, k_scale, v_scale, seqlens, block_tables, workspace, out, lse))

@@ -34,7 +34,8 @@ attn_status ok() {
 }
 
 size_t dtype_size(int dt) {
-    return dt == ATTN_DTYPE_F32 ? 4 : ((dt == ATTN_DTYPE_FP8_E4M3 || dt == ATTN_DTYPE_INT4X2) ? 1 : 2);
+    return dt == ATTN_DTYPE_F32 ? 4
+                                : ((dt == ATTN_DTYPE_FP8_E4M3 || dt == ATTN_DTYPE_INT4X2 || dt == ATTN_DTYPE_E8M0) ? 1 : 2);
 }
 
 constexpr unsigned DT_FLOAT = (1u << ATTN_DTYPE_F32) | (1u << ATTN_DTYPE_BF16);  // q/k/v/out of every path
@@ -51,7 +52,7 @@ struct View {
 // `dtypes`: bit set of the attn_dtype values accepted; `align`: byte alignment of row starts.
 attn_status make_view(const attn_tensor *t, const char *name, View *v, unsigned dtypes = DT_FLOAT, int align = 16) {
     if (!t) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: descriptor is NULL", name);
-    if (t->dtype < 0 || t->dtype > ATTN_DTYPE_INT4X2 || !((dtypes >> t->dtype) & 1u))
+    if (t->dtype < 0 || t->dtype > ATTN_DTYPE_E8M0 || !((dtypes >> t->dtype) & 1u))
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: dtype %d is not accepted here", name, t->dtype);
     if (t->ndim != 4 && t->ndim != 5)
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: ndim must be 4 [B,M,H,D] or 5 [B,M,G,H,D], got %d", name, t->ndim);
@@ -687,12 +688,12 @@ namespace {
 // Shared validation and launches of the split-KV decode entry points.  Without block tables
 // k/v are [B, cap, (G,) H, D] lanes; with them k/v are the paged cache [1, pages * page_size, ...].
 // `quant`: 0 = k/v share q's dtype; ATTN_DTYPE_FP8_E4M3 / ATTN_DTYPE_INT4X2 = k/v are codes of that
-// type with (scale, shift) metadata ksst / vsst.
+// type with (scale, shift) metadata ksst / vsst; `mx`: FP8 codes with E8M0 block scales instead.
 attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
                    const attn_tensor *ksst, const attn_tensor *vsst, const int32_t *seqlens,
                    const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
                    int32_t window_size, int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
-                   const attn_tensor *ot, float *lse, attn_stream_t stream) {
+                   const attn_tensor *ot, float *lse, attn_stream_t stream, bool mx = false) {
     View q, k, v, o, kss{}, vss{};
     attn_status st;
     const unsigned kv_dt = quant ? 1u << quant : DT_FLOAT;
@@ -700,8 +701,20 @@ attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_
     if ((st = make_view(kt, "k", &k, kv_dt)) != ATTN_OK) return st;
     if ((st = make_view(vt, "v", &v, kv_dt)) != ATTN_OK) return st;
     if ((st = make_view(ot, "out", &o)) != ATTN_OK) return st;
-    int group = 0;  // elements per (scale, shift) group
-    if (quant) {
+    int group = 0;  // elements per (scale, shift) group or E8M0 block
+    if (mx) {
+        if ((st = make_view(ksst, "k_scale", &kss, 1u << ATTN_DTYPE_E8M0, 1)) != ATTN_OK) return st;
+        if ((st = make_view(vsst, "v_scale", &vss, 1u << ATTN_DTYPE_E8M0, 1)) != ATTN_OK) return st;
+        if (q.dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q must be bf16", fn);
+        if (k.D % 32 || kss.D != k.D / 32 || vss.D != kss.D)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block scales need D a multiple of 32 and a last axis D/32",
+                        fn);
+        for (const View *m : {&kss, &vss})
+            if (!same_heads(*m, k) || m->B != k.B || m->M != k.M)
+                return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block scales must have k's shape with the last axis D/32",
+                            fn);
+        group = 32;
+    } else if (quant) {
         if ((st = make_view(ksst, "k_scale_shift", &kss, 1u << ATTN_DTYPE_F16, 4)) != ATTN_OK) return st;
         if ((st = make_view(vsst, "v_scale_shift", &vss, 1u << ATTN_DTYPE_F16, 4)) != ATTN_OK) return st;
         if (q.dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q must be bf16", fn);
@@ -809,7 +822,8 @@ attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_
     d.skss = kss.s;
     d.svss = vss.s;
     d.group = group;
-    const int elem = quant == ATTN_DTYPE_FP8_E4M3 ? attn::DECODE_FP8
+    const int elem = mx ? attn::DECODE_MXFP8
+                     : quant == ATTN_DTYPE_FP8_E4M3 ? attn::DECODE_FP8
                      : quant == ATTN_DTYPE_INT4X2 ? attn::DECODE_INT4
                      : (q.dtype == ATTN_DTYPE_F32 ? attn::DECODE_F32 : attn::DECODE_BF16);
     hipError_t e = attn::launch_decode_partials(d, elem, (hipStream_t)stream);
@@ -938,6 +952,20 @@ attn_status attn_decode_splitkv_int4(const attn_tensor *q, const attn_tensor *k,
     return decode(fn, ATTN_DTYPE_INT4X2, q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables,
                   max_blocks_per_seq, page_size, max_seqlen_k, window_size, num_splits, scale, workspace,
                   workspace_bytes, out, lse, stream);
+}
+
+attn_status attn_decode_splitkv_mxfp8(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                      const attn_tensor *k_scale, const attn_tensor *v_scale,
+                                      const int32_t *seqlens, const int32_t *block_tables,
+                                      int32_t max_blocks_per_seq, int32_t page_size, int32_t max_seqlen_k,
+                                      int32_t window_size,
+                                      int32_t num_splits, float scale, void *workspace, size_t workspace_bytes,
+                                      const attn_tensor *out, float *lse, attn_stream_t stream) {
+    const char *fn = "attn_decode_splitkv_mxfp8";
+    if (block_tables && !seqlens) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: block_tables need seqlens", fn);
+    return decode(fn, ATTN_DTYPE_FP8_E4M3, q, k, v, k_scale, v_scale, seqlens, block_tables, max_blocks_per_seq,
+                  page_size, max_seqlen_k, window_size, num_splits, scale, workspace, workspace_bytes, out, lse, stream,
+                  true);
 }
 
 }  // extern "C"

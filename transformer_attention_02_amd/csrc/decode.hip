@@ -21,7 +21,8 @@
 //     PagedBlockDiagonalPaddedKeysMask): per-sequence key counts on the device,
 //     and for a paged cache the physical row of every key of a sub-chunk is
 //     resolved once into LDS from the block table;
-//   * quantised caches: row-wise FP8 ("Attention - operator protocol", InputsFp8) and
+//   * quantised caches: row/group-wise FP8 ("Attention - operator protocol", InputsFp8),
+//     MXFP8 (InputsMXFp8: one E8M0 scale 2^(e - 127) per block of 32, no shift) and
 //     row/group-wise INT4 (triton_splitk.FwOp).  A lane takes 16 E4M3 codes (hardware
 //     conversion) or 32 4-bit codes per 16-byte load, all inside one (scale, shift) group;
 //     the group's pair is applied to the lane's partial dot product before the reduction
@@ -139,7 +140,7 @@ __device__ __forceinline__ unsigned int4_pair(unsigned w, int s, unsigned m, uns
 
 template <int ELEM>
 __device__ __forceinline__ void unpack_elem(const u32x4 &w, float *x) {
-    if constexpr (ELEM == DECODE_FP8)
+    if constexpr (ELEM == DECODE_FP8 || ELEM == DECODE_MXFP8)
         unpack_fp8(w, x);
     else if constexpr (ELEM == DECODE_INT4)
         unpack_int4(w, x);
@@ -150,6 +151,11 @@ __device__ __forceinline__ void unpack_elem(const u32x4 &w, float *x) {
 // (scale, shift) halves of a metadata word
 __device__ __forceinline__ float ss_scale(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float ss_shift(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+// An E8M0 block scale 2^(e - 127) as fp32: the exponent field itself, 2^-127 (a subnormal) for
+// e = 0, NaN for e = 255.
+__device__ __forceinline__ float e8m0_scale(uint32_t e) {
+    return __uint_as_float(e == 0 ? 0x00400000u : (e == 255 ? 0x7fc00000u : e << 23));
+}
 
 // Workgroups are dealt to the 8 XCDs round-robin (workgroup i to XCD i % 8).  Renumbered so
 // that every XCD takes one contiguous range of the logical order: the workgroups of one cache
@@ -165,8 +171,9 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
 // row block_tables[b][j / page_size] * page_size + j % page_size (page numbers clamped to the cache).
 template <int HD, int ELEM, int MODE>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
-    constexpr bool F32 = ELEM == DECODE_F32, INT4 = ELEM == DECODE_INT4;
-    constexpr bool QUANT = ELEM == DECODE_FP8 || INT4;             // codes + (scale, shift) metadata
+    constexpr bool F32 = ELEM == DECODE_F32, INT4 = ELEM == DECODE_INT4, MX = ELEM == DECODE_MXFP8;
+    constexpr bool QUANT = ELEM == DECODE_FP8 || INT4 || MX;       // codes + (scale, shift) or E8M0 metadata
+    constexpr int MES = MX ? 1 : 2;                                // bytes per metadata stride unit
     constexpr int EPL = F32 ? 4 : (INT4 ? 32 : (QUANT ? 16 : 8));  // elements per 16-byte load
     constexpr int LPK = HD / EPL;                                  // lanes per key row (a lane group)
     constexpr int KPP = NT / LPK;                                  // lane groups of the workgroup
@@ -200,14 +207,18 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const QT *qp = (const QT *)a.q + (int64_t)b * a.sq.b + head_offset(a.sq, hf, a.Hin) + cl * EPL;
     const T *kp = (const T *)a.k + kb + head_offset(a.sk, hf, a.Hin) + cl * TPL;
     const T *vp = (const T *)a.v + vb + head_offset(a.sv, hf, a.Hin) + cl * TPL;
-    // quantised caches: the metadata word of this lane's group in every row, addressed in fp16
-    // units like a [.., G, 2] tensor (a lane's EPL elements never straddle two groups)
-    const uint16_t *kss = nullptr, *vss = nullptr;
+    // quantised caches: the metadata of this lane's group in every row, a (scale, shift) word
+    // addressed in fp16 units like a [.., G, 2] tensor, or an E8M0 byte of a [.., D/32] tensor
+    // (a lane's EPL elements never straddle two groups)
+    const char *kss = nullptr, *vss = nullptr;
+    const int gw = QUANT ? (MX ? 1 : 2) * ((cl * EPL) / a.group) : 0;
     if constexpr (QUANT) {
-        const int gw = 2 * ((cl * EPL) / a.group);
-        kss = (const uint16_t *)a.kss + (MODE == 2 ? 0 : (int64_t)b * a.skss.b) + head_offset(a.skss, hf, a.Hin) + gw;
-        vss = (const uint16_t *)a.vss + (MODE == 2 ? 0 : (int64_t)b * a.svss.b) + head_offset(a.svss, hf, a.Hin) + gw;
+        kss = (const char *)a.kss + ((MODE == 2 ? 0 : (int64_t)b * a.skss.b) + head_offset(a.skss, hf, a.Hin) + gw) * MES;
+        vss = (const char *)a.vss + ((MODE == 2 ? 0 : (int64_t)b * a.svss.b) + head_offset(a.svss, hf, a.Hin) + gw) * MES;
     }
+    auto meta = [](const char *p) __attribute__((always_inline)) {
+        return MX ? (uint32_t)*(const uint8_t *)p : *(const uint32_t *)p;
+    };
 
     float qv[EPL];
     if constexpr (F32) {
@@ -268,14 +279,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     int64_t ksstr = 0, vsstr = 0;
     uint32_t kslane = 0, vslane = 0;
     if constexpr (QUANT) {
-        const int gw = 2 * ((cl * EPL) / a.group);
         const int64_t bk = MODE == 2 ? 0 : (int64_t)b * a.skss.b, bv = MODE == 2 ? 0 : (int64_t)b * a.svss.b;
-        ksbase = (const char *)a.kss + (bk + head_offset(a.skss, hf0, a.Hin)) * 2;
-        vsbase = (const char *)a.vss + (bv + head_offset(a.svss, hf0, a.Hin)) * 2;
-        ksstr = a.skss.m * 2;
-        vsstr = a.svss.m * 2;
-        kslane = (uint32_t)((head_offset(a.skss, hf, a.Hin) - head_offset(a.skss, hf0, a.Hin) + gw) * 2 + rs * ksstr);
-        vslane = (uint32_t)((head_offset(a.svss, hf, a.Hin) - head_offset(a.svss, hf0, a.Hin) + gw) * 2 + rs * vsstr);
+        ksbase = (const char *)a.kss + (bk + head_offset(a.skss, hf0, a.Hin)) * MES;
+        vsbase = (const char *)a.vss + (bv + head_offset(a.svss, hf0, a.Hin)) * MES;
+        ksstr = a.skss.m * MES;
+        vsstr = a.svss.m * MES;
+        kslane = (uint32_t)((head_offset(a.skss, hf, a.Hin) - head_offset(a.skss, hf0, a.Hin) + gw) * MES + rs * ksstr);
+        vslane = (uint32_t)((head_offset(a.svss, hf, a.Hin) - head_offset(a.svss, hf0, a.Hin) + gw) * MES + rs * vsstr);
     }
 
     // byte distance between row slot 0 of consecutive rows of a lane (RPP rows apart)
@@ -310,8 +320,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
                     for (int u = 0; u < U; ++u) {
                         wk[u] = *(const u32x4 *)(kr + u * kstep + klane);
                         wv[u] = *(const u32x4 *)(vr + u * vstep + vlane);
-                        sk[u] = *(const uint32_t *)(ksr + u * ksstep + kslane);
-                        sv[u] = *(const uint32_t *)(vsr + u * vsstep + vslane);
+                        sk[u] = meta(ksr + u * ksstep + kslane);
+                        sv[u] = meta(vsr + u * vsstep + vslane);
                     }
                     return;
                 }
@@ -325,16 +335,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
                     wk[u] = *(const u32x4 *)(kbase + ru * kstr + klane);
                     wv[u] = *(const u32x4 *)(vbase + ru * vstr + vlane);
                     if constexpr (QUANT) {
-                        sk[u] = *(const uint32_t *)(ksbase + ru * ksstr + kslane);
-                        sv[u] = *(const uint32_t *)(vsbase + ru * vsstr + vslane);
+                        sk[u] = meta(ksbase + ru * ksstr + kslane);
+                        sv[u] = meta(vsbase + ru * vsstr + vslane);
                     }
                 } else {
                     const int64_t row = MODE == 2 ? (ok ? rows_s[r] : 0) : sub0 + r;
                     wk[u] = ok ? *(const u32x4 *)(kp + row * a.sk.m) : u32x4{0, 0, 0, 0};
                     wv[u] = ok ? *(const u32x4 *)(vp + row * a.sv.m) : u32x4{0, 0, 0, 0};
                     if constexpr (QUANT) {
-                        sk[u] = ok ? *(const uint32_t *)(kss + row * a.skss.m) : 0u;
-                        sv[u] = ok ? *(const uint32_t *)(vss + row * a.svss.m) : 0u;
+                        sk[u] = ok ? meta(kss + row * a.skss.m * MES) : 0u;
+                        sv[u] = ok ? meta(vss + row * a.svss.m * MES) : 0u;
                     }
                 }
             }
@@ -370,7 +380,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
                     unpack_elem<ELEM>(wk[u], x);
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) dot = fmaf(qv[e], x[e], dot);
-                    if constexpr (QUANT) dot = fmaf(ss_scale(sk[u]), dot, ss_shift(sk[u]) * qsum);
+                    if constexpr (MX)
+                        dot *= e8m0_scale(sk[u]);
+                    else if constexpr (QUANT)
+                        dot = fmaf(ss_scale(sk[u]), dot, ss_shift(sk[u]) * qsum);
                 }
                 dot = lane_group_sum<LPK>(dot);
                 sc[u] = p + u * RPP + rs < n ? dot : -INFINITY;
@@ -388,7 +401,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
             for (int u = 0; u < U; ++u) {
                 float pr = __builtin_amdgcn_exp2f(sc[u] - mu);
                 l_run += pr;
-                if constexpr (QUANT) {
+                if constexpr (MX) {
+                    pr *= e8m0_scale(sv[u]);
+                } else if constexpr (QUANT) {
                     sh_acc = fmaf(pr, ss_shift(sv[u]), sh_acc);
                     pr *= ss_scale(sv[u]);
                 }
@@ -440,7 +455,8 @@ template <int HD, int ELEM, int MODE>
 hipError_t launch(const DecodeArgs &args, hipStream_t stream) {
     // heads per workgroup: enough neighbouring head segments for DECODE_ROW_BYTES contiguous bytes
     // per cache row, a power of two that divides Htot and leaves every head at least one lane group
-    constexpr int RB = ELEM == DECODE_F32 ? 4 * HD : (ELEM == DECODE_FP8 ? HD : (ELEM == DECODE_INT4 ? HD / 2 : 2 * HD));
+    constexpr bool FP8 = ELEM == DECODE_FP8 || ELEM == DECODE_MXFP8;
+    constexpr int RB = ELEM == DECODE_F32 ? 4 * HD : (FP8 ? HD : (ELEM == DECODE_INT4 ? HD / 2 : 2 * HD));
     constexpr int KPP = NT / (RB / 16);  // lane groups: one 16-byte load per lane per row
     DecodeArgs a = args;
     a.log2_hpw = 0;
@@ -449,7 +465,7 @@ hipError_t launch(const DecodeArgs &args, hipStream_t stream) {
         ++a.log2_hpw;
     // lane32: within every workgroup (hpw heads from a multiple of hpw, RPP row slots, LPK
     // 16-byte column slices) the offsets from the first head's row are >= 0 and < 2^32 bytes
-    constexpr int EPL = ELEM == DECODE_F32 ? 4 : (ELEM == DECODE_INT4 ? 32 : (ELEM == DECODE_FP8 ? 16 : 8));
+    constexpr int EPL = ELEM == DECODE_F32 ? 4 : (ELEM == DECODE_INT4 ? 32 : (FP8 ? 16 : 8));
     constexpr int LPK = HD / EPL;
     const int64_t RPP = (NT / LPK) >> a.log2_hpw, hpw = 1 << a.log2_hpw;
     auto fits = [&](const Strides &st, int64_t es, int64_t col) {
@@ -467,6 +483,8 @@ hipError_t launch(const DecodeArgs &args, hipStream_t stream) {
     if (ELEM == DECODE_FP8 || ELEM == DECODE_INT4)
         a.lane32 = a.lane32 && fits(a.skss, 2, 2 * ((LPK - 1) * EPL / a.group)) &&
                    fits(a.svss, 2, 2 * ((LPK - 1) * EPL / a.group));
+    if (ELEM == DECODE_MXFP8)  // one E8M0 byte per block
+        a.lane32 = a.lane32 && fits(a.skss, 1, (LPK - 1) * EPL / a.group) && fits(a.svss, 1, (LPK - 1) * EPL / a.group);
     const int64_t grid = (int64_t)a.S * a.B * (a.Htot >> a.log2_hpw);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -488,6 +506,7 @@ hipError_t launch_elem(const DecodeArgs &a, int elem, hipStream_t stream) {
     case DECODE_F32: return launch_mode<HD, DECODE_F32>(a, stream);
     case DECODE_FP8: return launch_mode<HD, DECODE_FP8>(a, stream);
     case DECODE_INT4: return launch_mode<HD, DECODE_INT4>(a, stream);
+    case DECODE_MXFP8: return launch_mode<HD, DECODE_MXFP8>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -71,7 +71,8 @@ struct DecodeArgs {
     int bt_stride, page_size, num_pages, cap;
     int window;  // > 0: the query sees only its sequence's last `window` keys; chunks cover those
     // FP8 / INT4 caches only: (scale, shift) fp16 pairs per cache row, head and group of
-    // `group` consecutive elements (a multiple of 32 dividing D); strides in fp16 units
+    // `group` consecutive elements (a multiple of 16 or 32 dividing D); strides in fp16 units.
+    // MXFP8: one E8M0 byte per row, head and block of 32; strides in bytes
     const void *kss, *vss;
     Strides skss, svss;
     int group;
@@ -81,7 +82,8 @@ struct DecodeArgs {
 
 // Element type of a decode K/V cache (q is bf16 for the quantised caches, else the cache's type).
 // INT4: two unsigned 4-bit codes per byte, element 2i in the low nibble of byte i.
-enum DecodeElem : int { DECODE_BF16 = 0, DECODE_F32 = 1, DECODE_FP8 = 2, DECODE_INT4 = 3 };
+// MXFP8: E4M3 codes with one E8M0 scale byte per block of 32 elements (group = 32, no shift).
+enum DecodeElem : int { DECODE_BF16 = 0, DECODE_F32 = 1, DECODE_FP8 = 2, DECODE_INT4 = 3, DECODE_MXFP8 = 4 };
 
 constexpr int kMaxChunks = 128;
 
