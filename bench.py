@@ -129,8 +129,8 @@ TRAFFIC_KERNELS = (
     ("decode bf16 paged 16x32768x32x128 page64 s64", "decode", "decode_kernel<128, 0, 2>", None),
     ("decode fp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 2, 0>", None),
     ("decode mxfp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 4, 0>", None),
-    ("decode int4 g1 16x32768x32x128 s64", "decode", "decode_kernel<128, 3, 0>", 0),
-    ("decode int4 g4 16x32768x32x128 s64", "decode", "decode_kernel<128, 3, 0>", 1),
+    ("decode int4 g1 16x32768x32x128 s32", "decode", "decode_kernel<128, 3, 0>", 0),
+    ("decode int4 g4 16x32768x32x128 s32", "decode", "decode_kernel<128, 3, 0>", 1),
 )
 COPY_KERNEL, COPY_KIB = "__amd_rocclr_copyBuffer", 1 << 20  # the 1 GiB copy row reads and writes 1 GiB
 
@@ -368,7 +368,7 @@ def main():
             "ms_per_call": round(ms_2, 5), "value": round(tf_2, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf_2, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf_2 / PEAK_BF16_TFLOPS, 4), "flops_per_call": flops,
-                         "kernel": "fwd_bf16_kernel<256, 256, 4, 2, false, false>"}, **tm}
+                         "kernel": "fwd_bf16_vsplit_kernel<256, 256, false, false>"}, **tm}
         if not args.no_cpu:  # batch element 0, heads 0..3 of 16
             sample = [synth.to_f64(x[:1, :, :4], "bf16") for x in (q2h, k2h, v2h)]
             result["rows"]["prefill_causal_hd256"]["cpu_oracle"] = oracle_timing(
@@ -577,19 +577,23 @@ def main():
             vs4 = torch.from_numpy(synth.int4_scale_shift(4, synth.TAG_V, (B, Mkv, H, G)).reshape(B, Mkv, H, 2 * G))
             ks4, vs4 = ks4.to("cuda"), vs4.to("cuda")
             tm = {}
-            ms_4 = timed(A.prepare_decode_int4(qd, k4, v4, ks4, vs4, S, ws, od, ld), 40, 3, torch, detail=tm)
+            # 32 chunks of 1024 keys: INT4 rows carry 4x the codes per byte of bf16, and a sweep over
+            # 4 .. 128 chunks ran G=1 fastest at 16-32 (386 us against 404 us at 64)
+            S4 = 32
+            ws4 = torch.empty(A.attn_decode_workspace_bytes(B, H, D, S4), dtype=torch.uint8, device="cuda")
+            ms_4 = timed(A.prepare_decode_int4(qd, k4, v4, ks4, vs4, S4, ws4, od, ld), 40, 3, torch, detail=tm)
             i4_bytes = 2.0 * B * Mkv * H * (D // 2 + 4 * G)
             gbs_4 = i4_bytes / (ms_4 * 1e-3) / 1e9
-            log(f"int4 decode G={G} S=64: {ms_4 * 1e3:.1f} us/call, {gbs_4:.0f} GB/s")
+            log(f"int4 decode G={G} S={S4}: {ms_4 * 1e3:.1f} us/call, {gbs_4:.0f} GB/s")
             result["rows"][f"decode_int4_g{G}"] = {
                 "workload": f"B=16 Mq=1 Mkv=32768 H=32 D=128, bf16 q, INT4 K/V (two codes per byte) with "
                             f"{'one fp16 (scale, shift) pair per row' if G == 1 else f'{G} groups of {D // G} per row'}"
-                            ", 64 chunks of 512",
+                            ", 32 chunks of 1024",
                 "ms_per_call": round(ms_4, 5), "value": round(gbs_4, 1), "unit": "GB/s",
                 "keys_per_s": round(B * Mkv * H / (ms_4 * 1e-3), 1),
                 "roofline": {"bound": "hbm", "achieved": round(gbs_4, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(gbs_4 / PEAK_HBM_GBS, 4), "bytes_per_call": i4_bytes,
-                             "traffic": recorded_traffic(f"decode int4 g{G} 16x32768x32x128 s64"),
+                             "traffic": recorded_traffic(f"decode int4 g{G} 16x32768x32x128 s32"),
                              "note": "algorithmic bytes = K+V codes and their metadata once"}, **tm}
             if not args.no_cpu:  # batch element 0: dequantise its codes, then the oracle
                 c4 = [synth.int4_codes(4, t, (1, Mkv, H, D // 2)) for t in (synth.TAG_K, synth.TAG_V)]
@@ -601,7 +605,7 @@ def main():
                     f"batch element 0 of 16 (32768 keys x 32 heads): INT4 (G={G}) dequantisation and fp64 exact "
                     "attention; GB/s of its codes and metadata")
                 del c4, s4
-            del k4, v4, ks4, vs4
+            del k4, v4, ks4, vs4, ws4
             torch.cuda.empty_cache()
         del qd, ws, od, ld
 

@@ -65,7 +65,7 @@ def test_write_traffic_from_counter_databases(tmp_path):
     bench.write_traffic(str(fdb), str(wdb), out_path=str(out))
     rec = json.loads(out.read_text())
     assert set(rec) == {k for k, *_ in bench.TRAFFIC_KERNELS}
-    g1, g4 = rec["decode int4 g1 16x32768x32x128 s64"], rec["decode int4 g4 16x32768x32x128 s64"]
+    g1, g4 = rec["decode int4 g1 16x32768x32x128 s32"], rec["decode int4 g4 16x32768x32x128 s32"]
     assert g1["fetch_kib"] == pytest.approx(3000.5) and g4["fetch_kib"] == pytest.approx(3499.5)
     assert g1["fetch_scale"] == pytest.approx(2.0) and g1["write_scale"] == pytest.approx(1.0)
     fwd = rec["fwd_bf16 causal 2x2048x32x128"]

@@ -82,10 +82,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 // pages per sequence.
 constexpr int kMaxPages = 8192;
 
-template <int KD, int VD, int NW, int STAGES, bool OUT_F32, int KSPLIT, bool PAGED>
+// VSPLIT waves share each 32-row block by value columns: with VSPLIT = 2 wave w + NW/2 computes
+// the same scores and softmax as wave w and keeps the second half of O^T.
+template <int KD, int VD, int NW, int STAGES, bool OUT_F32, int KSPLIT, bool PAGED, int VSPLIT = 1>
 __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     constexpr int NT = NW * 64;                  // threads per workgroup
-    constexpr int BM = NW / KSPLIT * 32;         // query rows per workgroup
+    constexpr int BM = NW / KSPLIT / VSPLIT * 32;  // query rows per workgroup
+    static_assert(VSPLIT == 1 || KSPLIT == 1, "keys or value columns are split, not both");
     static_assert(STAGES >= 2 && STAGES <= 4, "the unrolled tile loop names two to four LDS stages");
     // STAGES == 4: the ring is filled two tiles at a time, with one wait + barrier per two tiles
     constexpr bool PAIRS = STAGES == 4;
@@ -97,7 +100,8 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     constexpr int KROUNDS = KTILE / 16 / NT;         // 16-byte loads per thread per K tile
     constexpr int VROUNDS = VTILE / 16 / NT;         // and per V tile
     constexpr int KS = KD / 16;                      // k-steps of S^T
-    constexpr int MB = VD / 32;                      // 32-row blocks of O^T
+    constexpr int MB = VD / 32 / VSPLIT;             // 32-row blocks of this wave's O^T
+    constexpr int VW = VD / VSPLIT;                  // value columns of this wave
     static_assert(KROUNDS >= 1 && KROUNDS * NT * 16 == KTILE && VROUNDS >= 1 && VROUNDS * NT * 16 == VTILE,
                   "tile split");
 
@@ -223,7 +227,8 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
 
     // ---- Q^T fragments (B operand), resident for the whole kernel
     const int wsub = wave % KSPLIT;                // which tile of each pair this wave takes (KSPLIT = 2)
-    const int wrow0 = row0 + wave / KSPLIT * 32;  // first local row of this wave
+    const int vpart = wave / (NW / VSPLIT);        // which value columns this wave keeps (VSPLIT = 2)
+    const int wrow0 = row0 + (wave % (NW / VSPLIT)) / KSPLIT * 32;  // first local row of this wave
     const int qrow = wrow0 + l32;        // this lane's query row (local to the sequence)
     const int klo = clampk((int64_t)qrow + shift - a.wl, 0, Lk);       // this row's visible keys
     const int khi = clampk((int64_t)qrow + shift + a.wr, -1, Lk - 1);  // (empty when khi < klo)
@@ -261,7 +266,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int row = vrow + 8 * e, col = mb * 32 + vcol;
+            const int row = vrow + 8 * e, col = vpart * VW + mb * 32 + vcol;
             vaddr[mb][e] = V_BASE + row * VROWB + ((((col >> 3) ^ swz<VD>(row))) << 4) + ((col & 4) << 1);
         }
 
@@ -484,10 +489,11 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
         // bf16 rows go out whole, staged in the now idle ring (16-byte stores, whole rows, instead
         // of 8 bytes per lane at 32 rows 8 KB apart)
         __syncthreads();  // every wave has finished reading the K/V ring
-        store_rows_bf16<VD>(o, inv, (unsigned char LDS_AS *)smem + wave * 32 * VROWB, obase_p,
-                            (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) + (int64_t)(qs + wrow0) * a.so.m,
+        store_rows_bf16<VW>(o, inv, (unsigned char LDS_AS *)smem + wave * 32 * VW * 2, obase_p,
+                            (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) + (int64_t)(qs + wrow0) * a.so.m +
+                                vpart * VW,
                             a.so.m, Lq - wrow0);
-        if (qrow < Lq && lse_p && hh == 0)
+        if (qrow < Lq && lse_p && hh == 0 && vpart == 0)
             lse_p[((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow] =
                 l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     } else if (qrow < Lq) {
@@ -497,7 +503,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
         for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int d0 = mb * 32 + 8 * g + 4 * hh;
+                const int d0 = vpart * VW + mb * 32 + 8 * g + 4 * hh;
                 const float x0 = o[mb][4 * g] * inv, x1 = o[mb][4 * g + 1] * inv;
                 const float x2 = o[mb][4 * g + 2] * inv, x3 = o[mb][4 * g + 3] * inv;
                 if (OUT_F32) {
@@ -507,7 +513,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
                 }
             }
         }
-        if (lse_p && hh == 0) {
+        if (lse_p && hh == 0 && vpart == 0) {
             lse_p[((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow] =
                 l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
         }
@@ -523,6 +529,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 template <int KD, int VD, bool OUT_F32, bool PAGED>
 __global__ __launch_bounds__(128) void fwd_bf16_split_kernel(FwdArgs a) {
     fwd_bf16_body<KD, VD, 2, 4, OUT_F32, 2, PAGED>(a);
+}
+
+// 8 waves, two per 32-row block, each keeping half of the value columns (head dim 256)
+template <int KD, int VD, bool OUT_F32, bool PAGED>
+__global__ __launch_bounds__(512) void fwd_bf16_vsplit_kernel(FwdArgs a) {
+    fwd_bf16_body<KD, VD, 8, 2, OUT_F32, 1, PAGED, 2>(a);
+}
+
+template <int KD, int VD, bool OUT_F32, bool PAGED>
+hipError_t launch_vsplit(const FwdArgs &a, hipStream_t stream) {
+    const int64_t grid = (a.max_seqlen_q + 127) / 128 * a.nseq * (int64_t)a.B * a.Htot * a.splits;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_bf16_vsplit_kernel<KD, VD, OUT_F32, PAGED>), dim3((unsigned)grid), dim3(512), 0, stream, a);
+    return hipGetLastError();
 }
 
 template <int KD, int VD, int NW, int STAGES, bool OUT_F32, bool PAGED, int KSPLIT = 1>
@@ -558,9 +579,10 @@ hipError_t launch_nw(const FwdArgs &a, hipStream_t stream) {
     const int64_t units = (int64_t)a.nseq * a.B * a.Htot * a.splits;
     auto grid = [&](int bm) { return (a.max_seqlen_q + bm - 1) / bm * units; };
     if constexpr (VD == 256) {
-        // 512-byte K and V rows, a 256-column O^T (128 accumulator registers besides Q^T's 64):
-        // one wave per SIMD and a double-buffered ring (128 KB)
-        if (grid(128) >= FWD_MIN_GRID) return launch<KD, VD, 4, 2, OUT_F32, PAGED>(a, stream);
+        // 512-byte V rows and a 256-column O^T: a double-buffered ring (128 KB); 8 waves, two per
+        // 32-row block splitting the value columns (both compute the scores), so that two waves
+        // share each SIMD; on small grids 2 waves holding all 256 columns (one wave per SIMD)
+        if (grid(128) >= FWD_MIN_GRID) return launch_vsplit<KD, VD, OUT_F32, PAGED>(a, stream);
         return launch<KD, VD, 2, 2, OUT_F32, PAGED>(a, stream);
     } else if constexpr (KD == 256) {
         // 512-byte K rows: a 3-slot ring (144 KB with 256-byte V rows) fits the LDS, a 4-slot one
