@@ -224,7 +224,8 @@ size_t attn_fwd_kvcache_workspace_bytes(int64_t Mq, int64_t H_total, int64_t Kv,
  *     num_splits) rounded up to 64 keys; with num_splits >= 2 the chunks' fp32 partial results go to
  *     `workspace` (device, 256-byte aligned, >= attn_fwd_kvcache_workspace_bytes) and a merge
  *     launch combines them (for few query blocks over long caches).
- *   out [1, Mq, (G,) H, Kv] bf16; lse fp32 [1, H_total, Mq] or NULL.  K, Kv in {64, 128}.
+ *   out [1, Mq, (G,) H, Kv] bf16; lse fp32 [1, H_total, Mq] or NULL.  K, Kv in {64, 128, 256}
+ *     (a paged cache: K == Kv).
  *   Device metadata is not read by the host; bad values give unspecified results, never an
  *   out-of-bounds access.  Errors as attn_fwd. */
 attn_status attn_fwd_kvcache(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, const attn_mask *mask,

@@ -194,7 +194,7 @@ def test_forward_workgroup_sizes(A, H, D):
 @pytest.mark.parametrize("K,Kv", [(64, 128), (128, 64), (256, 256), (256, 128), (256, 64), (128, 256), (64, 256)])
 def test_bf16_distinct_head_dims(A, K, Kv):
     """q/k head dim K and v/out head dim Kv (each 64, 128 or 256; ck_splitk.FwOp takes head dims up
-    to 256, and Kv = 256 runs as two launches over the value columns): ragged shapes with no mask,
+    to 256): ragged shapes with no mask,
     causal and a causal window on small grids (the split-key kernel) and on 64 heads (8-wave
     workgroups, sampled heads), and packed block-diagonal causal sequences; bf16 out and the
     fp32 partial output."""
@@ -1592,6 +1592,17 @@ def test_kvcache_head_dim_64_and_grouped_heads(A):
                                   mask=oracle.MASK_CAUSAL_BR)
         check(out[:, ss[s]:ss[s + 1]].reshape(1, lq[s], G * H, D), lse[:, :, ss[s]:ss[s + 1]], oo, ol, TOL_BF16_OUT,
               TOL_LSE, f"grouped seq {s}")
+
+
+@pytest.mark.parametrize("H,page,splits,gappy", [(4, None, 1, False), (32, None, 1, False), (4, 64, 1, False),
+                                                  (16, 128, 2, False), (16, None, 2, True)])
+def test_kvcache_head_dim_256(A, H, page, splits, gappy):
+    """Head dim 256 against padded lanes, pages and gappy lanes, causal with offset: 4 heads run
+    two-wave workgroups, 16 heads in two key chunks and 32 heads the value-split workgroups."""
+    say(f"case: kv cache head dim 256 H={H} page={page} splits={splits} gappy={gappy}")
+    lq, lk = [300, 1, 129, 64], [1000, 700, 129, 1999]
+    kw = {"starts": [0, 1100, 50, 0]} if gappy else {}
+    _kvcache_case(A, lq, lk, 2048, H, 256, 4, 90 + H, page=page, splits=splits, **kw)
 
 
 def test_kvcache_chunked_prefill_full_size(A):

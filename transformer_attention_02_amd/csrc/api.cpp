@@ -420,6 +420,8 @@ attn_status attn_fwd_kvcache(const attn_tensor *qt, const attn_tensor *kt, const
         if (k.M % page_size || k.M == 0)
             return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: the cache must hold a whole number of pages", fn);
         if (k.D != v.D) return fail(ATTN_ERR_UNSUPPORTED, "%s: a paged cache needs equal head dims", fn);
+        if (k.D != 64 && k.D != 128 && k.D != 256)
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: paged head dims must be 64, 128 or 256", fn);
         cap = (int64_t)max_blocks_per_seq * page_size;
         if (cap > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "%s: sequences too long", fn);
     } else if (seqstart_k) {
@@ -436,8 +438,9 @@ attn_status attn_fwd_kvcache(const attn_tensor *qt, const attn_tensor *kt, const
     if (!(std::isnan(scale) || std::isfinite(scale)))
         return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: scale must be finite (or NaN for 1/sqrt(K))", fn);
     if (lse && ((uintptr_t)lse) % 4) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
-    if (!((q.D == 64 || q.D == 128) && (v.D == 64 || v.D == 128)))
-        return fail(ATTN_ERR_UNSUPPORTED, "%s: head dims K and Kv must be in {64, 128}", fn);
+    auto dim_ok = [](int64_t d) { return d == 64 || d == 128 || d == 256; };
+    if (!(dim_ok(q.D) && dim_ok(v.D)))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: head dims K and Kv must be in {64, 128, 256}", fn);
     if ((k.M > 1 && (k.s.m < k.D || v.s.m < v.D)) || (k.s.m * 2 * 64 + k.D * 2) >= (int64_t)1 << 31 ||
         (v.s.m * 2 * 64 + v.D * 2) >= (int64_t)1 << 31)
         return fail(ATTN_ERR_UNSUPPORTED, "%s: key/value row strides must be >= the head dim and < 2^24 bytes", fn);

@@ -605,9 +605,10 @@ hipError_t launch_out(const FwdArgs &a, bool out_f32, hipStream_t stream) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool out_f32, hipStream_t stream) {
-    if (a.block_tables) {  // paged KV caches: equal head dims only
+    if (a.block_tables) {  // paged KV caches: equal head dims only (the page table takes 32 KB of LDS)
         if (a.K == 128 && a.Kv == 128) return launch_out<128, 128, true>(a, out_f32, stream);
         if (a.K == 64 && a.Kv == 64) return launch_out<64, 64, true>(a, out_f32, stream);
+        if (a.K == 256 && a.Kv == 256) return launch_out<256, 256, true>(a, out_f32, stream);
         return hipErrorInvalidValue;
     }
     if (a.Kv == 256) {
