@@ -51,7 +51,7 @@ def parse():
                    "counters per kernel and grid) instead of running; no GPU needed")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE rocprofv3 run of "
-                        "'bench.py --rows decode,kvcache,copy,varlen,window --no-cpu --steps 3 --warmup 1'; no GPU needed")
+                        "'bench.py --rows decode,kvcache,copy,varlen,window,hd256 --no-cpu --steps 3 --warmup 1'; no GPU needed")
     return p.parse_args()
 
 
@@ -119,12 +119,13 @@ def recorded_traffic(key, path=None):
 # None for every grid)
 TRAFFIC_GRID = {"fwd_bf16 causal 2x2048x32x128": 512 * 512, "fwd_bf16 varlen gqa causal 8 seqs": 3584 * 512,
                 "fwd_bf16 sliding window 1024 2x8192x32x128": 2048 * 512,
-                "fwd_bf16 kvcache paged 16x256x32768 s4": 2048 * 512}
+                "fwd_bf16 kvcache paged 16x256x32768 s4": 2048 * 512, "fwd_bf16 causal hd256 2x2048x16x256": 512 * 512}
 TRAFFIC_KERNELS = (
     ("fwd_bf16 causal 2x2048x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
     ("fwd_bf16 varlen gqa causal 8 seqs", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
     ("fwd_bf16 sliding window 1024 2x8192x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
     ("fwd_bf16 kvcache paged 16x256x32768 s4", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, true, true>", None),
+    ("fwd_bf16 causal hd256 2x2048x16x256", "fwd", "fwd_bf16_vsplit_kernel<256, 256, false, false>", None),
     ("decode bf16 16x32768x32x128 s64", "decode", "decode_kernel<128, 0, 0>", None),
     ("decode bf16 paged 16x32768x32x128 page64 s64", "decode", "decode_kernel<128, 0, 2>", None),
     ("decode fp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 2, 0>", None),
@@ -175,7 +176,7 @@ def write_traffic(fetch_db, write_db, out_path=None):
     copy_f, copy_w = copy_mean(find(fetch, COPY_KERNEL)), copy_mean(find(write, COPY_KERNEL))
     cal = (f"{COPY_KERNEL} of 1 GiB (bench.py --rows copy): FETCH_SIZE {copy_f:.1f} KiB, "
            f"WRITE_SIZE {copy_w:.1f} KiB per dispatch")
-    cmd = "python bench.py --rows decode,kvcache,copy,varlen,window --no-cpu --steps 3 --warmup 1"
+    cmd = "python bench.py --rows decode,kvcache,copy,varlen,window,hd256 --no-cpu --steps 3 --warmup 1"
     out = {}
     for key, src, kname, which in TRAFFIC_KERNELS:
         grid = TRAFFIC_GRID.get(key)
@@ -368,6 +369,7 @@ def main():
             "ms_per_call": round(ms_2, 5), "value": round(tf_2, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf_2, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf_2 / PEAK_BF16_TFLOPS, 4), "flops_per_call": flops,
+                         "traffic": recorded_traffic("fwd_bf16 causal hd256 2x2048x16x256"),
                          "kernel": "fwd_bf16_vsplit_kernel<256, 256, false, false>"}, **tm}
         if not args.no_cpu:  # batch element 0, heads 0..3 of 16
             sample = [synth.to_f64(x[:1, :, :4], "bf16") for x in (q2h, k2h, v2h)]
