@@ -85,7 +85,8 @@ def rocpd_summary(db_path):
                 print(f"| {cn} | {len(v)} | {sum(v) / len(v):.1f} | {grid} | {name} |")
 
 
-TRAFFIC_SOURCES = {"fwd": ("fwd_bf16.hip", "kernels.h", "tile_common.h"), "decode": ("decode.hip", "kernels.h")}
+TRAFFIC_SOURCES = {"fwd": ("fwd_bf16.hip", "kernels.h", "tile_common.h"), "decode": ("decode.hip", "kernels.h"),
+                   "bwd": ("bwd_bf16.hip", "kernels.h", "tile_common.h")}
 
 
 def kernel_source_digest(kind="fwd"):
@@ -117,11 +118,14 @@ def recorded_traffic(key, path=None):
 # (record key, sources digested, kernel name, which value cluster of the dispatches when two workloads
 # launch the same kernel on the same grid: 0 the lower, 1 the higher, None all; grid in threads, or
 # None for every grid)
-TRAFFIC_GRID = {"fwd_bf16 causal 2x2048x32x128": 512 * 512, "fwd_bf16 varlen gqa causal 8 seqs": 3584 * 512,
+TRAFFIC_GRID = {"fwd_bf16 causal 2x2048x32x128": 512 * 512, "fwd_bf16 unmasked 2x2048x32x128": 512 * 512,
+                "fwd_bf16 varlen gqa causal 8 seqs": 3584 * 512,
                 "fwd_bf16 sliding window 1024 2x8192x32x128": 2048 * 512,
                 "fwd_bf16 kvcache paged 16x256x32768 s4": 2048 * 512, "fwd_bf16 causal hd256 2x2048x16x256": 512 * 512}
 TRAFFIC_KERNELS = (
-    ("fwd_bf16 causal 2x2048x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
+    # the causal and unmasked launches share kernel and grid: the unmasked one fetches more
+    ("fwd_bf16 causal 2x2048x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", 0),
+    ("fwd_bf16 unmasked 2x2048x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", 1),
     ("fwd_bf16 varlen gqa causal 8 seqs", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
     ("fwd_bf16 sliding window 1024 2x8192x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
     ("fwd_bf16 kvcache paged 16x256x32768 s4", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, true, true>", None),
@@ -132,7 +136,10 @@ TRAFFIC_KERNELS = (
     ("decode mxfp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 4, 0>", None),
     ("decode int4 g1 16x32768x32x128 s32", "decode", "decode_kernel<128, 3, 0>", 0),
     ("decode int4 g4 16x32768x32x128 s32", "decode", "decode_kernel<128, 3, 0>", 1),
+    ("bwd dq causal 2x2048x32x128", "bwd", "bwd_dq_kernel<128, 8, 2>", None),
+    ("bwd dkdv causal 2x2048x32x128", "bwd", "bwd_dkdv_pair_kernel<128, 2>", None),
 )
+TRAFFIC_ROWS = "full,bwd,decode,kvcache,copy,varlen,window,hd256"  # the rows the two counter runs time
 COPY_KERNEL, COPY_KIB = "__amd_rocclr_copyBuffer", 1 << 20  # the 1 GiB copy row reads and writes 1 GiB
 
 
@@ -176,7 +183,7 @@ def write_traffic(fetch_db, write_db, out_path=None):
     copy_f, copy_w = copy_mean(find(fetch, COPY_KERNEL)), copy_mean(find(write, COPY_KERNEL))
     cal = (f"{COPY_KERNEL} of 1 GiB (bench.py --rows copy): FETCH_SIZE {copy_f:.1f} KiB, "
            f"WRITE_SIZE {copy_w:.1f} KiB per dispatch")
-    cmd = "python bench.py --rows decode,kvcache,copy,varlen,window,hd256 --no-cpu --steps 3 --warmup 1"
+    cmd = f"python bench.py --rows {TRAFFIC_ROWS} --no-cpu --steps 3 --warmup 1"
     out = {}
     for key, src, kname, which in TRAFFIC_KERNELS:
         grid = TRAFFIC_GRID.get(key)
@@ -344,7 +351,9 @@ def main():
             "workload": "bf16 B=2 M=2048 H=32 K=Kv=128, no mask (the headline shape without the causal diagonal)",
             "ms_per_call": round(ms_f, 5), "value": round(tf_f, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf_f, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf_f / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_f}, **tm}
+                         "frac": round(tf_f / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_f,
+                         "traffic": recorded_traffic("fwd_bf16 unmasked 2x2048x32x128"),
+                         "algorithmic_bytes": 4 * 2 * 2048 * 32 * 128 * 2 + 2 * 32 * 2048 * 4}, **tm}
         if not args.no_cpu:  # batch element 0, heads 0..7 of 32, no mask
             sample = [synth.to_f64(x[:1, :, :8], "bf16") for x in (qh, kh, vh)]
             result["rows"]["prefill_unmasked"]["cpu_oracle"] = oracle_timing(
@@ -664,6 +673,8 @@ def main():
         ms_b = timed(A.prepare_bwd(gb_, qb_, kb_, vb_, ob_, lb_, dqb, dkb, dvb, wsb, mask=A.MASK_CAUSAL), 100, 20, torch,
                      detail=tm)
         fl_b = 2.5 * 4.0 * Bb * Hb * Mb * Mb * Db / 2  # five products of the forward's size, causal half
+        t_dq, t_kv = recorded_traffic("bwd dq causal 2x2048x32x128"), recorded_traffic("bwd dkdv causal 2x2048x32x128")
+        bwd_traffic = t_dq + t_kv if t_dq is not None and t_kv is not None else None
         tf_b = fl_b / (ms_b * 1e-3) / 1e12
         log(f"backward causal bf16 [2,2048,32,128]: {ms_b * 1e3:.1f} us/call, {tf_b:.1f} TFLOP/s")
         result["rows"]["bwd_causal"] = {
@@ -671,7 +682,12 @@ def main():
             "ms_per_call": round(ms_b, 5), "value": round(tf_b, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_b,
-                         "note": "algorithmic flops = 2.5x the forward's (dS recomputation not counted)"}, **tm}
+                         "traffic": bwd_traffic,
+                         # q, k, v, out, dout read and dq, dk, dv written once; lse read; D and L written
+                         # by the first launch and read by the second
+                         "algorithmic_bytes": 8 * Bb * Mb * Hb * Db * 2 + 5 * Bb * Hb * Mb * 4,
+                         "note": "algorithmic flops = 2.5x the forward's (dS recomputation not counted); traffic "
+                                 "is the two launches' together"}, **tm}
         if not args.no_cpu:  # batch element 0, heads 0..7: the oracle's forward (for out, lse) and backward
             hq, hk, hv = (synth.to_f64(x[:1, :, :8], "bf16") for x in synth.qkv(2, shp, shp, shp, "bf16"))
             hg = synth.to_f64(synth.normal(2, 3, shp, "bf16")[:1, :, :8], "bf16")

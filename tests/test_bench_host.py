@@ -46,9 +46,11 @@ def test_write_traffic_from_counter_databases(tmp_path):
     write = [(copy, 1048576.0), (copy, 1048576.0)]
     fwd_vals = {}
     for i, (key, src, kname, which) in enumerate(bench.TRAFFIC_KERNELS):
-        base = {"fwd": 1000.0, "decode": 5000.0}[src]
+        base = {"fwd": 1000.0, "decode": 5000.0, "bwd": 7000.0}[src]
         grid = bench.TRAFFIC_GRID.get(key)
-        if grid:  # one forward kernel on three grids: each record takes only its own grid's dispatches
+        # one forward kernel on several grids: each record takes only its own grid's dispatches (the
+        # causal and unmasked launches share one grid and are told apart by their byte counts)
+        if grid:
             fwd_vals[key] = base + 100.0 * i
             fetch.append((f"void attn::{kname}(args)", fwd_vals[key], grid))
             write.append((f"void attn::{kname}(args)", 10.0, grid))
@@ -72,6 +74,9 @@ def test_write_traffic_from_counter_databases(tmp_path):
     assert fwd["source_sha256"] == bench.kernel_source_digest("fwd")
     for key, val in fwd_vals.items():
         assert rec[key]["fetch_kib"] == pytest.approx(val)
+    for key in ("bwd dq causal 2x2048x32x128", "bwd dkdv causal 2x2048x32x128"):
+        assert rec[key]["fetch_kib"] == pytest.approx(7000.0)
+        assert rec[key]["source_sha256"] == bench.kernel_source_digest("bwd")
     # bytes per launch = FETCH x scale + WRITE x scale, in bytes
     assert bench.recorded_traffic("fwd_bf16 causal 2x2048x32x128", str(out)) == pytest.approx(
         (fwd_vals["fwd_bf16 causal 2x2048x32x128"] * 2.0 + 10.0) * 1024)
