@@ -82,8 +82,11 @@ __device__ __forceinline__ float pair_sum(float x) {
 // pages per sequence.
 constexpr int kMaxPages = 8192;
 
-// VSPLIT waves share each 32-row block by value columns: with VSPLIT = 2 wave w + NW/2 computes
-// the same scores and softmax as wave w and keeps the second half of O^T.
+// VSPLIT waves share each 32-row block by value columns: with VSPLIT = 2 wave w + NW/2 keeps the
+// second half of O^T.  Over a paged cache both waves compute the whole score tile and its softmax
+// (the page table fills the LDS past the ring); otherwise (SSPLIT) each computes the scores of
+// its own 32 keys of every tile, and the pair exchanges its row maxima and bf16 P halves through
+// LDS, so that neither the matrix ops nor the exponentials of the scores are done twice.
 template <int KD, int VD, int NW, int STAGES, bool OUT_F32, int KSPLIT, bool PAGED, int VSPLIT = 1>
 __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     constexpr int NT = NW * 64;                  // threads per workgroup
@@ -104,9 +107,20 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     constexpr int VW = VD / VSPLIT;                  // value columns of this wave
     static_assert(KROUNDS >= 1 && KROUNDS * NT * 16 == KTILE && VROUNDS >= 1 && VROUNDS * NT * 16 == VTILE,
                   "tile split");
+    constexpr bool SSPLIT = VSPLIT == 2 && !PAGED;
+    static_assert(!SSPLIT || (STAGES == 2 && NW == 8), "score halves pair wave w with wave w + 4");
+    // score-split exchange area: per wave its bf16 P half ([2][64 lanes][16 bytes]), its 32 row
+    // values (maxima, then the row sums) and its flag
+    constexpr int XP_BYTES = NW * 2 * 64 * 16, XM_BYTES = NW * 32 * 4, XF_BYTES = NW * 4;
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * (KTILE + VTILE)];
-    __shared__ int ptab[PAGED ? kMaxPages : 1];  // page numbers of this workgroup's key tiles
+    // past the ring: a paged workgroup's page numbers, or the score-split exchange area
+    __shared__ __attribute__((aligned(16))) unsigned char aux[PAGED ? kMaxPages * 4
+                                                                   : (SSPLIT ? XP_BYTES + XM_BYTES + XF_BYTES : 16)];
+    int LDS_AS *const ptab = (int LDS_AS *)aux;  // page numbers of this workgroup's key tiles
+    unsigned char LDS_AS *const xp = (unsigned char LDS_AS *)aux;
+    float LDS_AS *const xm = (float LDS_AS *)(aux + XP_BYTES);
+    int LDS_AS *const xf = (int LDS_AS *)(aux + XP_BYTES + XM_BYTES);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
@@ -257,6 +271,10 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     int kaddr[KS];  // K: row kb*32 + l32 (kb adds 32 rows), chunk 2s + hh
 #pragma unroll
     for (int s = 0; s < KS; ++s) kaddr[s] = l32 * KROWB + (((2 * s + hh) ^ swz<KD>(l32)) << 4);
+    if constexpr (SSPLIT) {  // score halves: this wave reads K rows 32 vpart + l32
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kaddr[s] += vpart * 32 * KROWB;
+    }
     // V: lane i of 16-lane group G addresses key row 4*hh + i/4 (+ 8e + 16kt + 32kb) and
     // head-dim columns mb*32 + 16*(G&1) + 4*(i%4) .. +3.
     const int vrow = 4 * hh + ((lane & 15) >> 2);
@@ -269,11 +287,147 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
             const int row = vrow + 8 * e, col = vpart * VW + mb * 32 + vcol;
             vaddr[mb][e] = V_BASE + row * VROWB + ((((col >> 3) ^ swz<VD>(row))) << 4) + ((col & 4) << 1);
         }
+    // score halves: V rows of this wave's 32 keys and of its partner's (32 rows keep the swizzle)
+    int vown[SSPLIT ? MB : 1][2], vpar[SSPLIT ? MB : 1][2];
+    if constexpr (SSPLIT) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                vown[mb][e] = vaddr[mb][e] + vpart * 32 * VROWB;
+                vpar[mb][e] = vaddr[mb][e] + (1 - vpart) * 32 * VROWB;
+            }
+    }
 
     f32x16 o[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) o[i] = f32x16{};
     float m_ref = -INFINITY, l_run = 0.f;
+
+    // Score-split tile (SSPLIT): this wave's 32 keys of the tile are keys kt0 + 32 vpart + ..., its
+    // partner (wave ^ NW/2, the same 32 rows) has the other 32.  Both keep one reference maximum per
+    // row: every change of it is decided from the maximum over both halves.  The fast path (no
+    // rescale due, the same check as the whole-tile kernel) needs one exchange; when any wave of
+    // the workgroup fails it or still has a row without a finite reference, every wave takes the
+    // exact path (row maxima exchanged, then P).  Every barrier sits in workgroup-uniform control
+    // flow: the decision is read from the LDS flags after a barrier, and waves whose rows see no key
+    // of the tile still meet every barrier.
+    auto step_halves = [&](int slot, int kt0, auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const bool skip = MASKED && ((int64_t)kt0 + BN - 1 < (int64_t)wrow0 + shift - a.wl ||
+                                     (int64_t)kt0 > (int64_t)wrow0 + 31 + shift + a.wr);
+        const unsigned char LDS_AS *kst = (const unsigned char LDS_AS *)smem + slot * KTILE;  // + kaddr (own rows)
+        const unsigned char LDS_AS *vst = (const unsigned char LDS_AS *)smem + slot * VTILE;
+        const int partner = wave ^ (NW / 2);
+        auto scores = [&](f32x16 &x) __attribute__((always_inline)) {
+            x = f32x16{};
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 LDS_AS *)(kst + kaddr[s]), qf[s], x, 0, 0, 0);
+            if (MASKED) {
+                // element r holds key kt0 + 32 vpart + 4 hh + off(r)
+                const int dlo = klo - kt0 - 32 * vpart - 4 * hh, dhi = khi - kt0 - 32 * vpart - 4 * hh;
+                const bool cut_lo = kt0 < klo_w, cut_hi = kt0 + BN - 1 > khi_w;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    if ((cut_lo && off < dlo) || (cut_hi && off > dhi)) x[r] = -INFINITY;
+                }
+            }
+        };
+        auto exponentials = [&](f32x16 &x, float m_use) __attribute__((always_inline)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c, -m_use));
+            float ps[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ps[i] = x[i] + x[i + 8];
+#pragma unroll
+            for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+                for (int i = 0; i < w; ++i) ps[i] += ps[i + w];
+            return ps[0];
+        };
+        bf16x8 pown[2];  // this wave's P half: B operands of its keys 32 vpart + 16 kt + ...
+        auto put_p = [&](const f32x16 &x) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pown[kt][i] = (__bf16)x[8 * kt + i];
+                *(bf16x8 LDS_AS *)(xp + ((wave * 2 + kt) * 64 + lane) * 16) = pown[kt];
+            }
+        };
+        f32x16 x;
+        float psum = 0.f;
+        int need = 0;
+        if (!skip) {
+            scores(x);
+            if (__builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
+                need = 1;
+            } else {
+                psum = exponentials(x, m_ref);
+                if (__builtin_amdgcn_ballot_w64(!(psum <= kSumThreshold))) need = 1;
+                else put_p(x);
+            }
+        }
+        if (lane == 0) xf[wave] = need;
+        lds_barrier();
+        const i32x4 f0 = *(const i32x4 LDS_AS *)xf, f1 = *(const i32x4 LDS_AS *)(xf + 4);
+        if ((f0[0] | f0[1] | f0[2] | f0[3] | f1[0] | f1[1] | f1[2] | f1[3]) != 0) {
+            // exact path for the whole workgroup: scores again (K is still in LDS), row maxima of
+            // both halves, one reference decision per row shared by the pair
+            float mxh = -INFINITY;
+            if (!skip) {
+                __asm__ volatile("" ::: "memory");  // read K again rather than keep its fragments live
+                scores(x);
+                float m8[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m8[i] = fmaxf(x[i], x[i + 8]);
+#pragma unroll
+                for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+                    for (int i = 0; i < w; ++i) m8[i] = fmaxf(m8[i], m8[i + w]);
+                mxh = pair_max(m8[0]);
+                if (hh == 0) xm[wave * 32 + l32] = mxh;
+            }
+            lds_barrier();
+            if (!skip) {
+                const float mx = fmaxf(mxh, xm[partner * 32 + l32]) * c;
+                const bool up = mx > m_ref + kRescaleThreshold;
+                if (__builtin_amdgcn_ballot_w64(up)) {
+                    const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
+                    m_ref = up ? mx : m_ref;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int i = 0; i < MB; ++i)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+                }
+                psum = exponentials(x, (m_ref == -INFINITY) ? 0.f : m_ref);
+                put_p(x);
+            }
+            lds_barrier();
+        }
+        if (skip) return;
+        l_run += psum;
+        // O^T += V^T P^T: this wave's 32 keys, then its partner's (V rows from vown / vpar)
+#pragma unroll
+        for (int side = 0; side < 2; ++side)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const bf16x8 pk = side == 0 ? pown[kt]
+                                            : *(const bf16x8 LDS_AS *)(xp + ((partner * 2 + kt) * 64 + lane) * 16);
+                const int roff = kt * 16 * VROWB;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int a0 = (side == 0 ? vown[mb][0] : vpar[mb][0]) + roff;
+                    const int a1 = (side == 0 ? vown[mb][1] : vpar[mb][1]) + roff;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS *)(vst + a0));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS *)(vst + a1));
+                    const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk, o[mb], 0, 0, 0);
+                }
+            }
+    };
 
     // One 64-key tile at loop position p: S^T, mask (MASKED only), online softmax, O^T update.
     // STAGE_C >= 0 names the LDS stage at compile time (p % STAGES == STAGE_C), so every LDS
@@ -299,6 +453,10 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
             if (p + 1 < nt) wait_barrier<KROUNDS + VROUNDS>();
             else wait_barrier<0>();
             if (p + 2 < nt) issue(p + 2);
+        }
+        if constexpr (SSPLIT) {
+            step_halves(slot, kt0, masked_tag);
+            return;
         }
         // split keys: the other wave of the block takes this tile
         if (KSPLIT > 1 && ((STAGE_C >= 0 ? STAGE_C : p) & 1) != wsub) return;
@@ -481,7 +639,14 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     }
 
     // ---- normalise and store
-    const float l_tot = pair_sum(l_run);
+    float l_tot = pair_sum(l_run);
+    if constexpr (SSPLIT) {
+        // the pair's halves of each row sum (the same reference maximum): every wave meets this
+        // barrier after its last tile
+        if (hh == 0) xm[wave * 32 + l32] = l_tot;
+        lds_barrier();
+        l_tot += xm[(wave ^ (NW / 2)) * 32 + l32];
+    }
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     unsigned char *const obase_p = (unsigned char *)a.o + split * a.o_split * (OUT_F32 ? 4 : 2);
     float *const lse_p = a.lse ? a.lse + split * a.lse_split : nullptr;

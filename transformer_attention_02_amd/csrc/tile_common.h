@@ -64,6 +64,10 @@ __device__ __forceinline__ void wait_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
+// A workgroup barrier after this wave's LDS accesses have completed, leaving its tile loads in
+// flight: for exchanges through LDS in the middle of a tile.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Writes one wave's 32 output rows of HD bf16 values held in the 32x32 matrix-core C layout
 // (lane l owns row l % 32; element 4g + j of block mb is column 32 mb + 8 g + 4 (l / 32) + j),
 // each value times the lane's `sc`.  The rows are staged in `stage` (32 * HD * 2 bytes of LDS
