@@ -226,6 +226,30 @@ def test_bf16_distinct_head_dims(A, K, Kv):
     check(out, lse, oo, ol, TOL_BF16_OUT, TOL_LSE, f"K={K} Kv={Kv} packed causal")
 
 
+@pytest.mark.parametrize("K", [256, 128])
+def test_head_dim_256_rows_without_keys(A, K):
+    """Value head dim 256 on 64 heads (the 8-wave kernel whose two waves per 32-row block each
+    take 32 keys of every tile and trade P halves through LDS), with rows that see no key:
+    bottom-right causal with more queries than keys (the first Mq - Mk rows of every head are
+    empty: out 0, lse -inf) and a bottom-right window over a ragged key tail, so that some row
+    blocks skip tiles, or every tile, while others compute and take the exact path."""
+    H, Kv = 64, 256
+    # 5 and 4 query tiles of 128 rows x 64 heads: at least 256 workgroups, the 8-wave kernel
+    for Mq, Mkv, mask, win in [(520, 200, A.MASK_CAUSAL_BR, None), (500, 333, A.MASK_CAUSAL_LOCAL_BR, 70)]:
+        say(f"case: K={K} Kv={Kv} H={H} Mq={Mq} Mkv={Mkv} mask={mask} window={win}")
+        qh, kh, vh = synth.qkv(2600 + Mq + K, (1, Mq, H, K), (1, Mkv, H, K), (1, Mkv, H, Kv), "bf16")
+        kw = {"window_size": win} if win else {}
+        out, lse = A.attn_fwd(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), mask=mask, **kw)
+        torch.cuda.synchronize()
+        heads = [0, 31, H - 1]
+        sub = lambda x: np.ascontiguousarray(x[:, :, heads])
+        oo, ol = run_oracle(sub(qh), sub(kh), sub(vh), mask, "bf16", window=win)
+        check(out[:, :, heads], lse[:, heads], oo, ol, TOL_BF16_OUT, TOL_LSE, f"K={K} Mq={Mq} Mkv={Mkv}")
+        assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+        if mask == A.MASK_CAUSAL_BR:  # rows before the bottom-right diagonal's first key, every head
+            assert torch.all(out[0, : Mq - Mkv] == 0) and torch.all(torch.isneginf(lse[0, :, : Mq - Mkv]))
+
+
 def test_causal_head_dim_256_full_size(A):
     """Causal [2, 2048, 16, 256] bf16 (the flop count of the [2, 2048, 32, 128] prefill): the
     whole launch, every out and lse element against the oracle."""
