@@ -51,7 +51,7 @@ def parse():
                    "counters per kernel and grid) instead of running; no GPU needed")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE rocprofv3 run of "
-                        "'bench.py --rows decode,kvcache,copy,varlen,window,hd256 --no-cpu --steps 3 --warmup 1'; no GPU needed")
+                        f"'bench.py --rows {TRAFFIC_ROWS} --no-cpu --steps 3 --warmup 1'; no GPU needed")
     return p.parse_args()
 
 
