@@ -630,6 +630,53 @@ def test_merge_fp32_exactness(A):
     assert math.isinf(lse[0, 0, 3].item()) and torch.all(out[0, 3, 0] == 0)
 
 
+# ------------------------------------------------------------------ seeded random forward sweep
+
+def test_random_forward_sweep(A):
+    """40 seeded random forwards against the oracle: head dims (K, Kv) in every built pairing up to
+    256, every mask kind (windows drawn at random, packed sequences with different query and key
+    packings, empty key blocks), ragged lengths from 1 to 900, occasional negative scales, and a
+    few 64-head cases that select the 8-wave kernels (sampled heads).  bf16 out and fp32 lse."""
+    rng = np.random.default_rng(4242)
+    dims = [(64, 64), (128, 128), (256, 256), (128, 256), (64, 128), (256, 64)]
+    for case in range(40):
+        K, Kv = dims[rng.integers(len(dims))]
+        mask = int(rng.integers(10))
+        scale = float(rng.choice([None, 0.05, -0.08]) or 0) or None
+        kw, ss, ssk, okw = {}, None, None, {}
+        if mask in (6,):
+            wl, wr = int(rng.integers(0, 200)), int(rng.integers(0, 40))
+            kw = {"window_left": wl, "window_right": wr}
+            okw = {"window": wl, "window_right": wr}
+        elif mask in (7, 8, 9):
+            w = int(rng.integers(1, 400))
+            kw = {"window_size": w}
+            okw = {"window": w}
+        if mask in (2, 3, 5, 8, 9):  # packed: one batch element, several sequences
+            n = int(rng.integers(1, 6))
+            lq = rng.integers(1, 400, n)
+            lk = lq.copy() if rng.random() < 0.5 else rng.integers(0, 400, n)
+            ss, ssk = synth.seqstarts(lq), synth.seqstarts(lk)
+            B, H, Mq, Mkv = 1, int(rng.integers(1, 5)), int(ss[-1]), int(ssk[-1])
+            kw.update(seqstart_q=torch.from_numpy(ss).to("cuda"), seqstart_k=torch.from_numpy(ssk).to("cuda"),
+                      max_seqlen_q=int(lq.max()))
+        elif rng.random() < 0.25:  # 64 heads, B = 2, at least 3 query tiles of 256: the 8-wave kernels
+            B, H, Mq, Mkv = 2, 64, int(rng.integers(513, 900)), int(rng.integers(1, 900))
+        else:
+            B, H = int(rng.integers(1, 3)), int(rng.integers(1, 6))
+            Mq, Mkv = int(rng.integers(1, 900)), int(rng.integers(1, 900))
+        say(f"case {case}: K={K} Kv={Kv} mask={mask} B={B} H={H} Mq={Mq} Mkv={Mkv} scale={scale} "
+            f"{ {k: v for k, v in kw.items() if not torch.is_tensor(v)} } lens_q={None if ss is None else np.diff(ss).tolist()} "
+            f"lens_k={None if ssk is None else np.diff(ssk).tolist()}")
+        qh, kh, vh = synth.qkv(5000 + case, (B, Mq, H, K), (B, Mkv, H, K), (B, Mkv, H, Kv), "bf16")
+        out, lse = A.attn_fwd(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), mask=mask, scale=scale, **kw)
+        torch.cuda.synchronize()
+        heads = list(range(H)) if H <= 5 else [0, 29, H - 1]
+        sub = lambda x: np.ascontiguousarray(x[:, :, heads])
+        oo, ol = run_oracle(sub(qh), sub(kh), sub(vh), mask, "bf16", scale=scale, ss=ss, ssk=ssk, **okw)
+        check(out[:, :, heads], lse[:, heads], oo, ol, TOL_BF16_OUT, TOL_LSE, f"case {case}")
+
+
 # ------------------------------------------------------------------ bottom-right and windowed masks
 
 WINDOW_CASES = [  # (mask, window_size, window_left, window_right, Mq, Mkv)
