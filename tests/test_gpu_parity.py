@@ -1086,6 +1086,39 @@ def test_bwd_packed_masks(A, mask, win):
     check_grads(got, ref, f"packed mask {mask}", bound)
 
 
+def test_random_backward_sweep(A):
+    """20 seeded random backwards (head dims 64 and 128, every mask kind, random windows, ragged
+    lengths, packed sequences with different key packings for the kinds that allow them, occasional
+    negative scales), every gradient element within the derived error bound."""
+    rng = np.random.default_rng(777)
+    for case in range(20):
+        D = int(rng.choice([64, 128]))
+        mask = int(rng.integers(10))
+        scale = float(rng.choice([None, 0.06, -0.09]) or 0) or None
+        win = winr = None
+        if mask == 6:
+            win, winr = int(rng.integers(0, 150)), int(rng.integers(0, 30))
+        elif mask in (7, 8, 9):
+            win = int(rng.integers(1, 300))
+        sq = sk = None
+        if mask in oracle.PACKED:
+            n = int(rng.integers(1, 5))
+            lq = rng.integers(1, 300, n)
+            lk = rng.integers(1, 300, n) if mask in (2, 5, 9) and rng.random() < 0.6 else lq
+            sq, sk = synth.seqstarts(lq), synth.seqstarts(lk)
+            B, H, Mq, Mkv = 1, int(rng.integers(1, 4)), int(sq[-1]), int(sk[-1])
+        else:
+            B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+            Mq, Mkv = int(rng.integers(1, 500)), int(rng.integers(1, 500))
+        say(f"case {case}: bwd D={D} mask={mask} win={win},{winr} B={B} H={H} Mq={Mq} Mkv={Mkv} scale={scale} "
+            f"lens_q={None if sq is None else np.diff(sq).tolist()} lens_k={None if sk is None else np.diff(sk).tolist()}")
+        qh, kh, vh = synth.qkv(7000 + case, (B, Mq, H, D), (B, Mkv, H, D), (B, Mkv, H, D))
+        gh = synth.normal(7000 + case, 3, (B, Mq, H, D), "bf16")
+        got, ref, bound = run_bwd(A, qh, kh, vh, gh, mask=mask, scale=scale, window=win, window_right=winr,
+                                  seqstarts=sq, sk=sk)
+        check_grads(got, ref, f"case {case}", bound)
+
+
 def test_bwd_negative_scale_strided_5d(A):
     """5-D [B, M, G, H, D] inputs viewed out of a wider buffer, negative scale, gradients written
     into strided views."""
