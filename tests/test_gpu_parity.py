@@ -1328,6 +1328,80 @@ def test_quantised_decodes_sliding_window(A):
                 check(out[b:b + 1], lse[b:b + 1], oo, ol, TOL_F32, TOL_F32, f"{kind} b={b} keys [{lo}, {n})")
 
 
+def test_random_decode_sweep(A):
+    """30 seeded random split-KV decodes against the oracle: bf16, row-wise FP8 and group-wise INT4
+    caches; head dims 64, 128 and 256; contiguous lanes, padded lanes (lengths down to 0) and paged
+    caches in a random page order; random split counts (or the library's choice), windows and
+    negative scales; bf16 or fp32 outputs."""
+    rng = np.random.default_rng(31337)
+    for case in range(30):
+        kind = str(rng.choice(["bf16", "fp8", "int4"]))
+        D = int(rng.choice([64, 128, 256]))
+        B, H = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+        layout = str(rng.choice(["contig", "padded", "paged"]))
+        S = None if rng.random() < 0.2 else int(rng.integers(1, 65))
+        scale = float(rng.choice([None, 0.07, -0.05]) or 0) or None
+        win = None if (rng.random() < 0.5 or (kind == "bf16" and layout == "contig")) else int(rng.integers(1, 500))
+        G = int(rng.choice([g for g in (1, 2, 4, 8) if D // g >= 32])) if kind == "int4" else 1
+        out_dtype = torch.float32 if kind != "bf16" and rng.random() < 0.5 else torch.bfloat16
+        page = int(rng.choice([16, 32, 64]))
+        if layout == "contig":
+            M = int(rng.integers(1, 3000))
+            lens, cshape = np.full(B, M, dtype=np.int32), (B, M, H, D)
+        elif layout == "padded":
+            M = int(rng.integers(1, 2000))
+            lens = rng.integers(0, M + 1, B).astype(np.int32)
+            cshape = (B, M, H, D)
+        else:
+            maxb = int(rng.integers(1, 40))
+            P = B * maxb + int(rng.integers(0, 10))
+            tables = rng.permutation(P)[:B * maxb].reshape(B, maxb).astype(np.int32)
+            lens = rng.integers(0, maxb * page + 1, B).astype(np.int32)
+            M, cshape = maxb * page, (1, P * page, H, D)
+        say(f"case {case}: {kind} D={D} B={B} H={H} {layout} page={page if layout == 'paged' else None} "
+            f"lens={lens.tolist()} S={S} scale={scale} window={win} G={G} out={out_dtype}")
+        qh = synth.normal(9000 + case, synth.TAG_Q, (B, 1, H, D), "bf16")
+        kw = {}
+        if layout != "contig" or win is not None:
+            kw = dict(seqlens=torch.from_numpy(lens).cuda(), max_seqlen_k=int(M))
+        if layout == "paged":
+            kw.update(block_tables=torch.from_numpy(tables).cuda(), page_size=page)
+        if win is not None:
+            kw["window_size"] = win
+        if kind == "bf16":
+            kh, vh = synth.normal(9000 + case, synth.TAG_K, cshape, "bf16"), synth.normal(9000 + case, synth.TAG_V, cshape, "bf16")
+            if layout == "contig":
+                out, lse = A.attn_decode_splitkv(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), S, scale=scale)
+            else:
+                out, lse = A.attn_decode_splitkv_paged(dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), kw.pop("seqlens"),
+                                                       S, kw.pop("max_seqlen_k"), scale=scale, **kw)
+        elif kind == "fp8":
+            kc, vc, kss, vss = _fp8_cache(9000 + case, cshape)
+            k, v = (torch.from_numpy(x).cuda().view(torch.float8_e4m3fn) for x in (kc, vc))
+            out, lse = A.attn_decode_splitkv_fp8(dev(qh, "bf16"), k, v, _f16(kss), _f16(vss), S, scale=scale,
+                                                 out_dtype=out_dtype, **kw)
+        else:
+            kc, vc, kss, vss = _int4_cache(9000 + case, cshape, G)
+            out, lse = A.attn_decode_splitkv_int4(dev(qh, "bf16"), _u8(kc), _u8(vc), _flat_ss(kss), _flat_ss(vss), S,
+                                                  scale=scale, out_dtype=out_dtype, **kw)
+        torch.cuda.synchronize()
+        tol_o, tol_l = (TOL_F32, TOL_F32) if out_dtype == torch.float32 else (TOL_BF16_OUT, TOL_LSE)
+        for b in range(B):
+            n = int(lens[b])
+            lo = 0 if win is None else max(0, n - win)
+            if layout == "paged":
+                rows = lambda x: _gather(x, tables[b], page, n)[:, lo:n]
+            else:
+                rows = lambda x: x[b:b + 1, lo:n]
+            if kind == "bf16":
+                oo, ol = run_oracle(qh[b:b + 1], rows(kh), rows(vh), 0, "bf16", scale=scale)
+            elif kind == "fp8":
+                oo, ol = _fp8_oracle(qh[b:b + 1], rows(kc), rows(vc), rows(kss), rows(vss), scale=scale)
+            else:
+                oo, ol = _int4_oracle(qh[b:b + 1], rows(kc), rows(vc), rows(kss), rows(vss), scale=scale)
+            check(out[b:b + 1], lse[b:b + 1], oo, ol, tol_o, tol_l, f"case {case} b={b} keys [{lo}, {n})")
+
+
 @pytest.mark.parametrize("kind", ["bf16", "int4"])
 def test_decode_permuted_head_order(A, kind):
     """5-D [B, M, G, H, D] caches viewed out of [B, M, H, G, D] memory (G inner to H): inside a
