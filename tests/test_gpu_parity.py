@@ -1783,6 +1783,36 @@ def test_kvcache_head_dim_256(A, H, page, splits, gappy):
     _kvcache_case(A, lq, lk, 2048, H, 256, 4, 90 + H, page=page, splits=splits, **kw)
 
 
+def test_random_kvcache_sweep(A):
+    """20 seeded random KV-cache forwards: 1 to 6 sequences of 1 to 400 queries against 0 to cap keys
+    in padded lanes, gappy lanes (random starts) or a paged cache (pages of 64 to 256 keys in a
+    random order); every mask kind the entry point takes, random windows; head dims 64, 128, 256;
+    1 to 4 key chunks.  Every sequence against the oracle on its own keys."""
+    rng = np.random.default_rng(2718)
+    for case in range(20):
+        nseq = int(rng.integers(1, 7))
+        D = int(rng.choice([64, 128, 256]))
+        H = int(rng.choice([2, 4, 8, 32])) if D < 256 else int(rng.choice([2, 4, 32]))
+        mask = int(rng.choice([0, 4, 6, 7]))
+        splits = int(rng.integers(1, 5))
+        layout = str(rng.choice(["padded", "paged", "gappy"]))
+        page = int(rng.choice([64, 128, 256])) if layout == "paged" else None
+        cap = int(rng.integers(1, 33)) * 64
+        if page:
+            cap = -(-cap // page) * page
+        lq = [int(x) for x in rng.integers(1, 401, nseq)]
+        lk = [int(x) for x in rng.integers(0, cap + 1, nseq)]
+        starts = [int(rng.integers(0, cap - n + 1)) for n in lk] if layout == "gappy" else None
+        kw = {}
+        if mask == 6:
+            kw = {"wl": int(rng.integers(0, 300)), "wr": int(rng.integers(0, 40))}
+        elif mask == 7:
+            kw = {"window_size": int(rng.integers(1, 500))}
+        say(f"case {case}: kv cache {layout} page={page} nseq={nseq} lq={lq} lk={lk} cap={cap} H={H} D={D} "
+            f"mask={mask} {kw} splits={splits} starts={starts}")
+        _kvcache_case(A, lq, lk, cap, H, D, mask, 8000 + case, page=page, splits=splits, starts=starts, **kw)
+
+
 def test_kvcache_chunked_prefill_full_size(A):
     """The bench's KV-cache launch: 16 sequences x 256 new queries against 32768 cached keys each in pages of 256
     (random order), causal with offset, H=32, D=128, 4 key chunks; the oracle checks sequences 0 and 15."""
