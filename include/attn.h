@@ -343,7 +343,9 @@ attn_status attn_decode_splitkv_paged(const attn_tensor *q, const attn_tensor *k
  *     stride-1 last axis and 4-byte aligned rows: G (scale, shift) pairs of every cache row
  *     and head, one per group of D/G consecutive elements (G = 1: row-wise; D/G a multiple
  *     of 16), each one 32-bit word with the scale in its low half; element d's value is
- *     fp8(code) * scale_g + shift_g with g = d / (D/G).
+ *     fp8(code) * scale_g + shift_g with g = d / (D/G).  Or ATTN_DTYPE_F32 (InputsFp8's
+ *     use_fp32_scales), the same shape with 8-byte aligned rows: each pair two fp32, scale
+ *     first.  k and v metadata share one dtype.
  *   out [B, 1, (G,) H, D] bf16 or fp32; lse fp32 [B, H_total, 1] or NULL.
  *   The codes and metadata are read as they are; NaN codes or metadata propagate.
  *   Workspace, splits, window_size, scale, device-metadata handling and errors as in
@@ -365,7 +367,8 @@ attn_status attn_decode_splitkv_fp8(const attn_tensor *q, const attn_tensor *k, 
  *     attn_decode_splitkv_fp8 (lanes, padded lanes or pages).
  *   k_scale_shift, v_scale_shift: ATTN_DTYPE_F16, the shape of k with the last axis 2G
  *     (G pairs, scale first), stride-1 last axis, 4-byte aligned rows; D/G must be a
- *     multiple of 32 (G in {1, 2, 4} for D = 128; {1, 2} for D = 64).
+ *     multiple of 32 (G in {1, 2, 4} for D = 128; {1, 2} for D = 64).  Or ATTN_DTYPE_F32
+ *     pairs with 8-byte aligned rows, as for attn_decode_splitkv_fp8.
  *   Everything else as in attn_decode_splitkv_fp8. */
 attn_status attn_decode_splitkv_int4(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                                      const attn_tensor *k_scale_shift, const attn_tensor *v_scale_shift,

@@ -267,6 +267,15 @@ def test_fp8_decode_rejects():
     assert call(bt=FAKE) == A.ATTN_ERR_INVALID_ARGUMENT and "seqlens" in A.attn_last_error()
     assert call(k=tensor([B, M, H, 96], A.ATTN_DTYPE_FP8_E4M3)) == A.ATTN_ERR_INVALID_ARGUMENT
     assert call(k=tensor([B, M, H, D], A.ATTN_DTYPE_FP8_E4M3, data=FAKE + 8)) == A.ATTN_ERR_INVALID_ARGUMENT
+    # fp32 (scale, shift) pairs (use_fp32_scales): both tensors fp32, rows 8-byte aligned
+    ss32 = tensor([B, M, H, 2], A.ATTN_DTYPE_F32)
+    assert call(kss=ss32, vss=ss) == A.ATTN_ERR_INVALID_ARGUMENT and "share one dtype" in A.attn_last_error()
+    assert call(kss=ss32, vss=tensor([B, M, H, 2], A.ATTN_DTYPE_F32, data=FAKE + 4)) == A.ATTN_ERR_INVALID_ARGUMENT
+    assert "8-byte aligned" in A.attn_last_error()
+    odd = tensor([B, M, H, 2], A.ATTN_DTYPE_F32)
+    odd.stride[1] = H * 2 + 1  # rows of an odd number of fp32: not 8-byte aligned
+    odd.stride[0] = M * odd.stride[1]
+    assert call(kss=odd, vss=odd) == A.ATTN_ERR_INVALID_ARGUMENT and "multiple of 8 bytes" in A.attn_last_error()
 
 
 def test_mxfp8_decode_rejects():

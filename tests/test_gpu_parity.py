@@ -1503,6 +1503,72 @@ def test_int4_decode_full_size(A):
         torch.cuda.empty_cache()
 
 
+# ------------------------------------------------------------------ fp32 (scale, shift) metadata
+
+def _f32(ss: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(ss, dtype=np.float32)).cuda()
+
+
+def _off_fp16_grid(ss, seed, tag):
+    """fp32 copies of fp16 (scale, shift) pairs moved off the fp16 grid by a relative jitter of up to 2^-8."""
+    r = np.random.Generator(np.random.PCG64([seed, tag, 35]))
+    return ss.astype(np.float32) * (1 + r.uniform(-2.0 ** -8, 2.0 ** -8, ss.shape)).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind,D,G", [("fp8", 128, 1), ("fp8", 128, 4), ("fp8", 256, 2),
+                                      ("int4", 128, 1), ("int4", 64, 2), ("int4", 128, 4)])
+def test_fp32_scale_shift_decode(A, kind, D, G):
+    """InputsFp8 use_fp32_scales: (scale, shift) as two fp32 per row or group, values off the fp16
+    grid; contiguous lanes with 3 splits, padded lanes and 64-row pages in a random order, fp32
+    outputs against the oracle's dequantisation with the same fp32 metadata.  fp32 copies of fp16
+    metadata give the fp16-metadata launch's outputs bit for bit."""
+    B, M, H, S, page = 3, 640, 4, 3, 64
+    lens = np.array([640, 1, 333], dtype=np.int32)
+    seed = 1400 + D + 10 * G + (0 if kind == "fp8" else 500)
+    say(f"case: {kind} decode, fp32 scale/shift, D={D} G={G}")
+    qh = synth.normal(seed, synth.TAG_Q, (B, 1, H, D), "bf16")
+    if kind == "fp8":
+        kc, vc = (synth.fp8_codes(seed, t, (B, M, H, D)) for t in (synth.TAG_K, synth.TAG_V))
+        k16, v16 = (synth.scale_shift(seed, t, (B, M, H, G)) for t in (synth.TAG_K, synth.TAG_V))
+        up, call, deq = _fp8, A.attn_decode_splitkv_fp8, oracle.dequant_fp8_groupwise
+    else:
+        kc, vc, k16, v16 = _int4_cache(seed, (B, M, H, D), G)
+        up, call, deq = _u8, A.attn_decode_splitkv_int4, oracle.dequant_int4_groupwise
+    k32, v32 = _off_fp16_grid(k16, seed, 1), _off_fp16_grid(v16, seed, 2)
+    assert np.mean(k32.astype(np.float16).astype(np.float32) != k32) > 0.9
+    flat = lambda x: x.reshape(x.shape[:-2] + (2 * G,))
+    q = dev(qh, "bf16")
+    kd, vd = up(kc), up(vc)
+    out, lse = call(q, kd, vd, _f32(flat(k32)), _f32(flat(v32)), S, out_dtype=torch.float32)
+    # the same fp16 values as fp16 and as fp32 words
+    o16, l16 = call(q, kd, vd, _f16(flat(k16)), _f16(flat(v16)), S, out_dtype=torch.float32)
+    o32, l32 = call(q, kd, vd, _f32(flat(k16)), _f32(flat(v16)), S, out_dtype=torch.float32)
+    pout, plse = call(q, kd, vd, _f32(flat(k32)), _f32(flat(v32)), S, seqlens=torch.from_numpy(lens).cuda(),
+                      max_seqlen_k=M, out_dtype=torch.float32)
+    nb = M // page
+    tables = np.random.Generator(np.random.PCG64(seed)).permutation(B * nb).astype(np.int32).reshape(B, nb)
+    order = np.argsort(tables.reshape(-1))
+
+    def pg(x):
+        pages = np.concatenate([x[b, i * page:(i + 1) * page] for b in range(B) for i in range(nb)])
+        pages = pages.reshape((B * nb, page) + x.shape[2:])[order]
+        return np.ascontiguousarray(pages.reshape((1, B * M) + x.shape[2:]))
+    go, gl = call(q, up(pg(kc)), up(pg(vc)), _f32(flat(pg(k32))), _f32(flat(pg(v32))), S,
+                  seqlens=torch.from_numpy(lens).cuda(), max_seqlen_k=M,
+                  block_tables=torch.from_numpy(tables).cuda(), page_size=page, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32) and torch.equal(l16, l32), "fp32 copies of fp16 metadata changed the result"
+    q64 = synth.to_f64(qh, "bf16")
+    for b in range(B):
+        sl = slice(b, b + 1)
+        oo, ol = oracle.attention(q64[sl], deq(kc[sl], k32[sl]), deq(vc[sl], v32[sl]))
+        check(out[sl], lse[sl], oo, ol, TOL_F32, TOL_F32, f"contiguous b={b}")
+        n = int(lens[b])
+        oo, ol = oracle.attention(q64[sl], deq(kc[sl, :n], k32[sl, :n]), deq(vc[sl, :n], v32[sl, :n]))
+        check(pout[sl], plse[sl], oo, ol, TOL_F32, TOL_F32, f"padded lane b={b} len={n}")
+        check(go[sl], gl[sl], oo, ol, TOL_F32, TOL_F32, f"paged b={b} len={n}")
+
+
 from tests.helpers import TOL_BWD_F32  # noqa: E402
 
 

@@ -455,6 +455,30 @@ def test_fp8_groupwise_dequant(oracle_mod, G):
     np.testing.assert_array_equal(z, [[0.5, 0.5, -0.5, -0.5]])
 
 
+def test_fp32_scale_shift_pairs_are_used_unrounded(oracle_mod):
+    """InputsFp8's use_fp32_scales: fp32 (scale, shift) pairs that fp16 cannot hold (scale 1 + 2^-20,
+    shift 2^-30 + a per-row term) give each code's value times that exact scale plus that exact
+    shift, for FP8 (codes decoded by torch.float8_e4m3fn, independently) and INT4 codes."""
+    import torch
+
+    rows, D, G = 3, 64, 2
+    scale, tiny = np.float32(1.0 + 2.0 ** -20), np.float32(2.0 ** -30)
+    assert np.float16(scale) != scale and np.float16(tiny) != tiny
+    ss = np.zeros((rows, G, 2), np.float32)
+    ss[..., 0] = scale
+    ss[..., 1] = tiny + np.arange(rows, dtype=np.float32)[:, None] * np.float32(0.25)
+    codes = synth.fp8_codes(21, 1, (rows, D))
+    x = oracle_mod.dequant_fp8_groupwise(codes, ss)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    shift = ss[:, 0, 1].astype(np.float64)[:, None]  # the stored fp32 shifts (row 0's is 2^-30 alone)
+    assert shift[0, 0] == 2.0 ** -30
+    np.testing.assert_array_equal(x, vals * float(scale) + shift)
+    c4 = np.random.default_rng(5).integers(0, 256, (rows, D // 2), dtype=np.uint8)
+    x4 = oracle_mod.dequant_int4_groupwise(c4, ss)
+    nib = np.stack([c4 & 15, c4 >> 4], axis=-1).reshape(rows, D).astype(np.float64)
+    np.testing.assert_array_equal(x4, nib * float(scale) + shift)
+
+
 def test_e8m0_scales_match_torch(oracle_mod):
     """All 256 E8M0 codes against torch.float8_e8m0fnu (an independent decoder); closed forms."""
     import torch

@@ -527,9 +527,9 @@ def _fp8_args(q, k, v, k_scale_shift, v_scale_shift, seqlens, block_tables, page
 def attn_decode_splitkv_fp8(q, k, v, k_scale_shift, v_scale_shift, num_splits, seqlens=None, max_seqlen_k=None,
                             block_tables=None, page_size=None, scale=None, workspace=None, out=None, lse=True,
                             out_dtype=None, stream=None, window_size=None):
-    """Split-KV decode over FP8 E4M3 K/V caches (torch.float8_e4m3fn) with float16 (scale, shift)
-    pairs [..., 2] per cache row and head; lanes, padded lanes (seqlens) or pages (block_tables).
-    Returns (out, lse or None)."""
+    """Split-KV decode over FP8 E4M3 K/V caches (torch.float8_e4m3fn) with float16 (or float32:
+    use_fp32_scales) (scale, shift) pairs [..., 2G] per cache row, head and group; lanes, padded
+    lanes (seqlens) or pages (block_tables).  Returns (out, lse or None)."""
     if num_splits is None:  # the library's choice for the keys a sequence may hold
         num_splits = attn_decode_num_splits(q.shape[0], _htot(q), max_seqlen_k or k.shape[1])
     if out is None:
@@ -604,7 +604,8 @@ def attn_decode_splitkv_int4(q, k, v, k_scale_shift, v_scale_shift, num_splits, 
                              block_tables=None, page_size=None, scale=None, workspace=None, out=None, lse=True,
                              out_dtype=None, stream=None, window_size=None):
     """Split-KV decode over INT4 K/V caches: uint8 tensors [..., D/2] (two 4-bit codes per byte,
-    even element low) with float16 (scale, shift) pairs [..., 2G] per cache row, head and group.
+    even element low) with float16 (or float32) (scale, shift) pairs [..., 2G] per cache row, head and
+    group.
     Lanes, padded lanes (seqlens) or pages (block_tables).  Returns (out, lse or None)."""
     if num_splits is None:  # the library's choice for the keys a sequence may hold
         num_splits = attn_decode_num_splits(q.shape[0], _htot(q), max_seqlen_k or k.shape[1])

@@ -718,8 +718,17 @@ attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_
                             fn);
         group = 32;
     } else if (quant) {
-        if ((st = make_view(ksst, "k_scale_shift", &kss, 1u << ATTN_DTYPE_F16, 4)) != ATTN_OK) return st;
-        if ((st = make_view(vsst, "v_scale_shift", &vss, 1u << ATTN_DTYPE_F16, 4)) != ATTN_OK) return st;
+        // (scale, shift) pairs of two fp16 (one 32-bit word) or, InputsFp8's use_fp32_scales, of two
+        // fp32 (one 64-bit word, rows 8-byte aligned)
+        const unsigned ss_dt = (1u << ATTN_DTYPE_F16) | (1u << ATTN_DTYPE_F32);
+        if ((st = make_view(ksst, "k_scale_shift", &kss, ss_dt, 4)) != ATTN_OK) return st;
+        if ((st = make_view(vsst, "v_scale_shift", &vss, ss_dt, 4)) != ATTN_OK) return st;
+        if (kss.dtype != vss.dtype)
+            return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: k and v scale/shift tensors must share one dtype", fn);
+        if (kss.dtype == ATTN_DTYPE_F32) {
+            if ((st = make_view(ksst, "k_scale_shift", &kss, ss_dt, 8)) != ATTN_OK) return st;
+            if ((st = make_view(vsst, "v_scale_shift", &vss, ss_dt, 8)) != ATTN_OK) return st;
+        }
         if (q.dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: q must be bf16", fn);
         // INT4 rows are D/2 bytes: compare head dims in elements
         if (quant == ATTN_DTYPE_INT4X2) {
@@ -825,6 +834,7 @@ attn_status decode(const char *fn, int quant, const attn_tensor *qt, const attn_
     d.skss = kss.s;
     d.svss = vss.s;
     d.group = group;
+    d.ss32 = quant && !mx && kss.dtype == ATTN_DTYPE_F32;
     const int elem = mx ? attn::DECODE_MXFP8
                      : quant == ATTN_DTYPE_FP8_E4M3 ? attn::DECODE_FP8
                      : quant == ATTN_DTYPE_INT4X2 ? attn::DECODE_INT4

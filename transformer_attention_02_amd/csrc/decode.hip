@@ -148,9 +148,12 @@ __device__ __forceinline__ void unpack_elem(const u32x4 &w, float *x) {
         unpack<ELEM == DECODE_F32>(w, x);
 }
 
-// (scale, shift) halves of a metadata word
+// (scale, shift) halves of a metadata word: two fp16 in 32 bits (scale in the low half), or two
+// fp32 in 64 bits (scale in the low word)
 __device__ __forceinline__ float ss_scale(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float ss_shift(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+__device__ __forceinline__ float ss_scale(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ float ss_shift(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
 // An E8M0 block scale 2^(e - 127) as fp32: the exponent field itself, 2^-127 (a subnormal) for
 // e = 0, NaN for e = 255.
 __device__ __forceinline__ float e8m0_scale(uint32_t e) {
@@ -169,11 +172,14 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
 // MODE 0: k/v [B, Mkv, ...], every sequence has Mkv keys.  MODE 1: padded lanes [B, cap, ...] with
 // seqlens[b] valid keys.  MODE 2: paged cache [1, num_pages * page_size, ...]; key j of sequence b is
 // row block_tables[b][j / page_size] * page_size + j % page_size (page numbers clamped to the cache).
-template <int HD, int ELEM, int MODE>
+// SS32 (FP8 and INT4 caches): (scale, shift) pairs of two fp32 instead of two fp16.
+template <int HD, int ELEM, int MODE, bool SS32 = false>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     constexpr bool F32 = ELEM == DECODE_F32, INT4 = ELEM == DECODE_INT4, MX = ELEM == DECODE_MXFP8;
     constexpr bool QUANT = ELEM == DECODE_FP8 || INT4 || MX;       // codes + (scale, shift) or E8M0 metadata
-    constexpr int MES = MX ? 1 : 2;                                // bytes per metadata stride unit
+    static_assert(!SS32 || ELEM == DECODE_FP8 || INT4, "fp32 scale/shift pairs: FP8 and INT4 caches");
+    constexpr int MES = MX ? 1 : (SS32 ? 4 : 2);                   // bytes per metadata stride unit
+    using MetaW = typename std::conditional<SS32, uint64_t, uint32_t>::type;  // one group's metadata
     constexpr int EPL = F32 ? 4 : (INT4 ? 32 : (QUANT ? 16 : 8));  // elements per 16-byte load
     constexpr int LPK = HD / EPL;                                  // lanes per key row (a lane group)
     constexpr int KPP = NT / LPK;                                  // lane groups of the workgroup
@@ -208,7 +214,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const T *kp = (const T *)a.k + kb + head_offset(a.sk, hf, a.Hin) + cl * TPL;
     const T *vp = (const T *)a.v + vb + head_offset(a.sv, hf, a.Hin) + cl * TPL;
     // quantised caches: the metadata of this lane's group in every row, a (scale, shift) word
-    // addressed in fp16 units like a [.., G, 2] tensor, or an E8M0 byte of a [.., D/32] tensor
+    // addressed in fp16 (fp32 with SS32) units like a [.., G, 2] tensor, or an E8M0 byte of a
+    // [.., D/32] tensor
     // (a lane's EPL elements never straddle two groups)
     const char *kss = nullptr, *vss = nullptr;
     const int gw = QUANT ? (MX ? 1 : 2) * ((cl * EPL) / a.group) : 0;
@@ -216,8 +223,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         kss = (const char *)a.kss + ((MODE == 2 ? 0 : (int64_t)b * a.skss.b) + head_offset(a.skss, hf, a.Hin) + gw) * MES;
         vss = (const char *)a.vss + ((MODE == 2 ? 0 : (int64_t)b * a.svss.b) + head_offset(a.svss, hf, a.Hin) + gw) * MES;
     }
-    auto meta = [](const char *p) __attribute__((always_inline)) {
-        return MX ? (uint32_t)*(const uint8_t *)p : *(const uint32_t *)p;
+    auto meta = [](const char *p) __attribute__((always_inline)) -> MetaW {
+        if constexpr (SS32)
+            return *(const uint64_t *)p;
+        else
+            return MX ? (uint32_t)*(const uint8_t *)p : *(const uint32_t *)p;
     };
 
     float qv[EPL];
@@ -264,7 +274,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 
     constexpr int NS = QUANT ? U : 1;
     u32x4 wk[U], wv[U];
-    uint32_t sk[NS], sv[NS];
+    MetaW sk[NS], sv[NS];
     // lane32 path: uniform bases at head hf0 = hg * hpw, byte strides, 32-bit lane offsets
     // (head part + 16-byte column slice + row slot); the launcher checks that they fit
     const int hf0 = hg << lh;
@@ -451,7 +461,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 #ifndef DECODE_ROW_BYTES
 #define DECODE_ROW_BYTES 512
 #endif
-template <int HD, int ELEM, int MODE>
+template <int HD, int ELEM, int MODE, bool SS32 = false>
 hipError_t launch(const DecodeArgs &args, hipStream_t stream) {
     // heads per workgroup: enough neighbouring head segments for DECODE_ROW_BYTES contiguous bytes
     // per cache row, a power of two that divides Htot and leaves every head at least one lane group
@@ -481,22 +491,22 @@ hipError_t launch(const DecodeArgs &args, hipStream_t stream) {
     const int64_t es = ELEM == DECODE_F32 ? 4 : (ELEM == DECODE_BF16 ? 2 : 1);
     a.lane32 = MODE != 2 && fits(a.sk, es, 16 / es * (LPK - 1)) && fits(a.sv, es, 16 / es * (LPK - 1));
     if (ELEM == DECODE_FP8 || ELEM == DECODE_INT4)
-        a.lane32 = a.lane32 && fits(a.skss, 2, 2 * ((LPK - 1) * EPL / a.group)) &&
-                   fits(a.svss, 2, 2 * ((LPK - 1) * EPL / a.group));
+        a.lane32 = a.lane32 && fits(a.skss, SS32 ? 4 : 2, 2 * ((LPK - 1) * EPL / a.group)) &&
+                   fits(a.svss, SS32 ? 4 : 2, 2 * ((LPK - 1) * EPL / a.group));
     if (ELEM == DECODE_MXFP8)  // one E8M0 byte per block
         a.lane32 = a.lane32 && fits(a.skss, 1, (LPK - 1) * EPL / a.group) && fits(a.svss, 1, (LPK - 1) * EPL / a.group);
     const int64_t grid = (int64_t)a.S * a.B * (a.Htot >> a.log2_hpw);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_kernel<HD, ELEM, MODE>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<HD, ELEM, MODE, SS32>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int HD, int ELEM>
+template <int HD, int ELEM, bool SS32 = false>
 hipError_t launch_mode(const DecodeArgs &a, hipStream_t stream) {
-    if (a.block_tables) return launch<HD, ELEM, 2>(a, stream);
-    if (a.seqlens) return launch<HD, ELEM, 1>(a, stream);
-    return launch<HD, ELEM, 0>(a, stream);
+    if (a.block_tables) return launch<HD, ELEM, 2, SS32>(a, stream);
+    if (a.seqlens) return launch<HD, ELEM, 1, SS32>(a, stream);
+    return launch<HD, ELEM, 0, SS32>(a, stream);
 }
 
 template <int HD>
@@ -504,8 +514,8 @@ hipError_t launch_elem(const DecodeArgs &a, int elem, hipStream_t stream) {
     switch (elem) {
     case DECODE_BF16: return launch_mode<HD, DECODE_BF16>(a, stream);
     case DECODE_F32: return launch_mode<HD, DECODE_F32>(a, stream);
-    case DECODE_FP8: return launch_mode<HD, DECODE_FP8>(a, stream);
-    case DECODE_INT4: return launch_mode<HD, DECODE_INT4>(a, stream);
+    case DECODE_FP8: return a.ss32 ? launch_mode<HD, DECODE_FP8, true>(a, stream) : launch_mode<HD, DECODE_FP8>(a, stream);
+    case DECODE_INT4: return a.ss32 ? launch_mode<HD, DECODE_INT4, true>(a, stream) : launch_mode<HD, DECODE_INT4>(a, stream);
     case DECODE_MXFP8: return launch_mode<HD, DECODE_MXFP8>(a, stream);
     default: return hipErrorInvalidValue;
     }

@@ -76,6 +76,7 @@ struct DecodeArgs {
     const void *kss, *vss;
     Strides skss, svss;
     int group;
+    int ss32;      // FP8 / INT4: (scale, shift) pairs of two fp32 (8 bytes) instead of two fp16
     int log2_hpw;  // heads per workgroup = 1 << log2_hpw (set by the launcher)
     int lane32;    // every lane's offset from its workgroup's first head and row fits 32 bits (set by the launcher)
 };
