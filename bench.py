@@ -136,9 +136,15 @@ TRAFFIC_KERNELS = (
     ("decode mxfp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 4, 0>", None),
     ("decode int4 g1 16x32768x32x128 s32", "decode", "decode_kernel<128, 3, 0>", 0),
     ("decode int4 g4 16x32768x32x128 s32", "decode", "decode_kernel<128, 3, 0>", 1),
+    ("bwd prep causal 2x2048x32x128", "bwd", "bwd_prep_kernel<128>", None),
+    ("bwd dkdv keep-ds causal 2x2048x32x128", "bwd", "bwd_dkdv_pair_kernel<128, 2, true>", None),
+    ("bwd dq keep-ds causal 2x2048x32x128", "bwd", "bwd_dq_ds_kernel<128, 3>", None),
     ("bwd dq causal 2x2048x32x128", "bwd", "bwd_dq_kernel<128, 8, 2>", None),
-    ("bwd dkdv causal 2x2048x32x128", "bwd", "bwd_dkdv_pair_kernel<128, 2>", None),
+    ("bwd dkdv causal 2x2048x32x128", "bwd", "bwd_dkdv_pair_kernel<128, 2, false>", None),
 )
+BWD_KEEP_DS_KEYS = ("bwd prep causal 2x2048x32x128", "bwd dkdv keep-ds causal 2x2048x32x128",
+                    "bwd dq keep-ds causal 2x2048x32x128")
+BWD_RECOMPUTE_KEYS = ("bwd dq causal 2x2048x32x128", "bwd dkdv causal 2x2048x32x128")
 TRAFFIC_ROWS = "full,bwd,decode,kvcache,copy,varlen,window,hd256"  # the rows the two counter runs time
 COPY_KERNEL, COPY_KIB = "__amd_rocclr_copyBuffer", 1 << 20  # the 1 GiB copy row reads and writes 1 GiB
 
@@ -668,17 +674,28 @@ def main():
         lb_ = torch.empty((Bb, Hb, Mb), dtype=torch.float32, device="cuda")
         A.attn_fwd(qb_, kb_, vb_, mask=A.MASK_CAUSAL, out=ob_, lse=lb_)
         dqb, dkb, dvb = torch.empty_like(qb_), torch.empty_like(kb_), torch.empty_like(vb_)
-        wsb = torch.empty(A.attn_bwd_workspace_bytes(Bb, Hb, Mb), dtype=torch.uint8, device="cuda")
-        tm = {}
+        # the binding's default at head dim 128: dS kept in the workspace (three launches)
+        wsb = torch.empty(A.attn_bwd_ds_workspace_bytes(Bb, Hb, Mb, Mb), dtype=torch.uint8, device="cuda")
+        wsr = torch.empty(A.attn_bwd_workspace_bytes(Bb, Hb, Mb), dtype=torch.uint8, device="cuda")
+        tm, tmr = {}, {}
         ms_b = timed(A.prepare_bwd(gb_, qb_, kb_, vb_, ob_, lb_, dqb, dkb, dvb, wsb, mask=A.MASK_CAUSAL), 100, 20, torch,
                      detail=tm)
+        ms_r = timed(A.prepare_bwd(gb_, qb_, kb_, vb_, ob_, lb_, dqb, dkb, dvb, wsr, mask=A.MASK_CAUSAL), 100, 20, torch,
+                     detail=tmr)
         fl_b = 2.5 * 4.0 * Bb * Hb * Mb * Mb * Db / 2  # five products of the forward's size, causal half
-        t_dq, t_kv = recorded_traffic("bwd dq causal 2x2048x32x128"), recorded_traffic("bwd dkdv causal 2x2048x32x128")
-        bwd_traffic = t_dq + t_kv if t_dq is not None and t_kv is not None else None
+        sum_traffic = lambda keys: (None if any(recorded_traffic(k) is None for k in keys)
+                                    else sum(recorded_traffic(k) for k in keys))
+        bwd_traffic, rec_traffic = sum_traffic(BWD_KEEP_DS_KEYS), sum_traffic(BWD_RECOMPUTE_KEYS)
+        # dS blocks (32 keys x 32 queries, 2 KB) the dK/dV launch writes and the dQ launch reads: those
+        # of every (32-key, 64-query) tile pair with a visible element
+        nblk = sum(2 for p in range(Mb // 32) for t in range(Mb // 64) if 64 * t + 63 >= 32 * p)
+        ds_bytes = 2 * nblk * 2048 * Bb * Hb
         tf_b = fl_b / (ms_b * 1e-3) / 1e12
-        log(f"backward causal bf16 [2,2048,32,128]: {ms_b * 1e3:.1f} us/call, {tf_b:.1f} TFLOP/s")
+        log(f"backward causal bf16 [2,2048,32,128]: {ms_b * 1e3:.1f} us/call, {tf_b:.1f} TFLOP/s "
+            f"(dS recomputed: {ms_r * 1e3:.1f} us/call)")
         result["rows"]["bwd_causal"] = {
-            "workload": "attn_bwd of the causal bf16 prefill B=2 M=2048 H=32 K=Kv=128 (dQ kernel, then the dK/dV kernel)",
+            "workload": "attn_bwd of the causal bf16 prefill B=2 M=2048 H=32 K=Kv=128 (D/LSE rows, then dK/dV "
+                        "keeping dS in bf16, then dQ from dS)",
             "ms_per_call": round(ms_b, 5), "value": round(tf_b, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(tf_b, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_b,
@@ -686,8 +703,13 @@ def main():
                          # q, k, v, out, dout read and dq, dk, dv written once; lse read; D and L written
                          # by the first launch and read by the second
                          "algorithmic_bytes": 8 * Bb * Mb * Hb * Db * 2 + 5 * Bb * Hb * Mb * 4,
-                         "note": "algorithmic flops = 2.5x the forward's (dS recomputation not counted); traffic "
-                                 "is the two launches' together"}, **tm}
+                         "ds_roundtrip_bytes": ds_bytes,
+                         "note": "algorithmic flops = 2.5x the forward's; traffic is the three launches' together; "
+                                 "ds_roundtrip_bytes = the bf16 dS blocks written and read back"},
+            "recompute_ds": {"ms_per_call": round(ms_r, 5), "value": round(fl_b / (ms_r * 1e-3) / 1e12, 2),
+                             "traffic": rec_traffic,
+                             "note": "minimum workspace: dQ launch recomputing S and dP, then dK/dV"},
+            **tm}
         if not args.no_cpu:  # batch element 0, heads 0..7: the oracle's forward (for out, lse) and backward
             hq, hk, hv = (synth.to_f64(x[:1, :, :8], "bf16") for x in synth.qkv(2, shp, shp, shp, "bf16"))
             hg = synth.to_f64(synth.normal(2, 3, shp, "bf16")[:1, :, :8], "bf16")
@@ -697,7 +719,7 @@ def main():
                 fl_b / 8 / 1e12, "TFLOP/s", "batch element 0, heads 0-7 (8 of 64), fp64 backward from the oracle's "
                 "own out and lse")
             del hq, hk, hv, hg, ho, hl
-        del qb_, kb_, vb_, gb_, ob_, lb_, dqb, dkb, dvb, wsb
+        del qb_, kb_, vb_, gb_, ob_, lb_, dqb, dkb, dvb, wsb, wsr
 
     # ------------------------------------------------------------ sliding-window causal prefill
     if "window" in rows:

@@ -27,7 +27,8 @@
  *   attn_decode_num_splits (a split count for a decode shape),
  *   attn_decode_splitkv_paged (padded lanes or a paged KV cache),
  *   attn_decode_splitkv_fp8 / attn_decode_splitkv_int4 (quantised KV caches) and
- *   attn_bwd (gradients from the forward's output and LSE).
+ *   attn_bwd (gradients from the forward's output and LSE; with a larger workspace,
+ *   attn_bwd_ds_workspace_bytes, it keeps dS instead of recomputing it).
  *
  * Conventions shared by every call
  *   - Tensors are described by attn_tensor: a device pointer, a dtype, 4 dims
@@ -239,6 +240,13 @@ attn_status attn_fwd_kvcache(const attn_tensor *q, const attn_tensor *k, const a
  * ([B, H_total, Mq] each, 256-byte aligned). */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H_total, int64_t Mq);
 
+/* Bytes of device workspace with which the bf16 backward at head dim 128 of one sequence per
+ * batch element (no block-diagonal mask) keeps dS instead of recomputing it:
+ * attn_bwd_workspace_bytes(B, H_total, Mq) followed by a bf16 dS buffer of round_up(Mkv, 128) x
+ * round_up(Mq, 256) elements per (batch, head).  SIZE_MAX when Mq exceeds 2^24 (that form then
+ * never runs). */
+size_t attn_bwd_ds_workspace_bytes(int64_t B, int64_t H_total, int64_t Mq, int64_t Mkv);
+
 /* memory_efficient_attention_backward ("Attention - Core fMHA"): the gradients of the
  * forward for an upstream gradient, from the forward's output and LSE and the original
  * q, k, v (no dropout, no bias gradient).  With P_ij = exp(scale q_i.k_j - lse_i) on the
@@ -252,7 +260,12 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H_total, int64_t Mq);
  *     share memory (a stride-0 expanded head axis is rejected: for expanded GQA keys
  *     pass dk/dv of the expanded shape and sum over each group's heads).
  *   workspace: device, 256-byte aligned, >= attn_bwd_workspace_bytes(B, H_total, Mq).
- *   Two launches on `stream`.  Errors as attn_fwd; nothing is written on error. */
+ *   Two launches on `stream`: dQ (recomputing S and dP per key tile), then dK and dV.
+ *   bf16 at head dim 128 without a block-diagonal mask and with workspace_bytes >=
+ *   attn_bwd_ds_workspace_bytes(B, H_total, Mq, Mkv): three launches instead (each row's D and LSE; dK and dV, keeping dS in
+ *   bf16 in the workspace; dQ = scale dS K), so S and dP are computed once.  Both forms round P and
+ *   dS to bf16 before the products that use them.
+ *   Errors as attn_fwd; nothing is written on error. */
 attn_status attn_bwd(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k,
                      const attn_tensor *v, const attn_tensor *out, const float *lse,
                      const attn_mask *mask, const attn_varlen *varlen, float scale, void *workspace,

@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
                                            "attn_decode_splitkv_noalloc",
                                            "attn_decode_splitkv_paged",
                                            "attn_decode_splitkv_fp8", "attn_decode_splitkv_int4",
-                                           "attn_decode_splitkv_mxfp8", "attn_bwd_workspace_bytes",
+                                           "attn_decode_splitkv_mxfp8", "attn_bwd_workspace_bytes", "attn_bwd_ds_workspace_bytes",
                                            "attn_bwd",
                                            "attn_last_error"])
 
@@ -304,6 +304,19 @@ def test_fp8_and_f16_tensors_are_rejected_outside_the_fp8_decode():
     assert fwd(q8, q8, q8, q8) == A.ATTN_ERR_INVALID_ARGUMENT and "dtype" in A.attn_last_error()
     assert fwd(h, h, h, h) == A.ATTN_ERR_INVALID_ARGUMENT
     assert fwd(std4(), q8, q8, std4()) == A.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_kept_ds_workspace_size():
+    """The kept-dS workspace: the two row arrays, then round_up(Mkv, 128) x round_up(Mq, 256) bf16
+    per (batch, head), 256-byte rounded; SIZE_MAX once Mq passes 2^24; 0 for negative sizes."""
+    for B, H, Mq, Mkv in [(2, 32, 2048, 2048), (1, 3, 300, 333), (2, 1, 1, 1), (1, 1, 0, 5), (3, 2, 257, 0)]:
+        rows = A.attn_bwd_workspace_bytes(B, H, Mq)
+        ds = B * H * ((Mkv + 127) // 128 * 128) * ((Mq + 255) // 256 * 256) * 2
+        assert A.attn_bwd_ds_workspace_bytes(B, H, Mq, Mkv) == rows + (ds + 255) // 256 * 256
+    assert A.attn_bwd_ds_workspace_bytes(2, 32, 2048, 2048) == 1048576 + 2 * 32 * 2048 * 2048 * 2
+    assert A.attn_bwd_ds_workspace_bytes(1, 1, (1 << 24) + 1, 1) == 2 ** 64 - 1
+    assert A.attn_bwd_ds_workspace_bytes(1, 1, 1 << 24, 1) < 2 ** 40
+    assert A.attn_bwd_ds_workspace_bytes(-1, 1, 1, 1) == 0
 
 
 def test_bwd_workspace_and_rejects():

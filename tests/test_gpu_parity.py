@@ -1032,7 +1032,8 @@ def check_grads(got, ref, what, bound):
         assert ratio <= 1.0, f"{what} {name}: an element exceeds its error bound ({ratio:.3f} of it; max|d| {err})"
 
 
-def run_bwd(A, qh, kh, vh, gh, mask=0, scale=None, window=None, window_right=None, seqstarts=None, sk=None):
+def run_bwd(A, qh, kh, vh, gh, mask=0, scale=None, window=None, window_right=None, seqstarts=None, sk=None,
+            keep_ds=None):
     """GPU forward then backward on bf16 inputs; oracle backward on the exact values."""
     q, k, v, g = dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), dev(gh, "bf16")
     kw = {}
@@ -1050,7 +1051,7 @@ def run_bwd(A, qh, kh, vh, gh, mask=0, scale=None, window=None, window_right=Non
     out, lse = A.attn_fwd(q, k, v, mask=mask, scale=scale, **kw, **wkw)
     if mask in oracle.PACKED:
         kw["max_seqlen_k"] = int(lk.max())
-    dq, dk, dv = A.attn_bwd(g, q, k, v, out, lse, mask=mask, scale=scale, **kw, **wkw)
+    dq, dk, dv = A.attn_bwd(g, q, k, v, out, lse, mask=mask, scale=scale, keep_ds=keep_ds, **kw, **wkw)
     torch.cuda.synchronize()
     okw = dict(mask=mask, scale=scale, window=window, window_right=window_right, seqstart_q=seqstarts, seqstart_k=sk)
     q64, k64, v64, g64 = (synth.to_f64(x, "bf16") for x in (qh, kh, vh, gh))
@@ -1059,16 +1060,18 @@ def run_bwd(A, qh, kh, vh, gh, mask=0, scale=None, window=None, window_right=Non
     return (dq, dk, dv), ref, bwd_error_bound(q64, k64, v64, g64, oo, ol, ref, **okw)
 
 
+@pytest.mark.parametrize("keep_ds", [True, False])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("mask,win,winr,Mq,Mkv", [
     (0, None, None, 200, 300), (1, None, None, 333, 333), (4, None, None, 150, 290), (4, None, None, 290, 150),
     (6, 50, 20, 200, 260), (7, 100, None, 257, 257)])
-def test_bwd_ragged_shapes_masks(A, D, mask, win, winr, Mq, Mkv):
-    say(f"case: bwd D={D} mask={mask} win={win},{winr} Mq={Mq} Mkv={Mkv}")
+def test_bwd_ragged_shapes_masks(A, D, mask, win, winr, Mq, Mkv, keep_ds):
+    """Both backward forms: dS kept (three launches) and dS recomputed by the dQ launch."""
+    say(f"case: bwd D={D} mask={mask} win={win},{winr} Mq={Mq} Mkv={Mkv} keep_ds={keep_ds}")
     B, H = 2, 3
     qh, kh, vh = synth.qkv(900 + mask + D, (B, Mq, H, D), (B, Mkv, H, D), (B, Mkv, H, D))
     gh = synth.normal(901 + mask + D, 3, (B, Mq, H, D), "bf16")
-    got, ref, bound = run_bwd(A, qh, kh, vh, gh, mask=mask, window=win, window_right=winr)
+    got, ref, bound = run_bwd(A, qh, kh, vh, gh, mask=mask, window=win, window_right=winr, keep_ds=keep_ds)
     check_grads(got, ref, f"mask {mask}", bound)
     if mask == 4 and Mq > Mkv:  # bottom-right with more queries than keys: the first rows see nothing
         assert torch.all(got[0][:, :Mq - Mkv] == 0)
@@ -1089,7 +1092,8 @@ def test_bwd_packed_masks(A, mask, win):
 def test_random_backward_sweep(A):
     """20 seeded random backwards (head dims 64 and 128, every mask kind, random windows, ragged
     lengths, packed sequences with different key packings for the kinds that allow them, occasional
-    negative scales), every gradient element within the derived error bound."""
+    negative scales; unpacked cases alternate between keeping dS and recomputing it), every gradient
+    element within the derived error bound."""
     rng = np.random.default_rng(777)
     for case in range(20):
         D = int(rng.choice([64, 128]))
@@ -1110,12 +1114,14 @@ def test_random_backward_sweep(A):
         else:
             B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
             Mq, Mkv = int(rng.integers(1, 500)), int(rng.integers(1, 500))
+        keep_ds = case % 2 == 0
         say(f"case {case}: bwd D={D} mask={mask} win={win},{winr} B={B} H={H} Mq={Mq} Mkv={Mkv} scale={scale} "
-            f"lens_q={None if sq is None else np.diff(sq).tolist()} lens_k={None if sk is None else np.diff(sk).tolist()}")
+            f"lens_q={None if sq is None else np.diff(sq).tolist()} lens_k={None if sk is None else np.diff(sk).tolist()} "
+            f"keep_ds={keep_ds}")
         qh, kh, vh = synth.qkv(7000 + case, (B, Mq, H, D), (B, Mkv, H, D), (B, Mkv, H, D))
         gh = synth.normal(7000 + case, 3, (B, Mq, H, D), "bf16")
         got, ref, bound = run_bwd(A, qh, kh, vh, gh, mask=mask, scale=scale, window=win, window_right=winr,
-                                  seqstarts=sq, sk=sk)
+                                  seqstarts=sq, sk=sk, keep_ds=keep_ds)
         check_grads(got, ref, f"case {case}", bound)
 
 
@@ -1167,20 +1173,49 @@ def test_bwd_expanded_gqa(A):
 
 
 def test_bwd_causal_full_size(A):
-    """The causal [2, 2048, 32, 128] workload: full launch, every gradient element against the oracle."""
+    """The causal [2, 2048, 32, 128] workload: full launch in both forms (dS kept, as timed, and
+    recomputed), every gradient element against the oracle."""
     B, M, H, D = 2, 2048, 32, 128
     say("case: bwd causal full size")
     qh, kh, vh = synth.qkv(2, (B, M, H, D), (B, M, H, D), (B, M, H, D))
     gh = synth.normal(2, 3, (B, M, H, D), "bf16")
     q, k, v, g = dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), dev(gh, "bf16")
     out, lse = A.attn_fwd(q, k, v, mask=1)
-    dq, dk, dv = A.attn_bwd(g, q, k, v, out, lse, mask=1)
+    kept = A.attn_bwd(g, q, k, v, out, lse, mask=1, keep_ds=True)
+    again = A.attn_bwd(g, q, k, v, out, lse, mask=1, keep_ds=False)
     torch.cuda.synchronize()
     q64, k64, v64, g64 = (f64_threads(x) for x in (qh, kh, vh, gh))
     oo, ol = oracle.attention(q64, k64, v64, mask=1)
     ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, mask=1)
     bound = bwd_error_bound(q64, k64, v64, g64, oo, ol, ref, mask=1)
-    check_grads((dq, dk, dv), ref, "all 64 (b, h)", bound)
+    check_grads(kept, ref, "all 64 (b, h), dS kept", bound)
+    check_grads(again, ref, "all 64 (b, h), dS recomputed", bound)
+
+
+@pytest.mark.parametrize("mask,Mq,Mkv", [(4, 300, 333), (0, 513, 130), (7, 700, 700)])
+def test_bwd_kept_ds_matches_recomputed(A, mask, Mq, Mkv):
+    """The two backward forms at head dim 128 agree to bf16 rounding in dQ, dK and dV (D is summed
+    in another order, and dQ comes from dS instead of recomputed scores): bottom-right causal with
+    more keys than queries, no mask with more queries than keys, a bottom-right causal window of
+    100; lengths that are not multiples of 128 or 256."""
+    B, H, D = 2, 3, 128
+    say(f"case: bwd kept dS against recomputed mask={mask} Mq={Mq} Mkv={Mkv}")
+    qh, kh, vh = synth.qkv(990 + mask, (B, Mq, H, D), (B, Mkv, H, D), (B, Mkv, H, D))
+    gh = synth.normal(991 + mask, 3, (B, Mq, H, D), "bf16")
+    q, k, v, g = dev(qh, "bf16"), dev(kh, "bf16"), dev(vh, "bf16"), dev(gh, "bf16")
+    wkw = dict(window_size=100) if mask == 7 else {}
+    out, lse = A.attn_fwd(q, k, v, mask=mask, **wkw)
+    small = A.attn_bwd_workspace_bytes(B, H, Mq)
+    ws = torch.full((A.attn_bwd_ds_workspace_bytes(B, H, Mq, Mkv),), 255, dtype=torch.uint8, device="cuda")
+    a = A.attn_bwd(g, q, k, v, out, lse, mask=mask, workspace=ws, **wkw)
+    b = A.attn_bwd(g, q, k, v, out, lse, mask=mask, keep_ds=False, **wkw)
+    torch.cuda.synchronize()
+    assert bool((ws[small:] != 255).any()), "the dS buffer was not written: the kept-dS form did not run"
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv"), a, b):
+        err = (x.float() - y.float()).abs().max().item()
+        mag = y.float().abs().max().item()
+        assert err <= 2 ** -6 * mag, (name, err, mag)
 
 
 # ------------------------------------------------------------------ row/group-wise INT4 K/V caches

@@ -94,6 +94,8 @@ _lib.attn_decode_splitkv_mxfp8.argtypes = _lib.attn_decode_splitkv_fp8.argtypes
 _lib.attn_decode_splitkv_mxfp8.restype = ctypes.c_int
 _lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
 _lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+_lib.attn_bwd_ds_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+_lib.attn_bwd_ds_workspace_bytes.restype = ctypes.c_size_t
 _lib.attn_bwd.argtypes = [_T, _T, _T, _T, _T, ctypes.c_void_p, _P(AttnMask), _P(AttnVarlen), ctypes.c_float,
                           ctypes.c_void_p, ctypes.c_size_t, _T, _T, _T, ctypes.c_void_p]
 _lib.attn_bwd.restype = ctypes.c_int
@@ -561,6 +563,14 @@ def attn_bwd_workspace_bytes(B: int, H_total: int, Mq: int) -> int:
     return int(_lib.attn_bwd_workspace_bytes(B, H_total, Mq))
 
 
+def attn_bwd_ds_workspace_bytes(B: int, H_total: int, Mq: int, Mkv: int) -> int:
+    return int(_lib.attn_bwd_ds_workspace_bytes(B, H_total, Mq, Mkv))
+
+
+# largest kept-dS workspace the binding allocates by itself
+KEEP_DS_MAX_BYTES = 8 << 30
+
+
 def _bwd_args(dout, q, k, v, out, lse, mask, scale, seqstart_q, seqstart_k, max_seqlen_q, max_seqlen_k,
               window_size, window_left, window_right, workspace, dq, dk, dv, stream):
     _lse_buf(lse, q.shape[0] * _htot(q) * q.shape[1])
@@ -577,13 +587,20 @@ def _bwd_args(dout, q, k, v, out, lse, mask, scale, seqstart_q, seqstart_k, max_
 
 def attn_bwd(dout, q, k, v, out, lse, mask=MASK_NONE, scale=None, seqstart_q=None, seqstart_k=None,
              max_seqlen_q=None, max_seqlen_k=None, window_size=None, window_left=None, window_right=None,
-             dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """memory_efficient_attention_backward: returns (dq, dk, dv) for the forward of the same arguments."""
+             dq=None, dk=None, dv=None, workspace=None, stream=None, keep_ds=None):
+    """memory_efficient_attention_backward: returns (dq, dk, dv) for the forward of the same arguments.
+    keep_ds (bf16 at head dim 128 without a block-diagonal mask, workspace allocated here): True
+    sizes the workspace so that dS is kept instead of recomputed, False leaves it at the minimum,
+    None keeps dS when that workspace is at most KEEP_DS_MAX_BYTES."""
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if workspace is None:
         need = attn_bwd_workspace_bytes(q.shape[0], _htot(q), q.shape[1])
+        if keep_ds is not False and q.dtype == torch.bfloat16 and q.shape[-1] == 128 and seqstart_q is None:
+            big = attn_bwd_ds_workspace_bytes(q.shape[0], _htot(q), q.shape[1], k.shape[1])
+            if big < (1 << 63) and (keep_ds or big <= KEEP_DS_MAX_BYTES):
+                need = big
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     args, _keep = _bwd_args(dout, q, k, v, out, lse, mask, scale, seqstart_q, seqstart_k, max_seqlen_q,
                             max_seqlen_k, window_size, window_left, window_right, workspace, dq, dk, dv, stream)

@@ -534,6 +534,20 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H_total, int64_t Mq) {
     return 2 * align256((size_t)B * (size_t)H_total * (size_t)Mq * 4);
 }
 
+// dS^T buffer of the kept-dS backward: per (batch, head) round_up(Mkv, 128) key rows of
+// round_up(Mq, 256) bf16 query columns, after the two row arrays
+static const int64_t kDsMaxPitch = (int64_t)1 << 24;  // 64 rows of a dS^T tile stay below 2^31 bytes
+
+size_t attn_bwd_ds_workspace_bytes(int64_t B, int64_t H_total, int64_t Mq, int64_t Mkv) {
+    if (B < 0 || H_total < 0 || Mq < 0 || Mkv < 0) return 0;
+    const int64_t pitch = (Mq + 255) / 256 * 256, krows = (Mkv + 127) / 128 * 128;
+    if (pitch > kDsMaxPitch) return SIZE_MAX;
+    typedef unsigned __int128 u128;
+    const u128 ds = (u128)B * (u128)H_total * (u128)krows * (u128)pitch * 2u;
+    const u128 total = (u128)attn_bwd_workspace_bytes(B, H_total, Mq) + (ds + 255) / 256 * 256;
+    return total >= (u128)SIZE_MAX ? SIZE_MAX : (size_t)total;
+}
+
 attn_status attn_bwd(const attn_tensor *dot, const attn_tensor *qt, const attn_tensor *kt, const attn_tensor *vt,
                      const attn_tensor *ot, const float *lse, const attn_mask *mask, const attn_varlen *varlen,
                      float scale, void *workspace, size_t workspace_bytes, const attn_tensor *dqt,
@@ -650,6 +664,15 @@ attn_status attn_bwd(const attn_tensor *dot, const attn_tensor *qt, const attn_t
         a.nseq = 1;
         a.max_seqlen_q = a.Mq;
         a.max_seqlen_k = a.Mkv;
+    }
+    a.ds = nullptr;
+    a.ds_pitch = a.ds_rows = 0;
+    const size_t need_ds = attn_bwd_ds_workspace_bytes(q.B, htot(q), q.M, k.M);
+    // head dim 128 only: at 64 the dS round trip costs more than the recomputation it saves
+    if (q.dtype == ATTN_DTYPE_BF16 && q.D == 128 && !ms.packed && need_ds != SIZE_MAX && workspace_bytes >= need_ds) {
+        a.ds = (char *)workspace + need;
+        a.ds_pitch = (q.M + 255) / 256 * 256;
+        a.ds_rows = (k.M + 127) / 128 * 128;
     }
     return launch_status(q.dtype == ATTN_DTYPE_BF16 ? attn::launch_bwd_bf16(a, (hipStream_t)stream)
                                                     : attn::launch_bwd_f32(a, (hipStream_t)stream),

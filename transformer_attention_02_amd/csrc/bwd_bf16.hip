@@ -87,7 +87,9 @@ __device__ __forceinline__ bf16x8 tr_frag(const unsigned char LDS_AS *base, int 
 // accumulator set and one resident operand (K or V), so two waves fit per SIMD and one's
 // matrix-core ops overlap the other's LDS reads and fp32 work (a single wave doing all
 // four products needs ~320 registers per lane and runs alone on its SIMD).
-template <int HD, int STAGES>
+// With DS the dS side also writes its bf16 dS blocks to the key-major dS^T buffer for the
+// dQ launch that follows (one sequence only: rows and keys count from 0).
+template <int HD, int STAGES, bool DS = false>
 __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
     constexpr int NW = 8, NT = NW * 64, BK = 128;  // keys per workgroup (32 per wave pair)
     constexpr int ROWB = HD * 2;
@@ -198,6 +200,27 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < MB; ++i) acc[i] = f32x16{};
 
+    // dS of the last computed tile (DS, dS side), written after the next ring barrier: stores
+    // count in vmcnt, and issued at once they would hold up that barrier.  The buffer holds
+    // 32-key x 32-query blocks in the order the registers hold them ([2][64 lanes][8]: element
+    // i of lane l in half kt is key l % 32 and query 16 kt + 8 (i / 4) + 4 (l / 32) + i % 4), so
+    // every store instruction writes 1 KB of consecutive bytes.
+    bf16x8 pend[2][2];
+    int pend_q0 = -1;
+    __bf16 *const dsw = DS ? (__bf16 *)a.ds + ((int64_t)b * a.Htot + hf) * a.ds_rows * a.ds_pitch +
+                                 (int64_t)(kw0 >> 5) * (a.ds_pitch >> 5) * 1024 + lane * 8
+                           : nullptr;
+    auto flush_ds = [&]() __attribute__((always_inline)) {
+        if (DS && pend_q0 >= 0) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)  // read once, by the dQ launch: streaming stores
+                    __builtin_nontemporal_store(pend[qb][kt], (bf16x8 *)(dsw + ((pend_q0 >> 5) + qb) * 1024 + kt * 512));
+            pend_q0 = -1;
+        }
+    };
+
     auto step = [&](int t, auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int q0 = t * BQ;
@@ -206,6 +229,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
         if (STAGES == 3 && t + 1 < te) wait_barrier<2 * ROUNDS>();
         else wait_barrier<0>();
         if (t + STAGES - 1 < te) issue(t + STAGES - 1);
+        if (DS) flush_ds();
         // this pair's keys see no row of the tile: compute nothing, still meet every barrier
         const bool active = kw0 < Lk && !(MASKED && ((int64_t)kw0 > (int64_t)q0 + BQ - 1 + shift + a.wr ||
                                                       (int64_t)kw0 + 31 < (int64_t)q0 + shift - a.wl));
@@ -281,6 +305,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
                     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                         for (int i = 0; i < 8; ++i) ob[kt][i] = (__bf16)ds[8 * kt + i];
+                    if (DS) {
+                        pend[qb][0] = ob[0];
+                        pend[qb][1] = ob[1];
+                        pend_q0 = q0;
+                    }
                 }
                 // dV^T += dout^T P (P side) or dK^T += Q^T dS (other side)
                 const int toff = pside ? TILE_BYTES : 0;
@@ -303,6 +332,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
     for (; t < ua; ++t) step(t, std::true_type{});
     for (; t < ub; ++t) step(t, std::false_type{});
     for (; t < te; ++t) step(t, std::true_type{});
+    if (DS) flush_ds();
 
     {
         // gradient rows go out whole, staged in the now idle ring
@@ -526,6 +556,228 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
                         a.sdq.m, Lq - wrow0);
 }
 
+// ------------------------------------------------------------------ kept-dS form (one sequence)
+//
+// 1. bwd_prep_kernel: D_i and the base-2 LSE L_i of every query row, as the dQ kernel forms them.
+// 2. bwd_dkdv_pair_kernel<DS>: dK, dV, and dS^T in bf16 (the values dK uses).
+// 3. bwd_dq_ds_kernel: dQ^T += K^T dS^T, both operands read transposed from LDS tiles; S and dP
+//    are computed once instead of twice.
+
+// D and L of every query row: HD / 8 lanes per row, 16 bytes each, a lane-tree sum per row.
+// Rows are numbered like the row arrays ((b * Htot + h) * Mq + m); a wave takes PREP_ITER groups
+// of 64 / (HD / 8) consecutive rows, every load issued before the first sum, and writes its
+// rows' D and L from consecutive lanes.
+constexpr int PREP_ITER = 8;
+
+template <int HD>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+    constexpr int LPR = HD / 8, RPW = 64 / LPR;  // lanes per row, rows per wave and group
+    static_assert(RPW * PREP_ITER <= 64, "one lane per row of the wave at the end");
+    const int lane = threadIdx.x & 63;
+    const int64_t rows = (int64_t)a.B * a.Htot * a.Mq;
+    const int64_t w0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (RPW * PREP_ITER);
+    const int c = (lane % LPR) * 8;
+    u32x4 gw[PREP_ITER], ow[PREP_ITER];
+#pragma unroll
+    for (int it = 0; it < PREP_ITER; ++it) {
+        const int64_t w = w0 + it * RPW + lane / LPR;
+        gw[it] = ow[it] = u32x4{};
+        if (w < rows) {
+            const int m = (int)(w % a.Mq);
+            const int64_t bh = w / a.Mq;
+            const int hf = (int)(bh % a.Htot), b = (int)(bh / a.Htot);
+            gw[it] = *(const u32x4 *)((const __bf16 *)a.dout + (int64_t)b * a.sdo.b + head_offset(a.sdo, hf, a.Hin) +
+                                      (int64_t)m * a.sdo.m + c);
+            ow[it] = *(const u32x4 *)((const __bf16 *)a.o + (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) +
+                                      (int64_t)m * a.so.m + c);
+        }
+    }
+    float mine = 0.f;  // D of row w0 + lane
+#pragma unroll
+    for (int it = 0; it < PREP_ITER; ++it) {
+        float dd = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dd = fmaf(__uint_as_float(ow[it][e] << 16), __uint_as_float(gw[it][e] << 16), dd);
+            dd = fmaf(__uint_as_float(ow[it][e] & 0xffff0000u), __uint_as_float(gw[it][e] & 0xffff0000u), dd);
+        }
+#pragma unroll
+        for (int x = LPR / 2; x >= 1; x >>= 1) dd += __shfl_xor(dd, x, LPR);
+        const float v = __shfl(dd, (lane % RPW) * LPR);
+        if (lane / RPW == it) mine = v;
+    }
+    const int64_t w = w0 + lane;
+    if (lane < RPW * PREP_ITER && w < rows) {
+        const float lse = a.lse[w];
+        a.ws_d[w] = mine;
+        a.ws_l2[w] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    }
+}
+
+// dQ from the kept dS: 8 waves, 32 query rows each (256 per workgroup), 64-key tiles of K and
+// of dS (2 x 8 blocks of 32 keys x 32 queries, two runs of 16 KB in the buffer) through a
+// 3-stage LDS ring.  The key tiles and the masked/unmasked split are those of bwd_dq_kernel; on
+// masked tiles the dS elements of invisible (query, key) pairs are zeroed (the dK/dV launch
+// writes only blocks that hold a visible pair, so anything else in the buffer is never used).
+// In LDS the 16-byte chunk n of a block (half n / 64, lane n % 64) sits at n ^ (4 (2 (n / 64) +
+// (n / 32) % 2)): the transposed reads of one half-wave then touch 16 chunks in distinct banks.
+template <int HD, int STAGES>
+__global__ __launch_bounds__(512) void bwd_dq_ds_kernel(BwdArgs a) {
+    constexpr int NW = 8, NT = NW * 64;
+    constexpr int BM = NW * 32;               // query rows per workgroup
+    constexpr int ROWB = HD * 2, CPR = HD / 8;
+    constexpr int KT_BYTES = BN * ROWB;       // one K tile
+    constexpr int DT_BYTES = BN * BM * 2;     // one dS tile: 2 x 8 blocks of 2 KB
+    constexpr int STAGE_BYTES = KT_BYTES + DT_BYTES;
+    constexpr int KR = KT_BYTES / 16 / NT, DR = DT_BYTES / 16 / NT;
+    constexpr int MB = HD / 32;
+    static_assert(KR >= 1 && KR * NT * 16 == KT_BYTES && DR * NT * 16 == DT_BYTES, "tile split");
+    static_assert(BM == 256 && DT_BYTES == 2 * 8 * 2048, "a dS tile is two runs of 8 blocks");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // ---- which (query tile, batch*head); heaviest tiles first
+    const int BH = a.B * a.Htot;
+    const int tiles = (a.Mq + BM - 1) / BM;
+    const int bh = blockIdx.x % BH;
+    const int tile = tiles - 1 - (int)(blockIdx.x / BH);
+    const int b = bh / a.Htot, hf = bh % a.Htot;
+    const int Lq = a.Mq, Lk = a.Mkv;
+    const int row0 = tile * BM;
+    if (tile < 0 || row0 >= Lq) return;
+    const int64_t shift = a.bottom_right ? (int64_t)Lk - Lq : 0;
+    const int row_last = min(row0 + BM, Lq) - 1;
+    const int kbeg = clampk((int64_t)row0 + shift - a.wl, 0, Lk);
+    const int kend = clampk((int64_t)row_last + shift + a.wr + 1, 0, Lk);
+    const int tb = kbeg / BN;
+    const int te = kend > kbeg ? (kend + BN - 1) / BN : tb;
+    int ua = (clampk((int64_t)row_last + shift - a.wl, 0, Lk) + BN - 1) / BN;
+    int ub = clampk((int64_t)row0 + shift + a.wr + 1, 0, Lk) / BN;
+    ua = min(max(ua, tb), te);
+    ub = min(max(ub, ua), te);
+
+    const __bf16 *kp = (const __bf16 *)a.k + (int64_t)b * a.sk.b + head_offset(a.sk, hf, a.Hin);
+    // block (key block kb, query block qb) starts at 2048 (kb * nqb + qb) bytes of the head's slab
+    const unsigned nqb = (unsigned)(a.ds_pitch >> 5), run = nqb * 2048u;
+    const unsigned char *dsp = (const unsigned char *)a.ds + (int64_t)bh * a.ds_rows * a.ds_pitch * 2 + (row0 >> 5) * 2048;
+    const unsigned kstride = (unsigned)a.sk.m * 2u;
+
+    unsigned koff[KR], doff[DR];
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+        const int p = (r * NW + wave) * 64 + lane;
+        const int row = p / CPR, c = (p % CPR) ^ swz<HD>(row);
+        koff[r] = row * kstride + c * 16;
+    }
+#pragma unroll
+    for (int r = 0; r < DR; ++r) {
+        // LDS chunk p of the tile: key half p / 1024, query block (p / 128) % 8, swizzled chunk p % 128
+        const int p = (r * NW + wave) * 64 + lane;
+        const int n = p & 127, src = n ^ ((2 * (n >> 6) + ((n >> 5) & 1)) << 2);
+        doff[r] = (unsigned)(p >> 10) * run + (unsigned)(((p >> 7) & 7) * 128 + src) * 16u;
+    }
+    const unsigned smem_base = (unsigned)(unsigned long long)(unsigned char LDS_AS *)smem;
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const int kt0 = t * BN;
+        const int nvalid = min(BN, Lk - kt0);
+        const unsigned st = smem_base + ((t - tb) % STAGES) * STAGE_BYTES;
+        const i32x4 kr = make_rsrc(kp + (int64_t)kt0 * a.sk.m, (nvalid - 1) * kstride + ROWB);
+        // key blocks kt0 / 32 and kt0 / 32 + 1 < ds_rows / 32, query blocks row0 / 32 + 0..7 < nqb
+        const i32x4 dr = make_rsrc(dsp + (int64_t)(kt0 >> 5) * run, run + 8 * 2048);
+#pragma unroll
+        for (int r = 0; r < KR; ++r) dma16(kr, koff[r], st + (r * NW + wave) * 1024);
+#pragma unroll
+        for (int r = 0; r < DR; ++r) dma16_nt(dr, doff[r], st + KT_BYTES + (r * NW + wave) * 1024);
+    };
+
+    const int wrow0 = row0 + wave * 32;
+    const int qrow = wrow0 + l32;
+    const int klo = clampk((int64_t)qrow + shift - a.wl, 0, Lk);
+    const int khi = clampk((int64_t)qrow + shift + a.wr, -1, Lk - 1);
+    const int klo_w = clampk((int64_t)wrow0 + 31 + shift - a.wl, 0, Lk);
+    const int khi_w = clampk((int64_t)wrow0 + shift + a.wr, -1, Lk - 1);
+
+    int taddr[MB][2];
+    tr_offsets<HD, MB>(lane, taddr);
+    // The transposed read of this wave's query block: lane l of 16-lane group G takes the 4
+    // queries 16 (G % 2) + 4 (l % 4) .. + 3 of key 16 kt + 4 hh + (l % 16) / 4 + 8 e; in the block
+    // those are bytes 8 ((l / 2) % 2) of the chunk of half G % 2, lane key + 32 (l % 2).
+    int daddr[2][2];
+    {
+        const int g1 = (lane >> 4) & 1, hb = lane & 1;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int key = 16 * kt + 4 * hh + ((lane & 15) >> 2) + 8 * e;
+                const int n = g1 * 64 + hb * 32 + key;
+                daddr[kt][e] = wave * 2048 + ((n ^ ((2 * g1 + hb) << 2)) << 4) + ((lane >> 1) & 1) * 8;
+            }
+    }
+
+    f32x16 dq[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) dq[i] = f32x16{};
+
+    auto step = [&](int t, auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const int kt0 = t * BN;
+        if (STAGES == 3 && t + 1 < te) wait_barrier<KR + DR>();
+        else wait_barrier<0>();
+        if (t + STAGES - 1 < te) issue(t + STAGES - 1);
+        if (MASKED && ((int64_t)kt0 + BN - 1 < (int64_t)wrow0 + shift - a.wl ||
+                       (int64_t)kt0 > (int64_t)wrow0 + 31 + shift + a.wr))
+            return;
+        const unsigned char LDS_AS *st = (const unsigned char LDS_AS *)smem + ((t - tb) % STAGES) * STAGE_BYTES;
+        const unsigned char LDS_AS *sd = st + KT_BYTES;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            // dS^T operand: lane owns query l32; element i of step kt is key kt0 + 32 kb + 16 kt +
+            // 8 (i / 4) + 4 hh + i % 4, the k order of the K^T operand below
+            bf16x8 dsb[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) dsb[kt] = tr_frag(sd + kb * 16384, daddr[kt][0], daddr[kt][1]);
+            if (MASKED) {
+                const int kb0 = kt0 + kb * 32;
+                const int dlo = klo - kb0 - 4 * hh, dhi = khi - kb0 - 4 * hh;
+                const bool cut_lo = kb0 < klo_w, cut_hi = kb0 + 31 > khi_w;
+                if (cut_lo || cut_hi) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = 8 * (r >> 2) + (r & 3);
+                        if ((cut_lo && off < dlo) || (cut_hi && off > dhi)) dsb[r >> 3][r & 7] = (__bf16)0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int roff = (kb * 32 + kt * 16) * ROWB;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const bf16x8 kt_ = tr_frag(st, taddr[mb][0] + roff, taddr[mb][1] + roff);
+                    dq[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_, dsb[kt], dq[mb], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    if (tb < te) issue(tb);
+    if (STAGES == 3 && tb + 1 < te) issue(tb + 1);
+    int t = tb;
+    for (; t < ua; ++t) step(t, std::true_type{});
+    for (; t < ub; ++t) step(t, std::false_type{});
+    for (; t < te; ++t) step(t, std::true_type{});
+
+    __syncthreads();  // every wave has finished reading the ring
+    store_rows_bf16<HD>(dq, a.scale, (unsigned char LDS_AS *)smem + wave * 32 * ROWB, (unsigned char *)a.dq,
+                        (int64_t)b * a.sdq.b + head_offset(a.sdq, hf, a.Hin) + (int64_t)wrow0 * a.sdq.m, a.sdq.m,
+                        Lq - wrow0);
+}
+
 template <int HD>
 hipError_t launch_hd(const BwdArgs &a, hipStream_t stream) {
     constexpr int NW_Q = 8;
@@ -540,6 +792,17 @@ hipError_t launch_hd(const BwdArgs &a, hipStream_t stream) {
     const int64_t gq = (int64_t)((a.max_seqlen_q + NW_Q * 32 - 1) / (NW_Q * 32)) * a.nseq * a.B * a.Htot;
     const int64_t gkv = (int64_t)((a.max_seqlen_k + 127) / 128) * a.nseq * a.B * a.Htot;
     if (gq > 0x7fffffff || gkv > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if constexpr (HD == 128) if (a.ds) {
+        // one sequence: D and L first, then dK/dV (writing dS), then dQ from dS
+        constexpr int PREP_ROWS = 4 * (64 / (HD / 8)) * PREP_ITER;  // rows per 256-thread workgroup
+        const int64_t gp = ((int64_t)a.B * a.Htot * a.Mq + PREP_ROWS - 1) / PREP_ROWS;
+        if (gp > 0x7fffffff) return hipErrorInvalidConfiguration;
+        if (gp > 0) hipLaunchKernelGGL((bwd_prep_kernel<HD>), dim3((unsigned)gp), dim3(256), 0, stream, a);
+        if (gkv > 0)
+            hipLaunchKernelGGL((bwd_dkdv_pair_kernel<HD, BWD_STAGES_KV, true>), dim3((unsigned)gkv), dim3(512), 0, stream, a);
+        if (gq > 0) hipLaunchKernelGGL((bwd_dq_ds_kernel<HD, 3>), dim3((unsigned)gq), dim3(512), 0, stream, a);
+        return hipGetLastError();
+    }
     // the dQ launch writes the per-row D and L that the dK/dV launch reads
     if (gq > 0) hipLaunchKernelGGL((bwd_dq_kernel<HD, NW_Q, BWD_STAGES_Q>), dim3((unsigned)gq), dim3(NW_Q * 64), 0, stream, a);
     if (gkv > 0) hipLaunchKernelGGL((bwd_dkdv_pair_kernel<HD, BWD_STAGES_KV>), dim3((unsigned)gkv), dim3(512), 0, stream, a);

@@ -115,6 +115,10 @@ struct BwdArgs {
     int packed, bottom_right, wl, wr;
     const int32_t *seqstart_q, *seqstart_k;
     int nseq, max_seqlen_q, max_seqlen_k;
+    // bf16, one sequence: dS^T kept in bf16, [B * Htot][ds_rows][ds_pitch] (key-major rows of
+    // ds_pitch query columns); NULL: dQ recomputes S and dP in its own launch
+    void *ds;
+    int64_t ds_pitch, ds_rows;
 };
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);

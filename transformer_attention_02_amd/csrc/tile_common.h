@@ -12,6 +12,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -42,6 +43,15 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, unsigned num_record
 // the kernels order them themselves with wait_barrier().
 __device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, unsigned lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds)
+                 : "memory");
+}
+
+// dma16 with the streaming (non-temporal) cache policy: for data read once, so that it does not
+// push reused tiles out of the L2.
+__device__ __forceinline__ void dma16_nt(i32x4 rsrc, unsigned voff, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(lds)
                  : "memory");
