@@ -265,6 +265,7 @@ size_t attn_bwd_ds_workspace_bytes(int64_t B, int64_t H_total, int64_t Mq, int64
  *   attn_bwd_ds_workspace_bytes(B, H_total, Mq, Mkv): three launches instead (each row's D and LSE; dK and dV, keeping dS in
  *   bf16 in the workspace; dQ = scale dS K), so S and dP are computed once.  Both forms round P and
  *   dS to bf16 before the products that use them.
+ *   The two forms measured within a few percent of each other.
  *   Errors as attn_fwd; nothing is written on error. */
 attn_status attn_bwd(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k,
                      const attn_tensor *v, const attn_tensor *out, const float *lse,

@@ -590,16 +590,17 @@ def attn_bwd(dout, q, k, v, out, lse, mask=MASK_NONE, scale=None, seqstart_q=Non
              dq=None, dk=None, dv=None, workspace=None, stream=None, keep_ds=None):
     """memory_efficient_attention_backward: returns (dq, dk, dv) for the forward of the same arguments.
     keep_ds (bf16 at head dim 128 without a block-diagonal mask, workspace allocated here): True
-    sizes the workspace so that dS is kept instead of recomputed, False leaves it at the minimum,
-    None keeps dS when that workspace is at most KEEP_DS_MAX_BYTES."""
+    sizes the workspace so that dS is kept instead of recomputed (when that workspace is at most
+    KEEP_DS_MAX_BYTES); False or None leaves it at the minimum.  The two forms measured within a
+    few percent of each other, either way round depending on what ran before."""
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if workspace is None:
         need = attn_bwd_workspace_bytes(q.shape[0], _htot(q), q.shape[1])
-        if keep_ds is not False and q.dtype == torch.bfloat16 and q.shape[-1] == 128 and seqstart_q is None:
+        if keep_ds and q.dtype == torch.bfloat16 and q.shape[-1] == 128 and seqstart_q is None:
             big = attn_bwd_ds_workspace_bytes(q.shape[0], _htot(q), q.shape[1], k.shape[1])
-            if big < (1 << 63) and (keep_ds or big <= KEEP_DS_MAX_BYTES):
+            if big <= KEEP_DS_MAX_BYTES:
                 need = big
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     args, _keep = _bwd_args(dout, q, k, v, out, lse, mask, scale, seqstart_q, seqstart_k, max_seqlen_q,
