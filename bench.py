@@ -130,12 +130,12 @@ TRAFFIC_KERNELS = (
     ("fwd_bf16 sliding window 1024 2x8192x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
     ("fwd_bf16 kvcache paged 16x256x32768 s4", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, true, true>", None),
     ("fwd_bf16 causal hd256 2x2048x16x256", "fwd", "fwd_bf16_vsplit_kernel<256, 256, false, false>", None),
-    ("decode bf16 16x32768x32x128 s64", "decode", "decode_kernel<128, 0, 0>", None),
-    ("decode bf16 paged 16x32768x32x128 page64 s64", "decode", "decode_kernel<128, 0, 2>", None),
-    ("decode fp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 2, 0>", None),
-    ("decode mxfp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 4, 0>", None),
-    ("decode int4 g1 16x32768x32x128 s32", "decode", "decode_kernel<128, 3, 0>", 0),
-    ("decode int4 g4 16x32768x32x128 s32", "decode", "decode_kernel<128, 3, 0>", 1),
+    ("decode bf16 16x32768x32x128 s64", "decode", "decode_kernel<128, 0, 0, false>", None),
+    ("decode bf16 paged 16x32768x32x128 page64 s64", "decode", "decode_kernel<128, 0, 2, false>", None),
+    ("decode fp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 2, 0, false>", None),
+    ("decode mxfp8 16x32768x32x128 s64", "decode", "decode_kernel<128, 4, 0, false>", None),
+    ("decode int4 g1 16x32768x32x128 s32", "decode", "decode_kernel<128, 3, 0, false>", 0),
+    ("decode int4 g4 16x32768x32x128 s32", "decode", "decode_kernel<128, 3, 0, false>", 1),
     ("bwd prep causal 2x2048x32x128", "bwd", "bwd_prep_kernel<128>", None),
     ("bwd dkdv keep-ds causal 2x2048x32x128", "bwd", "bwd_dkdv_pair_kernel<128, 2, true>", None),
     ("bwd dq keep-ds causal 2x2048x32x128", "bwd", "bwd_dq_ds_kernel<128, 3>", None),

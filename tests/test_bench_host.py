@@ -58,7 +58,7 @@ def test_write_traffic_from_counter_databases(tmp_path):
             fetch.append((f"void attn::{kname}(args)", base))
             write.append((f"void attn::{kname}(args)", 10.0))
     # the two INT4 workloads share a kernel name: values 3000 (G=1) and 3500 (G=4)
-    int4 = "void attn::decode_kernel<128, 3, 0>(args)"
+    int4 = "void attn::decode_kernel<128, 3, 0, false>(args)"
     fetch += [(int4, 3000.0), (int4, 3001.0), (int4, 3500.0), (int4, 3499.0)]
     write += [(int4, 20.0), (int4, 20.0)]
     fdb, wdb, out = tmp_path / "f.db", tmp_path / "w.db", tmp_path / "traffic.json"
