@@ -1148,10 +1148,12 @@ def test_bwd_negative_scale_strided_5d(A):
     check_grads([x.reshape(B, M, G * Hg, D) for x in (dq, dk, dv)], ref, "5-D strided", bound)
 
 
-def test_bwd_expanded_gqa(A):
-    """K/V heads broadcast with stride 0 (GQA); dk/dv come back per expanded head."""
+@pytest.mark.parametrize("keep_ds", [False, True])
+def test_bwd_expanded_gqa(A, keep_ds):
+    """K/V heads broadcast with stride 0 (GQA); dk/dv come back per expanded head.  Both backward
+    forms (the kept-dS one indexes its dS buffer by the expanded head)."""
     B, M, G, Hg, D = 1, 300, 2, 3, 128
-    say("case: bwd expanded GQA")
+    say(f"case: bwd expanded GQA keep_ds={keep_ds}")
     qh = synth.normal(980, 0, (B, M, G, Hg, D), "bf16")
     kb, vb = synth.normal(980, 1, (B, M, G, 1, D), "bf16"), synth.normal(980, 2, (B, M, G, 1, D), "bf16")
     gh = synth.normal(980, 3, (B, M, G, Hg, D), "bf16")
@@ -1161,7 +1163,7 @@ def test_bwd_expanded_gqa(A):
     dq = torch.empty_like(q)
     dk = torch.empty((B, M, G, Hg, D), dtype=torch.bfloat16, device="cuda")
     dv = torch.empty_like(dk)
-    A.attn_bwd(g, q, k, v, out, lse, mask=1, dq=dq, dk=dk, dv=dv)
+    A.attn_bwd(g, q, k, v, out, lse, mask=1, dq=dq, dk=dk, dv=dv, keep_ds=keep_ds)
     torch.cuda.synchronize()
     rep = lambda x: synth.to_f64(np.repeat(x, Hg, axis=3), "bf16").reshape(B, M, G * Hg, D)
     q64, g64 = synth.to_f64(qh, "bf16").reshape(B, M, G * Hg, D), synth.to_f64(gh, "bf16").reshape(B, M, G * Hg, D)
@@ -1170,6 +1172,31 @@ def test_bwd_expanded_gqa(A):
     ref = oracle.attention_backward(g64, oo, ol, q64, k64, v64, mask=1)
     bound = bwd_error_bound(q64, k64, v64, g64, oo, ol, ref, mask=1)
     check_grads([x.reshape(B, M, G * Hg, D) for x in (dq, dk, dv)], ref, "expanded GQA", bound)
+
+
+@pytest.mark.parametrize("keep_ds", [False, True])
+def test_bwd_empty_sides(A, keep_ds):
+    """No keys: the forward gives out = 0 and lse = -inf, and the backward writes dq = 0.  No
+    queries: dk = dv = 0.  Gradients start as NaN, so every element is seen written."""
+    B, H, D = 2, 3, 128
+    say(f"case: bwd with no keys and with no queries, keep_ds={keep_ds}")
+    q = dev(synth.normal(60, 0, (B, 100, H, D), "bf16"), "bf16")
+    g = dev(synth.normal(60, 3, (B, 100, H, D), "bf16"), "bf16")
+    k0 = torch.empty((B, 0, H, D), dtype=torch.bfloat16, device="cuda")
+    out, lse = A.attn_fwd(q, k0, k0, mask=0)
+    dq = torch.full_like(q, float("nan"))
+    A.attn_bwd(g, q, k0, k0, out, lse, mask=0, dq=dq, dk=torch.empty_like(k0), dv=torch.empty_like(k0),
+               keep_ds=keep_ds)
+    q0 = torch.empty((B, 0, H, D), dtype=torch.bfloat16, device="cuda")
+    k = dev(synth.normal(61, 1, (B, 70, H, D), "bf16"), "bf16")
+    v = dev(synth.normal(61, 2, (B, 70, H, D), "bf16"), "bf16")
+    out0, lse0 = A.attn_fwd(q0, k, v, mask=0)
+    dk, dv = torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    A.attn_bwd(q0, q0, k, v, out0, lse0, mask=0, dq=torch.empty_like(q0), dk=dk, dv=dv, keep_ds=keep_ds)
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 0)) and bool(torch.all(lse == float("-inf")))
+    assert bool(torch.all(dq == 0)), "dq with no keys"
+    assert bool(torch.all(dk == 0)) and bool(torch.all(dv == 0)), "dk, dv with no queries"
 
 
 def test_bwd_causal_full_size(A):
