@@ -612,7 +612,9 @@ def attn_bwd(dout, q, k, v, out, lse, mask=MASK_NONE, scale=None, seqstart_q=Non
 def prepare_bwd(dout, q, k, v, out, lse, dq, dk, dv, workspace, mask=MASK_NONE, scale=None, seqstart_q=None,
                 seqstart_k=None, max_seqlen_q=None, max_seqlen_k=None, window_size=None, window_left=None,
                 window_right=None, stream=None) -> Prepared:
-    """attn_bwd with every argument marshalled up front."""
+    """attn_bwd with every argument marshalled up front.  A workspace of at least
+    attn_bwd_ds_workspace_bytes(...) selects the kept-dS form (bf16, head dim 128, no block-diagonal
+    mask); attn_bwd_workspace_bytes(...) the two-kernel form."""
     args, keep = _bwd_args(dout, q, k, v, out, lse, mask, scale, seqstart_q, seqstart_k, max_seqlen_q,
                            max_seqlen_k, window_size, window_left, window_right, workspace, dq, dk, dv, stream)
     return Prepared(_lib.attn_bwd, args, (keep, dout, q, k, v, out, lse, dq, dk, dv, workspace))
