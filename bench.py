@@ -85,7 +85,7 @@ def rocpd_summary(db_path):
                 print(f"| {cn} | {len(v)} | {sum(v) / len(v):.1f} | {grid} | {name} |")
 
 
-TRAFFIC_SOURCES = {"fwd": ("fwd_bf16.hip", "kernels.h", "tile_common.h"), "decode": ("decode.hip", "kernels.h"),
+TRAFFIC_SOURCES = {"fwd": ("fwd_bf16.hip", "fwd_bf16_body.h", "fwd_bf16_v256.hip", "kernels.h", "tile_common.h"), "decode": ("decode.hip", "kernels.h"),
                    "bwd": ("bwd_bf16.hip", "kernels.h", "tile_common.h")}
 
 

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libattn.so")
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "merge.hip", "bwd_bf16.hip", "bwd_f32.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_bf16_v256.hip", "fwd_f32.hip", "decode.hip", "merge.hip", "bwd_bf16.hip", "bwd_f32.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
@@ -34,8 +34,10 @@ def _hipcc() -> str:
 
 
 # Per-file extra flags.  The prefill kernel never produces NaN (masked scores are -inf,
-# never inf - inf), so max() need not quiet NaN operands; infinities stay honoured.
-EXTRA = {"fwd_bf16.hip": ["-fno-honor-nans"]}
+# never inf - inf), so max() need not quiet NaN operands; infinities stay honoured.  The value
+# head dim 256 launches take LLVM's iterative ILP scheduler (5% faster there, same bits).
+EXTRA = {"fwd_bf16.hip": ["-fno-honor-nans"],
+         "fwd_bf16_v256.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _compile(src: str) -> str:

@@ -102,6 +102,7 @@ struct MergeArgs {
 
 // Launchers return a hipError_t from the launch.
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool out_f32, hipStream_t stream);
+hipError_t launch_fwd_bf16_v256(const FwdArgs &a, bool out_f32, hipStream_t stream);  // value head dim 256
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 // Backward of the forward above: dq, dk, dv from dout, out and lse (same masks and layouts).
 struct BwdArgs {
