@@ -85,17 +85,21 @@ def rocpd_summary(db_path):
                 print(f"| {cn} | {len(v)} | {sum(v) / len(v):.1f} | {grid} | {name} |")
 
 
-TRAFFIC_SOURCES = {"fwd": ("fwd_bf16.hip", "fwd_bf16_body.h", "fwd_bf16_v256.hip", "kernels.h", "tile_common.h"), "decode": ("decode.hip", "kernels.h"),
-                   "bwd": ("bwd_bf16.hip", "kernels.h", "tile_common.h")}
+# (paths under transformer_attention_02_amd/: the sources, and build.py for their compile flags)
+TRAFFIC_SOURCES = {"fwd": ("csrc/fwd_bf16.hip", "csrc/fwd_bf16_body.h", "csrc/fwd_bf16_v256.hip", "csrc/kernels.h",
+                           "csrc/tile_common.h", "build.py"),
+                   "decode": ("csrc/decode.hip", "csrc/kernels.h", "build.py"),
+                   "bwd": ("csrc/bwd_bf16.hip", "csrc/kernels.h", "csrc/tile_common.h", "build.py")}
 
 
 def kernel_source_digest(kind="fwd"):
-    """sha256 of a kernel's sources; HBM byte counters recorded for another digest are stale."""
+    """sha256 of a kernel's sources and build flags; HBM byte counters recorded for another digest
+    are stale."""
     import hashlib
 
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES[kind]:
-        with open(os.path.join(ROOT, "transformer_attention_02_amd", "csrc", f), "rb") as fh:
+        with open(os.path.join(ROOT, "transformer_attention_02_amd", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
