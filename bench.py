@@ -125,7 +125,7 @@ def recorded_traffic(key, path=None):
 TRAFFIC_GRID = {"fwd_bf16 causal 2x2048x32x128": 512 * 512, "fwd_bf16 unmasked 2x2048x32x128": 512 * 512,
                 "fwd_bf16 varlen gqa causal 8 seqs": 3584 * 512,
                 "fwd_bf16 sliding window 1024 2x8192x32x128": 2048 * 512,
-                "fwd_bf16 kvcache paged 16x256x32768 s4": 2048 * 512, "fwd_bf16 causal hd256 2x2048x16x256": 512 * 512}
+                "fwd_bf16 kvcache paged 16x256x32768 s4": 2048 * 512, "fwd_bf16 kvcache paged 16x256x32768 s1": 512 * 512, "fwd_bf16 causal hd256 2x2048x16x256": 512 * 512}
 TRAFFIC_KERNELS = (
     # the causal and unmasked launches share kernel and grid: the unmasked one fetches more
     ("fwd_bf16 causal 2x2048x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", 0),
@@ -133,6 +133,7 @@ TRAFFIC_KERNELS = (
     ("fwd_bf16 varlen gqa causal 8 seqs", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
     ("fwd_bf16 sliding window 1024 2x8192x32x128", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, false>", None),
     ("fwd_bf16 kvcache paged 16x256x32768 s4", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, true, true>", None),
+    ("fwd_bf16 kvcache paged 16x256x32768 s1", "fwd", "fwd_bf16_kernel<128, 128, 8, 4, false, true>", None),
     ("fwd_bf16 causal hd256 2x2048x16x256", "fwd", "fwd_bf16_vsplit_kernel<256, 256, false, false>", None),
     ("decode bf16 16x32768x32x128 s64", "decode", "decode_kernel<128, 0, 0, false>", None),
     ("decode bf16 paged 16x32768x32x128 page64 s64", "decode", "decode_kernel<128, 0, 2, false>", None),
@@ -488,28 +489,38 @@ def main():
             ssq = torch.from_numpy(np.arange(0, B * Lq + 1, Lq, dtype=np.int32)).to("cuda")
             ok_ = torch.empty_like(qk)
             lk_ = torch.empty((1, H, B * Lq), dtype=torch.float32, device="cuda")
+            cache = (kd.view(1, B * Mkv, H, D), vd.view(1, B * Mkv, H, D))
+            tm, tm4 = {}, {}
+            # one launch (no key chunks: 512 workgroups of 256 rows keep every CU busy), then the same
+            # work as 4 key chunks of fp32 partials plus the merge
+            ms_k = timed(A.prepare_fwd_kvcache(qk, *cache, ssq, lens, Lq, Mkv, ok_, lk_, mask=A.MASK_CAUSAL_BR,
+                                               block_tables=tab_k, page_size=pg, num_splits=1, workspace=None),
+                         20, 3, torch, detail=tm)
             Sk = 4
             wsk = torch.empty(A.attn_fwd_kvcache_workspace_bytes(B * Lq, H, D, Sk), dtype=torch.uint8, device="cuda")
-            tm = {}
-            ms_k = timed(A.prepare_fwd_kvcache(qk, kd.view(1, B * Mkv, H, D), vd.view(1, B * Mkv, H, D), ssq, lens, Lq,
-                                               Mkv, ok_, lk_, mask=A.MASK_CAUSAL_BR, block_tables=tab_k, page_size=pg,
-                                               num_splits=Sk, workspace=wsk), 20, 3, torch, detail=tm)
+            ms_4 = timed(A.prepare_fwd_kvcache(qk, *cache, ssq, lens, Lq, Mkv, ok_, lk_, mask=A.MASK_CAUSAL_BR,
+                                               block_tables=tab_k, page_size=pg, num_splits=Sk, workspace=wsk),
+                         20, 3, torch, detail=tm4)
             vis = Lq * (Mkv - Lq) + Lq * (Lq + 1) / 2  # keys seen per (sequence, head)
             fl_k = 4.0 * D * H * B * vis
             tf_k = fl_k / (ms_k * 1e-3) / 1e12
-            log(f"kv-cache chunked prefill: {ms_k * 1e3:.1f} us/call, {tf_k:.1f} TFLOP/s")
+            log(f"kv-cache chunked prefill: {ms_k * 1e3:.1f} us/call, {tf_k:.1f} TFLOP/s "
+                f"(4 key chunks + merge: {ms_4 * 1e3:.1f} us/call)")
             result["rows"]["kvcache_chunked_prefill"] = {
                 "workload": "16 sequences x 256 new queries against 32768 cached keys each, cache in 2048 pages of 256 "
-                            "keys (random order), causal with offset, H=32 K=Kv=128 bf16, 4 key chunks + merge "
-                            "(attn_fwd_kvcache)",
+                            "keys (random order), causal with offset, H=32 K=Kv=128 bf16, one launch (attn_fwd_kvcache)",
                 "ms_per_call": round(ms_k, 5), "value": round(tf_k, 2), "unit": "TFLOP/s",
                 "kv_GBps": round(kv_bytes / (ms_k * 1e-3) / 1e9, 1),
                 "roofline": {"bound": "mfma", "achieved": round(tf_k, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(tf_k / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl_k,
-                             "traffic": recorded_traffic("fwd_bf16 kvcache paged 16x256x32768 s4"),
-                             "algorithmic_bytes": kv_bytes + B * Lq * H * (2 * D + Sk * (4 * D + 4)),
-                             "note": "traffic and algorithmic bytes are the attention launch's: K+V once, q, and the "
-                                     "fp32 partial rows and LSEs of its 4 key chunks; the time covers it and the merge"},
+                             "traffic": recorded_traffic("fwd_bf16 kvcache paged 16x256x32768 s1"),
+                             "algorithmic_bytes": kv_bytes + B * Lq * H * (2 * D * 2 + 4),
+                             "note": "K+V once, q and out (bf16), lse"},
+                "key_chunks4": {"ms_per_call": round(ms_4, 5), "value": round(fl_k / (ms_4 * 1e-3) / 1e12, 2),
+                                "traffic": recorded_traffic("fwd_bf16 kvcache paged 16x256x32768 s4"),
+                                "algorithmic_bytes": kv_bytes + B * Lq * H * (2 * D + Sk * (4 * D + 4)),
+                                "note": "4 key chunks of fp32 partials, then the merge; traffic and algorithmic bytes "
+                                        "are the attention launch's (K+V once, q, the partial rows and LSEs)", **tm4},
                 **tm}
             if not args.no_cpu:  # sequence 0's keys gathered through its table, its 256 queries, all 32 heads
                 rows_k = (permk[:Mkv // pg, None] * pg + np.arange(pg)[None, :]).reshape(-1)
