@@ -149,7 +149,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     // L2 (otherwise every tile level of every sequence in turn, heaviest first)
     const bool seq_major = a.kv_groups > 0 && a.nseq > 1;
     const int seq = seq_major ? id / tiles : id % a.nseq;
-    const int tile = tiles - 1 - (seq_major ? id % tiles : id / a.nseq);
+    const int tidx = seq_major ? id % tiles : id / a.nseq;  // 0: the sequence's heaviest row block
     const int b = bh / a.Htot, hf = bh % a.Htot;
 
     int qs = 0, qe = a.Mq, ks = 0, ke = a.Mkv;
@@ -168,8 +168,18 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
         }
     }
     const int Lq = qe - qs, Lk = ke - ks;
-    const int row0 = tile * BM;
-    if (tile < 0 || row0 >= Lq) return;
+    // Row blocks start at row 0, or end at the sequence's last row when its length leaves a
+    // remainder r = Lq mod BM of at most BM - BN rows.  Aligned to the start, the ragged block is
+    // the last one, which sees the most keys under a causal mask; aligned to the end, it is the
+    // first one, which sees the fewest: (blocks - 1) (BM - ceil(r / BN) BN) / BN fewer key tiles.
+    // With a larger remainder the tile counts are equal, and start alignment keeps the diagonal
+    // on tile boundaries.  Either way tidx 0 is the block that ends at the last row.  A first
+    // block aligned to the end starts before row 0; those rows hold nothing.
+    const int rem = Lq % BM;
+    const bool end_aligned = rem != 0 && rem <= BM - BN;
+    const int row0 = end_aligned ? Lq - (tidx + 1) * BM : (tiles - 1 - tidx) * BM;
+    if (end_aligned ? row0 + BM <= 0 : row0 >= Lq) return;  // no row of this sequence
+    const int row0v = max(row0, 0);                          // the block's first row
     // this workgroup's key chunk [kc0, kc1) (the whole sequence unless the keys are split)
     const int kc0 = a.splits > 1 ? min(split * a.chunk, Lk) : 0;
     const int kc1 = a.splits > 1 ? min(kc0 + a.chunk, Lk) : Lk;
@@ -178,13 +188,13 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     const int64_t shift = a.bottom_right ? (int64_t)Lk - Lq : 0;
     auto clampk = [&](int64_t x, int64_t lo_, int64_t hi_) { return (int)(x < lo_ ? lo_ : (x > hi_ ? hi_ : x)); };
     const int row_last = min(row0 + BM, Lq) - 1;
-    const int kbeg = clampk((int64_t)row0 + shift - a.wl, kc0, kc1);
+    const int kbeg = clampk((int64_t)row0v + shift - a.wl, kc0, kc1);
     const int kend = clampk((int64_t)row_last + shift + a.wr + 1, kc0, kc1);
     // tiles [tb, te) hold every visible key; [ua, ub) need no mask for any row of the workgroup
     const int tb = kbeg / BN;
     const int te = kend > kbeg ? (kend + BN - 1) / BN : tb;
     int ua = (clampk((int64_t)row_last + shift - a.wl, 0, Lk) + BN - 1) / BN;
-    int ub = clampk((int64_t)row0 + shift + a.wr + 1, 0, Lk) / BN;
+    int ub = clampk((int64_t)row0v + shift + a.wr + 1, 0, Lk) / BN;
     ua = min(max(ua, tb), te);
     ub = min(max(ub, ua), te);
     // Position p of the key loop takes the tile of [tb, te) congruent to p modulo the tile count: workgroups whose ranges have the same length and overlap (the query tiles of a
@@ -258,7 +268,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
     const unsigned qflip = c < 0.f ? 0x80008000u : 0u;  // negative scale: negate q, keep c > 0
     c = fabsf(c);
     bf16x8 qf[KS];
-    if (qrow < Lq) {
+    if (qrow >= 0 && qrow < Lq) {
         const u32x4 *src = (const u32x4 *)(qp + (int64_t)qrow * a.sq.m + 8 * hh);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -661,11 +671,11 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs &a) {
         store_rows_bf16<VW>(o, inv, (unsigned char LDS_AS *)smem + wave * 32 * VW * 2, obase_p,
                             (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) + (int64_t)(qs + wrow0) * a.so.m +
                                 vpart * VW,
-                            a.so.m, Lq - wrow0);
-        if (qrow < Lq && lse_p && hh == 0 && vpart == 0)
+                            a.so.m, Lq - wrow0, -wrow0);
+        if (qrow >= 0 && qrow < Lq && lse_p && hh == 0 && vpart == 0)
             lse_p[((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow] =
                 l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
-    } else if (qrow < Lq) {
+    } else if (qrow >= 0 && qrow < Lq) {
         unsigned char *op = obase_p;
         const int64_t obase = (int64_t)b * a.so.b + head_offset(a.so, hf, a.Hin) + (int64_t)(qs + qrow) * a.so.m;
 #pragma unroll

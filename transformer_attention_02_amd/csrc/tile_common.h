@@ -84,10 +84,11 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // that no other wave touches; 16-byte chunk index XORed by the row, so that neither the 8-byte
 // writes nor the 16-byte reads conflict) and leave as whole rows: 16-byte stores, HD / 8
 // consecutive lanes per row.  Row r goes to out + 2 * (first + r * stride) bytes and is written
-// only when r < nrows.  Row starts must be 16-byte aligned.
+// only when rfirst <= r < nrows.  Row starts must be 16-byte aligned.
 template <int HD>
 __device__ __forceinline__ void store_rows_bf16(const f32x16 *acc, float sc, unsigned char LDS_AS *stage,
-                                                unsigned char *out, int64_t first, int64_t stride, int nrows) {
+                                                unsigned char *out, int64_t first, int64_t stride, int nrows,
+                                                int rfirst = 0) {
     constexpr int CPR = HD / 8;  // 16-byte chunks per row
     const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
@@ -103,7 +104,7 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16 *acc, float sc, uns
     for (int i = 0; i < 32 * CPR / 64; ++i) {
         const int idx = i * 64 + lane, r = idx / CPR, ch = idx % CPR;
         const u32x4 val = *(const u32x4 LDS_AS *)(stage + r * HD * 2 + ((ch ^ (r & (CPR - 1))) << 4));
-        if (r < nrows) *(u32x4 *)(out + (first + (int64_t)r * stride + ch * 8) * 2) = val;
+        if (r >= rfirst && r < nrows) *(u32x4 *)(out + (first + (int64_t)r * stride + ch * 8) * 2) = val;
     }
 }
 
