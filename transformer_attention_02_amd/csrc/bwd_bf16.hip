@@ -370,21 +370,27 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
     const int bh = id % BH;
     id /= BH;
     const int seq = id % a.nseq;
-    const int tile = tiles - 1 - id / a.nseq;
+    const int tidx = id / a.nseq;  // 0: the sequence's heaviest row block
     const int b = bh / a.Htot, hf = bh % a.Htot;
     int qs, qe, ks, ke;
     seq_bounds(a, seq, qs, qe, ks, ke);
     const int Lq = qe - qs, Lk = ke - ks;
-    const int row0 = tile * BM;
-    if (tile < 0 || row0 >= Lq) return;
+    // row blocks as in the forward: aligned to the sequence's last row when the remainder
+    // Lq mod BM is at most BM - BN rows (the ragged block is then the first, which sees the fewest
+    // keys under a causal mask), else to row 0; rows before row 0 hold nothing
+    const int rem = Lq % BM;
+    const bool end_aligned = rem != 0 && rem <= BM - BN;
+    const int row0 = end_aligned ? Lq - (tidx + 1) * BM : (tiles - 1 - tidx) * BM;
+    if (end_aligned ? row0 + BM <= 0 : row0 >= Lq) return;
+    const int row0v = max(row0, 0);
     const int64_t shift = a.bottom_right ? (int64_t)Lk - Lq : 0;
     const int row_last = min(row0 + BM, Lq) - 1;
-    const int kbeg = clampk((int64_t)row0 + shift - a.wl, 0, Lk);
+    const int kbeg = clampk((int64_t)row0v + shift - a.wl, 0, Lk);
     const int kend = clampk((int64_t)row_last + shift + a.wr + 1, 0, Lk);
     const int tb = kbeg / BN;
     const int te = kend > kbeg ? (kend + BN - 1) / BN : tb;
     int ua = (clampk((int64_t)row_last + shift - a.wl, 0, Lk) + BN - 1) / BN;
-    int ub = clampk((int64_t)row0 + shift + a.wr + 1, 0, Lk) / BN;
+    int ub = clampk((int64_t)row0v + shift + a.wr + 1, 0, Lk) / BN;
     ua = min(max(ua, tb), te);
     ub = min(max(ub, ua), te);
 
@@ -427,7 +433,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
     const int khi_w = clampk((int64_t)wrow0 + shift + a.wr, -1, Lk - 1);
     bf16x8 qf[KS], gf[KS];
     float l2 = INFINITY, dd = 0.f;
-    if (qrow < Lq) {
+    if (qrow >= 0 && qrow < Lq) {
         const u32x4 *qsrc = (const u32x4 *)(qp + (int64_t)qrow * a.sq.m + 8 * hh);
         const u32x4 *gsrc = (const u32x4 *)(gp + (int64_t)qrow * a.sdo.m + 8 * hh);
 #pragma unroll
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
         auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(dd), __float_as_uint(dd), false, false);
         dd = __uint_as_float(p[0]) + __uint_as_float(p[1]);
     }
-    if (qrow < Lq && hh == 0) {
+    if (qrow >= 0 && qrow < Lq && hh == 0) {
         const int64_t w = ((int64_t)b * a.Htot + hf) * a.Mq + qs + qrow;
         a.ws_d[w] = dd;
         a.ws_l2[w] = l2;
@@ -553,7 +559,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();  // every wave has finished reading the K/V ring
     store_rows_bf16<HD>(dq, a.scale, (unsigned char LDS_AS *)smem + wave * 32 * ROWB, (unsigned char *)a.dq,
                         (int64_t)b * a.sdq.b + head_offset(a.sdq, hf, a.Hin) + (int64_t)(qs + wrow0) * a.sdq.m,
-                        a.sdq.m, Lq - wrow0);
+                        a.sdq.m, Lq - wrow0, -wrow0);
 }
 
 // ------------------------------------------------------------------ kept-dS form (one sequence)
