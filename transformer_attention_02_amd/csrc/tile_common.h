@@ -22,8 +22,10 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // at 4 column offsets (the transpose reads), hit distinct banks.
 template <int HD>
 __device__ __forceinline__ int swz(int row) {
-    // rows of 256 bytes or more: the low four chunk bits span the 64 banks once
-    if (HD >= 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+    // rows of 256 bytes or more: the low four chunk bits span the 64 banks once.  16 consecutive
+    // rows take 16 distinct values, and 4 consecutive rows from a multiple of 4 differ in the
+    // upper two bits, so a transposed read's 32 lanes (4 rows x 32 columns) cover 16 chunks
+    if (HD >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
     return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
 }
 
