@@ -26,7 +26,9 @@ __device__ __forceinline__ int swz(int row) {
     // rows take 16 distinct values, and 4 consecutive rows from a multiple of 4 differ in the
     // upper two bits, so a transposed read's 32 lanes (4 rows x 32 columns) cover 16 chunks
     if (HD >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+    // 128-byte rows (two per bank span): 8 rows of one parity take 8 distinct values, and the two
+    // rows of one parity in an aligned 4-row group differ in the upper bit
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
 // Raw buffer descriptor: byte range [base, base + num_records) is readable, the rest reads as 0.
